@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Benchmark: encoded points/s of one forward + backward pass of the hash-grid encoding.
+
+Default workload: 3D d-linear, L=16, F=2, T=2^19 rows per level, N 16..2048, 2^20 points
+(the Instant-NGP standard size).  One step = zero the gradient buffer, forward (gamma),
+backward (scatter-add into the tables) with inputs already resident in GPU memory.
+
+Prints ONE JSON line.  Besides the headline value it carries
+  roofline      achieved algorithmic GB/s of the dominant kernel against the 8 TB/s HBM peak,
+                its average launch duration from HIP events on the launch stream, and the
+                HBM traffic measured by counters (when recorded for the current kernels);
+  cpu_baseline  the plain CPU oracle timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "encoded points/s fwd+bwd (3D L=16 T=2^19 F=2) + % of HBM roofline"
+HEADLINE = "dlinear3d_L16_T19"
+
+# HBM traffic per launch measured with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled
+# by the copy-kernel calibration), keyed by (workload, kernel).  Only valid for the kernel
+# source it was taken on; set to None when the kernel changes.
+MEASURED_TRAFFIC_BYTES: dict = {}
+
+
+def algorithmic_bytes_per_point(spec: dict) -> dict:
+    """Bytes the method itself moves per point: streamed inputs/outputs, every table value
+    referenced (4 B per fp32 gather) and every fp32 atomic as a read-modify-write (8 B)."""
+    d, L, F = spec["d"], spec["L"], spec["F"]
+    LF = L * F
+    x_bytes = 4 * d
+    if spec["kind"] == "hermite":
+        out_floats = LF * (1 + d + (d if spec.get("d2_mode") == "diag" else 1))
+        coeffs = L * (1 << d) * (1 << d) * F
+    else:
+        out_floats = LF
+        coeffs = L * (1 << d) * F
+    return {"forward": x_bytes + 4 * out_floats + 4 * coeffs,
+            "backward": x_bytes + 4 * out_floats + 8 * coeffs}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from multiresolution_hash_grid_multires_amd import api
+    from multiresolution_hash_grid_multires_amd import inputs as I
+
+    W = I.WORKLOADS[args.workload]
+    if "mlp" in W:
+        print("bench.py: use --workload on an encoder workload", file=sys.stderr)
+        return 2
+    spec = W["spec"]
+    n = W["n_points"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    enc = api.HashGridEncoding(spec)
+    x_h = I.points(W["id"], n, spec["d"])
+    params_h = I.tables(W["id"], enc.n_params, W["tables"])
+    shapes = enc.output_shapes(n)
+    ups_h = I.upstream(W["id"], list(shapes.values()))
+    x = torch.from_numpy(x_h).to(dev)
+    params = torch.from_numpy(params_h).to(dev)
+    outs = {k: torch.empty(s, device=dev) for k, s in shapes.items()}
+    ups = [torch.from_numpy(u).to(dev) for u in ups_h]
+    ups += [None] * (3 - len(ups))
+    grad = torch.zeros(enc.n_params, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        grad.zero_()
+        if ev is not None:
+            ev[0].record(stream)
+        api.hashenc_forward(enc.handle, x, params, outs["gamma"], outs.get("dgamma"), outs.get("d2gamma"))
+        if ev is not None:
+            ev[1].record(stream)
+        api.hashenc_backward(enc.handle, x, ups[0], ups[1], ups[2], grad)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, HIP events on the launch stream around each kernel
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = total_ms / args.steps
+    value = n / (ms_per_step * 1e-3)
+
+    alg = algorithmic_bytes_per_point(spec)
+    kern = {"forward": {"ms": fwd_ms, "alg_bytes": alg["forward"] * n},
+            "backward": {"ms": bwd_ms, "alg_bytes": alg["backward"] * n}}
+    for k in kern.values():
+        k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
+    dom = max(kern, key=lambda k: kern[k]["ms"])
+    traffic = MEASURED_TRAFFIC_BYTES.get((args.workload, dom))
+    roofline = {"bound": "hbm", "achieved": round(kern[dom]["GBps"], 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(kern[dom]["GBps"] / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "kernel": f"{spec['kind']}_{dom}",
+                "avg_launch_ms": round(kern[dom]["ms"], 4),
+                "alg_bytes_per_launch": kern[dom]["alg_bytes"]}
+    step_alg = alg["forward"] + alg["backward"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        m = min(n, 1 << 16)
+        for _ in range(8):
+            xs = x_h[:m]
+            us = [u[:m] for u in ups_h]
+            t0 = time.perf_counter()
+            O.forward(spec, xs, params_h)
+            O.backward(spec, xs, *us, n_params=enc.n_params)
+            dt = time.perf_counter() - t0
+            if dt > 0.2 * args.cpu_seconds or m == n:
+                break
+            m = min(n, int(m * min(16.0, max(2.0, 0.3 * args.cpu_seconds / max(dt, 1e-3)))))
+        cpu = {"value": round(m / dt, 1), "unit": "points/s", "cores": O.max_threads(), "kind": "oracle",
+               "sample": f"{m} of the {n} points of the same workload, one fwd+bwd, fp64 oracle",
+               "seconds": round(dt, 2)}
+
+    line = {
+        "metric": METRIC if args.workload == HEADLINE else f"encoded points/s fwd+bwd ({args.workload})",
+        "value": round(value, 1),
+        "unit": "points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n_points": n, "d": spec["d"], "L": spec["L"],
+                   "F": spec["F"], "T": spec["T"], "kind": spec["kind"]},
+        "hbm_roofline_pct_step": round(100.0 * value * step_alg / (HBM_PEAK_GBPS * 1e9), 2),
+        "kernels": {k: {"ms": round(v["ms"], 4), "GBps": round(v["GBps"], 1)} for k, v in kern.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

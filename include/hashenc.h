@@ -1,0 +1,164 @@
+/*
+ * hashenc — multiresolution hash-grid encoding on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Unless a comment says "host", every pointer
+ * argument is a DEVICE pointer to memory owned by the caller; the library never frees or
+ * retains it.  The handle owns host metadata only (no device memory), is immutable after
+ * creation, and may be used from several threads on several streams at once.
+ *
+ * The method (sources are the public pages this library was written from):
+ *  - Instant-NGP multiresolution hash encoding: "SIGGRAPH 2022 | InstantNGP and
+ *    multiresolution hash encoding" (nxrte.com), section on the encoding pipeline
+ *    (per level: the 2^d cell vertices around x, table lookup, d-linear interpolation,
+ *    concatenation over levels; the 1:1 map at coarse levels and the spatial hash at fine
+ *    ones), and the Instant-NGP news article (antipu.com.cn), paragraphs on adaptivity
+ *    (L levels of up to T F-dimensional vectors; colliding gradients combine) and on
+ *    efficiency (no control flow; all levels looked up in parallel), and the Figure 3
+ *    paragraph (levels in geometric progression between N_min and N_max).
+ *  - Hermite-NGP gradient-augmented encoding: "Hermite-NGP: Gradient-Augmented Hash
+ *    Encoding for Learning PDEs" notes (m0rtzz.github.io), key design 1 (tables bucketed
+ *    by derivative order holding all 2^d mixed partials per vertex; tensor-product cubic
+ *    Hermite reconstruction with the Delta x^{|alpha|} scaling) and key design 2 (analytic
+ *    first and second derivatives of the basis; SIREN chain rule).
+ *
+ * Readings fixed by this library where the pages lost the formula (stated once here):
+ *  - N_l = floor(N_min * b^l + 1e-6) in fp64, b = exp((ln N_max - ln N_min)/(L-1)) unless
+ *    a growth factor b or an explicit list is given;
+ *  - spatial hash of integer vertex v: XOR over axes of (v_i * pi_i mod 2^32),
+ *    pi = (1, 2654435761, 805459861), reduced mod T;
+ *  - a (table, level) is a dense 1:1 grid iff (N_l+1)^d <= T; then row = sum_i v_i (N_l+1)^i;
+ *    it stores min(T, (N_l+1)^d) rows;
+ *  - vertices sit at v / N_l; p = x * N_l is ONE rounded fp32 multiply, base =
+ *    min(floor(p), N_l - 1), t = p - base; x is clamped to [0, 1] (NaN -> 0);
+ *  - Hermite: d+1 tables, table k holds the C(d,k) derivative slots of order k in
+ *    lexicographic axis order (x, y, z | xy, xz, yz | xyz), each slot F floats;
+ *  - colliding rows receive the SUM of their gradient contributions.
+ *
+ * Return codes: 0 on success, a negative HASHENC_E* code otherwise; hashenc_last_error()
+ * then returns a message (thread-local).  All argument checks happen before any launch.
+ * Launches are asynchronous on `stream` (NULL = the null stream); device faults surface at
+ * the caller's next synchronisation.  Nothing throws or aborts across this boundary.
+ */
+#ifndef HASHENC_H
+#define HASHENC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define HASHENC_API __attribute__((visibility("default")))
+#else
+#define HASHENC_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hashenc_stream_t; /* a hipStream_t */
+
+enum {
+  HASHENC_OK = 0,
+  HASHENC_EINVAL = -1,       /* bad configuration, size or NULL required pointer */
+  HASHENC_EALIGN = -2,       /* a device pointer is not 16-byte aligned */
+  HASHENC_ENOMEM = -3,       /* host allocation failed */
+  HASHENC_EHIP = -4,         /* a HIP runtime / launch error (message has hipGetErrorString) */
+  HASHENC_EUNSUPPORTED = -5  /* valid request this build does not implement */
+};
+
+typedef enum { HASHENC_DLINEAR = 0, HASHENC_HERMITE = 1 } hashenc_kind;
+typedef enum { HASHENC_D2_LAPLACIAN = 1, HASHENC_D2_DIAG = 2 } hashenc_d2_mode;
+
+#define HASHENC_MAX_LEVELS 32
+
+typedef struct hashenc_config {
+  int32_t d;             /* spatial dimension: 2 or 3 */
+  int32_t n_levels;      /* L: 1..32 */
+  int32_t n_features;    /* F: 1, 2, 4 or 8 features per derivative slot */
+  int32_t kind;          /* hashenc_kind */
+  int32_t d2_mode;       /* Hermite only: hashenc_d2_mode of the second-order output */
+  int32_t n_min;         /* N_min >= 1: coarsest resolution */
+  int32_t n_max;         /* N_max >= N_min: finest resolution (used when growth <= 0) */
+  int32_t reserved;      /* must be 0 */
+  double growth;         /* b > 0: N_l = floor(N_min b^l + 1e-6); <= 0: derived from n_max */
+  uint32_t table_size[4];/* T_k >= 1 rows for table k (derivative order k); d-linear uses
+                            [0]; Hermite uses [0..d].  Powers of two take a mask fast path */
+  const int32_t* resolutions; /* host, optional: explicit N_l[L] (each 1..2^20); overrides
+                                 n_min/n_max/growth when not NULL */
+} hashenc_config;
+
+typedef struct hashenc hashenc; /* opaque */
+
+/* Validate `cfg` (host) and build a handle.  *out is set only on success. */
+HASHENC_API int hashenc_create(const hashenc_config* cfg, hashenc** out);
+
+/* Release a handle.  NULL is accepted. */
+HASHENC_API void hashenc_destroy(hashenc* h);
+
+/* Sizes (host outputs, each may be NULL): total parameter floats, output width L*F, and the
+ * level resolutions N_l (array of L). */
+HASHENC_API int hashenc_info(const hashenc* h, int64_t* n_params, int32_t* out_width, int32_t* resolutions);
+
+/* Where table `order` (derivative order k; 0 for d-linear) of level `level` lives in the
+ * flat parameter (and gradient) buffer: float offset, rows, floats per row (C(d,k) * F) and
+ * whether it is a dense 1:1 grid.  Host outputs, each may be NULL. */
+HASHENC_API int hashenc_param_layout(const hashenc* h, int32_t order, int32_t level, int64_t* offset,
+                         int64_t* rows, int32_t* row_width, int32_t* is_dense);
+
+/* Forward encoding of n points.
+ *   x       [n, d] fp32, row-major
+ *   params  [n_params] fp32 in the layout above
+ *   gamma   [n, L*F]  level-major then feature (may be NULL)
+ *   dgamma  Hermite only: [n, d, L*F] spatial gradient (may be NULL; must be NULL for d-linear)
+ *   d2gamma Hermite only: Laplacian [n, L*F] or diagonal [n, d, L*F] per cfg.d2_mode
+ *           (may be NULL; must be NULL for d-linear)
+ * Outputs are overwritten.  n == 0 is a no-op. */
+HASHENC_API int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* params,
+                    float* gamma, float* dgamma, float* d2gamma, hashenc_stream_t stream);
+
+/* Backward: grad_params += d<G, forward(theta)>/d theta for the upstream gradients G
+ * (shapes as the forward outputs; NULL = zero).  Contributions of colliding vertices sum.
+ * Accumulated with fp32 atomics: the summation order, and so the last bits, vary from
+ * run to run.  The caller zeroes grad_params when it wants a fresh gradient. */
+HASHENC_API int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
+                     const float* g_dgamma, const float* g_d2gamma, float* grad_params,
+                     hashenc_stream_t stream);
+
+/* SIREN decoder of the fused PINN residual (Hermite-NGP key design 2; loss section):
+ * `depth` hidden layers of width `hidden`, activation sin(omega (W v + b)), then a linear
+ * output of width 1.  `in` must equal L*F. */
+typedef struct hashenc_mlp {
+  int32_t in;
+  int32_t hidden;  /* 16, 32 or 64 */
+  int32_t depth;   /* 1..4 */
+  int32_t out;     /* must be 1 */
+  float omega;     /* e.g. 30 */
+  int32_t reserved;/* must be 0 */
+} hashenc_mlp;
+
+/* Device workspace (bytes) hashenc_residual needs for n points. */
+HASHENC_API int hashenc_residual_workspace_size(const hashenc* h, const hashenc_mlp* mlp, int64_t n,
+                                    size_t* bytes);
+
+/* One fused PINN residual step for the Poisson problem Lap u = g with the manufactured
+ * source g(x) = -d pi^2 prod_i sin(pi x_i), on a Hermite handle:
+ *   encode (gamma, grad gamma, Lap gamma) -> SIREN in forward mode (u, grad u, Lap u) ->
+ *   r = Lap u - g -> loss = mean r^2 -> reverse sweep -> encoder backward.
+ *   mlp_params  packed W1[hidden][in], b1, (Wk[hidden][hidden], bk)..., Wo[1][hidden], bo
+ *   residual    [n] r (may be NULL)
+ *   loss        [1] mean r^2 (overwritten)
+ *   grad_params += dloss/dtheta;  grad_mlp += dloss/dmlp_params (same packing)
+ *   workspace   >= hashenc_residual_workspace_size bytes, 256-byte aligned
+ * n must be >= 1. */
+HASHENC_API int hashenc_residual(const hashenc* h, const hashenc_mlp* mlp, int64_t n, const float* x,
+                     const float* params, const float* mlp_params, float* residual,
+                     float* loss, float* grad_params, float* grad_mlp, void* workspace,
+                     size_t workspace_bytes, hashenc_stream_t stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+HASHENC_API const char* hashenc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HASHENC_H */

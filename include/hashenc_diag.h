@@ -1,0 +1,29 @@
+/*
+ * hashenc diagnostics: entry points for parity testing and bandwidth calibration.
+ * Same conventions as hashenc.h (device pointers owned by the caller, 0 / HASHENC_E*
+ * return codes, asynchronous on `stream`).
+ */
+#ifndef HASHENC_DIAG_H
+#define HASHENC_DIAG_H
+
+#include "hashenc.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Export the lookup stage: for every point and level, the row of table `order` that each of
+ * the 2^d cell corners maps to (dense 1:1 index or spatial hash mod T; see hashenc.h for
+ * the rules).  out_rows [n, L, 2^d] int32, corner bit i = +1 along axis i.  Computed by
+ * the same device code the forward and backward kernels use. */
+HASHENC_API int hashenc_debug_indices(const hashenc* h, int64_t n, const float* x, int32_t order,
+                          int32_t* out_rows, hashenc_stream_t stream);
+
+/* Plain streaming copy dst[i] = src[i], i < n_floats (both 16-byte aligned, no overlap).
+ * Used to measure achievable HBM bandwidth and to calibrate memory counters. */
+HASHENC_API int hashenc_diag_copy(const float* src, float* dst, int64_t n_floats, hashenc_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HASHENC_DIAG_H */

@@ -1,0 +1,195 @@
+"""Thin Python binding over the C ABI in ``include/hashenc.h``.
+
+Functions keep the C names and only marshal arguments: torch tensors are checked (device,
+dtype, contiguity) and passed as raw device pointers with the current HIP stream.  Every
+step of the computation runs in the HIP library.  PyTorch supplies device memory and
+streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import check, load
+
+
+def _spec_to_config(spec: dict) -> tuple[_lib.HashencConfig, object]:
+    cfg = _lib.HashencConfig()
+    cfg.d = int(spec["d"])
+    cfg.n_levels = int(spec["L"])
+    cfg.n_features = int(spec["F"])
+    cfg.kind = _lib.HASHENC_HERMITE if spec["kind"] == "hermite" else _lib.HASHENC_DLINEAR
+    cfg.d2_mode = (_lib.HASHENC_D2_DIAG if spec.get("d2_mode") == "diag" else _lib.HASHENC_D2_LAPLACIAN)
+    cfg.n_min = int(spec.get("n_min", 0))
+    cfg.n_max = int(spec.get("n_max", 0))
+    cfg.reserved = 0
+    cfg.growth = float(spec.get("growth") or 0.0)
+    T = list(spec["T"])
+    n_tab = cfg.d + 1 if cfg.kind == _lib.HASHENC_HERMITE else 1
+    if len(T) == 1:
+        T = T * n_tab
+    for k in range(min(len(T), 4)):
+        cfg.table_size[k] = int(T[k])
+    keep = None
+    if spec.get("resolutions") is not None:
+        keep = (ctypes.c_int32 * cfg.n_levels)(*[int(v) for v in spec["resolutions"]])
+        cfg.resolutions = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
+    return cfg, keep
+
+
+class Handle:
+    """Owns one ``hashenc*``; destroyed with the object."""
+
+    def __init__(self, ptr: int, spec: dict):
+        self.ptr = ctypes.c_void_p(ptr)
+        self.spec = dict(spec)
+
+    def __del__(self):
+        if getattr(self, "ptr", None) is not None and self.ptr.value and _lib._lib is not None:
+            _lib._lib.hashenc_destroy(self.ptr)
+            self.ptr = None
+
+    @property
+    def _as_parameter_(self):
+        return self.ptr
+
+
+def _dev_ptr(t: torch.Tensor | None, name: str, dtype=torch.float32):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (cuda/HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def hashenc_create(spec: dict) -> Handle:
+    cfg, keep = _spec_to_config(spec)
+    out = ctypes.c_void_p()
+    check(load().hashenc_create(ctypes.byref(cfg), ctypes.byref(out)))
+    del keep
+    return Handle(out.value, spec)
+
+
+def hashenc_destroy(h: Handle) -> None:
+    if h.ptr is not None and h.ptr.value:
+        load().hashenc_destroy(h.ptr)
+        h.ptr = None
+
+
+def hashenc_info(h: Handle) -> tuple[int, int, list[int]]:
+    n_params = ctypes.c_int64()
+    width = ctypes.c_int32()
+    res = (ctypes.c_int32 * _lib.MAX_LEVELS)()
+    check(load().hashenc_info(h, ctypes.byref(n_params), ctypes.byref(width), res))
+    return n_params.value, width.value, [int(v) for v in res[: int(h.spec["L"])]]
+
+
+def hashenc_param_layout(h: Handle, order: int, level: int) -> dict:
+    off, rows = ctypes.c_int64(), ctypes.c_int64()
+    width, dense = ctypes.c_int32(), ctypes.c_int32()
+    check(load().hashenc_param_layout(h, order, level, ctypes.byref(off), ctypes.byref(rows),
+                                      ctypes.byref(width), ctypes.byref(dense)))
+    return {"offset": off.value, "rows": rows.value, "width": width.value, "dense": bool(dense.value)}
+
+
+def hashenc_forward(h: Handle, x: torch.Tensor, params: torch.Tensor, gamma=None, dgamma=None,
+                    d2gamma=None, stream=None) -> None:
+    n = x.shape[0]
+    check(load().hashenc_forward(h, n, _dev_ptr(x, "x"), _dev_ptr(params, "params"),
+                                 _dev_ptr(gamma, "gamma"), _dev_ptr(dgamma, "dgamma"),
+                                 _dev_ptr(d2gamma, "d2gamma"), _stream(stream)))
+
+
+def hashenc_backward(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_d2gamma=None,
+                     grad_params=None, stream=None) -> None:
+    n = x.shape[0]
+    check(load().hashenc_backward(h, n, _dev_ptr(x, "x"), _dev_ptr(g_gamma, "g_gamma"),
+                                  _dev_ptr(g_dgamma, "g_dgamma"), _dev_ptr(g_d2gamma, "g_d2gamma"),
+                                  _dev_ptr(grad_params, "grad_params"), _stream(stream)))
+
+
+@dataclass
+class Mlp:
+    n_in: int
+    hidden: int
+    depth: int
+    omega: float
+
+    def as_c(self) -> _lib.HashencMlp:
+        m = _lib.HashencMlp()
+        m.in_, m.hidden, m.depth, m.out, m.omega, m.reserved = self.n_in, self.hidden, self.depth, 1, self.omega, 0
+        return m
+
+
+def hashenc_residual_workspace_size(h: Handle, mlp: Mlp, n: int) -> int:
+    b = ctypes.c_size_t()
+    m = mlp.as_c()
+    check(load().hashenc_residual_workspace_size(h, ctypes.byref(m), n, ctypes.byref(b)))
+    return int(b.value)
+
+
+def hashenc_residual(h: Handle, mlp: Mlp, x: torch.Tensor, params: torch.Tensor,
+                     mlp_params: torch.Tensor, residual, loss: torch.Tensor, grad_params,
+                     grad_mlp, workspace: torch.Tensor, stream=None) -> None:
+    m = mlp.as_c()
+    check(load().hashenc_residual(h, ctypes.byref(m), x.shape[0], _dev_ptr(x, "x"),
+                                  _dev_ptr(params, "params"), _dev_ptr(mlp_params, "mlp_params"),
+                                  _dev_ptr(residual, "residual"), _dev_ptr(loss, "loss"),
+                                  _dev_ptr(grad_params, "grad_params"), _dev_ptr(grad_mlp, "grad_mlp"),
+                                  _dev_ptr(workspace, "workspace", dtype=workspace.dtype),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def hashenc_debug_indices(h: Handle, x: torch.Tensor, order: int, out_rows: torch.Tensor,
+                          stream=None) -> None:
+    check(load().hashenc_debug_indices(h, x.shape[0], _dev_ptr(x, "x"), order,
+                                       _dev_ptr(out_rows, "out_rows", dtype=torch.int32), _stream(stream)))
+
+
+def hashenc_diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    check(load().hashenc_diag_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), src.numel(), _stream(stream)))
+
+
+class HashGridEncoding:
+    """Convenience wrapper: a handle plus output allocation (torch tensors on the GPU)."""
+
+    def __init__(self, spec: dict):
+        self.spec = dict(spec)
+        self.handle = hashenc_create(spec)
+        self.n_params, self.out_width, self.resolutions = hashenc_info(self.handle)
+        self.d = int(spec["d"])
+        self.hermite = spec["kind"] == "hermite"
+        self.diag = spec.get("d2_mode") == "diag"
+
+    def output_shapes(self, n: int) -> dict:
+        s = {"gamma": (n, self.out_width)}
+        if self.hermite:
+            s["dgamma"] = (n, self.d, self.out_width)
+            s["d2gamma"] = (n, self.d, self.out_width) if self.diag else (n, self.out_width)
+        return s
+
+    def forward(self, x: torch.Tensor, params: torch.Tensor, stream=None) -> dict:
+        out = {k: torch.empty(v, device=x.device, dtype=torch.float32)
+               for k, v in self.output_shapes(x.shape[0]).items()}
+        hashenc_forward(self.handle, x, params, out["gamma"], out.get("dgamma"), out.get("d2gamma"), stream)
+        return out
+
+    def backward(self, x: torch.Tensor, grad_params: torch.Tensor, g_gamma=None, g_dgamma=None,
+                 g_d2gamma=None, stream=None) -> torch.Tensor:
+        hashenc_backward(self.handle, x, g_gamma, g_dgamma, g_d2gamma, grad_params, stream)
+        return grad_params

@@ -1,0 +1,66 @@
+// Diagnostic kernels: export of the lookup stage (corner rows per point and level) and a
+// plain streaming copy used to calibrate bandwidth figures.
+#include "hashenc_internal.h"
+
+namespace hg {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void debug_indices_kernel(const Grid g, int order, int64_t n,
+                                                               const float* __restrict__ x,
+                                                               int32_t* __restrict__ out) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= n) return;
+  float xp[D];
+  for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
+  for (int l = 0; l < g.L; ++l) {
+    uint32_t base[D];
+    float t[D];
+    locate<D>(xp, g.N[l], g.Nf[l], base, t);
+    const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
+    const bool dense = (g.dense[order] >> l) & 1u;
+    for (int c = 0; c < (1 << D); ++c)
+      out[(p * g.L + l) * (1 << D) + c] =
+          (int32_t)corner_row_rt<D>(keys, c, dense, g.T[order], g.Tmask[order]);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void copy_kernel(const float4* __restrict__ src,
+                                                      float4* __restrict__ dst, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
+}
+
+__global__ void copy_tail_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                 int64_t begin, int64_t n) {
+  const int64_t i = begin + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_debug_indices(const Grid& g, int d, int order, int64_t n, const float* x,
+                                int32_t* out, hipStream_t s) {
+  const dim3 grid((unsigned)((n + kBlock - 1) / kBlock));
+  if (d == 2)
+    hipLaunchKernelGGL(debug_indices_kernel<2>, grid, dim3(kBlock), 0, s, g, order, n, x, out);
+  else if (d == 3)
+    hipLaunchKernelGGL(debug_indices_kernel<3>, grid, dim3(kBlock), 0, s, g, order, n, x, out);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 > 0) {
+    int64_t blocks = (n4 + kBlock - 1) / kBlock;
+    if (blocks > 256 * 64) blocks = 256 * 64;  // grid-stride: 64 blocks per CU
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s,
+                       reinterpret_cast<const float4*>(src), reinterpret_cast<float4*>(dst), n4);
+  }
+  if (n % 4) hipLaunchKernelGGL(copy_tail_kernel, dim3(1), dim3(4), 0, s, src, dst, n4 * 4, n);
+  return hipGetLastError();
+}
+
+}  // namespace hg

@@ -1,0 +1,261 @@
+// Host side of the C ABI: configuration checks, level progression, parameter layout,
+// argument validation and kernel dispatch.  No device memory is owned by a handle.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "hashenc.h"
+#include "hashenc_diag.h"
+#include "hashenc_internal.h"
+
+using hg::Grid;
+using hg::kMaxLevels;
+using hg::kMaxTables;
+
+struct hashenc {
+  int32_t d, L, F, kind, d2_mode, n_tables;
+  int32_t N[kMaxLevels];
+  int64_t rows[kMaxTables][kMaxLevels];
+  int32_t width[kMaxTables][kMaxLevels];
+  bool dense[kMaxTables][kMaxLevels];
+  int64_t off[kMaxTables][kMaxLevels];
+  int64_t n_params;
+  Grid grid;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  return HASHENC_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HASHENC_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t binom(int n, int k) {
+  int64_t r = 1;
+  for (int i = 1; i <= k; ++i) r = r * (n - k + i) / i;
+  return r;
+}
+
+// Largest point count one 1-D launch covers (up to 16 lanes per point, 256-lane blocks).
+constexpr int64_t kMaxPoints = (int64_t)0x7fffffff * hg::kBlock / 16;
+
+}  // namespace
+
+extern "C" {
+
+const char* hashenc_last_error(void) { return g_last_error.c_str(); }
+
+int hashenc_create(const hashenc_config* cfg, hashenc** out) {
+  if (!cfg || !out) return fail(HASHENC_EINVAL, "hashenc_create: cfg and out must not be NULL");
+  if (cfg->d != 2 && cfg->d != 3) return fail(HASHENC_EINVAL, "d must be 2 or 3 (got %d)", cfg->d);
+  if (cfg->n_levels < 1 || cfg->n_levels > kMaxLevels)
+    return fail(HASHENC_EINVAL, "n_levels must be in 1..%d (got %d)", kMaxLevels, cfg->n_levels);
+  if (cfg->n_features != 1 && cfg->n_features != 2 && cfg->n_features != 4 && cfg->n_features != 8)
+    return fail(HASHENC_EINVAL, "n_features must be 1, 2, 4 or 8 (got %d)", cfg->n_features);
+  if (cfg->kind != HASHENC_DLINEAR && cfg->kind != HASHENC_HERMITE)
+    return fail(HASHENC_EINVAL, "kind must be HASHENC_DLINEAR or HASHENC_HERMITE (got %d)", cfg->kind);
+  if (cfg->kind == HASHENC_HERMITE && cfg->d2_mode != HASHENC_D2_LAPLACIAN &&
+      cfg->d2_mode != HASHENC_D2_DIAG)
+    return fail(HASHENC_EINVAL, "d2_mode must be HASHENC_D2_LAPLACIAN or HASHENC_D2_DIAG (got %d)",
+                cfg->d2_mode);
+  if (cfg->reserved != 0) return fail(HASHENC_EINVAL, "reserved field must be 0");
+
+  hashenc* h = new (std::nothrow) hashenc();
+  if (!h) return fail(HASHENC_ENOMEM, "hashenc_create: out of host memory");
+  h->d = cfg->d;
+  h->L = cfg->n_levels;
+  h->F = cfg->n_features;
+  h->kind = cfg->kind;
+  h->d2_mode = cfg->kind == HASHENC_HERMITE ? cfg->d2_mode : 0;
+  h->n_tables = cfg->kind == HASHENC_HERMITE ? cfg->d + 1 : 1;
+
+  // Level resolutions: explicit list, or the geometric progression N_min * b^l (floored,
+  // with a 1e-6 guard so exact powers are not lost to fp64 rounding).
+  if (cfg->resolutions) {
+    for (int l = 0; l < h->L; ++l) h->N[l] = cfg->resolutions[l];
+  } else {
+    if (cfg->n_min < 1) { delete h; return fail(HASHENC_EINVAL, "n_min must be >= 1 (got %d)", cfg->n_min); }
+    double b = cfg->growth;
+    if (!(b > 0.0)) {
+      if (h->L > 1 && cfg->n_max < cfg->n_min) {
+        delete h;
+        return fail(HASHENC_EINVAL, "n_max (%d) must be >= n_min (%d)", cfg->n_max, cfg->n_min);
+      }
+      b = h->L == 1 ? 1.0
+                    : std::exp((std::log((double)cfg->n_max) - std::log((double)cfg->n_min)) /
+                               (double)(h->L - 1));
+    }
+    for (int l = 0; l < h->L; ++l) {
+      const double v = std::floor((double)cfg->n_min * std::pow(b, (double)l) + 1e-6);
+      if (!(v >= 1.0 && v <= (double)(1 << 20))) {
+        delete h;
+        return fail(HASHENC_EINVAL, "level %d resolution %.0f outside 1..2^20", l, v);
+      }
+      h->N[l] = (int32_t)v;
+    }
+  }
+  for (int l = 0; l < h->L; ++l)
+    if (h->N[l] < 1 || h->N[l] > (1 << 20)) {
+      const int bad = h->N[l];
+      delete h;
+      return fail(HASHENC_EINVAL, "level %d resolution %d outside 1..2^20", l, bad);
+    }
+
+  // Layout: table k (derivative order), then level, then rows of C(d,k) * F floats.
+  int64_t off = 0;
+  for (int k = 0; k < h->n_tables; ++k) {
+    const uint32_t T = cfg->table_size[k];
+    if (T < 1) {
+      delete h;
+      return fail(HASHENC_EINVAL, "table_size[%d] must be >= 1", k);
+    }
+    const int32_t w = (int32_t)((h->kind == HASHENC_HERMITE ? binom(h->d, k) : 1) * h->F);
+    for (int l = 0; l < h->L; ++l) {
+      const double verts = std::pow((double)h->N[l] + 1.0, (double)h->d);
+      const bool dense = verts <= (double)T;
+      int64_t r = dense ? (int64_t)verts : (int64_t)T;
+      h->rows[k][l] = r;
+      h->width[k][l] = w;
+      h->dense[k][l] = dense;
+      h->off[k][l] = off;
+      off += r * w;
+    }
+  }
+  h->n_params = off;
+  if (off > ((int64_t)1 << 40)) {
+    delete h;
+    return fail(HASHENC_EINVAL, "parameter count %lld too large", (long long)off);
+  }
+
+  Grid& g = h->grid;
+  std::memset(&g, 0, sizeof g);
+  g.L = h->L;
+  g.n_tables = h->n_tables;
+  for (int l = 0; l < h->L; ++l) {
+    g.N[l] = h->N[l];
+    g.Nf[l] = (float)h->N[l];
+    g.invN[l] = 1.0f / (float)h->N[l];
+  }
+  for (int k = 0; k < h->n_tables; ++k) {
+    const uint32_t T = cfg->table_size[k];
+    g.T[k] = T;
+    g.Tmask[k] = (T > 1 && (T & (T - 1)) == 0) ? T - 1 : 0u;
+    for (int l = 0; l < h->L; ++l) {
+      if (h->dense[k][l]) g.dense[k] |= 1u << l;
+      g.off[k][l] = h->off[k][l];
+    }
+  }
+  *out = h;
+  return ok();
+}
+
+void hashenc_destroy(hashenc* h) { delete h; }
+
+int hashenc_info(const hashenc* h, int64_t* n_params, int32_t* out_width, int32_t* resolutions) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_info: NULL handle");
+  if (n_params) *n_params = h->n_params;
+  if (out_width) *out_width = h->L * h->F;
+  if (resolutions)
+    for (int l = 0; l < h->L; ++l) resolutions[l] = h->N[l];
+  return ok();
+}
+
+int hashenc_param_layout(const hashenc* h, int32_t order, int32_t level, int64_t* offset,
+                         int64_t* rows, int32_t* row_width, int32_t* is_dense) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_param_layout: NULL handle");
+  if (order < 0 || order >= h->n_tables)
+    return fail(HASHENC_EINVAL, "order %d outside 0..%d", order, h->n_tables - 1);
+  if (level < 0 || level >= h->L) return fail(HASHENC_EINVAL, "level %d outside 0..%d", level, h->L - 1);
+  if (offset) *offset = h->off[order][level];
+  if (rows) *rows = h->rows[order][level];
+  if (row_width) *row_width = h->width[order][level];
+  if (is_dense) *is_dense = h->dense[order][level] ? 1 : 0;
+  return ok();
+}
+
+int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* params,
+                    float* gamma, float* dgamma, float* d2gamma, hashenc_stream_t stream) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_forward: NULL handle");
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward: n = %lld out of range", (long long)n);
+  if (h->kind == HASHENC_DLINEAR && (dgamma || d2gamma))
+    return fail(HASHENC_EUNSUPPORTED, "hashenc_forward: derivative outputs need the Hermite kind");
+  if (n == 0 || (!gamma && !dgamma && !d2gamma)) return ok();
+  if (!x || !params) return fail(HASHENC_EINVAL, "hashenc_forward: x and params must not be NULL");
+  if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || !aligned16(dgamma) || !aligned16(d2gamma))
+    return fail(HASHENC_EALIGN, "hashenc_forward: device pointers must be 16-byte aligned");
+  hipError_t e;
+  if (h->kind == HASHENC_DLINEAR)
+    e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma, stream);
+  else
+    e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, gamma,
+                                        dgamma, d2gamma, stream);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_forward launch");
+  return ok();
+}
+
+int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
+                     const float* g_dgamma, const float* g_d2gamma, float* grad_params,
+                     hashenc_stream_t stream) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_backward: NULL handle");
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_backward: n = %lld out of range", (long long)n);
+  if (h->kind == HASHENC_DLINEAR && (g_dgamma || g_d2gamma))
+    return fail(HASHENC_EUNSUPPORTED, "hashenc_backward: derivative upstream needs the Hermite kind");
+  if (n == 0 || (!g_gamma && !g_dgamma && !g_d2gamma)) return ok();
+  if (!x || !grad_params) return fail(HASHENC_EINVAL, "hashenc_backward: x and grad_params must not be NULL");
+  if (!aligned16(x) || !aligned16(grad_params) || !aligned16(g_gamma) || !aligned16(g_dgamma) ||
+      !aligned16(g_d2gamma))
+    return fail(HASHENC_EALIGN, "hashenc_backward: device pointers must be 16-byte aligned");
+  hipError_t e;
+  if (h->kind == HASHENC_DLINEAR)
+    e = hg::launch_dlinear_backward(h->grid, h->d, h->F, n, x, g_gamma, grad_params, stream);
+  else
+    e = hg::launch_hermite_backward(h->grid, h->d, h->F, h->d2_mode, n, x, g_gamma, g_dgamma,
+                                         g_d2gamma, grad_params, stream);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_backward launch");
+  return ok();
+}
+
+int hashenc_debug_indices(const hashenc* h, int64_t n, const float* x, int32_t order,
+                          int32_t* out_rows, hashenc_stream_t stream) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_debug_indices: NULL handle");
+  if (order < 0 || order >= h->n_tables) return fail(HASHENC_EINVAL, "order %d outside 0..%d", order, h->n_tables - 1);
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_debug_indices: n out of range");
+  if (n == 0) return ok();
+  if (!x || !out_rows) return fail(HASHENC_EINVAL, "hashenc_debug_indices: NULL pointer");
+  if (!aligned16(x) || !aligned16(out_rows)) return fail(HASHENC_EALIGN, "hashenc_debug_indices: pointers must be 16-byte aligned");
+  hipError_t e = hg::launch_debug_indices(h->grid, h->d, order, n, x, out_rows, stream);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_debug_indices launch");
+  return ok();
+}
+
+int hashenc_diag_copy(const float* src, float* dst, int64_t n_floats, hashenc_stream_t stream) {
+  if (n_floats < 0) return fail(HASHENC_EINVAL, "hashenc_diag_copy: negative size");
+  if (n_floats == 0) return ok();
+  if (!src || !dst) return fail(HASHENC_EINVAL, "hashenc_diag_copy: NULL pointer");
+  if (!aligned16(src) || !aligned16(dst)) return fail(HASHENC_EALIGN, "hashenc_diag_copy: pointers must be 16-byte aligned");
+  hipError_t e = hg::launch_copy(src, dst, n_floats, stream);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_diag_copy launch");
+  return ok();
+}
+
+}  // extern "C"

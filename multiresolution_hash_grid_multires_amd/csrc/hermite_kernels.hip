@@ -1,0 +1,439 @@
+// Hermite-NGP gradient-augmented hash-grid encoding, gfx950: one pass gives gamma, its
+// spatial gradient and its second derivatives (diagonal or Laplacian); the backward
+// scatter-adds into the order-bucketed tables.
+//
+// Method: "Hermite-NGP: Gradient-Augmented Hash Encoding for Learning PDEs" notes
+// (m0rtzz.github.io), key design 1: every vertex stores all 2^d mixed partials f^(alpha),
+// alpha in {0,1}^d, bucketed into tables by |alpha|; the level field is
+//   gamma_l(x) = sum_g sum_alpha theta^(alpha)_{l,h(g)} H^(alpha)((x - x_g)/Dx_l) Dx_l^|alpha|
+// with H^(alpha) = prod_i h^(alpha_i), far-corner value basis 3t^2 - 2t^3 and derivative
+// basis t^3 - t^2 (the near corner uses their reflections); key design 2: derivatives
+// follow from the factorised basis derivatives, d/dx_i = N_l d/dt_i.
+//
+// Evaluation is sum-factorised: with m_i = 2 c_i + alpha_i in 0..3 (corner bit, derivative
+// bit) the coefficient tensor theta[m_0][m_1]...[F] is contracted one axis at a time
+// against per-axis basis vectors B_i[m], B'_i[m], B''_i[m] that already carry the
+// Dx^alpha_i scaling and the N_l chain-rule factors, so no per-term power or product chain
+// is evaluated.  Corners are visited in x-adjacent pairs (the axis-0 contraction needs
+// exactly one pair), which bounds the live coefficient registers to 2 * 2^d * F.
+#include "hashenc_internal.h"
+#include "vec_io.h"
+
+namespace hg {
+namespace {
+
+// Per-axis basis at local coordinate t, indexed m = 2 c + a.  Values include Dx^a;
+// first derivatives are d/dx (factor N); second derivatives d^2/dx^2 (factor N^2).
+struct AxisBasis {
+  float B[4], dB[4], d2B[4];
+};
+
+__device__ __forceinline__ AxisBasis axis_basis(float t, float N, float invN) {
+  const float s = 1.0f - t;
+  const float t2 = t * t;
+  AxisBasis a;
+  // near corner, value: 1 - 3t^2 + 2t^3 = (1 + 2t)(1 - t)^2
+  const float h00 = (1.0f + 2.0f * t) * s * s;
+  const float h00p = -6.0f * t * s;
+  const float h00pp = 12.0f * t - 6.0f;
+  // near corner, derivative: t - 2t^2 + t^3 = t (1 - t)^2
+  const float h10 = t * s * s;
+  const float h10p = s * (1.0f - 3.0f * t);
+  const float h10pp = 6.0f * t - 4.0f;
+  // far corner, value: 3t^2 - 2t^3
+  const float h01 = t2 * (3.0f - 2.0f * t);
+  // far corner, derivative: t^3 - t^2
+  const float h11 = -t2 * s;
+  const float h11p = t * (3.0f * t - 2.0f);
+  const float h11pp = 6.0f * t - 2.0f;
+  const float N2 = N * N;
+  a.B[0] = h00;          a.dB[0] = N * h00p;   a.d2B[0] = N2 * h00pp;
+  a.B[1] = invN * h10;   a.dB[1] = h10p;       a.d2B[1] = N * h10pp;
+  a.B[2] = h01;          a.dB[2] = -N * h00p;  a.d2B[2] = -N2 * h00pp;
+  a.B[3] = invN * h11;   a.dB[3] = h11p;       a.d2B[3] = N * h11pp;
+  return a;
+}
+
+__host__ __device__ constexpr int popc(int a) { return (a & 1) + ((a >> 1) & 1) + ((a >> 2) & 1); }
+
+// Slot of derivative multi-index `alpha` (bit i = axis i) inside its order table's row:
+// order 1: x, y, z; order 2: xy, xz, yz (lexicographic axis tuples).
+__host__ __device__ constexpr int slot_of(int alpha) {
+  return alpha == 0 ? 0 : alpha == 1 ? 0 : alpha == 2 ? 1 : alpha == 4 ? 2
+       : alpha == 3 ? 0 : alpha == 5 ? 1 : alpha == 6 ? 2 : 0;
+}
+
+__host__ __device__ constexpr int binom_d(int D, int k) {
+  return D == 2 ? (k == 1 ? 2 : 1) : (k == 1 || k == 2 ? 3 : 1);
+}
+
+// Coefficient rows of one corner: table k holds binom(D,k) slots of F floats.
+template <int D, int F>
+struct CornerRows {
+  float r0[F];
+  float r1[binom_d(D, 1) * F];
+  float r2[binom_d(D, 2) * F];
+  float r3[(D == 3 ? 1 : 1) * F];  // order-3 row (D = 3 only)
+
+  template <int ALPHA>
+  __device__ __forceinline__ float& at(int f) {
+    constexpr int k = popc(ALPHA);
+    constexpr int s = slot_of(ALPHA);
+    if constexpr (k == 0) return r0[f];
+    else if constexpr (k == 1) return r1[s * F + f];
+    else if constexpr (k == 2) return r2[s * F + f];
+    else return r3[f];
+  }
+};
+
+// Per-level table lookup state for all order tables.
+struct TableSel {
+  const float* base[kMaxTables];
+  bool dense[kMaxTables];
+};
+
+template <int D, int F, int C>
+__device__ __forceinline__ void gather_corner(const Grid& g, const CellKeys<D>& keys,
+                                              const TableSel& ts, CornerRows<D, F>& cr) {
+  load_vec<F>(ts.base[0] + (size_t)corner_row<D, C>(keys, ts.dense[0], g.T[0], g.Tmask[0]) * F, cr.r0);
+  load_vec<binom_d(D, 1) * F>(
+      ts.base[1] + (size_t)corner_row<D, C>(keys, ts.dense[1], g.T[1], g.Tmask[1]) * (binom_d(D, 1) * F), cr.r1);
+  load_vec<binom_d(D, 2) * F>(
+      ts.base[2] + (size_t)corner_row<D, C>(keys, ts.dense[2], g.T[2], g.Tmask[2]) * (binom_d(D, 2) * F), cr.r2);
+  if constexpr (D == 3)
+    load_vec<F>(ts.base[3] + (size_t)corner_row<D, C>(keys, ts.dense[3], g.T[3], g.Tmask[3]) * F, cr.r3);
+}
+
+template <int D, int F, int C>
+__device__ __forceinline__ void scatter_corner(const Grid& g, const CellKeys<D>& keys,
+                                               float* const (&base)[kMaxTables],
+                                               const bool (&dense)[kMaxTables],
+                                               CornerRows<D, F>& cr) {
+  float* p0 = base[0] + (size_t)corner_row<D, C>(keys, dense[0], g.T[0], g.Tmask[0]) * F;
+#pragma unroll
+  for (int j = 0; j < F; ++j) atomic_add_f32(p0 + j, cr.r0[j]);
+  constexpr int W1 = binom_d(D, 1) * F;
+  float* p1 = base[1] + (size_t)corner_row<D, C>(keys, dense[1], g.T[1], g.Tmask[1]) * W1;
+#pragma unroll
+  for (int j = 0; j < W1; ++j) atomic_add_f32(p1 + j, cr.r1[j]);
+  constexpr int W2 = binom_d(D, 2) * F;
+  float* p2 = base[2] + (size_t)corner_row<D, C>(keys, dense[2], g.T[2], g.Tmask[2]) * W2;
+#pragma unroll
+  for (int j = 0; j < W2; ++j) atomic_add_f32(p2 + j, cr.r2[j]);
+  if constexpr (D == 3) {
+    float* p3 = base[3] + (size_t)corner_row<D, C>(keys, dense[3], g.T[3], g.Tmask[3]) * F;
+#pragma unroll
+    for (int j = 0; j < F; ++j) atomic_add_f32(p3 + j, cr.r3[j]);
+  }
+}
+
+// ------------------------------------------------------------------ forward
+// Outputs of one level: value, d gradient components, d second-derivative components.
+template <int D, int F>
+struct LevelOut {
+  float v[F];
+  float g[D][F];
+  float h[D][F];
+};
+
+// Accumulate the contribution of the x-adjacent corner pair (0, Y) with Y the corner bits
+// of axes 1.. (Y = c1 | c2 << 1).
+template <int D, int F, int Y>
+__device__ __forceinline__ void fwd_pair(const Grid& g, const CellKeys<D>& keys, const TableSel& ts,
+                                         const AxisBasis (&ab)[D], LevelOut<D, F>& o) {
+  CornerRows<D, F> lo, hi;
+  gather_corner<D, F, (Y << 1)>(g, keys, ts, lo);
+  gather_corner<D, F, (Y << 1) | 1>(g, keys, ts, hi);
+  constexpr int c1 = Y & 1;
+  constexpr int c2 = (Y >> 1) & 1;
+  constexpr int NA = 1 << (D - 1);  // derivative patterns over axes 1..D-1
+  [&]<int... A>(std::integer_sequence<int, A...>) {
+    (([&] {
+       constexpr int a1 = A & 1;
+       constexpr int a2 = (A >> 1) & 1;
+       constexpr int m1 = 2 * c1 + a1;
+       constexpr int m2 = 2 * c2 + a2;
+       constexpr int al0 = (a1 << 1) | (a2 << 2);  // alpha with a0 = 0
+       constexpr int al1 = al0 | 1;                 // alpha with a0 = 1
+       float S[F], S1[F], S2[F];
+#pragma unroll
+       for (int f = 0; f < F; ++f) {
+         // contraction over m0 = 2 c0 + a0
+         const float t00 = lo.template at<al0>(f), t01 = lo.template at<al1>(f);
+         const float t10 = hi.template at<al0>(f), t11 = hi.template at<al1>(f);
+         S[f] = ab[0].B[0] * t00 + ab[0].B[1] * t01 + ab[0].B[2] * t10 + ab[0].B[3] * t11;
+         S1[f] = ab[0].dB[0] * t00 + ab[0].dB[1] * t01 + ab[0].dB[2] * t10 + ab[0].dB[3] * t11;
+         S2[f] = ab[0].d2B[0] * t00 + ab[0].d2B[1] * t01 + ab[0].d2B[2] * t10 + ab[0].d2B[3] * t11;
+       }
+       if constexpr (D == 2) {
+         const float w = ab[1].B[m1], wd = ab[1].dB[m1], wdd = ab[1].d2B[m1];
+#pragma unroll
+         for (int f = 0; f < F; ++f) {
+           o.v[f] = fmaf(S[f], w, o.v[f]);
+           o.g[0][f] = fmaf(S1[f], w, o.g[0][f]);
+           o.h[0][f] = fmaf(S2[f], w, o.h[0][f]);
+           o.g[1][f] = fmaf(S[f], wd, o.g[1][f]);
+           o.h[1][f] = fmaf(S[f], wdd, o.h[1][f]);
+         }
+       } else {
+         const float b1 = ab[1].B[m1], b2 = ab[2].B[m2];
+         const float w = b1 * b2;
+         const float w1 = ab[1].dB[m1] * b2, w11 = ab[1].d2B[m1] * b2;
+         const float w2 = b1 * ab[2].dB[m2], w22 = b1 * ab[2].d2B[m2];
+#pragma unroll
+         for (int f = 0; f < F; ++f) {
+           o.v[f] = fmaf(S[f], w, o.v[f]);
+           o.g[0][f] = fmaf(S1[f], w, o.g[0][f]);
+           o.h[0][f] = fmaf(S2[f], w, o.h[0][f]);
+           o.g[1][f] = fmaf(S[f], w1, o.g[1][f]);
+           o.h[1][f] = fmaf(S[f], w11, o.h[1][f]);
+           o.g[2][f] = fmaf(S[f], w2, o.g[2][f]);
+           o.h[2][f] = fmaf(S[f], w22, o.h[2][f]);
+         }
+       }
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, NA>{});
+}
+
+template <int D>
+__device__ __forceinline__ void level_setup(const Grid& g, int l, const float (&xp)[D],
+                                            CellKeys<D>& keys, AxisBasis (&ab)[D]) {
+  uint32_t base[D];
+  float t[D];
+  locate<D>(xp, g.N[l], g.Nf[l], base, t);
+  keys = cell_keys<D>(base, g.N[l]);
+#pragma unroll
+  for (int i = 0; i < D; ++i) ab[i] = axis_basis(t[i], g.Nf[l], g.invN[l]);
+}
+
+template <int D, int F>
+__global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
+    const Grid g, int64_t n, int d2_mode, const float* __restrict__ x,
+    const float* __restrict__ params, float* __restrict__ gamma, float* __restrict__ dgamma,
+    float* __restrict__ d2gamma) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= n) return;
+  float xp[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
+  const int64_t LF = (int64_t)g.L * F;
+  for (int l = 0; l < g.L; ++l) {
+    CellKeys<D> keys;
+    AxisBasis ab[D];
+    level_setup<D>(g, l, xp, keys, ab);
+    TableSel ts;
+#pragma unroll
+    for (int k = 0; k <= D; ++k) {
+      ts.base[k] = params + g.off[k][l];
+      ts.dense[k] = (g.dense[k] >> l) & 1u;
+    }
+    LevelOut<D, F> o;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      o.v[f] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) o.g[i][f] = o.h[i][f] = 0.0f;
+    }
+    fwd_pair<D, F, 0>(g, keys, ts, ab, o);
+    fwd_pair<D, F, 1>(g, keys, ts, ab, o);
+    if constexpr (D == 3) {
+      fwd_pair<D, F, 2>(g, keys, ts, ab, o);
+      fwd_pair<D, F, 3>(g, keys, ts, ab, o);
+    }
+    const int64_t col = (int64_t)l * F;
+    if (gamma) store_vec<F>(gamma + p * LF + col, o.v);
+    if (dgamma) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) store_vec<F>(dgamma + (p * D + i) * LF + col, o.g[i]);
+    }
+    if (d2gamma) {
+      if (d2_mode == HASHENC_D2_DIAG) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) store_vec<F>(d2gamma + (p * D + i) * LF + col, o.h[i]);
+      } else {
+        float lap[F];
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          float s = 0.0f;
+#pragma unroll
+          for (int i = 0; i < D; ++i) s += o.h[i][f];
+          lap[f] = s;
+        }
+        store_vec<F>(d2gamma + p * LF + col, lap);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ backward
+template <int D, int F>
+struct LevelUp {
+  float v[F];
+  float g[D][F];
+  float h[D][F];
+};
+
+// Reverse of fwd_pair: distribute the level upstream onto the coefficients of corner pair
+// (0, Y) and scatter-add them.
+template <int D, int F, int Y>
+__device__ __forceinline__ void bwd_pair(const Grid& g, const CellKeys<D>& keys,
+                                         float* const (&base)[kMaxTables],
+                                         const bool (&dense)[kMaxTables],
+                                         const AxisBasis (&ab)[D], const LevelUp<D, F>& u) {
+  CornerRows<D, F> lo, hi;
+  constexpr int c1 = Y & 1;
+  constexpr int c2 = (Y >> 1) & 1;
+  constexpr int NA = 1 << (D - 1);
+  [&]<int... A>(std::integer_sequence<int, A...>) {
+    (([&] {
+       constexpr int a1 = A & 1;
+       constexpr int a2 = (A >> 1) & 1;
+       constexpr int m1 = 2 * c1 + a1;
+       constexpr int m2 = 2 * c2 + a2;
+       constexpr int al0 = (a1 << 1) | (a2 << 2);
+       constexpr int al1 = al0 | 1;
+       float S[F], S1[F], S2[F];
+       if constexpr (D == 2) {
+         const float w = ab[1].B[m1], wd = ab[1].dB[m1], wdd = ab[1].d2B[m1];
+#pragma unroll
+         for (int f = 0; f < F; ++f) {
+           S[f] = u.v[f] * w + u.g[1][f] * wd + u.h[1][f] * wdd;
+           S1[f] = u.g[0][f] * w;
+           S2[f] = u.h[0][f] * w;
+         }
+       } else {
+         const float b1 = ab[1].B[m1], b2 = ab[2].B[m2];
+         const float w = b1 * b2;
+         const float w1 = ab[1].dB[m1] * b2, w11 = ab[1].d2B[m1] * b2;
+         const float w2 = b1 * ab[2].dB[m2], w22 = b1 * ab[2].d2B[m2];
+#pragma unroll
+         for (int f = 0; f < F; ++f) {
+           S[f] = u.v[f] * w + u.g[1][f] * w1 + u.h[1][f] * w11 + u.g[2][f] * w2 + u.h[2][f] * w22;
+           S1[f] = u.g[0][f] * w;
+           S2[f] = u.h[0][f] * w;
+         }
+       }
+#pragma unroll
+       for (int f = 0; f < F; ++f) {
+         lo.template at<al0>(f) = S[f] * ab[0].B[0] + S1[f] * ab[0].dB[0] + S2[f] * ab[0].d2B[0];
+         lo.template at<al1>(f) = S[f] * ab[0].B[1] + S1[f] * ab[0].dB[1] + S2[f] * ab[0].d2B[1];
+         hi.template at<al0>(f) = S[f] * ab[0].B[2] + S1[f] * ab[0].dB[2] + S2[f] * ab[0].d2B[2];
+         hi.template at<al1>(f) = S[f] * ab[0].B[3] + S1[f] * ab[0].dB[3] + S2[f] * ab[0].d2B[3];
+       }
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, NA>{});
+  scatter_corner<D, F, (Y << 1)>(g, keys, base, dense, lo);
+  scatter_corner<D, F, (Y << 1) | 1>(g, keys, base, dense, hi);
+}
+
+template <int D, int F>
+__global__ __launch_bounds__(kBlock) void hermite_backward_kernel(
+    const Grid g, int64_t n, int d2_mode, const float* __restrict__ x,
+    const float* __restrict__ g_gamma, const float* __restrict__ g_dgamma,
+    const float* __restrict__ g_d2gamma, float* __restrict__ grad) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= n) return;
+  float xp[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
+  const int64_t LF = (int64_t)g.L * F;
+  for (int l = 0; l < g.L; ++l) {
+    const int64_t col = (int64_t)l * F;
+    LevelUp<D, F> u;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      u.v[f] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) u.g[i][f] = u.h[i][f] = 0.0f;
+    }
+    if (g_gamma) load_vec<F>(g_gamma + p * LF + col, u.v);
+    if (g_dgamma) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) load_vec<F>(g_dgamma + (p * D + i) * LF + col, u.g[i]);
+    }
+    if (g_d2gamma) {
+      if (d2_mode == HASHENC_D2_DIAG) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) load_vec<F>(g_d2gamma + (p * D + i) * LF + col, u.h[i]);
+      } else {
+        load_vec<F>(g_d2gamma + p * LF + col, u.h[0]);
+#pragma unroll
+        for (int i = 1; i < D; ++i)
+#pragma unroll
+          for (int f = 0; f < F; ++f) u.h[i][f] = u.h[0][f];
+      }
+    }
+    CellKeys<D> keys;
+    AxisBasis ab[D];
+    level_setup<D>(g, l, xp, keys, ab);
+    float* base[kMaxTables];
+    bool dense[kMaxTables];
+#pragma unroll
+    for (int k = 0; k < kMaxTables; ++k) {
+      base[k] = grad + (k <= D ? g.off[k][l] : 0);
+      dense[k] = (g.dense[k] >> l) & 1u;
+    }
+    bwd_pair<D, F, 0>(g, keys, base, dense, ab, u);
+    bwd_pair<D, F, 1>(g, keys, base, dense, ab, u);
+    if constexpr (D == 3) {
+      bwd_pair<D, F, 2>(g, keys, base, dense, ab, u);
+      bwd_pair<D, F, 3>(g, keys, base, dense, ab, u);
+    }
+  }
+}
+
+template <int D, int F>
+hipError_t launch_fwd(const Grid& g, int d2_mode, int64_t n, const float* x, const float* params,
+                      float* gamma, float* dgamma, float* d2gamma, hipStream_t s) {
+  const dim3 grid((unsigned)((n + kBlock - 1) / kBlock));
+  hipLaunchKernelGGL((hermite_forward_kernel<D, F>), grid, dim3(kBlock), 0, s, g, n, d2_mode, x,
+                     params, gamma, dgamma, d2gamma);
+  return hipGetLastError();
+}
+
+template <int D, int F>
+hipError_t launch_bwd(const Grid& g, int d2_mode, int64_t n, const float* x, const float* gg,
+                      const float* gd, const float* gdd, float* grad, hipStream_t s) {
+  const dim3 grid((unsigned)((n + kBlock - 1) / kBlock));
+  hipLaunchKernelGGL((hermite_backward_kernel<D, F>), grid, dim3(kBlock), 0, s, g, n, d2_mode, x,
+                     gg, gd, gdd, grad);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define HASHENC_DISPATCH_DF(d, F, FN, ...)       \
+  do {                                           \
+    if (d == 2) {                                \
+      switch (F) {                               \
+        case 1: return FN<2, 1>(__VA_ARGS__);    \
+        case 2: return FN<2, 2>(__VA_ARGS__);    \
+        case 4: return FN<2, 4>(__VA_ARGS__);    \
+        case 8: return FN<2, 8>(__VA_ARGS__);    \
+      }                                          \
+    } else if (d == 3) {                         \
+      switch (F) {                               \
+        case 1: return FN<3, 1>(__VA_ARGS__);    \
+        case 2: return FN<3, 2>(__VA_ARGS__);    \
+        case 4: return FN<3, 4>(__VA_ARGS__);    \
+        case 8: return FN<3, 8>(__VA_ARGS__);    \
+      }                                          \
+    }                                            \
+    return hipErrorInvalidValue;                 \
+  } while (0)
+
+hipError_t launch_hermite_forward(const Grid& g, int d, int F, int d2_mode, int64_t n,
+                                  const float* x, const float* params, float* gamma,
+                                  float* dgamma, float* d2gamma, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, d2_mode, n, x, params, gamma, dgamma, d2gamma, s);
+}
+
+hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int64_t n,
+                                   const float* x, const float* g_gamma, const float* g_dgamma,
+                                   const float* g_d2gamma, float* grad, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_bwd, g, d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, grad, s);
+}
+
+}  // namespace hg

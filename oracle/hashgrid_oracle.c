@@ -553,3 +553,12 @@ int64_t orc_mlp_param_count(int32_t in, int32_t hidden, int32_t depth) {
   }
   return off;
 }
+
+/* Threads the OpenMP loops above use. */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -79,6 +79,8 @@ def _load():
         lib.orc_residual.restype = ctypes.c_int
         lib.orc_mlp_param_count.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         lib.orc_mlp_param_count.restype = ctypes.c_int64
+        lib.orc_max_threads.argtypes = []
+        lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -188,6 +190,10 @@ def backward(spec: dict, x: np.ndarray, g_gamma=None, g_dgamma=None, g_d2=None, 
     _load().orc_backward_f64(ctypes.byref(c), n, _ptr(x), _ptr(_f64(g_gamma)), _ptr(_f64(g_dgamma)),
                              _ptr(_f64(g_d2)), _ptr(grad))
     return grad
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
 
 
 def mlp_param_count(n_in: int, hidden: int, depth: int) -> int:

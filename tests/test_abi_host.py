@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports every
+declared entry point; configuration validation, level progression and parameter layout
+agree with the oracle's; every argument error is reported before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from multiresolution_hash_grid_multires_amd import _lib, api
+from multiresolution_hash_grid_multires_amd.inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for h in ("hashenc.h", "hashenc_diag.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"HASHENC_API\s+[\w\s\*]+?\b(hashenc_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = _declared_symbols()
+    assert {"hashenc_create", "hashenc_forward", "hashenc_backward", "hashenc_residual"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert {s[0] for s in _lib.SIGNATURES} == names
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_layout_matches_oracle(orc, name):
+    spec = WORKLOADS[name]["spec"]
+    h = api.hashenc_create(spec)
+    n_params, width, res = api.hashenc_info(h)
+    lay = orc.layout(spec)
+    assert n_params == lay["n_params"]
+    assert width == spec["L"] * spec["F"]
+    assert res == lay["N"]
+    nt = lay["offset"].shape[0]
+    for k in range(nt):
+        for l in range(spec["L"]):
+            pl = api.hashenc_param_layout(h, k, l)
+            assert pl["offset"] == lay["offset"][k, l]
+            assert pl["rows"] == lay["rows"][k, l]
+            assert pl["width"] == lay["width"][k, l]
+            assert pl["dense"] == bool(lay["dense"][k, l])
+
+
+def test_explicit_resolutions_and_growth(orc):
+    spec = {"d": 3, "L": 3, "F": 2, "kind": "hermite", "T": [1 << 10, 1 << 12, 1 << 8, 1 << 9],
+            "resolutions": [5, 9, 30], "d2_mode": "diag"}
+    h = api.hashenc_create(spec)
+    assert api.hashenc_info(h)[2] == [5, 9, 30]
+    assert api.hashenc_info(h)[0] == orc.layout(spec)["n_params"]
+    h2 = api.hashenc_create({"d": 2, "L": 4, "F": 1, "kind": "dlinear", "T": [4096], "n_min": 16, "growth": 1.5})
+    assert api.hashenc_info(h2)[2] == [16, 24, 36, 54]
+
+
+def _create_code(**over):
+    spec = {"d": 3, "L": 4, "F": 2, "kind": "dlinear", "T": [1 << 12], "n_min": 4, "n_max": 32}
+    spec.update(over)
+    return api._spec_to_config(spec)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("d", 1), ("d", 4), ("n_levels", 0), ("n_levels", 33), ("n_features", 3), ("n_features", 16),
+    ("kind", 7), ("reserved", 1), ("n_min", 0), ("n_max", 2),
+])
+def test_create_rejects_bad_config(field, value):
+    cfg, keep = _create_code()
+    setattr(cfg, field, value)
+    out = ctypes.c_void_p()
+    rc = _lib.load().hashenc_create(ctypes.byref(cfg), ctypes.byref(out))
+    assert rc == _lib.HASHENC_EINVAL
+    assert out.value is None
+    assert _lib.load().hashenc_last_error()
+
+
+def test_create_rejects_bad_hermite_mode_and_table():
+    cfg, keep = _create_code(kind="hermite")
+    cfg.d2_mode = 0
+    out = ctypes.c_void_p()
+    assert _lib.load().hashenc_create(ctypes.byref(cfg), ctypes.byref(out)) == _lib.HASHENC_EINVAL
+    cfg.d2_mode = 2
+    cfg.table_size[2] = 0
+    assert _lib.load().hashenc_create(ctypes.byref(cfg), ctypes.byref(out)) == _lib.HASHENC_EINVAL
+    assert b"table_size[2]" in _lib.load().hashenc_last_error()
+
+
+def test_create_rejects_resolution_out_of_range():
+    with pytest.raises(_lib.HashencError) as e:
+        api.hashenc_create({"d": 2, "L": 2, "F": 2, "kind": "dlinear", "T": [64], "resolutions": [4, 0]})
+    assert e.value.code == _lib.HASHENC_EINVAL
+    with pytest.raises(_lib.HashencError):
+        api.hashenc_create({"d": 2, "L": 2, "F": 2, "kind": "dlinear", "T": [64], "n_min": 4,
+                            "growth": 1e7})
+
+
+def test_null_arguments_and_destroy_null():
+    lib = _lib.load()
+    assert lib.hashenc_create(None, None) == _lib.HASHENC_EINVAL
+    lib.hashenc_destroy(None)
+    assert lib.hashenc_info(None, None, None, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_forward(None, 1, None, None, None, None, None, None) == _lib.HASHENC_EINVAL
+
+
+def test_forward_backward_validation_before_launch():
+    lib = _lib.load()
+    h = api.hashenc_create({"d": 3, "L": 2, "F": 2, "kind": "dlinear", "T": [1 << 10], "n_min": 4, "n_max": 8})
+    P = ctypes.c_void_p
+    a, b, c = P(0x10000), P(0x20000), P(0x30000)   # aligned, never dereferenced
+    mis = P(0x20004)
+    # n == 0 and "no outputs" are successful no-ops
+    assert lib.hashenc_forward(h, 0, None, None, None, None, None, None) == 0
+    assert lib.hashenc_forward(h, 5, a, b, None, None, None, None) == 0
+    assert lib.hashenc_backward(h, 5, a, None, None, None, c, None) == 0
+    # errors
+    assert lib.hashenc_forward(h, -1, a, b, c, None, None, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_forward(h, 5, None, b, c, None, None, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_forward(h, 5, a, None, c, None, None, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_forward(h, 5, a, mis, c, None, None, None) == _lib.HASHENC_EALIGN
+    assert lib.hashenc_forward(h, 5, a, b, c, c, None, None) == _lib.HASHENC_EUNSUPPORTED
+    assert lib.hashenc_backward(h, 5, a, b, None, None, None, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_backward(h, 5, a, b, None, None, mis, None) == _lib.HASHENC_EALIGN
+    assert lib.hashenc_backward(h, 5, a, b, c, None, c, None) == _lib.HASHENC_EUNSUPPORTED
+    assert lib.hashenc_backward(h, 1 << 62, a, b, None, None, c, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_debug_indices(h, 5, a, 1, c, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_debug_indices(h, 5, a, 0, mis, None) == _lib.HASHENC_EALIGN
+    assert lib.hashenc_diag_copy(a, mis, 8, None) == _lib.HASHENC_EALIGN
+    assert lib.hashenc_diag_copy(a, b, -1, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_param_layout(h, 1, 0, None, None, None, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_param_layout(h, 0, 2, None, None, None, None) == _lib.HASHENC_EINVAL
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    h = api.hashenc_create({"d": 2, "L": 1, "F": 2, "kind": "dlinear", "T": [64], "n_min": 4, "n_max": 4})
+    with pytest.raises(ValueError):
+        api.hashenc_forward(h, torch.zeros(4, 2), torch.zeros(50), torch.zeros(4, 2))
