@@ -235,6 +235,57 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
   return ok();
 }
 
+static int check_mlp(const hashenc* h, const hashenc_mlp* mlp, const char* who) {
+  if (!h) return fail(HASHENC_EINVAL, "%s: NULL handle", who);
+  if (!mlp) return fail(HASHENC_EINVAL, "%s: NULL mlp", who);
+  if (h->kind != HASHENC_HERMITE)
+    return fail(HASHENC_EUNSUPPORTED, "%s: the residual needs a Hermite handle (second derivatives)", who);
+  if (mlp->in != h->L * h->F)
+    return fail(HASHENC_EINVAL, "%s: mlp.in (%d) must equal L*F (%d)", who, mlp->in, h->L * h->F);
+  if (mlp->in > 64) return fail(HASHENC_EUNSUPPORTED, "%s: mlp.in must be <= 64", who);
+  if (mlp->hidden < 1 || mlp->hidden > 64)
+    return fail(HASHENC_EUNSUPPORTED, "%s: hidden width must be in 1..64 (got %d)", who, mlp->hidden);
+  if (mlp->depth < 1 || mlp->depth > 4)
+    return fail(HASHENC_EUNSUPPORTED, "%s: depth must be in 1..4 (got %d)", who, mlp->depth);
+  if (mlp->out != 1) return fail(HASHENC_EUNSUPPORTED, "%s: output width must be 1", who);
+  if (mlp->reserved != 0) return fail(HASHENC_EINVAL, "%s: mlp.reserved must be 0", who);
+  if (!std::isfinite(mlp->omega)) return fail(HASHENC_EINVAL, "%s: omega must be finite", who);
+  return HASHENC_OK;
+}
+
+int hashenc_residual_workspace_size(const hashenc* h, const hashenc_mlp* mlp, int64_t n,
+                                    size_t* bytes) {
+  int rc = check_mlp(h, mlp, "hashenc_residual_workspace_size");
+  if (rc) return rc;
+  if (n < 1 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_residual_workspace_size: n out of range");
+  if (!bytes) return fail(HASHENC_EINVAL, "hashenc_residual_workspace_size: NULL bytes");
+  *bytes = hg::residual_workspace_bytes(h->d, h->L * h->F, n, mlp->in, mlp->hidden, mlp->depth);
+  return ok();
+}
+
+int hashenc_residual(const hashenc* h, const hashenc_mlp* mlp, int64_t n, const float* x,
+                     const float* params, const float* mlp_params, float* residual, float* loss,
+                     float* grad_params, float* grad_mlp, void* workspace, size_t workspace_bytes,
+                     hashenc_stream_t stream) {
+  int rc = check_mlp(h, mlp, "hashenc_residual");
+  if (rc) return rc;
+  if (n < 1 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_residual: n = %lld out of range", (long long)n);
+  if (!x || !params || !mlp_params || !loss || !workspace)
+    return fail(HASHENC_EINVAL, "hashenc_residual: x, params, mlp_params, loss and workspace must not be NULL");
+  if (!aligned16(x) || !aligned16(params) || !aligned16(mlp_params) || !aligned16(residual) ||
+      !aligned16(loss) || !aligned16(grad_params) || !aligned16(grad_mlp) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(HASHENC_EALIGN, "hashenc_residual: pointers must be 16-byte aligned (workspace 256-byte)");
+  const size_t need = hg::residual_workspace_bytes(h->d, h->L * h->F, n, mlp->in, mlp->hidden, mlp->depth);
+  if (workspace_bytes < need)
+    return fail(HASHENC_EINVAL, "hashenc_residual: workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  hipError_t e = hg::run_residual(h->grid, h->d, h->F, n, x, params, mlp->in, mlp->hidden, mlp->depth,
+                                  mlp->omega, mlp_params, residual, loss, grad_params, grad_mlp,
+                                  workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_residual launch");
+  return ok();
+}
+
 int hashenc_debug_indices(const hashenc* h, int64_t n, const float* x, int32_t order,
                           int32_t* out_rows, hashenc_stream_t stream) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_debug_indices: NULL handle");

@@ -1,24 +1,401 @@
-// Fused PINN residual step (SIREN decoder on the Hermite encoding).
+// Fused PINN residual step on the Hermite encoding, gfx950.
+//
+// Method: "Hermite-NGP: Gradient-Augmented Hash Encoding for Learning PDEs" notes
+// (m0rtzz.github.io), key design 2: the encoding (gamma, grad gamma, Laplacian gamma from
+// one Hermite pass) feeds a SIREN MLP with activation sin(omega .); because
+// sin'' = -omega^2 sin, forward-mode propagation of the value, the d gradient rows and the
+// Laplacian row through each layer needs only the forward intermediates:
+//   z = W v + b,  Z_i = W V_i,  Z_lap = W V_lap,
+//   a = sin(omega z),  A_i = omega cos(omega z) Z_i,
+//   A_lap = -omega^2 sin(omega z) sum_i Z_i^2 + omega cos(omega z) Z_lap;
+// loss section: the PDE residual term, here mean (Lap u - g)^2 for the Poisson problem with
+// source g = -d pi^2 prod_i sin(pi x_i).
+//
+// Pipeline per chunk of points (workspace-backed):
+//   1. Hermite forward, Laplacian mode -> gamma, grad gamma, Lap gamma   (hermite kernels)
+//   2. siren_residual_kernel: one wavefront per point at a time, lane = neuron (width <= 64,
+//      zero-padded), weights resident in LDS in both orientations; forward mode, residual,
+//      reverse sweep; per-lane register accumulation of the lane's weight-gradient rows;
+//      writes the encoder upstream and per-wave partial MLP gradients
+//   3. Hermite backward with that upstream                                (hermite kernels)
+//   4. reduce_partials_kernel: MLP gradients and the loss, summed over waves in fp64
+#include <cmath>
+
 #include "hashenc.h"
 #include "hashenc_internal.h"
 
-extern "C" {
+namespace hg {
+namespace {
 
-int hashenc_residual_workspace_size(const hashenc* h, const hashenc_mlp* mlp, int64_t n,
-                                    size_t* bytes) {
-  (void)h; (void)mlp; (void)n;
-  if (bytes) *bytes = 0;
-  return HASHENC_EUNSUPPORTED;
+constexpr int kW = 64;           // padded layer width (one wavefront)
+constexpr int kWavesPerBlock = 4;
+constexpr int kMaxDepth = 4;
+
+struct MlpArgs {
+  int32_t in, H, depth;
+  float omega;
+  int64_t n_mlp;
+  int64_t woff[kMaxDepth + 1], boff[kMaxDepth + 1];
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
 }
 
-int hashenc_residual(const hashenc* h, const hashenc_mlp* mlp, int64_t n, const float* x,
-                     const float* params, const float* mlp_params, float* residual, float* loss,
-                     float* grad_params, float* grad_mlp, void* workspace, size_t workspace_bytes,
-                     hashenc_stream_t stream) {
-  (void)h; (void)mlp; (void)n; (void)x; (void)params; (void)mlp_params; (void)residual;
-  (void)loss; (void)grad_params; (void)grad_mlp; (void)workspace; (void)workspace_bytes;
-  (void)stream;
-  return HASHENC_EUNSUPPORTED;
+// Make this wavefront's LDS writes visible to its other lanes before they read them.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-}  // extern "C"
+// INP: the encoder width rounded up to 16, 32 or 64 (the first layer's fan-in).
+template <int D, int DEPTH, int INP>
+__global__ __launch_bounds__(kW * kWavesPerBlock) void siren_residual_kernel(
+    const MlpArgs a, int64_t n, double inv_n_total, const float* __restrict__ x,
+    const float* __restrict__ enc_g, const float* __restrict__ enc_d, const float* __restrict__ enc_l,
+    const float* __restrict__ mlp, float* __restrict__ up_g, float* __restrict__ up_d,
+    float* __restrict__ up_l, float* __restrict__ residual, float* __restrict__ partial) {
+  constexpr int R = D + 2;  // rows: value, D gradients, Laplacian
+  __shared__ float Wt[DEPTH][kW][kW];   // Wt[k][j][o] = W_k[o][j]  (forward: lane o)
+  __shared__ float Wr[DEPTH][kW][kW];   // Wr[k][o][j] = W_k[o][j]  (reverse: lane j)
+  __shared__ float bias[DEPTH][kW];
+  __shared__ float wout[kW];
+  __shared__ float act[kWavesPerBlock][DEPTH][R][kW];  // inputs of each hidden layer
+  __shared__ float zb[kWavesPerBlock][R][kW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kW - 1);
+  const int wv = tid / kW;
+  const int LF = a.in;
+  const float w = a.omega;
+
+  // weights into LDS, zero-padded to kW x kW
+  for (int k = 0; k < DEPTH; ++k) {
+    const int fi = k == 0 ? a.in : a.H;
+    const float* Wk = mlp + a.woff[k];
+    for (int e = tid; e < kW * kW; e += kW * kWavesPerBlock) {
+      const int o = e / kW, j = e % kW;
+      const float v = (o < a.H && j < fi) ? Wk[o * fi + j] : 0.0f;
+      Wr[k][o][j] = v;
+      Wt[k][j][o] = v;
+    }
+    for (int o = tid; o < kW; o += kW * kWavesPerBlock) bias[k][o] = o < a.H ? mlp[a.boff[k] + o] : 0.0f;
+  }
+  for (int o = tid; o < kW; o += kW * kWavesPerBlock) wout[o] = o < a.H ? mlp[a.woff[DEPTH] + o] : 0.0f;
+  __syncthreads();
+
+  // lane o: row o of dL/dW_k (layer 0 has INP columns, the others kW)
+  float gW0[INP];
+  float gW[DEPTH > 1 ? DEPTH - 1 : 1][kW];
+  float gb[DEPTH];
+  float gWo = 0.0f, sq = 0.0f;
+#pragma unroll
+  for (int j = 0; j < INP; ++j) gW0[j] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k) gb[k] = 0.0f;
+#pragma unroll
+  for (int k = 0; k + 1 < DEPTH; ++k)
+#pragma unroll
+    for (int j = 0; j < kW; ++j) gW[k][j] = 0.0f;
+
+  const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + wv;
+  const int64_t n_waves = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t p = wave_id; p < n; p += n_waves) {
+    // encoder outputs of point p -> act[wv][0]
+    {
+      const bool on = lane < LF;
+      act[wv][0][0][lane] = on ? enc_g[p * LF + lane] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) act[wv][0][1 + i][lane] = on ? enc_d[(p * D + i) * LF + lane] : 0.0f;
+      act[wv][0][R - 1][lane] = on ? enc_l[p * LF + lane] : 0.0f;
+    }
+    wave_lds_sync();
+
+    // forward mode through the hidden layers (lane = neuron o)
+    float ts[DEPTH], tc[DEPTH], tz[DEPTH][R];  // tape: sin, cos, Z rows
+    float a_lap_top = 0.0f;
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) {
+      const int fi = k == 0 ? INP : kW;
+      float z[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) z[r] = r == 0 ? bias[k][lane] : 0.0f;
+      for (int j = 0; j < fi; ++j) {
+        const float wj = Wt[k][j][lane];
+#pragma unroll
+        for (int r = 0; r < R; ++r) z[r] = fmaf(wj, act[wv][k][r][j], z[r]);
+      }
+      float s, c;
+      sincosf(w * z[0], &s, &c);
+      ts[k] = s;
+      tc[k] = c;
+      float sumsq = 0.0f;
+#pragma unroll
+      for (int i = 1; i <= D; ++i) sumsq = fmaf(z[i], z[i], sumsq);
+#pragma unroll
+      for (int r = 0; r < R; ++r) tz[k][r] = z[r];
+      const float wc = w * c;
+      const float a_lap = fmaf(-w * w * s, sumsq, wc * z[R - 1]);
+      if (k + 1 < DEPTH) {
+        act[wv][k + 1][0][lane] = s;
+#pragma unroll
+        for (int i = 1; i <= D; ++i) act[wv][k + 1][i][lane] = wc * z[i];
+        act[wv][k + 1][R - 1][lane] = a_lap;
+        wave_lds_sync();
+      } else {
+        a_lap_top = a_lap;
+      }
+    }
+    // linear output: Lap u = wout . A_lap
+    const float lap_u = wave_sum(wout[lane] * a_lap_top);
+    float src = -(float)D * 9.8696044010893586f;  // -d pi^2
+#pragma unroll
+    for (int i = 0; i < D; ++i) src *= sinpif(x[p * D + i]);
+    const float res = lap_u - src;
+    if (lane == 0) {
+      sq = fmaf(res, res, sq);
+      if (residual) residual[p] = res;
+    }
+    const float seed = (float)(2.0 * (double)res * inv_n_total);
+    gWo = fmaf(seed, a_lap_top, gWo);
+
+    // reverse sweep; the output layer seeds only the Laplacian row
+    float ab[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ab[r] = 0.0f;
+    ab[R - 1] = seed * wout[lane];
+#pragma unroll
+    for (int k = DEPTH - 1; k >= 0; --k) {
+      const float s = ts[k], c = tc[k];
+      const float wc = w * c, w2s = w * w * s;
+      float sumsq = 0.0f;
+#pragma unroll
+      for (int i = 1; i <= D; ++i) sumsq = fmaf(tz[k][i], tz[k][i], sumsq);
+      float zbar[R];
+      // d a/dz = w cos; d A_i/dz = -w^2 sin Z_i; d A_lap/dz = -w^3 cos sum Z_i^2 - w^2 sin Z_lap
+      float z0 = ab[0] * wc + ab[R - 1] * (-w * w * wc * sumsq - w2s * tz[k][R - 1]);
+#pragma unroll
+      for (int i = 1; i <= D; ++i) {
+        z0 = fmaf(ab[i], -w2s * tz[k][i], z0);
+        // d A_i/dZ_i = w cos; d A_lap/dZ_i = -2 w^2 sin Z_i
+        zbar[i] = ab[i] * wc + ab[R - 1] * (-2.0f * w2s * tz[k][i]);
+      }
+      zbar[0] = z0;
+      zbar[R - 1] = ab[R - 1] * wc;  // d A_lap/dZ_lap = w cos
+      gb[k] += zbar[0];
+      if (k == 0) {
+#pragma unroll
+        for (int j = 0; j < INP; ++j) {
+          float acc = gW0[j];
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc = fmaf(zbar[r], act[wv][0][r][j], acc);
+          gW0[j] = acc;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kW; ++j) {
+          float acc = gW[k - 1][j];
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc = fmaf(zbar[r], act[wv][k][r][j], acc);
+          gW[k - 1][j] = acc;
+        }
+      }
+      // input adjoint: lane j <- sum_o W_k[o][j] zbar[o]
+#pragma unroll
+      for (int r = 0; r < R; ++r) zb[wv][r][lane] = zbar[r];
+      wave_lds_sync();
+#pragma unroll
+      for (int r = 0; r < R; ++r) ab[r] = 0.0f;
+      for (int o = 0; o < a.H; ++o) {
+        const float wo = Wr[k][o][lane];
+#pragma unroll
+        for (int r = 0; r < R; ++r) ab[r] = fmaf(wo, zb[wv][r][o], ab[r]);
+      }
+      wave_lds_sync();  // zb is rewritten by the next layer
+    }
+    if (lane < LF) {
+      up_g[p * LF + lane] = ab[0];
+#pragma unroll
+      for (int i = 0; i < D; ++i) up_d[(p * D + i) * LF + lane] = ab[1 + i];
+      up_l[p * LF + lane] = ab[R - 1];
+    }
+  }
+
+  // this wave's partial MLP gradient and sum of r^2
+  float* part = partial + wave_id * (a.n_mlp + 1);
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k) {
+    const int fi = k == 0 ? a.in : a.H;
+    if (lane < a.H) {
+      if (k == 0) {
+#pragma unroll
+        for (int j = 0; j < INP; ++j)
+          if (j < fi) part[a.woff[0] + (int64_t)lane * fi + j] = gW0[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kW; ++j)
+          if (j < fi) part[a.woff[k] + (int64_t)lane * fi + j] = gW[k - 1][j];
+      }
+      part[a.boff[k] + lane] = gb[k];
+    }
+  }
+  if (lane < a.H) part[a.woff[DEPTH] + lane] = gWo;
+  if (lane == 0) {
+    part[a.boff[DEPTH]] = 0.0f;  // the output bias does not enter Lap u
+    part[a.n_mlp] = sq;
+  }
+}
+
+// grad_mlp[c] += sum_w partial[w][c] for c < n_mlp; loss (+)= sum_w partial[w][n_mlp] / n.
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ partial,
+                                                              int64_t n_waves, int64_t n_mlp,
+                                                              double inv_n_total, int first,
+                                                              float* __restrict__ grad_mlp,
+                                                              float* __restrict__ loss) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c > n_mlp) return;
+  double s = 0.0;
+  for (int64_t wv = 0; wv < n_waves; ++wv) s += (double)partial[wv * (n_mlp + 1) + c];
+  if (c < n_mlp) {
+    if (grad_mlp) grad_mlp[c] += (float)s;
+  } else {
+    const float v = (float)(s * inv_n_total);
+    *loss = first ? v : *loss + v;
+  }
+}
+
+constexpr int64_t kChunk = int64_t(1) << 20;  // points per pass over the workspace
+constexpr int kSirenBlocks = 1024;
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct WorkspaceLayout {
+  size_t enc_g, enc_d, enc_l, up_g, up_d, up_l, partial, total;
+};
+
+WorkspaceLayout workspace_layout(int d, int LF, int64_t n, int64_t n_mlp) {
+  const int64_t c = n < kChunk ? n : kChunk;
+  WorkspaceLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  w.enc_g = take(sizeof(float) * c * LF);
+  w.enc_d = take(sizeof(float) * c * d * LF);
+  w.enc_l = take(sizeof(float) * c * LF);
+  w.up_g = take(sizeof(float) * c * LF);
+  w.up_d = take(sizeof(float) * c * d * LF);
+  w.up_l = take(sizeof(float) * c * LF);
+  w.partial = take(sizeof(float) * (size_t)kSirenBlocks * kWavesPerBlock * (n_mlp + 1));
+  w.total = off;
+  return w;
+}
+
+template <int D, int DEPTH, int INP>
+hipError_t launch_siren(const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* eg,
+                        const float* ed, const float* el, const float* mlp, float* ug, float* ud,
+                        float* ul, float* residual, float* partial, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL((siren_residual_kernel<D, DEPTH, INP>), dim3(blocks), dim3(kW * kWavesPerBlock), 0, s,
+                     a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial);
+  return hipGetLastError();
+}
+
+template <int D, int DEPTH>
+hipError_t dispatch_in(int in, const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* eg,
+                       const float* ed, const float* el, const float* mlp, float* ug, float* ud, float* ul,
+                       float* residual, float* partial, int blocks, hipStream_t s) {
+  if (in <= 16) return launch_siren<D, DEPTH, 16>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+  if (in <= 32) return launch_siren<D, DEPTH, 32>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+  return launch_siren<D, DEPTH, 64>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+}
+
+template <int D>
+hipError_t dispatch_depth(int depth, int in, const MlpArgs& a, int64_t n, double inv_n, const float* x,
+                          const float* eg, const float* ed, const float* el, const float* mlp, float* ug,
+                          float* ud, float* ul, float* residual, float* partial, int blocks, hipStream_t s) {
+  switch (depth) {
+    case 1: return dispatch_in<D, 1>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+    case 2: return dispatch_in<D, 2>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+    case 3: return dispatch_in<D, 3>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+    default: return dispatch_in<D, 4>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+  }
+}
+
+hipError_t dispatch_siren(int d, int depth, int in, const MlpArgs& a, int64_t n, double inv_n,
+                          const float* x, const float* eg, const float* ed, const float* el,
+                          const float* mlp, float* ug, float* ud, float* ul, float* residual,
+                          float* partial, int blocks, hipStream_t s) {
+  if (d == 2) return dispatch_depth<2>(depth, in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+  return dispatch_depth<3>(depth, in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+}
+
+}  // namespace
+
+int64_t mlp_param_count(int in, int H, int depth) {
+  int64_t n = 0;
+  for (int k = 0; k <= depth; ++k) {
+    const int64_t fi = k == 0 ? in : H;
+    const int64_t fo = k == depth ? 1 : H;
+    n += fi * fo + fo;
+  }
+  return n;
+}
+
+size_t residual_workspace_bytes(int d, int LF, int64_t n, int in, int H, int depth) {
+  return workspace_layout(d, LF, n, mlp_param_count(in, H, depth)).total;
+}
+
+hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, const float* params,
+                        int in, int H, int depth, float omega, const float* mlp, float* residual,
+                        float* loss, float* grad_params, float* grad_mlp, void* workspace,
+                        hipStream_t s) {
+  const int LF = g.L * F;
+  MlpArgs a;
+  a.in = in;
+  a.H = H;
+  a.depth = depth;
+  a.omega = omega;
+  a.n_mlp = mlp_param_count(in, H, depth);
+  int64_t off = 0;
+  for (int k = 0; k <= kMaxDepth; ++k) { a.woff[k] = 0; a.boff[k] = 0; }
+  for (int k = 0; k <= depth; ++k) {
+    const int64_t fi = k == 0 ? in : H;
+    const int64_t fo = k == depth ? 1 : H;
+    a.woff[k] = off; off += fi * fo;
+    a.boff[k] = off; off += fo;
+  }
+  const WorkspaceLayout wl = workspace_layout(d, LF, n, a.n_mlp);
+  char* ws = static_cast<char*>(workspace);
+  float* eg = reinterpret_cast<float*>(ws + wl.enc_g);
+  float* ed = reinterpret_cast<float*>(ws + wl.enc_d);
+  float* el = reinterpret_cast<float*>(ws + wl.enc_l);
+  float* ug = reinterpret_cast<float*>(ws + wl.up_g);
+  float* ud = reinterpret_cast<float*>(ws + wl.up_d);
+  float* ul = reinterpret_cast<float*>(ws + wl.up_l);
+  float* partial = reinterpret_cast<float*>(ws + wl.partial);
+  const double inv_n = 1.0 / (double)n;
+  for (int64_t p0 = 0; p0 < n; p0 += kChunk) {
+    const int64_t c = (n - p0) < kChunk ? (n - p0) : kChunk;
+    const float* xc = x + p0 * d;
+    hipError_t e = launch_hermite_forward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, params, eg, ed, el, s);
+    if (e != hipSuccess) return e;
+    int blocks = (int)((c + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (blocks > kSirenBlocks) blocks = kSirenBlocks;
+    float* rc = residual ? residual + p0 : nullptr;
+    e = dispatch_siren(d, depth, in, a, c, inv_n, xc, eg, ed, el, mlp, ug, ud, ul, rc, partial, blocks, s);
+    if (e != hipSuccess) return e;
+    const int64_t n_waves = (int64_t)blocks * kWavesPerBlock;
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((a.n_mlp + 1 + 255) / 256)), dim3(256), 0, s,
+                       partial, n_waves, a.n_mlp, inv_n, p0 == 0 ? 1 : 0, grad_mlp, loss);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (grad_params) {
+      e = launch_hermite_backward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, ug, ud, ul, grad_params, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace hg

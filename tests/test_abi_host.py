@@ -141,3 +141,31 @@ def test_binding_rejects_host_tensors():
     h = api.hashenc_create({"d": 2, "L": 1, "F": 2, "kind": "dlinear", "T": [64], "n_min": 4, "n_max": 4})
     with pytest.raises(ValueError):
         api.hashenc_forward(h, torch.zeros(4, 2), torch.zeros(50), torch.zeros(4, 2))
+
+
+def test_residual_validation_on_host():
+    lib = _lib.load()
+    herm = api.hashenc_create({"d": 3, "L": 16, "F": 2, "kind": "hermite", "T": [1 << 19] * 4,
+                               "n_min": 16, "n_max": 1024, "d2_mode": "laplacian"})
+    lin = api.hashenc_create({"d": 3, "L": 2, "F": 2, "kind": "dlinear", "T": [1 << 10], "n_min": 4, "n_max": 8})
+    assert api.hashenc_residual_workspace_size(herm, api.Mlp(32, 64, 2, 30.0), 1 << 21) > 0
+    b = ctypes.c_size_t()
+    for mlp, code in [(api.Mlp(32, 64, 2, 30.0), _lib.HASHENC_EUNSUPPORTED)]:
+        m = mlp.as_c()
+        assert lib.hashenc_residual_workspace_size(lin, ctypes.byref(m), 8, ctypes.byref(b)) == code
+    for mlp, code in [(api.Mlp(16, 64, 2, 30.0), _lib.HASHENC_EINVAL),
+                      (api.Mlp(32, 65, 2, 30.0), _lib.HASHENC_EUNSUPPORTED),
+                      (api.Mlp(32, 64, 5, 30.0), _lib.HASHENC_EUNSUPPORTED),
+                      (api.Mlp(32, 64, 0, 30.0), _lib.HASHENC_EUNSUPPORTED),
+                      (api.Mlp(32, 64, 2, float("nan")), _lib.HASHENC_EINVAL)]:
+        m = mlp.as_c()
+        assert lib.hashenc_residual_workspace_size(herm, ctypes.byref(m), 8, ctypes.byref(b)) == code
+    m = api.Mlp(32, 64, 2, 30.0).as_c()
+    P = ctypes.c_void_p
+    a = P(0x10000)
+    need = api.hashenc_residual_workspace_size(herm, api.Mlp(32, 64, 2, 30.0), 8)
+    # too small a workspace, n = 0, a misaligned workspace: all rejected before any launch
+    assert lib.hashenc_residual(herm, ctypes.byref(m), 8, a, a, a, None, a, None, None, a, need - 1, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_residual(herm, ctypes.byref(m), 0, a, a, a, None, a, None, None, a, need, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_residual(herm, ctypes.byref(m), 8, a, a, a, None, a, None, None, P(0x10010), need, None) == _lib.HASHENC_EALIGN
+    assert lib.hashenc_residual(herm, ctypes.byref(m), 8, a, a, a, None, None, None, None, a, need, None) == _lib.HASHENC_EINVAL
