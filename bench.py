@@ -50,13 +50,39 @@ def algorithmic_bytes_per_point(spec: dict) -> dict:
             "backward": x_bytes + 4 * out_floats + 8 * coeffs}
 
 
+def copy_calibration(args, torch, api) -> int:
+    """Plain streaming copy of --copy-bytes bytes: achievable bandwidth, and a launch of known
+    traffic (read + write = 2 * bytes) against which memory counters are scaled."""
+    n = args.copy_bytes // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty(n, device="cuda:0")
+    for _ in range(args.warmup):
+        api.hashenc_diag_copy(src, dst)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        api.hashenc_diag_copy(src, dst)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"copy_bytes": 4 * n, "ms": round(ms, 4), "read_plus_write_GBps": round(8 * n / ms / 1e6, 1)}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--backward", choices=["binned", "atomic"], default="binned",
+                    help="binned: hashenc_backward_ws (workspace); atomic: hashenc_backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the benchmark, run the plain copy kernel over this many bytes "
+                         "(bandwidth and memory-counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     args = ap.parse_args()
@@ -69,6 +95,9 @@ def main() -> int:
 
     from multiresolution_hash_grid_multires_amd import api
     from multiresolution_hash_grid_multires_amd import inputs as I
+
+    if args.copy_bytes:
+        return copy_calibration(args, torch, api)
 
     W = I.WORKLOADS[args.workload]
     if "mlp" in W:
@@ -90,6 +119,7 @@ def main() -> int:
     ups += [None] * (3 - len(ups))
     grad = torch.zeros(enc.n_params, device=dev)
     stream = torch.cuda.current_stream()
+    workspace = enc.workspace(n) if args.backward == "binned" else None
 
     def step(ev=None):
         grad.zero_()
@@ -98,7 +128,10 @@ def main() -> int:
         api.hashenc_forward(enc.handle, x, params, outs["gamma"], outs.get("dgamma"), outs.get("d2gamma"))
         if ev is not None:
             ev[1].record(stream)
-        api.hashenc_backward(enc.handle, x, ups[0], ups[1], ups[2], grad)
+        if workspace is not None:
+            api.hashenc_backward_ws(enc.handle, x, ups[0], ups[1], ups[2], grad, workspace)
+        else:
+            api.hashenc_backward(enc.handle, x, ups[0], ups[1], ups[2], grad)
         if ev is not None:
             ev[2].record(stream)
 
@@ -170,7 +203,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "n_points": n, "d": spec["d"], "L": spec["L"],
-                   "F": spec["F"], "T": spec["T"], "kind": spec["kind"]},
+                   "F": spec["F"], "T": spec["T"], "kind": spec["kind"], "backward": args.backward},
         "hbm_roofline_pct_step": round(100.0 * value * step_alg / (HBM_PEAK_GBPS * 1e9), 2),
         "kernels": {k: {"ms": round(v["ms"], 4), "GBps": round(v["GBps"], 1)} for k, v in kern.items()},
         "roofline": roofline,

@@ -124,6 +124,20 @@ HASHENC_API int hashenc_backward(const hashenc* h, int64_t n, const float* x, co
                      const float* g_dgamma, const float* g_d2gamma, float* grad_params,
                      hashenc_stream_t stream);
 
+/* Device workspace (bytes) that hashenc_backward_ws needs for n points (0 when this handle's
+ * configuration does not use one; hashenc_backward_ws then takes the atomic path). */
+HASHENC_API int hashenc_backward_workspace_size(const hashenc* h, int64_t n, size_t* bytes);
+
+/* Same result as hashenc_backward (grad_params += dL/dtheta), computed without global
+ * atomics on the hot part: the contributions are counted and sorted into bins of rows
+ * small enough for the LDS of one workgroup, then each bin is accumulated on chip and added
+ * to grad_params.  workspace: >= hashenc_backward_workspace_size bytes, 256-byte aligned,
+ * owned by the caller, contents irrelevant on entry; calls sharing a workspace must not
+ * overlap.  Points are processed in chunks of 2^20. */
+HASHENC_API int hashenc_backward_ws(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
+                                    const float* g_dgamma, const float* g_d2gamma, float* grad_params,
+                                    void* workspace, size_t workspace_bytes, hashenc_stream_t stream);
+
 /* SIREN decoder of the fused PINN residual (Hermite-NGP key design 2; loss section):
  * `depth` hidden layers of width `hidden`, activation sin(omega (W v + b)), then a linear
  * output of width 1.  `in` must equal L*F. */

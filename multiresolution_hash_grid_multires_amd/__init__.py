@@ -7,6 +7,8 @@ from .api import (  # noqa: F401
     HashGridEncoding,
     Mlp,
     hashenc_backward,
+    hashenc_backward_workspace_size,
+    hashenc_backward_ws,
     hashenc_create,
     hashenc_debug_indices,
     hashenc_destroy,

@@ -63,6 +63,8 @@ SIGNATURES = [
      [P, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
     ("hashenc_forward", ctypes.c_int, [P, I64, P, P, P, P, P, P]),
     ("hashenc_backward", ctypes.c_int, [P, I64, P, P, P, P, P, P]),
+    ("hashenc_backward_workspace_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)]),
+    ("hashenc_backward_ws", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),
     ("hashenc_residual_workspace_size", ctypes.c_int,
      [P, ctypes.POINTER(HashencMlp), I64, ctypes.POINTER(ctypes.c_size_t)]),
     ("hashenc_residual", ctypes.c_int,

@@ -123,6 +123,24 @@ def hashenc_backward(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_
                                   _dev_ptr(grad_params, "grad_params"), _stream(stream)))
 
 
+def hashenc_backward_workspace_size(h: Handle, n: int) -> int:
+    b = ctypes.c_size_t()
+    check(load().hashenc_backward_workspace_size(h, n, ctypes.byref(b)))
+    return int(b.value)
+
+
+def hashenc_backward_ws(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_d2gamma=None,
+                        grad_params=None, workspace: torch.Tensor | None = None, stream=None) -> None:
+    n = x.shape[0]
+    ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None and workspace.device.type != "cuda":
+        raise ValueError("workspace must be a device tensor")
+    check(load().hashenc_backward_ws(h, n, _dev_ptr(x, "x"), _dev_ptr(g_gamma, "g_gamma"),
+                                     _dev_ptr(g_dgamma, "g_dgamma"), _dev_ptr(g_d2gamma, "g_d2gamma"),
+                                     _dev_ptr(grad_params, "grad_params"), ws_ptr, ws_bytes, _stream(stream)))
+
+
 @dataclass
 class Mlp:
     n_in: int
@@ -191,5 +209,20 @@ class HashGridEncoding:
 
     def backward(self, x: torch.Tensor, grad_params: torch.Tensor, g_gamma=None, g_dgamma=None,
                  g_d2gamma=None, stream=None) -> torch.Tensor:
+        """Atomic scatter-add backward (no workspace)."""
         hashenc_backward(self.handle, x, g_gamma, g_dgamma, g_d2gamma, grad_params, stream)
+        return grad_params
+
+    def workspace(self, n: int) -> torch.Tensor | None:
+        """A device workspace for backward_ws on n points (None when none is needed)."""
+        b = hashenc_backward_workspace_size(self.handle, n)
+        return torch.empty(b, dtype=torch.uint8, device="cuda") if b else None
+
+    def backward_ws(self, x: torch.Tensor, grad_params: torch.Tensor, g_gamma=None, g_dgamma=None,
+                    g_d2gamma=None, workspace=None, stream=None) -> torch.Tensor:
+        """Binned backward (no global atomics on the hot part); allocates a workspace when
+        none is given."""
+        if workspace is None:
+            workspace = self.workspace(x.shape[0])
+        hashenc_backward_ws(self.handle, x, g_gamma, g_dgamma, g_d2gamma, grad_params, workspace, stream)
         return grad_params

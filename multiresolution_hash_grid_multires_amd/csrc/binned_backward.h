@@ -1,0 +1,123 @@
+// Binned backward: plan, workspace layout and device helpers shared by the generic stages
+// (scan, plan, reduce) and the interpolant-specific count / scatter kernels.
+#pragma once
+
+#include "hashenc_internal.h"
+
+namespace hg {
+
+constexpr int kMaxSeg = kMaxTables * kMaxLevels;  // segment s = table k * L + level l
+constexpr int kBinLdsValues = 8192;               // 64 KB fp64 LDS accumulator per work item
+constexpr int kBinTilePoints = 1024;              // points per count / scatter workgroup (max)
+constexpr int kBinThreads = 256;
+constexpr int kBinItemEntries = 1 << 18;          // entries per reduce work item (at most)
+constexpr int kReduceThreads = 512;
+constexpr int kBinReduceBlocks = 512;             // persistent reduce workgroups (2 per CU)
+constexpr int64_t kStageBytes = 116 * 1024;       // LDS staging of the d-linear scatter
+constexpr int kScatterThreads = 512;              // d-linear scatter workgroup
+constexpr size_t kMaxScatterLds = 150 * 1024;     // of the 160 KB LDS of a gfx950 CU
+
+// Small, by-value plan: bins are (segment, chunk of 2^cshift rows) in segment order.
+struct BinPlan {
+  int32_t d, L, ntab, nseg, nbins;
+  int32_t max_seg_bins;         // most bins of any one segment
+  int32_t width[kMaxTables];    // floats per row of table k
+  int32_t cshift[kMaxTables];   // log2 rows per chunk of table k
+  int32_t seg_bin0[kMaxSeg + 1];
+};
+
+struct WorkItem {
+  int32_t bin, seg, begin, end, split;
+};
+
+// Device-side results of the plan stage.
+struct BinState {
+  int32_t n_items;
+  int32_t next_item;
+  int32_t seg_ebase[kMaxSeg];   // first entry of segment s
+  int64_t seg_vbase[kMaxSeg];   // first value float of segment s
+};
+
+struct BinWorkspace {
+  int32_t tile;   // points per count / scatter workgroup
+  int32_t nblk;
+  int64_t max_items;
+  size_t counts, totals, state, bin_start, items, rows, vals, total;
+};
+
+__host__ __device__ inline int64_t seg_rows(const Grid& g, int d, int k, int l) {
+  if ((g.dense[k] >> l) & 1u) {
+    int64_t r = 1;
+    for (int i = 0; i < d; ++i) r *= (int64_t)g.N[l] + 1;
+    return r;
+  }
+  return (int64_t)g.T[k];
+}
+
+// Add 1 to hist[bin] for every active lane; lanes of the wavefront that share a bin are
+// combined first (one LDS atomic per distinct bin).  With RTN the lane's own slot is
+// returned: the counter's old value plus its rank among the lanes sharing the bin.  Used
+// where a level has few bins, so that a wavefront's lanes would otherwise serialise on one
+// LDS address.
+template <bool RTN>
+__device__ __forceinline__ int32_t wave_aggregated_add(int32_t* hist, int32_t bin) {
+  const int lane = (int)__lane_id();
+  int32_t result = 0;
+  uint64_t todo = __ballot(1);
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int32_t b = __shfl(bin, leader);
+    const uint64_t same = __ballot(bin == b) & todo;
+    int32_t base = 0;
+    if (lane == leader) base = atomicAdd(&hist[b], (int32_t)__popcll(same));
+    if constexpr (RTN) {
+      base = __shfl(base, leader);
+      if (bin == b) result = base + (int32_t)__popcll(same & ((uint64_t(1) << lane) - 1));
+    }
+    todo &= ~same;
+  }
+  return result;
+}
+
+// Levels with at most this many bins use the wavefront-aggregated counters.
+constexpr int kFewBins = 16;
+
+// Bin of a row of segment (k, l) and its row inside the chunk.
+__device__ __forceinline__ void bin_of(const BinPlan& bp, int k, int l, uint32_t row, int32_t& bin,
+                                       uint32_t& local) {
+  const int cs = bp.cshift[k];
+  bin = bp.seg_bin0[k * bp.L + l] + (int32_t)(row >> cs);
+  local = row & ((1u << cs) - 1u);
+}
+
+int bin_cshift_for_width(int W);
+void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp);
+int bin_tile_points(const BinPlan& bp, int F, bool hermite);
+BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64_t entries_per_point,
+                                  int64_t floats_per_point, int tile);
+// Stages 2-3 (after the interpolant's count kernel) and stage 5 (after its scatter kernel).
+hipError_t run_bin_middle(const BinPlan& bp, const BinWorkspace& w, char* ws, hipStream_t s);
+hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws,
+                          float* grad, hipStream_t s);
+
+// Interpolant-specific count / scatter launches (d-linear and Hermite kernel files).
+hipError_t launch_dlinear_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws,
+                              int d, int F, bool scatter, int64_t n, const float* x,
+                              const float* g_gamma, hipStream_t s);
+hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws,
+                              int d, int F, int d2_mode, bool scatter, int64_t n, const float* x,
+                              const float* g_gamma, const float* g_dgamma, const float* g_d2gamma,
+                              hipStream_t s);
+
+constexpr int32_t kMaxBins = 16384;
+
+// Whether this configuration's bins and staging fit the LDS budgets of the binned path.
+bool binned_fits(const Grid& g, int d, int F, bool hermite);
+
+// Whole binned backward over n points, in chunks that fit the workspace.
+size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite, int64_t n);
+hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2_mode, int64_t n,
+                               const float* x, const float* g_gamma, const float* g_dgamma,
+                               const float* g_d2gamma, float* grad, void* workspace, hipStream_t s);
+
+}  // namespace hg

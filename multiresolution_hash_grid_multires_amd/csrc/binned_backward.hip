@@ -1,0 +1,369 @@
+// Binned backward: the scatter-add dL/dtheta += sum over (point, level, corner) without
+// global atomics on the hot part, gfx950.
+//
+// Why: fp32 global atomics on this part run at ~21 G requests/s whatever the footprint, so
+// a backward issuing one request per corner row is bounded far below HBM bandwidth.  Here
+// the contributions are instead routed to the workgroup that owns their rows:
+//   1. count   per point tile, histogram of contributions over bins (table, level, chunk
+//              of rows small enough to accumulate in LDS)
+//   2. scan    per bin, exclusive prefix over point tiles (and the bin totals)
+//   3. plan    exclusive scan over bins, per-segment bases, work items (bin, entry range)
+//   4. scatter recompute the contributions and write compact entries (local row, values)
+//              to their bin's range
+//   5. reduce  one workgroup per work item accumulates its entries into an LDS copy of the
+//              chunk and adds it to the gradient (plain read-modify-write when the bin is a
+//              single item, atomics only when a large bin was split across items)
+// Steps 1 and 4 are interpolant-specific (d-linear, Hermite kernel files); 2, 3 and 5 live
+// here.  Within one call the chunks of points run back to back on the stream.
+#include "binned_backward.h"
+#include "vec_io.h"
+
+namespace hg {
+
+namespace {
+
+constexpr int64_t kBinChunkPoints = int64_t(1) << 20;
+
+__global__ __launch_bounds__(256) void bin_scan_kernel(int32_t* __restrict__ counts, int32_t nblk,
+                                                       int32_t* __restrict__ totals) {
+  // counts[bin][0..nblk) -> exclusive prefix in place; totals[bin] = sum.  nblk <= 256 * 16.
+  __shared__ int32_t part[256];
+  const int bin = blockIdx.x;
+  int32_t* c = counts + (int64_t)bin * nblk;
+  const int per = (nblk + 255) / 256;
+  const int b0 = threadIdx.x * per;
+  int32_t local[16];
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int b = b0 + i;
+    local[i] = (i < per && b < nblk) ? c[b] : 0;
+    s += local[i];
+  }
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int32_t run = part[threadIdx.x] - s;  // exclusive
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int b = b0 + i;
+    if (i < per && b < nblk) c[b] = run;
+    run += local[i];
+  }
+  if (threadIdx.x == 255) totals[bin] = part[255];
+}
+
+__global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const int32_t* __restrict__ totals,
+                                                        int32_t* __restrict__ bin_start,
+                                                        WorkItem* __restrict__ items,
+                                                        BinState* __restrict__ st, int32_t emax) {
+  // One workgroup: bin_start = exclusive scan of totals; work items; segment bases.
+  __shared__ int32_t part[1024];
+  __shared__ int32_t ipart[1024];
+  __shared__ int32_t seg0[kMaxSeg + 1];
+  const int t = threadIdx.x;
+  for (int i = t; i <= bp.nseg; i += 1024) seg0[i] = bp.seg_bin0[i];
+  const int nb = bp.nbins;
+  const int per = (nb + 1023) / 1024;
+  const int b0 = t * per;
+  int32_t s = 0, si = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < nb) {
+      const int32_t tot = totals[b];
+      s += tot;
+      si += (tot + emax - 1) / emax;
+    }
+  }
+  part[t] = s;
+  ipart[t] = si;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = t >= off ? part[t - off] : 0;
+    const int32_t vi = t >= off ? ipart[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    ipart[t] += vi;
+    __syncthreads();
+  }
+  int32_t run = part[t] - s;
+  int32_t irun = ipart[t] - si;
+  int sg = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < nb) {
+      const int32_t tot = totals[b];
+      bin_start[b] = run;
+      while (sg + 1 < bp.nseg && seg0[sg + 1] <= b) ++sg;  // segment owning bin b
+      const int32_t nit = (tot + emax - 1) / emax;
+      for (int j = 0; j < nit; ++j) {
+        WorkItem w;
+        w.bin = b;
+        w.seg = sg;
+        w.begin = run + j * emax;
+        w.end = min(run + tot, run + (j + 1) * emax);
+        w.split = nit > 1 ? 1 : 0;
+        items[irun + j] = w;
+      }
+      run += tot;
+      irun += nit;
+    }
+  }
+  if (t == 1023) {
+    bin_start[nb] = part[1023];
+    st->n_items = ipart[1023];
+    st->next_item = 0;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int64_t vb = 0;
+    for (int g = 0; g < bp.nseg; ++g) {
+      const int32_t e0 = g == 0 ? 0 : bin_start[seg0[g]];
+      const int32_t e1 = seg0[g + 1] >= nb ? part[1023] : bin_start[seg0[g + 1]];
+      st->seg_ebase[g] = e0;
+      st->seg_vbase[g] = vb;
+      vb += (int64_t)(e1 - e0) * bp.width[g / bp.L];
+    }
+  }
+}
+
+// Accumulate entries [begin, end) of one segment (rows of W floats) into the LDS chunk:
+// each thread keeps U entries (about 32 value registers) in flight before its LDS atomics.
+// acc holds the chunk component-major (acc[j * plane + row]) so that the W components of
+// one row fall in different LDS banks' rotation and a wavefront's random rows spread over
+// all banks.
+template <int W>
+__device__ __forceinline__ void accumulate_entries(double* __restrict__ acc, int plane,
+                                                   const uint16_t* __restrict__ rows,
+                                                   const float* __restrict__ vseg, int32_t ebase,
+                                                   int32_t begin, int32_t end) {
+  constexpr int U = W >= 32 ? 1 : 32 / W > 8 ? 8 : 32 / W;
+  const int T = blockDim.x;
+  for (int32_t e0 = begin + (int32_t)threadIdx.x; e0 < end; e0 += T * U) {
+    int r[U];
+    float val[U][W];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t e = e0 + u * T;
+      if (e < end) {
+        r[u] = __builtin_nontemporal_load(rows + e);
+        load_vec_nt<W>(vseg + (int64_t)(e - ebase) * W, val[u]);
+      } else {
+        r[u] = -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (r[u] >= 0)
+#pragma unroll
+        for (int j = 0; j < W; ++j) atomicAdd(&acc[j * plane + r[u]], (double)val[u][j]);
+  }
+}
+
+__global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g, const BinPlan bp,
+                                                                    BinState* __restrict__ st,
+                                                                    const WorkItem* __restrict__ items,
+                                                                    const uint16_t* __restrict__ rows,
+                                                                    const float* __restrict__ vals,
+                                                                    float* __restrict__ grad) {
+  // fp64 accumulator: LDS fp64 atomics run several times faster than fp32 ones on gfx950
+  // and the chunk sum is exact to far below the fp32 result precision.
+  __shared__ double acc[kBinLdsValues];
+  __shared__ int item_sh;
+  const int n_items = st->n_items;
+  for (;;) {
+    if (threadIdx.x == 0) item_sh = atomicAdd(&st->next_item, 1);
+    __syncthreads();
+    const int it = item_sh;
+    __syncthreads();
+    if (it >= n_items) break;
+    const WorkItem w = items[it];
+    const int sg = __builtin_amdgcn_readfirstlane(w.seg);
+    const int k = sg / bp.L, l = sg % bp.L;
+    const int W = bp.width[k];
+    const int cs = bp.cshift[k];
+    const int64_t chunk = __builtin_amdgcn_readfirstlane(w.bin) - bp.seg_bin0[sg];
+    const int64_t row0 = chunk << cs;
+    const int64_t rem = seg_rows(g, bp.d, k, l) - row0;
+    const int64_t nrows = rem < ((int64_t)1 << cs) ? rem : ((int64_t)1 << cs);
+    const int nfl = (int)(nrows * W);
+    for (int i = threadIdx.x; i < nfl; i += kReduceThreads) acc[i] = 0.0;
+    __syncthreads();
+    // values of entry e of segment sg start at vseg + (e - ebase) * W
+    const float* vseg = vals + st->seg_vbase[sg];
+    const int32_t eb = st->seg_ebase[sg];
+    const int plane = (int)nrows;
+    switch (W) {
+      case 1: accumulate_entries<1>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+      case 2: accumulate_entries<2>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+      case 3: accumulate_entries<3>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+      case 4: accumulate_entries<4>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+      case 6: accumulate_entries<6>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+      case 8: accumulate_entries<8>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+      case 12: accumulate_entries<12>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+      case 16: accumulate_entries<16>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+      default: accumulate_entries<24>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+    }
+    __syncthreads();
+    // flush: element i of the chunk is row i / W, component i % W
+    float* dst = grad + g.off[k][l] + row0 * W;
+    if (w.split) {
+      for (int i = threadIdx.x; i < nfl; i += kReduceThreads) {
+        const float a = (float)acc[(i % W) * plane + i / W];
+        if (a != 0.0f) atomic_add_f32(dst + i, a);
+      }
+    } else {
+      for (int i = threadIdx.x; i < nfl; i += kReduceThreads) dst[i] += (float)acc[(i % W) * plane + i / W];
+    }
+    __syncthreads();
+  }
+}
+
+int64_t entries_per_point(int d, int L, bool hermite) {
+  return (int64_t)L * (1 << d) * (hermite ? d + 1 : 1);
+}
+
+int64_t floats_per_point(const BinPlan& bp, int d) {
+  int64_t w = 0;
+  for (int k = 0; k < bp.ntab; ++k) w += bp.width[k];
+  return (int64_t)bp.L * (1 << d) * w;
+}
+
+}  // namespace
+
+int bin_cshift_for_width(int W) {
+  int c = 0;
+  while (((int64_t)2 << c) * W <= kBinLdsValues) ++c;
+  return c;  // largest c with (1 << c) * W <= kBinLdsValues
+}
+
+void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
+  bp.d = d;
+  bp.L = g.L;
+  bp.ntab = hermite ? d + 1 : 1;
+  bp.nseg = bp.ntab * g.L;
+  for (int k = 0; k < kMaxTables; ++k) { bp.width[k] = 0; bp.cshift[k] = 0; }
+  int32_t bin = 0;
+  bp.max_seg_bins = 0;
+  for (int k = 0; k < bp.ntab; ++k) {
+    const int W = hermite ? (k == 0 || k == d ? F : (d == 3 ? 3 * F : 2 * F)) : F;
+    bp.width[k] = W;
+    bp.cshift[k] = bin_cshift_for_width(W);
+    for (int l = 0; l < g.L; ++l) {
+      const int64_t rows = seg_rows(g, d, k, l);
+      bp.seg_bin0[k * g.L + l] = bin;
+      const int32_t nb = (int32_t)((rows + ((int64_t)1 << bp.cshift[k]) - 1) >> bp.cshift[k]);
+      if (nb > bp.max_seg_bins) bp.max_seg_bins = nb;
+      bin += nb;
+    }
+  }
+  bp.seg_bin0[bp.nseg] = bin;
+  bp.nbins = bin;
+}
+
+int bin_tile_points(const BinPlan& bp, int F, bool hermite) {
+  if (hermite) return kBinTilePoints;
+  // d-linear scatter stages a tile-level of entries (row, position, F values) in LDS
+  const int64_t per_point = (int64_t)(1 << bp.d) * (6 + 4 * F);
+  int tp = (int)(kStageBytes / per_point) / kScatterThreads * kScatterThreads;
+  if (tp > 2 * kScatterThreads) tp = 2 * kScatterThreads;  // at most 2 points per scatter lane
+  if (tp > kBinTilePoints) tp = kBinTilePoints;
+  if (tp < kScatterThreads) tp = kScatterThreads;
+  return tp;
+}
+
+BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64_t epp, int64_t fpp, int tile) {
+  BinWorkspace w;
+  auto al = [](size_t b) { return (b + 255) & ~size_t(255); };
+  w.tile = tile;
+  w.nblk = (int32_t)((chunk_points + tile - 1) / tile);
+  const int64_t entries = chunk_points * epp;
+  w.max_items = bp.nbins + entries / kBinItemEntries + 1;
+  size_t off = 0;
+  w.counts = off; off += al(sizeof(int32_t) * (size_t)bp.nbins * w.nblk);
+  w.totals = off; off += al(sizeof(int32_t) * (size_t)bp.nbins);
+  w.state = off; off += al(sizeof(BinState));
+  w.bin_start = off; off += al(sizeof(int32_t) * (size_t)(bp.nbins + 1));
+  w.items = off; off += al(sizeof(WorkItem) * (size_t)w.max_items);
+  w.rows = off; off += al(sizeof(uint16_t) * (size_t)entries);
+  w.vals = off; off += al(sizeof(float) * (size_t)(chunk_points * fpp));
+  w.total = off;
+  return w;
+}
+
+hipError_t run_bin_middle(const BinPlan& bp, const BinWorkspace& w, char* ws, hipStream_t s) {
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
+  int32_t* totals = reinterpret_cast<int32_t*>(ws + w.totals);
+  hipLaunchKernelGGL(bin_scan_kernel, dim3(bp.nbins), dim3(256), 0, s, counts, w.nblk, totals);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bin_plan_kernel, dim3(1), dim3(1024), 0, s, bp, totals,
+                     reinterpret_cast<int32_t*>(ws + w.bin_start), reinterpret_cast<WorkItem*>(ws + w.items),
+                     reinterpret_cast<BinState*>(ws + w.state), (int32_t)kBinItemEntries);
+  return hipGetLastError();
+}
+
+hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, float* grad,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(bin_reduce_kernel, dim3(kBinReduceBlocks), dim3(kReduceThreads), 0, s, g, bp,
+                     reinterpret_cast<BinState*>(ws + w.state), reinterpret_cast<const WorkItem*>(ws + w.items),
+                     reinterpret_cast<const uint16_t*>(ws + w.rows), reinterpret_cast<const float*>(ws + w.vals),
+                     grad);
+  return hipGetLastError();
+}
+
+bool binned_fits(const Grid& g, int d, int F, bool hermite) {
+  BinPlan bp;
+  make_bin_plan(g, d, F, hermite, bp);
+  if (bp.nbins > kMaxBins) return false;  // one LDS counter per bin in the count pass
+  if (hermite) return true;
+  const int tile = bin_tile_points(bp, F, hermite);
+  const size_t lds = sizeof(int32_t) * (2 * (size_t)bp.nbins + 2 * (size_t)bp.max_seg_bins + kScatterThreads) +
+                     (size_t)tile * (1 << d) * (sizeof(float) * F + sizeof(int32_t) + sizeof(uint16_t));
+  return lds <= kMaxScatterLds;
+}
+
+size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite, int64_t n) {
+  BinPlan bp;
+  make_bin_plan(g, d, F, hermite, bp);
+  const int64_t c = n < kBinChunkPoints ? n : kBinChunkPoints;
+  return bin_workspace_layout(bp, c, entries_per_point(d, g.L, hermite), floats_per_point(bp, d),
+                              bin_tile_points(bp, F, hermite)).total;
+}
+
+hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2_mode, int64_t n,
+                               const float* x, const float* g_gamma, const float* g_dgamma,
+                               const float* g_d2gamma, float* grad, void* workspace, hipStream_t s) {
+  BinPlan bp;
+  make_bin_plan(g, d, F, hermite, bp);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t LF = (int64_t)g.L * F;
+  for (int64_t p0 = 0; p0 < n; p0 += kBinChunkPoints) {
+    const int64_t c = (n - p0) < kBinChunkPoints ? (n - p0) : kBinChunkPoints;
+    const BinWorkspace w = bin_workspace_layout(bp, c, entries_per_point(d, g.L, hermite), floats_per_point(bp, d),
+                                                bin_tile_points(bp, F, hermite));
+    const float* xc = x + p0 * d;
+    const float* gg = g_gamma ? g_gamma + p0 * LF : nullptr;
+    const float* gd = g_dgamma ? g_dgamma + p0 * d * LF : nullptr;
+    const float* g2 = g_d2gamma ? g_d2gamma + p0 * (d2_mode == HASHENC_D2_DIAG ? d : 1) * LF : nullptr;
+    for (int pass = 0; pass < 2; ++pass) {
+      hipError_t e = hermite ? launch_hermite_bin(g, bp, w, ws, d, F, d2_mode, pass == 1, c, xc, gg, gd, g2, s)
+                             : launch_dlinear_bin(g, bp, w, ws, d, F, pass == 1, c, xc, gg, s);
+      if (e != hipSuccess) return e;
+      if (pass == 0) {
+        e = run_bin_middle(bp, w, ws, s);
+        if (e != hipSuccess) return e;
+      }
+    }
+    hipError_t e = run_bin_reduce(g, bp, w, ws, grad, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace hg

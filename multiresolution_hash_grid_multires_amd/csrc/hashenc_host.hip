@@ -9,6 +9,7 @@
 
 #include "hashenc.h"
 #include "hashenc_diag.h"
+#include "binned_backward.h"
 #include "hashenc_internal.h"
 
 using hg::Grid;
@@ -56,8 +57,9 @@ int64_t binom(int n, int k) {
   return r;
 }
 
-// Largest point count one 1-D launch covers (up to 16 lanes per point, 256-lane blocks).
-constexpr int64_t kMaxPoints = (int64_t)0x7fffffff * hg::kBlock / 16;
+// Largest point count: every 1-D launch (level-major forward with up to 32 levels, backward
+// with up to 16 lanes per point) then stays below 2^31 workgroups.
+constexpr int64_t kMaxPoints = int64_t(1) << 33;
 
 }  // namespace
 
@@ -235,6 +237,12 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
   return ok();
 }
 
+// The binned path keeps per-bin counters and staging in LDS; larger configurations take the
+// atomic path.
+static bool binned_supported(const hashenc* h) {
+  return hg::binned_fits(h->grid, h->d, h->F, h->kind == HASHENC_HERMITE);
+}
+
 static int check_mlp(const hashenc* h, const hashenc_mlp* mlp, const char* who) {
   if (!h) return fail(HASHENC_EINVAL, "%s: NULL handle", who);
   if (!mlp) return fail(HASHENC_EINVAL, "%s: NULL mlp", who);
@@ -259,7 +267,8 @@ int hashenc_residual_workspace_size(const hashenc* h, const hashenc_mlp* mlp, in
   if (rc) return rc;
   if (n < 1 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_residual_workspace_size: n out of range");
   if (!bytes) return fail(HASHENC_EINVAL, "hashenc_residual_workspace_size: NULL bytes");
-  *bytes = hg::residual_workspace_bytes(h->d, h->L * h->F, n, mlp->in, mlp->hidden, mlp->depth);
+  *bytes = hg::residual_workspace_bytes(h->grid, h->d, h->F, n, mlp->in, mlp->hidden, mlp->depth,
+                                        binned_supported(h));
   return ok();
 }
 
@@ -276,13 +285,48 @@ int hashenc_residual(const hashenc* h, const hashenc_mlp* mlp, int64_t n, const 
       !aligned16(loss) || !aligned16(grad_params) || !aligned16(grad_mlp) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(HASHENC_EALIGN, "hashenc_residual: pointers must be 16-byte aligned (workspace 256-byte)");
-  const size_t need = hg::residual_workspace_bytes(h->d, h->L * h->F, n, mlp->in, mlp->hidden, mlp->depth);
+  const size_t need = hg::residual_workspace_bytes(h->grid, h->d, h->F, n, mlp->in, mlp->hidden, mlp->depth,
+                                                   binned_supported(h));
   if (workspace_bytes < need)
     return fail(HASHENC_EINVAL, "hashenc_residual: workspace of %zu bytes < %zu needed", workspace_bytes, need);
   hipError_t e = hg::run_residual(h->grid, h->d, h->F, n, x, params, mlp->in, mlp->hidden, mlp->depth,
                                   mlp->omega, mlp_params, residual, loss, grad_params, grad_mlp,
-                                  workspace, stream);
+                                  workspace, binned_supported(h), stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_residual launch");
+  return ok();
+}
+
+int hashenc_backward_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_backward_workspace_size: NULL handle");
+  if (!bytes) return fail(HASHENC_EINVAL, "hashenc_backward_workspace_size: NULL bytes");
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_backward_workspace_size: n out of range");
+  *bytes = (n == 0 || !binned_supported(h))
+               ? 0
+               : hg::binned_backward_workspace_bytes(h->grid, h->d, h->F, h->kind == HASHENC_HERMITE, n);
+  return ok();
+}
+
+int hashenc_backward_ws(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
+                        const float* g_dgamma, const float* g_d2gamma, float* grad_params,
+                        void* workspace, size_t workspace_bytes, hashenc_stream_t stream) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_backward_ws: NULL handle");
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_backward_ws: n = %lld out of range", (long long)n);
+  if (h->kind == HASHENC_DLINEAR && (g_dgamma || g_d2gamma))
+    return fail(HASHENC_EUNSUPPORTED, "hashenc_backward_ws: derivative upstream needs the Hermite kind");
+  if (n == 0 || (!g_gamma && !g_dgamma && !g_d2gamma)) return ok();
+  if (!binned_supported(h))
+    return hashenc_backward(h, n, x, g_gamma, g_dgamma, g_d2gamma, grad_params, stream);
+  if (!x || !grad_params || !workspace)
+    return fail(HASHENC_EINVAL, "hashenc_backward_ws: x, grad_params and workspace must not be NULL");
+  if (!aligned16(x) || !aligned16(grad_params) || !aligned16(g_gamma) || !aligned16(g_dgamma) ||
+      !aligned16(g_d2gamma) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(HASHENC_EALIGN, "hashenc_backward_ws: pointers must be 16-byte aligned (workspace 256-byte)");
+  const size_t need = hg::binned_backward_workspace_bytes(h->grid, h->d, h->F, h->kind == HASHENC_HERMITE, n);
+  if (workspace_bytes < need)
+    return fail(HASHENC_EINVAL, "hashenc_backward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  hipError_t e = hg::run_binned_backward(h->grid, h->d, h->F, h->kind == HASHENC_HERMITE, h->d2_mode, n, x,
+                                         g_gamma, g_dgamma, g_d2gamma, grad_params, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_backward_ws launch");
   return ok();
 }
 

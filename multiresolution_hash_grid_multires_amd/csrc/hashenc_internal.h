@@ -139,10 +139,11 @@ hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t s);
 
 // Fused PINN residual (Hermite handle): workspace size and the full step.
 int64_t mlp_param_count(int in, int H, int depth);
-size_t residual_workspace_bytes(int d, int LF, int64_t n, int in, int H, int depth);
+size_t residual_workspace_bytes(const Grid& g, int d, int F, int64_t n, int in, int H, int depth,
+                                bool binned);
 hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, const float* params,
                         int in, int H, int depth, float omega, const float* mlp, float* residual,
                         float* loss, float* grad_params, float* grad_mlp, void* workspace,
-                        hipStream_t s);
+                        bool binned, hipStream_t s);
 
 }  // namespace hg

@@ -16,6 +16,7 @@
 // Dx^alpha_i scaling and the N_l chain-rule factors, so no per-term power or product chain
 // is evaluated.  Corners are visited in x-adjacent pairs (the axis-0 contraction needs
 // exactly one pair), which bounds the live coefficient registers to 2 * 2^d * F.
+#include "binned_backward.h"
 #include "hashenc_internal.h"
 #include "vec_io.h"
 
@@ -207,61 +208,62 @@ __device__ __forceinline__ void level_setup(const Grid& g, int l, const float (&
   for (int i = 0; i < D; ++i) ab[i] = axis_basis(t[i], g.Nf[l], g.invN[l]);
 }
 
+// Level-major order as in the d-linear forward: workgroup b handles level b / n_tiles, so
+// the chip streams one level's order tables at a time (they stay in L2 / Infinity Cache).
 template <int D, int F>
 __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
-    const Grid g, int64_t n, int d2_mode, const float* __restrict__ x,
+    const Grid g, int64_t n, int32_t n_tiles, int d2_mode, const float* __restrict__ x,
     const float* __restrict__ params, float* __restrict__ gamma, float* __restrict__ dgamma,
     float* __restrict__ d2gamma) {
-  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int l = blockIdx.x / n_tiles;
+  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
   if (p >= n) return;
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
   const int64_t LF = (int64_t)g.L * F;
-  for (int l = 0; l < g.L; ++l) {
-    CellKeys<D> keys;
-    AxisBasis ab[D];
-    level_setup<D>(g, l, xp, keys, ab);
-    TableSel ts;
+  CellKeys<D> keys;
+  AxisBasis ab[D];
+  level_setup<D>(g, l, xp, keys, ab);
+  TableSel ts;
 #pragma unroll
-    for (int k = 0; k <= D; ++k) {
-      ts.base[k] = params + g.off[k][l];
-      ts.dense[k] = (g.dense[k] >> l) & 1u;
-    }
-    LevelOut<D, F> o;
+  for (int k = 0; k <= D; ++k) {
+    ts.base[k] = params + g.off[k][l];
+    ts.dense[k] = (g.dense[k] >> l) & 1u;
+  }
+  LevelOut<D, F> o;
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-      o.v[f] = 0.0f;
+  for (int f = 0; f < F; ++f) {
+    o.v[f] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < D; ++i) o.g[i][f] = o.h[i][f] = 0.0f;
-    }
-    fwd_pair<D, F, 0>(g, keys, ts, ab, o);
-    fwd_pair<D, F, 1>(g, keys, ts, ab, o);
-    if constexpr (D == 3) {
-      fwd_pair<D, F, 2>(g, keys, ts, ab, o);
-      fwd_pair<D, F, 3>(g, keys, ts, ab, o);
-    }
-    const int64_t col = (int64_t)l * F;
-    if (gamma) store_vec<F>(gamma + p * LF + col, o.v);
-    if (dgamma) {
+    for (int i = 0; i < D; ++i) o.g[i][f] = o.h[i][f] = 0.0f;
+  }
+  fwd_pair<D, F, 0>(g, keys, ts, ab, o);
+  fwd_pair<D, F, 1>(g, keys, ts, ab, o);
+  if constexpr (D == 3) {
+    fwd_pair<D, F, 2>(g, keys, ts, ab, o);
+    fwd_pair<D, F, 3>(g, keys, ts, ab, o);
+  }
+  const int64_t col = (int64_t)l * F;
+  if (gamma) store_vec<F>(gamma + p * LF + col, o.v);
+  if (dgamma) {
 #pragma unroll
-      for (int i = 0; i < D; ++i) store_vec<F>(dgamma + (p * D + i) * LF + col, o.g[i]);
-    }
-    if (d2gamma) {
-      if (d2_mode == HASHENC_D2_DIAG) {
+    for (int i = 0; i < D; ++i) store_vec<F>(dgamma + (p * D + i) * LF + col, o.g[i]);
+  }
+  if (d2gamma) {
+    if (d2_mode == HASHENC_D2_DIAG) {
 #pragma unroll
-        for (int i = 0; i < D; ++i) store_vec<F>(d2gamma + (p * D + i) * LF + col, o.h[i]);
-      } else {
-        float lap[F];
+      for (int i = 0; i < D; ++i) store_vec<F>(d2gamma + (p * D + i) * LF + col, o.h[i]);
+    } else {
+      float lap[F];
 #pragma unroll
-        for (int f = 0; f < F; ++f) {
-          float s = 0.0f;
+      for (int f = 0; f < F; ++f) {
+        float s = 0.0f;
 #pragma unroll
-          for (int i = 0; i < D; ++i) s += o.h[i][f];
-          lap[f] = s;
-        }
-        store_vec<F>(d2gamma + p * LF + col, lap);
+        for (int i = 0; i < D; ++i) s += o.h[i][f];
+        lap[f] = s;
       }
+      store_vec<F>(d2gamma + p * LF + col, lap);
     }
   }
 }
@@ -276,11 +278,8 @@ struct LevelUp {
 
 // Reverse of fwd_pair: distribute the level upstream onto the coefficients of corner pair
 // (0, Y) and scatter-add them.
-template <int D, int F, int Y>
-__device__ __forceinline__ void bwd_pair(const Grid& g, const CellKeys<D>& keys,
-                                         float* const (&base)[kMaxTables],
-                                         const bool (&dense)[kMaxTables],
-                                         const AxisBasis (&ab)[D], const LevelUp<D, F>& u) {
+template <int D, int F, int Y, class Sink>
+__device__ __forceinline__ void bwd_pair(Sink& sink, const AxisBasis (&ab)[D], const LevelUp<D, F>& u) {
   CornerRows<D, F> lo, hi;
   constexpr int c1 = Y & 1;
   constexpr int c2 = (Y >> 1) & 1;
@@ -324,8 +323,88 @@ __device__ __forceinline__ void bwd_pair(const Grid& g, const CellKeys<D>& keys,
      }()),
      ...);
   }(std::make_integer_sequence<int, NA>{});
-  scatter_corner<D, F, (Y << 1)>(g, keys, base, dense, lo);
-  scatter_corner<D, F, (Y << 1) | 1>(g, keys, base, dense, hi);
+  sink.template emit<(Y << 1)>(lo);
+  sink.template emit<(Y << 1) | 1>(hi);
+}
+
+// Backward sink: fp32 atomics straight into the gradient tables.
+template <int D, int F>
+struct AtomicSink {
+  const Grid& g;
+  const CellKeys<D>& keys;
+  float* base[kMaxTables];
+  bool dense[kMaxTables];
+  template <int C>
+  __device__ __forceinline__ void emit(CornerRows<D, F>& cr) {
+    scatter_corner<D, F, C>(g, keys, base, dense, cr);
+  }
+};
+
+// Backward sink: compact entries into the bins of the binned backward.
+template <int D, int F>
+struct BinSink {
+  const Grid& g;
+  const BinPlan& bp;
+  const CellKeys<D>& keys;
+  int l;
+  int32_t* hist;
+  uint16_t* rows_out;
+  float* vbase[kMaxTables];
+  int32_t ebase[kMaxTables];
+  bool dense[kMaxTables];
+
+  template <int K, int W>
+  __device__ __forceinline__ void put(uint32_t row, const float (&v)[W]) {
+    int32_t bin;
+    uint32_t local;
+    bin_of(bp, K, l, row, bin, local);
+    const int32_t pos = atomicAdd(&hist[bin], 1);
+    rows_out[pos] = (uint16_t)local;
+    store_vec<W>(vbase[K] + (int64_t)(pos - ebase[K]) * W, v);
+  }
+  template <int C>
+  __device__ __forceinline__ void emit(CornerRows<D, F>& cr) {
+    put<0, F>(corner_row<D, C>(keys, dense[0], g.T[0], g.Tmask[0]), cr.r0);
+    put<1, binom_d(D, 1) * F>(corner_row<D, C>(keys, dense[1], g.T[1], g.Tmask[1]), cr.r1);
+    put<2, binom_d(D, 2) * F>(corner_row<D, C>(keys, dense[2], g.T[2], g.Tmask[2]), cr.r2);
+    if constexpr (D == 3) put<3, F>(corner_row<D, C>(keys, dense[3], g.T[3], g.Tmask[3]), cr.r3);
+  }
+};
+
+// Upstream of one point at one level (NULL arrays read as zero; the Laplacian upstream is
+// the same for every diagonal term).
+template <int D, int F>
+__device__ __forceinline__ LevelUp<D, F> load_level_up(const Grid& g, int64_t p, int l, int d2_mode,
+                                                       const float* __restrict__ g_gamma,
+                                                       const float* __restrict__ g_dgamma,
+                                                       const float* __restrict__ g_d2gamma) {
+  const int64_t LF = (int64_t)g.L * F;
+  const int64_t col = (int64_t)l * F;
+  LevelUp<D, F> u;
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    u.v[f] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) u.g[i][f] = u.h[i][f] = 0.0f;
+  }
+  if (g_gamma) load_vec<F>(g_gamma + p * LF + col, u.v);
+  if (g_dgamma) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) load_vec<F>(g_dgamma + (p * D + i) * LF + col, u.g[i]);
+  }
+  if (g_d2gamma) {
+    if (d2_mode == HASHENC_D2_DIAG) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) load_vec<F>(g_d2gamma + (p * D + i) * LF + col, u.h[i]);
+    } else {
+      load_vec<F>(g_d2gamma + p * LF + col, u.h[0]);
+#pragma unroll
+      for (int i = 1; i < D; ++i)
+#pragma unroll
+        for (int f = 0; f < F; ++f) u.h[i][f] = u.h[0][f];
+    }
+  }
+  return u;
 }
 
 template <int D, int F>
@@ -338,57 +417,127 @@ __global__ __launch_bounds__(kBlock) void hermite_backward_kernel(
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
-  const int64_t LF = (int64_t)g.L * F;
   for (int l = 0; l < g.L; ++l) {
-    const int64_t col = (int64_t)l * F;
-    LevelUp<D, F> u;
-#pragma unroll
-    for (int f = 0; f < F; ++f) {
-      u.v[f] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < D; ++i) u.g[i][f] = u.h[i][f] = 0.0f;
-    }
-    if (g_gamma) load_vec<F>(g_gamma + p * LF + col, u.v);
-    if (g_dgamma) {
-#pragma unroll
-      for (int i = 0; i < D; ++i) load_vec<F>(g_dgamma + (p * D + i) * LF + col, u.g[i]);
-    }
-    if (g_d2gamma) {
-      if (d2_mode == HASHENC_D2_DIAG) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) load_vec<F>(g_d2gamma + (p * D + i) * LF + col, u.h[i]);
-      } else {
-        load_vec<F>(g_d2gamma + p * LF + col, u.h[0]);
-#pragma unroll
-        for (int i = 1; i < D; ++i)
-#pragma unroll
-          for (int f = 0; f < F; ++f) u.h[i][f] = u.h[0][f];
-      }
-    }
+    const LevelUp<D, F> u = load_level_up<D, F>(g, p, l, d2_mode, g_gamma, g_dgamma, g_d2gamma);
     CellKeys<D> keys;
     AxisBasis ab[D];
     level_setup<D>(g, l, xp, keys, ab);
-    float* base[kMaxTables];
-    bool dense[kMaxTables];
+    AtomicSink<D, F> sink{g, keys};
 #pragma unroll
     for (int k = 0; k < kMaxTables; ++k) {
-      base[k] = grad + (k <= D ? g.off[k][l] : 0);
-      dense[k] = (g.dense[k] >> l) & 1u;
+      sink.base[k] = grad + (k <= D ? g.off[k][l] : 0);
+      sink.dense[k] = (g.dense[k] >> l) & 1u;
     }
-    bwd_pair<D, F, 0>(g, keys, base, dense, ab, u);
-    bwd_pair<D, F, 1>(g, keys, base, dense, ab, u);
+    bwd_pair<D, F, 0>(sink, ab, u);
+    bwd_pair<D, F, 1>(sink, ab, u);
     if constexpr (D == 3) {
-      bwd_pair<D, F, 2>(g, keys, base, dense, ab, u);
-      bwd_pair<D, F, 3>(g, keys, base, dense, ab, u);
+      bwd_pair<D, F, 2>(sink, ab, u);
+      bwd_pair<D, F, 3>(sink, ab, u);
     }
   }
+}
+
+// Binned backward, count (SCATTER = false) and scatter (SCATTER = true) passes: as the
+// d-linear ones, with one entry per (corner, order table) carrying that table's row.
+template <int D, int F, bool SCATTER>
+__global__ __launch_bounds__(kBinThreads) void hermite_bin_kernel(
+    const Grid g, const BinPlan bp, int64_t n, int32_t nblk, int d2_mode, const float* __restrict__ x,
+    const float* __restrict__ g_gamma, const float* __restrict__ g_dgamma,
+    const float* __restrict__ g_d2gamma, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ bin_start, const BinState* __restrict__ st,
+    uint16_t* __restrict__ rows_out, float* __restrict__ vals_out) {
+  extern __shared__ int32_t hist[];
+  constexpr int PPT = kBinTilePoints / kBinThreads;
+  const int blk = blockIdx.x;
+  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads)
+    hist[i] = SCATTER ? bin_start[i] + counts[(int64_t)i * nblk + blk] : 0;
+  __syncthreads();
+  const int64_t p0 = (int64_t)blk * kBinTilePoints + threadIdx.x;
+  // points outer, levels inner: a point's upstream rows are read in one short burst
+  for (int j = 0; j < PPT; ++j) {
+    const int64_t p = p0 + (int64_t)j * kBinThreads;
+    if (p >= n) break;
+    float xp[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
+    for (int l = 0; l < g.L; ++l) {
+      bool dense[kMaxTables];
+#pragma unroll
+      for (int k = 0; k < kMaxTables; ++k) dense[k] = (g.dense[k] >> l) & 1u;
+      if constexpr (!SCATTER) {
+        uint32_t base[D];
+        float t[D];
+        locate<D>(xp, g.N[l], g.Nf[l], base, t);
+        const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
+        [&]<int... C>(std::integer_sequence<int, C...>) {
+          ((
+               [&] {
+#pragma unroll
+                 for (int k = 0; k <= D; ++k) {
+                   int32_t bin;
+                   uint32_t local;
+                   bin_of(bp, k, l, corner_row<D, C>(keys, dense[k], g.T[k], g.Tmask[k]), bin, local);
+                   atomicAdd(&hist[bin], 1);
+                 }
+               }()),
+           ...);
+        }(std::make_integer_sequence<int, 1 << D>{});
+      } else {
+        const LevelUp<D, F> u = load_level_up<D, F>(g, p, l, d2_mode, g_gamma, g_dgamma, g_d2gamma);
+        CellKeys<D> keys;
+        AxisBasis ab[D];
+        level_setup<D>(g, l, xp, keys, ab);
+        BinSink<D, F> sink{g, bp, keys, l, hist, rows_out};
+#pragma unroll
+        for (int k = 0; k < kMaxTables; ++k) {
+          const int sg = k * bp.L + l;
+          const bool used = k <= D;
+          sink.vbase[k] = vals_out + (used ? st->seg_vbase[sg] : 0);
+          sink.ebase[k] = used ? st->seg_ebase[sg] : 0;
+          sink.dense[k] = dense[k];
+        }
+        bwd_pair<D, F, 0>(sink, ab, u);
+        bwd_pair<D, F, 1>(sink, ab, u);
+        if constexpr (D == 3) {
+          bwd_pair<D, F, 2>(sink, ab, u);
+          bwd_pair<D, F, 3>(sink, ab, u);
+        }
+      }
+    }
+  }
+  if constexpr (!SCATTER) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) counts[(int64_t)i * nblk + blk] = hist[i];
+  }
+}
+
+template <int D, int F>
+hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int d2_mode,
+                      bool scatter, int64_t n, const float* x, const float* gg, const float* gd,
+                      const float* g2, hipStream_t s) {
+  const dim3 grid((unsigned)w.nblk);
+  const size_t lds = sizeof(int32_t) * (size_t)bp.nbins;
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
+  const int32_t* bin_start = reinterpret_cast<const int32_t*>(ws + w.bin_start);
+  const BinState* st = reinterpret_cast<const BinState*>(ws + w.state);
+  uint16_t* rows = reinterpret_cast<uint16_t*>(ws + w.rows);
+  float* vals = reinterpret_cast<float*>(ws + w.vals);
+  if (scatter)
+    hipLaunchKernelGGL((hermite_bin_kernel<D, F, true>), grid, dim3(kBinThreads), lds, s, g, bp, n, w.nblk,
+                       d2_mode, x, gg, gd, g2, counts, bin_start, st, rows, vals);
+  else
+    hipLaunchKernelGGL((hermite_bin_kernel<D, F, false>), grid, dim3(kBinThreads), lds, s, g, bp, n, w.nblk,
+                       d2_mode, x, gg, gd, g2, counts, bin_start, st, rows, vals);
+  return hipGetLastError();
 }
 
 template <int D, int F>
 hipError_t launch_fwd(const Grid& g, int d2_mode, int64_t n, const float* x, const float* params,
                       float* gamma, float* dgamma, float* d2gamma, hipStream_t s) {
-  const dim3 grid((unsigned)((n + kBlock - 1) / kBlock));
-  hipLaunchKernelGGL((hermite_forward_kernel<D, F>), grid, dim3(kBlock), 0, s, g, n, d2_mode, x,
+  const int64_t tiles = (n + kBlock - 1) / kBlock;
+  if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(tiles * g.L));
+  hipLaunchKernelGGL((hermite_forward_kernel<D, F>), grid, dim3(kBlock), 0, s, g, n, (int32_t)tiles, d2_mode, x,
                      params, gamma, dgamma, d2gamma);
   return hipGetLastError();
 }
@@ -434,6 +583,12 @@ hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int
                                    const float* x, const float* g_gamma, const float* g_dgamma,
                                    const float* g_d2gamma, float* grad, hipStream_t s) {
   HASHENC_DISPATCH_DF(d, F, launch_bwd, g, d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, grad, s);
+}
+
+hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int d, int F,
+                              int d2_mode, bool scatter, int64_t n, const float* x, const float* g_gamma,
+                              const float* g_dgamma, const float* g_d2gamma, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_bin, g, bp, w, ws, d2_mode, scatter, n, x, g_gamma, g_dgamma, g_d2gamma, s);
 }
 
 }  // namespace hg

@@ -21,6 +21,7 @@
 //   4. reduce_partials_kernel: MLP gradients and the loss, summed over waves in fp64
 #include <cmath>
 
+#include "binned_backward.h"
 #include "hashenc.h"
 #include "hashenc_internal.h"
 
@@ -273,10 +274,11 @@ constexpr int kSirenBlocks = 1024;
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct WorkspaceLayout {
-  size_t enc_g, enc_d, enc_l, up_g, up_d, up_l, partial, total;
+  size_t enc_g, enc_d, enc_l, up_g, up_d, up_l, partial, bins, total;
 };
 
-WorkspaceLayout workspace_layout(int d, int LF, int64_t n, int64_t n_mlp) {
+WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t n_mlp, bool binned) {
+  const int LF = g.L * F;
   const int64_t c = n < kChunk ? n : kChunk;
   WorkspaceLayout w;
   size_t off = 0;
@@ -288,6 +290,7 @@ WorkspaceLayout workspace_layout(int d, int LF, int64_t n, int64_t n_mlp) {
   w.up_d = take(sizeof(float) * c * d * LF);
   w.up_l = take(sizeof(float) * c * LF);
   w.partial = take(sizeof(float) * (size_t)kSirenBlocks * kWavesPerBlock * (n_mlp + 1));
+  w.bins = take(binned ? binned_backward_workspace_bytes(g, d, F, true, c) : 0);
   w.total = off;
   return w;
 }
@@ -342,15 +345,15 @@ int64_t mlp_param_count(int in, int H, int depth) {
   return n;
 }
 
-size_t residual_workspace_bytes(int d, int LF, int64_t n, int in, int H, int depth) {
-  return workspace_layout(d, LF, n, mlp_param_count(in, H, depth)).total;
+size_t residual_workspace_bytes(const Grid& g, int d, int F, int64_t n, int in, int H, int depth,
+                                bool binned) {
+  return workspace_layout(g, d, F, n, mlp_param_count(in, H, depth), binned).total;
 }
 
 hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, const float* params,
                         int in, int H, int depth, float omega, const float* mlp, float* residual,
                         float* loss, float* grad_params, float* grad_mlp, void* workspace,
-                        hipStream_t s) {
-  const int LF = g.L * F;
+                        bool binned, hipStream_t s) {
   MlpArgs a;
   a.in = in;
   a.H = H;
@@ -365,7 +368,7 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
     a.woff[k] = off; off += fi * fo;
     a.boff[k] = off; off += fo;
   }
-  const WorkspaceLayout wl = workspace_layout(d, LF, n, a.n_mlp);
+  const WorkspaceLayout wl = workspace_layout(g, d, F, n, a.n_mlp, binned);
   char* ws = static_cast<char*>(workspace);
   float* eg = reinterpret_cast<float*>(ws + wl.enc_g);
   float* ed = reinterpret_cast<float*>(ws + wl.enc_d);
@@ -391,7 +394,9 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (grad_params) {
-      e = launch_hermite_backward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, ug, ud, ul, grad_params, s);
+      e = binned ? run_binned_backward(g, d, F, true, HASHENC_D2_LAPLACIAN, c, xc, ug, ud, ul, grad_params,
+                                       ws + wl.bins, s)
+                 : launch_hermite_backward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, ug, ud, ul, grad_params, s);
       if (e != hipSuccess) return e;
     }
   }

@@ -89,13 +89,19 @@ def _gpu_forward(spec, x, params):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def _gpu_backward(spec, x, ups, n_params):
+def _gpu_backward(spec, x, ups, n_params, path="binned"):
     enc = api.HashGridEncoding(spec)
     grad = torch.zeros(n_params, device=DEV)
     U = [_dev(u) for u in ups] + [None] * (3 - len(ups))
-    enc.backward(_dev(x), grad, *U)
+    if path == "binned":
+        enc.backward_ws(_dev(x), grad, *U)
+    else:
+        enc.backward(_dev(x), grad, *U)
     torch.cuda.synchronize()
     return grad.cpu().numpy()
+
+
+PATHS = ["atomic", "binned"]
 
 
 CONFIGS = ["dlinear2d_L4_T12", "hermite2d_L8_T14", "dlinear3d_L16_T19", "hermite3d_L16_T19"]
@@ -143,22 +149,23 @@ def test_forward_parity(orc, name):
         _blocks_close(got["d2gamma"], d2, spec, FWD_TOL, "d2gamma")
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name", CONFIGS)
-def test_backward_parity(orc, name):
+def test_backward_parity(orc, name, path):
     W = I.WORKLOADS[name]
     spec = W["spec"]
     lay = orc.layout(spec)
     n = 3 * 1024 + 37
     x = _points(name, n)
     ups = I.upstream(W["id"], _upstream_shapes(spec, n))
-    got = _gpu_backward(spec, x, ups, lay["n_params"])
+    got = _gpu_backward(spec, x, ups, lay["n_params"], path)
     ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
     _grad_close(got, ref, lay, BWD_TOL)
 
 
 @pytest.mark.parametrize("F", [1, 4, 8])
 @pytest.mark.parametrize("kind", ["dlinear", "hermite"])
-def test_feature_widths(orc, kind, F):
+def test_feature_widths(orc, kind, F):  # both backward paths
     spec = {"d": 3, "L": 5, "F": F, "kind": kind, "T": [1 << 12] * 4, "n_min": 6, "n_max": 90,
             "d2_mode": "laplacian"}
     if kind == "dlinear":
@@ -175,8 +182,9 @@ def test_feature_widths(orc, kind, F):
         _blocks_close(got["d2gamma"], d2, spec, FWD_TOL, "d2gamma")
     ups = [u.astype(np.float32) for u in
            (rng.standard_normal(s) for s in _upstream_shapes(spec, 777))]
-    _grad_close(_gpu_backward(spec, x, ups, lay["n_params"]),
-                orc.backward(spec, x, *ups, n_params=lay["n_params"]), lay, BWD_TOL)
+    ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
+    for path in PATHS:
+        _grad_close(_gpu_backward(spec, x, ups, lay["n_params"], path), ref, lay, BWD_TOL)
 
 
 def test_laplacian_is_trace_of_diagonal():
@@ -254,9 +262,28 @@ def test_full_size_backward(orc, name):
     n = W["n_points"]
     x = I.points(W["id"], n, spec["d"])
     ups = I.upstream(W["id"], _upstream_shapes(spec, n))
-    got = _gpu_backward(spec, x, ups, lay["n_params"])
     ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
-    _grad_close(got, ref, lay, BWD_TOL)
+    for path in PATHS:
+        _grad_close(_gpu_backward(spec, x, ups, lay["n_params"], path), ref, lay, BWD_TOL)
+
+
+def test_binned_backward_chunks_and_clusters(orc):
+    # more points than one 2^20 chunk, half of them clustered (hot bins split across work
+    # items), a workspace reused across calls and accumulation into a non-zero gradient
+    W = I.WORKLOADS["dlinear3d_L16_T19"]
+    spec = dict(W["spec"], L=6, n_max=600)
+    lay = orc.layout(spec)
+    n = (1 << 20) + 777
+    x = I.points(5, n, 3, clustered_half=True)
+    (G,) = I.upstream(3, [(n, 12)])
+    enc = api.HashGridEncoding(spec)
+    ws = enc.workspace(n)
+    grad = torch.full((lay["n_params"],), 0.5, device=DEV)
+    for _ in range(2):
+        enc.backward_ws(_dev(x), grad, _dev(G), workspace=ws)
+    torch.cuda.synchronize()
+    ref = orc.backward(spec, x, G, n_params=lay["n_params"])
+    _grad_close(grad.cpu().numpy() - 0.5, 2 * ref, lay, BWD_TOL)
 
 
 @pytest.mark.parametrize("name", CONFIGS)
@@ -289,9 +316,12 @@ def test_backward_run_to_run_spread():
     G = _dev(G)
     a = torch.zeros(enc.n_params, device=DEV)
     b = torch.zeros(enc.n_params, device=DEV)
+    c = torch.zeros(enc.n_params, device=DEV)
     enc.backward(x, a, G)
     enc.backward(x, b, G)
+    enc.backward_ws(x, c, G)
     assert float((a - b).abs().max()) <= 1e-5 * float(a.abs().max())
+    assert float((a - c).abs().max()) <= 1e-5 * float(a.abs().max())
     # accumulation: a second call adds
     enc.backward(x, a, G)
     assert float((a - 2 * b).abs().max()) <= 1e-5 * float(b.abs().max())
