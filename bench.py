@@ -71,6 +71,67 @@ def copy_calibration(args, torch, api) -> int:
     return 0
 
 
+def mlp_flops_per_point(d: int, n_in: int, hidden: int, depth: int) -> int:
+    """Multiply-add FLOPs of the SIREN part per point: forward mode carries d + 2 rows
+    (value, d gradients, Laplacian) through every layer; the reverse sweep costs one product
+    for the weight gradients and one for the input adjoints per layer."""
+    rows = d + 2
+    fwd = 0
+    for k in range(depth):
+        fan_in = n_in if k == 0 else hidden
+        fwd += 2 * rows * fan_in * hidden
+    fwd += 2 * hidden  # output layer (Laplacian row)
+    return 3 * fwd
+
+
+def residual_bench(args, torch, api, I, W) -> int:
+    spec, m = W["spec"], W["mlp"]
+    n = W["n_points"]
+    dev = torch.device("cuda:0")
+    enc = api.HashGridEncoding(spec)
+    n_in = spec["L"] * spec["F"]
+    mlp = api.Mlp(n_in, m["hidden"], m["depth"], m["omega"])
+    x = torch.from_numpy(I.points(W["id"], n, spec["d"], clustered_half=W.get("clustered_half", False))).to(dev)
+    params = torch.from_numpy(I.tables(W["id"], enc.n_params, W["tables"])).to(dev)
+    mlp_params = torch.from_numpy(I.siren_mlp(W["id"], n_in, m["hidden"], m["depth"])).to(dev)
+    ws = torch.empty(api.hashenc_residual_workspace_size(enc.handle, mlp, n), dtype=torch.uint8, device=dev)
+    r = torch.empty(n, device=dev)
+    loss = torch.empty(1, device=dev)
+    gp = torch.zeros(enc.n_params, device=dev)
+    gm = torch.zeros(mlp_params.numel(), device=dev)
+
+    def step():
+        gp.zero_()
+        gm.zero_()
+        api.hashenc_residual(enc.handle, mlp, x, params, mlp_params, r, loss, gp, gm, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    lap_spec = dict(spec, d2_mode="laplacian")
+    alg = algorithmic_bytes_per_point(lap_spec)
+    enc_bytes = (alg["forward"] + alg["backward"]) * n
+    flops = mlp_flops_per_point(spec["d"], n_in, m["hidden"], m["depth"]) * n
+    print(json.dumps({
+        "metric": f"PINN residual steps: points/s ({args.workload})", "value": round(n / (ms * 1e-3), 1),
+        "unit": "points/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "n_points": n, "hidden": m["hidden"], "depth": m["depth"],
+                   "omega": m["omega"]},
+        "encoder_alg_GBps_over_step": round(enc_bytes / (ms * 1e-3) / 1e9, 1),
+        "mlp_TFLOPs_over_step": round(flops / (ms * 1e-3) / 1e12, 2),
+        "loss": float(loss.item())}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,7 +139,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--backward", choices=["binned", "atomic"], default="binned",
-                    help="binned: hashenc_backward_ws (workspace); atomic: hashenc_backward")
+                    help="binned: hashenc_forward_ws + hashenc_backward_ws (workspace); "
+                         "atomic: hashenc_forward + hashenc_backward (no workspace)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run the plain copy kernel over this many bytes "
@@ -101,8 +163,7 @@ def main() -> int:
 
     W = I.WORKLOADS[args.workload]
     if "mlp" in W:
-        print("bench.py: use --workload on an encoder workload", file=sys.stderr)
-        return 2
+        return residual_bench(args, torch, api, I, W)
     spec = W["spec"]
     n = W["n_points"]
     dev = torch.device("cuda:0")
@@ -125,7 +186,11 @@ def main() -> int:
         grad.zero_()
         if ev is not None:
             ev[0].record(stream)
-        api.hashenc_forward(enc.handle, x, params, outs["gamma"], outs.get("dgamma"), outs.get("d2gamma"))
+        if workspace is not None:
+            api.hashenc_forward_ws(enc.handle, x, params, outs["gamma"], outs.get("dgamma"), outs.get("d2gamma"),
+                                   workspace)
+        else:
+            api.hashenc_forward(enc.handle, x, params, outs["gamma"], outs.get("dgamma"), outs.get("d2gamma"))
         if ev is not None:
             ev[1].record(stream)
         if workspace is not None:

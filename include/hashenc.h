@@ -116,6 +116,18 @@ HASHENC_API int hashenc_param_layout(const hashenc* h, int32_t order, int32_t le
 HASHENC_API int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* params,
                     float* gamma, float* dgamma, float* d2gamma, hashenc_stream_t stream);
 
+/* Device workspace (bytes) that hashenc_forward_ws needs for n points (0: none used). */
+HASHENC_API int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size_t* bytes);
+
+/* Same outputs as hashenc_forward.  With a workspace the d-linear encoding is computed
+ * level by level into a level-major staging buffer [L][n][F] (every store writes whole
+ * cache lines) and then rearranged into gamma [n, L*F] in one pass.  workspace: >=
+ * hashenc_forward_workspace_size bytes, 256-byte aligned; calls sharing it must not
+ * overlap.  Hermite handles ignore the workspace. */
+HASHENC_API int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float* params,
+                                   float* gamma, float* dgamma, float* d2gamma, void* workspace,
+                                   size_t workspace_bytes, hashenc_stream_t stream);
+
 /* Backward: grad_params += d<G, forward(theta)>/d theta for the upstream gradients G
  * (shapes as the forward outputs; NULL = zero).  Contributions of colliding vertices sum.
  * Accumulated with fp32 atomics: the summation order, and so the last bits, vary from

@@ -14,6 +14,8 @@ from .api import (  # noqa: F401
     hashenc_destroy,
     hashenc_diag_copy,
     hashenc_forward,
+    hashenc_forward_workspace_size,
+    hashenc_forward_ws,
     hashenc_info,
     hashenc_param_layout,
     hashenc_residual,

@@ -62,6 +62,8 @@ SIGNATURES = [
     ("hashenc_param_layout", ctypes.c_int,
      [P, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
     ("hashenc_forward", ctypes.c_int, [P, I64, P, P, P, P, P, P]),
+    ("hashenc_forward_workspace_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)]),
+    ("hashenc_forward_ws", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),
     ("hashenc_backward", ctypes.c_int, [P, I64, P, P, P, P, P, P]),
     ("hashenc_backward_workspace_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)]),
     ("hashenc_backward_ws", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),

@@ -123,6 +123,28 @@ def hashenc_backward(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_
                                   _dev_ptr(grad_params, "grad_params"), _stream(stream)))
 
 
+def hashenc_forward_workspace_size(h: Handle, n: int) -> int:
+    b = ctypes.c_size_t()
+    check(load().hashenc_forward_workspace_size(h, n, ctypes.byref(b)))
+    return int(b.value)
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if workspace.device.type != "cuda":
+        raise ValueError("workspace must be a device tensor")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def hashenc_forward_ws(h: Handle, x: torch.Tensor, params: torch.Tensor, gamma=None, dgamma=None,
+                       d2gamma=None, workspace: torch.Tensor | None = None, stream=None) -> None:
+    ws_ptr, ws_bytes = _ws(workspace)
+    check(load().hashenc_forward_ws(h, x.shape[0], _dev_ptr(x, "x"), _dev_ptr(params, "params"),
+                                    _dev_ptr(gamma, "gamma"), _dev_ptr(dgamma, "dgamma"),
+                                    _dev_ptr(d2gamma, "d2gamma"), ws_ptr, ws_bytes, _stream(stream)))
+
+
 def hashenc_backward_workspace_size(h: Handle, n: int) -> int:
     b = ctypes.c_size_t()
     check(load().hashenc_backward_workspace_size(h, n, ctypes.byref(b)))
@@ -132,10 +154,7 @@ def hashenc_backward_workspace_size(h: Handle, n: int) -> int:
 def hashenc_backward_ws(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_d2gamma=None,
                         grad_params=None, workspace: torch.Tensor | None = None, stream=None) -> None:
     n = x.shape[0]
-    ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if workspace is not None and workspace.device.type != "cuda":
-        raise ValueError("workspace must be a device tensor")
+    ws_ptr, ws_bytes = _ws(workspace)
     check(load().hashenc_backward_ws(h, n, _dev_ptr(x, "x"), _dev_ptr(g_gamma, "g_gamma"),
                                      _dev_ptr(g_dgamma, "g_dgamma"), _dev_ptr(g_d2gamma, "g_d2gamma"),
                                      _dev_ptr(grad_params, "grad_params"), ws_ptr, ws_bytes, _stream(stream)))
@@ -214,9 +233,19 @@ class HashGridEncoding:
         return grad_params
 
     def workspace(self, n: int) -> torch.Tensor | None:
-        """A device workspace for backward_ws on n points (None when none is needed)."""
-        b = hashenc_backward_workspace_size(self.handle, n)
+        """A device workspace for forward_ws and backward_ws on n points (None when neither
+        uses one); the two calls may share it when they do not overlap."""
+        b = max(hashenc_backward_workspace_size(self.handle, n), hashenc_forward_workspace_size(self.handle, n))
         return torch.empty(b, dtype=torch.uint8, device="cuda") if b else None
+
+    def forward_ws(self, x: torch.Tensor, params: torch.Tensor, workspace=None, stream=None) -> dict:
+        out = {k: torch.empty(v, device=x.device, dtype=torch.float32)
+               for k, v in self.output_shapes(x.shape[0]).items()}
+        if workspace is None:
+            workspace = self.workspace(x.shape[0])
+        hashenc_forward_ws(self.handle, x, params, out["gamma"], out.get("dgamma"), out.get("d2gamma"),
+                           workspace, stream)
+        return out
 
     def backward_ws(self, x: torch.Tensor, grad_params: torch.Tensor, g_gamma=None, g_dgamma=None,
                     g_d2gamma=None, workspace=None, stream=None) -> torch.Tensor:

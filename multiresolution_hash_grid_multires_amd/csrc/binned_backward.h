@@ -17,12 +17,23 @@ constexpr int64_t kStageBytes = 116 * 1024;       // LDS staging of the d-linear
 constexpr int kScatterThreads = 512;              // d-linear scatter workgroup
 constexpr size_t kMaxScatterLds = 150 * 1024;     // of the 160 KB LDS of a gfx950 CU
 
-// Small, by-value plan: bins are (segment, chunk of 2^cshift rows) in segment order.
+// Small, by-value plan: bins are (segment, chunk of rows) in segment order.  A chunk has
+// 2^cshift rows, except on dense d-linear segments in pair mode, where it holds whole
+// x-lines (seg_chunk rows, not a power of two) so that x-neighbour rows never straddle.
+//
+// Entries of d-linear segments are records {uint32 rows, float t, float aG[F]}: rows packs
+// the chunk-local row of the x-corner pair's lower (c0 = 0) corner in the low 16 bits and
+// the upper corner's in the high 16 bits (0xFFFF: a single corner); the lower row receives
+// (1 - t) * aG and the upper t * aG.  Entries of Hermite segments are a uint16 local row plus
+// the row's W values.
 struct BinPlan {
   int32_t d, L, ntab, nseg, nbins;
+  int32_t records;              // 1: d-linear records (2 + F floats); 0: Hermite rows + values
   int32_t max_seg_bins;         // most bins of any one segment
   int32_t width[kMaxTables];    // floats per row of table k
-  int32_t cshift[kMaxTables];   // log2 rows per chunk of table k
+  int32_t cshift[kMaxTables];   // log2 rows per chunk of table k (power-of-two chunks)
+  uint32_t pair_mask;           // d-linear: bit l set = level l uses x-corner pair records
+  int32_t seg_chunk[kMaxSeg];   // rows per chunk of segment s
   int32_t seg_bin0[kMaxSeg + 1];
 };
 
@@ -85,9 +96,17 @@ constexpr int kFewBins = 16;
 // Bin of a row of segment (k, l) and its row inside the chunk.
 __device__ __forceinline__ void bin_of(const BinPlan& bp, int k, int l, uint32_t row, int32_t& bin,
                                        uint32_t& local) {
-  const int cs = bp.cshift[k];
-  bin = bp.seg_bin0[k * bp.L + l] + (int32_t)(row >> cs);
-  local = row & ((1u << cs) - 1u);
+  const int s = k * bp.L + l;
+  const uint32_t C = (uint32_t)bp.seg_chunk[s];
+  if (C & (C - 1u)) {  // whole x-lines of a dense level
+    const uint32_t q = row / C;
+    bin = bp.seg_bin0[s] + (int32_t)q;
+    local = row - q * C;
+  } else {
+    const int cs = bp.cshift[k];
+    bin = bp.seg_bin0[s] + (int32_t)(row >> cs);
+    local = row & ((1u << cs) - 1u);
+  }
 }
 
 int bin_cshift_for_width(int W);

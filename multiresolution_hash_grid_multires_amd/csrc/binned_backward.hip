@@ -127,7 +127,7 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
       const int32_t e1 = seg0[g + 1] >= nb ? part[1023] : bin_start[seg0[g + 1]];
       st->seg_ebase[g] = e0;
       st->seg_vbase[g] = vb;
-      vb += (int64_t)(e1 - e0) * bp.width[g / bp.L];
+      vb += (int64_t)(e1 - e0) * (bp.records ? 2 + bp.width[0] : bp.width[g / bp.L]);
     }
   }
 }
@@ -165,6 +165,39 @@ __device__ __forceinline__ void accumulate_entries(double* __restrict__ acc, int
   }
 }
 
+// d-linear records {rows, t, aG[F]}: the lower row gets (1 - t) aG, the upper (if any) t aG.
+template <int F>
+__device__ __forceinline__ void accumulate_records(double* __restrict__ acc, int plane,
+                                                   const float* __restrict__ vseg, int32_t ebase,
+                                                   int32_t begin, int32_t end) {
+  constexpr int R = 2 + F;
+  constexpr int U = 32 / R > 8 ? 8 : (32 / R < 1 ? 1 : 32 / R);
+  const int T = blockDim.x;
+  for (int32_t e0 = begin + (int32_t)threadIdx.x; e0 < end; e0 += T * U) {
+    float rec[U][R];
+    bool on[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t e = e0 + u * T;
+      on[u] = e < end;
+      if (on[u]) load_vec_nt<R>(vseg + (int64_t)(e - ebase) * R, rec[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!on[u]) continue;
+      const uint32_t rows = __float_as_uint(rec[u][0]);
+      const int lo = (int)(rows & 0xFFFFu), hi = (int)(rows >> 16);
+      const double t = rec[u][1];
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const double a = rec[u][2 + f];
+        atomicAdd(&acc[f * plane + lo], (1.0 - t) * a);
+        if (hi != 0xFFFF) atomicAdd(&acc[f * plane + hi], t * a);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g, const BinPlan bp,
                                                                     BinState* __restrict__ st,
                                                                     const WorkItem* __restrict__ items,
@@ -186,11 +219,11 @@ __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g
     const int sg = __builtin_amdgcn_readfirstlane(w.seg);
     const int k = sg / bp.L, l = sg % bp.L;
     const int W = bp.width[k];
-    const int cs = bp.cshift[k];
+    const int64_t C = bp.seg_chunk[sg];
     const int64_t chunk = __builtin_amdgcn_readfirstlane(w.bin) - bp.seg_bin0[sg];
-    const int64_t row0 = chunk << cs;
+    const int64_t row0 = chunk * C;
     const int64_t rem = seg_rows(g, bp.d, k, l) - row0;
-    const int64_t nrows = rem < ((int64_t)1 << cs) ? rem : ((int64_t)1 << cs);
+    const int64_t nrows = rem < C ? rem : C;
     const int nfl = (int)(nrows * W);
     for (int i = threadIdx.x; i < nfl; i += kReduceThreads) acc[i] = 0.0;
     __syncthreads();
@@ -198,7 +231,14 @@ __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g
     const float* vseg = vals + st->seg_vbase[sg];
     const int32_t eb = st->seg_ebase[sg];
     const int plane = (int)nrows;
-    switch (W) {
+    if (bp.records) {
+      switch (W) {
+        case 1: accumulate_records<1>(acc, plane, vseg, eb, w.begin, w.end); break;
+        case 2: accumulate_records<2>(acc, plane, vseg, eb, w.begin, w.end); break;
+        case 4: accumulate_records<4>(acc, plane, vseg, eb, w.begin, w.end); break;
+        default: accumulate_records<8>(acc, plane, vseg, eb, w.begin, w.end); break;
+      }
+    } else switch (W) {
       case 1: accumulate_entries<1>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
       case 2: accumulate_entries<2>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
       case 3: accumulate_entries<3>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
@@ -224,11 +264,13 @@ __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g
   }
 }
 
+// Workspace bound: every corner its own entry (single records on d-linear segments).
 int64_t entries_per_point(int d, int L, bool hermite) {
   return (int64_t)L * (1 << d) * (hermite ? d + 1 : 1);
 }
 
 int64_t floats_per_point(const BinPlan& bp, int d) {
+  if (bp.records) return (int64_t)bp.L * (1 << d) * (2 + bp.width[0]);
   int64_t w = 0;
   for (int k = 0; k < bp.ntab; ++k) w += bp.width[k];
   return (int64_t)bp.L * (1 << d) * w;
@@ -247,6 +289,8 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
   bp.L = g.L;
   bp.ntab = hermite ? d + 1 : 1;
   bp.nseg = bp.ntab * g.L;
+  bp.records = hermite ? 0 : 1;
+  bp.pair_mask = 0;
   for (int k = 0; k < kMaxTables; ++k) { bp.width[k] = 0; bp.cshift[k] = 0; }
   int32_t bin = 0;
   bp.max_seg_bins = 0;
@@ -254,10 +298,25 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
     const int W = hermite ? (k == 0 || k == d ? F : (d == 3 ? 3 * F : 2 * F)) : F;
     bp.width[k] = W;
     bp.cshift[k] = bin_cshift_for_width(W);
+    const int64_t C = (int64_t)1 << bp.cshift[k];
     for (int l = 0; l < g.L; ++l) {
+      const int s = k * g.L + l;
       const int64_t rows = seg_rows(g, d, k, l);
-      bp.seg_bin0[k * g.L + l] = bin;
-      const int32_t nb = (int32_t)((rows + ((int64_t)1 << bp.cshift[k]) - 1) >> bp.cshift[k]);
+      int64_t chunk = C;
+      if (!hermite) {
+        const bool dense = (g.dense[k] >> l) & 1u;
+        const int64_t line = (int64_t)g.N[l] + 1;
+        if (dense && line <= C) {
+          chunk = C / line * line;  // whole x-lines: x-neighbours share a chunk
+          bp.pair_mask |= 1u << l;
+        } else if (!dense && g.Tmask[k] != 0 && 2 * (int64_t)g.N[l] <= C) {
+          // XOR-adjacent rows differ below bit log2(2 N) <= cshift: same chunk
+          bp.pair_mask |= 1u << l;
+        }
+      }
+      bp.seg_chunk[s] = (int32_t)chunk;
+      bp.seg_bin0[s] = bin;
+      const int32_t nb = (int32_t)((rows + chunk - 1) / chunk);
       if (nb > bp.max_seg_bins) bp.max_seg_bins = nb;
       bin += nb;
     }
@@ -268,8 +327,8 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
 
 int bin_tile_points(const BinPlan& bp, int F, bool hermite) {
   if (hermite) return kBinTilePoints;
-  // d-linear scatter stages a tile-level of entries (row, position, F values) in LDS
-  const int64_t per_point = (int64_t)(1 << bp.d) * (6 + 4 * F);
+  // d-linear scatter stages a tile-level of pair records (2 + F floats and a position)
+  const int64_t per_point = (int64_t)(1 << (bp.d - 1)) * (4 * (2 + F) + 4);
   int tp = (int)(kStageBytes / per_point) / kScatterThreads * kScatterThreads;
   if (tp > 2 * kScatterThreads) tp = 2 * kScatterThreads;  // at most 2 points per scatter lane
   if (tp > kBinTilePoints) tp = kBinTilePoints;
@@ -290,7 +349,7 @@ BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64
   w.state = off; off += al(sizeof(BinState));
   w.bin_start = off; off += al(sizeof(int32_t) * (size_t)(bp.nbins + 1));
   w.items = off; off += al(sizeof(WorkItem) * (size_t)w.max_items);
-  w.rows = off; off += al(sizeof(uint16_t) * (size_t)entries);
+  w.rows = off; off += al(bp.records ? 0 : sizeof(uint16_t) * (size_t)entries);
   w.vals = off; off += al(sizeof(float) * (size_t)(chunk_points * fpp));
   w.total = off;
   return w;
@@ -324,7 +383,7 @@ bool binned_fits(const Grid& g, int d, int F, bool hermite) {
   if (hermite) return true;
   const int tile = bin_tile_points(bp, F, hermite);
   const size_t lds = sizeof(int32_t) * (2 * (size_t)bp.nbins + 2 * (size_t)bp.max_seg_bins + kScatterThreads) +
-                     (size_t)tile * (1 << d) * (sizeof(float) * F + sizeof(int32_t) + sizeof(uint16_t));
+                     (size_t)tile * (1 << (d - 1)) * (sizeof(float) * (2 + F) + sizeof(int32_t));
   return lds <= kMaxScatterLds;
 }
 

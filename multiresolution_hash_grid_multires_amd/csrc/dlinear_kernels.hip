@@ -22,7 +22,9 @@ namespace {
 // moment the whole chip works on one or two levels and each XCD's L2 holds those levels'
 // tables (4 MB for a hashed level of 2^19 rows of F = 2) instead of streaming every level's
 // table from the Infinity Cache.  x is re-read per level (12 bytes per point, cache hits).
-template <int D, int F>
+// LM_OUT: write level-major [L][n][F] (whole cache lines per workgroup) instead of the
+// point-major [n][L*F] rows, for the workspace path that transposes afterwards.
+template <int D, int F, bool LM_OUT>
 __global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, int64_t n, int32_t n_tiles,
                                                                  const float* __restrict__ x,
                                                                  const float* __restrict__ params,
@@ -55,7 +57,34 @@ __global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, i
 #pragma unroll
     for (int f = 0; f < F; ++f) acc[f] = fmaf(w, rows[c][f], acc[f]);
   }
-  store_vec<F>(gamma + p * (int64_t)g.L * F + (int64_t)l * F, acc);
+  if constexpr (LM_OUT) store_vec<F>(gamma + ((int64_t)l * n + p) * F, acc);
+  else store_vec<F>(gamma + p * (int64_t)g.L * F + (int64_t)l * F, acc);
+}
+
+// [L][n][F] -> [n][L*F]: one lane per point assembles its output row 4 floats at a time
+// from the level-major rows (loads coalesced across lanes) and writes 16-byte pieces, so
+// every output line is written whole by one wavefront.
+template <int F>
+__global__ __launch_bounds__(kBlock) void level_major_to_rows_kernel(int32_t L, int64_t n,
+                                                                     const float* __restrict__ lm,
+                                                                     float* __restrict__ out) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= n) return;
+  const int LF = L * F;
+  float* row = out + p * (int64_t)LF;
+  for (int c = 0; c < LF; c += 4) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = c + i;
+      v[i] = col < LF ? lm[((int64_t)(col / F) * n + p) * F + col % F] : 0.0f;
+    }
+    if ((LF & 3) == 0) {  // rows 16-byte aligned
+      reinterpret_cast<float4*>(row)[c / 4] = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      for (int i = 0; c + i < LF; ++i) row[c + i] = v[i];
+    }
+  }
 }
 
 // Backward.  Fp32 atomics are issued as one memory request per 64-byte segment that the
@@ -103,7 +132,9 @@ __global__ __launch_bounds__(kBlock) void dlinear_backward_kernel(const Grid g, 
 }
 
 // Binned backward, count pass: a workgroup owns a tile of `tile` points (at most 4 per
-// lane) and histograms their corner contributions over all bins in LDS.
+// lane) and histograms their entries over all bins in LDS.  On pair-mode levels the two
+// x-corners of each (y, z) corner pair make one entry (they always share a bin); elsewhere
+// each corner is its own entry.
 template <int D>
 __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g, const BinPlan bp, int64_t n,
                                                                     int32_t tile, int32_t nblk,
@@ -124,6 +155,7 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
   }
   for (int l = 0; l < g.L; ++l) {
     const bool dense = (g.dense[0] >> l) & 1u;
+    const bool pair = (bp.pair_mask >> l) & 1u;
     const bool few = bp.seg_bin0[l + 1] - bp.seg_bin0[l] <= kFewBins;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -133,27 +165,33 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
       float t[D];
       locate<D>(xp[j], g.N[l], g.Nf[l], base, t);
       const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
-      [&]<int... C>(std::integer_sequence<int, C...>) {
+      [&]<int... Y>(std::integer_sequence<int, Y...>) {
         ((
              [&] {
-               int32_t bin;
+               int32_t b0, b1;
                uint32_t local;
-               bin_of(bp, 0, l, corner_row<D, C>(keys, dense, g.T[0], g.Tmask[0]), bin, local);
-               if (few) wave_aggregated_add<false>(hist, bin);
-               else atomicAdd(&hist[bin], 1);
+               bin_of(bp, 0, l, corner_row<D, (Y << 1)>(keys, dense, g.T[0], g.Tmask[0]), b0, local);
+               if (few) wave_aggregated_add<false>(hist, b0);
+               else atomicAdd(&hist[b0], 1);
+               if (!pair) {
+                 bin_of(bp, 0, l, corner_row<D, (Y << 1) | 1>(keys, dense, g.T[0], g.Tmask[0]), b1, local);
+                 if (few) wave_aggregated_add<false>(hist, b1);
+                 else atomicAdd(&hist[b1], 1);
+               }
              }()),
          ...);
-      }(std::make_integer_sequence<int, 1 << D>{});
+      }(std::make_integer_sequence<int, 1 << (D - 1)>{});
     }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) counts[(int64_t)i * nblk + blk] = hist[i];
 }
 
-// Binned backward, scatter pass.  Per level, the tile's entries are first sorted by bin in
-// LDS (a local counting sort seeded with the tile's per-bin counts from the count pass),
+// Binned backward, scatter pass.  Per level, the tile's pair records are first sorted by bin
+// in LDS (a local counting sort seeded with the tile's per-bin counts from the count pass),
 // then copied out so that each bin receives one contiguous run: consecutive lanes write
-// consecutive rows / values and every cache line is written whole.
+// consecutive records and cache lines are written whole.  Single-corner records (levels
+// not in pair mode) are written straight to their slots.
 // PRE: the tile's upstream rows (L*F <= 32 floats per point) are read once into registers
 // before the level loop; otherwise each level reads its F floats of the row.
 template <int D, int F, bool PRE>
@@ -161,19 +199,19 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
     const Grid g, const BinPlan bp, int64_t n, int32_t tile, int32_t nblk, const float* __restrict__ x,
     const float* __restrict__ g_gamma, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
-    const BinState* __restrict__ st, uint16_t* __restrict__ rows_out, float* __restrict__ vals_out) {
-  constexpr int NC = 1 << D;
+    const BinState* __restrict__ st, float* __restrict__ vals_out) {
+  constexpr int NP = 1 << (D - 1);  // x-corner pairs per cell
+  constexpr int R = 2 + F;          // floats per record
   extern __shared__ int32_t lds[];
   const int mb = bp.max_seg_bins;
   const int nbins = bp.nbins;
-  int32_t* gstart = lds;                 // [nbins] global position of this tile's run in each bin
+  int32_t* gstart = lds;                 // [nbins] global slot of this tile's run in each bin
   int32_t* bcnt = lds + nbins;           // [nbins] this tile's entries in each bin
   int32_t* lstart = lds + 2 * nbins;     // [mb] start of each bin's run in the staging area
-  int32_t* lcur = lstart + mb;           // [mb] staging cursors
+  int32_t* lcur = lstart + mb;           // [mb] slot cursors
   int32_t* scan = lcur + mb;             // [kScatterThreads]
-  float* st_val = reinterpret_cast<float*>(scan + kScatterThreads);                     // [tile*NC*F]
-  int32_t* st_pos = reinterpret_cast<int32_t*>(st_val + (int64_t)tile * NC * F);    // [tile*NC]
-  uint16_t* st_row = reinterpret_cast<uint16_t*>(st_pos + (int64_t)tile * NC);      // [tile*NC]
+  float* st_rec = reinterpret_cast<float*>(scan + kScatterThreads);          // [tile*NP*R]
+  int32_t* st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)tile * NP * R);  // [tile*NP]
 
   const int blk = blockIdx.x;
   const int ppt = tile / kScatterThreads;
@@ -208,7 +246,7 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
   for (int l = 0; l < g.L; ++l) {
     const int32_t b0 = bp.seg_bin0[l];
     const int nb = bp.seg_bin0[l + 1] - b0;
-    // this tile's count and global start in each bin of the level; exclusive scan of counts
+    // exclusive scan of this tile's counts over the level's bins -> staging starts
     const int per = (nb + kScatterThreads - 1) / kScatterThreads;
     int32_t mysum = 0;
     for (int q = 0; q < per; ++q) {
@@ -234,7 +272,10 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
     }
     __syncthreads();
     const bool dense = (g.dense[0] >> l) & 1u;
+    const bool pair = (bp.pair_mask >> l) & 1u;
     const bool few = nb <= kFewBins;
+    const int32_t ebase = st->seg_ebase[l];
+    float* vseg = vals_out + st->seg_vbase[l];
 #pragma unroll
     for (int j = 0; j < MAXP; ++j) {
       const int64_t p = p0 + (int64_t)j * kScatterThreads;
@@ -260,38 +301,54 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
 #pragma unroll
         for (int f = 0; f < F; ++f) G[f] = 0.0f;
       }
-      [&]<int... C>(std::integer_sequence<int, C...>) {
+      [&]<int... Y>(std::integer_sequence<int, Y...>) {
         ((
              [&] {
-               int32_t bin;
-               uint32_t local;
-               bin_of(bp, 0, l, corner_row<D, C>(keys, dense, g.T[0], g.Tmask[0]), bin, local);
-               const int i = bin - b0;
-               const int32_t lp = few ? wave_aggregated_add<true>(lcur, i) : atomicAdd(&lcur[i], 1);
-               float w = 1.0f;
+               float a = 1.0f;  // weight of the (y, z) corner pair
 #pragma unroll
-               for (int a = 0; a < D; ++a) w *= ((C >> a) & 1) ? t[a] : 1.0f - t[a];
-               st_row[lp] = (uint16_t)local;
-               st_pos[lp] = gstart[bin] + (lp - lstart[i]);
+               for (int i = 1; i < D; ++i) a *= ((Y >> (i - 1)) & 1) ? t[i] : 1.0f - t[i];
+               float rec[R];
 #pragma unroll
-               for (int f = 0; f < F; ++f) st_val[(int64_t)lp * F + f] = w * G[f];
+               for (int f = 0; f < F; ++f) rec[2 + f] = a * G[f];
+               int32_t bn0, bn1;
+               uint32_t lo, hi;
+               bin_of(bp, 0, l, corner_row<D, (Y << 1)>(keys, dense, g.T[0], g.Tmask[0]), bn0, lo);
+               bin_of(bp, 0, l, corner_row<D, (Y << 1) | 1>(keys, dense, g.T[0], g.Tmask[0]), bn1, hi);
+               if (pair) {
+                 const int i = bn0 - b0;
+                 const int32_t lp = few ? wave_aggregated_add<true>(lcur, i) : atomicAdd(&lcur[i], 1);
+                 rec[0] = __uint_as_float(lo | (hi << 16));
+                 rec[1] = t[0];
+#pragma unroll
+                 for (int q = 0; q < R; ++q) st_rec[(int64_t)lp * R + q] = rec[q];
+                 st_pos[lp] = gstart[bn0] + (lp - lstart[i]);
+               } else {
+                 // two single-corner records, lower row gets (1 - t) aG
+                 const int i0 = bn0 - b0, i1 = bn1 - b0;
+                 const int32_t s0 = few ? wave_aggregated_add<true>(lcur, i0) : atomicAdd(&lcur[i0], 1);
+                 rec[0] = __uint_as_float(lo | 0xFFFF0000u);
+                 rec[1] = t[0];
+                 store_vec<R>(vseg + (int64_t)(gstart[bn0] + (s0 - lstart[i0]) - ebase) * R, rec);
+                 const int32_t s1 = few ? wave_aggregated_add<true>(lcur, i1) : atomicAdd(&lcur[i1], 1);
+                 rec[0] = __uint_as_float(hi | 0xFFFF0000u);
+                 rec[1] = 1.0f - t[0];
+                 store_vec<R>(vseg + (int64_t)(gstart[bn1] + (s1 - lstart[i1]) - ebase) * R, rec);
+               }
              }()),
          ...);
-      }(std::make_integer_sequence<int, NC>{});
+      }(std::make_integer_sequence<int, NP>{});
     }
     __syncthreads();
-    const int32_t ebase = st->seg_ebase[l];
-    float* vseg = vals_out + st->seg_vbase[l];
-    const int32_t total = (int32_t)(tile_pts * NC);
-    for (int32_t q = threadIdx.x; q < total; q += kScatterThreads) {
-      const int32_t gp = st_pos[q];
-      rows_out[gp] = st_row[q];
-      float v[F];
+    if (pair) {
+      const int32_t total = (int32_t)(tile_pts * NP);
+      for (int32_t q = threadIdx.x; q < total; q += kScatterThreads) {
+        float rec[R];
 #pragma unroll
-      for (int f = 0; f < F; ++f) v[f] = st_val[(int64_t)q * F + f];
-      store_vec<F>(vseg + (int64_t)(gp - ebase) * F, v);
+        for (int c = 0; c < R; ++c) rec[c] = st_rec[(int64_t)q * R + c];
+        store_vec<R>(vseg + (int64_t)(st_pos[q] - ebase) * R, rec);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -306,35 +363,43 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
     return hipGetLastError();
   }
   const size_t lds = sizeof(int32_t) * (2 * (size_t)bp.nbins + 2 * (size_t)bp.max_seg_bins + kScatterThreads) +
-                     (size_t)w.tile * (1 << D) * (sizeof(float) * F + sizeof(int32_t) + sizeof(uint16_t));
+                     (size_t)w.tile * (1 << (D - 1)) * (sizeof(float) * (2 + F) + sizeof(int32_t));
   const int32_t* totals = reinterpret_cast<const int32_t*>(ws + w.totals);
   const int32_t* bin_start = reinterpret_cast<const int32_t*>(ws + w.bin_start);
   const BinState* st = reinterpret_cast<const BinState*>(ws + w.state);
-  uint16_t* rows = reinterpret_cast<uint16_t*>(ws + w.rows);
   float* vals = reinterpret_cast<float*>(ws + w.vals);
   if (g.L * F <= 32) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, true>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, true>), grid, dim3(kScatterThreads), lds, s, g, bp, n, w.tile,
-                       w.nblk, x, gg, counts, totals, bin_start, st, rows, vals);
+                       w.nblk, x, gg, counts, totals, bin_start, st, vals);
   } else {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, false>), grid, dim3(kScatterThreads), lds, s, g, bp, n, w.tile,
-                       w.nblk, x, gg, counts, totals, bin_start, st, rows, vals);
+                       w.nblk, x, gg, counts, totals, bin_start, st, vals);
   }
   return hipGetLastError();
 }
 
 template <int D, int F>
 hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* params, float* gamma,
-                      hipStream_t s) {
+                      float* scratch, hipStream_t s) {
   const int64_t tiles = (n + kBlock - 1) / kBlock;
   if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles * g.L));
-  hipLaunchKernelGGL((dlinear_forward_kernel<D, F>), grid, dim3(kBlock), 0, s, g, n, (int32_t)tiles, x, params,
+  if (!scratch) {
+    hipLaunchKernelGGL((dlinear_forward_kernel<D, F, false>), grid, dim3(kBlock), 0, s, g, n, (int32_t)tiles, x,
+                       params, gamma);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, n, (int32_t)tiles, x,
+                     params, scratch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((level_major_to_rows_kernel<F>), dim3((unsigned)tiles), dim3(kBlock), 0, s, g.L, n, scratch,
                      gamma);
   return hipGetLastError();
 }
@@ -371,8 +436,8 @@ hipError_t launch_bwd(const Grid& g, int64_t n, const float* x, const float* gg,
   } while (0)
 
 hipError_t launch_dlinear_forward(const Grid& g, int d, int F, int64_t n, const float* x,
-                                  const float* params, float* gamma, hipStream_t s) {
-  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, n, x, params, gamma, s);
+                                  const float* params, float* gamma, float* scratch, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, n, x, params, gamma, scratch, s);
 }
 
 hipError_t launch_dlinear_backward(const Grid& g, int d, int F, int64_t n, const float* x,

@@ -207,11 +207,41 @@ int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* pa
     return fail(HASHENC_EALIGN, "hashenc_forward: device pointers must be 16-byte aligned");
   hipError_t e;
   if (h->kind == HASHENC_DLINEAR)
-    e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma, stream);
+    e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma, nullptr, stream);
   else
     e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, gamma,
                                         dgamma, d2gamma, stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_forward launch");
+  return ok();
+}
+
+int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL handle");
+  if (!bytes) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL bytes");
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: n out of range");
+  *bytes = h->kind == HASHENC_DLINEAR ? sizeof(float) * (size_t)n * h->L * h->F : 0;
+  return ok();
+}
+
+int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float* params, float* gamma,
+                       float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
+                       hashenc_stream_t stream) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_ws: NULL handle");
+  if (h->kind != HASHENC_DLINEAR || !gamma || n == 0)
+    return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_ws: n = %lld out of range", (long long)n);
+  if (dgamma || d2gamma)
+    return fail(HASHENC_EUNSUPPORTED, "hashenc_forward_ws: derivative outputs need the Hermite kind");
+  if (!x || !params || !workspace)
+    return fail(HASHENC_EINVAL, "hashenc_forward_ws: x, params and workspace must not be NULL");
+  if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(HASHENC_EALIGN, "hashenc_forward_ws: pointers must be 16-byte aligned (workspace 256-byte)");
+  const size_t need = sizeof(float) * (size_t)n * h->L * h->F;
+  if (workspace_bytes < need)
+    return fail(HASHENC_EINVAL, "hashenc_forward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  hipError_t e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma,
+                                            static_cast<float*>(workspace), stream);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_forward_ws launch");
   return ok();
 }
 

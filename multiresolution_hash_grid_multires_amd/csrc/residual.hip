@@ -18,7 +18,7 @@
 //      reverse sweep; per-lane register accumulation of the lane's weight-gradient rows;
 //      writes the encoder upstream and per-wave partial MLP gradients
 //   3. Hermite backward with that upstream                                (hermite kernels)
-//   4. reduce_partials_kernel: MLP gradients and the loss, summed over waves in fp64
+//   4. reduce_partials_*: MLP gradients and the loss, summed over waves in fp64
 #include <cmath>
 
 #include "binned_backward.h"
@@ -250,16 +250,32 @@ __global__ __launch_bounds__(kW * kWavesPerBlock) void siren_residual_kernel(
   }
 }
 
-// grad_mlp[c] += sum_w partial[w][c] for c < n_mlp; loss (+)= sum_w partial[w][n_mlp] / n.
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ partial,
-                                                              int64_t n_waves, int64_t n_mlp,
-                                                              double inv_n_total, int first,
-                                                              float* __restrict__ grad_mlp,
-                                                              float* __restrict__ loss) {
+// Sum of the per-wave partial rows, in two passes: each workgroup of the first pass adds a
+// slice of kSliceRows rows for 256 columns in fp64; the second pass adds the slices and
+// applies the result (grad_mlp += ..., loss (+)= ... / n).
+constexpr int kSliceRows = 128;
+
+__global__ __launch_bounds__(256) void reduce_partials_slices_kernel(const float* __restrict__ partial,
+                                                                     int64_t n_waves, int64_t n_cols,
+                                                                     double* __restrict__ slices) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= n_cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * kSliceRows;
+  const int64_t r1 = r0 + kSliceRows < n_waves ? r0 + kSliceRows : n_waves;
+  double s = 0.0;
+  for (int64_t r = r0; r < r1; ++r) s += (double)partial[r * n_cols + c];
+  slices[(int64_t)blockIdx.y * n_cols + c] = s;
+}
+
+__global__ __launch_bounds__(256) void reduce_partials_apply_kernel(const double* __restrict__ slices,
+                                                                    int n_slices, int64_t n_mlp,
+                                                                    double inv_n_total, int first,
+                                                                    float* __restrict__ grad_mlp,
+                                                                    float* __restrict__ loss) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c > n_mlp) return;
   double s = 0.0;
-  for (int64_t wv = 0; wv < n_waves; ++wv) s += (double)partial[wv * (n_mlp + 1) + c];
+  for (int i = 0; i < n_slices; ++i) s += slices[(int64_t)i * (n_mlp + 1) + c];
   if (c < n_mlp) {
     if (grad_mlp) grad_mlp[c] += (float)s;
   } else {
@@ -274,7 +290,7 @@ constexpr int kSirenBlocks = 1024;
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct WorkspaceLayout {
-  size_t enc_g, enc_d, enc_l, up_g, up_d, up_l, partial, bins, total;
+  size_t enc_g, enc_d, enc_l, up_g, up_d, up_l, partial, slices, bins, total;
 };
 
 WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t n_mlp, bool binned) {
@@ -290,6 +306,8 @@ WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t
   w.up_d = take(sizeof(float) * c * d * LF);
   w.up_l = take(sizeof(float) * c * LF);
   w.partial = take(sizeof(float) * (size_t)kSirenBlocks * kWavesPerBlock * (n_mlp + 1));
+  w.slices = take(sizeof(double) * (size_t)((kSirenBlocks * kWavesPerBlock + kSliceRows - 1) / kSliceRows) *
+                  (n_mlp + 1));
   w.bins = take(binned ? binned_backward_workspace_bytes(g, d, F, true, c) : 0);
   w.total = off;
   return w;
@@ -389,8 +407,15 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
     e = dispatch_siren(d, depth, in, a, c, inv_n, xc, eg, ed, el, mlp, ug, ud, ul, rc, partial, blocks, s);
     if (e != hipSuccess) return e;
     const int64_t n_waves = (int64_t)blocks * kWavesPerBlock;
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((a.n_mlp + 1 + 255) / 256)), dim3(256), 0, s,
-                       partial, n_waves, a.n_mlp, inv_n, p0 == 0 ? 1 : 0, grad_mlp, loss);
+    const int n_slices = (int)((n_waves + kSliceRows - 1) / kSliceRows);
+    double* slices = reinterpret_cast<double*>(ws + wl.slices);
+    const unsigned col_blocks = (unsigned)((a.n_mlp + 1 + 255) / 256);
+    hipLaunchKernelGGL(reduce_partials_slices_kernel, dim3(col_blocks, (unsigned)n_slices), dim3(256), 0, s,
+                       partial, n_waves, a.n_mlp + 1, slices);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_partials_apply_kernel, dim3(col_blocks), dim3(256), 0, s, slices, n_slices, a.n_mlp,
+                       inv_n, p0 == 0 ? 1 : 0, grad_mlp, loss);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (grad_params) {

@@ -149,6 +149,22 @@ def test_forward_parity(orc, name):
         _blocks_close(got["d2gamma"], d2, spec, FWD_TOL, "d2gamma")
 
 
+@pytest.mark.parametrize("name", ["dlinear2d_L4_T12", "dlinear3d_L16_T19", "hermite2d_L8_T14"])
+def test_forward_ws_matches_forward(orc, name):
+    spec = I.WORKLOADS[name]["spec"]
+    lay = orc.layout(spec)
+    params = _dev(_tables(name, lay["n_params"]))
+    x = _dev(_points(name, 5000 + 3))
+    enc = api.HashGridEncoding(spec)
+    a = enc.forward(x, params)
+    ws = enc.workspace(5003)
+    for _ in range(2):  # workspace reused
+        b = enc.forward_ws(x, params, workspace=ws)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name", CONFIGS)
 def test_backward_parity(orc, name, path):
@@ -185,6 +201,35 @@ def test_feature_widths(orc, kind, F):  # both backward paths
     ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
     for path in PATHS:
         _grad_close(_gpu_backward(spec, x, ups, lay["n_params"], path), ref, lay, BWD_TOL)
+
+
+# The binned d-linear backward writes one record per x-corner pair where both corners fall
+# in one reduction chunk, and one record per corner elsewhere.  With F = 8 a chunk holds
+# 1024 rows, so these grids take every branch:
+PAIR_MODE_SPECS = {
+    # dense levels N = 300, 501, 837 (chunks of whole x-lines, not powers of two) and 1400
+    # (x-lines longer than a chunk: single records)
+    "dense2d": {"d": 2, "L": 4, "F": 8, "kind": "dlinear", "T": [1 << 21], "n_min": 300, "n_max": 1400},
+    # dense N = 16, 36; hashed N = 83, 191, 437 (2N within a chunk) and 1000 (single records)
+    "hashed3d": {"d": 3, "L": 6, "F": 8, "kind": "dlinear", "T": [1 << 16], "n_min": 16, "n_max": 1000},
+    # T not a power of two: hashed rows taken modulo T, single records
+    "modulo3d": {"d": 3, "L": 4, "F": 2, "kind": "dlinear", "T": [50000], "n_min": 16, "n_max": 300},
+}
+
+
+@pytest.mark.parametrize("case", sorted(PAIR_MODE_SPECS))
+def test_dlinear_record_modes(orc, case):
+    spec = PAIR_MODE_SPECS[case]
+    lay = orc.layout(spec)
+    n = 5000
+    rng = np.random.default_rng(len(case))
+    x = rng.random((n, spec["d"]), dtype=np.float32)
+    e = _edge_points(spec["d"])
+    x[: e.shape[0]] = e
+    (G,) = [u.astype(np.float32) for u in (rng.standard_normal(s) for s in _upstream_shapes(spec, n))]
+    ref = orc.backward(spec, x, G, n_params=lay["n_params"])
+    for path in PATHS:
+        _grad_close(_gpu_backward(spec, x, [G], lay["n_params"], path), ref, lay, BWD_TOL)
 
 
 def test_laplacian_is_trace_of_diagonal():
