@@ -13,7 +13,6 @@ constexpr int kBinThreads = 256;
 constexpr int kBinItemEntries = 1 << 18;          // entries per reduce work item (at most)
 constexpr int kReduceThreads = 512;
 constexpr int kBinReduceBlocks = 512;             // persistent reduce workgroups (2 per CU)
-constexpr int64_t kStageBytes = 116 * 1024;       // LDS staging of the d-linear scatter
 constexpr int kScatterThreads = 512;              // d-linear scatter workgroup
 constexpr size_t kMaxScatterLds = 150 * 1024;     // of the 160 KB LDS of a gfx950 CU
 
@@ -112,6 +111,8 @@ __device__ __forceinline__ void bin_of(const BinPlan& bp, int k, int l, uint32_t
 int bin_cshift_for_width(int W);
 void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp);
 int bin_tile_points(const BinPlan& bp, int F, bool hermite);
+// LDS of the d-linear scatter workgroup: three per-bin arrays and the pair-record staging.
+size_t dlinear_scatter_lds_bytes(const BinPlan& bp, int d, int F, int tile);
 BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64_t entries_per_point,
                                   int64_t floats_per_point, int tile);
 // Stages 2-3 (after the interpolant's count kernel) and stage 5 (after its scatter kernel).

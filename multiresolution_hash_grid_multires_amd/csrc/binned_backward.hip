@@ -326,14 +326,14 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
 }
 
 int bin_tile_points(const BinPlan& bp, int F, bool hermite) {
-  if (hermite) return kBinTilePoints;
-  // d-linear scatter stages a tile-level of pair records (2 + F floats and a position)
-  const int64_t per_point = (int64_t)(1 << (bp.d - 1)) * (4 * (2 + F) + 4);
-  int tp = (int)(kStageBytes / per_point) / kScatterThreads * kScatterThreads;
-  if (tp > 2 * kScatterThreads) tp = 2 * kScatterThreads;  // at most 2 points per scatter lane
-  if (tp > kBinTilePoints) tp = kBinTilePoints;
-  if (tp < kScatterThreads) tp = kScatterThreads;
-  return tp;
+  (void)bp;
+  (void)F;
+  return hermite ? kBinTilePoints : kScatterThreads;  // d-linear scatter: one point per lane
+}
+
+size_t dlinear_scatter_lds_bytes(const BinPlan& bp, int d, int F, int tile) {
+  return sizeof(int32_t) * (3 * (size_t)bp.nbins + kScatterThreads / 64) +
+         (size_t)tile * (1 << (d - 1)) * (sizeof(float) * (2 + F) + sizeof(int32_t));
 }
 
 BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64_t epp, int64_t fpp, int tile) {
@@ -382,9 +382,7 @@ bool binned_fits(const Grid& g, int d, int F, bool hermite) {
   if (bp.nbins > kMaxBins) return false;  // one LDS counter per bin in the count pass
   if (hermite) return true;
   const int tile = bin_tile_points(bp, F, hermite);
-  const size_t lds = sizeof(int32_t) * (2 * (size_t)bp.nbins + 2 * (size_t)bp.max_seg_bins + kScatterThreads) +
-                     (size_t)tile * (1 << (d - 1)) * (sizeof(float) * (2 + F) + sizeof(int32_t));
-  return lds <= kMaxScatterLds;
+  return dlinear_scatter_lds_bytes(bp, d, F, tile) <= kMaxScatterLds;
 }
 
 size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite, int64_t n) {

@@ -7,9 +7,10 @@
 // levels looked up independently) and adaptivity paragraph (colliding gradients combine:
 // here they sum).
 //
-// Mapping: one lane per point, the level loop wave-uniform so the per-level block
-// description stays in scalar registers; the 2^d corner gathers of a level are
-// independent loads issued back to back; x-adjacent corners usually share a cache line.
+// Mapping: the level loop is wave-uniform so the per-level block description stays in
+// scalar registers; the corner gathers of a level are independent loads issued back to
+// back; x-adjacent corners usually share a cache line, which the forward exploits by giving
+// the two x-corners of a pair to neighbouring lanes.
 #include "binned_backward.h"
 #include "hashenc_internal.h"
 #include "vec_io.h"
@@ -17,73 +18,136 @@
 namespace hg {
 namespace {
 
-// Forward.  Workgroups are ordered level-major: workgroup b handles level b / n_tiles for
-// the b % n_tiles-th tile of kBlock points.  Workgroups are dispatched in order, so at any
-// moment the whole chip works on one or two levels and each XCD's L2 holds those levels'
-// tables (4 MB for a hashed level of 2^19 rows of F = 2) instead of streaming every level's
-// table from the Infinity Cache.  x is re-read per level (12 bytes per point, cache hits).
+// Forward.  Workgroups are ordered by pass: workgroup b handles pass b / n_tiles for the
+// b % n_tiles-th tile of points, a pass being one level or a run of consecutive small levels
+// whose tables together fit kFwdPassBytes.  Workgroups are dispatched in order, so at any
+// moment the whole chip works on one or two passes and each XCD's L2 holds those tables (4 MB
+// for a hashed level of 2^19 rows of F = 2) instead of streaming every level's table from
+// the Infinity Cache.  x is re-read per pass (12 bytes per point).
 // LM_OUT: write level-major [L][n][F] (whole cache lines per workgroup) instead of the
-// point-major [n][L*F] rows, for the workspace path that transposes afterwards.
+// point-major [n][L*F] rows; without it every level is one pass.
+constexpr int64_t kFwdPassBytes = int64_t(3) << 20;
+
+struct FwdPlan {
+  int32_t n_pass;
+  uint8_t first[kMaxLevels];  // levels [first, last] of a pass
+  uint8_t last[kMaxLevels];
+};
+
+FwdPlan make_fwd_plan(const Grid& g, int d, int F, bool group) {
+  FwdPlan fp;
+  fp.n_pass = 0;
+  int64_t group_bytes = 0;
+  for (int l = 0; l < g.L; ++l) {
+    int64_t rows = g.T[0];
+    if ((g.dense[0] >> l) & 1u) {
+      rows = 1;
+      for (int i = 0; i < d; ++i) rows *= (int64_t)g.N[l] + 1;
+    }
+    const int64_t bytes = rows * F * (int64_t)sizeof(float);
+    if (group && fp.n_pass > 0 && group_bytes + bytes <= kFwdPassBytes) {
+      fp.last[fp.n_pass - 1] = (uint8_t)l;
+      group_bytes += bytes;
+      continue;
+    }
+    fp.first[fp.n_pass] = fp.last[fp.n_pass] = (uint8_t)l;
+    ++fp.n_pass;
+    group_bytes = bytes;
+  }
+  return fp;
+}
+
+// Two lanes per point: lane c0 gathers the 2^(d-1) corners with x-bit c0, so the two corners
+// of every x-pair -- adjacent rows on dense levels, rows differing in the low bits on hashed
+// levels -- are read by neighbouring lanes of one load instruction and share one L2 request
+// whenever they share a cache line.  The lane sums meet through one cross-lane add.
 template <int D, int F, bool LM_OUT>
-__global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, int64_t n, int32_t n_tiles,
-                                                                 const float* __restrict__ x,
+__global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, const FwdPlan fp, int64_t n,
+                                                                 int32_t n_tiles, const float* __restrict__ x,
                                                                  const float* __restrict__ params,
                                                                  float* __restrict__ gamma) {
-  const int l = blockIdx.x / n_tiles;
-  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
-  if (p >= n) return;
+  constexpr int PTS = kBlock / 2;  // points per workgroup
+  const int pass = blockIdx.x / n_tiles;
+  const int l0 = fp.first[pass], l1 = fp.last[pass];
+  const int c0 = threadIdx.x & 1;
+  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * PTS + (threadIdx.x >> 1);
+  if (p >= n) return;  // both lanes of a point leave together
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
-  uint32_t base[D];
-  float t[D];
-  locate<D>(xp, g.N[l], g.Nf[l], base, t);
-  const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
-  const bool dense = (g.dense[0] >> l) & 1u;
-  const float* tab = params + g.off[0][l];
-  float rows[1 << D][F];
-  // issue every gather of the level before using any of them
-  [&]<int... C>(std::integer_sequence<int, C...>) {
-    ((load_vec<F>(tab + (size_t)corner_row<D, C>(keys, dense, g.T[0], g.Tmask[0]) * F, rows[C])), ...);
-  }(std::make_integer_sequence<int, 1 << D>{});
-  float acc[F];
+  for (int l = l0; l <= l1; ++l) {
+    uint32_t base[D];
+    float t[D];
+    locate<D>(xp, g.N[l], g.Nf[l], base, t);
+    const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
+    const bool dense = (g.dense[0] >> l) & 1u;
+    const float* tab = params + g.off[0][l];
+    constexpr int NP = 1 << (D - 1);
+    float rows[NP][F];
+    // issue every gather of the level before using any of them
+    [&]<int... Y>(std::integer_sequence<int, Y...>) {
+      ((
+           [&] {
+             const uint32_t r = c0 ? corner_row<D, (Y << 1) | 1>(keys, dense, g.T[0], g.Tmask[0])
+                                   : corner_row<D, (Y << 1)>(keys, dense, g.T[0], g.Tmask[0]);
+             load_vec<F>(tab + (size_t)r * F, rows[Y]);
+           }()),
+       ...);
+    }(std::make_integer_sequence<int, NP>{});
+    float acc[F];
 #pragma unroll
-  for (int f = 0; f < F; ++f) acc[f] = 0.0f;
+    for (int f = 0; f < F; ++f) acc[f] = 0.0f;
+    const float wx = c0 ? t[0] : 1.0f - t[0];
 #pragma unroll
-  for (int c = 0; c < (1 << D); ++c) {
-    float w = 1.0f;
+    for (int y = 0; y < NP; ++y) {
+      float w = wx;
 #pragma unroll
-    for (int i = 0; i < D; ++i) w *= ((c >> i) & 1) ? t[i] : 1.0f - t[i];
+      for (int i = 1; i < D; ++i) w *= ((y >> (i - 1)) & 1) ? t[i] : 1.0f - t[i];
 #pragma unroll
-    for (int f = 0; f < F; ++f) acc[f] = fmaf(w, rows[c][f], acc[f]);
+      for (int f = 0; f < F; ++f) acc[f] = fmaf(w, rows[y][f], acc[f]);
+    }
+#pragma unroll
+    for (int f = 0; f < F; ++f) acc[f] += __shfl_xor(acc[f], 1, 64);
+    if (c0 == 0) {
+      if constexpr (LM_OUT) store_vec<F>(gamma + ((int64_t)l * n + p) * F, acc);
+      else store_vec<F>(gamma + p * (int64_t)g.L * F + (int64_t)l * F, acc);
+    }
   }
-  if constexpr (LM_OUT) store_vec<F>(gamma + ((int64_t)l * n + p) * F, acc);
-  else store_vec<F>(gamma + p * (int64_t)g.L * F + (int64_t)l * F, acc);
 }
 
-// [L][n][F] -> [n][L*F]: one lane per point assembles its output row 4 floats at a time
-// from the level-major rows (loads coalesced across lanes) and writes 16-byte pieces, so
-// every output line is written whole by one wavefront.
+// [L][n][F] -> [n][L*F] through LDS.  A workgroup owns P consecutive points: it reads the
+// P*F contiguous floats of each level (coalesced runs), parks them in LDS as P rows of L*F
+// (pitch L*F + 1 keeps the scattered LDS writes free of bank conflicts) and writes the
+// P*L*F contiguous output floats as 16-byte pieces, so every output line is written whole.
 template <int F>
-__global__ __launch_bounds__(kBlock) void level_major_to_rows_kernel(int32_t L, int64_t n,
+__global__ __launch_bounds__(kBlock) void level_major_to_rows_kernel(int32_t L, int64_t n, int32_t P,
                                                                      const float* __restrict__ lm,
                                                                      float* __restrict__ out) {
-  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (p >= n) return;
+  extern __shared__ float tile[];
   const int LF = L * F;
-  float* row = out + p * (int64_t)LF;
-  for (int c = 0; c < LF; c += 4) {
-    float v[4];
+  const int pitch = LF + 1;
+  const int64_t p0 = (int64_t)blockIdx.x * P;
+  const int np = (int)min((int64_t)P, n - p0);
+  const int per_level = np * F;
+  for (int i = threadIdx.x; i < L * per_level; i += kBlock) {
+    const int l = i / per_level, r = i - l * per_level;
+    tile[(r / F) * pitch + l * F + r % F] = lm[((int64_t)l * n + p0) * F + r];
+  }
+  __syncthreads();
+  float* dst = out + p0 * LF;
+  const int total = np * LF;
+  if ((LF & 3) == 0) {  // every row, hence the block's output, is 16-byte aligned
+    for (int q = threadIdx.x; 4 * q < total; q += kBlock) {
+      float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = c + i;
-      v[i] = col < LF ? lm[((int64_t)(col / F) * n + p) * F + col % F] : 0.0f;
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * q + k;
+        v[k] = tile[(e / LF) * pitch + e % LF];
+      }
+      reinterpret_cast<float4*>(dst)[q] = make_float4(v[0], v[1], v[2], v[3]);
     }
-    if ((LF & 3) == 0) {  // rows 16-byte aligned
-      reinterpret_cast<float4*>(row)[c / 4] = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-      for (int i = 0; c + i < LF; ++i) row[c + i] = v[i];
-    }
+  } else {
+    for (int e = threadIdx.x; e < total; e += kBlock) dst[e] = tile[(e / LF) * pitch + e % LF];
   }
 }
 
@@ -187,13 +251,46 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
   for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) counts[(int64_t)i * nblk + blk] = hist[i];
 }
 
-// Binned backward, scatter pass.  Per level, the tile's pair records are first sorted by bin
-// in LDS (a local counting sort seeded with the tile's per-bin counts from the count pass),
-// then copied out so that each bin receives one contiguous run: consecutive lanes write
+// Exclusive prefix sum of v[0..n) in place over the whole workgroup (T threads, each
+// scanning a run of consecutive elements); wsum holds T / 64 partial sums.
+template <int T>
+__device__ void block_exclusive_scan(int32_t* v, int n, int32_t* wsum) {
+  const int per = (n + T - 1) / T;
+  const int lo = threadIdx.x * per;
+  const int hi = min(n, lo + per);
+  int32_t own = 0;
+  for (int i = lo; i < hi; ++i) own += v[i];
+  // inclusive scan of the per-thread sums inside the wavefront
+  const int lane = (int)__lane_id();
+  int32_t inc = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += u;
+  }
+  const int wave = threadIdx.x / 64;
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int32_t run = before + inc - own;
+  for (int i = lo; i < hi; ++i) {
+    const int32_t c = v[i];
+    v[i] = run;
+    run += c;
+  }
+  __syncthreads();
+}
+
+// Binned backward, scatter pass.  One lane per point.  At the start the workgroup turns the
+// tile's per-bin counts (from the count pass) into an exclusive prefix over all bins, which
+// is both each bin's slot range in the LDS staging area (relative to the level's first bin)
+// and its cursor.  Per level, the tile's pair records are sorted by bin in LDS and then
+// copied out so that each bin receives one contiguous run: consecutive lanes write
 // consecutive records and cache lines are written whole.  Single-corner records (levels
 // not in pair mode) are written straight to their slots.
-// PRE: the tile's upstream rows (L*F <= 32 floats per point) are read once into registers
-// before the level loop; otherwise each level reads its F floats of the row.
+// PRE: the point's upstream row (L*F <= 32 floats) is read once into registers before the
+// level loop; otherwise each level reads its F floats of the row.
 template <int D, int F, bool PRE>
 __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
     const Grid g, const BinPlan bp, int64_t n, int32_t tile, int32_t nblk, const float* __restrict__ x,
@@ -203,86 +300,54 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
   constexpr int NP = 1 << (D - 1);  // x-corner pairs per cell
   constexpr int R = 2 + F;          // floats per record
   extern __shared__ int32_t lds[];
-  const int mb = bp.max_seg_bins;
   const int nbins = bp.nbins;
-  int32_t* gstart = lds;                 // [nbins] global slot of this tile's run in each bin
-  int32_t* bcnt = lds + nbins;           // [nbins] this tile's entries in each bin
-  int32_t* lstart = lds + 2 * nbins;     // [mb] start of each bin's run in the staging area
-  int32_t* lcur = lstart + mb;           // [mb] slot cursors
-  int32_t* scan = lcur + mb;             // [kScatterThreads]
-  float* st_rec = reinterpret_cast<float*>(scan + kScatterThreads);          // [tile*NP*R]
+  int32_t* gstart = lds;                  // [nbins] global slot of this tile's run in each bin
+  int32_t* excl = lds + nbins;            // [nbins] exclusive prefix of the tile's bin counts
+  int32_t* lcur = lds + 2 * nbins;        // [nbins] cursors (start at excl)
+  int32_t* wsum = lds + 3 * nbins;        // [kScatterThreads / 64]
+  float* st_rec = reinterpret_cast<float*>(wsum + kScatterThreads / 64);           // [tile*NP*R]
   int32_t* st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)tile * NP * R);  // [tile*NP]
 
   const int blk = blockIdx.x;
-  const int ppt = tile / kScatterThreads;
-  const int64_t p0 = (int64_t)blk * tile + threadIdx.x;
-  const int64_t tile_pts = min((int64_t)tile, n - (int64_t)blk * tile);
+  const int64_t p = (int64_t)blk * tile + threadIdx.x;
+  const bool on = p < n;
+  const int np = (int)min((int64_t)tile, n - (int64_t)blk * tile);
   for (int i = threadIdx.x; i < nbins; i += kScatterThreads) {
     const int32_t pre = counts[(int64_t)i * nblk + blk];
     const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)i * nblk + blk + 1] : totals[i];
     gstart[i] = bin_start[i] + pre;
-    bcnt[i] = nxt - pre;
+    excl[i] = nxt - pre;
   }
   __syncthreads();
-  constexpr int MAXP = 2;  // points per lane (tile <= 2 * kScatterThreads)
-  float xp[MAXP][D];
+  block_exclusive_scan<kScatterThreads>(excl, nbins, wsum);
+  for (int i = threadIdx.x; i < nbins; i += kScatterThreads) lcur[i] = excl[i];
+  float xp[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) xp[i] = on ? x[p * D + i] : 0.0f;
   const int64_t LF = (int64_t)g.L * F;
-  float up[PRE ? MAXP : 1][PRE ? 32 : 1];
+  float up[PRE ? 32 : 1];
+  if constexpr (PRE) {
 #pragma unroll
-  for (int j = 0; j < MAXP; ++j) {
-    const int64_t p = p0 + (int64_t)j * kScatterThreads;
-    const bool on = j < ppt && p < n;
-#pragma unroll
-    for (int i = 0; i < D; ++i) xp[j][i] = on ? x[p * D + i] : 0.0f;
-    if constexpr (PRE) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (on && g_gamma && 4 * q < LF) a = reinterpret_cast<const float4*>(g_gamma + p * LF)[q];
-        up[j][4 * q] = a.x; up[j][4 * q + 1] = a.y; up[j][4 * q + 2] = a.z; up[j][4 * q + 3] = a.w;
-      }
+    for (int q = 0; q < 8; ++q) {
+      float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (on && g_gamma && 4 * q < LF) a = reinterpret_cast<const float4*>(g_gamma + p * LF)[q];
+      up[4 * q] = a.x; up[4 * q + 1] = a.y; up[4 * q + 2] = a.z; up[4 * q + 3] = a.w;
     }
   }
+  __syncthreads();
   for (int l = 0; l < g.L; ++l) {
     const int32_t b0 = bp.seg_bin0[l];
     const int nb = bp.seg_bin0[l + 1] - b0;
-    // exclusive scan of this tile's counts over the level's bins -> staging starts
-    const int per = (nb + kScatterThreads - 1) / kScatterThreads;
-    int32_t mysum = 0;
-    for (int q = 0; q < per; ++q) {
-      const int i = threadIdx.x * per + q;
-      if (i < nb) mysum += bcnt[b0 + i];
-    }
-    scan[threadIdx.x] = mysum;
-    __syncthreads();
-    for (int off = 1; off < kScatterThreads; off <<= 1) {
-      const int32_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
-      __syncthreads();
-      scan[threadIdx.x] += v;
-      __syncthreads();
-    }
-    int32_t run = scan[threadIdx.x] - mysum;
-    for (int q = 0; q < per; ++q) {
-      const int i = threadIdx.x * per + q;
-      if (i < nb) {
-        lstart[i] = run;
-        lcur[i] = run;
-        run += bcnt[b0 + i];
-      }
-    }
-    __syncthreads();
+    const int32_t lbase = excl[b0];  // staging slots of this level start here
     const bool dense = (g.dense[0] >> l) & 1u;
     const bool pair = (bp.pair_mask >> l) & 1u;
     const bool few = nb <= kFewBins;
     const int32_t ebase = st->seg_ebase[l];
     float* vseg = vals_out + st->seg_vbase[l];
-#pragma unroll
-    for (int j = 0; j < MAXP; ++j) {
-      const int64_t p = p0 + (int64_t)j * kScatterThreads;
-      if (j >= ppt || p >= n) break;
+    if (on) {
       uint32_t base[D];
       float t[D];
-      locate<D>(xp[j], g.N[l], g.Nf[l], base, t);
+      locate<D>(xp, g.N[l], g.Nf[l], base, t);
       const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
       float G[F];
       if constexpr (PRE) {
@@ -292,7 +357,7 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
           float v = 0.0f;
 #pragma unroll
           for (int c = f; c < 32; c += F)
-            if (c == l * F + f) v = up[j][c];
+            if (c == l * F + f) v = up[c];
           G[f] = v;
         }
       } else if (g_gamma) {
@@ -315,32 +380,31 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
                bin_of(bp, 0, l, corner_row<D, (Y << 1)>(keys, dense, g.T[0], g.Tmask[0]), bn0, lo);
                bin_of(bp, 0, l, corner_row<D, (Y << 1) | 1>(keys, dense, g.T[0], g.Tmask[0]), bn1, hi);
                if (pair) {
-                 const int i = bn0 - b0;
-                 const int32_t lp = few ? wave_aggregated_add<true>(lcur, i) : atomicAdd(&lcur[i], 1);
+                 const int32_t s0 = few ? wave_aggregated_add<true>(lcur, bn0) : atomicAdd(&lcur[bn0], 1);
+                 const int32_t lp = s0 - lbase;
                  rec[0] = __uint_as_float(lo | (hi << 16));
                  rec[1] = t[0];
 #pragma unroll
                  for (int q = 0; q < R; ++q) st_rec[(int64_t)lp * R + q] = rec[q];
-                 st_pos[lp] = gstart[bn0] + (lp - lstart[i]);
+                 st_pos[lp] = gstart[bn0] + (s0 - excl[bn0]);
                } else {
                  // two single-corner records, lower row gets (1 - t) aG
-                 const int i0 = bn0 - b0, i1 = bn1 - b0;
-                 const int32_t s0 = few ? wave_aggregated_add<true>(lcur, i0) : atomicAdd(&lcur[i0], 1);
+                 const int32_t s0 = few ? wave_aggregated_add<true>(lcur, bn0) : atomicAdd(&lcur[bn0], 1);
                  rec[0] = __uint_as_float(lo | 0xFFFF0000u);
                  rec[1] = t[0];
-                 store_vec<R>(vseg + (int64_t)(gstart[bn0] + (s0 - lstart[i0]) - ebase) * R, rec);
-                 const int32_t s1 = few ? wave_aggregated_add<true>(lcur, i1) : atomicAdd(&lcur[i1], 1);
+                 store_vec<R>(vseg + (int64_t)(gstart[bn0] + (s0 - excl[bn0]) - ebase) * R, rec);
+                 const int32_t s1 = few ? wave_aggregated_add<true>(lcur, bn1) : atomicAdd(&lcur[bn1], 1);
                  rec[0] = __uint_as_float(hi | 0xFFFF0000u);
                  rec[1] = 1.0f - t[0];
-                 store_vec<R>(vseg + (int64_t)(gstart[bn1] + (s1 - lstart[i1]) - ebase) * R, rec);
+                 store_vec<R>(vseg + (int64_t)(gstart[bn1] + (s1 - excl[bn1]) - ebase) * R, rec);
                }
              }()),
          ...);
       }(std::make_integer_sequence<int, NP>{});
     }
-    __syncthreads();
-    if (pair) {
-      const int32_t total = (int32_t)(tile_pts * NP);
+    if (pair) {  // uniform over the workgroup
+      __syncthreads();
+      const int32_t total = np * NP;
       for (int32_t q = threadIdx.x; q < total; q += kScatterThreads) {
         float rec[R];
 #pragma unroll
@@ -362,8 +426,7 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
                        g, bp, n, w.tile, w.nblk, x, counts);
     return hipGetLastError();
   }
-  const size_t lds = sizeof(int32_t) * (2 * (size_t)bp.nbins + 2 * (size_t)bp.max_seg_bins + kScatterThreads) +
-                     (size_t)w.tile * (1 << (D - 1)) * (sizeof(float) * (2 + F) + sizeof(int32_t));
+  const size_t lds = dlinear_scatter_lds_bytes(bp, D, F, w.tile);
   const int32_t* totals = reinterpret_cast<const int32_t*>(ws + w.totals);
   const int32_t* bin_start = reinterpret_cast<const int32_t*>(ws + w.bin_start);
   const BinState* st = reinterpret_cast<const BinState*>(ws + w.state);
@@ -387,20 +450,23 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
 template <int D, int F>
 hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* params, float* gamma,
                       float* scratch, hipStream_t s) {
-  const int64_t tiles = (n + kBlock - 1) / kBlock;
-  if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(tiles * g.L));
+  const int64_t tiles = (n + kBlock / 2 - 1) / (kBlock / 2);  // two lanes per point
+  const FwdPlan fp = make_fwd_plan(g, D, F, scratch != nullptr);
+  if (tiles * fp.n_pass > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(tiles * fp.n_pass));
   if (!scratch) {
-    hipLaunchKernelGGL((dlinear_forward_kernel<D, F, false>), grid, dim3(kBlock), 0, s, g, n, (int32_t)tiles, x,
+    hipLaunchKernelGGL((dlinear_forward_kernel<D, F, false>), grid, dim3(kBlock), 0, s, g, fp, n, (int32_t)tiles, x,
                        params, gamma);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, n, (int32_t)tiles, x,
+  hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, fp, n, (int32_t)tiles, x,
                      params, scratch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((level_major_to_rows_kernel<F>), dim3((unsigned)tiles), dim3(kBlock), 0, s, g.L, n, scratch,
-                     gamma);
+  const int32_t P = g.L * F <= 128 ? 64 : 32;  // LDS tile at most 32 x 257 floats
+  const size_t lds = sizeof(float) * (size_t)P * (g.L * F + 1);
+  hipLaunchKernelGGL((level_major_to_rows_kernel<F>), dim3((unsigned)((n + P - 1) / P)), dim3(kBlock), lds, s, g.L,
+                     n, P, scratch, gamma);
   return hipGetLastError();
 }
 
@@ -434,6 +500,11 @@ hipError_t launch_bwd(const Grid& g, int64_t n, const float* x, const float* gg,
     }                                                                 \
     return hipErrorInvalidValue;                                      \
   } while (0)
+
+size_t dlinear_forward_workspace_bytes(const Grid& g, int d, int F, int64_t n) {
+  (void)d;
+  return sizeof(float) * (size_t)n * g.L * F;
+}
 
 hipError_t launch_dlinear_forward(const Grid& g, int d, int F, int64_t n, const float* x,
                                   const float* params, float* gamma, float* scratch, hipStream_t s) {

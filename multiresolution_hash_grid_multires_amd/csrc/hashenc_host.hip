@@ -219,7 +219,7 @@ int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL handle");
   if (!bytes) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL bytes");
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: n out of range");
-  *bytes = h->kind == HASHENC_DLINEAR ? sizeof(float) * (size_t)n * h->L * h->F : 0;
+  *bytes = h->kind == HASHENC_DLINEAR ? hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n) : 0;
   return ok();
 }
 
@@ -236,7 +236,7 @@ int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float*
     return fail(HASHENC_EINVAL, "hashenc_forward_ws: x, params and workspace must not be NULL");
   if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(HASHENC_EALIGN, "hashenc_forward_ws: pointers must be 16-byte aligned (workspace 256-byte)");
-  const size_t need = sizeof(float) * (size_t)n * h->L * h->F;
+  const size_t need = hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n);
   if (workspace_bytes < need)
     return fail(HASHENC_EINVAL, "hashenc_forward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
   hipError_t e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma,

@@ -123,7 +123,8 @@ __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
 
 // ---------------------------------------------------------------- launchers
 // All launchers assume validated arguments (host side) and n >= 1.
-// scratch: NULL, or n * L * F floats for the level-major staging of the output
+// scratch: NULL, or dlinear_forward_workspace_bytes for the level-major staging of the output
+size_t dlinear_forward_workspace_bytes(const Grid& g, int d, int F, int64_t n);
 hipError_t launch_dlinear_forward(const Grid& g, int d, int F, int64_t n, const float* x,
                                   const float* params, float* gamma, float* scratch, hipStream_t s);
 hipError_t launch_dlinear_backward(const Grid& g, int d, int F, int64_t n, const float* x,
