@@ -23,11 +23,12 @@ constexpr size_t kMaxScatterLds = 150 * 1024;     // of the 160 KB LDS of a gfx9
 // Entries of d-linear segments are records {uint32 rows, float t, float aG[F]}: rows packs
 // the chunk-local row of the x-corner pair's lower (c0 = 0) corner in the low 16 bits and
 // the upper corner's in the high 16 bits (0xFFFF: a single corner); the lower row receives
-// (1 - t) * aG and the upper t * aG.  Entries of Hermite segments are a uint16 local row plus
-// the row's W values.
+// (1 - t) * aG and the upper t * aG.  Entries of Hermite segments are {uint32 local row,
+// float v[W]}: the row's W values.  Either way the row index travels as the bits of the
+// record's first float, so every entry is written and read as one contiguous record.
 struct BinPlan {
   int32_t d, L, ntab, nseg, nbins;
-  int32_t records;              // 1: d-linear records (2 + F floats); 0: Hermite rows + values
+  int32_t records;              // 1: d-linear records (2 + F floats); 0: Hermite (1 + W floats)
   int32_t max_seg_bins;         // most bins of any one segment
   int32_t width[kMaxTables];    // floats per row of table k
   int32_t cshift[kMaxTables];   // log2 rows per chunk of table k (power-of-two chunks)
@@ -52,7 +53,7 @@ struct BinWorkspace {
   int32_t tile;   // points per count / scatter workgroup
   int32_t nblk;
   int64_t max_items;
-  size_t counts, totals, state, bin_start, items, rows, vals, total;
+  size_t counts, totals, seg_sums, state, bin_start, items, vals, total;
 };
 
 __host__ __device__ inline int64_t seg_rows(const Grid& g, int d, int k, int l) {
@@ -89,6 +90,47 @@ __device__ __forceinline__ int32_t wave_aggregated_add(int32_t* hist, int32_t bi
   return result;
 }
 
+// Tile handled by workgroup b of an nblk-workgroup count or scatter launch.  Workgroups are
+// dealt round-robin to the 8 XCDs (b % 8), so this hands each XCD a contiguous range of
+// tiles: the runs that neighbouring tiles write into one bin are adjacent in memory, and
+// partially written cache lines at run boundaries then meet in one XCD's L2.
+__device__ __forceinline__ int bin_tile_of_block(int b, int nblk) {
+  const int q = nblk / 8;
+  if (b >= 8 * q) return b;  // the last nblk % 8 tiles, in order
+  return (b % 8) * q + b / 8;
+}
+
+// Exclusive prefix sum of v[0..n) in place over the whole workgroup (T threads, each
+// scanning a run of consecutive elements); wsum holds T / 64 partial sums.
+template <int T>
+__device__ inline void block_exclusive_scan(int32_t* v, int n, int32_t* wsum) {
+  const int per = (n + T - 1) / T;
+  const int lo = threadIdx.x * per;
+  const int hi = min(n, lo + per);
+  int32_t own = 0;
+  for (int i = lo; i < hi; ++i) own += v[i];
+  // inclusive scan of the per-thread sums inside the wavefront
+  const int lane = (int)__lane_id();
+  int32_t inc = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += u;
+  }
+  const int wave = threadIdx.x / 64;
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int32_t run = before + inc - own;
+  for (int i = lo; i < hi; ++i) {
+    const int32_t c = v[i];
+    v[i] = run;
+    run += c;
+  }
+  __syncthreads();
+}
+
 // Levels with at most this many bins use the wavefront-aggregated counters.
 constexpr int kFewBins = 16;
 
@@ -111,6 +153,10 @@ __device__ __forceinline__ void bin_of(const BinPlan& bp, int k, int l, uint32_t
 int bin_cshift_for_width(int W);
 void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp);
 int bin_tile_points(const BinPlan& bp, int F, bool hermite);
+// Points (= threads) of a Hermite scatter workgroup: its LDS staging holds one order table's
+// records for every corner of the tile.
+constexpr int hermite_scatter_points(int F) { return F <= 2 ? 256 : F == 4 ? 128 : 64; }
+size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F);
 // LDS of the d-linear scatter workgroup: three per-bin arrays and the pair-record staging.
 size_t dlinear_scatter_lds_bytes(const BinPlan& bp, int d, int F, int tile);
 BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64_t entries_per_point,

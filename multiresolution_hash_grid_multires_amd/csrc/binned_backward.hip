@@ -6,7 +6,9 @@
 // the contributions are instead routed to the workgroup that owns their rows:
 //   1. count   per point tile, histogram of contributions over bins (table, level, chunk
 //              of rows small enough to accumulate in LDS)
-//   2. scan    per bin, exclusive prefix over point tiles (and the bin totals)
+//   2. scan    per bin, exclusive prefix over point tiles (and the bin totals); the counts
+//              are stored tile-major, counts[tile][bin], so every tile writes and reads
+//              its own row contiguously
 //   3. plan    exclusive scan over bins, per-segment bases, work items (bin, entry range)
 //   4. scatter recompute the contributions and write compact entries (local row, values)
 //              to their bin's range
@@ -24,38 +26,50 @@ namespace {
 
 constexpr int64_t kBinChunkPoints = int64_t(1) << 20;
 
-__global__ __launch_bounds__(256) void bin_scan_kernel(int32_t* __restrict__ counts, int32_t nblk,
-                                                       int32_t* __restrict__ totals) {
-  // counts[bin][0..nblk) -> exclusive prefix in place; totals[bin] = sum.  nblk <= 256 * 16.
-  __shared__ int32_t part[256];
-  const int bin = blockIdx.x;
-  int32_t* c = counts + (int64_t)bin * nblk;
-  const int per = (nblk + 255) / 256;
-  const int b0 = threadIdx.x * per;
-  int32_t local[16];
+// counts[tile][bin] -> exclusive prefix over tiles in place; totals[bin] = sum.  The tiles
+// are cut into kScanSegs consecutive segments, one per wavefront of a (64-bin group,
+// segment group) workgroup; a lane owns one bin, so every row access is one coalesced
+// 256-byte run.  First pass: segment sums; second pass: each wavefront adds the sums of the
+// segments before its own and rewrites its rows as running prefixes.
+constexpr int kScanWavesPerBlock = 4;
+constexpr int kScanSegs = 16 * kScanWavesPerBlock;
+
+__device__ __forceinline__ void scan_segment(int nblk, int& r0, int& r1, int& seg) {
+  const int rows = (nblk + kScanSegs - 1) / kScanSegs;
+  seg = blockIdx.y * kScanWavesPerBlock + (int)(threadIdx.x >> 6);
+  r0 = seg * rows;
+  r1 = min(nblk, r0 + rows);
+}
+
+__global__ __launch_bounds__(64 * kScanWavesPerBlock) void bin_scan_sums_kernel(const int32_t* __restrict__ counts,
+                                                                               int32_t nblk, int32_t nbins,
+                                                                               int32_t* __restrict__ seg_sums) {
+  const int bin = blockIdx.x * 64 + (int)(threadIdx.x & 63);
+  if (bin >= nbins) return;
+  int r0, r1, seg;
+  scan_segment(nblk, r0, r1, seg);
   int32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int b = b0 + i;
-    local[i] = (i < per && b < nblk) ? c[b] : 0;
-    s += local[i];
+#pragma unroll 8
+  for (int r = r0; r < r1; ++r) s += counts[(int64_t)r * nbins + bin];
+  seg_sums[(int64_t)seg * nbins + bin] = s;
+}
+
+__global__ __launch_bounds__(64 * kScanWavesPerBlock) void bin_scan_apply_kernel(int32_t* __restrict__ counts,
+                                                                                int32_t nblk, int32_t nbins,
+                                                                                const int32_t* __restrict__ seg_sums,
+                                                                                int32_t* __restrict__ totals) {
+  const int bin = blockIdx.x * 64 + (int)(threadIdx.x & 63);
+  if (bin >= nbins) return;
+  int r0, r1, seg;
+  scan_segment(nblk, r0, r1, seg);
+  int32_t run = 0;
+  for (int j = 0; j < seg; ++j) run += seg_sums[(int64_t)j * nbins + bin];
+  if (seg == kScanSegs - 1) totals[bin] = run + seg_sums[(int64_t)seg * nbins + bin];
+  for (int r = r0; r < r1; ++r) {
+    const int32_t c = counts[(int64_t)r * nbins + bin];
+    counts[(int64_t)r * nbins + bin] = run;
+    run += c;
   }
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int32_t run = part[threadIdx.x] - s;  // exclusive
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int b = b0 + i;
-    if (i < per && b < nblk) c[b] = run;
-    run += local[i];
-  }
-  if (threadIdx.x == 255) totals[bin] = part[255];
 }
 
 __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const int32_t* __restrict__ totals,
@@ -127,21 +141,21 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
       const int32_t e1 = seg0[g + 1] >= nb ? part[1023] : bin_start[seg0[g + 1]];
       st->seg_ebase[g] = e0;
       st->seg_vbase[g] = vb;
-      vb += (int64_t)(e1 - e0) * (bp.records ? 2 + bp.width[0] : bp.width[g / bp.L]);
+      vb += (int64_t)(e1 - e0) * (bp.records ? 2 + bp.width[0] : 1 + bp.width[g / bp.L]);
     }
   }
 }
 
-// Accumulate entries [begin, end) of one segment (rows of W floats) into the LDS chunk:
-// each thread keeps U entries (about 32 value registers) in flight before its LDS atomics.
-// acc holds the chunk component-major (acc[j * plane + row]) so that the W components of
-// one row fall in different LDS banks' rotation and a wavefront's random rows spread over
-// all banks.
+// Accumulate entries [begin, end) of one segment (a chunk-local row stored as the bits of
+// the first float, then the row's W values) into the LDS chunk: each thread keeps U entries
+// (about 32 value registers) in flight before its LDS atomics.  acc holds the chunk
+// component-major (acc[j * plane + row]) so that the W components of one row fall in
+// different LDS banks' rotation and a wavefront's random rows spread over all banks.
 template <int W>
 __device__ __forceinline__ void accumulate_entries(double* __restrict__ acc, int plane,
-                                                   const uint16_t* __restrict__ rows,
                                                    const float* __restrict__ vseg, int32_t ebase,
                                                    int32_t begin, int32_t end) {
+  constexpr int R = W + 1;
   constexpr int U = W >= 32 ? 1 : 32 / W > 8 ? 8 : 32 / W;
   const int T = blockDim.x;
   for (int32_t e0 = begin + (int32_t)threadIdx.x; e0 < end; e0 += T * U) {
@@ -151,8 +165,10 @@ __device__ __forceinline__ void accumulate_entries(double* __restrict__ acc, int
     for (int u = 0; u < U; ++u) {
       const int32_t e = e0 + u * T;
       if (e < end) {
-        r[u] = __builtin_nontemporal_load(rows + e);
-        load_vec_nt<W>(vseg + (int64_t)(e - ebase) * W, val[u]);
+        const float* rec = vseg + (int64_t)(e - ebase) * R;
+        r[u] = (int)__float_as_uint(__builtin_nontemporal_load(rec));
+#pragma unroll
+        for (int j = 0; j < W; ++j) val[u][j] = __builtin_nontemporal_load(rec + 1 + j);
       } else {
         r[u] = -1;
       }
@@ -201,7 +217,6 @@ __device__ __forceinline__ void accumulate_records(double* __restrict__ acc, int
 __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g, const BinPlan bp,
                                                                     BinState* __restrict__ st,
                                                                     const WorkItem* __restrict__ items,
-                                                                    const uint16_t* __restrict__ rows,
                                                                     const float* __restrict__ vals,
                                                                     float* __restrict__ grad) {
   // fp64 accumulator: LDS fp64 atomics run several times faster than fp32 ones on gfx950
@@ -239,15 +254,15 @@ __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g
         default: accumulate_records<8>(acc, plane, vseg, eb, w.begin, w.end); break;
       }
     } else switch (W) {
-      case 1: accumulate_entries<1>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
-      case 2: accumulate_entries<2>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
-      case 3: accumulate_entries<3>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
-      case 4: accumulate_entries<4>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
-      case 6: accumulate_entries<6>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
-      case 8: accumulate_entries<8>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
-      case 12: accumulate_entries<12>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
-      case 16: accumulate_entries<16>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
-      default: accumulate_entries<24>(acc, plane, rows, vseg, eb, w.begin, w.end); break;
+      case 1: accumulate_entries<1>(acc, plane, vseg, eb, w.begin, w.end); break;
+      case 2: accumulate_entries<2>(acc, plane, vseg, eb, w.begin, w.end); break;
+      case 3: accumulate_entries<3>(acc, plane, vseg, eb, w.begin, w.end); break;
+      case 4: accumulate_entries<4>(acc, plane, vseg, eb, w.begin, w.end); break;
+      case 6: accumulate_entries<6>(acc, plane, vseg, eb, w.begin, w.end); break;
+      case 8: accumulate_entries<8>(acc, plane, vseg, eb, w.begin, w.end); break;
+      case 12: accumulate_entries<12>(acc, plane, vseg, eb, w.begin, w.end); break;
+      case 16: accumulate_entries<16>(acc, plane, vseg, eb, w.begin, w.end); break;
+      default: accumulate_entries<24>(acc, plane, vseg, eb, w.begin, w.end); break;
     }
     __syncthreads();
     // flush: element i of the chunk is row i / W, component i % W
@@ -272,7 +287,7 @@ int64_t entries_per_point(int d, int L, bool hermite) {
 int64_t floats_per_point(const BinPlan& bp, int d) {
   if (bp.records) return (int64_t)bp.L * (1 << d) * (2 + bp.width[0]);
   int64_t w = 0;
-  for (int k = 0; k < bp.ntab; ++k) w += bp.width[k];
+  for (int k = 0; k < bp.ntab; ++k) w += 1 + bp.width[k];
   return (int64_t)bp.L * (1 << d) * w;
 }
 
@@ -327,8 +342,15 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
 
 int bin_tile_points(const BinPlan& bp, int F, bool hermite) {
   (void)bp;
-  (void)F;
-  return hermite ? kBinTilePoints : kScatterThreads;  // d-linear scatter: one point per lane
+  // one point per scatter lane
+  return hermite ? hermite_scatter_points(F) : kScatterThreads;
+}
+
+size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F) {
+  const int P = hermite_scatter_points(F);
+  const int rmax = 1 + (d == 3 ? 3 : 2) * F;  // widest order table's record
+  return sizeof(int32_t) * (3 * (size_t)bp.max_seg_bins + P / 64) +
+         (size_t)P * (1 << d) * (sizeof(float) * rmax + sizeof(int32_t));
 }
 
 size_t dlinear_scatter_lds_bytes(const BinPlan& bp, int d, int F, int tile) {
@@ -346,10 +368,10 @@ BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64
   size_t off = 0;
   w.counts = off; off += al(sizeof(int32_t) * (size_t)bp.nbins * w.nblk);
   w.totals = off; off += al(sizeof(int32_t) * (size_t)bp.nbins);
+  w.seg_sums = off; off += al(sizeof(int32_t) * (size_t)bp.nbins * kScanSegs);
   w.state = off; off += al(sizeof(BinState));
   w.bin_start = off; off += al(sizeof(int32_t) * (size_t)(bp.nbins + 1));
   w.items = off; off += al(sizeof(WorkItem) * (size_t)w.max_items);
-  w.rows = off; off += al(bp.records ? 0 : sizeof(uint16_t) * (size_t)entries);
   w.vals = off; off += al(sizeof(float) * (size_t)(chunk_points * fpp));
   w.total = off;
   return w;
@@ -358,8 +380,15 @@ BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64
 hipError_t run_bin_middle(const BinPlan& bp, const BinWorkspace& w, char* ws, hipStream_t s) {
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
   int32_t* totals = reinterpret_cast<int32_t*>(ws + w.totals);
-  hipLaunchKernelGGL(bin_scan_kernel, dim3(bp.nbins), dim3(256), 0, s, counts, w.nblk, totals);
+  int32_t* seg_sums = reinterpret_cast<int32_t*>(ws + w.seg_sums);
+  const dim3 sgrid((unsigned)((bp.nbins + 63) / 64), kScanSegs / kScanWavesPerBlock);
+  hipLaunchKernelGGL(bin_scan_sums_kernel, sgrid, dim3(64 * kScanWavesPerBlock), 0, s, counts, w.nblk, bp.nbins,
+                     seg_sums);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bin_scan_apply_kernel, sgrid, dim3(64 * kScanWavesPerBlock), 0, s, counts, w.nblk, bp.nbins,
+                     seg_sums, totals);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bin_plan_kernel, dim3(1), dim3(1024), 0, s, bp, totals,
                      reinterpret_cast<int32_t*>(ws + w.bin_start), reinterpret_cast<WorkItem*>(ws + w.items),
@@ -371,7 +400,7 @@ hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& 
                           hipStream_t s) {
   hipLaunchKernelGGL(bin_reduce_kernel, dim3(kBinReduceBlocks), dim3(kReduceThreads), 0, s, g, bp,
                      reinterpret_cast<BinState*>(ws + w.state), reinterpret_cast<const WorkItem*>(ws + w.items),
-                     reinterpret_cast<const uint16_t*>(ws + w.rows), reinterpret_cast<const float*>(ws + w.vals),
+                     reinterpret_cast<const float*>(ws + w.vals),
                      grad);
   return hipGetLastError();
 }
@@ -380,7 +409,7 @@ bool binned_fits(const Grid& g, int d, int F, bool hermite) {
   BinPlan bp;
   make_bin_plan(g, d, F, hermite, bp);
   if (bp.nbins > kMaxBins) return false;  // one LDS counter per bin in the count pass
-  if (hermite) return true;
+  if (hermite) return hermite_scatter_lds_bytes(bp, d, F) <= kMaxScatterLds;
   const int tile = bin_tile_points(bp, F, hermite);
   return dlinear_scatter_lds_bytes(bp, d, F, tile) <= kMaxScatterLds;
 }

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
                                                                     const float* __restrict__ x,
                                                                     int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
-  const int blk = blockIdx.x;
+  const int blk = bin_tile_of_block(blockIdx.x, nblk);
   for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) hist[i] = 0;
   __syncthreads();
   const int ppt = tile / kBinThreads;
@@ -248,38 +248,7 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) counts[(int64_t)i * nblk + blk] = hist[i];
-}
-
-// Exclusive prefix sum of v[0..n) in place over the whole workgroup (T threads, each
-// scanning a run of consecutive elements); wsum holds T / 64 partial sums.
-template <int T>
-__device__ void block_exclusive_scan(int32_t* v, int n, int32_t* wsum) {
-  const int per = (n + T - 1) / T;
-  const int lo = threadIdx.x * per;
-  const int hi = min(n, lo + per);
-  int32_t own = 0;
-  for (int i = lo; i < hi; ++i) own += v[i];
-  // inclusive scan of the per-thread sums inside the wavefront
-  const int lane = (int)__lane_id();
-  int32_t inc = own;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t u = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += u;
-  }
-  const int wave = threadIdx.x / 64;
-  if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
-  int32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  int32_t run = before + inc - own;
-  for (int i = lo; i < hi; ++i) {
-    const int32_t c = v[i];
-    v[i] = run;
-    run += c;
-  }
-  __syncthreads();
+  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) counts[(int64_t)blk * bp.nbins + i] = hist[i];
 }
 
 // Binned backward, scatter pass.  One lane per point.  At the start the workgroup turns the
@@ -308,13 +277,13 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
   float* st_rec = reinterpret_cast<float*>(wsum + kScatterThreads / 64);           // [tile*NP*R]
   int32_t* st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)tile * NP * R);  // [tile*NP]
 
-  const int blk = blockIdx.x;
+  const int blk = bin_tile_of_block(blockIdx.x, nblk);
   const int64_t p = (int64_t)blk * tile + threadIdx.x;
   const bool on = p < n;
   const int np = (int)min((int64_t)tile, n - (int64_t)blk * tile);
   for (int i = threadIdx.x; i < nbins; i += kScatterThreads) {
-    const int32_t pre = counts[(int64_t)i * nblk + blk];
-    const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)i * nblk + blk + 1] : totals[i];
+    const int32_t pre = counts[(int64_t)blk * nbins + i];
+    const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)(blk + 1) * nbins + i] : totals[i];
     gstart[i] = bin_start[i] + pre;
     excl[i] = nxt - pre;
   }

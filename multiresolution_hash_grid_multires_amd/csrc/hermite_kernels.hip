@@ -327,6 +327,63 @@ __device__ __forceinline__ void bwd_pair(Sink& sink, const AxisBasis (&ab)[D], c
   sink.template emit<(Y << 1) | 1>(hi);
 }
 
+// Table-K part of bwd_pair: the coefficient gradients of order table K (slots with
+// |alpha| = K) of the x-corner pair (0, Y), lower corner into lo, upper into hi.
+template <int D, int F, int Y, int K>
+__device__ __forceinline__ void bwd_pair_table(const AxisBasis (&ab)[D], const LevelUp<D, F>& u,
+                                               float (&lo)[binom_d(D, K) * F],
+                                               float (&hi)[binom_d(D, K) * F]) {
+  constexpr int c1 = Y & 1;
+  constexpr int c2 = (Y >> 1) & 1;
+  constexpr int NA = 1 << (D - 1);
+  [&]<int... A>(std::integer_sequence<int, A...>) {
+    (([&] {
+       constexpr int a1 = A & 1;
+       constexpr int a2 = (A >> 1) & 1;
+       constexpr int m1 = 2 * c1 + a1;
+       constexpr int m2 = 2 * c2 + a2;
+       constexpr int al0 = (a1 << 1) | (a2 << 2);
+       constexpr int al1 = al0 | 1;
+       constexpr bool want0 = popc(al0) == K, want1 = popc(al1) == K;
+       if constexpr (want0 || want1) {
+         float S[F], S1[F], S2[F];
+         if constexpr (D == 2) {
+           const float w = ab[1].B[m1], wd = ab[1].dB[m1], wdd = ab[1].d2B[m1];
+#pragma unroll
+           for (int f = 0; f < F; ++f) {
+             S[f] = u.v[f] * w + u.g[1][f] * wd + u.h[1][f] * wdd;
+             S1[f] = u.g[0][f] * w;
+             S2[f] = u.h[0][f] * w;
+           }
+         } else {
+           const float b1 = ab[1].B[m1], b2 = ab[2].B[m2];
+           const float w = b1 * b2;
+           const float w1 = ab[1].dB[m1] * b2, w11 = ab[1].d2B[m1] * b2;
+           const float w2 = b1 * ab[2].dB[m2], w22 = b1 * ab[2].d2B[m2];
+#pragma unroll
+           for (int f = 0; f < F; ++f) {
+             S[f] = u.v[f] * w + u.g[1][f] * w1 + u.h[1][f] * w11 + u.g[2][f] * w2 + u.h[2][f] * w22;
+             S1[f] = u.g[0][f] * w;
+             S2[f] = u.h[0][f] * w;
+           }
+         }
+#pragma unroll
+         for (int f = 0; f < F; ++f) {
+           if constexpr (want0) {
+             lo[slot_of(al0) * F + f] = S[f] * ab[0].B[0] + S1[f] * ab[0].dB[0] + S2[f] * ab[0].d2B[0];
+             hi[slot_of(al0) * F + f] = S[f] * ab[0].B[2] + S1[f] * ab[0].dB[2] + S2[f] * ab[0].d2B[2];
+           }
+           if constexpr (want1) {
+             lo[slot_of(al1) * F + f] = S[f] * ab[0].B[1] + S1[f] * ab[0].dB[1] + S2[f] * ab[0].d2B[1];
+             hi[slot_of(al1) * F + f] = S[f] * ab[0].B[3] + S1[f] * ab[0].dB[3] + S2[f] * ab[0].d2B[3];
+           }
+         }
+       }
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, NA>{});
+}
+
 // Backward sink: fp32 atomics straight into the gradient tables.
 template <int D, int F>
 struct AtomicSink {
@@ -337,37 +394,6 @@ struct AtomicSink {
   template <int C>
   __device__ __forceinline__ void emit(CornerRows<D, F>& cr) {
     scatter_corner<D, F, C>(g, keys, base, dense, cr);
-  }
-};
-
-// Backward sink: compact entries into the bins of the binned backward.
-template <int D, int F>
-struct BinSink {
-  const Grid& g;
-  const BinPlan& bp;
-  const CellKeys<D>& keys;
-  int l;
-  int32_t* hist;
-  uint16_t* rows_out;
-  float* vbase[kMaxTables];
-  int32_t ebase[kMaxTables];
-  bool dense[kMaxTables];
-
-  template <int K, int W>
-  __device__ __forceinline__ void put(uint32_t row, const float (&v)[W]) {
-    int32_t bin;
-    uint32_t local;
-    bin_of(bp, K, l, row, bin, local);
-    const int32_t pos = atomicAdd(&hist[bin], 1);
-    rows_out[pos] = (uint16_t)local;
-    store_vec<W>(vbase[K] + (int64_t)(pos - ebase[K]) * W, v);
-  }
-  template <int C>
-  __device__ __forceinline__ void emit(CornerRows<D, F>& cr) {
-    put<0, F>(corner_row<D, C>(keys, dense[0], g.T[0], g.Tmask[0]), cr.r0);
-    put<1, binom_d(D, 1) * F>(corner_row<D, C>(keys, dense[1], g.T[1], g.Tmask[1]), cr.r1);
-    put<2, binom_d(D, 2) * F>(corner_row<D, C>(keys, dense[2], g.T[2], g.Tmask[2]), cr.r2);
-    if constexpr (D == 3) put<3, F>(corner_row<D, C>(keys, dense[3], g.T[3], g.Tmask[3]), cr.r3);
   }
 };
 
@@ -437,77 +463,181 @@ __global__ __launch_bounds__(kBlock) void hermite_backward_kernel(
   }
 }
 
-// Binned backward, count (SCATTER = false) and scatter (SCATTER = true) passes: as the
-// d-linear ones, with one entry per (corner, order table) carrying that table's row.
-template <int D, int F, bool SCATTER>
-__global__ __launch_bounds__(kBinThreads) void hermite_bin_kernel(
-    const Grid g, const BinPlan bp, int64_t n, int32_t nblk, int d2_mode, const float* __restrict__ x,
-    const float* __restrict__ g_gamma, const float* __restrict__ g_dgamma,
-    const float* __restrict__ g_d2gamma, int32_t* __restrict__ counts,
-    const int32_t* __restrict__ bin_start, const BinState* __restrict__ st,
-    uint16_t* __restrict__ rows_out, float* __restrict__ vals_out) {
+// Binned backward, count pass: a workgroup histograms the entries of its tile of `tile`
+// points (one per corner and order table) over all bins in LDS.
+template <int D>
+__global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g, const BinPlan bp, int64_t n,
+                                                                    int32_t tile, int32_t nblk,
+                                                                    const float* __restrict__ x,
+                                                                    int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
-  constexpr int PPT = kBinTilePoints / kBinThreads;
-  const int blk = blockIdx.x;
-  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads)
-    hist[i] = SCATTER ? bin_start[i] + counts[(int64_t)i * nblk + blk] : 0;
+  const int blk = bin_tile_of_block(blockIdx.x, nblk);
+  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) hist[i] = 0;
   __syncthreads();
-  const int64_t p0 = (int64_t)blk * kBinTilePoints + threadIdx.x;
-  // points outer, levels inner: a point's upstream rows are read in one short burst
-  for (int j = 0; j < PPT; ++j) {
-    const int64_t p = p0 + (int64_t)j * kBinThreads;
+  for (int j = threadIdx.x; j < tile; j += kBinThreads) {
+    const int64_t p = (int64_t)blk * tile + j;
     if (p >= n) break;
     float xp[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
     for (int l = 0; l < g.L; ++l) {
-      bool dense[kMaxTables];
+      uint32_t base[D];
+      float t[D];
+      locate<D>(xp, g.N[l], g.Nf[l], base, t);
+      const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
 #pragma unroll
-      for (int k = 0; k < kMaxTables; ++k) dense[k] = (g.dense[k] >> l) & 1u;
-      if constexpr (!SCATTER) {
-        uint32_t base[D];
-        float t[D];
-        locate<D>(xp, g.N[l], g.Nf[l], base, t);
-        const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
+      for (int k = 0; k <= D; ++k) {
+        const bool dense = (g.dense[k] >> l) & 1u;
+        const bool few = bp.seg_bin0[k * bp.L + l + 1] - bp.seg_bin0[k * bp.L + l] <= kFewBins;
         [&]<int... C>(std::integer_sequence<int, C...>) {
           ((
                [&] {
-#pragma unroll
-                 for (int k = 0; k <= D; ++k) {
-                   int32_t bin;
-                   uint32_t local;
-                   bin_of(bp, k, l, corner_row<D, C>(keys, dense[k], g.T[k], g.Tmask[k]), bin, local);
-                   atomicAdd(&hist[bin], 1);
-                 }
+                 int32_t bin;
+                 uint32_t local;
+                 bin_of(bp, k, l, corner_row<D, C>(keys, dense, g.T[k], g.Tmask[k]), bin, local);
+                 if (few) wave_aggregated_add<false>(hist, bin);
+                 else atomicAdd(&hist[bin], 1);
                }()),
            ...);
         }(std::make_integer_sequence<int, 1 << D>{});
-      } else {
-        const LevelUp<D, F> u = load_level_up<D, F>(g, p, l, d2_mode, g_gamma, g_dgamma, g_d2gamma);
-        CellKeys<D> keys;
-        AxisBasis ab[D];
-        level_setup<D>(g, l, xp, keys, ab);
-        BinSink<D, F> sink{g, bp, keys, l, hist, rows_out};
-#pragma unroll
-        for (int k = 0; k < kMaxTables; ++k) {
-          const int sg = k * bp.L + l;
-          const bool used = k <= D;
-          sink.vbase[k] = vals_out + (used ? st->seg_vbase[sg] : 0);
-          sink.ebase[k] = used ? st->seg_ebase[sg] : 0;
-          sink.dense[k] = dense[k];
-        }
-        bwd_pair<D, F, 0>(sink, ab, u);
-        bwd_pair<D, F, 1>(sink, ab, u);
-        if constexpr (D == 3) {
-          bwd_pair<D, F, 2>(sink, ab, u);
-          bwd_pair<D, F, 3>(sink, ab, u);
-        }
       }
     }
   }
-  if constexpr (!SCATTER) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) counts[(int64_t)i * nblk + blk] = hist[i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) counts[(int64_t)blk * bp.nbins + i] = hist[i];
+}
+
+// LDS layout of the Hermite scatter workgroup (P points).
+template <int D, int F, int P>
+struct HScatterLds {
+  static constexpr int NC = 1 << D;
+  static constexpr int RMAX = 1 + binom_d(D, 1) * F;  // widest record (orders 1 and 2)
+  int32_t* gstart;  // [max_seg_bins] global slot of this tile's run in each bin of the segment
+  int32_t* excl;    // [max_seg_bins] exclusive prefix of the tile's counts
+  int32_t* lcur;    // [max_seg_bins] cursors
+  int32_t* wsum;    // [P / 64]
+  float* st_rec;    // [P * NC * RMAX]
+  int32_t* st_pos;  // [P * NC]
+  __device__ HScatterLds(int32_t* lds, int mb) {
+    gstart = lds;
+    excl = lds + mb;
+    lcur = lds + 2 * mb;
+    wsum = lds + 3 * mb;
+    st_rec = reinterpret_cast<float*>(wsum + P / 64);
+    st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)P * NC * RMAX);
+  }
+};
+
+// Stage the two records of corner pair (0, Y) for order table K.
+template <int D, int F, int K, int Y>
+__device__ __forceinline__ void stage_pair(const Grid& g, const BinPlan& bp, int l, bool dense, bool few,
+                                           int32_t b0, const CellKeys<D>& keys, const AxisBasis (&ab)[D],
+                                           const LevelUp<D, F>& u, int32_t* lcur, const int32_t* excl,
+                                           const int32_t* gstart, float* st_rec, int32_t* st_pos) {
+  constexpr int W = binom_d(D, K) * F;
+  constexpr int R = W + 1;
+  float v[2][W];
+  bwd_pair_table<D, F, Y, K>(ab, u, v[0], v[1]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int32_t bin;
+    uint32_t local;
+    const uint32_t row = h ? corner_row<D, (Y << 1) | 1>(keys, dense, g.T[K], g.Tmask[K])
+                           : corner_row<D, (Y << 1)>(keys, dense, g.T[K], g.Tmask[K]);
+    bin_of(bp, K, l, row, bin, local);
+    const int i = bin - b0;
+    const int32_t slot = few ? wave_aggregated_add<true>(lcur, i) : atomicAdd(&lcur[i], 1);
+    float* rec = st_rec + (int64_t)slot * R;
+    rec[0] = __uint_as_float(local);
+#pragma unroll
+    for (int j = 0; j < W; ++j) rec[1 + j] = v[h][j];
+    st_pos[slot] = gstart[i] + (slot - excl[i]);
+  }
+}
+
+// One (level, order table K) phase of the scatter workgroup.
+template <int D, int F, int P, int K>
+__device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, int l, int blk, int nblk, bool on,
+                                              int np, const CellKeys<D>& keys, const AxisBasis (&ab)[D],
+                                              const LevelUp<D, F>& u, const int32_t* __restrict__ counts,
+                                              const int32_t* __restrict__ totals,
+                                              const int32_t* __restrict__ bin_start,
+                                              const BinState* __restrict__ st, float* __restrict__ vals_out,
+                                              const HScatterLds<D, F, P>& sh) {
+  constexpr int W = binom_d(D, K) * F;
+  constexpr int R = W + 1;
+  constexpr int NC = 1 << D;
+  const int sg = K * bp.L + l;
+  const int32_t b0 = bp.seg_bin0[sg];
+  const int nb = bp.seg_bin0[sg + 1] - b0;
+  const bool dense = (g.dense[K] >> l) & 1u;
+  const bool few = nb <= kFewBins;
+  for (int i = threadIdx.x; i < nb; i += P) {
+    const int32_t pre = counts[(int64_t)blk * bp.nbins + b0 + i];
+    const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)(blk + 1) * bp.nbins + b0 + i] : totals[b0 + i];
+    sh.gstart[i] = bin_start[b0 + i] + pre;
+    sh.excl[i] = nxt - pre;
+  }
+  __syncthreads();
+  block_exclusive_scan<P>(sh.excl, nb, sh.wsum);
+  for (int i = threadIdx.x; i < nb; i += P) sh.lcur[i] = sh.excl[i];
+  __syncthreads();
+  if (on) {
+    stage_pair<D, F, K, 0>(g, bp, l, dense, few, b0, keys, ab, u, sh.lcur, sh.excl, sh.gstart, sh.st_rec, sh.st_pos);
+    stage_pair<D, F, K, 1>(g, bp, l, dense, few, b0, keys, ab, u, sh.lcur, sh.excl, sh.gstart, sh.st_rec, sh.st_pos);
+    if constexpr (D == 3) {
+      stage_pair<D, F, K, 2>(g, bp, l, dense, few, b0, keys, ab, u, sh.lcur, sh.excl, sh.gstart, sh.st_rec,
+                             sh.st_pos);
+      stage_pair<D, F, K, 3>(g, bp, l, dense, few, b0, keys, ab, u, sh.lcur, sh.excl, sh.gstart, sh.st_rec,
+                             sh.st_pos);
+    }
+  }
+  __syncthreads();
+  const int32_t ebase = st->seg_ebase[sg];
+  float* vseg = vals_out + st->seg_vbase[sg];
+  const int32_t words = np * NC * R;
+  for (int32_t e = threadIdx.x; e < words; e += P) {
+    const int32_t q = e / R, j = e - q * R;
+    vseg[(int64_t)(sh.st_pos[q] - ebase) * R + j] = sh.st_rec[e];
+  }
+  __syncthreads();
+}
+
+// Binned backward, scatter pass.  One lane per point of a P-point tile.  Per level and
+// order table K, the tile's records {local row, W values} are computed (table K's part of
+// the pair reverse), sorted by bin in LDS (slots from the tile's exclusive prefix of its
+// per-bin counts) and copied out as flat words: consecutive lanes write consecutive words
+// of each bin's contiguous run, so lines are written whole apart from run ends.
+template <int D, int F, int P>
+__global__ __launch_bounds__(P) void hermite_scatter_kernel(
+    const Grid g, const BinPlan bp, int64_t n, int32_t nblk, int d2_mode, const float* __restrict__ x,
+    const float* __restrict__ g_gamma, const float* __restrict__ g_dgamma,
+    const float* __restrict__ g_d2gamma, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
+    const BinState* __restrict__ st, float* __restrict__ vals_out) {
+  extern __shared__ int32_t lds[];
+  const HScatterLds<D, F, P> sh(lds, bp.max_seg_bins);
+  const int blk = bin_tile_of_block(blockIdx.x, nblk);
+  const int64_t p = (int64_t)blk * P + threadIdx.x;
+  const bool on = p < n;
+  const int np = (int)min((int64_t)P, n - (int64_t)blk * P);
+  float xp[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) xp[i] = on ? x[p * D + i] : 0.0f;
+  for (int l = 0; l < g.L; ++l) {
+    LevelUp<D, F> u;
+    CellKeys<D> keys;
+    AxisBasis ab[D];
+    if (on) {
+      u = load_level_up<D, F>(g, p, l, d2_mode, g_gamma, g_dgamma, g_d2gamma);
+      level_setup<D>(g, l, xp, keys, ab);
+    }
+    scatter_table<D, F, P, 0>(g, bp, l, blk, nblk, on, np, keys, ab, u, counts, totals, bin_start, st, vals_out, sh);
+    scatter_table<D, F, P, 1>(g, bp, l, blk, nblk, on, np, keys, ab, u, counts, totals, bin_start, st, vals_out, sh);
+    scatter_table<D, F, P, 2>(g, bp, l, blk, nblk, on, np, keys, ab, u, counts, totals, bin_start, st, vals_out, sh);
+    if constexpr (D == 3)
+      scatter_table<D, F, P, 3>(g, bp, l, blk, nblk, on, np, keys, ab, u, counts, totals, bin_start, st, vals_out,
+                                sh);
   }
 }
 
@@ -516,18 +646,24 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
                       bool scatter, int64_t n, const float* x, const float* gg, const float* gd,
                       const float* g2, hipStream_t s) {
   const dim3 grid((unsigned)w.nblk);
-  const size_t lds = sizeof(int32_t) * (size_t)bp.nbins;
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
+  if (!scatter) {
+    hipLaunchKernelGGL((hermite_count_kernel<D>), grid, dim3(kBinThreads), sizeof(int32_t) * (size_t)bp.nbins, s,
+                       g, bp, n, w.tile, w.nblk, x, counts);
+    return hipGetLastError();
+  }
+  constexpr int P = hermite_scatter_points(F);
+  if (w.tile != P) return hipErrorInvalidValue;
+  const size_t lds = hermite_scatter_lds_bytes(bp, D, F);
+  const int32_t* totals = reinterpret_cast<const int32_t*>(ws + w.totals);
   const int32_t* bin_start = reinterpret_cast<const int32_t*>(ws + w.bin_start);
   const BinState* st = reinterpret_cast<const BinState*>(ws + w.state);
-  uint16_t* rows = reinterpret_cast<uint16_t*>(ws + w.rows);
   float* vals = reinterpret_cast<float*>(ws + w.vals);
-  if (scatter)
-    hipLaunchKernelGGL((hermite_bin_kernel<D, F, true>), grid, dim3(kBinThreads), lds, s, g, bp, n, w.nblk,
-                       d2_mode, x, gg, gd, g2, counts, bin_start, st, rows, vals);
-  else
-    hipLaunchKernelGGL((hermite_bin_kernel<D, F, false>), grid, dim3(kBinThreads), lds, s, g, bp, n, w.nblk,
-                       d2_mode, x, gg, gd, g2, counts, bin_start, st, rows, vals);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hermite_scatter_kernel<D, F, P>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((hermite_scatter_kernel<D, F, P>), grid, dim3(P), lds, s, g, bp, n, w.nblk, d2_mode, x, gg, gd,
+                     g2, counts, totals, bin_start, st, vals);
   return hipGetLastError();
 }
 
