@@ -33,6 +33,11 @@ struct BinPlan {
   int32_t width[kMaxTables];    // floats per row of table k
   int32_t cshift[kMaxTables];   // log2 rows per chunk of table k (power-of-two chunks)
   uint32_t pair_mask;           // d-linear: bit l set = level l uses x-corner pair records
+  // Hermite with equal table sizes: every order table maps a vertex to the same row, so the
+  // count pass histograms rows once per level in chunks of 2^fine_shift rows (the narrowest
+  // chunk) and derives each table's bin counts by summing consecutive fine bins.  -1: off.
+  int32_t fine_shift;
+  int32_t fine_bin0[kMaxLevels + 1];
   int32_t seg_chunk[kMaxSeg];   // rows per chunk of segment s
   int32_t seg_bin0[kMaxSeg + 1];
 };

@@ -338,6 +338,24 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
   }
   bp.seg_bin0[bp.nseg] = bin;
   bp.nbins = bin;
+  bp.fine_shift = -1;
+  if (hermite) {
+    bool uniform = true;
+    int fine = bp.cshift[0];
+    for (int k = 1; k < bp.ntab; ++k) {
+      uniform = uniform && g.T[k] == g.T[0];
+      if (bp.cshift[k] < fine) fine = bp.cshift[k];
+    }
+    if (uniform) {
+      bp.fine_shift = fine;
+      int32_t fb = 0;
+      for (int l = 0; l < g.L; ++l) {
+        bp.fine_bin0[l] = fb;
+        fb += (int32_t)((seg_rows(g, d, 0, l) + ((int64_t)1 << fine) - 1) >> fine);
+      }
+      bp.fine_bin0[g.L] = fb;
+    }
+  }
 }
 
 int bin_tile_points(const BinPlan& bp, int F, bool hermite) {
@@ -408,7 +426,8 @@ hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& 
 bool binned_fits(const Grid& g, int d, int F, bool hermite) {
   BinPlan bp;
   make_bin_plan(g, d, F, hermite, bp);
-  if (bp.nbins > kMaxBins) return false;  // one LDS counter per bin in the count pass
+  const int32_t count_bins = bp.fine_shift >= 0 ? bp.fine_bin0[g.L] : bp.nbins;
+  if (bp.nbins > kMaxBins || count_bins > kMaxBins) return false;  // LDS counters of the count pass
   if (hermite) return hermite_scatter_lds_bytes(bp, d, F) <= kMaxScatterLds;
   const int tile = bin_tile_points(bp, F, hermite);
   return dlinear_scatter_lds_bytes(bp, d, F, tile) <= kMaxScatterLds;

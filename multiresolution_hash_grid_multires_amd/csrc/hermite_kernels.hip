@@ -77,6 +77,15 @@ struct CornerRows {
   float r3[(D == 3 ? 1 : 1) * F];  // order-3 row (D = 3 only)
 
   template <int ALPHA>
+  __device__ __forceinline__ float get(int f) const {
+    constexpr int k = popc(ALPHA);
+    constexpr int s = slot_of(ALPHA);
+    if constexpr (k == 0) return r0[f];
+    else if constexpr (k == 1) return r1[s * F + f];
+    else if constexpr (k == 2) return r2[s * F + f];
+    else return r3[f];
+  }
+  template <int ALPHA>
   __device__ __forceinline__ float& at(int f) {
     constexpr int k = popc(ALPHA);
     constexpr int s = slot_of(ALPHA);
@@ -160,8 +169,8 @@ __device__ __forceinline__ void fwd_pair(const Grid& g, const CellKeys<D>& keys,
 #pragma unroll
        for (int f = 0; f < F; ++f) {
          // contraction over m0 = 2 c0 + a0
-         const float t00 = lo.template at<al0>(f), t01 = lo.template at<al1>(f);
-         const float t10 = hi.template at<al0>(f), t11 = hi.template at<al1>(f);
+         const float t00 = lo.template get<al0>(f), t01 = lo.template get<al1>(f);
+         const float t10 = hi.template get<al0>(f), t11 = hi.template get<al1>(f);
          S[f] = ab[0].B[0] * t00 + ab[0].B[1] * t01 + ab[0].B[2] * t10 + ab[0].B[3] * t11;
          S1[f] = ab[0].dB[0] * t00 + ab[0].dB[1] * t01 + ab[0].dB[2] * t10 + ab[0].dB[3] * t11;
          S2[f] = ab[0].d2B[0] * t00 + ab[0].d2B[1] * t01 + ab[0].d2B[2] * t10 + ab[0].d2B[3] * t11;
@@ -464,7 +473,9 @@ __global__ __launch_bounds__(kBlock) void hermite_backward_kernel(
 }
 
 // Binned backward, count pass: a workgroup histograms the entries of its tile of `tile`
-// points (one per corner and order table) over all bins in LDS.
+// points (one per corner and order table) over all bins in LDS.  With equal table sizes
+// (bp.fine_shift >= 0) the rows are histogrammed once per level in fine chunks and each
+// table's bin counts are sums of consecutive fine bins.
 template <int D>
 __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g, const BinPlan bp, int64_t n,
                                                                     int32_t tile, int32_t nblk,
@@ -472,7 +483,9 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
                                                                     int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
-  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) hist[i] = 0;
+  const bool fine = bp.fine_shift >= 0;
+  const int nh = fine ? bp.fine_bin0[g.L] : bp.nbins;
+  for (int i = threadIdx.x; i < nh; i += kBinThreads) hist[i] = 0;
   __syncthreads();
   for (int j = threadIdx.x; j < tile; j += kBinThreads) {
     const int64_t p = (int64_t)blk * tile + j;
@@ -485,6 +498,21 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
       float t[D];
       locate<D>(xp, g.N[l], g.Nf[l], base, t);
       const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
+      if (fine) {
+        const bool dense = (g.dense[0] >> l) & 1u;
+        const bool few = bp.fine_bin0[l + 1] - bp.fine_bin0[l] <= kFewBins;
+        [&]<int... C>(std::integer_sequence<int, C...>) {
+          ((
+               [&] {
+                 const int32_t bin =
+                     bp.fine_bin0[l] + (int32_t)(corner_row<D, C>(keys, dense, g.T[0], g.Tmask[0]) >> bp.fine_shift);
+                 if (few) wave_aggregated_add<false>(hist, bin);
+                 else atomicAdd(&hist[bin], 1);
+               }()),
+           ...);
+        }(std::make_integer_sequence<int, 1 << D>{});
+        continue;
+      }
 #pragma unroll
       for (int k = 0; k <= D; ++k) {
         const bool dense = (g.dense[k] >> l) & 1u;
@@ -504,7 +532,24 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) counts[(int64_t)blk * bp.nbins + i] = hist[i];
+  int32_t* row = counts + (int64_t)blk * bp.nbins;
+  if (!fine) {
+    for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) row[i] = hist[i];
+    return;
+  }
+  for (int sg = 0; sg < bp.nseg; ++sg) {
+    const int k = sg / bp.L, l = sg % bp.L;
+    const int ratio_shift = bp.cshift[k] - bp.fine_shift;
+    const int32_t f0 = bp.fine_bin0[l], f1 = bp.fine_bin0[l + 1];
+    const int32_t b0 = bp.seg_bin0[sg], nb = bp.seg_bin0[sg + 1] - b0;
+    for (int jb = threadIdx.x; jb < nb; jb += kBinThreads) {
+      const int32_t lo = f0 + (jb << ratio_shift);
+      const int32_t hi = min(f1, f0 + ((jb + 1) << ratio_shift));
+      int32_t c = 0;
+      for (int i = lo; i < hi; ++i) c += hist[i];
+      row[b0 + jb] = c;
+    }
+  }
 }
 
 // LDS layout of the Hermite scatter workgroup (P points).
@@ -648,7 +693,8 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   const dim3 grid((unsigned)w.nblk);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
   if (!scatter) {
-    hipLaunchKernelGGL((hermite_count_kernel<D>), grid, dim3(kBinThreads), sizeof(int32_t) * (size_t)bp.nbins, s,
+    const size_t hist = sizeof(int32_t) * (size_t)(bp.fine_shift >= 0 ? bp.fine_bin0[g.L] : bp.nbins);
+    hipLaunchKernelGGL((hermite_count_kernel<D>), grid, dim3(kBinThreads), hist, s,
                        g, bp, n, w.tile, w.nblk, x, counts);
     return hipGetLastError();
   }

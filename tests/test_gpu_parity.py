@@ -224,6 +224,24 @@ def test_feature_widths(orc, kind, F):  # both backward paths
         _grad_close(_gpu_backward(spec, x, ups, lay["n_params"], path), ref, lay, BWD_TOL)
 
 
+@pytest.mark.parametrize("T", [[1000, 3001, 777, 5], [1 << 12, 1 << 13, 1 << 11, 1 << 12]])
+def test_hermite_unequal_tables(orc, T):
+    # order tables of different sizes (dense on different levels, modulo and mask hashing):
+    # the count pass histograms every table separately
+    spec = {"d": 3, "L": 4, "F": 2, "kind": "hermite", "T": T, "n_min": 8, "n_max": 64, "d2_mode": "diag"}
+    lay = orc.layout(spec)
+    rng = np.random.default_rng(sum(T))
+    params = rng.standard_normal(lay["n_params"]).astype(np.float32)
+    x = rng.random((3000, 3), dtype=np.float32)
+    got = _gpu_forward(spec, x, params)
+    for name, r in zip(("gamma", "dgamma", "d2gamma"), orc.forward(spec, x, params)):
+        _blocks_close(got[name], r, spec, FWD_TOL, name)
+    ups = [u.astype(np.float32) for u in (rng.standard_normal(s) for s in _upstream_shapes(spec, 3000))]
+    ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
+    for path in PATHS:
+        _grad_close(_gpu_backward(spec, x, ups, lay["n_params"], path), ref, lay, BWD_TOL)
+
+
 # The binned d-linear backward writes one record per x-corner pair where both corners fall
 # in one reduction chunk, and one record per corner elsewhere.  With F = 8 a chunk holds
 # 1024 rows, so these grids take every branch:
