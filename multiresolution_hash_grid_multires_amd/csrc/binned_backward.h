@@ -24,8 +24,9 @@ constexpr size_t kMaxScatterLds = 150 * 1024;     // of the 160 KB LDS of a gfx9
 // the chunk-local row of the x-corner pair's lower (c0 = 0) corner in the low 16 bits and
 // the upper corner's in the high 16 bits (0xFFFF: a single corner); the lower row receives
 // (1 - t) * aG and the upper t * aG.  Entries of Hermite segments are {uint32 local row,
-// float v[W]}: the row's W values.  Either way the row index travels as the bits of the
-// record's first float, so every entry is written and read as one contiguous record.
+// float v[W]} (hermite_rec_width(W) floats).  Either way the row index travels
+// as the bits of the record's first float, so every entry is written and read as one
+// contiguous record.
 struct BinPlan {
   int32_t d, L, ntab, nseg, nbins;
   int32_t records;              // 1: d-linear records (2 + F floats); 0: Hermite (1 + W floats)
@@ -41,6 +42,11 @@ struct BinPlan {
   int32_t seg_chunk[kMaxSeg];   // rows per chunk of segment s
   int32_t seg_bin0[kMaxSeg + 1];
 };
+
+// Floats per Hermite record of a W-wide row: the row word and the W values.
+__host__ __device__ constexpr int hermite_rec_width(int W) { return W + 1; }
+// Value floats of every segment start on a 128-byte boundary.
+constexpr int64_t kSegAlignFloats = 32;
 
 struct WorkItem {
   int32_t bin, seg, begin, end, split;
@@ -58,7 +64,7 @@ struct BinWorkspace {
   int32_t tile;   // points per count / scatter workgroup
   int32_t nblk;
   int64_t max_items;
-  size_t counts, totals, seg_sums, state, bin_start, items, vals, total;
+  size_t counts, totals, seg_sums, state, bin_start, items, vals, ups, total;
 };
 
 __host__ __device__ inline int64_t seg_rows(const Grid& g, int d, int k, int l) {

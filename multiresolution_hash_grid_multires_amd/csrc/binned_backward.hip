@@ -141,7 +141,8 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
       const int32_t e1 = seg0[g + 1] >= nb ? part[1023] : bin_start[seg0[g + 1]];
       st->seg_ebase[g] = e0;
       st->seg_vbase[g] = vb;
-      vb += (int64_t)(e1 - e0) * (bp.records ? 2 + bp.width[0] : 1 + bp.width[g / bp.L]);
+      vb += (int64_t)(e1 - e0) * (bp.records ? 2 + bp.width[0] : hermite_rec_width(bp.width[g / bp.L]));
+      vb = (vb + kSegAlignFloats - 1) / kSegAlignFloats * kSegAlignFloats;
     }
   }
 }
@@ -155,20 +156,18 @@ template <int W>
 __device__ __forceinline__ void accumulate_entries(double* __restrict__ acc, int plane,
                                                    const float* __restrict__ vseg, int32_t ebase,
                                                    int32_t begin, int32_t end) {
-  constexpr int R = W + 1;
+  constexpr int R = hermite_rec_width(W);
   constexpr int U = W >= 32 ? 1 : 32 / W > 8 ? 8 : 32 / W;
   const int T = blockDim.x;
   for (int32_t e0 = begin + (int32_t)threadIdx.x; e0 < end; e0 += T * U) {
     int r[U];
-    float val[U][W];
+    float rec[U][R];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int32_t e = e0 + u * T;
       if (e < end) {
-        const float* rec = vseg + (int64_t)(e - ebase) * R;
-        r[u] = (int)__float_as_uint(__builtin_nontemporal_load(rec));
-#pragma unroll
-        for (int j = 0; j < W; ++j) val[u][j] = __builtin_nontemporal_load(rec + 1 + j);
+        load_vec_nt<R>(vseg + (int64_t)(e - ebase) * R, rec[u]);
+        r[u] = (int)__float_as_uint(rec[u][0]);
       } else {
         r[u] = -1;
       }
@@ -177,7 +176,7 @@ __device__ __forceinline__ void accumulate_entries(double* __restrict__ acc, int
     for (int u = 0; u < U; ++u)
       if (r[u] >= 0)
 #pragma unroll
-        for (int j = 0; j < W; ++j) atomicAdd(&acc[j * plane + r[u]], (double)val[u][j]);
+        for (int j = 0; j < W; ++j) atomicAdd(&acc[j * plane + r[u]], (double)rec[u][1 + j]);
   }
 }
 
@@ -287,7 +286,7 @@ int64_t entries_per_point(int d, int L, bool hermite) {
 int64_t floats_per_point(const BinPlan& bp, int d) {
   if (bp.records) return (int64_t)bp.L * (1 << d) * (2 + bp.width[0]);
   int64_t w = 0;
-  for (int k = 0; k < bp.ntab; ++k) w += 1 + bp.width[k];
+  for (int k = 0; k < bp.ntab; ++k) w += hermite_rec_width(bp.width[k]);
   return (int64_t)bp.L * (1 << d) * w;
 }
 
@@ -366,8 +365,8 @@ int bin_tile_points(const BinPlan& bp, int F, bool hermite) {
 
 size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F) {
   const int P = hermite_scatter_points(F);
-  const int rmax = 1 + (d == 3 ? 3 : 2) * F;  // widest order table's record
-  return sizeof(int32_t) * (3 * (size_t)bp.max_seg_bins + P / 64) +
+  const int rmax = hermite_rec_width((d == 3 ? 3 : 2) * F);  // widest order table's record
+  return sizeof(int32_t) * (3 * (size_t)bp.max_seg_bins + P / 64 + 3) +
          (size_t)P * (1 << d) * (sizeof(float) * rmax + sizeof(int32_t));
 }
 
@@ -390,7 +389,9 @@ BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64
   w.state = off; off += al(sizeof(BinState));
   w.bin_start = off; off += al(sizeof(int32_t) * (size_t)(bp.nbins + 1));
   w.items = off; off += al(sizeof(WorkItem) * (size_t)w.max_items);
-  w.vals = off; off += al(sizeof(float) * (size_t)(chunk_points * fpp));
+  w.vals = off; off += al(sizeof(float) * (size_t)(chunk_points * fpp + bp.nseg * kSegAlignFloats));
+  // Hermite: the chunk's upstream rearranged level-major, [L][point][1 + 2d][F] at most
+  w.ups = off; off += al(bp.records ? 0 : sizeof(float) * (size_t)chunk_points * bp.L * (1 + 2 * bp.d) * bp.width[0]);
   w.total = off;
   return w;
 }

@@ -16,6 +16,8 @@
 // Dx^alpha_i scaling and the N_l chain-rule factors, so no per-term power or product chain
 // is evaluated.  Corners are visited in x-adjacent pairs (the axis-0 contraction needs
 // exactly one pair), which bounds the live coefficient registers to 2 * 2^d * F.
+#include <algorithm>
+
 #include "binned_backward.h"
 #include "hashenc_internal.h"
 #include "vec_io.h"
@@ -442,6 +444,100 @@ __device__ __forceinline__ LevelUp<D, F> load_level_up(const Grid& g, int64_t p,
   return u;
 }
 
+// Upstream of the binned scatter, rearranged level-major: U[l][p][m][F] with components
+// m = value, d gradient components, then the d diagonal second derivatives (d2_mode
+// diagonal) or the one Laplacian.  One workgroup owns P consecutive points: it reads their
+// rows of every upstream array (contiguous runs) into LDS and writes each level's
+// P * M * F floats as one contiguous run, so the scatter, which runs level by level, reads
+// each level's upstream once and in whole lines instead of 8 bytes from every point's row
+// per level.
+template <int F, int D, int M>
+__global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t L, int64_t n, int32_t P,
+                                                                         const float* __restrict__ gg,
+                                                                         const float* __restrict__ gd,
+                                                                         const float* __restrict__ g2,
+                                                                         float* __restrict__ U) {
+  // LDS holds each point's upstream already in output order: tile[i * pitch + l * M * F +
+  // m * F + f], so the write phase reads consecutive words.
+  extern __shared__ float tile[];
+  constexpr int MF = M * F;
+  constexpr int D2 = M - 1 - D;  // second-derivative components (d or 1)
+  const int LF = L * F;
+  const int pitch = L * MF + 1;
+  const int64_t p0 = (int64_t)blockIdx.x * P;
+  const int np = (int)min((int64_t)P, n - p0);
+  // read phase: one thread per (point, component) row of L*F floats, read with independent
+  // 16-byte loads when rows are 16-byte aligned
+  for (int row = threadIdx.x; row < np * M; row += kBlock) {
+    const int i = row / M, m = row - i * M;
+    const int64_t p = p0 + i;
+    const float* src = m == 0 ? (gg ? gg + p * LF : nullptr)
+                     : m <= D ? (gd ? gd + (p * D + (m - 1)) * LF : nullptr)
+                              : (g2 ? g2 + (p * D2 + (m - 1 - D)) * LF : nullptr);
+    float* t = tile + i * pitch + m * F;
+    if ((LF & 3) == 0) {
+      for (int c = 0; c < LF; c += 4) {
+        const float4 v = src ? *reinterpret_cast<const float4*>(src + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int l = (c + j) / F, f = (c + j) - l * F;
+          t[l * MF + f] = e[j];
+        }
+      }
+    } else {
+      for (int c = 0; c < LF; ++c) {
+        const int l = c / F, f = c - l * F;
+        t[l * MF + f] = src ? src[c] : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+  for (int l = 0; l < L; ++l) {
+    float* dst = U + ((int64_t)l * n + p0) * MF;
+    for (int e = threadIdx.x; e < np * MF; e += kBlock) {
+      const int i = e / MF, q = e - i * MF;
+      dst[e] = tile[i * pitch + l * MF + q];
+    }
+  }
+}
+
+// Upstream of one point at one level from the level-major copy (the Laplacian upstream is
+// the same for every diagonal term).
+template <int D, int F>
+__device__ __forceinline__ LevelUp<D, F> load_level_up_lm(const float* __restrict__ U, int64_t n, int64_t p, int l,
+                                                          bool diag) {
+  constexpr int MD = 1 + 2 * D;
+  LevelUp<D, F> u;
+  if (diag) {
+    float v[MD * F];
+    load_vec<MD * F>(U + ((int64_t)l * n + p) * MD * F, v);
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      u.v[f] = v[f];
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        u.g[i][f] = v[(1 + i) * F + f];
+        u.h[i][f] = v[(1 + D + i) * F + f];
+      }
+    }
+  } else {
+    constexpr int ML = 2 + D;
+    float v[ML * F];
+    load_vec<ML * F>(U + ((int64_t)l * n + p) * ML * F, v);
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      u.v[f] = v[f];
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        u.g[i][f] = v[(1 + i) * F + f];
+        u.h[i][f] = v[(1 + D) * F + f];
+      }
+    }
+  }
+  return u;
+}
+
 template <int D, int F>
 __global__ __launch_bounds__(kBlock) void hermite_backward_kernel(
     const Grid g, int64_t n, int d2_mode, const float* __restrict__ x,
@@ -556,7 +652,7 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
 template <int D, int F, int P>
 struct HScatterLds {
   static constexpr int NC = 1 << D;
-  static constexpr int RMAX = 1 + binom_d(D, 1) * F;  // widest record (orders 1 and 2)
+  static constexpr int RMAX = hermite_rec_width(binom_d(D, 1) * F);  // widest record (orders 1 and 2)
   int32_t* gstart;  // [max_seg_bins] global slot of this tile's run in each bin of the segment
   int32_t* excl;    // [max_seg_bins] exclusive prefix of the tile's counts
   int32_t* lcur;    // [max_seg_bins] cursors
@@ -568,7 +664,7 @@ struct HScatterLds {
     excl = lds + mb;
     lcur = lds + 2 * mb;
     wsum = lds + 3 * mb;
-    st_rec = reinterpret_cast<float*>(wsum + P / 64);
+    st_rec = reinterpret_cast<float*>(lds + ((3 * mb + P / 64 + 3) & ~3));  // 16-byte aligned
     st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)P * NC * RMAX);
   }
 };
@@ -580,7 +676,7 @@ __device__ __forceinline__ void stage_pair(const Grid& g, const BinPlan& bp, int
                                            const LevelUp<D, F>& u, int32_t* lcur, const int32_t* excl,
                                            const int32_t* gstart, float* st_rec, int32_t* st_pos) {
   constexpr int W = binom_d(D, K) * F;
-  constexpr int R = W + 1;
+  constexpr int R = hermite_rec_width(W);
   float v[2][W];
   bwd_pair_table<D, F, Y, K>(ab, u, v[0], v[1]);
 #pragma unroll
@@ -592,10 +688,11 @@ __device__ __forceinline__ void stage_pair(const Grid& g, const BinPlan& bp, int
     bin_of(bp, K, l, row, bin, local);
     const int i = bin - b0;
     const int32_t slot = few ? wave_aggregated_add<true>(lcur, i) : atomicAdd(&lcur[i], 1);
-    float* rec = st_rec + (int64_t)slot * R;
+    float rec[R];
     rec[0] = __uint_as_float(local);
 #pragma unroll
     for (int j = 0; j < W; ++j) rec[1 + j] = v[h][j];
+    store_vec<R>(st_rec + (int64_t)slot * R, rec);
     st_pos[slot] = gstart[i] + (slot - excl[i]);
   }
 }
@@ -610,7 +707,7 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
                                               const BinState* __restrict__ st, float* __restrict__ vals_out,
                                               const HScatterLds<D, F, P>& sh) {
   constexpr int W = binom_d(D, K) * F;
-  constexpr int R = W + 1;
+  constexpr int R = hermite_rec_width(W);
   constexpr int NC = 1 << D;
   const int sg = K * bp.L + l;
   const int32_t b0 = bp.seg_bin0[sg];
@@ -640,10 +737,14 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
   __syncthreads();
   const int32_t ebase = st->seg_ebase[sg];
   float* vseg = vals_out + st->seg_vbase[sg];
-  const int32_t words = np * NC * R;
-  for (int32_t e = threadIdx.x; e < words; e += P) {
-    const int32_t q = e / R, j = e - q * R;
-    vseg[(int64_t)(sh.st_pos[q] - ebase) * R + j] = sh.st_rec[e];
+  // copy out in pieces of V floats (as wide as the record width's alignment allows)
+  constexpr int V = R % 4 == 0 ? 4 : R % 2 == 0 ? 2 : 1;
+  const int32_t pieces = np * NC * (R / V);
+  for (int32_t e = threadIdx.x; e < pieces; e += P) {
+    const int32_t q = e / (R / V), j = (e - q * (R / V)) * V;
+    float v[V];
+    load_vec<V>(sh.st_rec + (int64_t)q * R + j, v);
+    store_vec<V>(vseg + (int64_t)(sh.st_pos[q] - ebase) * R + j, v);
   }
   __syncthreads();
 }
@@ -655,9 +756,8 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
 // of each bin's contiguous run, so lines are written whole apart from run ends.
 template <int D, int F, int P>
 __global__ __launch_bounds__(P) void hermite_scatter_kernel(
-    const Grid g, const BinPlan bp, int64_t n, int32_t nblk, int d2_mode, const float* __restrict__ x,
-    const float* __restrict__ g_gamma, const float* __restrict__ g_dgamma,
-    const float* __restrict__ g_d2gamma, const int32_t* __restrict__ counts,
+    const Grid g, const BinPlan bp, int64_t n, int32_t nblk, bool diag, const float* __restrict__ x,
+    const float* __restrict__ U, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
     const BinState* __restrict__ st, float* __restrict__ vals_out) {
   extern __shared__ int32_t lds[];
@@ -674,7 +774,7 @@ __global__ __launch_bounds__(P) void hermite_scatter_kernel(
     CellKeys<D> keys;
     AxisBasis ab[D];
     if (on) {
-      u = load_level_up<D, F>(g, p, l, d2_mode, g_gamma, g_dgamma, g_d2gamma);
+      u = load_level_up_lm<D, F>(U, n, p, l, diag);
       level_setup<D>(g, l, xp, keys, ab);
     }
     scatter_table<D, F, P, 0>(g, bp, l, blk, nblk, on, np, keys, ab, u, counts, totals, bin_start, st, vals_out, sh);
@@ -705,11 +805,31 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   const int32_t* bin_start = reinterpret_cast<const int32_t*>(ws + w.bin_start);
   const BinState* st = reinterpret_cast<const BinState*>(ws + w.state);
   float* vals = reinterpret_cast<float*>(ws + w.vals);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hermite_scatter_kernel<D, F, P>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // upstream rearranged level-major for the level-by-level scatter
+  const bool diag = d2_mode == HASHENC_D2_DIAG;
+  const int M = 1 + D + (diag ? D : 1);
+  const int LF = g.L * F;
+  const int PU = (int)std::max(1, std::min(64, 16384 / (M * LF)));  // LDS tile <= 64 KB
+  float* U = reinterpret_cast<float*>(ws + w.ups);
+  const size_t ulds = sizeof(float) * (size_t)PU * (M * LF + 1);
+  const void* ukern = diag ? reinterpret_cast<const void*>(&hermite_upstream_levels_kernel<F, D, 1 + 2 * D>)
+                           : reinterpret_cast<const void*>(&hermite_upstream_levels_kernel<F, D, 2 + D>);
+  hipError_t e = hipFuncSetAttribute(ukern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ulds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((hermite_scatter_kernel<D, F, P>), grid, dim3(P), lds, s, g, bp, n, w.nblk, d2_mode, x, gg, gd,
-                     g2, counts, totals, bin_start, st, vals);
+  const dim3 ugrid((unsigned)((n + PU - 1) / PU));
+  if (diag)
+    hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 1 + 2 * D>), ugrid, dim3(kBlock), ulds, s, g.L, n, PU,
+                       gg, gd, g2, U);
+  else
+    hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 2 + D>), ugrid, dim3(kBlock), ulds, s, g.L, n, PU, gg,
+                       gd, g2, U);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hermite_scatter_kernel<D, F, P>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((hermite_scatter_kernel<D, F, P>), grid, dim3(P), lds, s, g, bp, n, w.nblk, diag, x, U, counts,
+                     totals, bin_start, st, vals);
   return hipGetLastError();
 }
 
