@@ -29,7 +29,7 @@ namespace hg {
 namespace {
 
 constexpr int kW = 64;           // padded layer width (one wavefront)
-constexpr int kWavesPerBlock = 4;
+constexpr int kMaxWavesPerBlock = 8;
 constexpr int kMaxDepth = 4;
 
 struct MlpArgs {
@@ -52,20 +52,47 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// INP: the encoder width rounded up to 16, 32 or 64 (the first layer's fan-in).
+// Points per wavefront iteration: every LDS weight read feeds PB * R FMAs and the
+// activation rows of the PB points are read as 16-byte broadcasts.
+constexpr int kPB = 4;
+
+// Wavefronts per workgroup: as many as the workgroup's LDS (mostly per-wave activation
+// rows) allows within the CU's 160 KB.
+__host__ __device__ constexpr int siren_waves(int depth, int inp) {
+  return depth <= 2 ? 8 : (depth == 3 || inp <= 32) ? 4 : 2;
+}
+// Layer-0 fan-in as compiled: the encoder width rounded up to 16, 32 or 64.
+constexpr int siren_inp(int in) { return in <= 16 ? 16 : in <= 32 ? 32 : 64; }
+
+// LDS of one workgroup (a single orientation of the weights, padded to kW + 1 columns so
+// that both the forward read W[lane][j] and the reverse read W[o][lane] are conflict-free).
 template <int D, int DEPTH, int INP>
-__global__ __launch_bounds__(kW * kWavesPerBlock) void siren_residual_kernel(
+struct SirenLds {
+  static constexpr int R = D + 2;
+  static constexpr int RB = kPB * R;  // floats per activation row (PB points x R rows)
+  static constexpr int WV = siren_waves(DEPTH, INP);
+  float W[DEPTH][kW][kW + 1];         // W[k][o][j] = W_k[o][j]
+  float bias[DEPTH][kW];
+  float wout[kW];
+  __attribute__((aligned(16))) float act0[WV][INP][RB];                       // layer-0 inputs
+  __attribute__((aligned(16))) float act[WV][DEPTH > 1 ? DEPTH - 1 : 1][kW][RB];  // inputs of layers 1..
+  __attribute__((aligned(16))) float zb[WV][kW][RB];                         // z-adjoints, reverse
+};
+
+// INP: the encoder width rounded up to 16, 32 or 64 (the first layer's fan-in).  One
+// wavefront handles kPB points at a time, lane = neuron o.
+template <int D, int DEPTH, int INP>
+__global__ __launch_bounds__(kW * siren_waves(DEPTH, INP)) void siren_residual_kernel(
     const MlpArgs a, int64_t n, double inv_n_total, const float* __restrict__ x,
     const float* __restrict__ enc_g, const float* __restrict__ enc_d, const float* __restrict__ enc_l,
     const float* __restrict__ mlp, float* __restrict__ up_g, float* __restrict__ up_d,
     float* __restrict__ up_l, float* __restrict__ residual, float* __restrict__ partial) {
-  constexpr int R = D + 2;  // rows: value, D gradients, Laplacian
-  __shared__ float Wt[DEPTH][kW][kW];   // Wt[k][j][o] = W_k[o][j]  (forward: lane o)
-  __shared__ float Wr[DEPTH][kW][kW];   // Wr[k][o][j] = W_k[o][j]  (reverse: lane j)
-  __shared__ float bias[DEPTH][kW];
-  __shared__ float wout[kW];
-  __shared__ float act[kWavesPerBlock][DEPTH][R][kW];  // inputs of each hidden layer
-  __shared__ float zb[kWavesPerBlock][R][kW];
+  using Sh = SirenLds<D, DEPTH, INP>;
+  constexpr int R = Sh::R;
+  constexpr int RB = Sh::RB;
+  constexpr int WV = Sh::WV;
+  static_assert(sizeof(Sh) <= 160 * 1024, "SIREN workgroup LDS exceeds the CU's 160 KB");
+  __shared__ Sh sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kW - 1);
@@ -73,19 +100,16 @@ __global__ __launch_bounds__(kW * kWavesPerBlock) void siren_residual_kernel(
   const int LF = a.in;
   const float w = a.omega;
 
-  // weights into LDS, zero-padded to kW x kW
   for (int k = 0; k < DEPTH; ++k) {
     const int fi = k == 0 ? a.in : a.H;
     const float* Wk = mlp + a.woff[k];
-    for (int e = tid; e < kW * kW; e += kW * kWavesPerBlock) {
+    for (int e = tid; e < kW * kW; e += kW * WV) {
       const int o = e / kW, j = e % kW;
-      const float v = (o < a.H && j < fi) ? Wk[o * fi + j] : 0.0f;
-      Wr[k][o][j] = v;
-      Wt[k][j][o] = v;
+      sh.W[k][o][j] = (o < a.H && j < fi) ? Wk[o * fi + j] : 0.0f;
     }
-    for (int o = tid; o < kW; o += kW * kWavesPerBlock) bias[k][o] = o < a.H ? mlp[a.boff[k] + o] : 0.0f;
+    for (int o = tid; o < kW; o += kW * WV) sh.bias[k][o] = o < a.H ? mlp[a.boff[k] + o] : 0.0f;
   }
-  for (int o = tid; o < kW; o += kW * kWavesPerBlock) wout[o] = o < a.H ? mlp[a.woff[DEPTH] + o] : 0.0f;
+  for (int o = tid; o < kW; o += kW * WV) sh.wout[o] = o < a.H ? mlp[a.woff[DEPTH] + o] : 0.0f;
   __syncthreads();
 
   // lane o: row o of dL/dW_k (layer 0 has INP columns, the others kW)
@@ -102,126 +126,196 @@ __global__ __launch_bounds__(kW * kWavesPerBlock) void siren_residual_kernel(
 #pragma unroll
     for (int j = 0; j < kW; ++j) gW[k][j] = 0.0f;
 
-  const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + wv;
-  const int64_t n_waves = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t p = wave_id; p < n; p += n_waves) {
-    // encoder outputs of point p -> act[wv][0]
-    {
-      const bool on = lane < LF;
-      act[wv][0][0][lane] = on ? enc_g[p * LF + lane] : 0.0f;
+  auto in_row = [&](int k, int j) -> float* { return k == 0 ? sh.act0[wv][j] : sh.act[wv][k - 1][j]; };
+
+  const int64_t wave_id = (int64_t)blockIdx.x * WV + wv;
+  const int64_t n_waves = (int64_t)gridDim.x * WV;
+  for (int64_t p0 = wave_id * kPB; p0 < n; p0 += n_waves * kPB) {
+    // encoder outputs of points p0 .. p0 + kPB - 1 -> layer-0 input rows (lane j = column)
+    if (lane < INP) {
+      float row[RB];
 #pragma unroll
-      for (int i = 0; i < D; ++i) act[wv][0][1 + i][lane] = on ? enc_d[(p * D + i) * LF + lane] : 0.0f;
-      act[wv][0][R - 1][lane] = on ? enc_l[p * LF + lane] : 0.0f;
+      for (int b = 0; b < kPB; ++b) {
+        const int64_t p = p0 + b;
+        const bool on = lane < LF && p < n;
+        row[b * R] = on ? enc_g[p * LF + lane] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) row[b * R + 1 + i] = on ? enc_d[(p * D + i) * LF + lane] : 0.0f;
+        row[b * R + R - 1] = on ? enc_l[p * LF + lane] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < RB; q += 4)
+        *reinterpret_cast<float4*>(&sh.act0[wv][lane][q]) = make_float4(row[q], row[q + 1], row[q + 2], row[q + 3]);
     }
     wave_lds_sync();
 
-    // forward mode through the hidden layers (lane = neuron o)
-    float ts[DEPTH], tc[DEPTH], tz[DEPTH][R];  // tape: sin, cos, Z rows
-    float a_lap_top = 0.0f;
+    // forward mode through the hidden layers
+    float ts[DEPTH][kPB], tc[DEPTH][kPB], tz[DEPTH][kPB][R];  // tape: sin, cos, Z rows
+    float a_lap_top[kPB];
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) {
       const int fi = k == 0 ? INP : kW;
-      float z[R];
+      float z[RB];
 #pragma unroll
-      for (int r = 0; r < R; ++r) z[r] = r == 0 ? bias[k][lane] : 0.0f;
+      for (int q = 0; q < RB; ++q) z[q] = (q % R == 0) ? sh.bias[k][lane] : 0.0f;
+#pragma unroll 4
       for (int j = 0; j < fi; ++j) {
-        const float wj = Wt[k][j][lane];
+        const float wj = sh.W[k][lane][j];
+        const float* v = in_row(k, j);
 #pragma unroll
-        for (int r = 0; r < R; ++r) z[r] = fmaf(wj, act[wv][k][r][j], z[r]);
+        for (int q = 0; q < RB; q += 4) {
+          const float4 a4 = *reinterpret_cast<const float4*>(v + q);
+          z[q] = fmaf(wj, a4.x, z[q]);
+          z[q + 1] = fmaf(wj, a4.y, z[q + 1]);
+          z[q + 2] = fmaf(wj, a4.z, z[q + 2]);
+          z[q + 3] = fmaf(wj, a4.w, z[q + 3]);
+        }
       }
-      float s, c;
-      sincosf(w * z[0], &s, &c);
-      ts[k] = s;
-      tc[k] = c;
-      float sumsq = 0.0f;
+      float out[RB];
 #pragma unroll
-      for (int i = 1; i <= D; ++i) sumsq = fmaf(z[i], z[i], sumsq);
+      for (int b = 0; b < kPB; ++b) {
+        const float* zz = z + b * R;
+        float s, c;
+        sincosf(w * zz[0], &s, &c);
+        ts[k][b] = s;
+        tc[k][b] = c;
+        float sumsq = 0.0f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) tz[k][r] = z[r];
-      const float wc = w * c;
-      const float a_lap = fmaf(-w * w * s, sumsq, wc * z[R - 1]);
+        for (int i = 1; i <= D; ++i) sumsq = fmaf(zz[i], zz[i], sumsq);
+#pragma unroll
+        for (int r = 0; r < R; ++r) tz[k][b][r] = zz[r];
+        const float wc = w * c;
+        const float a_lap = fmaf(-w * w * s, sumsq, wc * zz[R - 1]);
+        out[b * R] = s;
+#pragma unroll
+        for (int i = 1; i <= D; ++i) out[b * R + i] = wc * zz[i];
+        out[b * R + R - 1] = a_lap;
+        a_lap_top[b] = a_lap;
+      }
       if (k + 1 < DEPTH) {
-        act[wv][k + 1][0][lane] = s;
 #pragma unroll
-        for (int i = 1; i <= D; ++i) act[wv][k + 1][i][lane] = wc * z[i];
-        act[wv][k + 1][R - 1][lane] = a_lap;
+        for (int q = 0; q < RB; q += 4)
+          *reinterpret_cast<float4*>(&sh.act[wv][k][lane][q]) = make_float4(out[q], out[q + 1], out[q + 2], out[q + 3]);
         wave_lds_sync();
-      } else {
-        a_lap_top = a_lap;
       }
     }
-    // linear output: Lap u = wout . A_lap
-    const float lap_u = wave_sum(wout[lane] * a_lap_top);
-    float src = -(float)D * 9.8696044010893586f;  // -d pi^2
+    // linear output: Lap u = wout . A_lap; residual and seed per point
+    float seed[kPB];
 #pragma unroll
-    for (int i = 0; i < D; ++i) src *= sinpif(x[p * D + i]);
-    const float res = lap_u - src;
-    if (lane == 0) {
-      sq = fmaf(res, res, sq);
-      if (residual) residual[p] = res;
+    for (int b = 0; b < kPB; ++b) {
+      const int64_t p = p0 + b;
+      const float lap_u = wave_sum(sh.wout[lane] * a_lap_top[b]);
+      float res = 0.0f;
+      if (p < n) {
+        float src = -(float)D * 9.8696044010893586f;  // -d pi^2
+#pragma unroll
+        for (int i = 0; i < D; ++i) src *= sinpif(x[p * D + i]);
+        res = lap_u - src;
+        if (lane == 0) {
+          sq = fmaf(res, res, sq);
+          if (residual) residual[p] = res;
+        }
+      }
+      seed[b] = (float)(2.0 * (double)res * inv_n_total);
+      gWo = fmaf(seed[b], a_lap_top[b], gWo);
     }
-    const float seed = (float)(2.0 * (double)res * inv_n_total);
-    gWo = fmaf(seed, a_lap_top, gWo);
 
-    // reverse sweep; the output layer seeds only the Laplacian row
-    float ab[R];
+    // reverse sweep; the output layer seeds only the Laplacian rows
+    float ab[RB];
 #pragma unroll
-    for (int r = 0; r < R; ++r) ab[r] = 0.0f;
-    ab[R - 1] = seed * wout[lane];
+    for (int b = 0; b < kPB; ++b) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) ab[b * R + r] = 0.0f;
+      ab[b * R + R - 1] = seed[b] * sh.wout[lane];
+    }
 #pragma unroll
     for (int k = DEPTH - 1; k >= 0; --k) {
-      const float s = ts[k], c = tc[k];
-      const float wc = w * c, w2s = w * w * s;
-      float sumsq = 0.0f;
+      float zbar[RB];
 #pragma unroll
-      for (int i = 1; i <= D; ++i) sumsq = fmaf(tz[k][i], tz[k][i], sumsq);
-      float zbar[R];
-      // d a/dz = w cos; d A_i/dz = -w^2 sin Z_i; d A_lap/dz = -w^3 cos sum Z_i^2 - w^2 sin Z_lap
-      float z0 = ab[0] * wc + ab[R - 1] * (-w * w * wc * sumsq - w2s * tz[k][R - 1]);
+      for (int b = 0; b < kPB; ++b) {
+        const float s = ts[k][b], c = tc[k][b];
+        const float wc = w * c, w2s = w * w * s;
+        const float* zz = tz[k][b];
+        const float* aa = ab + b * R;
+        float sumsq = 0.0f;
 #pragma unroll
-      for (int i = 1; i <= D; ++i) {
-        z0 = fmaf(ab[i], -w2s * tz[k][i], z0);
-        // d A_i/dZ_i = w cos; d A_lap/dZ_i = -2 w^2 sin Z_i
-        zbar[i] = ab[i] * wc + ab[R - 1] * (-2.0f * w2s * tz[k][i]);
+        for (int i = 1; i <= D; ++i) sumsq = fmaf(zz[i], zz[i], sumsq);
+        // d a/dz = w cos; d A_i/dz = -w^2 sin Z_i; d A_lap/dz = -w^3 cos sum Z_i^2 - w^2 sin Z_lap
+        float z0 = aa[0] * wc + aa[R - 1] * (-w * w * wc * sumsq - w2s * zz[R - 1]);
+#pragma unroll
+        for (int i = 1; i <= D; ++i) {
+          z0 = fmaf(aa[i], -w2s * zz[i], z0);
+          // d A_i/dZ_i = w cos; d A_lap/dZ_i = -2 w^2 sin Z_i
+          zbar[b * R + i] = aa[i] * wc + aa[R - 1] * (-2.0f * w2s * zz[i]);
+        }
+        zbar[b * R] = z0;
+        zbar[b * R + R - 1] = aa[R - 1] * wc;  // d A_lap/dZ_lap = w cos
+        gb[k] += z0;
       }
-      zbar[0] = z0;
-      zbar[R - 1] = ab[R - 1] * wc;  // d A_lap/dZ_lap = w cos
-      gb[k] += zbar[0];
+      // dL/dW_k row `lane` += sum over points and rows of zbar * input row
       if (k == 0) {
 #pragma unroll
         for (int j = 0; j < INP; ++j) {
+          const float* v = sh.act0[wv][j];
           float acc = gW0[j];
 #pragma unroll
-          for (int r = 0; r < R; ++r) acc = fmaf(zbar[r], act[wv][0][r][j], acc);
+          for (int q = 0; q < RB; q += 4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(v + q);
+            acc = fmaf(zbar[q], a4.x, acc);
+            acc = fmaf(zbar[q + 1], a4.y, acc);
+            acc = fmaf(zbar[q + 2], a4.z, acc);
+            acc = fmaf(zbar[q + 3], a4.w, acc);
+          }
           gW0[j] = acc;
         }
       } else {
 #pragma unroll
         for (int j = 0; j < kW; ++j) {
+          const float* v = sh.act[wv][k - 1][j];
           float acc = gW[k - 1][j];
 #pragma unroll
-          for (int r = 0; r < R; ++r) acc = fmaf(zbar[r], act[wv][k][r][j], acc);
+          for (int q = 0; q < RB; q += 4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(v + q);
+            acc = fmaf(zbar[q], a4.x, acc);
+            acc = fmaf(zbar[q + 1], a4.y, acc);
+            acc = fmaf(zbar[q + 2], a4.z, acc);
+            acc = fmaf(zbar[q + 3], a4.w, acc);
+          }
           gW[k - 1][j] = acc;
         }
       }
-      // input adjoint: lane j <- sum_o W_k[o][j] zbar[o]
+      // input adjoint: lane j <- sum_o W_k[o][j] zbar_o
 #pragma unroll
-      for (int r = 0; r < R; ++r) zb[wv][r][lane] = zbar[r];
+      for (int q = 0; q < RB; q += 4)
+        *reinterpret_cast<float4*>(&sh.zb[wv][lane][q]) = make_float4(zbar[q], zbar[q + 1], zbar[q + 2], zbar[q + 3]);
       wave_lds_sync();
 #pragma unroll
-      for (int r = 0; r < R; ++r) ab[r] = 0.0f;
-      for (int o = 0; o < a.H; ++o) {
-        const float wo = Wr[k][o][lane];
+      for (int q = 0; q < RB; ++q) ab[q] = 0.0f;
+#pragma unroll 4
+      for (int o = 0; o < kW; ++o) {
+        const float wo = sh.W[k][o][lane];
+        const float* zr = sh.zb[wv][o];
 #pragma unroll
-        for (int r = 0; r < R; ++r) ab[r] = fmaf(wo, zb[wv][r][o], ab[r]);
+        for (int q = 0; q < RB; q += 4) {
+          const float4 z4 = *reinterpret_cast<const float4*>(zr + q);
+          ab[q] = fmaf(wo, z4.x, ab[q]);
+          ab[q + 1] = fmaf(wo, z4.y, ab[q + 1]);
+          ab[q + 2] = fmaf(wo, z4.z, ab[q + 2]);
+          ab[q + 3] = fmaf(wo, z4.w, ab[q + 3]);
+        }
       }
       wave_lds_sync();  // zb is rewritten by the next layer
     }
     if (lane < LF) {
-      up_g[p * LF + lane] = ab[0];
 #pragma unroll
-      for (int i = 0; i < D; ++i) up_d[(p * D + i) * LF + lane] = ab[1 + i];
-      up_l[p * LF + lane] = ab[R - 1];
+      for (int b = 0; b < kPB; ++b) {
+        const int64_t p = p0 + b;
+        if (p >= n) break;
+        up_g[p * LF + lane] = ab[b * R];
+#pragma unroll
+        for (int i = 0; i < D; ++i) up_d[(p * D + i) * LF + lane] = ab[b * R + 1 + i];
+        up_l[p * LF + lane] = ab[b * R + R - 1];
+      }
     }
   }
 
@@ -285,7 +379,7 @@ __global__ __launch_bounds__(256) void reduce_partials_apply_kernel(const double
 }
 
 constexpr int64_t kChunk = int64_t(1) << 20;  // points per pass over the workspace
-constexpr int kSirenBlocks = 1024;
+constexpr int kSirenBlocks = 256;  // one workgroup per CU (LDS-limited)
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -305,8 +399,8 @@ WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t
   w.up_g = take(sizeof(float) * c * LF);
   w.up_d = take(sizeof(float) * c * d * LF);
   w.up_l = take(sizeof(float) * c * LF);
-  w.partial = take(sizeof(float) * (size_t)kSirenBlocks * kWavesPerBlock * (n_mlp + 1));
-  w.slices = take(sizeof(double) * (size_t)((kSirenBlocks * kWavesPerBlock + kSliceRows - 1) / kSliceRows) *
+  w.partial = take(sizeof(float) * (size_t)kSirenBlocks * kMaxWavesPerBlock * (n_mlp + 1));
+  w.slices = take(sizeof(double) * (size_t)((kSirenBlocks * kMaxWavesPerBlock + kSliceRows - 1) / kSliceRows) *
                   (n_mlp + 1));
   w.bins = take(binned ? binned_backward_workspace_bytes(g, d, F, true, c) : 0);
   w.total = off;
@@ -317,7 +411,7 @@ template <int D, int DEPTH, int INP>
 hipError_t launch_siren(const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* eg,
                         const float* ed, const float* el, const float* mlp, float* ug, float* ud,
                         float* ul, float* residual, float* partial, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL((siren_residual_kernel<D, DEPTH, INP>), dim3(blocks), dim3(kW * kWavesPerBlock), 0, s,
+  hipLaunchKernelGGL((siren_residual_kernel<D, DEPTH, INP>), dim3(blocks), dim3(kW * siren_waves(DEPTH, INP)), 0, s,
                      a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial);
   return hipGetLastError();
 }
@@ -401,12 +495,13 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
     const float* xc = x + p0 * d;
     hipError_t e = launch_hermite_forward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, params, eg, ed, el, s);
     if (e != hipSuccess) return e;
-    int blocks = (int)((c + kWavesPerBlock - 1) / kWavesPerBlock);
+    const int wpb = siren_waves(depth, siren_inp(in));  // waves per SIREN workgroup
+    int blocks = (int)((c + wpb * kPB - 1) / (wpb * kPB));
     if (blocks > kSirenBlocks) blocks = kSirenBlocks;
     float* rc = residual ? residual + p0 : nullptr;
     e = dispatch_siren(d, depth, in, a, c, inv_n, xc, eg, ed, el, mlp, ug, ud, ul, rc, partial, blocks, s);
     if (e != hipSuccess) return e;
-    const int64_t n_waves = (int64_t)blocks * kWavesPerBlock;
+    const int64_t n_waves = (int64_t)blocks * wpb;
     const int n_slices = (int)((n_waves + kSliceRows - 1) / kSliceRows);
     double* slices = reinterpret_cast<double*>(ws + wl.slices);
     const unsigned col_blocks = (unsigned)((a.n_mlp + 1 + 255) / 256);
