@@ -57,6 +57,25 @@ def algorithmic_bytes_per_point(spec: dict) -> dict:
             "backward": x_bytes + 4 * out_floats + 8 * coeffs}
 
 
+def copy_bandwidth(torch, api, nbytes: int = 4 << 30, steps: int = 10) -> float:
+    """Achievable HBM bandwidth, read + write GB/s of the plain copy kernel over nbytes (16x
+    the Infinity Cache, so the copy streams from HBM)."""
+    n = nbytes // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty(n, device="cuda:0")
+    api.hashenc_diag_copy(src, dst)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        api.hashenc_diag_copy(src, dst)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    del src, dst
+    return 8 * n / ms / 1e6
+
+
 def copy_calibration(args, torch, api) -> int:
     """Plain streaming copy of --copy-bytes bytes: achievable bandwidth, and a launch of known
     traffic (read + write = 2 * bytes) against which memory counters are scaled."""
@@ -156,7 +175,7 @@ def main() -> int:
                     help="approximate CPU time budget of the oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: runs on one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
         return 2
 
@@ -244,6 +263,13 @@ def main() -> int:
                            + f" ({spec['kind']}; its kernels back to back on one stream)"),
                 "avg_launch_ms": round(kern[dom]["ms"], 4),
                 "alg_bytes_per_launch": kern[dom]["alg_bytes"]}
+    # the same launch against the copy kernel's bandwidth measured now, and the counter-
+    # measured traffic of the launch as a bandwidth
+    achievable = copy_bandwidth(torch, api)
+    roofline["achievable_GBps"] = round(achievable, 1)
+    roofline["frac_of_achievable"] = round(kern[dom]["GBps"] / achievable, 4)
+    if traffic is not None:
+        roofline["traffic_GBps"] = round(traffic / (kern[dom]["ms"] * 1e-3) / 1e9, 1)
     step_alg = alg["forward"] + alg["backward"]
 
     cpu = None

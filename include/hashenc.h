@@ -63,7 +63,7 @@ enum {
   HASHENC_EALIGN = -2,       /* a device pointer is not 16-byte aligned */
   HASHENC_ENOMEM = -3,       /* host allocation failed */
   HASHENC_EHIP = -4,         /* a HIP runtime / launch error (message has hipGetErrorString) */
-  HASHENC_EUNSUPPORTED = -5  /* valid request this build does not implement */
+  HASHENC_EUNSUPPORTED = -5  /* valid request the library does not implement */
 };
 
 typedef enum { HASHENC_DLINEAR = 0, HASHENC_HERMITE = 1 } hashenc_kind;

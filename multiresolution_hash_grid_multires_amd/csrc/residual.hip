@@ -344,6 +344,317 @@ __global__ __launch_bounds__(kW * siren_waves(DEPTH, INP)) void siren_residual_k
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Matrix-core formulation for SIREN depth <= 2.  A workgroup of 4 wavefronts takes 16 points
+// per iteration; the columns of every layer's matrices are (row kind r, point p), c = 16 r + p,
+// r over value, d gradients, Laplacian.  Wavefront w owns neurons 16w..16w+15 on the output
+// side of each product.  The three products per layer run on v_mfma_f32_16x16x4_f32
+// (lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]; D[4 (l / 16) + i][l % 16] in
+// register i):
+//   forward          Z_k = W_k V_k (+ b_k on the value rows)   A = W_k rows (registers),
+//                                                             B = V_k from LDS
+//   input adjoint    Vbar_k = W_k^T Zbar_k                   A = W_k columns (registers),
+//                                                             B = Zbar_k from LDS
+//   weight gradient  dL/dW_k += Zbar_k V_k^T (over columns)  A = Zbar_k, B = V_k, both read
+//                                                             from LDS transposed; the
+//                                                             accumulator lives across
+//                                                             iterations
+// The elementwise forward-mode activation and its reverse are lane-local: a lane's D registers
+// hold the same (neuron, point) for every row kind.  Layer inputs V_k and the z-adjoints are
+// exchanged through LDS as [row][column] matrices (pitch kMPitch, bank-conflict-free for both
+// access patterns); the Z tape of a wavefront's own neurons stays in registers.
+typedef float mf4 __attribute__((ext_vector_type(4)));
+constexpr int kMP = 16;      // points per workgroup iteration
+constexpr int kMWaves = 4;   // wavefronts per workgroup (kW / 16 neuron tiles)
+constexpr int kMPitch = 84;  // LDS row pitch in floats (columns: 16 * (d + 2) <= 80)
+constexpr int kMfmaBlocks = 512;  // two resident workgroups per CU, all in one round
+
+template <int D, int DEPTH, int NI>
+struct MfmaLds {
+  float w0[kW][NI + 4];                               // W_0 (padded rows)
+  float w1[DEPTH > 1 ? kW : 1][kW + 4];               // W_1
+  float act0[NI][kMPitch];                            // V_0: encoder rows
+  float act1[DEPTH > 1 ? kW : 1][kMPitch];            // V_1: layer-0 activations
+  float zb[kW][kMPitch];                              // Zbar of the layer in reverse
+  float lapw[kMWaves][kMP];                           // per-wave partial Laplacians
+};
+
+__device__ __forceinline__ mf4 mfma16(float a, float b, mf4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D, int DEPTH, int NI>
+__global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
+    const MlpArgs a, int64_t n, double inv_n_total, const float* __restrict__ x,
+    const float* __restrict__ enc_g, const float* __restrict__ enc_d, const float* __restrict__ enc_l,
+    const float* __restrict__ mlp, float* __restrict__ up_g, float* __restrict__ up_d,
+    float* __restrict__ up_l, float* __restrict__ residual, float* __restrict__ partial) {
+  static_assert(DEPTH == 1 || DEPTH == 2, "matrix-core SIREN covers one or two hidden layers");
+  constexpr int R = D + 2;
+  constexpr int NC = kMP * R;  // columns
+  __shared__ MfmaLds<D, DEPTH, NI> sh;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lm = lane & 15, lq = lane >> 4;
+  const int LF = a.in, H = a.H;
+  const float om = a.omega;
+
+  // weights into LDS, zero-padded to the compiled widths; the forward reads W_k[16w + lm][4kk + lq]
+  // (conflict-free with rows padded by 4 floats), the input adjoint W_k[4kk + lq][16w + lm]
+  for (int e = threadIdx.x; e < kW * NI; e += kW * kMWaves) {
+    const int o = e / NI, j = e % NI;
+    sh.w0[o][j] = (o < H && j < a.in) ? mlp[a.woff[0] + o * a.in + j] : 0.0f;
+  }
+  if constexpr (DEPTH > 1) {
+    for (int e = threadIdx.x; e < kW * kW; e += kW * kMWaves) {
+      const int o = e / kW, j = e % kW;
+      sh.w1[o][j] = (o < H && j < H) ? mlp[a.woff[1] + o * H + j] : 0.0f;
+    }
+  }
+  // per-lane neurons in D layout: o = 16w + 4lq + i
+  float bias[DEPTH][4], wout[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = 16 * w + 4 * lq + i;
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) bias[k][i] = o < H ? mlp[a.boff[k] + o] : 0.0f;
+    wout[i] = o < H ? mlp[a.woff[DEPTH] + o] : 0.0f;
+  }
+  mf4 gW0[NI / 16];
+  mf4 gW1[DEPTH > 1 ? 4 : 1];
+#pragma unroll
+  for (int t = 0; t < NI / 16; ++t) gW0[t] = mf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < (DEPTH > 1 ? 4 : 1); ++t) gW1[t] = mf4{0.f, 0.f, 0.f, 0.f};
+  float gb[DEPTH][4], gWo[4], sq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    gWo[i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) gb[k][i] = 0.0f;
+  }
+
+  const int64_t n_iter = (n + kMP - 1) / kMP;
+  for (int64_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
+    const int64_t p0 = it * kMP;
+    // encoder rows -> V_0[j][16 r + p]
+    for (int e = threadIdx.x; e < kMP * R * NI; e += kW * kMWaves) {
+      const int j = e % NI, t2 = e / NI;
+      const int r = t2 % R, p = t2 / R;
+      const int64_t pp = p0 + p;
+      float v = 0.0f;
+      if (j < LF && pp < n) {
+        if (r == 0) v = enc_g[pp * LF + j];
+        else if (r <= D) v = enc_d[(pp * D + (r - 1)) * LF + j];
+        else v = enc_l[pp * LF + j];
+      }
+      sh.act0[j][r * kMP + p] = v;
+    }
+    __syncthreads();
+
+    // forward mode
+    mf4 z[DEPTH][R];  // tape: the wavefront's neurons
+    float alap[4];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) {
+      mf4 acc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = mf4{0.f, 0.f, 0.f, 0.f};
+      if (k == 0) {
+#pragma unroll
+        for (int kk = 0; kk < NI / 4; ++kk) {
+          const float aw = sh.w0[16 * w + lm][4 * kk + lq];
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r] = mfma16(aw, sh.act0[4 * kk + lq][r * kMP + lm], acc[r]);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const float aw = sh.w1[16 * w + lm][4 * kk + lq];
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r] = mfma16(aw, sh.act1[4 * kk + lq][r * kMP + lm], acc[r]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[0][i] += bias[k][i];
+#pragma unroll
+      for (int r = 0; r < R; ++r) z[k][r] = acc[r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float s, c;
+        sincosf(om * acc[0][i], &s, &c);
+        float sumsq = 0.0f;
+#pragma unroll
+        for (int r = 1; r <= D; ++r) sumsq = fmaf(acc[r][i], acc[r][i], sumsq);
+        const float wc = om * c;
+        const float a_lap = fmaf(-om * om * s, sumsq, wc * acc[R - 1][i]);
+        if (k + 1 < DEPTH) {
+          const int o = 16 * w + 4 * lq + i;
+          sh.act1[o][lm] = s;
+#pragma unroll
+          for (int r = 1; r <= D; ++r) sh.act1[o][r * kMP + lm] = wc * acc[r][i];
+          sh.act1[o][(R - 1) * kMP + lm] = a_lap;
+        } else {
+          alap[i] = a_lap;
+        }
+      }
+      if (k + 1 < DEPTH) __syncthreads();
+    }
+    // linear output: Lap u = wout . A_lap (sum over the 64 neurons of 4 wavefronts)
+    {
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part = fmaf(wout[i], alap[i], part);
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      if (lq == 0) sh.lapw[w][lm] = part;
+    }
+    __syncthreads();
+    const int64_t pp = p0 + lm;
+    float seed = 0.0f;
+    if (pp < n) {
+      float lap_u = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kMWaves; ++v) lap_u += sh.lapw[v][lm];
+      float src = -(float)D * 9.8696044010893586f;  // -d pi^2
+#pragma unroll
+      for (int i = 0; i < D; ++i) src *= sinpif(x[pp * D + i]);
+      const float res = lap_u - src;
+      if (w == 0 && lq == 0) {
+        sq = fmaf(res, res, sq);
+        if (residual) residual[pp] = res;
+      }
+      seed = (float)(2.0 * (double)res * inv_n_total);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gWo[i] = fmaf(seed, alap[i], gWo[i]);
+
+    // reverse sweep, top layer down; abar: adjoint of the layer's output rows (D layout)
+    mf4 abar[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) abar[r] = mf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) abar[R - 1][i] = seed * wout[i];
+#pragma unroll
+    for (int k = DEPTH - 1; k >= 0; --k) {
+      mf4 zbar[R];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float s, c;
+        sincosf(om * z[k][0][i], &s, &c);
+        const float wc = om * c, w2s = om * om * s;
+        float sumsq = 0.0f;
+#pragma unroll
+        for (int r = 1; r <= D; ++r) sumsq = fmaf(z[k][r][i], z[k][r][i], sumsq);
+        const float al = abar[R - 1][i];
+        // d a/dz = w cos; d A_i/dz = -w^2 sin Z_i; d A_lap/dz = -w^3 cos sum Z_i^2 - w^2 sin Z_lap
+        float z0 = abar[0][i] * wc + al * (-om * om * wc * sumsq - w2s * z[k][R - 1][i]);
+#pragma unroll
+        for (int r = 1; r <= D; ++r) {
+          z0 = fmaf(abar[r][i], -w2s * z[k][r][i], z0);
+          // d A_i/dZ_i = w cos; d A_lap/dZ_i = -2 w^2 sin Z_i
+          zbar[r][i] = abar[r][i] * wc + al * (-2.0f * w2s * z[k][r][i]);
+        }
+        zbar[0][i] = z0;
+        zbar[R - 1][i] = al * wc;  // d A_lap/dZ_lap = w cos
+        gb[k][i] += z0;
+        const int o = 16 * w + 4 * lq + i;
+#pragma unroll
+        for (int r = 0; r < R; ++r) sh.zb[o][r * kMP + lm] = zbar[r][i];
+      }
+      __syncthreads();
+      // weight gradient: dL/dW_k[16w + .][j] += sum_c Zbar[o][c] V_k[j][c]
+#pragma unroll
+      for (int kk = 0; kk < NC / 4; ++kk) {
+        const float az = sh.zb[16 * w + lm][4 * kk + lq];
+        if (k == 0) {
+#pragma unroll
+          for (int t = 0; t < NI / 16; ++t) gW0[t] = mfma16(az, sh.act0[16 * t + lm][4 * kk + lq], gW0[t]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) gW1[t] = mfma16(az, sh.act1[16 * t + lm][4 * kk + lq], gW1[t]);
+        }
+      }
+      // input adjoint for the wavefront's tile of input neurons j = 16w + .
+      const int fi = k == 0 ? NI : kW;
+      mf4 vbar[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) vbar[r] = mf4{0.f, 0.f, 0.f, 0.f};
+      if (16 * w < fi) {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const float aw = k == 0 ? sh.w0[4 * kk + lq][16 * w + lm] : sh.w1[4 * kk + lq][16 * w + lm];
+#pragma unroll
+          for (int r = 0; r < R; ++r) vbar[r] = mfma16(aw, sh.zb[4 * kk + lq][r * kMP + lm], vbar[r]);
+        }
+      }
+      __syncthreads();  // zb and the layer's inputs are rewritten next
+      if (k > 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) abar[r] = vbar[r];
+      } else if (16 * w < fi && pp < n) {
+        // encoder upstream, inputs j = 16w + 4lq + i of point pp
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * w + 4 * lq + i;
+          if (j < LF) {
+            up_g[pp * LF + j] = vbar[0][i];
+#pragma unroll
+            for (int r = 1; r <= D; ++r) up_d[(pp * D + (r - 1)) * LF + j] = vbar[r][i];
+            up_l[pp * LF + j] = vbar[R - 1][i];
+          }
+        }
+      }
+    }
+  }
+
+  // this workgroup's partial MLP gradient and sum of r^2
+  float* part = partial + (int64_t)blockIdx.x * (a.n_mlp + 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = 16 * w + 4 * lq + i;
+    if (o < H) {
+#pragma unroll
+      for (int t = 0; t < NI / 16; ++t) {
+        const int j = 16 * t + lm;
+        if (j < a.in) part[a.woff[0] + (int64_t)o * a.in + j] = gW0[t][i];
+      }
+      if constexpr (DEPTH > 1) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = 16 * t + lm;
+          if (j < H) part[a.woff[1] + (int64_t)o * H + j] = gW1[t][i];
+        }
+      }
+    }
+  }
+  // bias and output-weight gradients: sum over the 16 points (lanes lm) of each lane group
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[DEPTH + 1];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) v[k] = gb[k][i];
+    v[DEPTH] = gWo[i];
+#pragma unroll
+    for (int k = 0; k <= DEPTH; ++k)
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) v[k] += __shfl_xor(v[k], off, 64);
+    const int o = 16 * w + 4 * lq + i;
+    if (lm == 0 && o < H) {
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) part[a.boff[k] + o] = v[k];
+      part[a.woff[DEPTH] + o] = v[DEPTH];
+    }
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) sq += __shfl_xor(sq, off, 64);
+    if (lane == 0) {
+      part[a.boff[DEPTH]] = 0.0f;  // the output bias does not enter Lap u
+      part[a.n_mlp] = sq;
+    }
+  }
+}
+
 // Sum of the per-wave partial rows, in two passes: each workgroup of the first pass adds a
 // slice of kSliceRows rows for 256 columns in fp64; the second pass adds the slices and
 // applies the result (grad_mlp += ..., loss (+)= ... / n).
@@ -410,39 +721,53 @@ WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t
 template <int D, int DEPTH, int INP>
 hipError_t launch_siren(const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* eg,
                         const float* ed, const float* el, const float* mlp, float* ug, float* ud,
-                        float* ul, float* residual, float* partial, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL((siren_residual_kernel<D, DEPTH, INP>), dim3(blocks), dim3(kW * siren_waves(DEPTH, INP)), 0, s,
-                     a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial);
+                        float* ul, float* residual, float* partial, int& rows, hipStream_t s) {
+  if constexpr (DEPTH <= 2) {
+    // matrix cores: one partial row per workgroup
+    int blocks = (int)((n + kMP - 1) / kMP);
+    if (blocks > kMfmaBlocks) blocks = kMfmaBlocks;
+    rows = blocks;
+    hipLaunchKernelGGL((siren_mfma_kernel<D, DEPTH, INP>), dim3(blocks), dim3(kW * kMWaves), 0, s, a, n, inv_n, x,
+                       eg, ed, el, mlp, ug, ud, ul, residual, partial);
+  } else {
+    // vector ALUs: one partial row per wavefront
+    const int wpb = siren_waves(DEPTH, INP);
+    int blocks = (int)((n + wpb * kPB - 1) / (wpb * kPB));
+    if (blocks > kSirenBlocks) blocks = kSirenBlocks;
+    rows = blocks * wpb;
+    hipLaunchKernelGGL((siren_residual_kernel<D, DEPTH, INP>), dim3(blocks), dim3(kW * wpb), 0, s, a, n, inv_n, x,
+                       eg, ed, el, mlp, ug, ud, ul, residual, partial);
+  }
   return hipGetLastError();
 }
 
 template <int D, int DEPTH>
 hipError_t dispatch_in(int in, const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* eg,
                        const float* ed, const float* el, const float* mlp, float* ug, float* ud, float* ul,
-                       float* residual, float* partial, int blocks, hipStream_t s) {
-  if (in <= 16) return launch_siren<D, DEPTH, 16>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
-  if (in <= 32) return launch_siren<D, DEPTH, 32>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
-  return launch_siren<D, DEPTH, 64>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+                       float* residual, float* partial, int& rows, hipStream_t s) {
+  if (in <= 16) return launch_siren<D, DEPTH, 16>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
+  if (in <= 32) return launch_siren<D, DEPTH, 32>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
+  return launch_siren<D, DEPTH, 64>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
 }
 
 template <int D>
 hipError_t dispatch_depth(int depth, int in, const MlpArgs& a, int64_t n, double inv_n, const float* x,
                           const float* eg, const float* ed, const float* el, const float* mlp, float* ug,
-                          float* ud, float* ul, float* residual, float* partial, int blocks, hipStream_t s) {
+                          float* ud, float* ul, float* residual, float* partial, int& rows, hipStream_t s) {
   switch (depth) {
-    case 1: return dispatch_in<D, 1>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
-    case 2: return dispatch_in<D, 2>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
-    case 3: return dispatch_in<D, 3>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
-    default: return dispatch_in<D, 4>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+    case 1: return dispatch_in<D, 1>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
+    case 2: return dispatch_in<D, 2>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
+    case 3: return dispatch_in<D, 3>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
+    default: return dispatch_in<D, 4>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
   }
 }
 
 hipError_t dispatch_siren(int d, int depth, int in, const MlpArgs& a, int64_t n, double inv_n,
                           const float* x, const float* eg, const float* ed, const float* el,
                           const float* mlp, float* ug, float* ud, float* ul, float* residual,
-                          float* partial, int blocks, hipStream_t s) {
-  if (d == 2) return dispatch_depth<2>(depth, in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
-  return dispatch_depth<3>(depth, in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, blocks, s);
+                          float* partial, int& rows, hipStream_t s) {
+  if (d == 2) return dispatch_depth<2>(depth, in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
+  return dispatch_depth<3>(depth, in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
 }
 
 }  // namespace
@@ -495,13 +820,11 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
     const float* xc = x + p0 * d;
     hipError_t e = launch_hermite_forward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, params, eg, ed, el, s);
     if (e != hipSuccess) return e;
-    const int wpb = siren_waves(depth, siren_inp(in));  // waves per SIREN workgroup
-    int blocks = (int)((c + wpb * kPB - 1) / (wpb * kPB));
-    if (blocks > kSirenBlocks) blocks = kSirenBlocks;
     float* rc = residual ? residual + p0 : nullptr;
-    e = dispatch_siren(d, depth, in, a, c, inv_n, xc, eg, ed, el, mlp, ug, ud, ul, rc, partial, blocks, s);
+    int rows = 0;  // partial rows written (per wavefront or per workgroup)
+    e = dispatch_siren(d, depth, in, a, c, inv_n, xc, eg, ed, el, mlp, ug, ud, ul, rc, partial, rows, s);
     if (e != hipSuccess) return e;
-    const int64_t n_waves = (int64_t)blocks * wpb;
+    const int64_t n_waves = rows;
     const int n_slices = (int)((n_waves + kSliceRows - 1) / kSliceRows);
     double* slices = reinterpret_cast<double*>(ws + wl.slices);
     const unsigned col_blocks = (unsigned)((a.n_mlp + 1 + 255) / 256);
