@@ -11,6 +11,16 @@ constexpr int kBinLdsValues = 8192;               // 64 KB fp64 LDS accumulator 
 constexpr int kBinTilePoints = 1024;              // points per count / scatter workgroup (max)
 constexpr int kBinThreads = 256;
 constexpr int kBinItemEntries = 1 << 18;          // entries per reduce work item (at most)
+constexpr int kBinItemMin = 1 << 12;              // ... and at least, when bins are split
+
+// Entries per reduce work item for a chunk of `entries` entries: about 512 items, so small
+// problems still spread over every CU, between kBinItemMin and kBinItemEntries.
+inline int32_t bin_item_entries(int64_t entries) {
+  int64_t e = entries / 512;
+  if (e < kBinItemMin) e = kBinItemMin;
+  if (e > kBinItemEntries) e = kBinItemEntries;
+  return (int32_t)e;
+}
 constexpr int kReduceThreads = 512;
 constexpr int kBinReduceBlocks = 512;             // persistent reduce workgroups (2 per CU)
 constexpr int kScatterThreads = 512;              // d-linear scatter workgroup
@@ -64,6 +74,7 @@ struct BinWorkspace {
   int32_t tile;   // points per count / scatter workgroup
   int32_t nblk;
   int64_t max_items;
+  int32_t item_entries;  // entries per reduce work item
   size_t counts, totals, seg_sums, state, bin_start, items, vals, ups, total;
 };
 

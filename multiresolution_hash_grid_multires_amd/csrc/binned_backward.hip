@@ -381,7 +381,10 @@ BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64
   w.tile = tile;
   w.nblk = (int32_t)((chunk_points + tile - 1) / tile);
   const int64_t entries = chunk_points * epp;
-  w.max_items = bp.nbins + entries / kBinItemEntries + 1;
+  w.item_entries = bin_item_entries(entries);
+  // bins split into items of item_entries: at most entries / item_entries <= max(512,
+  // entries / kBinItemEntries) extra items, a bound that only grows with the chunk
+  w.max_items = bp.nbins + 514 + entries / kBinItemEntries;
   size_t off = 0;
   w.counts = off; off += al(sizeof(int32_t) * (size_t)bp.nbins * w.nblk);
   w.totals = off; off += al(sizeof(int32_t) * (size_t)bp.nbins);
@@ -411,7 +414,7 @@ hipError_t run_bin_middle(const BinPlan& bp, const BinWorkspace& w, char* ws, hi
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bin_plan_kernel, dim3(1), dim3(1024), 0, s, bp, totals,
                      reinterpret_cast<int32_t*>(ws + w.bin_start), reinterpret_cast<WorkItem*>(ws + w.items),
-                     reinterpret_cast<BinState*>(ws + w.state), (int32_t)kBinItemEntries);
+                     reinterpret_cast<BinState*>(ws + w.state), w.item_entries);
   return hipGetLastError();
 }
 
