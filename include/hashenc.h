@@ -121,9 +121,12 @@ HASHENC_API int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size
 
 /* Same outputs as hashenc_forward.  With a workspace the d-linear encoding is computed
  * level by level into a level-major staging buffer [L][n][F] (every store writes whole
- * cache lines) and then rearranged into gamma [n, L*F] in one pass.  workspace: >=
- * hashenc_forward_workspace_size bytes, 256-byte aligned; calls sharing it must not
- * overlap.  Hermite handles ignore the workspace. */
+ * cache lines) and then rearranged into gamma [n, L*F] in one pass.  A Hermite handle whose
+ * order tables all have the same size first packs the tables into the workspace (one
+ * contiguous row of every order table per vertex) and reads the corners from that copy;
+ * with unequal sizes it needs no workspace (size 0) and runs as hashenc_forward.
+ * workspace: >= hashenc_forward_workspace_size bytes, 256-byte aligned; calls sharing it
+ * must not overlap.  Results are bit-identical to hashenc_forward. */
 HASHENC_API int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float* params,
                                    float* gamma, float* dgamma, float* d2gamma, void* workspace,
                                    size_t workspace_bytes, hashenc_stream_t stream);

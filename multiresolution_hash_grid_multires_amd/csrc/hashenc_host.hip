@@ -209,8 +209,8 @@ int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* pa
   if (h->kind == HASHENC_DLINEAR)
     e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma, nullptr, stream);
   else
-    e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, gamma,
-                                        dgamma, d2gamma, stream);
+    e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, nullptr, gamma,
+                                   dgamma, d2gamma, stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_forward launch");
   return ok();
 }
@@ -219,7 +219,8 @@ int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL handle");
   if (!bytes) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL bytes");
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: n out of range");
-  *bytes = h->kind == HASHENC_DLINEAR ? hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n) : 0;
+  *bytes = h->kind == HASHENC_DLINEAR ? hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n)
+                                      : hg::hermite_packed_bytes(h->grid, h->d, h->F);
   return ok();
 }
 
@@ -227,8 +228,29 @@ int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float*
                        float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
                        hashenc_stream_t stream) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_ws: NULL handle");
-  if (h->kind != HASHENC_DLINEAR || !gamma || n == 0)
-    return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
+  if (h->kind == HASHENC_HERMITE) {
+    // packed copy of the order tables in the workspace (equal table sizes), else as hashenc_forward
+    const size_t need = hg::hermite_packed_bytes(h->grid, h->d, h->F);
+    if (need == 0 || n == 0 || (!gamma && !dgamma && !d2gamma))
+      return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
+    if (n < 0 || n > kMaxPoints)
+      return fail(HASHENC_EINVAL, "hashenc_forward_ws: n = %lld out of range", (long long)n);
+    if (!x || !params || !workspace)
+      return fail(HASHENC_EINVAL, "hashenc_forward_ws: x, params and workspace must not be NULL");
+    if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || !aligned16(dgamma) || !aligned16(d2gamma) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+      return fail(HASHENC_EALIGN, "hashenc_forward_ws: pointers must be 16-byte aligned (workspace 256-byte)");
+    if (workspace_bytes < need)
+      return fail(HASHENC_EINVAL, "hashenc_forward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    float* packed = static_cast<float*>(workspace);
+    hipError_t e = hg::launch_hermite_pack(h->grid, h->d, h->F, params, packed, stream);
+    if (e == hipSuccess)
+      e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, packed, gamma, dgamma,
+                                     d2gamma, stream);
+    if (e != hipSuccess) return hip_fail(e, "hashenc_forward_ws launch");
+    return ok();
+  }
+  if (!gamma || n == 0) return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_ws: n = %lld out of range", (long long)n);
   if (dgamma || d2gamma)
     return fail(HASHENC_EUNSUPPORTED, "hashenc_forward_ws: derivative outputs need the Hermite kind");

@@ -129,8 +129,14 @@ hipError_t launch_dlinear_forward(const Grid& g, int d, int F, int64_t n, const 
                                   const float* params, float* gamma, float* scratch, hipStream_t s);
 hipError_t launch_dlinear_backward(const Grid& g, int d, int F, int64_t n, const float* x,
                                    const float* g_gamma, float* grad, hipStream_t s);
+// Hermite tables of equal size: the packed copy (one contiguous row of all order tables per
+// vertex) that the forward can read instead of the tables; 0 bytes when not packable.
+bool hermite_packable(const Grid& g, int d);
+size_t hermite_packed_bytes(const Grid& g, int d, int F);
+hipError_t launch_hermite_pack(const Grid& g, int d, int F, const float* params, float* packed, hipStream_t s);
+// packed: NULL to read params directly, else the packed copy of params
 hipError_t launch_hermite_forward(const Grid& g, int d, int F, int d2_mode, int64_t n,
-                                  const float* x, const float* params, float* gamma,
+                                  const float* x, const float* params, const float* packed, float* gamma,
                                   float* dgamma, float* d2gamma, hipStream_t s);
 hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int64_t n,
                                    const float* x, const float* g_gamma, const float* g_dgamma,

@@ -116,6 +116,54 @@ __device__ __forceinline__ void gather_corner(const Grid& g, const CellKeys<D>& 
     load_vec<F>(ts.base[3] + (size_t)corner_row<D, C>(keys, ts.dense[3], g.T[3], g.Tmask[3]) * F, cr.r3);
 }
 
+// Packed copy of the order tables, for handles whose tables all have the same size (then a
+// vertex has the same row in every order table): row r of level l holds [order 0: F |
+// order 1: C(d,1) F | order 2: C(d,2) F | order 3: F] contiguously, 2^d F floats (one 64-byte
+// sector for d = 3, F = 2), so the forward reads a corner's coefficients in one contiguous
+// access instead of one per order table.
+struct PackPlan {
+  int64_t poff[kMaxLevels + 1];  // float offset of level l in the packed copy
+};
+
+template <int D, int F>
+__device__ __forceinline__ void gather_corner_packed(const float* __restrict__ base, uint32_t row,
+                                                     CornerRows<D, F>& cr) {
+  constexpr int W1 = binom_d(D, 1) * F, W2 = binom_d(D, 2) * F;
+  constexpr int RW = (1 << D) * F;
+  float v[RW];
+  load_vec<RW>(base + (size_t)row * RW, v);
+#pragma unroll
+  for (int j = 0; j < F; ++j) cr.r0[j] = v[j];
+#pragma unroll
+  for (int j = 0; j < W1; ++j) cr.r1[j] = v[F + j];
+#pragma unroll
+  for (int j = 0; j < W2; ++j) cr.r2[j] = v[F + W1 + j];
+  if constexpr (D == 3) {
+#pragma unroll
+    for (int j = 0; j < F; ++j) cr.r3[j] = v[F + W1 + W2 + j];
+  }
+}
+
+// One thread per packed row: gather the row's slots from the d + 1 order tables.
+template <int D, int F>
+__global__ __launch_bounds__(kBlock) void hermite_pack_kernel(const Grid g, const PackPlan pp,
+                                                              const float* __restrict__ params,
+                                                              float* __restrict__ packed) {
+  constexpr int W1 = binom_d(D, 1) * F, W2 = binom_d(D, 2) * F;
+  constexpr int RW = (1 << D) * F;
+  const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (t * RW >= pp.poff[g.L]) return;
+  int l = 0;
+  while (l + 1 < g.L && t * RW >= pp.poff[l + 1]) ++l;
+  const int64_t r = t - pp.poff[l] / RW;
+  float v[RW];
+  load_vec_at<F>(params + g.off[0][l] + r * F, v, 0);
+  load_vec_at<W1>(params + g.off[1][l] + r * W1, v, F);
+  load_vec_at<W2>(params + g.off[2][l] + r * W2, v, F + W1);
+  if constexpr (D == 3) load_vec_at<F>(params + g.off[3][l] + r * F, v, F + W1 + W2);
+  store_vec<RW>(packed + pp.poff[l] + r * RW, v);
+}
+
 template <int D, int F, int C>
 __device__ __forceinline__ void scatter_corner(const Grid& g, const CellKeys<D>& keys,
                                                float* const (&base)[kMaxTables],
@@ -150,12 +198,18 @@ struct LevelOut {
 
 // Accumulate the contribution of the x-adjacent corner pair (0, Y) with Y the corner bits
 // of axes 1.. (Y = c1 | c2 << 1).
-template <int D, int F, int Y>
+template <int D, int F, int Y, bool PACKED>
 __device__ __forceinline__ void fwd_pair(const Grid& g, const CellKeys<D>& keys, const TableSel& ts,
-                                         const AxisBasis (&ab)[D], LevelOut<D, F>& o) {
+                                         const float* __restrict__ pbase, const AxisBasis (&ab)[D],
+                                         LevelOut<D, F>& o) {
   CornerRows<D, F> lo, hi;
-  gather_corner<D, F, (Y << 1)>(g, keys, ts, lo);
-  gather_corner<D, F, (Y << 1) | 1>(g, keys, ts, hi);
+  if constexpr (PACKED) {
+    gather_corner_packed<D, F>(pbase, corner_row<D, (Y << 1)>(keys, ts.dense[0], g.T[0], g.Tmask[0]), lo);
+    gather_corner_packed<D, F>(pbase, corner_row<D, (Y << 1) | 1>(keys, ts.dense[0], g.T[0], g.Tmask[0]), hi);
+  } else {
+    gather_corner<D, F, (Y << 1)>(g, keys, ts, lo);
+    gather_corner<D, F, (Y << 1) | 1>(g, keys, ts, hi);
+  }
   constexpr int c1 = Y & 1;
   constexpr int c2 = (Y >> 1) & 1;
   constexpr int NA = 1 << (D - 1);  // derivative patterns over axes 1..D-1
@@ -221,9 +275,11 @@ __device__ __forceinline__ void level_setup(const Grid& g, int l, const float (&
 
 // Level-major order as in the d-linear forward: workgroup b handles level b / n_tiles, so
 // the chip streams one level's order tables at a time (they stay in L2 / Infinity Cache).
-template <int D, int F>
+// PACKED: read the corner rows from the packed copy (params points at it; pp gives the
+// level offsets) instead of the d + 1 order tables.
+template <int D, int F, bool PACKED>
 __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
-    const Grid g, int64_t n, int32_t n_tiles, int d2_mode, const float* __restrict__ x,
+    const Grid g, const PackPlan pp, int64_t n, int32_t n_tiles, int d2_mode, const float* __restrict__ x,
     const float* __restrict__ params, float* __restrict__ gamma, float* __restrict__ dgamma,
     float* __restrict__ d2gamma) {
   const int l = blockIdx.x / n_tiles;
@@ -249,11 +305,12 @@ __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
 #pragma unroll
     for (int i = 0; i < D; ++i) o.g[i][f] = o.h[i][f] = 0.0f;
   }
-  fwd_pair<D, F, 0>(g, keys, ts, ab, o);
-  fwd_pair<D, F, 1>(g, keys, ts, ab, o);
+  const float* pbase = PACKED ? params + pp.poff[l] : nullptr;
+  fwd_pair<D, F, 0, PACKED>(g, keys, ts, pbase, ab, o);
+  fwd_pair<D, F, 1, PACKED>(g, keys, ts, pbase, ab, o);
   if constexpr (D == 3) {
-    fwd_pair<D, F, 2>(g, keys, ts, ab, o);
-    fwd_pair<D, F, 3>(g, keys, ts, ab, o);
+    fwd_pair<D, F, 2, PACKED>(g, keys, ts, pbase, ab, o);
+    fwd_pair<D, F, 3, PACKED>(g, keys, ts, pbase, ab, o);
   }
   const int64_t col = (int64_t)l * F;
   if (gamma) store_vec<F>(gamma + p * LF + col, o.v);
@@ -737,14 +794,16 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
   __syncthreads();
   const int32_t ebase = st->seg_ebase[sg];
   float* vseg = vals_out + st->seg_vbase[sg];
-  // copy out in pieces of V floats (as wide as the record width's alignment allows)
-  constexpr int V = R % 4 == 0 ? 4 : R % 2 == 0 ? 2 : 1;
-  const int32_t pieces = np * NC * (R / V);
-  for (int32_t e = threadIdx.x; e < pieces; e += P) {
-    const int32_t q = e / (R / V), j = (e - q * (R / V)) * V;
-    float v[V];
-    load_vec<V>(sh.st_rec + (int64_t)q * R + j, v);
-    store_vec<V>(vseg + (int64_t)(sh.st_pos[q] - ebase) * R + j, v);
+  // copy out one record per lane: consecutive lanes hold consecutive records of a bin's run,
+  // so the R stores of a wavefront fill the run's lines between them
+  const int32_t recs = np * NC;
+  for (int32_t q = threadIdx.x; q < recs; q += P) {
+    float v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = sh.st_rec[(int64_t)q * R + j];
+    float* dst = vseg + (int64_t)(sh.st_pos[q] - ebase) * R;
+#pragma unroll
+    for (int j = 0; j < R; ++j) dst[j] = v[j];
   }
   __syncthreads();
 }
@@ -833,14 +892,42 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   return hipGetLastError();
 }
 
+PackPlan make_pack_plan(const Grid& g, int d, int F) {
+  PackPlan pp;
+  pp.poff[0] = 0;
+  for (int l = 0; l < g.L; ++l) {
+    int64_t rows = g.T[0];
+    if ((g.dense[0] >> l) & 1u) {
+      rows = 1;
+      for (int i = 0; i < d; ++i) rows *= (int64_t)g.N[l] + 1;
+    }
+    pp.poff[l + 1] = pp.poff[l] + rows * ((int64_t)1 << d) * F;
+  }
+  return pp;
+}
+
+template <int D, int F>
+hipError_t launch_pack(const Grid& g, const float* params, float* packed, hipStream_t s) {
+  const PackPlan pp = make_pack_plan(g, D, F);
+  const int64_t rows = pp.poff[g.L] / ((1 << D) * F);
+  hipLaunchKernelGGL((hermite_pack_kernel<D, F>), dim3((unsigned)((rows + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                     g, pp, params, packed);
+  return hipGetLastError();
+}
+
 template <int D, int F>
 hipError_t launch_fwd(const Grid& g, int d2_mode, int64_t n, const float* x, const float* params,
-                      float* gamma, float* dgamma, float* d2gamma, hipStream_t s) {
+                      const float* packed, float* gamma, float* dgamma, float* d2gamma, hipStream_t s) {
   const int64_t tiles = (n + kBlock - 1) / kBlock;
   if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles * g.L));
-  hipLaunchKernelGGL((hermite_forward_kernel<D, F>), grid, dim3(kBlock), 0, s, g, n, (int32_t)tiles, d2_mode, x,
-                     params, gamma, dgamma, d2gamma);
+  const PackPlan pp = make_pack_plan(g, D, F);
+  if (packed)
+    hipLaunchKernelGGL((hermite_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, pp, n, (int32_t)tiles,
+                       d2_mode, x, packed, gamma, dgamma, d2gamma);
+  else
+    hipLaunchKernelGGL((hermite_forward_kernel<D, F, false>), grid, dim3(kBlock), 0, s, g, pp, n, (int32_t)tiles,
+                       d2_mode, x, params, gamma, dgamma, d2gamma);
   return hipGetLastError();
 }
 
@@ -875,10 +962,24 @@ hipError_t launch_bwd(const Grid& g, int d2_mode, int64_t n, const float* x, con
     return hipErrorInvalidValue;                 \
   } while (0)
 
+bool hermite_packable(const Grid& g, int d) {
+  for (int k = 1; k <= d; ++k)
+    if (g.T[k] != g.T[0]) return false;
+  return true;
+}
+
+size_t hermite_packed_bytes(const Grid& g, int d, int F) {
+  return hermite_packable(g, d) ? sizeof(float) * (size_t)make_pack_plan(g, d, F).poff[g.L] : 0;
+}
+
+hipError_t launch_hermite_pack(const Grid& g, int d, int F, const float* params, float* packed, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_pack, g, params, packed, s);
+}
+
 hipError_t launch_hermite_forward(const Grid& g, int d, int F, int d2_mode, int64_t n,
-                                  const float* x, const float* params, float* gamma,
+                                  const float* x, const float* params, const float* packed, float* gamma,
                                   float* dgamma, float* d2gamma, hipStream_t s) {
-  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, d2_mode, n, x, params, gamma, dgamma, d2gamma, s);
+  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, d2_mode, n, x, params, packed, gamma, dgamma, d2gamma, s);
 }
 
 hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int64_t n,

@@ -695,7 +695,7 @@ constexpr int kSirenBlocks = 256;  // one workgroup per CU (LDS-limited)
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct WorkspaceLayout {
-  size_t enc_g, enc_d, enc_l, up_g, up_d, up_l, partial, slices, bins, total;
+  size_t enc_g, enc_d, enc_l, up_g, up_d, up_l, partial, slices, packed, bins, total;
 };
 
 WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t n_mlp, bool binned) {
@@ -713,6 +713,7 @@ WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t
   w.partial = take(sizeof(float) * (size_t)kSirenBlocks * kMaxWavesPerBlock * (n_mlp + 1));
   w.slices = take(sizeof(double) * (size_t)((kSirenBlocks * kMaxWavesPerBlock + kSliceRows - 1) / kSliceRows) *
                   (n_mlp + 1));
+  w.packed = take(hermite_packed_bytes(g, d, F));  // packed order tables for the forward
   w.bins = take(binned ? binned_backward_workspace_bytes(g, d, F, true, c) : 0);
   w.total = off;
   return w;
@@ -815,10 +816,16 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
   float* ul = reinterpret_cast<float*>(ws + wl.up_l);
   float* partial = reinterpret_cast<float*>(ws + wl.partial);
   const double inv_n = 1.0 / (double)n;
+  // the parameters do not change between chunks: pack the order tables once
+  float* packed = hermite_packed_bytes(g, d, F) ? reinterpret_cast<float*>(ws + wl.packed) : nullptr;
+  if (packed) {
+    hipError_t e = launch_hermite_pack(g, d, F, params, packed, s);
+    if (e != hipSuccess) return e;
+  }
   for (int64_t p0 = 0; p0 < n; p0 += kChunk) {
     const int64_t c = (n - p0) < kChunk ? (n - p0) : kChunk;
     const float* xc = x + p0 * d;
-    hipError_t e = launch_hermite_forward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, params, eg, ed, el, s);
+    hipError_t e = launch_hermite_forward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, params, packed, eg, ed, el, s);
     if (e != hipSuccess) return e;
     float* rc = residual ? residual + p0 : nullptr;
     int rows = 0;  // partial rows written (per wavefront or per workgroup)

@@ -149,7 +149,7 @@ def test_forward_parity(orc, name):
         _blocks_close(got["d2gamma"], d2, spec, FWD_TOL, "d2gamma")
 
 
-@pytest.mark.parametrize("name", ["dlinear2d_L4_T12", "dlinear3d_L16_T19", "hermite2d_L8_T14"])
+@pytest.mark.parametrize("name", ["dlinear2d_L4_T12", "dlinear3d_L16_T19", "hermite2d_L8_T14", "hermite3d_L16_T19"])
 def test_forward_ws_matches_forward(orc, name):
     spec = I.WORKLOADS[name]["spec"]
     lay = orc.layout(spec)
@@ -217,6 +217,12 @@ def test_feature_widths(orc, kind, F):  # both backward paths
     if kind == "hermite":
         _blocks_close(got["dgamma"], dg, spec, FWD_TOL, "dgamma")
         _blocks_close(got["d2gamma"], d2, spec, FWD_TOL, "d2gamma")
+    # the workspace forward (packed order tables for Hermite) gives the same bits
+    enc = api.HashGridEncoding(spec)
+    ws_out = enc.forward_ws(_dev(x), _dev(params), workspace=enc.workspace(x.shape[0]))
+    torch.cuda.synchronize()
+    for k in got:
+        assert np.array_equal(ws_out[k].cpu().numpy(), got[k]), k
     ups = [u.astype(np.float32) for u in
            (rng.standard_normal(s) for s in _upstream_shapes(spec, 777))]
     ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
@@ -236,6 +242,12 @@ def test_hermite_unequal_tables(orc, T):
     got = _gpu_forward(spec, x, params)
     for name, r in zip(("gamma", "dgamma", "d2gamma"), orc.forward(spec, x, params)):
         _blocks_close(got[name], r, spec, FWD_TOL, name)
+    enc = api.HashGridEncoding(spec)
+    assert api.hashenc_forward_workspace_size(enc.handle, 3000) == 0  # unequal tables: nothing to pack
+    ws_out = enc.forward_ws(_dev(x), _dev(params))
+    torch.cuda.synchronize()
+    for k in got:
+        assert np.array_equal(ws_out[k].cpu().numpy(), got[k]), k
     ups = [u.astype(np.float32) for u in (rng.standard_normal(s) for s in _upstream_shapes(spec, 3000))]
     ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
     for path in PATHS:
