@@ -447,9 +447,11 @@ size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite
 
 hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2_mode, int64_t n,
                                const float* x, const float* g_gamma, const float* g_dgamma,
-                               const float* g_d2gamma, float* grad, void* workspace, hipStream_t s) {
+                               const float* g_d2gamma, const float* u_levels, float* grad, void* workspace,
+                               hipStream_t s) {
   BinPlan bp;
   make_bin_plan(g, d, F, hermite, bp);
+  if (u_levels && (!hermite || n > kBinChunkPoints)) return hipErrorInvalidValue;  // one chunk only
   char* ws = static_cast<char*>(workspace);
   const int64_t LF = (int64_t)g.L * F;
   for (int64_t p0 = 0; p0 < n; p0 += kBinChunkPoints) {
@@ -461,7 +463,8 @@ hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2
     const float* gd = g_dgamma ? g_dgamma + p0 * d * LF : nullptr;
     const float* g2 = g_d2gamma ? g_d2gamma + p0 * (d2_mode == HASHENC_D2_DIAG ? d : 1) * LF : nullptr;
     for (int pass = 0; pass < 2; ++pass) {
-      hipError_t e = hermite ? launch_hermite_bin(g, bp, w, ws, d, F, d2_mode, pass == 1, c, xc, gg, gd, g2, s)
+      hipError_t e = hermite ? launch_hermite_bin(g, bp, w, ws, d, F, d2_mode, pass == 1, c, xc, gg, gd, g2,
+                                                  u_levels, s)
                              : launch_dlinear_bin(g, bp, w, ws, d, F, pass == 1, c, xc, gg, s);
       if (e != hipSuccess) return e;
       if (pass == 0) {

@@ -63,6 +63,13 @@ constexpr int64_t kMaxPoints = int64_t(1) << 33;
 
 }  // namespace
 
+// Hermite forward_ws workspace: the packed order tables (when their sizes are equal), then
+// the level-major output staging.
+static size_t hermite_forward_ws_bytes(const hashenc* h, int64_t n) {
+  const size_t pk = hg::hermite_packed_bytes(h->grid, h->d, h->F);
+  return ((pk + 255) & ~size_t(255)) + hg::hermite_stage_bytes(h->grid, h->d, h->F, h->d2_mode, n);
+}
+
 extern "C" {
 
 const char* hashenc_last_error(void) { return g_last_error.c_str(); }
@@ -209,7 +216,7 @@ int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* pa
   if (h->kind == HASHENC_DLINEAR)
     e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma, nullptr, stream);
   else
-    e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, nullptr, gamma,
+    e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, nullptr, nullptr, false, gamma,
                                    dgamma, d2gamma, stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_forward launch");
   return ok();
@@ -220,7 +227,7 @@ int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
   if (!bytes) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL bytes");
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: n out of range");
   *bytes = h->kind == HASHENC_DLINEAR ? hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n)
-                                      : hg::hermite_packed_bytes(h->grid, h->d, h->F);
+                                      : hermite_forward_ws_bytes(h, n);
   return ok();
 }
 
@@ -229,9 +236,9 @@ int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float*
                        hashenc_stream_t stream) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_ws: NULL handle");
   if (h->kind == HASHENC_HERMITE) {
-    // packed copy of the order tables in the workspace (equal table sizes), else as hashenc_forward
-    const size_t need = hg::hermite_packed_bytes(h->grid, h->d, h->F);
-    if (need == 0 || n == 0 || (!gamma && !dgamma && !d2gamma))
+    // workspace: [packed copy of the order tables (equal table sizes) | level-major staging]
+    const size_t need = hermite_forward_ws_bytes(h, n);
+    if (n == 0 || (!gamma && !dgamma && !d2gamma))
       return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
     if (n < 0 || n > kMaxPoints)
       return fail(HASHENC_EINVAL, "hashenc_forward_ws: n = %lld out of range", (long long)n);
@@ -242,11 +249,13 @@ int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float*
       return fail(HASHENC_EALIGN, "hashenc_forward_ws: pointers must be 16-byte aligned (workspace 256-byte)");
     if (workspace_bytes < need)
       return fail(HASHENC_EINVAL, "hashenc_forward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
-    float* packed = static_cast<float*>(workspace);
-    hipError_t e = hg::launch_hermite_pack(h->grid, h->d, h->F, params, packed, stream);
+    const size_t pk = hg::hermite_packed_bytes(h->grid, h->d, h->F);
+    float* packed = pk ? static_cast<float*>(workspace) : nullptr;
+    float* stage = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((pk + 255) & ~size_t(255)));
+    hipError_t e = packed ? hg::launch_hermite_pack(h->grid, h->d, h->F, params, packed, stream) : hipSuccess;
     if (e == hipSuccess)
-      e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, packed, gamma, dgamma,
-                                     d2gamma, stream);
+      e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, packed, stage, true, gamma,
+                                     dgamma, d2gamma, stream);
     if (e != hipSuccess) return hip_fail(e, "hashenc_forward_ws launch");
     return ok();
   }
@@ -284,7 +293,7 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
     e = hg::launch_dlinear_backward(h->grid, h->d, h->F, n, x, g_gamma, grad_params, stream);
   else
     e = hg::launch_hermite_backward(h->grid, h->d, h->F, h->d2_mode, n, x, g_gamma, g_dgamma,
-                                         g_d2gamma, grad_params, stream);
+                                         g_d2gamma, nullptr, grad_params, stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_backward launch");
   return ok();
 }
@@ -377,7 +386,7 @@ int hashenc_backward_ws(const hashenc* h, int64_t n, const float* x, const float
   if (workspace_bytes < need)
     return fail(HASHENC_EINVAL, "hashenc_backward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
   hipError_t e = hg::run_binned_backward(h->grid, h->d, h->F, h->kind == HASHENC_HERMITE, h->d2_mode, n, x,
-                                         g_gamma, g_dgamma, g_d2gamma, grad_params, workspace, stream);
+                                         g_gamma, g_dgamma, g_d2gamma, nullptr, grad_params, workspace, stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_backward_ws launch");
   return ok();
 }

@@ -134,13 +134,18 @@ hipError_t launch_dlinear_backward(const Grid& g, int d, int F, int64_t n, const
 bool hermite_packable(const Grid& g, int d);
 size_t hermite_packed_bytes(const Grid& g, int d, int F);
 hipError_t launch_hermite_pack(const Grid& g, int d, int F, const float* params, float* packed, hipStream_t s);
-// packed: NULL to read params directly, else the packed copy of params
+// Level-major output staging of the Hermite forward: [L][n][M][F] floats, M = 1 + d + (d or 1).
+size_t hermite_stage_bytes(const Grid& g, int d, int F, int d2_mode, int64_t n);
+// packed: NULL to read params directly, else the packed copy of params.  stage: NULL to write
+// the point-major outputs directly; else the outputs go level-major into stage and, when
+// to_rows, are then rearranged into gamma / dgamma / d2gamma.
 hipError_t launch_hermite_forward(const Grid& g, int d, int F, int d2_mode, int64_t n,
-                                  const float* x, const float* params, const float* packed, float* gamma,
-                                  float* dgamma, float* d2gamma, hipStream_t s);
+                                  const float* x, const float* params, const float* packed, float* stage,
+                                  bool to_rows, float* gamma, float* dgamma, float* d2gamma, hipStream_t s);
+// u_levels: NULL, or the upstream level-major ([L][n][M][F]) in place of the three arrays
 hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int64_t n,
                                    const float* x, const float* g_gamma, const float* g_dgamma,
-                                   const float* g_d2gamma, float* grad, hipStream_t s);
+                                   const float* g_d2gamma, const float* u_levels, float* grad, hipStream_t s);
 hipError_t launch_debug_indices(const Grid& g, int d, int order, int64_t n, const float* x,
                                 int32_t* out, hipStream_t s);
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t s);

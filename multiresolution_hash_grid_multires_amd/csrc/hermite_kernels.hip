@@ -277,11 +277,14 @@ __device__ __forceinline__ void level_setup(const Grid& g, int l, const float (&
 // the chip streams one level's order tables at a time (they stay in L2 / Infinity Cache).
 // PACKED: read the corner rows from the packed copy (params points at it; pp gives the
 // level offsets) instead of the d + 1 order tables.
-template <int D, int F, bool PACKED>
+// LM: write the level's outputs level-major into stage[l][p][m][F], m = value, d gradient
+// components, then the second-derivative components (d diagonal ones or the Laplacian):
+// whole lines per workgroup, where the point-major rows take 8-byte pieces of many lines.
+template <int D, int F, bool PACKED, bool LM>
 __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
     const Grid g, const PackPlan pp, int64_t n, int32_t n_tiles, int d2_mode, const float* __restrict__ x,
     const float* __restrict__ params, float* __restrict__ gamma, float* __restrict__ dgamma,
-    float* __restrict__ d2gamma) {
+    float* __restrict__ d2gamma, float* __restrict__ stage) {
   const int l = blockIdx.x / n_tiles;
   const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
   if (p >= n) return;
@@ -311,6 +314,29 @@ __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
   if constexpr (D == 3) {
     fwd_pair<D, F, 2, PACKED>(g, keys, ts, pbase, ab, o);
     fwd_pair<D, F, 3, PACKED>(g, keys, ts, pbase, ab, o);
+  }
+  if constexpr (LM) {
+    const bool diag = d2_mode == HASHENC_D2_DIAG;
+    const int M = 1 + D + (diag ? D : 1);
+    float* dst = stage + ((int64_t)l * n + p) * M * F;
+    store_vec<F>(dst, o.v);
+#pragma unroll
+    for (int i = 0; i < D; ++i) store_vec<F>(dst + (1 + i) * F, o.g[i]);
+    if (diag) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) store_vec<F>(dst + (1 + D + i) * F, o.h[i]);
+    } else {
+      float lap[F];
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) s += o.h[i][f];
+        lap[f] = s;
+      }
+      store_vec<F>(dst + (1 + D) * F, lap);
+    }
+    return;
   }
   const int64_t col = (int64_t)l * F;
   if (gamma) store_vec<F>(gamma + p * LF + col, o.v);
@@ -559,6 +585,54 @@ __global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t
   }
 }
 
+// The forward's level-major staging [l][p][m][F] -> gamma [n, L*F], dgamma [n, d, L*F],
+// d2gamma [n, d2, L*F] (NULL outputs skipped).  A workgroup owns P consecutive points: it
+// reads each level's P * M * F contiguous floats into LDS (each point's rows in output
+// order, pitch M * L * F + 1) and writes every (point, component) row of L*F floats with
+// 16-byte stores when rows are 16-byte aligned; the P rows of one output array are
+// contiguous, so lines are written whole.
+template <int F, int D, int M>
+__global__ __launch_bounds__(kBlock) void hermite_levels_to_rows_kernel(int32_t L, int64_t n, int32_t P,
+                                                                        const float* __restrict__ stage,
+                                                                        float* __restrict__ gamma,
+                                                                        float* __restrict__ dgamma,
+                                                                        float* __restrict__ d2gamma) {
+  extern __shared__ float tile[];
+  constexpr int MF = M * F;
+  constexpr int D2 = M - 1 - D;
+  const int LF = L * F;
+  const int pitch = M * LF + 1;
+  const int64_t p0 = (int64_t)blockIdx.x * P;
+  const int np = (int)min((int64_t)P, n - p0);
+  // one thread per (level, point): its M * F contiguous floats, loaded before any is stored
+  for (int pr = threadIdx.x; pr < L * np; pr += kBlock) {
+    const int l = pr / np, i = pr - l * np;
+    float v[MF];
+    load_vec<MF>(stage + ((int64_t)l * n + p0 + i) * MF, v);
+    float* t = tile + i * pitch + l * F;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int f = 0; f < F; ++f) t[m * LF + f] = v[m * F + f];
+  }
+  __syncthreads();
+  for (int row = threadIdx.x; row < np * M; row += kBlock) {
+    const int i = row / M, m = row - i * M;
+    const int64_t p = p0 + i;
+    float* dst = m == 0 ? (gamma ? gamma + p * LF : nullptr)
+               : m <= D ? (dgamma ? dgamma + (p * D + (m - 1)) * LF : nullptr)
+                        : (d2gamma ? d2gamma + (p * D2 + (m - 1 - D)) * LF : nullptr);
+    if (!dst) continue;
+    const float* t = tile + i * pitch + m * LF;
+    if ((LF & 3) == 0) {
+      for (int c = 0; c < LF; c += 4)
+        *reinterpret_cast<float4*>(dst + c) = make_float4(t[c], t[c + 1], t[c + 2], t[c + 3]);
+    } else {
+      for (int c = 0; c < LF; ++c) dst[c] = t[c];
+    }
+  }
+}
+
 // Upstream of one point at one level from the level-major copy (the Laplacian upstream is
 // the same for every diagonal term).
 template <int D, int F>
@@ -595,18 +669,20 @@ __device__ __forceinline__ LevelUp<D, F> load_level_up_lm(const float* __restric
   return u;
 }
 
+// u_levels: NULL, or the upstream level-major ([L][n][M][F]); then the row pointers are unused.
 template <int D, int F>
 __global__ __launch_bounds__(kBlock) void hermite_backward_kernel(
     const Grid g, int64_t n, int d2_mode, const float* __restrict__ x,
     const float* __restrict__ g_gamma, const float* __restrict__ g_dgamma,
-    const float* __restrict__ g_d2gamma, float* __restrict__ grad) {
+    const float* __restrict__ g_d2gamma, const float* __restrict__ u_levels, float* __restrict__ grad) {
   const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (p >= n) return;
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
   for (int l = 0; l < g.L; ++l) {
-    const LevelUp<D, F> u = load_level_up<D, F>(g, p, l, d2_mode, g_gamma, g_dgamma, g_d2gamma);
+    const LevelUp<D, F> u = u_levels ? load_level_up_lm<D, F>(u_levels, n, p, l, d2_mode == HASHENC_D2_DIAG)
+                                     : load_level_up<D, F>(g, p, l, d2_mode, g_gamma, g_dgamma, g_d2gamma);
     CellKeys<D> keys;
     AxisBasis ab[D];
     level_setup<D>(g, l, xp, keys, ab);
@@ -848,7 +924,7 @@ __global__ __launch_bounds__(P) void hermite_scatter_kernel(
 template <int D, int F>
 hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int d2_mode,
                       bool scatter, int64_t n, const float* x, const float* gg, const float* gd,
-                      const float* g2, hipStream_t s) {
+                      const float* g2, const float* u_levels, hipStream_t s) {
   const dim3 grid((unsigned)w.nblk);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
   if (!scatter) {
@@ -864,26 +940,30 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   const int32_t* bin_start = reinterpret_cast<const int32_t*>(ws + w.bin_start);
   const BinState* st = reinterpret_cast<const BinState*>(ws + w.state);
   float* vals = reinterpret_cast<float*>(ws + w.vals);
-  // upstream rearranged level-major for the level-by-level scatter
+  // upstream rearranged level-major for the level-by-level scatter (unless given so)
   const bool diag = d2_mode == HASHENC_D2_DIAG;
   const int M = 1 + D + (diag ? D : 1);
   const int LF = g.L * F;
   const int PU = (int)std::max(1, std::min(64, 16384 / (M * LF)));  // LDS tile <= 64 KB
-  float* U = reinterpret_cast<float*>(ws + w.ups);
+  const float* U = u_levels ? u_levels : reinterpret_cast<const float*>(ws + w.ups);
+  float* Uw = reinterpret_cast<float*>(ws + w.ups);
   const size_t ulds = sizeof(float) * (size_t)PU * (M * LF + 1);
   const void* ukern = diag ? reinterpret_cast<const void*>(&hermite_upstream_levels_kernel<F, D, 1 + 2 * D>)
                            : reinterpret_cast<const void*>(&hermite_upstream_levels_kernel<F, D, 2 + D>);
-  hipError_t e = hipFuncSetAttribute(ukern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ulds);
-  if (e != hipSuccess) return e;
-  const dim3 ugrid((unsigned)((n + PU - 1) / PU));
-  if (diag)
-    hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 1 + 2 * D>), ugrid, dim3(kBlock), ulds, s, g.L, n, PU,
-                       gg, gd, g2, U);
-  else
-    hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 2 + D>), ugrid, dim3(kBlock), ulds, s, g.L, n, PU, gg,
-                       gd, g2, U);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!u_levels) {
+    e = hipFuncSetAttribute(ukern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ulds);
+    if (e != hipSuccess) return e;
+    const dim3 ugrid((unsigned)((n + PU - 1) / PU));
+    if (diag)
+      hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 1 + 2 * D>), ugrid, dim3(kBlock), ulds, s, g.L, n,
+                         PU, gg, gd, g2, Uw);
+    else
+      hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 2 + D>), ugrid, dim3(kBlock), ulds, s, g.L, n, PU,
+                         gg, gd, g2, Uw);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hermite_scatter_kernel<D, F, P>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -915,28 +995,56 @@ hipError_t launch_pack(const Grid& g, const float* params, float* packed, hipStr
   return hipGetLastError();
 }
 
+// stage: NULL for point-major outputs; else the level-major staging buffer, and when
+// to_rows also the rearrangement into gamma / dgamma / d2gamma
 template <int D, int F>
 hipError_t launch_fwd(const Grid& g, int d2_mode, int64_t n, const float* x, const float* params,
-                      const float* packed, float* gamma, float* dgamma, float* d2gamma, hipStream_t s) {
+                      const float* packed, float* stage, bool to_rows, float* gamma, float* dgamma,
+                      float* d2gamma, hipStream_t s) {
   const int64_t tiles = (n + kBlock - 1) / kBlock;
   if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles * g.L));
   const PackPlan pp = make_pack_plan(g, D, F);
-  if (packed)
-    hipLaunchKernelGGL((hermite_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, pp, n, (int32_t)tiles,
-                       d2_mode, x, packed, gamma, dgamma, d2gamma);
+  const float* tab = packed ? packed : params;
+  if (packed && stage)
+    hipLaunchKernelGGL((hermite_forward_kernel<D, F, true, true>), grid, dim3(kBlock), 0, s, g, pp, n,
+                       (int32_t)tiles, d2_mode, x, tab, gamma, dgamma, d2gamma, stage);
+  else if (packed)
+    hipLaunchKernelGGL((hermite_forward_kernel<D, F, true, false>), grid, dim3(kBlock), 0, s, g, pp, n,
+                       (int32_t)tiles, d2_mode, x, tab, gamma, dgamma, d2gamma, stage);
+  else if (stage)
+    hipLaunchKernelGGL((hermite_forward_kernel<D, F, false, true>), grid, dim3(kBlock), 0, s, g, pp, n,
+                       (int32_t)tiles, d2_mode, x, tab, gamma, dgamma, d2gamma, stage);
   else
-    hipLaunchKernelGGL((hermite_forward_kernel<D, F, false>), grid, dim3(kBlock), 0, s, g, pp, n, (int32_t)tiles,
-                       d2_mode, x, params, gamma, dgamma, d2gamma);
+    hipLaunchKernelGGL((hermite_forward_kernel<D, F, false, false>), grid, dim3(kBlock), 0, s, g, pp, n,
+                       (int32_t)tiles, d2_mode, x, tab, gamma, dgamma, d2gamma, stage);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !stage || !to_rows) return e;
+  const bool diag = d2_mode == HASHENC_D2_DIAG;
+  const int M = 1 + D + (diag ? D : 1);
+  const int LF = g.L * F;
+  const int P = (int)std::max(1, std::min(64, 16384 / (M * LF)));  // LDS tile <= 64 KB
+  const size_t lds = sizeof(float) * (size_t)P * (M * LF + 1);
+  const void* kern = diag ? reinterpret_cast<const void*>(&hermite_levels_to_rows_kernel<F, D, 1 + 2 * D>)
+                          : reinterpret_cast<const void*>(&hermite_levels_to_rows_kernel<F, D, 2 + D>);
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const dim3 tgrid((unsigned)((n + P - 1) / P));
+  if (diag)
+    hipLaunchKernelGGL((hermite_levels_to_rows_kernel<F, D, 1 + 2 * D>), tgrid, dim3(kBlock), lds, s, g.L, n, P,
+                       stage, gamma, dgamma, d2gamma);
+  else
+    hipLaunchKernelGGL((hermite_levels_to_rows_kernel<F, D, 2 + D>), tgrid, dim3(kBlock), lds, s, g.L, n, P, stage,
+                       gamma, dgamma, d2gamma);
   return hipGetLastError();
 }
 
 template <int D, int F>
 hipError_t launch_bwd(const Grid& g, int d2_mode, int64_t n, const float* x, const float* gg,
-                      const float* gd, const float* gdd, float* grad, hipStream_t s) {
+                      const float* gd, const float* gdd, const float* u_levels, float* grad, hipStream_t s) {
   const dim3 grid((unsigned)((n + kBlock - 1) / kBlock));
   hipLaunchKernelGGL((hermite_backward_kernel<D, F>), grid, dim3(kBlock), 0, s, g, n, d2_mode, x,
-                     gg, gd, gdd, grad);
+                     gg, gd, gdd, u_levels, grad);
   return hipGetLastError();
 }
 
@@ -976,22 +1084,29 @@ hipError_t launch_hermite_pack(const Grid& g, int d, int F, const float* params,
   HASHENC_DISPATCH_DF(d, F, launch_pack, g, params, packed, s);
 }
 
+size_t hermite_stage_bytes(const Grid& g, int d, int F, int d2_mode, int64_t n) {
+  const int M = 1 + d + (d2_mode == HASHENC_D2_DIAG ? d : 1);
+  return sizeof(float) * (size_t)n * g.L * M * F;
+}
+
 hipError_t launch_hermite_forward(const Grid& g, int d, int F, int d2_mode, int64_t n,
-                                  const float* x, const float* params, const float* packed, float* gamma,
-                                  float* dgamma, float* d2gamma, hipStream_t s) {
-  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, d2_mode, n, x, params, packed, gamma, dgamma, d2gamma, s);
+                                  const float* x, const float* params, const float* packed, float* stage,
+                                  bool to_rows, float* gamma, float* dgamma, float* d2gamma, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, d2_mode, n, x, params, packed, stage, to_rows, gamma, dgamma, d2gamma,
+                      s);
 }
 
 hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int64_t n,
                                    const float* x, const float* g_gamma, const float* g_dgamma,
-                                   const float* g_d2gamma, float* grad, hipStream_t s) {
-  HASHENC_DISPATCH_DF(d, F, launch_bwd, g, d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, grad, s);
+                                   const float* g_d2gamma, const float* u_levels, float* grad, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_bwd, g, d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, u_levels, grad, s);
 }
 
 hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int d, int F,
                               int d2_mode, bool scatter, int64_t n, const float* x, const float* g_gamma,
-                              const float* g_dgamma, const float* g_d2gamma, hipStream_t s) {
-  HASHENC_DISPATCH_DF(d, F, launch_bin, g, bp, w, ws, d2_mode, scatter, n, x, g_gamma, g_dgamma, g_d2gamma, s);
+                              const float* g_dgamma, const float* g_d2gamma, const float* u_levels, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_bin, g, bp, w, ws, d2_mode, scatter, n, x, g_gamma, g_dgamma, g_d2gamma, u_levels,
+                      s);
 }
 
 }  // namespace hg

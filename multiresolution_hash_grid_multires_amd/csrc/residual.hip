@@ -34,6 +34,7 @@ constexpr int kMaxDepth = 4;
 
 struct MlpArgs {
   int32_t in, H, depth;
+  int32_t fshift;  // log2 F: encoder feature j is feature j % F of level j / F
   float omega;
   int64_t n_mlp;
   int64_t woff[kMaxDepth + 1], boff[kMaxDepth + 1];
@@ -50,6 +51,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Encoder outputs and their upstream are level-major, [L][n][R][F] (R = value, d gradient
+// rows, Laplacian): the index of feature j = l F + f, row r of point p.
+__device__ __forceinline__ int64_t lm_index(const MlpArgs& a, int64_t n, int64_t p, int j, int r, int R) {
+  const int l = j >> a.fshift, f = j & ((1 << a.fshift) - 1);
+  return (((int64_t)l * n + p) * R + r << a.fshift) + f;
 }
 
 // Points per wavefront iteration: every LDS weight read feeds PB * R FMAs and the
@@ -84,9 +92,8 @@ struct SirenLds {
 template <int D, int DEPTH, int INP>
 __global__ __launch_bounds__(kW * siren_waves(DEPTH, INP)) void siren_residual_kernel(
     const MlpArgs a, int64_t n, double inv_n_total, const float* __restrict__ x,
-    const float* __restrict__ enc_g, const float* __restrict__ enc_d, const float* __restrict__ enc_l,
-    const float* __restrict__ mlp, float* __restrict__ up_g, float* __restrict__ up_d,
-    float* __restrict__ up_l, float* __restrict__ residual, float* __restrict__ partial) {
+    const float* __restrict__ enc, const float* __restrict__ mlp, float* __restrict__ up,
+    float* __restrict__ residual, float* __restrict__ partial) {
   using Sh = SirenLds<D, DEPTH, INP>;
   constexpr int R = Sh::R;
   constexpr int RB = Sh::RB;
@@ -138,10 +145,8 @@ __global__ __launch_bounds__(kW * siren_waves(DEPTH, INP)) void siren_residual_k
       for (int b = 0; b < kPB; ++b) {
         const int64_t p = p0 + b;
         const bool on = lane < LF && p < n;
-        row[b * R] = on ? enc_g[p * LF + lane] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < D; ++i) row[b * R + 1 + i] = on ? enc_d[(p * D + i) * LF + lane] : 0.0f;
-        row[b * R + R - 1] = on ? enc_l[p * LF + lane] : 0.0f;
+        for (int r = 0; r < R; ++r) row[b * R + r] = on ? enc[lm_index(a, n, p, lane, r, R)] : 0.0f;
       }
 #pragma unroll
       for (int q = 0; q < RB; q += 4)
@@ -311,10 +316,8 @@ __global__ __launch_bounds__(kW * siren_waves(DEPTH, INP)) void siren_residual_k
       for (int b = 0; b < kPB; ++b) {
         const int64_t p = p0 + b;
         if (p >= n) break;
-        up_g[p * LF + lane] = ab[b * R];
 #pragma unroll
-        for (int i = 0; i < D; ++i) up_d[(p * D + i) * LF + lane] = ab[b * R + 1 + i];
-        up_l[p * LF + lane] = ab[b * R + R - 1];
+        for (int r = 0; r < R; ++r) up[lm_index(a, n, p, lane, r, R)] = ab[b * R + r];
       }
     }
   }
@@ -386,9 +389,8 @@ __device__ __forceinline__ mf4 mfma16(float a, float b, mf4 c) {
 template <int D, int DEPTH, int NI>
 __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
     const MlpArgs a, int64_t n, double inv_n_total, const float* __restrict__ x,
-    const float* __restrict__ enc_g, const float* __restrict__ enc_d, const float* __restrict__ enc_l,
-    const float* __restrict__ mlp, float* __restrict__ up_g, float* __restrict__ up_d,
-    float* __restrict__ up_l, float* __restrict__ residual, float* __restrict__ partial) {
+    const float* __restrict__ enc, const float* __restrict__ mlp, float* __restrict__ up,
+    float* __restrict__ residual, float* __restrict__ partial) {
   static_assert(DEPTH == 1 || DEPTH == 2, "matrix-core SIREN covers one or two hidden layers");
   constexpr int R = D + 2;
   constexpr int NC = kMP * R;  // columns
@@ -436,18 +438,15 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
   const int64_t n_iter = (n + kMP - 1) / kMP;
   for (int64_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
     const int64_t p0 = it * kMP;
-    // encoder rows -> V_0[j][16 r + p]
+    // encoder rows -> V_0[j][16 r + p]; walked level by level, the 16 points' R rows of F
+    // features of one level being contiguous in the level-major encoder output
     for (int e = threadIdx.x; e < kMP * R * NI; e += kW * kMWaves) {
-      const int j = e % NI, t2 = e / NI;
-      const int r = t2 % R, p = t2 / R;
+      const int f = e & ((1 << a.fshift) - 1), t = e >> a.fshift;
+      const int r = t % R, t2 = t / R;
+      const int p = t2 % kMP, l = t2 / kMP;
+      const int j = (l << a.fshift) + f;
       const int64_t pp = p0 + p;
-      float v = 0.0f;
-      if (j < LF && pp < n) {
-        if (r == 0) v = enc_g[pp * LF + j];
-        else if (r <= D) v = enc_d[(pp * D + (r - 1)) * LF + j];
-        else v = enc_l[pp * LF + j];
-      }
-      sh.act0[j][r * kMP + p] = v;
+      sh.act0[j][r * kMP + p] = (j < LF && pp < n) ? enc[lm_index(a, n, pp, j, r, R)] : 0.0f;
     }
     __syncthreads();
 
@@ -597,10 +596,8 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
         for (int i = 0; i < 4; ++i) {
           const int j = 16 * w + 4 * lq + i;
           if (j < LF) {
-            up_g[pp * LF + j] = vbar[0][i];
 #pragma unroll
-            for (int r = 1; r <= D; ++r) up_d[(pp * D + (r - 1)) * LF + j] = vbar[r][i];
-            up_l[pp * LF + j] = vbar[R - 1][i];
+            for (int r = 0; r < R; ++r) up[lm_index(a, n, pp, j, r, R)] = vbar[r][i];
           }
         }
       }
@@ -695,7 +692,7 @@ constexpr int kSirenBlocks = 256;  // one workgroup per CU (LDS-limited)
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct WorkspaceLayout {
-  size_t enc_g, enc_d, enc_l, up_g, up_d, up_l, partial, slices, packed, bins, total;
+  size_t enc, up, partial, slices, packed, bins, total;
 };
 
 WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t n_mlp, bool binned) {
@@ -704,12 +701,9 @@ WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t
   WorkspaceLayout w;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
-  w.enc_g = take(sizeof(float) * c * LF);
-  w.enc_d = take(sizeof(float) * c * d * LF);
-  w.enc_l = take(sizeof(float) * c * LF);
-  w.up_g = take(sizeof(float) * c * LF);
-  w.up_d = take(sizeof(float) * c * d * LF);
-  w.up_l = take(sizeof(float) * c * LF);
+  // encoder outputs and their upstream, level-major [L][c][d + 2][F] (value, gradient, Laplacian)
+  w.enc = take(sizeof(float) * c * LF * (d + 2));
+  w.up = take(sizeof(float) * c * LF * (d + 2));
   w.partial = take(sizeof(float) * (size_t)kSirenBlocks * kMaxWavesPerBlock * (n_mlp + 1));
   w.slices = take(sizeof(double) * (size_t)((kSirenBlocks * kMaxWavesPerBlock + kSliceRows - 1) / kSliceRows) *
                   (n_mlp + 1));
@@ -720,16 +714,15 @@ WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t
 }
 
 template <int D, int DEPTH, int INP>
-hipError_t launch_siren(const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* eg,
-                        const float* ed, const float* el, const float* mlp, float* ug, float* ud,
-                        float* ul, float* residual, float* partial, int& rows, hipStream_t s) {
+hipError_t launch_siren(const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* enc,
+                        const float* mlp, float* up, float* residual, float* partial, int& rows, hipStream_t s) {
   if constexpr (DEPTH <= 2) {
     // matrix cores: one partial row per workgroup
     int blocks = (int)((n + kMP - 1) / kMP);
     if (blocks > kMfmaBlocks) blocks = kMfmaBlocks;
     rows = blocks;
     hipLaunchKernelGGL((siren_mfma_kernel<D, DEPTH, INP>), dim3(blocks), dim3(kW * kMWaves), 0, s, a, n, inv_n, x,
-                       eg, ed, el, mlp, ug, ud, ul, residual, partial);
+                       enc, mlp, up, residual, partial);
   } else {
     // vector ALUs: one partial row per wavefront
     const int wpb = siren_waves(DEPTH, INP);
@@ -737,38 +730,36 @@ hipError_t launch_siren(const MlpArgs& a, int64_t n, double inv_n, const float* 
     if (blocks > kSirenBlocks) blocks = kSirenBlocks;
     rows = blocks * wpb;
     hipLaunchKernelGGL((siren_residual_kernel<D, DEPTH, INP>), dim3(blocks), dim3(kW * wpb), 0, s, a, n, inv_n, x,
-                       eg, ed, el, mlp, ug, ud, ul, residual, partial);
+                       enc, mlp, up, residual, partial);
   }
   return hipGetLastError();
 }
 
 template <int D, int DEPTH>
-hipError_t dispatch_in(int in, const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* eg,
-                       const float* ed, const float* el, const float* mlp, float* ug, float* ud, float* ul,
+hipError_t dispatch_in(int in, const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* enc, const float* mlp, float* up,
                        float* residual, float* partial, int& rows, hipStream_t s) {
-  if (in <= 16) return launch_siren<D, DEPTH, 16>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
-  if (in <= 32) return launch_siren<D, DEPTH, 32>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
-  return launch_siren<D, DEPTH, 64>(a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
+  if (in <= 16) return launch_siren<D, DEPTH, 16>(a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
+  if (in <= 32) return launch_siren<D, DEPTH, 32>(a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
+  return launch_siren<D, DEPTH, 64>(a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
 }
 
 template <int D>
 hipError_t dispatch_depth(int depth, int in, const MlpArgs& a, int64_t n, double inv_n, const float* x,
-                          const float* eg, const float* ed, const float* el, const float* mlp, float* ug,
-                          float* ud, float* ul, float* residual, float* partial, int& rows, hipStream_t s) {
+                          const float* enc, const float* mlp, float* up, float* residual, float* partial, int& rows, hipStream_t s) {
   switch (depth) {
-    case 1: return dispatch_in<D, 1>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
-    case 2: return dispatch_in<D, 2>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
-    case 3: return dispatch_in<D, 3>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
-    default: return dispatch_in<D, 4>(in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
+    case 1: return dispatch_in<D, 1>(in, a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
+    case 2: return dispatch_in<D, 2>(in, a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
+    case 3: return dispatch_in<D, 3>(in, a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
+    default: return dispatch_in<D, 4>(in, a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
   }
 }
 
 hipError_t dispatch_siren(int d, int depth, int in, const MlpArgs& a, int64_t n, double inv_n,
-                          const float* x, const float* eg, const float* ed, const float* el,
-                          const float* mlp, float* ug, float* ud, float* ul, float* residual,
+                          const float* x, const float* enc,
+                          const float* mlp, float* up, float* residual,
                           float* partial, int& rows, hipStream_t s) {
-  if (d == 2) return dispatch_depth<2>(depth, in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
-  return dispatch_depth<3>(depth, in, a, n, inv_n, x, eg, ed, el, mlp, ug, ud, ul, residual, partial, rows, s);
+  if (d == 2) return dispatch_depth<2>(depth, in, a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
+  return dispatch_depth<3>(depth, in, a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
 }
 
 }  // namespace
@@ -797,6 +788,7 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
   a.H = H;
   a.depth = depth;
   a.omega = omega;
+  a.fshift = F == 1 ? 0 : F == 2 ? 1 : F == 4 ? 2 : 3;
   a.n_mlp = mlp_param_count(in, H, depth);
   int64_t off = 0;
   for (int k = 0; k <= kMaxDepth; ++k) { a.woff[k] = 0; a.boff[k] = 0; }
@@ -808,12 +800,8 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
   }
   const WorkspaceLayout wl = workspace_layout(g, d, F, n, a.n_mlp, binned);
   char* ws = static_cast<char*>(workspace);
-  float* eg = reinterpret_cast<float*>(ws + wl.enc_g);
-  float* ed = reinterpret_cast<float*>(ws + wl.enc_d);
-  float* el = reinterpret_cast<float*>(ws + wl.enc_l);
-  float* ug = reinterpret_cast<float*>(ws + wl.up_g);
-  float* ud = reinterpret_cast<float*>(ws + wl.up_d);
-  float* ul = reinterpret_cast<float*>(ws + wl.up_l);
+  float* enc = reinterpret_cast<float*>(ws + wl.enc);
+  float* up = reinterpret_cast<float*>(ws + wl.up);
   float* partial = reinterpret_cast<float*>(ws + wl.partial);
   const double inv_n = 1.0 / (double)n;
   // the parameters do not change between chunks: pack the order tables once
@@ -825,11 +813,13 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
   for (int64_t p0 = 0; p0 < n; p0 += kChunk) {
     const int64_t c = (n - p0) < kChunk ? (n - p0) : kChunk;
     const float* xc = x + p0 * d;
-    hipError_t e = launch_hermite_forward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, params, packed, eg, ed, el, s);
+    // Hermite forward straight into the level-major layout the SIREN kernels read
+    hipError_t e = launch_hermite_forward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, params, packed, enc, false, nullptr,
+                                          nullptr, nullptr, s);
     if (e != hipSuccess) return e;
     float* rc = residual ? residual + p0 : nullptr;
     int rows = 0;  // partial rows written (per wavefront or per workgroup)
-    e = dispatch_siren(d, depth, in, a, c, inv_n, xc, eg, ed, el, mlp, ug, ud, ul, rc, partial, rows, s);
+    e = dispatch_siren(d, depth, in, a, c, inv_n, xc, enc, mlp, up, rc, partial, rows, s);
     if (e != hipSuccess) return e;
     const int64_t n_waves = rows;
     const int n_slices = (int)((n_waves + kSliceRows - 1) / kSliceRows);
@@ -844,9 +834,11 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (grad_params) {
-      e = binned ? run_binned_backward(g, d, F, true, HASHENC_D2_LAPLACIAN, c, xc, ug, ud, ul, grad_params,
-                                       ws + wl.bins, s)
-                 : launch_hermite_backward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, ug, ud, ul, grad_params, s);
+      // the SIREN kernels wrote the upstream level-major, as the backward reads it
+      e = binned ? run_binned_backward(g, d, F, true, HASHENC_D2_LAPLACIAN, c, xc, nullptr, nullptr, nullptr, up,
+                                       grad_params, ws + wl.bins, s)
+                 : launch_hermite_backward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, nullptr, nullptr, nullptr, up,
+                                           grad_params, s);
       if (e != hipSuccess) return e;
     }
   }

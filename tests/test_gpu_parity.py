@@ -243,7 +243,8 @@ def test_hermite_unequal_tables(orc, T):
     for name, r in zip(("gamma", "dgamma", "d2gamma"), orc.forward(spec, x, params)):
         _blocks_close(got[name], r, spec, FWD_TOL, name)
     enc = api.HashGridEncoding(spec)
-    assert api.hashenc_forward_workspace_size(enc.handle, 3000) == 0  # unequal tables: nothing to pack
+    # unequal tables: nothing to pack, only the level-major staging [L][n][1 + 2d][F]
+    assert api.hashenc_forward_workspace_size(enc.handle, 3000) == 4 * 3000 * spec["L"] * 7 * spec["F"]
     ws_out = enc.forward_ws(_dev(x), _dev(params))
     torch.cuda.synchronize()
     for k in got:
