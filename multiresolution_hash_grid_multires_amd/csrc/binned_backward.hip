@@ -371,7 +371,7 @@ size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F) {
 }
 
 size_t dlinear_scatter_lds_bytes(const BinPlan& bp, int d, int F, int tile) {
-  return sizeof(int32_t) * (3 * (size_t)bp.nbins + kScatterThreads / 64) +
+  return sizeof(int32_t) * (3 * (size_t)bp.nbins + kScatterThreads / 64 + 3) +
          (size_t)tile * (1 << (d - 1)) * (sizeof(float) * (2 + F) + sizeof(int32_t));
 }
 

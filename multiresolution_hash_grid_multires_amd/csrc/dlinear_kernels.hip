@@ -274,8 +274,9 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
   int32_t* excl = lds + nbins;            // [nbins] exclusive prefix of the tile's bin counts
   int32_t* lcur = lds + 2 * nbins;        // [nbins] cursors (start at excl)
   int32_t* wsum = lds + 3 * nbins;        // [kScatterThreads / 64]
-  float* st_rec = reinterpret_cast<float*>(wsum + kScatterThreads / 64);           // [tile*NP*R]
-  int32_t* st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)tile * NP * R);  // [tile*NP]
+  // staged records start 16-byte aligned so each record moves with the widest LDS access
+  float* st_rec = reinterpret_cast<float*>(lds + ((3 * nbins + kScatterThreads / 64 + 3) & ~3));  // [tile*NP*R]
+  int32_t* st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)tile * NP * R);                  // [tile*NP]
 
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
   const int64_t p = (int64_t)blk * tile + threadIdx.x;
@@ -353,8 +354,7 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
                  const int32_t lp = s0 - lbase;
                  rec[0] = __uint_as_float(lo | (hi << 16));
                  rec[1] = t[0];
-#pragma unroll
-                 for (int q = 0; q < R; ++q) st_rec[(int64_t)lp * R + q] = rec[q];
+                 store_vec<R>(st_rec + (int64_t)lp * R, rec);
                  st_pos[lp] = gstart[bn0] + (s0 - excl[bn0]);
                } else {
                  // two single-corner records, lower row gets (1 - t) aG
@@ -376,8 +376,7 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
       const int32_t total = np * NP;
       for (int32_t q = threadIdx.x; q < total; q += kScatterThreads) {
         float rec[R];
-#pragma unroll
-        for (int c = 0; c < R; ++c) rec[c] = st_rec[(int64_t)q * R + c];
+        load_vec<R>(st_rec + (int64_t)q * R, rec);
         store_vec<R>(vseg + (int64_t)(st_pos[q] - ebase) * R, rec);
       }
       __syncthreads();
