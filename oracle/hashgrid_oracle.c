@@ -15,8 +15,9 @@
  *                     the paragraph under Figure 3 (geometric progression of levels).
  *   [HNGP]            "Hermite-NGP: Gradient-Augmented Hash Encoding for Learning
  *                     PDEs" reading notes (m0rtzz.github.io), section 方法详解,
- *                     key design 1 (reconstruction equation, 1D basis) and key
- *                     design 2 (basis derivatives, SIREN chain rule); section
+ *                     key design 1 (reconstruction equation, 1D basis), key
+ *                     design 2 (basis derivatives, SIREN chain rule) and key
+ *                     design 3 (coarse-to-fine level activation); section
  *                     损失函数 / 训练策略 (omega_0 = 30).
  *
  * Readings taken where the pages are silent or garbled (the formula bodies for
@@ -33,7 +34,10 @@
  *     C(d,k) slots of order k in lexicographic axis order, times F features;
  *   - near-corner basis is the reflection of the far-corner basis printed on
  *     the Hermite-NGP page;
- *   - colliding rows receive the sum of their contributions.
+ *   - colliding rows receive the sum of their contributions;
+ *   - coarse-to-fine activation: L_active counts the active levels (levels
+ *     l < L_active); an inactive level contributes zeros to the encoding and
+ *     receives no gradient, and the encoding keeps its full L*F width.
  *
  * Parity of the hash against any third-party implementation is unpinned (the
  * pages print no example value); it is pinned against its own definition's
@@ -59,7 +63,21 @@ typedef struct {
   int32_t d2_mode;    /* Hermite second-order output: 1 = Laplacian [n,L*F], 2 = diagonal [n,d,L*F] */
   uint32_t T[ORC_MAX_D + 1]; /* rows of table k (derivative order k); d-linear uses T[0] */
   int32_t N[ORC_MAX_LEVELS]; /* level resolutions */
+  int32_t active;     /* levels l < active are active [HNGP key design 3]; 0 = all L */
 } orc_cfg;
+
+/* Number of active levels of a configuration (0 in the field means all of them). */
+static int active_levels(const orc_cfg* c) {
+  return (c->active > 0 && c->active < c->L) ? c->active : c->L;
+}
+
+/* Coarse-to-fine schedule [HNGP key design 3]: at step t the first L0 + floor(t / tau)
+ * levels are active, at most L.  Returns -1 on L < 1, L0 < 1, t < 0 or tau < 1. */
+int32_t orc_c2f_active(int32_t L, int32_t L0, int64_t t, int64_t tau) {
+  if (L < 1 || L0 < 1 || t < 0 || tau < 1) return -1;
+  const int64_t a = (int64_t)L0 + t / tau;
+  return a < (int64_t)L ? (int32_t)a : L;
+}
 
 /* one prime per axis; the first is 1 so that the x axis maps to itself */
 static const uint32_t ORC_PRIMES[3] = {1u, 2654435761u, 805459861u};
@@ -264,7 +282,8 @@ static void corner_weights(const orc_cfg* c, int l, int cc, int alpha, const dou
 
 /* Forward encoding [INGP-explainer steps 1-4; HNGP key design 1].
  * gamma[n][L*F]; Hermite only: dgamma[n][d][L*F], d2gamma per d2_mode
- * (Laplacian [n][L*F] or diagonal [n][d][L*F]).  Any output may be NULL. */
+ * (Laplacian [n][L*F] or diagonal [n][d][L*F]).  Any output may be NULL.
+ * Columns of inactive levels (l >= active) are zero. */
 void orc_forward(const orc_cfg* c, int64_t n, const float* x, const double* params,
                  double* gamma, double* dgamma, double* d2gamma) {
   int64_t offs[(ORC_MAX_D + 1) * ORC_MAX_LEVELS];
@@ -281,7 +300,9 @@ void orc_forward(const orc_cfg* c, int64_t n, const float* x, const double* para
       double t[ORC_MAX_D];
       locate(c, l, x + p * d, base, t);
       double g0[ORC_MAX_F] = {0}, g1[ORC_MAX_F][ORC_MAX_D] = {{0}}, g2[ORC_MAX_F][ORC_MAX_D] = {{0}};
-      for (int cc = 0; cc < nc; ++cc) {
+      /* an inactive level keeps its columns at zero [HNGP key design 3] */
+      const int ncorner = l < active_levels(c) ? nc : 0;
+      for (int cc = 0; cc < ncorner; ++cc) {
         uint32_t v[ORC_MAX_D];
         for (int i = 0; i < d; ++i) v[i] = base[i] + (uint32_t)((cc >> i) & 1);
         for (int alpha = 0; alpha < na; ++alpha) {
@@ -324,7 +345,8 @@ void orc_forward(const orc_cfg* c, int64_t n, const float* x, const double* para
 /* Backward into the tables [INGP-news, adaptivity paragraph: gradients of colliding
  * vertices combine; here they sum, the exact gradient of the linear map theta -> gamma].
  * Upstream in fp64 (any may be NULL = zero); g_d2 is [n][L*F] in Laplacian mode, else
- * [n][d][L*F].  grad (fp64, same layout as params) is ACCUMULATED.  Deterministic: each
+ * [n][d][L*F].  grad (fp64, same layout as params) is ACCUMULATED; inactive levels
+ * (l >= active) are left untouched.  Deterministic: each
  * (table, level) slice is owned by one thread, points in ascending order. */
 void orc_backward_f64(const orc_cfg* c, int64_t n, const float* x, const double* g_gamma,
                       const double* g_dgamma, const double* g_d2, double* grad) {
@@ -339,6 +361,7 @@ void orc_backward_f64(const orc_cfg* c, int64_t n, const float* x, const double*
 #pragma omp parallel for schedule(dynamic, 1)
   for (int task = 0; task < ntab * c->L; ++task) {
     const int k = task / c->L, l = task % c->L;
+    if (l >= active_levels(c)) continue; /* inactive level: no gradient [HNGP key design 3] */
     for (int64_t p = 0; p < n; ++p) {
       uint32_t base[ORC_MAX_D];
       double t[ORC_MAX_D];

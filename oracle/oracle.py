@@ -14,6 +14,8 @@ returns fp64 NumPy arrays.  The spec keys are:
     growth            optional per-level growth factor b (overrides n_max)
     resolutions       optional explicit list of N_l
     d2_mode           "laplacian" or "diag" (Hermite second-order output)
+    active_levels     optional number of active levels (coarse-to-fine schedule: levels
+                      l >= active_levels encode to zero and receive no gradient)
 """
 from __future__ import annotations
 
@@ -49,6 +51,7 @@ class _Cfg(ctypes.Structure):
         ("d", ctypes.c_int32), ("L", ctypes.c_int32), ("F", ctypes.c_int32),
         ("kind", ctypes.c_int32), ("d2_mode", ctypes.c_int32),
         ("T", ctypes.c_uint32 * (MAX_D + 1)), ("N", ctypes.c_int32 * MAX_LEVELS),
+        ("active", ctypes.c_int32),
     ]
 
 
@@ -79,6 +82,8 @@ def _load():
         lib.orc_residual.restype = ctypes.c_int
         lib.orc_mlp_param_count.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         lib.orc_mlp_param_count.restype = ctypes.c_int64
+        lib.orc_c2f_active.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]
+        lib.orc_c2f_active.restype = ctypes.c_int32
         lib.orc_max_threads.argtypes = []
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -121,6 +126,10 @@ def make_cfg(spec: dict) -> _Cfg:
         c.T[k] = int(T[k])
     for l, v in enumerate(resolutions(spec)):
         c.N[l] = v
+    a = spec.get("active_levels")
+    if a is not None and not 1 <= int(a) <= c.L:
+        raise ValueError("active_levels outside 1..L")
+    c.active = 0 if a is None else int(a)
     return c
 
 
@@ -190,6 +199,14 @@ def backward(spec: dict, x: np.ndarray, g_gamma=None, g_dgamma=None, g_d2=None, 
     _load().orc_backward_f64(ctypes.byref(c), n, _ptr(x), _ptr(_f64(g_gamma)), _ptr(_f64(g_dgamma)),
                              _ptr(_f64(g_d2)), _ptr(grad))
     return grad
+
+
+def c2f_active_levels(L: int, L0: int, t: int, tau: int) -> int:
+    """Active level count of the coarse-to-fine schedule at step t."""
+    a = int(_load().orc_c2f_active(L, L0, t, tau))
+    if a < 0:
+        raise ValueError("bad coarse-to-fine schedule")
+    return a
 
 
 def max_threads() -> int:
