@@ -99,6 +99,28 @@ HASHENC_API void hashenc_destroy(hashenc* h);
  * level resolutions N_l (array of L). */
 HASHENC_API int hashenc_info(const hashenc* h, int64_t* n_params, int32_t* out_width, int32_t* resolutions);
 
+/* Coarse-to-fine level activation (Hermite-NGP reading notes, section 方法详解, key design 3:
+ * train the coarse levels first and activate finer ones step by step).
+ *
+ * hashenc_derive_active: a new handle (*out, host; release with hashenc_destroy) that
+ * shares h's configuration and parameter layout but computes only the first n_active
+ * levels (levels l < n_active; 1 <= n_active <= L).  Every entry point keeps the full L*F
+ * row width: on such a handle the forward writes zeros in the columns of the inactive
+ * levels, the backward adds nothing to their parameter blocks (and ignores the upstream
+ * there), and the fused residual feeds zeros to the network for them.  Deriving from a
+ * derived handle counts levels of the same configuration.  No device memory is involved.
+ * HASHENC_EINVAL on a NULL pointer or n_active outside 1..L. */
+HASHENC_API int hashenc_derive_active(const hashenc* h, int32_t n_active, hashenc** out);
+
+/* Active level count of a handle (host output): L unless derived with fewer. */
+HASHENC_API int hashenc_active_levels(const hashenc* h, int32_t* n_active);
+
+/* The schedule L_active(t) = min(L, L0 + floor(t / tau)) of the same passage, as a count of
+ * active levels at training step `step` (host output).  HASHENC_EINVAL unless n_levels >= 1,
+ * l0 >= 1, step >= 0 and tau >= 1. */
+HASHENC_API int hashenc_c2f_active_levels(int32_t n_levels, int32_t l0, int64_t step, int64_t tau,
+                                          int32_t* n_active);
+
 /* Where table `order` (derivative order k; 0 for d-linear) of level `level` lives in the
  * flat parameter (and gradient) buffer: float offset, rows, floats per row (C(d,k) * F) and
  * whether it is a dense 1:1 grid.  Host outputs, each may be NULL. */

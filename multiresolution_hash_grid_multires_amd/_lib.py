@@ -59,6 +59,9 @@ SIGNATURES = [
     ("hashenc_create", ctypes.c_int, [ctypes.POINTER(HashencConfig), ctypes.POINTER(P)]),
     ("hashenc_destroy", None, [P]),
     ("hashenc_info", ctypes.c_int, [P, ctypes.POINTER(I64), ctypes.POINTER(I32), P]),
+    ("hashenc_derive_active", ctypes.c_int, [P, I32, ctypes.POINTER(P)]),
+    ("hashenc_active_levels", ctypes.c_int, [P, ctypes.POINTER(I32)]),
+    ("hashenc_c2f_active_levels", ctypes.c_int, [I32, I32, I64, I64, ctypes.POINTER(I32)]),
     ("hashenc_param_layout", ctypes.c_int,
      [P, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
     ("hashenc_forward", ctypes.c_int, [P, I64, P, P, P, P, P, P]),

@@ -99,6 +99,25 @@ def hashenc_info(h: Handle) -> tuple[int, int, list[int]]:
     return n_params.value, width.value, [int(v) for v in res[: int(h.spec["L"])]]
 
 
+def hashenc_derive_active(h: Handle, n_active: int) -> Handle:
+    """Handle computing only the first n_active levels (coarse-to-fine activation)."""
+    out = ctypes.c_void_p()
+    check(load().hashenc_derive_active(h, int(n_active), ctypes.byref(out)))
+    return Handle(out.value, dict(h.spec, active_levels=int(n_active)))
+
+
+def hashenc_active_levels(h: Handle) -> int:
+    a = ctypes.c_int32()
+    check(load().hashenc_active_levels(h, ctypes.byref(a)))
+    return int(a.value)
+
+
+def hashenc_c2f_active_levels(n_levels: int, l0: int, step: int, tau: int) -> int:
+    a = ctypes.c_int32()
+    check(load().hashenc_c2f_active_levels(int(n_levels), int(l0), int(step), int(tau), ctypes.byref(a)))
+    return int(a.value)
+
+
 def hashenc_param_layout(h: Handle, order: int, level: int) -> dict:
     off, rows = ctypes.c_int64(), ctypes.c_int64()
     width, dense = ctypes.c_int32(), ctypes.c_int32()
@@ -207,11 +226,24 @@ class HashGridEncoding:
 
     def __init__(self, spec: dict):
         self.spec = dict(spec)
-        self.handle = hashenc_create(spec)
+        self._full = hashenc_create(spec)
+        self.handle = self._full
         self.n_params, self.out_width, self.resolutions = hashenc_info(self.handle)
+        if spec.get("active_levels") is not None:
+            self.set_active_levels(spec["active_levels"])
         self.d = int(spec["d"])
         self.hermite = spec["kind"] == "hermite"
         self.diag = spec.get("d2_mode") == "diag"
+
+    def set_active_levels(self, n_active: int) -> None:
+        """Coarse-to-fine activation: compute only levels l < n_active from now on (outputs
+        keep the full width; inactive columns are zero and get no gradient)."""
+        n_active = int(n_active)
+        self.handle = self._full if n_active == len(self.resolutions) else hashenc_derive_active(self._full, n_active)
+
+    @property
+    def active_levels(self) -> int:
+        return hashenc_active_levels(self.handle)
 
     def output_shapes(self, n: int) -> dict:
         s = {"gamma": (n, self.out_width)}

@@ -453,7 +453,7 @@ hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2
   make_bin_plan(g, d, F, hermite, bp);
   if (u_levels && (!hermite || n > kBinChunkPoints)) return hipErrorInvalidValue;  // one chunk only
   char* ws = static_cast<char*>(workspace);
-  const int64_t LF = (int64_t)g.L * F;
+  const int64_t LF = (int64_t)g.Lrow * F;  // upstream row stride
   for (int64_t p0 = 0; p0 < n; p0 += kBinChunkPoints) {
     const int64_t c = (n - p0) < kBinChunkPoints ? (n - p0) : kBinChunkPoints;
     const BinWorkspace w = bin_workspace_layout(bp, c, entries_per_point(d, g.L, hermite), floats_per_point(bp, d),

@@ -110,22 +110,24 @@ __global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, c
     for (int f = 0; f < F; ++f) acc[f] += __shfl_xor(acc[f], 1, 64);
     if (c0 == 0) {
       if constexpr (LM_OUT) store_vec<F>(gamma + ((int64_t)l * n + p) * F, acc);
-      else store_vec<F>(gamma + p * (int64_t)g.L * F + (int64_t)l * F, acc);
+      else store_vec<F>(gamma + p * (int64_t)g.Lrow * F + (int64_t)l * F, acc);
     }
   }
 }
 
-// [L][n][F] -> [n][L*F] through LDS.  A workgroup owns P consecutive points: it reads the
-// P*F contiguous floats of each level (coalesced runs), parks them in LDS as P rows of L*F
-// (pitch L*F + 1 keeps the scattered LDS writes free of bank conflicts) and writes the
-// P*L*F contiguous output floats as 16-byte pieces, so every output line is written whole.
+// [L][n][F] -> [n][Lrow*F] through LDS.  A workgroup owns P consecutive points: it reads
+// the P*F contiguous floats of each level (coalesced runs), parks them in LDS as P rows of
+// L*F (pitch L*F + 1 keeps the scattered LDS writes free of bank conflicts) and writes the
+// P*Lrow*F contiguous output floats as 16-byte pieces, so every output line is written
+// whole.  Columns of the inactive levels L..Lrow-1 are written as zeros.
 template <int F>
-__global__ __launch_bounds__(kBlock) void level_major_to_rows_kernel(int32_t L, int64_t n, int32_t P,
+__global__ __launch_bounds__(kBlock) void level_major_to_rows_kernel(int32_t L, int32_t Lrow, int64_t n, int32_t P,
                                                                      const float* __restrict__ lm,
                                                                      float* __restrict__ out) {
   extern __shared__ float tile[];
-  const int LF = L * F;
-  const int pitch = LF + 1;
+  const int AF = L * F;     // active columns (held in LDS)
+  const int LF = Lrow * F;  // output row
+  const int pitch = AF + 1;
   const int64_t p0 = (int64_t)blockIdx.x * P;
   const int np = (int)min((int64_t)P, n - p0);
   const int per_level = np * F;
@@ -142,12 +144,16 @@ __global__ __launch_bounds__(kBlock) void level_major_to_rows_kernel(int32_t L, 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e = 4 * q + k;
-        v[k] = tile[(e / LF) * pitch + e % LF];
+        const int c = e % LF;
+        v[k] = c < AF ? tile[(e / LF) * pitch + c] : 0.0f;
       }
       reinterpret_cast<float4*>(dst)[q] = make_float4(v[0], v[1], v[2], v[3]);
     }
   } else {
-    for (int e = threadIdx.x; e < total; e += kBlock) dst[e] = tile[(e / LF) * pitch + e % LF];
+    for (int e = threadIdx.x; e < total; e += kBlock) {
+      const int c = e % LF;
+      dst[e] = c < AF ? tile[(e / LF) * pitch + c] : 0.0f;
+    }
   }
 }
 
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(kBlock) void dlinear_backward_kernel(const Grid g, 
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
-  const int64_t LF = (int64_t)g.L * F;
+  const int64_t LF = (int64_t)g.Lrow * F;
   const float* up = g_gamma + p * LF + f;
   for (int l = 0; l < g.L; ++l) {
     const float G = up[(int64_t)l * F];
@@ -258,8 +264,8 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
 // copied out so that each bin receives one contiguous run: consecutive lanes write
 // consecutive records and cache lines are written whole.  Single-corner records (levels
 // not in pair mode) are written straight to their slots.
-// PRE: the point's upstream row (L*F <= 32 floats) is read once into registers before the
-// level loop; otherwise each level reads its F floats of the row.
+// PRE: the point's upstream row (Lrow*F <= 32 floats, a multiple of 4) is read once into
+// registers before the level loop; otherwise each level reads its F floats of the row.
 template <int D, int F, bool PRE>
 __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
     const Grid g, const BinPlan bp, int64_t n, int32_t tile, int32_t nblk, const float* __restrict__ x,
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = on ? x[p * D + i] : 0.0f;
-  const int64_t LF = (int64_t)g.L * F;
+  const int64_t LF = (int64_t)g.Lrow * F;
   float up[PRE ? 32 : 1];
   if constexpr (PRE) {
 #pragma unroll
@@ -399,7 +405,9 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   const int32_t* bin_start = reinterpret_cast<const int32_t*>(ws + w.bin_start);
   const BinState* st = reinterpret_cast<const BinState*>(ws + w.state);
   float* vals = reinterpret_cast<float*>(ws + w.vals);
-  if (g.L * F <= 32) {
+  // PRE reads the row as 16-byte pieces: rows of a multiple of 4 floats only, so that every
+  // piece is aligned and inside the row
+  if (g.Lrow * F <= 32 && (g.Lrow * F) % 4 == 0) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, true>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -425,7 +433,9 @@ hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* par
   if (!scratch) {
     hipLaunchKernelGGL((dlinear_forward_kernel<D, F, false>), grid, dim3(kBlock), 0, s, g, fp, n, (int32_t)tiles, x,
                        params, gamma);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || g.L == g.Lrow) return e;
+    return launch_zero_columns(gamma, n, g.Lrow * F, g.L * F, s);
   }
   hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, fp, n, (int32_t)tiles, x,
                      params, scratch);
@@ -434,7 +444,7 @@ hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* par
   const int32_t P = g.L * F <= 128 ? 64 : 32;  // LDS tile at most 32 x 257 floats
   const size_t lds = sizeof(float) * (size_t)P * (g.L * F + 1);
   hipLaunchKernelGGL((level_major_to_rows_kernel<F>), dim3((unsigned)((n + P - 1) / P)), dim3(kBlock), lds, s, g.L,
-                     n, P, scratch, gamma);
+                     g.Lrow, n, P, scratch, gamma);
   return hipGetLastError();
 }
 

@@ -159,6 +159,7 @@ int hashenc_create(const hashenc_config* cfg, hashenc** out) {
   Grid& g = h->grid;
   std::memset(&g, 0, sizeof g);
   g.L = h->L;
+  g.Lrow = h->L;
   g.n_tables = h->n_tables;
   for (int l = 0; l < h->L; ++l) {
     g.N[l] = h->N[l];
@@ -186,6 +187,32 @@ int hashenc_info(const hashenc* h, int64_t* n_params, int32_t* out_width, int32_
   if (out_width) *out_width = h->L * h->F;
   if (resolutions)
     for (int l = 0; l < h->L; ++l) resolutions[l] = h->N[l];
+  return ok();
+}
+
+int hashenc_derive_active(const hashenc* h, int32_t n_active, hashenc** out) {
+  if (!h || !out) return fail(HASHENC_EINVAL, "hashenc_derive_active: h and out must not be NULL");
+  if (n_active < 1 || n_active > h->L)
+    return fail(HASHENC_EINVAL, "hashenc_derive_active: n_active must be in 1..%d (got %d)", h->L, n_active);
+  hashenc* c = new (std::nothrow) hashenc(*h);
+  if (!c) return fail(HASHENC_ENOMEM, "hashenc_derive_active: out of host memory");
+  c->grid.L = n_active;  // kernels compute levels < n_active; rows keep h->L levels
+  *out = c;
+  return ok();
+}
+
+int hashenc_active_levels(const hashenc* h, int32_t* n_active) {
+  if (!h || !n_active) return fail(HASHENC_EINVAL, "hashenc_active_levels: NULL pointer");
+  *n_active = h->grid.L;
+  return ok();
+}
+
+int hashenc_c2f_active_levels(int32_t n_levels, int32_t l0, int64_t step, int64_t tau, int32_t* n_active) {
+  if (!n_active) return fail(HASHENC_EINVAL, "hashenc_c2f_active_levels: NULL n_active");
+  if (n_levels < 1 || l0 < 1 || step < 0 || tau < 1)
+    return fail(HASHENC_EINVAL, "hashenc_c2f_active_levels: need n_levels >= 1, l0 >= 1, step >= 0, tau >= 1");
+  const int64_t a = (int64_t)l0 + step / tau;
+  *n_active = a < (int64_t)n_levels ? (int32_t)a : n_levels;
   return ok();
 }
 
@@ -399,7 +426,9 @@ int hashenc_debug_indices(const hashenc* h, int64_t n, const float* x, int32_t o
   if (n == 0) return ok();
   if (!x || !out_rows) return fail(HASHENC_EINVAL, "hashenc_debug_indices: NULL pointer");
   if (!aligned16(x) || !aligned16(out_rows)) return fail(HASHENC_EALIGN, "hashenc_debug_indices: pointers must be 16-byte aligned");
-  hipError_t e = hg::launch_debug_indices(h->grid, h->d, order, n, x, out_rows, stream);
+  Grid g = h->grid;
+  g.L = g.Lrow;  // the lookup stage of every level, active or not
+  hipError_t e = hg::launch_debug_indices(g, h->d, order, n, x, out_rows, stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_debug_indices launch");
   return ok();
 }

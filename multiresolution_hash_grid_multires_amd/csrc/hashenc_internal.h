@@ -22,8 +22,12 @@ constexpr uint32_t kPrime2 = 805459861u;
 // Everything a kernel needs to find a (table, level) block and the rows of a cell.
 // Passed by value as a kernel argument (about 1.3 KB, well inside the kernarg limit);
 // kernels index it only with wave-uniform level numbers, so it stays in scalar loads.
+// L counts the levels the kernels compute; Lrow the levels of an encoding row (the
+// configured level count).  L < Lrow under coarse-to-fine activation: levels l >= L are
+// inactive, their columns of every output row are zero and their blocks get no gradient.
 struct Grid {
   int32_t L;
+  int32_t Lrow;
   int32_t n_tables;
   int32_t N[kMaxLevels];        // resolution N_l
   float Nf[kMaxLevels];         // N_l as fp32 (exact: N_l <= 2^20)
@@ -149,6 +153,8 @@ hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int
 hipError_t launch_debug_indices(const Grid& g, int d, int order, int64_t n, const float* x,
                                 int32_t* out, hipStream_t s);
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t s);
+// Zero columns [from, row_floats) of rows rows x row_floats floats (inactive levels).
+hipError_t launch_zero_columns(float* out, int64_t rows, int32_t row_floats, int32_t from, hipStream_t s);
 
 // Fused PINN residual (Hermite handle): workspace size and the full step.
 int64_t mlp_param_count(int in, int H, int depth);

@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
-  const int64_t LF = (int64_t)g.L * F;
+  const int64_t LF = (int64_t)g.Lrow * F;
   CellKeys<D> keys;
   AxisBasis ab[D];
   level_setup<D>(g, l, xp, keys, ab);
@@ -498,7 +498,7 @@ __device__ __forceinline__ LevelUp<D, F> load_level_up(const Grid& g, int64_t p,
                                                        const float* __restrict__ g_gamma,
                                                        const float* __restrict__ g_dgamma,
                                                        const float* __restrict__ g_d2gamma) {
-  const int64_t LF = (int64_t)g.L * F;
+  const int64_t LF = (int64_t)g.Lrow * F;
   const int64_t col = (int64_t)l * F;
   LevelUp<D, F> u;
 #pragma unroll
@@ -533,9 +533,10 @@ __device__ __forceinline__ LevelUp<D, F> load_level_up(const Grid& g, int64_t p,
 // rows of every upstream array (contiguous runs) into LDS and writes each level's
 // P * M * F floats as one contiguous run, so the scatter, which runs level by level, reads
 // each level's upstream once and in whole lines instead of 8 bytes from every point's row
-// per level.
+// per level.  Rows are Lrow * F floats; only the L active levels are rearranged.
 template <int F, int D, int M>
-__global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t L, int64_t n, int32_t P,
+__global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t L, int32_t Lrow, int64_t n,
+                                                                         int32_t P,
                                                                          const float* __restrict__ gg,
                                                                          const float* __restrict__ gd,
                                                                          const float* __restrict__ g2,
@@ -545,7 +546,8 @@ __global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t
   extern __shared__ float tile[];
   constexpr int MF = M * F;
   constexpr int D2 = M - 1 - D;  // second-derivative components (d or 1)
-  const int LF = L * F;
+  const int AF = L * F;         // active floats of a row
+  const int LF = Lrow * F;      // row stride
   const int pitch = L * MF + 1;
   const int64_t p0 = (int64_t)blockIdx.x * P;
   const int np = (int)min((int64_t)P, n - p0);
@@ -558,8 +560,8 @@ __global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t
                      : m <= D ? (gd ? gd + (p * D + (m - 1)) * LF : nullptr)
                               : (g2 ? g2 + (p * D2 + (m - 1 - D)) * LF : nullptr);
     float* t = tile + i * pitch + m * F;
-    if ((LF & 3) == 0) {
-      for (int c = 0; c < LF; c += 4) {
+    if (((LF | AF) & 3) == 0) {
+      for (int c = 0; c < AF; c += 4) {
         const float4 v = src ? *reinterpret_cast<const float4*>(src + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         const float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t
         }
       }
     } else {
-      for (int c = 0; c < LF; ++c) {
+      for (int c = 0; c < AF; ++c) {
         const int l = c / F, f = c - l * F;
         t[l * MF + f] = src ? src[c] : 0.0f;
       }
@@ -590,9 +592,11 @@ __global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t
 // reads each level's P * M * F contiguous floats into LDS (each point's rows in output
 // order, pitch M * L * F + 1) and writes every (point, component) row of L*F floats with
 // 16-byte stores when rows are 16-byte aligned; the P rows of one output array are
-// contiguous, so lines are written whole.
+// contiguous, so lines are written whole.  Rows are Lrow * F floats: the columns of the
+// inactive levels L..Lrow-1 are written as zeros.
 template <int F, int D, int M>
-__global__ __launch_bounds__(kBlock) void hermite_levels_to_rows_kernel(int32_t L, int64_t n, int32_t P,
+__global__ __launch_bounds__(kBlock) void hermite_levels_to_rows_kernel(int32_t L, int32_t Lrow, int64_t n,
+                                                                        int32_t P,
                                                                         const float* __restrict__ stage,
                                                                         float* __restrict__ gamma,
                                                                         float* __restrict__ dgamma,
@@ -600,7 +604,8 @@ __global__ __launch_bounds__(kBlock) void hermite_levels_to_rows_kernel(int32_t 
   extern __shared__ float tile[];
   constexpr int MF = M * F;
   constexpr int D2 = M - 1 - D;
-  const int LF = L * F;
+  const int LF = L * F;     // active floats of a row (LDS layout)
+  const int RF = Lrow * F;  // output row stride
   const int pitch = M * LF + 1;
   const int64_t p0 = (int64_t)blockIdx.x * P;
   const int np = (int)min((int64_t)P, n - p0);
@@ -619,16 +624,18 @@ __global__ __launch_bounds__(kBlock) void hermite_levels_to_rows_kernel(int32_t 
   for (int row = threadIdx.x; row < np * M; row += kBlock) {
     const int i = row / M, m = row - i * M;
     const int64_t p = p0 + i;
-    float* dst = m == 0 ? (gamma ? gamma + p * LF : nullptr)
-               : m <= D ? (dgamma ? dgamma + (p * D + (m - 1)) * LF : nullptr)
-                        : (d2gamma ? d2gamma + (p * D2 + (m - 1 - D)) * LF : nullptr);
+    float* dst = m == 0 ? (gamma ? gamma + p * RF : nullptr)
+               : m <= D ? (dgamma ? dgamma + (p * D + (m - 1)) * RF : nullptr)
+                        : (d2gamma ? d2gamma + (p * D2 + (m - 1 - D)) * RF : nullptr);
     if (!dst) continue;
     const float* t = tile + i * pitch + m * LF;
-    if ((LF & 3) == 0) {
+    if (((LF | RF) & 3) == 0) {
       for (int c = 0; c < LF; c += 4)
         *reinterpret_cast<float4*>(dst + c) = make_float4(t[c], t[c + 1], t[c + 2], t[c + 3]);
+      for (int c = LF; c < RF; c += 4) *reinterpret_cast<float4*>(dst + c) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     } else {
       for (int c = 0; c < LF; ++c) dst[c] = t[c];
+      for (int c = LF; c < RF; ++c) dst[c] = 0.0f;
     }
   }
 }
@@ -956,11 +963,11 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
     if (e != hipSuccess) return e;
     const dim3 ugrid((unsigned)((n + PU - 1) / PU));
     if (diag)
-      hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 1 + 2 * D>), ugrid, dim3(kBlock), ulds, s, g.L, n,
-                         PU, gg, gd, g2, Uw);
+      hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 1 + 2 * D>), ugrid, dim3(kBlock), ulds, s, g.L,
+                         g.Lrow, n, PU, gg, gd, g2, Uw);
     else
-      hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 2 + D>), ugrid, dim3(kBlock), ulds, s, g.L, n, PU,
-                         gg, gd, g2, Uw);
+      hipLaunchKernelGGL((hermite_upstream_levels_kernel<F, D, 2 + D>), ugrid, dim3(kBlock), ulds, s, g.L, g.Lrow,
+                         n, PU, gg, gd, g2, Uw);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1019,8 +1026,16 @@ hipError_t launch_fwd(const Grid& g, int d2_mode, int64_t n, const float* x, con
     hipLaunchKernelGGL((hermite_forward_kernel<D, F, false, false>), grid, dim3(kBlock), 0, s, g, pp, n,
                        (int32_t)tiles, d2_mode, x, tab, gamma, dgamma, d2gamma, stage);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !stage || !to_rows) return e;
+  if (e != hipSuccess || (stage && !to_rows)) return e;
   const bool diag = d2_mode == HASHENC_D2_DIAG;
+  if (!stage) {  // point-major outputs: zero the inactive levels' columns
+    if (g.L == g.Lrow) return e;
+    const int RF = g.Lrow * F, AF = g.L * F;
+    if (gamma) e = launch_zero_columns(gamma, n, RF, AF, s);
+    if (e == hipSuccess && dgamma) e = launch_zero_columns(dgamma, n * D, RF, AF, s);
+    if (e == hipSuccess && d2gamma) e = launch_zero_columns(d2gamma, n * (diag ? D : 1), RF, AF, s);
+    return e;
+  }
   const int M = 1 + D + (diag ? D : 1);
   const int LF = g.L * F;
   const int P = (int)std::max(1, std::min(64, 16384 / (M * LF)));  // LDS tile <= 64 KB
@@ -1031,11 +1046,11 @@ hipError_t launch_fwd(const Grid& g, int d2_mode, int64_t n, const float* x, con
   if (e != hipSuccess) return e;
   const dim3 tgrid((unsigned)((n + P - 1) / P));
   if (diag)
-    hipLaunchKernelGGL((hermite_levels_to_rows_kernel<F, D, 1 + 2 * D>), tgrid, dim3(kBlock), lds, s, g.L, n, P,
-                       stage, gamma, dgamma, d2gamma);
+    hipLaunchKernelGGL((hermite_levels_to_rows_kernel<F, D, 1 + 2 * D>), tgrid, dim3(kBlock), lds, s, g.L, g.Lrow,
+                       n, P, stage, gamma, dgamma, d2gamma);
   else
-    hipLaunchKernelGGL((hermite_levels_to_rows_kernel<F, D, 2 + D>), tgrid, dim3(kBlock), lds, s, g.L, n, P, stage,
-                       gamma, dgamma, d2gamma);
+    hipLaunchKernelGGL((hermite_levels_to_rows_kernel<F, D, 2 + D>), tgrid, dim3(kBlock), lds, s, g.L, g.Lrow, n,
+                       P, stage, gamma, dgamma, d2gamma);
   return hipGetLastError();
 }
 

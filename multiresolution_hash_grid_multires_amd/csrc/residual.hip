@@ -34,6 +34,7 @@ constexpr int kMaxDepth = 4;
 
 struct MlpArgs {
   int32_t in, H, depth;
+  int32_t ain;     // encoder inputs of the active levels (the rest are zero, coarse-to-fine)
   int32_t fshift;  // log2 F: encoder feature j is feature j % F of level j / F
   float omega;
   int64_t n_mlp;
@@ -57,7 +58,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // rows, Laplacian): the index of feature j = l F + f, row r of point p.
 __device__ __forceinline__ int64_t lm_index(const MlpArgs& a, int64_t n, int64_t p, int j, int r, int R) {
   const int l = j >> a.fshift, f = j & ((1 << a.fshift) - 1);
-  return (((int64_t)l * n + p) * R + r << a.fshift) + f;
+  return ((((int64_t)l * n + p) * R + r) << a.fshift) + f;
 }
 
 // Points per wavefront iteration: every LDS weight read feeds PB * R FMAs and the
@@ -104,7 +105,6 @@ __global__ __launch_bounds__(kW * siren_waves(DEPTH, INP)) void siren_residual_k
   const int tid = threadIdx.x;
   const int lane = tid & (kW - 1);
   const int wv = tid / kW;
-  const int LF = a.in;
   const float w = a.omega;
 
   for (int k = 0; k < DEPTH; ++k) {
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kW * siren_waves(DEPTH, INP)) void siren_residual_k
 #pragma unroll
       for (int b = 0; b < kPB; ++b) {
         const int64_t p = p0 + b;
-        const bool on = lane < LF && p < n;
+        const bool on = lane < a.ain && p < n;
 #pragma unroll
         for (int r = 0; r < R; ++r) row[b * R + r] = on ? enc[lm_index(a, n, p, lane, r, R)] : 0.0f;
       }
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kW * siren_waves(DEPTH, INP)) void siren_residual_k
       }
       wave_lds_sync();  // zb is rewritten by the next layer
     }
-    if (lane < LF) {
+    if (lane < a.ain) {
 #pragma unroll
       for (int b = 0; b < kPB; ++b) {
         const int64_t p = p0 + b;
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
   __shared__ MfmaLds<D, DEPTH, NI> sh;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lm = lane & 15, lq = lane >> 4;
-  const int LF = a.in, H = a.H;
+  const int H = a.H;
   const float om = a.omega;
 
   // weights into LDS, zero-padded to the compiled widths; the forward reads W_k[16w + lm][4kk + lq]
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
       const int p = t2 % kMP, l = t2 / kMP;
       const int j = (l << a.fshift) + f;
       const int64_t pp = p0 + p;
-      sh.act0[j][r * kMP + p] = (j < LF && pp < n) ? enc[lm_index(a, n, pp, j, r, R)] : 0.0f;
+      sh.act0[j][r * kMP + p] = (j < a.ain && pp < n) ? enc[lm_index(a, n, pp, j, r, R)] : 0.0f;
     }
     __syncthreads();
 
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = 16 * w + 4 * lq + i;
-          if (j < LF) {
+          if (j < a.ain) {
 #pragma unroll
             for (int r = 0; r < R; ++r) up[lm_index(a, n, pp, j, r, R)] = vbar[r][i];
           }
@@ -785,6 +785,7 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
                         bool binned, hipStream_t s) {
   MlpArgs a;
   a.in = in;
+  a.ain = g.L * F;  // levels l >= g.L are inactive: zero inputs, no upstream
   a.H = H;
   a.depth = depth;
   a.omega = omega;

@@ -169,3 +169,50 @@ def test_residual_validation_on_host():
     assert lib.hashenc_residual(herm, ctypes.byref(m), 0, a, a, a, None, a, None, None, a, need, None) == _lib.HASHENC_EINVAL
     assert lib.hashenc_residual(herm, ctypes.byref(m), 8, a, a, a, None, a, None, None, P(0x10010), need, None) == _lib.HASHENC_EALIGN
     assert lib.hashenc_residual(herm, ctypes.byref(m), 8, a, a, a, None, None, None, None, a, need, None) == _lib.HASHENC_EINVAL
+
+
+# ---------------------------------------------------------------- coarse-to-fine activation
+def test_c2f_schedule_matches_oracle(orc):
+    for L in (1, 8, 16):
+        for L0 in (1, 3, 16):
+            for tau in (1, 7, 500):
+                for t in (0, 1, tau - 1, tau, 2 * tau + 1, 40 * tau, 10 ** 15):
+                    assert api.hashenc_c2f_active_levels(L, L0, t, tau) == orc.c2f_active_levels(L, L0, t, tau)
+
+
+@pytest.mark.parametrize("args", [(0, 1, 0, 1), (16, 0, 0, 1), (16, 1, -1, 1), (16, 1, 0, 0)])
+def test_c2f_schedule_rejects_bad_arguments(args):
+    out = ctypes.c_int32()
+    assert _lib.load().hashenc_c2f_active_levels(*args, ctypes.byref(out)) == _lib.HASHENC_EINVAL
+    assert _lib.load().hashenc_c2f_active_levels(16, 1, 0, 1, None) == _lib.HASHENC_EINVAL
+
+
+def test_derive_active_keeps_layout_and_width(orc):
+    spec = {"d": 3, "L": 6, "F": 2, "kind": "hermite", "T": [1 << 10] * 4, "n_min": 4, "n_max": 64,
+            "d2_mode": "laplacian"}
+    h = api.hashenc_create(spec)
+    assert api.hashenc_active_levels(h) == 6
+    for a in (1, 3, 6):
+        ha = api.hashenc_derive_active(h, a)
+        assert api.hashenc_active_levels(ha) == a
+        assert api.hashenc_info(ha) == api.hashenc_info(h)
+        for l in range(6):
+            assert api.hashenc_param_layout(ha, 2, l) == api.hashenc_param_layout(h, 2, l)
+        # counted against the configuration, also from a derived handle
+        hb = api.hashenc_derive_active(ha, 5)
+        assert api.hashenc_active_levels(hb) == 5
+    enc = api.HashGridEncoding(dict(spec, active_levels=2))
+    assert enc.active_levels == 2 and enc.out_width == 12
+    enc.set_active_levels(6)
+    assert enc.active_levels == 6
+
+
+@pytest.mark.parametrize("n_active", [0, -1, 7])
+def test_derive_active_rejects_bad_count(n_active):
+    spec = {"d": 2, "L": 6, "F": 2, "kind": "dlinear", "T": [1 << 10], "n_min": 4, "n_max": 64}
+    h = api.hashenc_create(spec)
+    out = ctypes.c_void_p()
+    assert _lib.load().hashenc_derive_active(h, n_active, ctypes.byref(out)) == _lib.HASHENC_EINVAL
+    assert out.value is None
+    assert _lib.load().hashenc_derive_active(None, 1, ctypes.byref(out)) == _lib.HASHENC_EINVAL
+    assert _lib.load().hashenc_derive_active(h, 1, None) == _lib.HASHENC_EINVAL
