@@ -43,18 +43,17 @@ MEASURED_TRAFFIC_BYTES: dict = {
 
 def algorithmic_bytes_per_point(spec: dict) -> dict:
     """Bytes the method itself moves per point: streamed inputs/outputs, every table value
-    referenced (4 B per fp32 gather) and every fp32 atomic as a read-modify-write (8 B)."""
+    referenced (4 B per fp32 gather) and every fp32 atomic as a read-modify-write (8 B).
+    With A of the L levels active (coarse-to-fine), the forward still writes full rows
+    (zeros for the inactive levels) while gathers, upstream reads and scatters cover the A
+    active levels."""
     d, L, F = spec["d"], spec["L"], spec["F"]
-    LF = L * F
+    A = int(spec.get("active_levels") or L)
+    comps = 1 + d + (d if spec.get("d2_mode") == "diag" else 1) if spec["kind"] == "hermite" else 1
+    corners = (1 << d) * (1 << d) if spec["kind"] == "hermite" else (1 << d)
     x_bytes = 4 * d
-    if spec["kind"] == "hermite":
-        out_floats = LF * (1 + d + (d if spec.get("d2_mode") == "diag" else 1))
-        coeffs = L * (1 << d) * (1 << d) * F
-    else:
-        out_floats = LF
-        coeffs = L * (1 << d) * F
-    return {"forward": x_bytes + 4 * out_floats + 4 * coeffs,
-            "backward": x_bytes + 4 * out_floats + 8 * coeffs}
+    return {"forward": x_bytes + 4 * L * F * comps + 4 * A * corners * F,
+            "backward": x_bytes + 4 * A * F * comps + 8 * A * corners * F}
 
 
 def copy_bandwidth(torch, api, nbytes: int = 4 << 30, steps: int = 10) -> float:
@@ -141,17 +140,19 @@ def residual_bench(args, torch, api, I, W) -> int:
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.steps
-    lap_spec = dict(spec, d2_mode="laplacian")
+    lap_spec = dict(spec, d2_mode="laplacian")  # active_levels carried over
     alg = algorithmic_bytes_per_point(lap_spec)
     enc_bytes = (alg["forward"] + alg["backward"]) * n
     flops = mlp_flops_per_point(spec["d"], n_in, m["hidden"], m["depth"]) * n
     print(json.dumps({
-        "metric": f"PINN residual steps: points/s ({args.workload})", "value": round(n / (ms * 1e-3), 1),
+        "metric": f"PINN residual steps: points/s ({args.workload}"
+                  + (f", {args.active_levels} of {spec['L']} levels active)" if args.active_levels else ")"),
+        "value": round(n / (ms * 1e-3), 1),
         "unit": "points/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "n_points": n, "hidden": m["hidden"], "depth": m["depth"],
-                   "omega": m["omega"]},
+                   "omega": m["omega"], "active_levels": int(spec.get("active_levels") or spec["L"])},
         "encoder_alg_GBps_over_step": round(enc_bytes / (ms * 1e-3) / 1e9, 1),
         "mlp_TFLOPs_over_step": round(flops / (ms * 1e-3) / 1e12, 2),
         "loss": float(loss.item())}), flush=True)
@@ -167,6 +168,8 @@ def main() -> int:
     ap.add_argument("--backward", choices=["binned", "atomic"], default="binned",
                     help="binned: hashenc_forward_ws + hashenc_backward_ws (workspace); "
                          "atomic: hashenc_forward + hashenc_backward (no workspace)")
+    ap.add_argument("--active-levels", type=int, default=0,
+                    help="coarse-to-fine activation: compute only the first A levels (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run the plain copy kernel over this many bytes "
@@ -188,6 +191,8 @@ def main() -> int:
         return copy_calibration(args, torch, api)
 
     W = I.WORKLOADS[args.workload]
+    if args.active_levels:
+        W = dict(W, spec=dict(W["spec"], active_levels=args.active_levels))
     if "mlp" in W:
         return residual_bench(args, torch, api, I, W)
     spec = W["spec"]
@@ -255,7 +260,8 @@ def main() -> int:
         k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
     dom = max(kern, key=lambda k: kern[k]["ms"])
     # recorded for the default (workspace) entry points only
-    traffic = MEASURED_TRAFFIC_BYTES.get((args.workload, dom)) if workspace is not None else None
+    traffic = (MEASURED_TRAFFIC_BYTES.get((args.workload, dom))
+               if workspace is not None and not args.active_levels else None)
     roofline = {"bound": "hbm", "achieved": round(kern[dom]["GBps"], 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(kern[dom]["GBps"] / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
@@ -302,8 +308,11 @@ def main() -> int:
         cpu = {"value": round(reps * m / total, 1), "unit": "points/s", "cores": O.max_threads(),
                "kind": "oracle", "sample": what + " (fp64-accumulating oracle)", "seconds": round(total, 2)}
 
+    metric = METRIC if args.workload == HEADLINE else f"encoded points/s fwd+bwd ({args.workload})"
+    if args.active_levels:
+        metric = f"encoded points/s fwd+bwd ({args.workload}, {args.active_levels} of {spec['L']} levels active)"
     line = {
-        "metric": METRIC if args.workload == HEADLINE else f"encoded points/s fwd+bwd ({args.workload})",
+        "metric": metric,
         "value": round(value, 1),
         "unit": "points/s",
         "n_gpus": 1,
@@ -316,7 +325,8 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "n_points": n, "d": spec["d"], "L": spec["L"],
-                   "F": spec["F"], "T": spec["T"], "kind": spec["kind"], "backward": args.backward},
+                   "F": spec["F"], "T": spec["T"], "kind": spec["kind"], "backward": args.backward,
+                   "active_levels": int(spec.get("active_levels") or spec["L"])},
         "hbm_roofline_pct_step": round(100.0 * value * step_alg / (HBM_PEAK_GBPS * 1e9), 2),
         "kernels": {k: {"ms": round(v["ms"], 4), "GBps": round(v["GBps"], 1)} for k, v in kern.items()},
         "roofline": roofline,
