@@ -17,8 +17,9 @@
  *                     PDEs" reading notes (m0rtzz.github.io), section 方法详解,
  *                     key design 1 (reconstruction equation, 1D basis), key
  *                     design 2 (basis derivatives, SIREN chain rule) and key
- *                     design 3 (coarse-to-fine level activation); section
- *                     损失函数 / 训练策略 (omega_0 = 30).
+ *                     design 3 (coarse-to-fine level activation); the 现有痛点
+ *                     paragraph (INGP-FD: Laplacian by central differences over
+ *                     2d+1 forward passes); section 损失函数 / 训练策略 (omega_0 = 30).
  *
  * Readings taken where the pages are silent or garbled (the formula bodies for
  * the level progression and the spatial hash did not survive extraction):
@@ -564,6 +565,144 @@ int orc_residual(const orc_cfg* c, int32_t hidden, int32_t depth, double omega, 
   if (residual) for (int64_t p = 0; p < n; ++p) residual[p] = rr[p];
   if (grad_params) orc_backward_f64(&lc, n, x, ug, ud, ul, grad_params);
   free(g); free(dg); free(lp); free(ug); free(ud); free(ul); free(rr); free(gm_all);
+  return 0;
+}
+
+/* ---- INGP-FD comparator [HNGP 现有痛点 paragraph and key design 2's comparison: the
+ * Laplacian of an Instant-NGP encoding + network by central finite differences, 2d+1
+ * forward passes per point] ----
+ * Stencil point s of point p: s = 0 is x itself, s = 2i+1 is x + eps e_i and s = 2i+2 is
+ * x - eps e_i, the shifted coordinate being one fp32 addition (it is an fp32 encoder input;
+ * the encoder clamps to [0, 1] as always).  Every stencil point goes through the d-linear
+ * encoding and the same SIREN as the fused residual (value only): a = sin(omega (W v + b)),
+ * u = Wo a + bo.  Then
+ *     Lap_FD u = sum_i (u(x + eps e_i) - 2 u(x) + u(x - eps e_i)) / eps^2,
+ *     r = Lap_FD u - g(x),  loss = mean r^2,  g as for the fused residual.
+ * The reverse sweep seeds d loss / d u_s = (2 r / n) c_s, c_0 = -2d / eps^2, c_s = 1 / eps^2
+ * otherwise, through each stencil point's network and encoding.  The stencil weights sum to
+ * zero, so the output bias does not enter r: its gradient is zero.
+ * Outputs (fp64, each may be NULL): u_stencil [n][2d+1], residual [n], loss [1],
+ * grad_params (+=, table layout), grad_mlp (+=).  Returns 0, or -1 on a bad shape. */
+int orc_fd_residual(const orc_cfg* c, int32_t hidden, int32_t depth, double omega, double eps, int64_t n,
+                    const float* x, const double* params, const double* mlp, double* u_stencil,
+                    double* residual, double* loss, double* grad_params, double* grad_mlp) {
+  if (c->kind != 0 || depth < 1 || depth > 14 || hidden < 1 || !(eps > 0.0)) return -1;
+  const int d = c->d, LF = c->L * c->F, H = hidden, S = 2 * d + 1;
+  const int W = H > LF ? H : LF;
+  int64_t woff[16], boff[16], in_w[16];
+  int64_t off = 0;
+  for (int k = 0; k <= depth; ++k) {
+    int64_t fan_in = k == 0 ? LF : H;
+    int64_t fan_out = k == depth ? 1 : H;
+    in_w[k] = fan_in;
+    woff[k] = off; off += fan_in * fan_out;
+    boff[k] = off; off += fan_out;
+  }
+  const int64_t n_mlp = off;
+  const int64_t ns = n * S;
+  /* the shifted point sets */
+  float* xs = (float*)malloc(sizeof(float) * (size_t)(ns * d + 1));
+  const float e32 = (float)eps;
+  for (int64_t p = 0; p < n; ++p)
+    for (int s = 0; s < S; ++s) {
+      float* q = xs + (p * S + s) * d;
+      for (int i = 0; i < d; ++i) q[i] = x[p * d + i];
+      if (s > 0) {
+        const int i = (s - 1) / 2;
+        volatile float shifted = (s % 2 == 1) ? x[p * d + i] + e32 : x[p * d + i] - e32;
+        q[i] = shifted;
+      }
+    }
+  double* g = (double*)malloc(sizeof(double) * (size_t)(ns * LF + 1));
+  orc_forward(c, ns, xs, params, g, NULL, NULL);
+  double* ug = (double*)calloc((size_t)(ns * LF + 1), sizeof(double));
+  double* rr = (double*)malloc(sizeof(double) * (size_t)(n + 1));
+  int nthreads = 1;
+#ifdef _OPENMP
+  nthreads = omp_get_max_threads();
+#endif
+  double* gm_all = (double*)calloc((size_t)(nthreads * n_mlp), sizeof(double));
+  const double inv_n = n > 0 ? 1.0 / (double)n : 0.0;
+  const double PI = 3.14159265358979323846;
+#pragma omp parallel
+  {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    double* gm = gm_all + (int64_t)tid * n_mlp;
+    /* tape per stencil point: act[s][k] = inputs of layer k (width W), zs[s][k] = z */
+    double* act = (double*)malloc(sizeof(double) * (size_t)(S * (depth + 1) * W));
+    double* zs = (double*)malloc(sizeof(double) * (size_t)(S * depth * H));
+    double* bar = (double*)malloc(sizeof(double) * (size_t)W);
+    double* nbar = (double*)malloc(sizeof(double) * (size_t)W);
+    double u[2 * ORC_MAX_D + 1];
+#pragma omp for schedule(static)
+    for (int64_t p = 0; p < n; ++p) {
+      for (int s = 0; s < S; ++s) {
+        double* a_s = act + (int64_t)s * (depth + 1) * W;
+        double* z_s = zs + (int64_t)s * depth * H;
+        for (int j = 0; j < LF; ++j) a_s[j] = g[(p * S + s) * LF + j];
+        for (int k = 0; k < depth; ++k) {
+          const double* Wk = mlp + woff[k];
+          for (int o = 0; o < H; ++o) {
+            double z = mlp[boff[k] + o];
+            for (int j = 0; j < in_w[k]; ++j) z += Wk[o * in_w[k] + j] * a_s[k * W + j];
+            z_s[k * H + o] = z;
+            a_s[(k + 1) * W + o] = sin(omega * z);
+          }
+        }
+        double us = mlp[boff[depth]];
+        for (int j = 0; j < H; ++j) us += mlp[woff[depth] + j] * a_s[depth * W + j];
+        u[s] = us;
+        if (u_stencil) u_stencil[p * S + s] = us;
+      }
+      double lap = 0.0;
+      for (int i = 0; i < d; ++i) lap += (u[2 * i + 1] - 2.0 * u[0] + u[2 * i + 2]) / (eps * eps);
+      double src = -(double)d * PI * PI;
+      for (int i = 0; i < d; ++i) src *= sin(PI * (double)x[p * d + i]);
+      const double r = lap - src;
+      rr[p] = r;
+      const double seed = 2.0 * r * inv_n;
+      for (int s = 0; s < S; ++s) {
+        const double cs = s == 0 ? -2.0 * (double)d / (eps * eps) : 1.0 / (eps * eps);
+        const double ubar = seed * cs;
+        double* a_s = act + (int64_t)s * (depth + 1) * W;
+        double* z_s = zs + (int64_t)s * depth * H;
+        for (int j = 0; j < H; ++j) {
+          gm[woff[depth] + j] += ubar * a_s[depth * W + j];
+          bar[j] = ubar * mlp[woff[depth] + j];
+        }
+        for (int k = depth - 1; k >= 0; --k) {
+          const double* Wk = mlp + woff[k];
+          const int64_t fi = in_w[k];
+          for (int j = 0; j < fi; ++j) nbar[j] = 0.0;
+          for (int o = 0; o < H; ++o) {
+            const double zbar = bar[o] * omega * cos(omega * z_s[k * H + o]); /* d sin(w z)/dz */
+            gm[boff[k] + o] += zbar;
+            for (int j = 0; j < fi; ++j) {
+              gm[woff[k] + o * fi + j] += zbar * a_s[k * W + j];
+              nbar[j] += Wk[o * fi + j] * zbar;
+            }
+          }
+          double* tmp = bar; bar = nbar; nbar = tmp;
+        }
+        for (int j = 0; j < LF; ++j) ug[(p * S + s) * LF + j] = bar[j];
+      }
+    }
+    free(act); free(zs); free(bar); free(nbar);
+  }
+  if (grad_mlp) {
+    for (int tdx = 0; tdx < nthreads; ++tdx)
+      for (int64_t j = 0; j < n_mlp; ++j) grad_mlp[j] += gm_all[(int64_t)tdx * n_mlp + j];
+    /* the output bias is not in r (the stencil weights sum to zero) */
+  }
+  double sum_sq = 0.0;
+  for (int64_t p = 0; p < n; ++p) sum_sq += rr[p] * rr[p];
+  if (loss) *loss = sum_sq * inv_n;
+  if (residual) for (int64_t p = 0; p < n; ++p) residual[p] = rr[p];
+  if (grad_params) orc_backward_f64(c, ns, xs, ug, NULL, NULL, grad_params);
+  free(xs); free(g); free(ug); free(rr); free(gm_all);
   return 0;
 }
 

@@ -80,6 +80,9 @@ def _load():
         lib.orc_residual.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                      ctypes.c_int64, P, P, P, P, P, P, P, P, P, P]
         lib.orc_residual.restype = ctypes.c_int
+        lib.orc_fd_residual.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+                                        ctypes.c_int64, P, P, P, P, P, P, P, P]
+        lib.orc_fd_residual.restype = ctypes.c_int
         lib.orc_mlp_param_count.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         lib.orc_mlp_param_count.restype = ctypes.c_int64
         lib.orc_c2f_active.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]
@@ -232,5 +235,24 @@ def residual(spec: dict, hidden: int, depth: int, omega: float, x, params, mlp):
                               _ptr(out["grad_mlp"]))
     if rc != 0:
         raise ValueError("bad residual configuration")
+    out["loss"] = float(loss[0])
+    return out
+
+
+def fd_residual(spec: dict, hidden: int, depth: int, omega: float, eps: float, x, params, mlp):
+    """INGP-FD comparator: the residual with the Laplacian of u taken by central differences
+    over the 2d+1 stencil points (d-linear encoding).  Returns a dict of fp64 results:
+    u_stencil [n, 2d+1], r [n], loss (float), grad_params [n_params], grad_mlp [n_mlp]."""
+    c = make_cfg(spec)
+    x, params, mlp = _f32(x), _f64(params), _f64(mlp)
+    n, d = x.shape[0], spec["d"]
+    out = {"u_stencil": np.zeros((n, 2 * d + 1)), "r": np.zeros(n),
+           "grad_params": np.zeros(params.size), "grad_mlp": np.zeros(mlp.size)}
+    loss = np.zeros(1)
+    rc = _load().orc_fd_residual(ctypes.byref(c), hidden, depth, float(omega), float(eps), n, _ptr(x),
+                                 _ptr(params), _ptr(mlp), _ptr(out["u_stencil"]), _ptr(out["r"]), _ptr(loss),
+                                 _ptr(out["grad_params"]), _ptr(out["grad_mlp"]))
+    if rc != 0:
+        raise ValueError("bad FD residual configuration")
     out["loss"] = float(loss[0])
     return out
