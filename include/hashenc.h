@@ -206,6 +206,31 @@ HASHENC_API int hashenc_residual(const hashenc* h, const hashenc_mlp* mlp, int64
                      float* loss, float* grad_params, float* grad_mlp, void* workspace,
                      size_t workspace_bytes, hashenc_stream_t stream);
 
+/* INGP-FD comparator (Hermite-NGP reading notes, the 现有痛点 paragraph and key design 2's
+ * comparison: Instant-NGP + central finite differences needs 2d+1 forward passes per
+ * Laplacian).  The same Poisson residual step as hashenc_residual, on a d-LINEAR handle: each
+ * point's 2d+1 stencil points x, x + eps e_i, x - eps e_i (s = 0, 2i+1, 2i+2; the shifted
+ * coordinate is one fp32 addition, then the encoder's usual clamp) are encoded and pushed
+ * through the SIREN (value only: a = sin(omega (W v + b)), u = Wo a + bo), and
+ *   Lap u = sum_i (u(x + eps e_i) - 2 u(x) + u(x - eps e_i)) / eps^2,  r = Lap u - g(x),
+ *   loss = mean r^2, with g as for hashenc_residual; the reverse sweep runs through all
+ *   2d+1 stencil points' networks and encodings.  The output bias cancels in the stencil:
+ *   its gradient is zero.
+ *   mlp          depth 1 or 2 (matrix-core kernel), hidden <= 64, in == L*F <= 64
+ *   eps          FD step (> 0, finite)
+ *   u_stencil    [n, 2d+1] u at the stencil points (may be NULL)
+ *   residual     [n] r (may be NULL);  loss [1] (overwritten)
+ *   grad_params  += dloss/dtheta;  grad_mlp += dloss/dmlp_params (either may be NULL)
+ *   workspace    >= hashenc_fd_residual_workspace_size bytes, 256-byte aligned
+ * HASHENC_EUNSUPPORTED for a Hermite handle or depth > 2.  n must be >= 1. */
+HASHENC_API int hashenc_fd_residual_workspace_size(const hashenc* h, const hashenc_mlp* mlp, int64_t n,
+                                                   size_t* bytes);
+HASHENC_API int hashenc_fd_residual(const hashenc* h, const hashenc_mlp* mlp, float eps, int64_t n,
+                                    const float* x, const float* params, const float* mlp_params,
+                                    float* u_stencil, float* residual, float* loss, float* grad_params,
+                                    float* grad_mlp, void* workspace, size_t workspace_bytes,
+                                    hashenc_stream_t stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 HASHENC_API const char* hashenc_last_error(void);
 

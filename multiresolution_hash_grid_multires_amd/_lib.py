@@ -74,6 +74,10 @@ SIGNATURES = [
      [P, ctypes.POINTER(HashencMlp), I64, ctypes.POINTER(ctypes.c_size_t)]),
     ("hashenc_residual", ctypes.c_int,
      [P, ctypes.POINTER(HashencMlp), I64, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    ("hashenc_fd_residual_workspace_size", ctypes.c_int,
+     [P, ctypes.POINTER(HashencMlp), I64, ctypes.POINTER(ctypes.c_size_t)]),
+    ("hashenc_fd_residual", ctypes.c_int,
+     [P, ctypes.POINTER(HashencMlp), ctypes.c_float, I64, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     ("hashenc_last_error", ctypes.c_char_p, []),
     ("hashenc_debug_indices", ctypes.c_int, [P, I64, P, I32, P, P]),
     ("hashenc_diag_copy", ctypes.c_int, [P, P, I64, P]),

@@ -48,8 +48,10 @@ class Handle:
         self.spec = dict(spec)
 
     def __del__(self):
-        if getattr(self, "ptr", None) is not None and self.ptr.value and _lib._lib is not None:
-            _lib._lib.hashenc_destroy(self.ptr)
+        # at interpreter shutdown the module globals may already be gone
+        lib = getattr(_lib, "_lib", None) if _lib is not None else None
+        if getattr(self, "ptr", None) is not None and self.ptr.value and lib is not None:
+            lib.hashenc_destroy(self.ptr)
             self.ptr = None
 
     @property
@@ -209,6 +211,26 @@ def hashenc_residual(h: Handle, mlp: Mlp, x: torch.Tensor, params: torch.Tensor,
                                   _dev_ptr(grad_params, "grad_params"), _dev_ptr(grad_mlp, "grad_mlp"),
                                   _dev_ptr(workspace, "workspace", dtype=workspace.dtype),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def hashenc_fd_residual_workspace_size(h: Handle, mlp: Mlp, n: int) -> int:
+    b = ctypes.c_size_t()
+    m = mlp.as_c()
+    check(load().hashenc_fd_residual_workspace_size(h, ctypes.byref(m), n, ctypes.byref(b)))
+    return int(b.value)
+
+
+def hashenc_fd_residual(h: Handle, mlp: Mlp, eps: float, x: torch.Tensor, params: torch.Tensor,
+                        mlp_params: torch.Tensor, u_stencil, residual, loss: torch.Tensor, grad_params,
+                        grad_mlp, workspace: torch.Tensor, stream=None) -> None:
+    m = mlp.as_c()
+    check(load().hashenc_fd_residual(h, ctypes.byref(m), float(eps), x.shape[0], _dev_ptr(x, "x"),
+                                     _dev_ptr(params, "params"), _dev_ptr(mlp_params, "mlp_params"),
+                                     _dev_ptr(u_stencil, "u_stencil"), _dev_ptr(residual, "residual"),
+                                     _dev_ptr(loss, "loss"), _dev_ptr(grad_params, "grad_params"),
+                                     _dev_ptr(grad_mlp, "grad_mlp"),
+                                     _dev_ptr(workspace, "workspace", dtype=workspace.dtype),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def hashenc_debug_indices(h: Handle, x: torch.Tensor, order: int, out_rows: torch.Tensor,

@@ -189,9 +189,11 @@ hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& 
                           float* grad, hipStream_t s);
 
 // Interpolant-specific count / scatter launches (d-linear and Hermite kernel files).
+// d-linear count / scatter; u_levels: the chunk's upstream level-major ([L][n][F]) or NULL
+// to read the rows of g_gamma
 hipError_t launch_dlinear_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws,
                               int d, int F, bool scatter, int64_t n, const float* x,
-                              const float* g_gamma, hipStream_t s);
+                              const float* g_gamma, const float* u_levels, hipStream_t s);
 // Hermite count / scatter; u_levels: the chunk's upstream already level-major
 // ([L][n][M][F], as the forward's staging) or NULL to rearrange g_gamma / g_dgamma / g_d2gamma
 hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws,
@@ -200,14 +202,16 @@ hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspa
                               const float* u_levels, hipStream_t s);
 
 constexpr int32_t kMaxBins = 16384;
+constexpr int64_t kBinChunkPoints = int64_t(1) << 20;  // points per pass of the binned backward
 
 // Whether this configuration's bins and staging fit the LDS budgets of the binned path.
 bool binned_fits(const Grid& g, int d, int F, bool hermite);
 
 // Whole binned backward over n points, in chunks that fit the workspace.
 size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite, int64_t n);
-// u_levels (Hermite only, else NULL): upstream already level-major for all n points
-// ([L][n][M][F]); then the row-major upstream pointers are ignored.
+// u_levels (else NULL): upstream already level-major for all n points (Hermite [L][n][M][F],
+// d-linear [L][n][F]; n at most one internal chunk); then the row-major upstream pointers are
+// ignored.
 hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2_mode, int64_t n,
                                const float* x, const float* g_gamma, const float* g_dgamma,
                                const float* g_d2gamma, const float* u_levels, float* grad, void* workspace,

@@ -24,8 +24,6 @@ namespace hg {
 
 namespace {
 
-constexpr int64_t kBinChunkPoints = int64_t(1) << 20;
-
 // counts[tile][bin] -> exclusive prefix over tiles in place; totals[bin] = sum.  The tiles
 // are cut into kScanSegs consecutive segments, one per wavefront of a (64-bin group,
 // segment group) workgroup; a lane owns one bin, so every row access is one coalesced
@@ -451,7 +449,7 @@ hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2
                                hipStream_t s) {
   BinPlan bp;
   make_bin_plan(g, d, F, hermite, bp);
-  if (u_levels && (!hermite || n > kBinChunkPoints)) return hipErrorInvalidValue;  // one chunk only
+  if (u_levels && n > kBinChunkPoints) return hipErrorInvalidValue;  // one chunk only
   char* ws = static_cast<char*>(workspace);
   const int64_t LF = (int64_t)g.Lrow * F;  // upstream row stride
   for (int64_t p0 = 0; p0 < n; p0 += kBinChunkPoints) {
@@ -465,7 +463,7 @@ hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2
     for (int pass = 0; pass < 2; ++pass) {
       hipError_t e = hermite ? launch_hermite_bin(g, bp, w, ws, d, F, d2_mode, pass == 1, c, xc, gg, gd, g2,
                                                   u_levels, s)
-                             : launch_dlinear_bin(g, bp, w, ws, d, F, pass == 1, c, xc, gg, s);
+                             : launch_dlinear_bin(g, bp, w, ws, d, F, pass == 1, c, xc, gg, u_levels, s);
       if (e != hipSuccess) return e;
       if (pass == 0) {
         e = run_bin_middle(bp, w, ws, s);

@@ -164,10 +164,12 @@ __global__ __launch_bounds__(kBlock) void level_major_to_rows_kernel(int32_t L, 
 // the hash through XOR with prime 1), so 2F lanes cooperate on one point: lane
 // (c0, f) owns feature f of the x-corner c0 of every (y, z) corner pair, and each atomic
 // instruction then covers 64 / (2F) points with 2F contiguous dwords each.
+// u_lm: the upstream level-major ([L][n][F]) instead of the rows of g_gamma, or NULL.
 template <int D, int F>
 __global__ __launch_bounds__(kBlock) void dlinear_backward_kernel(const Grid g, int64_t n,
                                                                   const float* __restrict__ x,
                                                                   const float* __restrict__ g_gamma,
+                                                                  const float* __restrict__ u_lm,
                                                                   float* __restrict__ grad) {
   constexpr int LANES = 2 * F;  // lanes per point
   const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
@@ -180,9 +182,10 @@ __global__ __launch_bounds__(kBlock) void dlinear_backward_kernel(const Grid g, 
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
   const int64_t LF = (int64_t)g.Lrow * F;
-  const float* up = g_gamma + p * LF + f;
+  const float* up = u_lm ? u_lm + p * F + f : g_gamma + p * LF + f;
+  const int64_t lstride = u_lm ? n * F : F;  // floats between a point's levels
   for (int l = 0; l < g.L; ++l) {
-    const float G = up[(int64_t)l * F];
+    const float G = up[(int64_t)l * lstride];
     uint32_t base[D];
     float t[D];
     locate<D>(xp, g.N[l], g.Nf[l], base, t);
@@ -265,11 +268,12 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
 // consecutive records and cache lines are written whole.  Single-corner records (levels
 // not in pair mode) are written straight to their slots.
 // PRE: the point's upstream row (Lrow*F <= 32 floats, a multiple of 4) is read once into
-// registers before the level loop; otherwise each level reads its F floats of the row.
+// registers before the level loop; otherwise each level reads its F floats of the row, or of
+// the level-major upstream u_lm when given.
 template <int D, int F, bool PRE>
 __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
     const Grid g, const BinPlan bp, int64_t n, int32_t tile, int32_t nblk, const float* __restrict__ x,
-    const float* __restrict__ g_gamma, const int32_t* __restrict__ counts,
+    const float* __restrict__ g_gamma, const float* __restrict__ u_lm, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
     const BinState* __restrict__ st, float* __restrict__ vals_out) {
   constexpr int NP = 1 << (D - 1);  // x-corner pairs per cell
@@ -336,6 +340,8 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
             if (c == l * F + f) v = up[c];
           G[f] = v;
         }
+      } else if (u_lm) {
+        load_vec<F>(u_lm + ((int64_t)l * n + p) * F, G);  // level-major: coalesced per level
       } else if (g_gamma) {
         load_vec<F>(g_gamma + p * LF + (int64_t)l * F, G);
       } else {
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
 
 template <int D, int F>
 hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, bool scatter,
-                      int64_t n, const float* x, const float* gg, hipStream_t s) {
+                      int64_t n, const float* x, const float* gg, const float* u_lm, hipStream_t s) {
   const dim3 grid((unsigned)w.nblk);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
   if (!scatter) {
@@ -407,18 +413,18 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   float* vals = reinterpret_cast<float*>(ws + w.vals);
   // PRE reads the row as 16-byte pieces: rows of a multiple of 4 floats only, so that every
   // piece is aligned and inside the row
-  if (g.Lrow * F <= 32 && (g.Lrow * F) % 4 == 0) {
+  if (!u_lm && g.Lrow * F <= 32 && (g.Lrow * F) % 4 == 0) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, true>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, true>), grid, dim3(kScatterThreads), lds, s, g, bp, n, w.tile,
-                       w.nblk, x, gg, counts, totals, bin_start, st, vals);
+                       w.nblk, x, gg, nullptr, counts, totals, bin_start, st, vals);
   } else {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, false>), grid, dim3(kScatterThreads), lds, s, g, bp, n, w.tile,
-                       w.nblk, x, gg, counts, totals, bin_start, st, vals);
+                       w.nblk, x, gg, u_lm, counts, totals, bin_start, st, vals);
   }
   return hipGetLastError();
 }
@@ -440,7 +446,7 @@ hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* par
   hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, fp, n, (int32_t)tiles, x,
                      params, scratch);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !gamma) return e;  // no gamma: the level-major staging is the output
   const int32_t P = g.L * F <= 128 ? 64 : 32;  // LDS tile at most 32 x 257 floats
   const size_t lds = sizeof(float) * (size_t)P * (g.L * F + 1);
   hipLaunchKernelGGL((level_major_to_rows_kernel<F>), dim3((unsigned)((n + P - 1) / P)), dim3(kBlock), lds, s, g.L,
@@ -449,11 +455,11 @@ hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* par
 }
 
 template <int D, int F>
-hipError_t launch_bwd(const Grid& g, int64_t n, const float* x, const float* gg, float* grad,
+hipError_t launch_bwd(const Grid& g, int64_t n, const float* x, const float* gg, const float* u_lm, float* grad,
                       hipStream_t s) {
   const int64_t lanes = n * 2 * F;
   const dim3 grid((unsigned)((lanes + kBlock - 1) / kBlock));
-  hipLaunchKernelGGL((dlinear_backward_kernel<D, F>), grid, dim3(kBlock), 0, s, g, n, x, gg, grad);
+  hipLaunchKernelGGL((dlinear_backward_kernel<D, F>), grid, dim3(kBlock), 0, s, g, n, x, gg, u_lm, grad);
   return hipGetLastError();
 }
 
@@ -490,13 +496,14 @@ hipError_t launch_dlinear_forward(const Grid& g, int d, int F, int64_t n, const 
 }
 
 hipError_t launch_dlinear_backward(const Grid& g, int d, int F, int64_t n, const float* x,
-                                   const float* g_gamma, float* grad, hipStream_t s) {
-  HASHENC_DISPATCH_DF(d, F, launch_bwd, g, n, x, g_gamma, grad, s);
+                                   const float* g_gamma, const float* u_levels, float* grad, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_bwd, g, n, x, g_gamma, u_levels, grad, s);
 }
 
 hipError_t launch_dlinear_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int d, int F,
-                              bool scatter, int64_t n, const float* x, const float* g_gamma, hipStream_t s) {
-  HASHENC_DISPATCH_DF(d, F, launch_bin, g, bp, w, ws, scatter, n, x, g_gamma, s);
+                              bool scatter, int64_t n, const float* x, const float* g_gamma,
+                              const float* u_levels, hipStream_t s) {
+  HASHENC_DISPATCH_DF(d, F, launch_bin, g, bp, w, ws, scatter, n, x, g_gamma, u_levels, s);
 }
 
 }  // namespace hg

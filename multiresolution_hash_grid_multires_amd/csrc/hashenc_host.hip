@@ -317,7 +317,7 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
     return fail(HASHENC_EALIGN, "hashenc_backward: device pointers must be 16-byte aligned");
   hipError_t e;
   if (h->kind == HASHENC_DLINEAR)
-    e = hg::launch_dlinear_backward(h->grid, h->d, h->F, n, x, g_gamma, grad_params, stream);
+    e = hg::launch_dlinear_backward(h->grid, h->d, h->F, n, x, g_gamma, nullptr, grad_params, stream);
   else
     e = hg::launch_hermite_backward(h->grid, h->d, h->F, h->d2_mode, n, x, g_gamma, g_dgamma,
                                          g_d2gamma, nullptr, grad_params, stream);
@@ -381,6 +381,59 @@ int hashenc_residual(const hashenc* h, const hashenc_mlp* mlp, int64_t n, const 
                                   mlp->omega, mlp_params, residual, loss, grad_params, grad_mlp,
                                   workspace, binned_supported(h), stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_residual launch");
+  return ok();
+}
+
+static int check_fd(const hashenc* h, const hashenc_mlp* mlp, const char* who) {
+  if (!h) return fail(HASHENC_EINVAL, "%s: NULL handle", who);
+  if (!mlp) return fail(HASHENC_EINVAL, "%s: NULL mlp", who);
+  if (h->kind != HASHENC_DLINEAR)
+    return fail(HASHENC_EUNSUPPORTED, "%s: the finite-difference comparator takes a d-linear handle", who);
+  if (mlp->in != h->L * h->F)
+    return fail(HASHENC_EINVAL, "%s: mlp.in (%d) must equal L*F (%d)", who, mlp->in, h->L * h->F);
+  if (mlp->in > 64) return fail(HASHENC_EUNSUPPORTED, "%s: mlp.in must be <= 64", who);
+  if (mlp->hidden < 1 || mlp->hidden > 64)
+    return fail(HASHENC_EUNSUPPORTED, "%s: hidden width must be in 1..64 (got %d)", who, mlp->hidden);
+  if (mlp->depth < 1 || mlp->depth > 2)
+    return fail(HASHENC_EUNSUPPORTED, "%s: depth must be 1 or 2 (got %d)", who, mlp->depth);
+  if (mlp->out != 1) return fail(HASHENC_EUNSUPPORTED, "%s: output width must be 1", who);
+  if (mlp->reserved != 0) return fail(HASHENC_EINVAL, "%s: mlp.reserved must be 0", who);
+  if (!std::isfinite(mlp->omega)) return fail(HASHENC_EINVAL, "%s: omega must be finite", who);
+  return HASHENC_OK;
+}
+
+int hashenc_fd_residual_workspace_size(const hashenc* h, const hashenc_mlp* mlp, int64_t n, size_t* bytes) {
+  int rc = check_fd(h, mlp, "hashenc_fd_residual_workspace_size");
+  if (rc) return rc;
+  if (n < 1 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_fd_residual_workspace_size: n out of range");
+  if (!bytes) return fail(HASHENC_EINVAL, "hashenc_fd_residual_workspace_size: NULL bytes");
+  *bytes = hg::fd_residual_workspace_bytes(h->grid, h->d, h->F, n, mlp->in, mlp->hidden, mlp->depth,
+                                           binned_supported(h));
+  return ok();
+}
+
+int hashenc_fd_residual(const hashenc* h, const hashenc_mlp* mlp, float eps, int64_t n, const float* x,
+                        const float* params, const float* mlp_params, float* u_stencil, float* residual,
+                        float* loss, float* grad_params, float* grad_mlp, void* workspace, size_t workspace_bytes,
+                        hashenc_stream_t stream) {
+  int rc = check_fd(h, mlp, "hashenc_fd_residual");
+  if (rc) return rc;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(HASHENC_EINVAL, "hashenc_fd_residual: eps must be > 0 and finite");
+  if (n < 1 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_fd_residual: n = %lld out of range", (long long)n);
+  if (!x || !params || !mlp_params || !loss || !workspace)
+    return fail(HASHENC_EINVAL, "hashenc_fd_residual: x, params, mlp_params, loss and workspace must not be NULL");
+  if (!aligned16(x) || !aligned16(params) || !aligned16(mlp_params) || !aligned16(u_stencil) ||
+      !aligned16(residual) || !aligned16(loss) || !aligned16(grad_params) || !aligned16(grad_mlp) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(HASHENC_EALIGN, "hashenc_fd_residual: pointers must be 16-byte aligned (workspace 256-byte)");
+  const size_t need = hg::fd_residual_workspace_bytes(h->grid, h->d, h->F, n, mlp->in, mlp->hidden, mlp->depth,
+                                                      binned_supported(h));
+  if (workspace_bytes < need)
+    return fail(HASHENC_EINVAL, "hashenc_fd_residual: workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  hipError_t e = hg::run_fd_residual(h->grid, h->d, h->F, n, x, params, mlp->in, mlp->hidden, mlp->depth,
+                                     mlp->omega, eps, mlp_params, u_stencil, residual, loss, grad_params, grad_mlp,
+                                     workspace, binned_supported(h), stream);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_fd_residual launch");
   return ok();
 }
 

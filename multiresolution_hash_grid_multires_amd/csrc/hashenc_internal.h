@@ -128,11 +128,13 @@ __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
 // ---------------------------------------------------------------- launchers
 // All launchers assume validated arguments (host side) and n >= 1.
 // scratch: NULL, or dlinear_forward_workspace_bytes for the level-major staging of the output
+// ([L][n][F], active levels); with scratch and gamma NULL the output stays level-major there.
 size_t dlinear_forward_workspace_bytes(const Grid& g, int d, int F, int64_t n);
 hipError_t launch_dlinear_forward(const Grid& g, int d, int F, int64_t n, const float* x,
                                   const float* params, float* gamma, float* scratch, hipStream_t s);
+// u_levels: NULL, or the upstream level-major ([L][n][F], active levels) instead of g_gamma
 hipError_t launch_dlinear_backward(const Grid& g, int d, int F, int64_t n, const float* x,
-                                   const float* g_gamma, float* grad, hipStream_t s);
+                                   const float* g_gamma, const float* u_levels, float* grad, hipStream_t s);
 // Hermite tables of equal size: the packed copy (one contiguous row of all order tables per
 // vertex) that the forward can read instead of the tables; 0 bytes when not packable.
 bool hermite_packable(const Grid& g, int d);
@@ -158,6 +160,12 @@ hipError_t launch_zero_columns(float* out, int64_t rows, int32_t row_floats, int
 
 // Fused PINN residual (Hermite handle): workspace size and the full step.
 int64_t mlp_param_count(int in, int H, int depth);
+// INGP-FD comparator (d-linear handle, SIREN depth 1..2): workspace size and the full step.
+size_t fd_residual_workspace_bytes(const Grid& g, int d, int F, int64_t n, int in, int H, int depth, bool binned);
+hipError_t run_fd_residual(const Grid& g, int d, int F, int64_t n, const float* x, const float* params, int in,
+                           int H, int depth, float omega, float eps, const float* mlp, float* u_stencil,
+                           float* residual, float* loss, float* grad_params, float* grad_mlp, void* workspace,
+                           bool binned, hipStream_t s);
 size_t residual_workspace_bytes(const Grid& g, int d, int F, int64_t n, int in, int H, int depth,
                                 bool binned);
 hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, const float* params,

@@ -652,6 +652,313 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// INGP-FD comparator (Hermite-NGP notes, the 现有痛点 paragraph: the Laplacian of an
+// Instant-NGP encoding + network by central differences, 2d+1 forward passes).  The same
+// matrix-core layout as above, but the R = 2d+1 column groups are the stencil points
+// x, x + eps e_i, x - eps e_i of each of the 16 points (s = 0, 2i+1, 2i+2), each a plain value
+// row with its own nonlinearity:
+//   forward   z_s = W v_s + b,  a_s = sin(omega z_s),  u_s = Wo a_s + bo
+//   FD        Lap u = sum_i (u_{2i+1} - 2 u_0 + u_{2i+2}) / eps^2,  r = Lap u - g(x)
+//   reverse   ubar_s = (2 r / n) c_s (c_0 = -2d / eps^2, else 1 / eps^2),
+//             zbar_s = abar_s omega cos(omega z_s),  vbar_s = W^T zbar_s
+// The encoder rows come from the d-linear forward of the stencil points ordered (point,
+// stencil point), level-major: exactly lm_index's layout with R = 2d+1.
+constexpr int fd_pitch(int D) { return kMP * (2 * D + 1) + 4; }
+
+template <int D, int DEPTH, int NI>
+struct FdLds {
+  float w0[kW][NI + 4];
+  float w1[DEPTH > 1 ? kW : 1][kW + 4];
+  float act0[NI][fd_pitch(D)];                        // V_0: encoder rows of the stencil points
+  float act1[DEPTH > 1 ? kW : 1][fd_pitch(D)];        // V_1
+  float zb[kW][fd_pitch(D)];                          // Zbar of the layer in reverse
+  float uw[kMWaves][2 * D + 1][kMP];                  // per-wave partial u of each stencil point
+};
+
+template <int D, int DEPTH, int NI>
+__global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
+    const MlpArgs a, int64_t n, double inv_n_total, float inv_eps2, const float* __restrict__ x,
+    const float* __restrict__ enc, const float* __restrict__ mlp, float* __restrict__ up,
+    float* __restrict__ u_stencil, float* __restrict__ residual, float* __restrict__ partial) {
+  static_assert(DEPTH == 1 || DEPTH == 2, "matrix-core SIREN covers one or two hidden layers");
+  constexpr int R = 2 * D + 1;
+  constexpr int NC = kMP * R;  // columns
+  static_assert(sizeof(FdLds<D, DEPTH, NI>) <= 160 * 1024, "FD SIREN workgroup LDS exceeds the CU's 160 KB");
+  __shared__ FdLds<D, DEPTH, NI> sh;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lm = lane & 15, lq = lane >> 4;
+  const int H = a.H;
+  const float om = a.omega;
+
+  for (int e = threadIdx.x; e < kW * NI; e += kW * kMWaves) {
+    const int o = e / NI, j = e % NI;
+    sh.w0[o][j] = (o < H && j < a.in) ? mlp[a.woff[0] + o * a.in + j] : 0.0f;
+  }
+  if constexpr (DEPTH > 1) {
+    for (int e = threadIdx.x; e < kW * kW; e += kW * kMWaves) {
+      const int o = e / kW, j = e % kW;
+      sh.w1[o][j] = (o < H && j < H) ? mlp[a.woff[1] + o * H + j] : 0.0f;
+    }
+  }
+  float bias[DEPTH][4], wout[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = 16 * w + 4 * lq + i;
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) bias[k][i] = o < H ? mlp[a.boff[k] + o] : 0.0f;
+    wout[i] = o < H ? mlp[a.woff[DEPTH] + o] : 0.0f;
+  }
+  const float bo = mlp[a.boff[DEPTH]];
+  mf4 gW0[NI / 16];
+  mf4 gW1[DEPTH > 1 ? 4 : 1];
+#pragma unroll
+  for (int t = 0; t < NI / 16; ++t) gW0[t] = mf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < (DEPTH > 1 ? 4 : 1); ++t) gW1[t] = mf4{0.f, 0.f, 0.f, 0.f};
+  float gb[DEPTH][4], gWo[4], sq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    gWo[i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) gb[k][i] = 0.0f;
+  }
+
+  const int64_t n_iter = (n + kMP - 1) / kMP;
+  for (int64_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
+    const int64_t p0 = it * kMP;
+    for (int e = threadIdx.x; e < kMP * R * NI; e += kW * kMWaves) {
+      const int f = e & ((1 << a.fshift) - 1), t = e >> a.fshift;
+      const int r = t % R, t2 = t / R;
+      const int p = t2 % kMP, l = t2 / kMP;
+      const int j = (l << a.fshift) + f;
+      const int64_t pp = p0 + p;
+      sh.act0[j][r * kMP + p] = (j < a.ain && pp < n) ? enc[lm_index(a, n, pp, j, r, R)] : 0.0f;
+    }
+    __syncthreads();
+
+    // forward: every column group is a value row; layers as compile-time steps so the tape
+    // stays in registers
+    mf4 z[DEPTH][R];
+    mf4 atop[R];
+    auto fwd_layer = [&]<int K>() {
+      mf4 acc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = mf4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (K == 0) {
+#pragma unroll
+        for (int kk = 0; kk < NI / 4; ++kk) {
+          const float aw = sh.w0[16 * w + lm][4 * kk + lq];
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r] = mfma16(aw, sh.act0[4 * kk + lq][r * kMP + lm], acc[r]);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const float aw = sh.w1[16 * w + lm][4 * kk + lq];
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r] = mfma16(aw, sh.act1[4 * kk + lq][r * kMP + lm], acc[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[r][i] += bias[K][i];
+        z[K][r] = acc[r];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 16 * w + 4 * lq + i;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float sv = sinf(om * acc[r][i]);
+          if constexpr (K + 1 < DEPTH) sh.act1[o][r * kMP + lm] = sv;
+          else atop[r][i] = sv;
+        }
+      }
+      if constexpr (K + 1 < DEPTH) __syncthreads();
+    };
+    fwd_layer.template operator()<0>();
+    if constexpr (DEPTH > 1) fwd_layer.template operator()<1>();
+
+    // u_s = wout . a_s (+ bo): partial sums over the wavefront's 16 neurons, then over waves
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part = fmaf(wout[i], atop[r][i], part);
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      if (lq == 0) sh.uw[w][r][lm] = part;
+    }
+    __syncthreads();
+    const int64_t pp = p0 + lm;
+    float seed = 0.0f;
+    if (pp < n) {
+      float u0 = 0.0f, lap = 0.0f;  // the output bias cancels in every second difference
+#pragma unroll
+      for (int q = 0; q < kMWaves; ++q) u0 += sh.uw[q][0][lm];
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        float up1 = 0.0f, um1 = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kMWaves; ++q) {
+          up1 += sh.uw[q][2 * i + 1][lm];
+          um1 += sh.uw[q][2 * i + 2][lm];
+        }
+        lap += (up1 - 2.0f * u0 + um1) * inv_eps2;
+        if (u_stencil && w == 0 && lq == 0) {
+          u_stencil[pp * R + 2 * i + 1] = up1 + bo;
+          u_stencil[pp * R + 2 * i + 2] = um1 + bo;
+        }
+      }
+      float src = -(float)D * 9.8696044010893586f;  // -d pi^2
+#pragma unroll
+      for (int i = 0; i < D; ++i) src *= sinpif(x[pp * D + i]);
+      const float res = lap - src;
+      if (w == 0 && lq == 0) {
+        sq = fmaf(res, res, sq);
+        if (residual) residual[pp] = res;
+        if (u_stencil) u_stencil[pp * R] = u0 + bo;
+      }
+      seed = (float)(2.0 * (double)res * inv_n_total) * inv_eps2;  // times c_s / (-2d) or 1
+    }
+    // seeds of the stencil points: c_0 = -2d / eps^2, the others 1 / eps^2
+    mf4 abar[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float sr = r == 0 ? -2.0f * (float)D * seed : seed;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        gWo[i] = fmaf(sr, atop[r][i], gWo[i]);
+        abar[r][i] = sr * wout[i];
+      }
+    }
+    auto rev_layer = [&]<int K>() {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 16 * w + 4 * lq + i;
+        float zsum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float zbar = abar[r][i] * om * cosf(om * z[K][r][i]);
+          zsum += zbar;
+          sh.zb[o][r * kMP + lm] = zbar;
+        }
+        gb[K][i] += zsum;
+      }
+      __syncthreads();
+      // weight gradient: dL/dW_K[16w + .][j] += sum_c Zbar[o][c] V_K[j][c]
+      for (int kk = 0; kk < NC / 4; ++kk) {
+        const float az = sh.zb[16 * w + lm][4 * kk + lq];
+        if constexpr (K == 0) {
+#pragma unroll
+          for (int t = 0; t < NI / 16; ++t) gW0[t] = mfma16(az, sh.act0[16 * t + lm][4 * kk + lq], gW0[t]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) gW1[t] = mfma16(az, sh.act1[16 * t + lm][4 * kk + lq], gW1[t]);
+        }
+      }
+      constexpr int fi = K == 0 ? NI : kW;
+      mf4 vbar[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) vbar[r] = mf4{0.f, 0.f, 0.f, 0.f};
+      if (16 * w < fi) {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const float aw = K == 0 ? sh.w0[4 * kk + lq][16 * w + lm] : sh.w1[4 * kk + lq][16 * w + lm];
+#pragma unroll
+          for (int r = 0; r < R; ++r) vbar[r] = mfma16(aw, sh.zb[4 * kk + lq][r * kMP + lm], vbar[r]);
+        }
+      }
+      __syncthreads();  // zb and the layer's inputs are rewritten next
+      if constexpr (K > 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) abar[r] = vbar[r];
+      } else if (16 * w < fi && pp < n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * w + 4 * lq + i;
+          if (j < a.ain) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) up[lm_index(a, n, pp, j, r, R)] = vbar[r][i];
+          }
+        }
+      }
+    };
+    if constexpr (DEPTH > 1) rev_layer.template operator()<1>();
+    rev_layer.template operator()<0>();
+  }
+
+  float* part = partial + (int64_t)blockIdx.x * (a.n_mlp + 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = 16 * w + 4 * lq + i;
+    if (o < H) {
+#pragma unroll
+      for (int t = 0; t < NI / 16; ++t) {
+        const int j = 16 * t + lm;
+        if (j < a.in) part[a.woff[0] + (int64_t)o * a.in + j] = gW0[t][i];
+      }
+      if constexpr (DEPTH > 1) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = 16 * t + lm;
+          if (j < H) part[a.woff[1] + (int64_t)o * H + j] = gW1[t][i];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[DEPTH + 1];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) v[k] = gb[k][i];
+    v[DEPTH] = gWo[i];
+#pragma unroll
+    for (int k = 0; k <= DEPTH; ++k)
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) v[k] += __shfl_xor(v[k], off, 64);
+    const int o = 16 * w + 4 * lq + i;
+    if (lm == 0 && o < H) {
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) part[a.boff[k] + o] = v[k];
+      part[a.woff[DEPTH] + o] = v[DEPTH];
+    }
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) sq += __shfl_xor(sq, off, 64);
+    if (lane == 0) {
+      part[a.boff[DEPTH]] = 0.0f;  // the output bias cancels in the stencil
+      part[a.n_mlp] = sq;
+    }
+  }
+}
+
+// Stencil point sets: xs[p][s][d], s = 0: x; s = 2i+1: x + eps e_i; s = 2i+2: x - eps e_i
+// (one fp32 addition, as any fp32 input of the encoder).
+template <int D>
+__global__ __launch_bounds__(kBlock) void fd_stencil_kernel(int64_t n, float eps, const float* __restrict__ x,
+                                                            float* __restrict__ xs) {
+  constexpr int S = 2 * D + 1;
+  const int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // (point, stencil point)
+  if (q >= n * S) return;
+  const int64_t p = q / S;
+  const int s = (int)(q - p * S);
+  float v[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) v[i] = x[p * D + i];
+  if (s > 0) {
+    const int i = (s - 1) >> 1;
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+      if (k == i) v[k] = (s & 1) ? v[k] + eps : v[k] - eps;
+  }
+#pragma unroll
+  for (int i = 0; i < D; ++i) xs[q * D + i] = v[i];
+}
+
 // Sum of the per-wave partial rows, in two passes: each workgroup of the first pass adds a
 // slice of kSliceRows rows for 256 columns in fp64; the second pass adds the slices and
 // applies the result (grad_mlp += ..., loss (+)= ... / n).
@@ -762,7 +1069,150 @@ hipError_t dispatch_siren(int d, int depth, int in, const MlpArgs& a, int64_t n,
   return dispatch_depth<3>(depth, in, a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
 }
 
+constexpr int kFdBlocks = 256;  // one workgroup per CU (LDS-limited)
+
+template <int D, int DEPTH, int NI>
+hipError_t launch_fd_siren(const MlpArgs& a, int64_t n, double inv_n, float inv_eps2, const float* x,
+                           const float* enc, const float* mlp, float* up, float* u_stencil, float* residual,
+                           float* partial, int& rows, hipStream_t s) {
+  int blocks = (int)((n + kMP - 1) / kMP);
+  if (blocks > kFdBlocks) blocks = kFdBlocks;
+  rows = blocks;
+  hipLaunchKernelGGL((siren_fd_mfma_kernel<D, DEPTH, NI>), dim3(blocks), dim3(kW * kMWaves), 0, s, a, n, inv_n,
+                     inv_eps2, x, enc, mlp, up, u_stencil, residual, partial);
+  return hipGetLastError();
+}
+
+template <int D, int DEPTH>
+hipError_t fd_dispatch_in(int in, const MlpArgs& a, int64_t n, double inv_n, float inv_eps2, const float* x,
+                          const float* enc, const float* mlp, float* up, float* u_stencil, float* residual,
+                          float* partial, int& rows, hipStream_t s) {
+  if (in <= 16)
+    return launch_fd_siren<D, DEPTH, 16>(a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s);
+  if (in <= 32)
+    return launch_fd_siren<D, DEPTH, 32>(a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s);
+  return launch_fd_siren<D, DEPTH, 64>(a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s);
+}
+
+hipError_t fd_dispatch(int d, int depth, int in, const MlpArgs& a, int64_t n, double inv_n, float inv_eps2,
+                       const float* x, const float* enc, const float* mlp, float* up, float* u_stencil,
+                       float* residual, float* partial, int& rows, hipStream_t s) {
+  if (d == 2)
+    return depth == 1 ? fd_dispatch_in<2, 1>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s)
+                      : fd_dispatch_in<2, 2>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s);
+  return depth == 1 ? fd_dispatch_in<3, 1>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s)
+                    : fd_dispatch_in<3, 2>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s);
+}
+
+// Centre points per FD chunk: the chunk's 2d+1 stencil sets fit one binned-backward chunk,
+// whose level-major upstream then comes straight from the SIREN kernel.
+int64_t fd_chunk_points(int d) { return (kBinChunkPoints / (2 * d + 1)) & ~int64_t(kMP - 1); }
+
+struct FdWorkspaceLayout {
+  size_t xs, enc, up, partial, slices, bins, total;
+};
+
+FdWorkspaceLayout fd_workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t n_mlp, bool binned) {
+  const int64_t cmax = fd_chunk_points(d);
+  const int64_t c = n < cmax ? n : cmax;
+  const int64_t cs = c * (2 * d + 1);
+  FdWorkspaceLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  w.xs = take(sizeof(float) * (size_t)cs * d);
+  w.enc = take(dlinear_forward_workspace_bytes(g, d, F, cs));  // level-major [L][c (2d+1)][F]
+  w.up = take(dlinear_forward_workspace_bytes(g, d, F, cs));
+  w.partial = take(sizeof(float) * (size_t)kFdBlocks * (n_mlp + 1));
+  w.slices = take(sizeof(double) * (size_t)((kFdBlocks + kSliceRows - 1) / kSliceRows) * (n_mlp + 1));
+  w.bins = take(binned ? binned_backward_workspace_bytes(g, d, F, false, cs) : 0);
+  w.total = off;
+  return w;
+}
+
+MlpArgs make_mlp_args(const Grid& g, int F, int in, int H, int depth, float omega) {
+  MlpArgs a;
+  a.in = in;
+  a.ain = g.L * F;  // levels l >= g.L are inactive: zero inputs, no upstream
+  a.H = H;
+  a.depth = depth;
+  a.omega = omega;
+  a.fshift = F == 1 ? 0 : F == 2 ? 1 : F == 4 ? 2 : 3;
+  a.n_mlp = 0;
+  for (int k = 0; k <= kMaxDepth; ++k) { a.woff[k] = 0; a.boff[k] = 0; }
+  int64_t off = 0;
+  for (int k = 0; k <= depth; ++k) {
+    const int64_t fi = k == 0 ? in : H;
+    const int64_t fo = k == depth ? 1 : H;
+    a.woff[k] = off; off += fi * fo;
+    a.boff[k] = off; off += fo;
+  }
+  a.n_mlp = off;
+  return a;
+}
+
+// Sum the partial rows of one chunk into grad_mlp and the loss (first chunk: loss = ...).
+hipError_t reduce_partials(const MlpArgs& a, const float* partial, int64_t rows, double* slices, double inv_n,
+                           bool first, float* grad_mlp, float* loss, hipStream_t s) {
+  const int n_slices = (int)((rows + kSliceRows - 1) / kSliceRows);
+  const unsigned col_blocks = (unsigned)((a.n_mlp + 1 + 255) / 256);
+  hipLaunchKernelGGL(reduce_partials_slices_kernel, dim3(col_blocks, (unsigned)n_slices), dim3(256), 0, s,
+                     partial, rows, a.n_mlp + 1, slices);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_partials_apply_kernel, dim3(col_blocks), dim3(256), 0, s, slices, n_slices, a.n_mlp,
+                     inv_n, first ? 1 : 0, grad_mlp, loss);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t fd_residual_workspace_bytes(const Grid& g, int d, int F, int64_t n, int in, int H, int depth, bool binned) {
+  return fd_workspace_layout(g, d, F, n, mlp_param_count(in, H, depth), binned).total;
+}
+
+hipError_t run_fd_residual(const Grid& g, int d, int F, int64_t n, const float* x, const float* params, int in,
+                           int H, int depth, float omega, float eps, const float* mlp, float* u_stencil,
+                           float* residual, float* loss, float* grad_params, float* grad_mlp, void* workspace,
+                           bool binned, hipStream_t s) {
+  const MlpArgs a = make_mlp_args(g, F, in, H, depth, omega);
+  const FdWorkspaceLayout wl = fd_workspace_layout(g, d, F, n, a.n_mlp, binned);
+  char* ws = static_cast<char*>(workspace);
+  float* xs = reinterpret_cast<float*>(ws + wl.xs);
+  float* enc = reinterpret_cast<float*>(ws + wl.enc);
+  float* up = reinterpret_cast<float*>(ws + wl.up);
+  float* partial = reinterpret_cast<float*>(ws + wl.partial);
+  double* slices = reinterpret_cast<double*>(ws + wl.slices);
+  const double inv_n = 1.0 / (double)n;
+  const float inv_eps2 = (float)(1.0 / ((double)eps * (double)eps));
+  const int S = 2 * d + 1;
+  const int64_t cmax = fd_chunk_points(d);
+  for (int64_t p0 = 0; p0 < n; p0 += cmax) {
+    const int64_t c = (n - p0) < cmax ? (n - p0) : cmax;
+    const float* xc = x + p0 * d;
+    const int64_t cs = c * S;
+    const dim3 sgrid((unsigned)((cs + kBlock - 1) / kBlock));
+    if (d == 2) hipLaunchKernelGGL(fd_stencil_kernel<2>, sgrid, dim3(kBlock), 0, s, c, eps, xc, xs);
+    else hipLaunchKernelGGL(fd_stencil_kernel<3>, sgrid, dim3(kBlock), 0, s, c, eps, xc, xs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the 2d+1 encodings of every point, level-major: the SIREN kernel's input layout
+    e = launch_dlinear_forward(g, d, F, cs, xs, params, nullptr, enc, s);
+    if (e != hipSuccess) return e;
+    int rows = 0;
+    e = fd_dispatch(d, depth, in, a, c, inv_n, inv_eps2, xc, enc, mlp, up, u_stencil ? u_stencil + p0 * S : nullptr,
+                    residual ? residual + p0 : nullptr, partial, rows, s);
+    if (e != hipSuccess) return e;
+    e = reduce_partials(a, partial, rows, slices, inv_n, p0 == 0, grad_mlp, loss, s);
+    if (e != hipSuccess) return e;
+    if (grad_params) {
+      e = binned ? run_binned_backward(g, d, F, false, 0, cs, xs, nullptr, nullptr, nullptr, up, grad_params,
+                                       ws + wl.bins, s)
+                 : launch_dlinear_backward(g, d, F, cs, xs, nullptr, up, grad_params, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
 
 int64_t mlp_param_count(int in, int H, int depth) {
   int64_t n = 0;

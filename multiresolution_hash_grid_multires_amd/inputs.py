@@ -1,6 +1,6 @@
 """Seeded synthetic workloads shared by the tests, the benchmark and the smoke check.
 
-This module holds data only: the five workload specifications and NumPy generators for
+This module holds data only: the workload specifications and NumPy generators for
 points, table entries, upstream gradients and MLP weights.  It contains none of the
 encoding's arithmetic, so both the HIP path and the CPU oracle can be fed from it.
 
@@ -64,6 +64,21 @@ WORKLOADS: dict[str, dict] = {
         "n_points": 1 << 21,
         "tables": ("normal", 1e-2),
         "mlp": {"hidden": 64, "depth": 2, "omega": 30.0},
+        "clustered_half": True,
+        "outputs": ("residual", "loss"),
+    },
+    # INGP-FD comparator: the same residual step with the 3D d-linear encoding of the standard
+    # size (N 16..2048) and the Laplacian of u by central differences over 7 stencil points,
+    # step eps = 2^-11 (the finest level's cell width); same SIREN, points and table scale as
+    # the fused Hermite residual.
+    "fd_residual3d": {
+        "id": 6,
+        "spec": {"d": 3, "L": 16, "F": 2, "kind": "dlinear", "T": [1 << 19], "n_min": 16,
+                 "n_max": 2048},
+        "n_points": 1 << 21,
+        "tables": ("normal", 1e-2),
+        "mlp": {"hidden": 64, "depth": 2, "omega": 30.0},
+        "fd_eps": 2.0 ** -11,
         "clustered_half": True,
         "outputs": ("residual", "loss"),
     },
