@@ -109,17 +109,38 @@ def mlp_flops_per_point(d: int, n_in: int, hidden: int, depth: int) -> int:
     return 3 * fwd
 
 
+def fd_mlp_flops_per_point(d: int, n_in: int, hidden: int, depth: int) -> int:
+    """Multiply-add FLOPs of the SIREN part per point of the finite-difference comparator:
+    2d+1 stencil points, each a value-only forward, and a reverse sweep costing twice the
+    forward (weight gradients and input adjoints)."""
+    fwd = 0
+    for k in range(depth):
+        fan_in = n_in if k == 0 else hidden
+        fwd += 2 * fan_in * hidden
+    fwd += 2 * hidden
+    return (2 * d + 1) * 3 * fwd
+
+
 def residual_bench(args, torch, api, I, W) -> int:
+    """One fused residual step (hashenc_residual, Hermite) or one finite-difference comparator
+    step (hashenc_fd_residual, d-linear, when the workload names an FD step)."""
     spec, m = W["spec"], W["mlp"]
+    fd = "fd_eps" in W
     n = W["n_points"]
     dev = torch.device("cuda:0")
     enc = api.HashGridEncoding(spec)
     n_in = spec["L"] * spec["F"]
+    d = spec["d"]
     mlp = api.Mlp(n_in, m["hidden"], m["depth"], m["omega"])
-    x = torch.from_numpy(I.points(W["id"], n, spec["d"], clustered_half=W.get("clustered_half", False))).to(dev)
-    params = torch.from_numpy(I.tables(W["id"], enc.n_params, W["tables"])).to(dev)
-    mlp_params = torch.from_numpy(I.siren_mlp(W["id"], n_in, m["hidden"], m["depth"])).to(dev)
-    ws = torch.empty(api.hashenc_residual_workspace_size(enc.handle, mlp, n), dtype=torch.uint8, device=dev)
+    x_h = I.points(W["id"], n, d, clustered_half=W.get("clustered_half", False))
+    params_h = I.tables(W["id"], enc.n_params, W["tables"])
+    mlp_h = I.siren_mlp(W["id"], n_in, m["hidden"], m["depth"])
+    x = torch.from_numpy(x_h).to(dev)
+    params = torch.from_numpy(params_h).to(dev)
+    mlp_params = torch.from_numpy(mlp_h).to(dev)
+    wsb = (api.hashenc_fd_residual_workspace_size(enc.handle, mlp, n) if fd
+           else api.hashenc_residual_workspace_size(enc.handle, mlp, n))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     r = torch.empty(n, device=dev)
     loss = torch.empty(1, device=dev)
     gp = torch.zeros(enc.n_params, device=dev)
@@ -128,7 +149,10 @@ def residual_bench(args, torch, api, I, W) -> int:
     def step():
         gp.zero_()
         gm.zero_()
-        api.hashenc_residual(enc.handle, mlp, x, params, mlp_params, r, loss, gp, gm, ws)
+        if fd:
+            api.hashenc_fd_residual(enc.handle, mlp, W["fd_eps"], x, params, mlp_params, None, r, loss, gp, gm, ws)
+        else:
+            api.hashenc_residual(enc.handle, mlp, x, params, mlp_params, r, loss, gp, gm, ws)
 
     for _ in range(args.warmup):
         step()
@@ -140,21 +164,53 @@ def residual_bench(args, torch, api, I, W) -> int:
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.steps
-    lap_spec = dict(spec, d2_mode="laplacian")  # active_levels carried over
-    alg = algorithmic_bytes_per_point(lap_spec)
-    enc_bytes = (alg["forward"] + alg["backward"]) * n
-    flops = mlp_flops_per_point(spec["d"], n_in, m["hidden"], m["depth"]) * n
+    if fd:
+        # every stencil point: a d-linear forward and backward, plus the level-major encoder
+        # rows and their upstream written and read once each
+        alg = algorithmic_bytes_per_point(spec)
+        active = int(spec.get("active_levels") or spec["L"])
+        enc_bytes = (2 * d + 1) * (alg["forward"] + alg["backward"] + 4 * 4 * active * spec["F"]) * n
+        flops = fd_mlp_flops_per_point(d, n_in, m["hidden"], m["depth"]) * n
+    else:
+        lap_spec = dict(spec, d2_mode="laplacian")  # active_levels carried over
+        alg = algorithmic_bytes_per_point(lap_spec)
+        enc_bytes = (alg["forward"] + alg["backward"]) * n
+        flops = mlp_flops_per_point(d, n_in, m["hidden"], m["depth"]) * n
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle as it stands on the host cores, on the first points of the same workload
+        # (about --cpu-seconds of work), scaled to points/s
+        from oracle import oracle as O
+        k = 256
+        while True:
+            t0 = time.perf_counter()
+            if fd:
+                O.fd_residual(spec, m["hidden"], m["depth"], m["omega"], W["fd_eps"], x_h[:k], params_h, mlp_h)
+            else:
+                O.residual(spec, m["hidden"], m["depth"], m["omega"], x_h[:k], params_h, mlp_h)
+            dt = time.perf_counter() - t0
+            if dt > 0.3 * args.cpu_seconds or k >= n:
+                break
+            k = min(n, int(k * min(16.0, max(2.0, 0.5 * args.cpu_seconds / max(dt, 1e-3)))))
+        cpu = {"value": round(k / dt, 1), "unit": "points/s", "cores": O.max_threads(), "kind": "oracle",
+               "sample": f"the first {k} of the {n} points of the same workload, one step (fp64 oracle)",
+               "seconds": round(dt, 2)}
+
+    what = "INGP-FD comparator steps" if fd else "PINN residual steps"
     print(json.dumps({
-        "metric": f"PINN residual steps: points/s ({args.workload}"
+        "metric": f"{what}: points/s ({args.workload}"
                   + (f", {args.active_levels} of {spec['L']} levels active)" if args.active_levels else ")"),
         "value": round(n / (ms * 1e-3), 1),
         "unit": "points/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "n_points": n, "hidden": m["hidden"], "depth": m["depth"],
-                   "omega": m["omega"], "active_levels": int(spec.get("active_levels") or spec["L"])},
+                   "omega": m["omega"], "active_levels": int(spec.get("active_levels") or spec["L"]),
+                   **({"fd_eps": W["fd_eps"]} if fd else {})},
         "encoder_alg_GBps_over_step": round(enc_bytes / (ms * 1e-3) / 1e9, 1),
         "mlp_TFLOPs_over_step": round(flops / (ms * 1e-3) / 1e12, 2),
+        "cpu_baseline": cpu,
         "loss": float(loss.item())}), flush=True)
     return 0
 

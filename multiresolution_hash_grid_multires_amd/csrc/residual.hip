@@ -662,9 +662,18 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
 //   FD        Lap u = sum_i (u_{2i+1} - 2 u_0 + u_{2i+2}) / eps^2,  r = Lap u - g(x)
 //   reverse   ubar_s = (2 r / n) c_s (c_0 = -2d / eps^2, else 1 / eps^2),
 //             zbar_s = abar_s omega cos(omega z_s),  vbar_s = W^T zbar_s
-// The encoder rows come from the d-linear forward of the stencil points ordered (point,
-// stencil point), level-major: exactly lm_index's layout with R = 2d+1.
+// A point's 2d+1 stencil copies share their cells on all but the finest levels.  The forward
+// runs them point-major (copies on neighbouring lanes share the gathers' cache lines), so the
+// encoder rows arrive in lm_index's layout with R = 2d+1; the upstream goes out
+// stencil-major, [L][2d+1][n][F], and the backward runs on the stencil-major copy of the
+// point sets, which keeps a point's copies out of one wavefront (no same-row conflicts in the
+// reduction's LDS accumulation).
 constexpr int fd_pitch(int D) { return kMP * (2 * D + 1) + 4; }
+
+__device__ __forceinline__ int64_t fd_index(const MlpArgs& a, int64_t n, int64_t p, int j, int r, int R) {
+  const int l = j >> a.fshift, f = j & ((1 << a.fshift) - 1);
+  return ((((int64_t)l * R + r) * n + p) << a.fshift) + f;
+}
 
 template <int D, int DEPTH, int NI>
 struct FdLds {
@@ -727,6 +736,7 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
   const int64_t n_iter = (n + kMP - 1) / kMP;
   for (int64_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
     const int64_t p0 = it * kMP;
+    // walked level by level: the 16 points' R stencil rows of F features are contiguous
     for (int e = threadIdx.x; e < kMP * R * NI; e += kW * kMWaves) {
       const int f = e & ((1 << a.fshift) - 1), t = e >> a.fshift;
       const int r = t % R, t2 = t / R;
@@ -881,7 +891,7 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
           const int j = 16 * w + 4 * lq + i;
           if (j < a.ain) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) up[lm_index(a, n, pp, j, r, R)] = vbar[r][i];
+            for (int r = 0; r < R; ++r) up[fd_index(a, n, pp, j, r, R)] = vbar[r][i];
           }
         }
       }
@@ -936,27 +946,27 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
   }
 }
 
-// Stencil point sets: xs[p][s][d], s = 0: x; s = 2i+1: x + eps e_i; s = 2i+2: x - eps e_i
-// (one fp32 addition, as any fp32 input of the encoder).
+// Stencil point sets, s = 0: x; s = 2i+1: x + eps e_i; s = 2i+2: x - eps e_i (one fp32
+// addition, as any fp32 input of the encoder), written point-major (xp[p][s][d], for the
+// forward) and stencil-major (xs[s][p][d], for the backward).
 template <int D>
 __global__ __launch_bounds__(kBlock) void fd_stencil_kernel(int64_t n, float eps, const float* __restrict__ x,
-                                                            float* __restrict__ xs) {
+                                                            float* __restrict__ xp, float* __restrict__ xs) {
   constexpr int S = 2 * D + 1;
-  const int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // (point, stencil point)
-  if (q >= n * S) return;
-  const int64_t p = q / S;
-  const int s = (int)(q - p * S);
-  float v[D];
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // one point, all its stencil points
+  if (p >= n) return;
+  float x0[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) v[i] = x[p * D + i];
-  if (s > 0) {
-    const int i = (s - 1) >> 1;
+  for (int i = 0; i < D; ++i) x0[i] = x[p * D + i];
 #pragma unroll
-    for (int k = 0; k < D; ++k)
-      if (k == i) v[k] = (s & 1) ? v[k] + eps : v[k] - eps;
+  for (int s = 0; s < S; ++s) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const float v = (s > 0 && i == (s - 1) / 2) ? ((s & 1) ? x0[i] + eps : x0[i] - eps) : x0[i];
+      xp[(p * S + s) * D + i] = v;
+      xs[((int64_t)s * n + p) * D + i] = v;
+    }
   }
-#pragma unroll
-  for (int i = 0; i < D; ++i) xs[q * D + i] = v[i];
 }
 
 // Sum of the per-wave partial rows, in two passes: each workgroup of the first pass adds a
@@ -1109,7 +1119,7 @@ hipError_t fd_dispatch(int d, int depth, int in, const MlpArgs& a, int64_t n, do
 int64_t fd_chunk_points(int d) { return (kBinChunkPoints / (2 * d + 1)) & ~int64_t(kMP - 1); }
 
 struct FdWorkspaceLayout {
-  size_t xs, enc, up, partial, slices, bins, total;
+  size_t xp, xs, enc, up, partial, slices, bins, total;
 };
 
 FdWorkspaceLayout fd_workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t n_mlp, bool binned) {
@@ -1119,6 +1129,7 @@ FdWorkspaceLayout fd_workspace_layout(const Grid& g, int d, int F, int64_t n, in
   FdWorkspaceLayout w;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  w.xp = take(sizeof(float) * (size_t)cs * d);
   w.xs = take(sizeof(float) * (size_t)cs * d);
   w.enc = take(dlinear_forward_workspace_bytes(g, d, F, cs));  // level-major [L][c (2d+1)][F]
   w.up = take(dlinear_forward_workspace_bytes(g, d, F, cs));
@@ -1177,6 +1188,7 @@ hipError_t run_fd_residual(const Grid& g, int d, int F, int64_t n, const float* 
   const MlpArgs a = make_mlp_args(g, F, in, H, depth, omega);
   const FdWorkspaceLayout wl = fd_workspace_layout(g, d, F, n, a.n_mlp, binned);
   char* ws = static_cast<char*>(workspace);
+  float* xp = reinterpret_cast<float*>(ws + wl.xp);
   float* xs = reinterpret_cast<float*>(ws + wl.xs);
   float* enc = reinterpret_cast<float*>(ws + wl.enc);
   float* up = reinterpret_cast<float*>(ws + wl.up);
@@ -1190,13 +1202,13 @@ hipError_t run_fd_residual(const Grid& g, int d, int F, int64_t n, const float* 
     const int64_t c = (n - p0) < cmax ? (n - p0) : cmax;
     const float* xc = x + p0 * d;
     const int64_t cs = c * S;
-    const dim3 sgrid((unsigned)((cs + kBlock - 1) / kBlock));
-    if (d == 2) hipLaunchKernelGGL(fd_stencil_kernel<2>, sgrid, dim3(kBlock), 0, s, c, eps, xc, xs);
-    else hipLaunchKernelGGL(fd_stencil_kernel<3>, sgrid, dim3(kBlock), 0, s, c, eps, xc, xs);
+    const dim3 sgrid((unsigned)((c + kBlock - 1) / kBlock));
+    if (d == 2) hipLaunchKernelGGL(fd_stencil_kernel<2>, sgrid, dim3(kBlock), 0, s, c, eps, xc, xp, xs);
+    else hipLaunchKernelGGL(fd_stencil_kernel<3>, sgrid, dim3(kBlock), 0, s, c, eps, xc, xp, xs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // the 2d+1 encodings of every point, level-major: the SIREN kernel's input layout
-    e = launch_dlinear_forward(g, d, F, cs, xs, params, nullptr, enc, s);
+    // the 2d+1 encodings of every point, point-major then level-major: the SIREN kernel's input
+    e = launch_dlinear_forward(g, d, F, cs, xp, params, nullptr, enc, s);
     if (e != hipSuccess) return e;
     int rows = 0;
     e = fd_dispatch(d, depth, in, a, c, inv_n, inv_eps2, xc, enc, mlp, up, u_stencil ? u_stencil + p0 * S : nullptr,
