@@ -685,27 +685,36 @@ struct FdLds {
   float uw[kMWaves][2 * D + 1][kMP];                  // per-wave partial u of each stencil point
 };
 
+// Two row groups of four wavefronts: wavefront w owns neurons 16 (w % 4) .. + 15 for the
+// stencil rows of group w / 4 (rows 0..3 and 4..2d), so each wavefront carries about half the
+// rows' tape and accumulators and two wavefronts share every SIMD.  Every row group writes its
+// own partial-gradient row.
+constexpr int kFdGroups = 2;
+constexpr int kFdWaves = kMWaves * kFdGroups;
+
 template <int D, int DEPTH, int NI>
-__global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
+__global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
     const MlpArgs a, int64_t n, double inv_n_total, float inv_eps2, const float* __restrict__ x,
     const float* __restrict__ enc, const float* __restrict__ mlp, float* __restrict__ up,
     float* __restrict__ u_stencil, float* __restrict__ residual, float* __restrict__ partial) {
   static_assert(DEPTH == 1 || DEPTH == 2, "matrix-core SIREN covers one or two hidden layers");
   constexpr int R = 2 * D + 1;
-  constexpr int NC = kMP * R;  // columns
+  constexpr int RG = (R + kFdGroups - 1) / kFdGroups;  // rows per group (the last may have fewer)
   static_assert(sizeof(FdLds<D, DEPTH, NI>) <= 160 * 1024, "FD SIREN workgroup LDS exceeds the CU's 160 KB");
   __shared__ FdLds<D, DEPTH, NI> sh;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wn = w & (kMWaves - 1), rg = w / kMWaves;  // neuron tile, row group
+  const int r0 = rg * RG;                              // first row of the group
   const int lm = lane & 15, lq = lane >> 4;
   const int H = a.H;
   const float om = a.omega;
 
-  for (int e = threadIdx.x; e < kW * NI; e += kW * kMWaves) {
+  for (int e = threadIdx.x; e < kW * NI; e += kW * kFdWaves) {
     const int o = e / NI, j = e % NI;
     sh.w0[o][j] = (o < H && j < a.in) ? mlp[a.woff[0] + o * a.in + j] : 0.0f;
   }
   if constexpr (DEPTH > 1) {
-    for (int e = threadIdx.x; e < kW * kW; e += kW * kMWaves) {
+    for (int e = threadIdx.x; e < kW * kW; e += kW * kFdWaves) {
       const int o = e / kW, j = e % kW;
       sh.w1[o][j] = (o < H && j < H) ? mlp[a.woff[1] + o * H + j] : 0.0f;
     }
@@ -713,7 +722,7 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
   float bias[DEPTH][4], wout[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int o = 16 * w + 4 * lq + i;
+    const int o = 16 * wn + 4 * lq + i;
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) bias[k][i] = o < H ? mlp[a.boff[k] + o] : 0.0f;
     wout[i] = o < H ? mlp[a.woff[DEPTH] + o] : 0.0f;
@@ -737,7 +746,7 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
   for (int64_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
     const int64_t p0 = it * kMP;
     // walked level by level: the 16 points' R stencil rows of F features are contiguous
-    for (int e = threadIdx.x; e < kMP * R * NI; e += kW * kMWaves) {
+    for (int e = threadIdx.x; e < kMP * R * NI; e += kW * kFdWaves) {
       const int f = e & ((1 << a.fshift) - 1), t = e >> a.fshift;
       const int r = t % R, t2 = t / R;
       const int p = t2 % kMP, l = t2 / kMP;
@@ -749,41 +758,46 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
 
     // forward: every column group is a value row; layers as compile-time steps so the tape
     // stays in registers
-    mf4 z[DEPTH][R];
-    mf4 atop[R];
+    mf4 z[DEPTH][RG];
+    mf4 atop[RG];
     auto fwd_layer = [&]<int K>() {
-      mf4 acc[R];
+      mf4 acc[RG];
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = mf4{0.f, 0.f, 0.f, 0.f};
+      for (int rr = 0; rr < RG; ++rr) acc[rr] = mf4{0.f, 0.f, 0.f, 0.f};
       if constexpr (K == 0) {
 #pragma unroll
         for (int kk = 0; kk < NI / 4; ++kk) {
-          const float aw = sh.w0[16 * w + lm][4 * kk + lq];
+          const float aw = sh.w0[16 * wn + lm][4 * kk + lq];
 #pragma unroll
-          for (int r = 0; r < R; ++r) acc[r] = mfma16(aw, sh.act0[4 * kk + lq][r * kMP + lm], acc[r]);
+          for (int rr = 0; rr < RG; ++rr)
+            if (r0 + rr < R) acc[rr] = mfma16(aw, sh.act0[4 * kk + lq][(r0 + rr) * kMP + lm], acc[rr]);
         }
       } else {
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-          const float aw = sh.w1[16 * w + lm][4 * kk + lq];
+          const float aw = sh.w1[16 * wn + lm][4 * kk + lq];
 #pragma unroll
-          for (int r = 0; r < R; ++r) acc[r] = mfma16(aw, sh.act1[4 * kk + lq][r * kMP + lm], acc[r]);
+          for (int rr = 0; rr < RG; ++rr)
+            if (r0 + rr < R) acc[rr] = mfma16(aw, sh.act1[4 * kk + lq][(r0 + rr) * kMP + lm], acc[rr]);
         }
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
+      for (int rr = 0; rr < RG; ++rr) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[r][i] += bias[K][i];
-        z[K][r] = acc[r];
+        for (int i = 0; i < 4; ++i) acc[rr][i] += bias[K][i];
+        z[K][rr] = acc[rr];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int o = 16 * w + 4 * lq + i;
+        const int o = 16 * wn + 4 * lq + i;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float sv = sinf(om * acc[r][i]);
-          if constexpr (K + 1 < DEPTH) sh.act1[o][r * kMP + lm] = sv;
-          else atop[r][i] = sv;
+        for (int rr = 0; rr < RG; ++rr) {
+          const float sv = sinf(om * acc[rr][i]);
+          if constexpr (K + 1 < DEPTH) {
+            if (r0 + rr < R) sh.act1[o][(r0 + rr) * kMP + lm] = sv;
+          } else {
+            atop[rr][i] = sv;
+          }
         }
       }
       if constexpr (K + 1 < DEPTH) __syncthreads();
@@ -793,13 +807,13 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
 
     // u_s = wout . a_s (+ bo): partial sums over the wavefront's 16 neurons, then over waves
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int rr = 0; rr < RG; ++rr) {
       float part = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part = fmaf(wout[i], atop[r][i], part);
+      for (int i = 0; i < 4; ++i) part = fmaf(wout[i], atop[rr][i], part);
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
-      if (lq == 0) sh.uw[w][r][lm] = part;
+      if (lq == 0 && r0 + rr < R) sh.uw[wn][r0 + rr][lm] = part;
     }
     __syncthreads();
     const int64_t pp = p0 + lm;
@@ -833,65 +847,72 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
       }
       seed = (float)(2.0 * (double)res * inv_n_total) * inv_eps2;  // times c_s / (-2d) or 1
     }
-    // seeds of the stencil points: c_0 = -2d / eps^2, the others 1 / eps^2
-    mf4 abar[R];
+    // seeds of the group's stencil rows: c_0 = -2d / eps^2, the others 1 / eps^2
+    mf4 abar[RG];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float sr = r == 0 ? -2.0f * (float)D * seed : seed;
+    for (int rr = 0; rr < RG; ++rr) {
+      const int r = r0 + rr;
+      const float sr = r >= R ? 0.0f : r == 0 ? -2.0f * (float)D * seed : seed;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        gWo[i] = fmaf(sr, atop[r][i], gWo[i]);
-        abar[r][i] = sr * wout[i];
+        gWo[i] = fmaf(sr, atop[rr][i], gWo[i]);
+        abar[rr][i] = sr * wout[i];
       }
     }
     auto rev_layer = [&]<int K>() {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int o = 16 * w + 4 * lq + i;
+        const int o = 16 * wn + 4 * lq + i;
         float zsum = 0.0f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float zbar = abar[r][i] * om * cosf(om * z[K][r][i]);
-          zsum += zbar;
-          sh.zb[o][r * kMP + lm] = zbar;
+        for (int rr = 0; rr < RG; ++rr) {
+          if (r0 + rr < R) {
+            const float zbar = abar[rr][i] * om * cosf(om * z[K][rr][i]);
+            zsum += zbar;
+            sh.zb[o][(r0 + rr) * kMP + lm] = zbar;
+          }
         }
         gb[K][i] += zsum;
       }
       __syncthreads();
-      // weight gradient: dL/dW_K[16w + .][j] += sum_c Zbar[o][c] V_K[j][c]
-      for (int kk = 0; kk < NC / 4; ++kk) {
-        const float az = sh.zb[16 * w + lm][4 * kk + lq];
+      // weight gradient over the group's columns: dL/dW_K[16wn + .][j] += sum_c Zbar[o][c] V_K[j][c]
+      const int nc4 = (R - r0 < RG ? R - r0 : RG) * (kMP / 4);
+      for (int kk = 0; kk < nc4; ++kk) {
+        const int c = r0 * kMP + 4 * kk + lq;
+        const float az = sh.zb[16 * wn + lm][c];
         if constexpr (K == 0) {
 #pragma unroll
-          for (int t = 0; t < NI / 16; ++t) gW0[t] = mfma16(az, sh.act0[16 * t + lm][4 * kk + lq], gW0[t]);
+          for (int t = 0; t < NI / 16; ++t) gW0[t] = mfma16(az, sh.act0[16 * t + lm][c], gW0[t]);
         } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) gW1[t] = mfma16(az, sh.act1[16 * t + lm][4 * kk + lq], gW1[t]);
+          for (int t = 0; t < 4; ++t) gW1[t] = mfma16(az, sh.act1[16 * t + lm][c], gW1[t]);
         }
       }
       constexpr int fi = K == 0 ? NI : kW;
-      mf4 vbar[R];
+      mf4 vbar[RG];
 #pragma unroll
-      for (int r = 0; r < R; ++r) vbar[r] = mf4{0.f, 0.f, 0.f, 0.f};
-      if (16 * w < fi) {
+      for (int rr = 0; rr < RG; ++rr) vbar[rr] = mf4{0.f, 0.f, 0.f, 0.f};
+      if (16 * wn < fi) {
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-          const float aw = K == 0 ? sh.w0[4 * kk + lq][16 * w + lm] : sh.w1[4 * kk + lq][16 * w + lm];
+          const float aw = K == 0 ? sh.w0[4 * kk + lq][16 * wn + lm] : sh.w1[4 * kk + lq][16 * wn + lm];
 #pragma unroll
-          for (int r = 0; r < R; ++r) vbar[r] = mfma16(aw, sh.zb[4 * kk + lq][r * kMP + lm], vbar[r]);
+          for (int rr = 0; rr < RG; ++rr)
+            if (r0 + rr < R) vbar[rr] = mfma16(aw, sh.zb[4 * kk + lq][(r0 + rr) * kMP + lm], vbar[rr]);
         }
       }
       __syncthreads();  // zb and the layer's inputs are rewritten next
       if constexpr (K > 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) abar[r] = vbar[r];
-      } else if (16 * w < fi && pp < n) {
+        for (int rr = 0; rr < RG; ++rr) abar[rr] = vbar[rr];
+      } else if (16 * wn < fi && pp < n) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = 16 * w + 4 * lq + i;
+          const int j = 16 * wn + 4 * lq + i;
           if (j < a.ain) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) up[fd_index(a, n, pp, j, r, R)] = vbar[r][i];
+            for (int rr = 0; rr < RG; ++rr)
+              if (r0 + rr < R) up[fd_index(a, n, pp, j, r0 + rr, R)] = vbar[rr][i];
           }
         }
       }
@@ -900,10 +921,11 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
     rev_layer.template operator()<0>();
   }
 
-  float* part = partial + (int64_t)blockIdx.x * (a.n_mlp + 1);
+  // this row group's partial MLP gradient (and, for group 0, the sum of r^2)
+  float* part = partial + ((int64_t)blockIdx.x * kFdGroups + rg) * (a.n_mlp + 1);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int o = 16 * w + 4 * lq + i;
+    const int o = 16 * wn + 4 * lq + i;
     if (o < H) {
 #pragma unroll
       for (int t = 0; t < NI / 16; ++t) {
@@ -929,19 +951,19 @@ __global__ __launch_bounds__(kW * kMWaves) void siren_fd_mfma_kernel(
     for (int k = 0; k <= DEPTH; ++k)
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) v[k] += __shfl_xor(v[k], off, 64);
-    const int o = 16 * w + 4 * lq + i;
+    const int o = 16 * wn + 4 * lq + i;
     if (lm == 0 && o < H) {
 #pragma unroll
       for (int k = 0; k < DEPTH; ++k) part[a.boff[k] + o] = v[k];
       part[a.woff[DEPTH] + o] = v[DEPTH];
     }
   }
-  if (w == 0) {
+  if (wn == 0) {
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) sq += __shfl_xor(sq, off, 64);
     if (lane == 0) {
       part[a.boff[DEPTH]] = 0.0f;  // the output bias cancels in the stencil
-      part[a.n_mlp] = sq;
+      part[a.n_mlp] = rg == 0 ? sq : 0.0f;
     }
   }
 }
@@ -1087,8 +1109,8 @@ hipError_t launch_fd_siren(const MlpArgs& a, int64_t n, double inv_n, float inv_
                            float* partial, int& rows, hipStream_t s) {
   int blocks = (int)((n + kMP - 1) / kMP);
   if (blocks > kFdBlocks) blocks = kFdBlocks;
-  rows = blocks;
-  hipLaunchKernelGGL((siren_fd_mfma_kernel<D, DEPTH, NI>), dim3(blocks), dim3(kW * kMWaves), 0, s, a, n, inv_n,
+  rows = blocks * kFdGroups;  // one partial row per row group
+  hipLaunchKernelGGL((siren_fd_mfma_kernel<D, DEPTH, NI>), dim3(blocks), dim3(kW * kFdWaves), 0, s, a, n, inv_n,
                      inv_eps2, x, enc, mlp, up, u_stencil, residual, partial);
   return hipGetLastError();
 }
@@ -1133,8 +1155,8 @@ FdWorkspaceLayout fd_workspace_layout(const Grid& g, int d, int F, int64_t n, in
   w.xs = take(sizeof(float) * (size_t)cs * d);
   w.enc = take(dlinear_forward_workspace_bytes(g, d, F, cs));  // level-major [L][c (2d+1)][F]
   w.up = take(dlinear_forward_workspace_bytes(g, d, F, cs));
-  w.partial = take(sizeof(float) * (size_t)kFdBlocks * (n_mlp + 1));
-  w.slices = take(sizeof(double) * (size_t)((kFdBlocks + kSliceRows - 1) / kSliceRows) * (n_mlp + 1));
+  w.partial = take(sizeof(float) * (size_t)kFdBlocks * kFdGroups * (n_mlp + 1));
+  w.slices = take(sizeof(double) * (size_t)((kFdBlocks * kFdGroups + kSliceRows - 1) / kSliceRows) * (n_mlp + 1));
   w.bins = take(binned ? binned_backward_workspace_bytes(g, d, F, false, cs) : 0);
   w.total = off;
   return w;
