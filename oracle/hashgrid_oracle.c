@@ -13,6 +13,10 @@
  *   [INGP-news]       "NVIDIA cuts NeRF training from 5 hours to 5 seconds"
  *                     (antipu.com.cn), the adaptivity / efficiency paragraphs and
  *                     the paragraph under Figure 3 (geometric progression of levels).
+ *   [DInf-Grid]       "DInf-Grid: a neural differential equation solver with
+ *                     differentiable feature grids" summary (shdxiang-github-io), sections
+ *                     可微的径向基函数插值 (normalised Gaussian RBF weights, precomputed
+ *                     k-ring neighbourhoods) and 多分辨率特征网格 (concatenated levels).
  *   [HNGP]            "Hermite-NGP: Gradient-Augmented Hash Encoding for Learning
  *                     PDEs" reading notes (m0rtzz.github.io), section 方法详解,
  *                     key design 1 (reconstruction equation, 1D basis), key
@@ -36,6 +40,11 @@
  *   - near-corner basis is the reflection of the far-corner basis printed on
  *     the Hermite-NGP page;
  *   - colliding rows receive the sum of their contributions;
+ *   - Gaussian RBF (kind 2): distances in units of the level's grid spacing
+ *     (r = |p - v| with p = fl32(x N_l)); the k-ring neighbourhood of a point is the box
+ *     of (2k)^d vertices base_i - k + 1 .. base_i + k around its cell, clipped to the
+ *     grid; weights phi(r) / sum phi over that box, phi(r) = exp(-(eps r)^2); storage as
+ *     for d-linear (one table per level, dense 1:1 where the vertices fit);
  *   - coarse-to-fine activation: L_active counts the active levels (levels
  *     l < L_active); an inactive level contributes zeros to the encoding and
  *     receives no gradient, and the encoding keeps its full L*F width.
@@ -60,12 +69,16 @@ typedef struct {
   int32_t d;          /* spatial dimension, 1..3 */
   int32_t L;          /* number of levels */
   int32_t F;          /* features per slot */
-  int32_t kind;       /* 0 = d-linear, 1 = cubic Hermite */
+  int32_t kind;       /* 0 = d-linear, 1 = cubic Hermite, 2 = Gaussian RBF */
   int32_t d2_mode;    /* Hermite second-order output: 1 = Laplacian [n,L*F], 2 = diagonal [n,d,L*F] */
   uint32_t T[ORC_MAX_D + 1]; /* rows of table k (derivative order k); d-linear uses T[0] */
   int32_t N[ORC_MAX_LEVELS]; /* level resolutions */
   int32_t active;     /* levels l < active are active [HNGP key design 3]; 0 = all L */
+  int32_t rings;      /* Gaussian RBF: neighbourhood rings k (1..4) */
+  double eps;         /* Gaussian RBF: shape parameter epsilon (> 0) */
 } orc_cfg;
+
+#define ORC_MAX_RBF_VERTS 512 /* (2k)^d for k <= 4, d <= 3 */
 
 /* Number of active levels of a configuration (0 in the field means all of them). */
 static int active_levels(const orc_cfg* c) {
@@ -281,6 +294,66 @@ static void corner_weights(const orc_cfg* c, int l, int cc, int alpha, const dou
   }
 }
 
+/* Gaussian-RBF weights of one point at one level [DInf-Grid, 可微的径向基函数插值]: for
+ * every vertex v of the point's k-ring box (clipped to the grid) its row, and the weight
+ * that multiplies its coefficient in gamma (w), in d gamma / dx_i (w1[.][i]) and in
+ * d^2 gamma / dx_i^2 (w2[.][i]):
+ *     phi_v = exp(-eps^2 |p - v|^2),  S = sum_v phi_v,  w_v = phi_v / S,
+ * differentiated by the quotient rule, with d/dx_i = N_l d/dp_i:
+ *     dphi/dp_i = -2 eps^2 (p_i - v_i) phi,  d^2phi/dp_i^2 = (4 eps^4 (p_i - v_i)^2 - 2 eps^2) phi,
+ *     dw = (dphi - w dS) / S,  d^2w = (d^2phi - 2 dw dS - w d^2S) / S.
+ * Returns the number of vertices. */
+static int rbf_weights(const orc_cfg* c, int l, const float* x, int64_t* rows, double* w,
+                       double (*w1)[ORC_MAX_D], double (*w2)[ORC_MAX_D]) {
+  const int d = c->d, k = c->rings;
+  const double e2 = c->eps * c->eps, N = (double)c->N[l];
+  uint32_t base[ORC_MAX_D];
+  double t[ORC_MAX_D];
+  locate(c, l, x, base, t);
+  double p[ORC_MAX_D];
+  for (int i = 0; i < d; ++i) p[i] = (double)base[i] + t[i]; /* = fl32(x N), exactly */
+  double phi[ORC_MAX_RBF_VERTS], d1[ORC_MAX_RBF_VERTS][ORC_MAX_D], d2[ORC_MAX_RBF_VERTS][ORC_MAX_D];
+  int nv = 0;
+  const int side = 2 * k;
+  int total = 1;
+  for (int i = 0; i < d; ++i) total *= side;
+  for (int m = 0; m < total; ++m) {
+    int64_t v[ORC_MAX_D];
+    int inside = 1, mm = m;
+    for (int i = 0; i < d; ++i) {
+      v[i] = (int64_t)base[i] - k + 1 + mm % side;
+      mm /= side;
+      if (v[i] < 0 || v[i] > (int64_t)c->N[l]) inside = 0;
+    }
+    if (!inside) continue;
+    double r2 = 0.0;
+    for (int i = 0; i < d; ++i) r2 += (p[i] - (double)v[i]) * (p[i] - (double)v[i]);
+    phi[nv] = exp(-e2 * r2);
+    for (int i = 0; i < d; ++i) {
+      const double del = p[i] - (double)v[i];
+      d1[nv][i] = -2.0 * e2 * del * phi[nv] * N;
+      d2[nv][i] = (4.0 * e2 * e2 * del * del - 2.0 * e2) * phi[nv] * N * N;
+    }
+    uint32_t vu[ORC_MAX_D];
+    for (int i = 0; i < d; ++i) vu[i] = (uint32_t)v[i];
+    rows[nv] = vertex_row(c, 0, l, vu);
+    ++nv;
+  }
+  double S = 0.0, S1[ORC_MAX_D] = {0}, S2[ORC_MAX_D] = {0};
+  for (int q = 0; q < nv; ++q) {
+    S += phi[q];
+    for (int i = 0; i < d; ++i) { S1[i] += d1[q][i]; S2[i] += d2[q][i]; }
+  }
+  for (int q = 0; q < nv; ++q) {
+    w[q] = phi[q] / S;
+    for (int i = 0; i < d; ++i) {
+      w1[q][i] = (d1[q][i] - w[q] * S1[i]) / S;
+      w2[q][i] = (d2[q][i] - 2.0 * w1[q][i] * S1[i] - w[q] * S2[i]) / S;
+    }
+  }
+  return nv;
+}
+
 /* Forward encoding [INGP-explainer steps 1-4; HNGP key design 1].
  * gamma[n][L*F]; Hermite only: dgamma[n][d][L*F], d2gamma per d2_mode
  * (Laplacian [n][L*F] or diagonal [n][d][L*F]).  Any output may be NULL.
@@ -301,8 +374,24 @@ void orc_forward(const orc_cfg* c, int64_t n, const float* x, const double* para
       double t[ORC_MAX_D];
       locate(c, l, x + p * d, base, t);
       double g0[ORC_MAX_F] = {0}, g1[ORC_MAX_F][ORC_MAX_D] = {{0}}, g2[ORC_MAX_F][ORC_MAX_D] = {{0}};
+      if (c->kind == 2 && l < active_levels(c)) {
+        /* Gaussian RBF: sum over the k-ring box [DInf-Grid] */
+        int64_t rows[ORC_MAX_RBF_VERTS];
+        double w[ORC_MAX_RBF_VERTS], w1[ORC_MAX_RBF_VERTS][ORC_MAX_D], w2[ORC_MAX_RBF_VERTS][ORC_MAX_D];
+        const int nv = rbf_weights(c, l, x + p * d, rows, w, w1, w2);
+        for (int q = 0; q < nv; ++q) {
+          const double* th = params + offs[l] + rows[q] * wid[l];
+          for (int f = 0; f < c->F; ++f) {
+            g0[f] += w[q] * th[f];
+            for (int i = 0; i < d; ++i) {
+              g1[f][i] += w1[q][i] * th[f];
+              g2[f][i] += w2[q][i] * th[f];
+            }
+          }
+        }
+      }
       /* an inactive level keeps its columns at zero [HNGP key design 3] */
-      const int ncorner = l < active_levels(c) ? nc : 0;
+      const int ncorner = (c->kind != 2 && l < active_levels(c)) ? nc : 0;
       for (int cc = 0; cc < ncorner; ++cc) {
         uint32_t v[ORC_MAX_D];
         for (int i = 0; i < d; ++i) v[i] = base[i] + (uint32_t)((cc >> i) & 1);
@@ -326,7 +415,7 @@ void orc_forward(const orc_cfg* c, int64_t n, const float* x, const double* para
       for (int f = 0; f < c->F; ++f) {
         const int col = l * c->F + f;
         if (gamma) gamma[p * LF + col] = g0[f];
-        if (c->kind == 1) {
+        if (c->kind != 0) {
           if (dgamma) for (int i = 0; i < d; ++i) dgamma[(p * d + i) * LF + col] = g1[f][i];
           if (d2gamma) {
             if (c->d2_mode == 2) {
@@ -363,6 +452,29 @@ void orc_backward_f64(const orc_cfg* c, int64_t n, const float* x, const double*
   for (int task = 0; task < ntab * c->L; ++task) {
     const int k = task / c->L, l = task % c->L;
     if (l >= active_levels(c)) continue; /* inactive level: no gradient [HNGP key design 3] */
+    if (c->kind == 2) {
+      /* Gaussian RBF: each box vertex receives its weights times the upstream */
+      for (int64_t p = 0; p < n; ++p) {
+        int64_t rows[ORC_MAX_RBF_VERTS];
+        double w[ORC_MAX_RBF_VERTS], w1[ORC_MAX_RBF_VERTS][ORC_MAX_D], w2[ORC_MAX_RBF_VERTS][ORC_MAX_D];
+        const int nv = rbf_weights(c, l, x + p * d, rows, w, w1, w2);
+        for (int q = 0; q < nv; ++q)
+          for (int f = 0; f < c->F; ++f) {
+            const int col = l * c->F + f;
+            double acc = 0.0;
+            if (g_gamma) acc += w[q] * g_gamma[p * LF + col];
+            for (int i = 0; i < d; ++i) {
+              if (g_dgamma) acc += w1[q][i] * g_dgamma[(p * d + i) * LF + col];
+              if (g_d2) {
+                double up = c->d2_mode == 2 ? g_d2[(p * d + i) * LF + col] : g_d2[p * LF + col];
+                acc += w2[q][i] * up;
+              }
+            }
+            grad[offs[l] + rows[q] * wid[l] + f] += acc;
+          }
+      }
+      continue;
+    }
     for (int64_t p = 0; p < n; ++p) {
       uint32_t base[ORC_MAX_D];
       double t[ORC_MAX_D];

@@ -8,7 +8,8 @@ Every function takes a plain configuration ``spec`` (a dict) and host NumPy arra
 returns fp64 NumPy arrays.  The spec keys are:
 
     d, L, F           dimension (1..3), number of levels, features per slot
-    kind              "dlinear" (Instant-NGP d-linear) or "hermite" (Hermite-NGP)
+    kind              "dlinear" (Instant-NGP d-linear), "hermite" (Hermite-NGP) or "rbf"
+                      (DInf-Grid Gaussian RBF; rbf_eps = epsilon, rbf_rings = k)
     T                 list of table sizes, one per derivative order (d-linear: [T])
     n_min, n_max      coarsest / finest resolution (geometric progression)
     growth            optional per-level growth factor b (overrides n_max)
@@ -51,7 +52,7 @@ class _Cfg(ctypes.Structure):
         ("d", ctypes.c_int32), ("L", ctypes.c_int32), ("F", ctypes.c_int32),
         ("kind", ctypes.c_int32), ("d2_mode", ctypes.c_int32),
         ("T", ctypes.c_uint32 * (MAX_D + 1)), ("N", ctypes.c_int32 * MAX_LEVELS),
-        ("active", ctypes.c_int32),
+        ("active", ctypes.c_int32), ("rings", ctypes.c_int32), ("eps", ctypes.c_double),
     ]
 
 
@@ -120,7 +121,11 @@ def make_cfg(spec: dict) -> _Cfg:
     c.d, c.L, c.F = spec["d"], spec["L"], spec["F"]
     if not (1 <= c.d <= MAX_D and 1 <= c.L <= MAX_LEVELS and 1 <= c.F <= 8):
         raise ValueError("unsupported shape")
-    c.kind = 1 if spec["kind"] == "hermite" else 0
+    c.kind = {"dlinear": 0, "hermite": 1, "rbf": 2}[spec["kind"]]
+    if c.kind == 2:
+        c.rings, c.eps = int(spec["rbf_rings"]), float(spec["rbf_eps"])
+        if not (1 <= c.rings <= 4 and c.eps > 0):
+            raise ValueError("rbf_rings must be 1..4 and rbf_eps > 0")
     c.d2_mode = 2 if spec.get("d2_mode", "laplacian") == "diag" else 1
     T = list(spec["T"])
     if len(T) == 1:
@@ -175,15 +180,15 @@ def _f64(a):
 
 
 def forward(spec: dict, x: np.ndarray, params: np.ndarray):
-    """gamma [n, L*F]; Hermite adds dgamma [n, d, L*F] and d2gamma (Laplacian [n, L*F] or
-    diagonal [n, d, L*F]).  Returns (gamma, dgamma, d2gamma), None where not defined.
-    ``params`` may be fp32 (widened exactly) or fp64."""
+    """gamma [n, L*F]; Hermite and RBF add dgamma [n, d, L*F] and d2gamma (Laplacian
+    [n, L*F] or diagonal [n, d, L*F]).  Returns (gamma, dgamma, d2gamma), None where not
+    defined.  ``params`` may be fp32 (widened exactly) or fp64."""
     c = make_cfg(spec)
     x, params = _f32(x), _f64(params)
     n, d, LF = x.shape[0], spec["d"], spec["L"] * spec["F"]
     gamma = np.zeros((n, LF))
     dg = d2 = None
-    if spec["kind"] == "hermite":
+    if spec["kind"] in ("hermite", "rbf"):
         dg = np.zeros((n, d, LF))
         d2 = np.zeros((n, d, LF)) if c.d2_mode == 2 else np.zeros((n, LF))
     _load().orc_forward(ctypes.byref(c), n, _ptr(x), _ptr(params), _ptr(gamma), _ptr(dg), _ptr(d2))
