@@ -66,7 +66,14 @@ enum {
   HASHENC_EUNSUPPORTED = -5  /* valid request the library does not implement */
 };
 
-typedef enum { HASHENC_DLINEAR = 0, HASHENC_HERMITE = 1 } hashenc_kind;
+/* HASHENC_RBF: the DInf-Grid Gaussian-RBF interpolant (DInf-Grid summary, sections
+ * 可微的径向基函数插值 and 多分辨率特征网格): per level, the features of the vertices of the
+ * point's k-ring neighbourhood -- the (2k)^d vertex box around its cell, clipped to the grid
+ * -- weighted by phi(r) / sum phi, phi(r) = exp(-(eps r)^2), r the distance in units of the
+ * level's grid spacing; one table of F floats per vertex per level (dense 1:1 where the
+ * vertices fit table_size[0], else hashed as d-linear); outputs gamma, grad gamma and the
+ * second derivatives like the Hermite kind. */
+typedef enum { HASHENC_DLINEAR = 0, HASHENC_HERMITE = 1, HASHENC_RBF = 2 } hashenc_kind;
 typedef enum { HASHENC_D2_LAPLACIAN = 1, HASHENC_D2_DIAG = 2 } hashenc_d2_mode;
 
 #define HASHENC_MAX_LEVELS 32
@@ -76,7 +83,7 @@ typedef struct hashenc_config {
   int32_t n_levels;      /* L: 1..32 */
   int32_t n_features;    /* F: 1, 2, 4 or 8 features per derivative slot */
   int32_t kind;          /* hashenc_kind */
-  int32_t d2_mode;       /* Hermite only: hashenc_d2_mode of the second-order output */
+  int32_t d2_mode;       /* Hermite and RBF: hashenc_d2_mode of the second-order output */
   int32_t n_min;         /* N_min >= 1: coarsest resolution */
   int32_t n_max;         /* N_max >= N_min: finest resolution (used when growth <= 0) */
   int32_t reserved;      /* must be 0 */
@@ -85,6 +92,9 @@ typedef struct hashenc_config {
                             [0]; Hermite uses [0..d].  Powers of two take a mask fast path */
   const int32_t* resolutions; /* host, optional: explicit N_l[L] (each 1..2^20); overrides
                                  n_min/n_max/growth when not NULL */
+  double rbf_eps;        /* RBF only: shape parameter eps > 0 (finite); ignored otherwise */
+  int32_t rbf_rings;     /* RBF only: neighbourhood rings k, 1..4; ignored otherwise */
+  int32_t reserved2;     /* must be 0 */
 } hashenc_config;
 
 typedef struct hashenc hashenc; /* opaque */
@@ -131,8 +141,9 @@ HASHENC_API int hashenc_param_layout(const hashenc* h, int32_t order, int32_t le
  *   x       [n, d] fp32, row-major
  *   params  [n_params] fp32 in the layout above
  *   gamma   [n, L*F]  level-major then feature (may be NULL)
- *   dgamma  Hermite only: [n, d, L*F] spatial gradient (may be NULL; must be NULL for d-linear)
- *   d2gamma Hermite only: Laplacian [n, L*F] or diagonal [n, d, L*F] per cfg.d2_mode
+ *   dgamma  Hermite and RBF: [n, d, L*F] spatial gradient (may be NULL; must be NULL for
+ *           d-linear)
+ *   d2gamma Hermite and RBF: Laplacian [n, L*F] or diagonal [n, d, L*F] per cfg.d2_mode
  *           (may be NULL; must be NULL for d-linear)
  * Outputs are overwritten.  n == 0 is a no-op. */
 HASHENC_API int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* params,
@@ -143,10 +154,11 @@ HASHENC_API int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size
 
 /* Same outputs as hashenc_forward.  With a workspace the d-linear encoding is computed
  * level by level into a level-major staging buffer [L][n][F] (every store writes whole
- * cache lines) and then rearranged into gamma [n, L*F] in one pass.  A Hermite handle whose
- * order tables all have the same size first packs the tables into the workspace (one
- * contiguous row of every order table per vertex) and reads the corners from that copy;
- * with unequal sizes it needs no workspace (size 0) and runs as hashenc_forward.
+ * cache lines) and then rearranged into gamma [n, L*F] in one pass.  A Hermite handle also
+ * stages its outputs level-major ([L][n][M][F], M = 1 + d + (d or 1)) and, when its order
+ * tables all have the same size, first packs the tables into the workspace (one contiguous
+ * row of every order table per vertex) and reads the corners from that copy.  An RBF handle
+ * needs no workspace (size 0) and runs as hashenc_forward.
  * workspace: >= hashenc_forward_workspace_size bytes, 256-byte aligned; calls sharing it
  * must not overlap.  Results are bit-identical to hashenc_forward. */
 HASHENC_API int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float* params,

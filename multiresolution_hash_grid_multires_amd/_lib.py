@@ -19,6 +19,7 @@ HASHENC_EUNSUPPORTED = -5
 
 HASHENC_DLINEAR = 0
 HASHENC_HERMITE = 1
+HASHENC_RBF = 2
 HASHENC_D2_LAPLACIAN = 1
 HASHENC_D2_DIAG = 2
 MAX_LEVELS = 32
@@ -37,6 +38,9 @@ class HashencConfig(ctypes.Structure):
         ("growth", ctypes.c_double),
         ("table_size", ctypes.c_uint32 * 4),
         ("resolutions", ctypes.POINTER(ctypes.c_int32)),
+        ("rbf_eps", ctypes.c_double),
+        ("rbf_rings", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32),
     ]
 
 

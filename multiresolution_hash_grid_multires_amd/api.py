@@ -21,12 +21,15 @@ def _spec_to_config(spec: dict) -> tuple[_lib.HashencConfig, object]:
     cfg.d = int(spec["d"])
     cfg.n_levels = int(spec["L"])
     cfg.n_features = int(spec["F"])
-    cfg.kind = _lib.HASHENC_HERMITE if spec["kind"] == "hermite" else _lib.HASHENC_DLINEAR
+    cfg.kind = {"dlinear": _lib.HASHENC_DLINEAR, "hermite": _lib.HASHENC_HERMITE, "rbf": _lib.HASHENC_RBF}[spec["kind"]]
     cfg.d2_mode = (_lib.HASHENC_D2_DIAG if spec.get("d2_mode") == "diag" else _lib.HASHENC_D2_LAPLACIAN)
     cfg.n_min = int(spec.get("n_min", 0))
     cfg.n_max = int(spec.get("n_max", 0))
     cfg.reserved = 0
     cfg.growth = float(spec.get("growth") or 0.0)
+    cfg.rbf_eps = float(spec.get("rbf_eps") or 0.0)
+    cfg.rbf_rings = int(spec.get("rbf_rings") or 0)
+    cfg.reserved2 = 0
     T = list(spec["T"])
     n_tab = cfg.d + 1 if cfg.kind == _lib.HASHENC_HERMITE else 1
     if len(T) == 1:
@@ -255,6 +258,7 @@ class HashGridEncoding:
             self.set_active_levels(spec["active_levels"])
         self.d = int(spec["d"])
         self.hermite = spec["kind"] == "hermite"
+        self.derivatives = spec["kind"] in ("hermite", "rbf")  # outputs grad gamma, d2 gamma
         self.diag = spec.get("d2_mode") == "diag"
 
     def set_active_levels(self, n_active: int) -> None:
@@ -269,7 +273,7 @@ class HashGridEncoding:
 
     def output_shapes(self, n: int) -> dict:
         s = {"gamma": (n, self.out_width)}
-        if self.hermite:
+        if self.derivatives:
             s["dgamma"] = (n, self.d, self.out_width)
             s["d2gamma"] = (n, self.d, self.out_width) if self.diag else (n, self.out_width)
         return s

@@ -81,13 +81,18 @@ int hashenc_create(const hashenc_config* cfg, hashenc** out) {
     return fail(HASHENC_EINVAL, "n_levels must be in 1..%d (got %d)", kMaxLevels, cfg->n_levels);
   if (cfg->n_features != 1 && cfg->n_features != 2 && cfg->n_features != 4 && cfg->n_features != 8)
     return fail(HASHENC_EINVAL, "n_features must be 1, 2, 4 or 8 (got %d)", cfg->n_features);
-  if (cfg->kind != HASHENC_DLINEAR && cfg->kind != HASHENC_HERMITE)
-    return fail(HASHENC_EINVAL, "kind must be HASHENC_DLINEAR or HASHENC_HERMITE (got %d)", cfg->kind);
-  if (cfg->kind == HASHENC_HERMITE && cfg->d2_mode != HASHENC_D2_LAPLACIAN &&
-      cfg->d2_mode != HASHENC_D2_DIAG)
+  if (cfg->kind != HASHENC_DLINEAR && cfg->kind != HASHENC_HERMITE && cfg->kind != HASHENC_RBF)
+    return fail(HASHENC_EINVAL, "kind must be HASHENC_DLINEAR, HASHENC_HERMITE or HASHENC_RBF (got %d)", cfg->kind);
+  if (cfg->kind != HASHENC_DLINEAR && cfg->d2_mode != HASHENC_D2_LAPLACIAN && cfg->d2_mode != HASHENC_D2_DIAG)
     return fail(HASHENC_EINVAL, "d2_mode must be HASHENC_D2_LAPLACIAN or HASHENC_D2_DIAG (got %d)",
                 cfg->d2_mode);
-  if (cfg->reserved != 0) return fail(HASHENC_EINVAL, "reserved field must be 0");
+  if (cfg->reserved != 0 || cfg->reserved2 != 0) return fail(HASHENC_EINVAL, "reserved fields must be 0");
+  if (cfg->kind == HASHENC_RBF) {
+    if (!(cfg->rbf_eps > 0.0) || !std::isfinite(cfg->rbf_eps))
+      return fail(HASHENC_EINVAL, "rbf_eps must be > 0 and finite");
+    if (cfg->rbf_rings < 1 || cfg->rbf_rings > 4)
+      return fail(HASHENC_EINVAL, "rbf_rings must be in 1..4 (got %d)", cfg->rbf_rings);
+  }
 
   hashenc* h = new (std::nothrow) hashenc();
   if (!h) return fail(HASHENC_ENOMEM, "hashenc_create: out of host memory");
@@ -95,7 +100,7 @@ int hashenc_create(const hashenc_config* cfg, hashenc** out) {
   h->L = cfg->n_levels;
   h->F = cfg->n_features;
   h->kind = cfg->kind;
-  h->d2_mode = cfg->kind == HASHENC_HERMITE ? cfg->d2_mode : 0;
+  h->d2_mode = cfg->kind != HASHENC_DLINEAR ? cfg->d2_mode : 0;
   h->n_tables = cfg->kind == HASHENC_HERMITE ? cfg->d + 1 : 1;
 
   // Level resolutions: explicit list, or the geometric progression N_min * b^l (floored,
@@ -160,6 +165,10 @@ int hashenc_create(const hashenc_config* cfg, hashenc** out) {
   std::memset(&g, 0, sizeof g);
   g.L = h->L;
   g.Lrow = h->L;
+  if (h->kind == HASHENC_RBF) {
+    g.rbf_e2 = (float)(cfg->rbf_eps * cfg->rbf_eps);
+    g.rings = cfg->rbf_rings;
+  }
   g.n_tables = h->n_tables;
   for (int l = 0; l < h->L; ++l) {
     g.N[l] = h->N[l];
@@ -234,7 +243,7 @@ int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* pa
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward: NULL handle");
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward: n = %lld out of range", (long long)n);
   if (h->kind == HASHENC_DLINEAR && (dgamma || d2gamma))
-    return fail(HASHENC_EUNSUPPORTED, "hashenc_forward: derivative outputs need the Hermite kind");
+    return fail(HASHENC_EUNSUPPORTED, "hashenc_forward: derivative outputs need the Hermite or RBF kind");
   if (n == 0 || (!gamma && !dgamma && !d2gamma)) return ok();
   if (!x || !params) return fail(HASHENC_EINVAL, "hashenc_forward: x and params must not be NULL");
   if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || !aligned16(dgamma) || !aligned16(d2gamma))
@@ -242,6 +251,8 @@ int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* pa
   hipError_t e;
   if (h->kind == HASHENC_DLINEAR)
     e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma, nullptr, stream);
+  else if (h->kind == HASHENC_RBF)
+    e = hg::launch_rbf_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, gamma, dgamma, d2gamma, stream);
   else
     e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, nullptr, nullptr, false, gamma,
                                    dgamma, d2gamma, stream);
@@ -253,8 +264,9 @@ int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL handle");
   if (!bytes) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL bytes");
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: n out of range");
-  *bytes = h->kind == HASHENC_DLINEAR ? hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n)
-                                      : hermite_forward_ws_bytes(h, n);
+  *bytes = h->kind == HASHENC_DLINEAR   ? hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n)
+           : h->kind == HASHENC_HERMITE ? hermite_forward_ws_bytes(h, n)
+                                        : 0;  // the RBF forward needs no workspace
   return ok();
 }
 
@@ -262,6 +274,7 @@ int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float*
                        float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
                        hashenc_stream_t stream) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_ws: NULL handle");
+  if (h->kind == HASHENC_RBF) return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
   if (h->kind == HASHENC_HERMITE) {
     // workspace: [packed copy of the order tables (equal table sizes) | level-major staging]
     const size_t need = hermite_forward_ws_bytes(h, n);
@@ -309,7 +322,7 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
   if (!h) return fail(HASHENC_EINVAL, "hashenc_backward: NULL handle");
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_backward: n = %lld out of range", (long long)n);
   if (h->kind == HASHENC_DLINEAR && (g_dgamma || g_d2gamma))
-    return fail(HASHENC_EUNSUPPORTED, "hashenc_backward: derivative upstream needs the Hermite kind");
+    return fail(HASHENC_EUNSUPPORTED, "hashenc_backward: derivative upstream needs the Hermite or RBF kind");
   if (n == 0 || (!g_gamma && !g_dgamma && !g_d2gamma)) return ok();
   if (!x || !grad_params) return fail(HASHENC_EINVAL, "hashenc_backward: x and grad_params must not be NULL");
   if (!aligned16(x) || !aligned16(grad_params) || !aligned16(g_gamma) || !aligned16(g_dgamma) ||
@@ -318,6 +331,9 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
   hipError_t e;
   if (h->kind == HASHENC_DLINEAR)
     e = hg::launch_dlinear_backward(h->grid, h->d, h->F, n, x, g_gamma, nullptr, grad_params, stream);
+  else if (h->kind == HASHENC_RBF)
+    e = hg::launch_rbf_backward(h->grid, h->d, h->F, h->d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, grad_params,
+                                stream);
   else
     e = hg::launch_hermite_backward(h->grid, h->d, h->F, h->d2_mode, n, x, g_gamma, g_dgamma,
                                          g_d2gamma, nullptr, grad_params, stream);
@@ -328,6 +344,7 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
 // The binned path keeps per-bin counters and staging in LDS; larger configurations take the
 // atomic path.
 static bool binned_supported(const hashenc* h) {
+  if (h->kind == HASHENC_RBF) return false;  // the RBF backward scatters with atomics
   return hg::binned_fits(h->grid, h->d, h->F, h->kind == HASHENC_HERMITE);
 }
 

@@ -36,6 +36,8 @@ struct Grid {
   uint32_t Tmask[kMaxTables];   // T - 1 when T is a power of two > 1, else 0
   uint32_t dense[kMaxTables];   // bit l set: level l of table k is a dense 1:1 grid
   int64_t off[kMaxTables][kMaxLevels];  // float offset of block (k, l) in params / grads
+  float rbf_e2;                 // Gaussian RBF: eps^2
+  int32_t rings;                // Gaussian RBF: neighbourhood rings k
 };
 
 // One rounded fp32 product, never fused into a neighbouring add: the cell a point falls in
@@ -152,6 +154,12 @@ hipError_t launch_hermite_forward(const Grid& g, int d, int F, int d2_mode, int6
 hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int64_t n,
                                    const float* x, const float* g_gamma, const float* g_dgamma,
                                    const float* g_d2gamma, const float* u_levels, float* grad, hipStream_t s);
+// Gaussian RBF (one table per level, derivative outputs as the Hermite ones; fp32-atomic backward)
+hipError_t launch_rbf_forward(const Grid& g, int d, int F, int d2_mode, int64_t n, const float* x,
+                              const float* params, float* gamma, float* dgamma, float* d2gamma, hipStream_t s);
+hipError_t launch_rbf_backward(const Grid& g, int d, int F, int d2_mode, int64_t n, const float* x,
+                               const float* g_gamma, const float* g_dgamma, const float* g_d2gamma, float* grad,
+                               hipStream_t s);
 hipError_t launch_debug_indices(const Grid& g, int d, int order, int64_t n, const float* x,
                                 int32_t* out, hipStream_t s);
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t s);

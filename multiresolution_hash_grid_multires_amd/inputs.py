@@ -82,6 +82,30 @@ WORKLOADS: dict[str, dict] = {
         "clustered_half": True,
         "outputs": ("residual", "loss"),
     },
+    # DInf-Grid Gaussian RBF, 2D: four co-located dense grids N = 64..512 (the largest 512 on
+    # a side, the 2D setting the summary recommends), eps = 1 with 3-ring neighbourhoods (36
+    # vertices per level), one stratified point per pixel of a 512 x 512 image.
+    "rbf2d_L4_N512": {
+        "id": 7,
+        "spec": {"d": 2, "L": 4, "F": 2, "kind": "rbf", "T": [1 << 19], "n_min": 64, "n_max": 512,
+                 "rbf_eps": 1.0, "rbf_rings": 3, "d2_mode": "laplacian"},
+        "n_points": 1 << 18,
+        "stratified_side": 512,
+        "tables": ("normal", 1e-2),
+        "outputs": ("gamma", "dgamma", "d2gamma"),
+    },
+    # DInf-Grid Gaussian RBF, 3D: N = 7..56 (about 56 on a side, the 3D setting the summary
+    # recommends), eps = 1, 3 rings (216 vertices per level), one stratified point per cell
+    # of a 64^3 grid, diagonal second derivatives.
+    "rbf3d_L4_N56": {
+        "id": 8,
+        "spec": {"d": 3, "L": 4, "F": 2, "kind": "rbf", "T": [1 << 18], "n_min": 7, "n_max": 56,
+                 "rbf_eps": 1.0, "rbf_rings": 3, "d2_mode": "diag"},
+        "n_points": 1 << 18,
+        "stratified_side": 64,
+        "tables": ("normal", 1e-2),
+        "outputs": ("gamma", "dgamma", "d2gamma"),
+    },
 }
 
 
@@ -112,6 +136,28 @@ def points(workload_id: int, n: int, d: int, clustered_half: bool = False) -> np
     # float32 rounding can carry a value just below 1 up to 1.0: pull it back inside.
     np.minimum(x, np.float32(1.0 - 2.0 ** -24), out=x)
     return x
+
+
+def stratified_points(workload_id: int, side: int, d: int) -> np.ndarray:
+    """One point uniform in each of the side^d cells of [0,1)^d (stratified sampling), cells
+    in row-major order with the first axis fastest, float32 [side^d, d]."""
+    r = rng(workload_id, STREAM_POINTS)
+    idx = np.indices((side,) * d).reshape(d, -1)[::-1].T  # first axis fastest
+    x = (idx + r.random(idx.shape)) / side
+    x = x.astype(np.float32)
+    np.minimum(x, np.float32(1.0 - 2.0 ** -24), out=x)
+    return x
+
+
+def workload_points(name: str, n: int | None = None) -> np.ndarray:
+    """The points of a workload (its first n, when given)."""
+    W = WORKLOADS[name]
+    d = W["spec"]["d"]
+    if "stratified_side" in W:
+        x = stratified_points(W["id"], W["stratified_side"], d)
+    else:
+        x = points(W["id"], W["n_points"], d, W.get("clustered_half", False))
+    return x if n is None else x[:n]
 
 
 def tables(workload_id: int, n_params: int, dist: tuple) -> np.ndarray:
