@@ -49,8 +49,11 @@ def algorithmic_bytes_per_point(spec: dict) -> dict:
     active levels."""
     d, L, F = spec["d"], spec["L"], spec["F"]
     A = int(spec.get("active_levels") or L)
-    comps = 1 + d + (d if spec.get("d2_mode") == "diag" else 1) if spec["kind"] == "hermite" else 1
-    corners = (1 << d) * (1 << d) if spec["kind"] == "hermite" else (1 << d)
+    comps = 1 + d + (d if spec.get("d2_mode") == "diag" else 1) if spec["kind"] != "dlinear" else 1
+    # table values referenced per point and level: the 2^d corners (Hermite: times the 2^d
+    # coefficients of each); RBF: the (2k)^d vertices of the k-ring box
+    corners = {"dlinear": 1 << d, "hermite": (1 << d) * (1 << d),
+               "rbf": (2 * int(spec.get("rbf_rings") or 0)) ** d}[spec["kind"]]
     x_bytes = 4 * d
     return {"forward": x_bytes + 4 * L * F * comps + 4 * A * corners * F,
             "backward": x_bytes + 4 * A * F * comps + 8 * A * corners * F}
@@ -256,7 +259,7 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     enc = api.HashGridEncoding(spec)
-    x_h = I.points(W["id"], n, spec["d"])
+    x_h = I.workload_points(args.workload) if "stratified_side" in W else I.points(W["id"], n, spec["d"])
     params_h = I.tables(W["id"], enc.n_params, W["tables"])
     shapes = enc.output_shapes(n)
     ups_h = I.upstream(W["id"], list(shapes.values()))

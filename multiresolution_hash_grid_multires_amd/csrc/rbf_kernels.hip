@@ -14,8 +14,9 @@
 // weighted sums of the vertex features accumulated along x inside a row, then over y, then
 // over z.  The x-runs of a box row are contiguous rows of a dense level.  The quotient rule
 // turns the sums into gamma, d gamma/dx_i and d^2 gamma/dx_i^2.  The backward distributes the
-// upstream through the same factors (no vertex-dependent division) and scatter-adds with
-// fp32 atomics.
+// upstream through the same factors (no vertex-dependent division), pre-aggregates a
+// workgroup's contributions in LDS where its points' neighbourhoods fit, and adds them to the
+// table with fp32 atomics.
 #include "hashenc_internal.h"
 #include "vec_io.h"
 
@@ -243,6 +244,14 @@ __global__ __launch_bounds__(kBlock) void rbf_forward_kernel(const Grid g, int64
 //   a = G0/S - sum_i (dS_i G1_i + d2S_i G2_i)/S^2 + 2 sum_i dS_i^2 G2_i / S^3,
 //   b_i = G1_i/S - 2 dS_i G2_i / S^2,   c_i = G2_i / S,
 // the transpose of the forward's quotient rule, with the per-axis factors of phi.
+//
+// A workgroup owns kBlock consecutive points at one level.  Neighbouring points share most
+// of their box vertices, so the workgroup first takes the bounding box of its points' boxes;
+// when that fits kRbfLdsFloats it accumulates there with LDS atomics and then adds every
+// touched vertex to the table once (one global atomic per vertex feature instead of one per
+// point, vertex and feature); otherwise every contribution goes straight to the table.
+constexpr int kRbfLdsFloats = 12288;  // 48 KB
+
 template <int D, int F>
 __global__ __launch_bounds__(kBlock) void rbf_backward_kernel(const Grid g, int64_t n, int32_t n_tiles, int d2_mode,
                                                               const float* __restrict__ x,
@@ -250,99 +259,171 @@ __global__ __launch_bounds__(kBlock) void rbf_backward_kernel(const Grid g, int6
                                                               const float* __restrict__ g_dgamma,
                                                               const float* __restrict__ g_d2gamma,
                                                               float* __restrict__ grad) {
+  __shared__ float acc[kRbfLdsFloats];
+  __shared__ int32_t bounds[2 * D][kBlock / 64];
   const int l = blockIdx.x / n_tiles;
   const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
-  if (p >= n) return;
-  float xp[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
-  RbfSetup<D> s;
-  rbf_setup<D>(g, l, xp, s);
-  const int64_t LF = (int64_t)g.Lrow * F;
-  const int64_t col = (int64_t)l * F;
-  float G0[F], G1[D][F], G2[D][F];
-#pragma unroll
-  for (int f = 0; f < F; ++f) {
-    G0[f] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < D; ++i) G1[i][f] = G2[i][f] = 0.0f;
-  }
-  if (g_gamma) load_vec<F>(g_gamma + p * LF + col, G0);
-  if (g_dgamma) {
-#pragma unroll
-    for (int i = 0; i < D; ++i) load_vec<F>(g_dgamma + (p * D + i) * LF + col, G1[i]);
-  }
-  if (g_d2gamma) {
-    if (d2_mode == HASHENC_D2_DIAG) {
-#pragma unroll
-      for (int i = 0; i < D; ++i) load_vec<F>(g_d2gamma + (p * D + i) * LF + col, G2[i]);
-    } else {
-      load_vec<F>(g_d2gamma + p * LF + col, G2[0]);
-#pragma unroll
-      for (int i = 1; i < D; ++i)
-#pragma unroll
-        for (int f = 0; f < F; ++f) G2[i][f] = G2[0][f];
-    }
-  }
-  const float inv = 1.0f / s.S;
-  float ca[F], cb[D][F], cc[D][F];
-#pragma unroll
-  for (int f = 0; f < F; ++f) {
-    float a = G0[f] * inv;
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      a -= (s.dS[i] * G1[i][f] + s.d2S[i] * G2[i][f]) * inv * inv;
-      a += 2.0f * s.dS[i] * s.dS[i] * G2[i][f] * inv * inv * inv;
-      cb[i][f] = G1[i][f] * inv - 2.0f * s.dS[i] * G2[i][f] * inv * inv;
-      cc[i][f] = G2[i][f] * inv;
-    }
-    ca[f] = a;
-  }
+  const bool on = p < n;
   const int k = g.rings, side = 2 * k;
   const int32_t N = g.N[l];
-  const float e2 = g.rbf_e2, Nf = g.Nf[l];
+  float xp[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) xp[i] = on ? x[p * D + i] : 0.0f;
+  RbfSetup<D> s;
+  rbf_setup<D>(g, l, xp, s);
+
+  // bounding box of the workgroup's k-ring boxes (clipped to the grid)
+  int32_t lo[D], ext[D];
+  {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      int32_t mn = on ? (int32_t)s.base[i] : INT32_MAX, mx = on ? (int32_t)s.base[i] : INT32_MIN;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        mn = min(mn, __shfl_xor(mn, off, 64));
+        mx = max(mx, __shfl_xor(mx, off, 64));
+      }
+      if (lane == 0) { bounds[2 * i][wv] = mn; bounds[2 * i + 1][wv] = mx; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      int32_t mn = bounds[2 * i][0], mx = bounds[2 * i + 1][0];
+      for (int w = 1; w < kBlock / 64; ++w) {
+        mn = min(mn, bounds[2 * i][w]);
+        mx = max(mx, bounds[2 * i + 1][w]);
+      }
+      lo[i] = max(mn - k + 1, 0);
+      ext[i] = min(mx + k, N) - lo[i] + 1;
+    }
+  }
+  int64_t vol = F;
+#pragma unroll
+  for (int i = 0; i < D; ++i) vol *= ext[i];
+  const bool use_lds = vol <= kRbfLdsFloats;  // uniform over the workgroup
+  if (use_lds) {
+    for (int i = threadIdx.x; i < (int)vol; i += kBlock) acc[i] = 0.0f;
+    __syncthreads();
+  }
+
   const bool dense = (g.dense[0] >> l) & 1u;
   float* tab = grad + g.off[0][l];
-  AxisG gx[kMaxSide];
+  if (on) {
+    const int64_t LF = (int64_t)g.Lrow * F;
+    const int64_t col = (int64_t)l * F;
+    float G0[F], G1[D][F], G2[D][F];
 #pragma unroll
-  for (int m = 0; m < kMaxSide; ++m)
-    gx[m] = m < side ? rbf_axis(s.t[0], (int32_t)s.base[0], k, m, N, e2, Nf) : AxisG{0.0f, 0.0f, 0.0f};
-  const int zs = D > 2 ? side : 1;
-  for (int mz = 0; mz < zs; ++mz) {
-    AxisG gz{1.0f, 0.0f, 0.0f};
-    uint32_t vz = 0;
-    if constexpr (D > 2) {
-      gz = rbf_axis(s.t[2], (int32_t)s.base[2], k, mz, N, e2, Nf);
-      if (gz.g == 0.0f) continue;
-      vz = s.base[2] - k + 1 + mz;
+    for (int f = 0; f < F; ++f) {
+      G0[f] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) G1[i][f] = G2[i][f] = 0.0f;
     }
-    for (int my = 0; my < side; ++my) {
-      const AxisG gy = rbf_axis(s.t[1], (int32_t)s.base[1], k, my, N, e2, Nf);
-      if (gy.g == 0.0f) continue;
-      const uint32_t vy = s.base[1] - k + 1 + my;
-      const uint32_t key = rbf_key(vy, vz, N, dense);
-      // this row's part, independent of x: P multiplies (gx a + g1x b_x + g2x c_x), Q
-      // multiplies gx
-      const float P = gy.g * gz.g;
-      float Q[F];
+    if (g_gamma) load_vec<F>(g_gamma + p * LF + col, G0);
+    if (g_dgamma) {
 #pragma unroll
-      for (int f = 0; f < F; ++f) {
-        float q = (gy.g1 * cb[1][f] + gy.g2 * cc[1][f]) * gz.g;
-        if constexpr (D > 2) q += gy.g * (gz.g1 * cb[2][f] + gz.g2 * cc[2][f]);
-        Q[f] = q;
+      for (int i = 0; i < D; ++i) load_vec<F>(g_dgamma + (p * D + i) * LF + col, G1[i]);
+    }
+    if (g_d2gamma) {
+      if (d2_mode == HASHENC_D2_DIAG) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) load_vec<F>(g_d2gamma + (p * D + i) * LF + col, G2[i]);
+      } else {
+        load_vec<F>(g_d2gamma + p * LF + col, G2[0]);
+#pragma unroll
+        for (int i = 1; i < D; ++i)
+#pragma unroll
+          for (int f = 0; f < F; ++f) G2[i][f] = G2[0][f];
       }
+    }
+    const float inv = 1.0f / s.S;
+    float ca[F], cb[D][F], cc[D][F];
 #pragma unroll
-      for (int m = 0; m < kMaxSide; ++m) {
-        if (m < side && gx[m].g != 0.0f) {
-          const uint32_t row = rbf_row(s.base[0] - k + 1 + m, key, dense, g.T[0], g.Tmask[0]);
+    for (int f = 0; f < F; ++f) {
+      float a = G0[f] * inv;
 #pragma unroll
-          for (int f = 0; f < F; ++f) {
-            const float c = P * (gx[m].g * ca[f] + gx[m].g1 * cb[0][f] + gx[m].g2 * cc[0][f]) + gx[m].g * Q[f];
-            atomic_add_f32(tab + (size_t)row * F + f, c);
+      for (int i = 0; i < D; ++i) {
+        a -= (s.dS[i] * G1[i][f] + s.d2S[i] * G2[i][f]) * inv * inv;
+        a += 2.0f * s.dS[i] * s.dS[i] * G2[i][f] * inv * inv * inv;
+        cb[i][f] = G1[i][f] * inv - 2.0f * s.dS[i] * G2[i][f] * inv * inv;
+        cc[i][f] = G2[i][f] * inv;
+      }
+      ca[f] = a;
+    }
+    const float e2 = g.rbf_e2, Nf = g.Nf[l];
+    AxisG gx[kMaxSide];
+#pragma unroll
+    for (int m = 0; m < kMaxSide; ++m)
+      gx[m] = m < side ? rbf_axis(s.t[0], (int32_t)s.base[0], k, m, N, e2, Nf) : AxisG{0.0f, 0.0f, 0.0f};
+    const int zs = D > 2 ? side : 1;
+    for (int mz = 0; mz < zs; ++mz) {
+      AxisG gz{1.0f, 0.0f, 0.0f};
+      uint32_t vz = 0;
+      if constexpr (D > 2) {
+        gz = rbf_axis(s.t[2], (int32_t)s.base[2], k, mz, N, e2, Nf);
+        if (gz.g == 0.0f) continue;
+        vz = s.base[2] - k + 1 + mz;
+      }
+      for (int my = 0; my < side; ++my) {
+        const AxisG gy = rbf_axis(s.t[1], (int32_t)s.base[1], k, my, N, e2, Nf);
+        if (gy.g == 0.0f) continue;
+        const uint32_t vy = s.base[1] - k + 1 + my;
+        // this row's part, independent of x: P multiplies (gx a + g1x b_x + g2x c_x), Q
+        // multiplies gx
+        const float P = gy.g * gz.g;
+        float Q[F];
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          float q = (gy.g1 * cb[1][f] + gy.g2 * cc[1][f]) * gz.g;
+          if constexpr (D > 2) q += gy.g * (gz.g1 * cb[2][f] + gz.g2 * cc[2][f]);
+          Q[f] = q;
+        }
+        if (use_lds) {
+          int32_t lrow = (int32_t)vy - lo[1];
+          if constexpr (D > 2) lrow += ext[1] * ((int32_t)vz - lo[2]);
+          const int32_t lbase = lrow * ext[0] + ((int32_t)s.base[0] - k + 1 - lo[0]);
+#pragma unroll
+          for (int m = 0; m < kMaxSide; ++m) {
+            if (m < side && gx[m].g != 0.0f) {
+#pragma unroll
+              for (int f = 0; f < F; ++f) {
+                const float c = P * (gx[m].g * ca[f] + gx[m].g1 * cb[0][f] + gx[m].g2 * cc[0][f]) + gx[m].g * Q[f];
+                atomicAdd(&acc[(lbase + m) * F + f], c);
+              }
+            }
+          }
+        } else {
+          const uint32_t key = rbf_key(vy, vz, N, dense);
+#pragma unroll
+          for (int m = 0; m < kMaxSide; ++m) {
+            if (m < side && gx[m].g != 0.0f) {
+              const uint32_t row = rbf_row(s.base[0] - k + 1 + m, key, dense, g.T[0], g.Tmask[0]);
+#pragma unroll
+              for (int f = 0; f < F; ++f) {
+                const float c = P * (gx[m].g * ca[f] + gx[m].g1 * cb[0][f] + gx[m].g2 * cc[0][f]) + gx[m].g * Q[f];
+                atomic_add_f32(tab + (size_t)row * F + f, c);
+              }
+            }
           }
         }
       }
     }
+  }
+  if (!use_lds) return;
+  __syncthreads();
+  // one global add per touched vertex feature, consecutive threads on consecutive features
+  for (int i = threadIdx.x; i < (int)vol; i += kBlock) {
+    const float v = acc[i];
+    if (v == 0.0f) continue;
+    const int f = i % F;
+    int32_t r = i / F;
+    const uint32_t vx = (uint32_t)(lo[0] + r % ext[0]);
+    r /= ext[0];
+    uint32_t vy = 0, vz = 0;
+    if constexpr (D > 1) { vy = (uint32_t)(lo[1] + r % ext[1]); r /= ext[1]; }
+    if constexpr (D > 2) vz = (uint32_t)(lo[2] + r);
+    const uint32_t row = rbf_row(vx, rbf_key(vy, vz, N, dense), dense, g.T[0], g.Tmask[0]);
+    atomic_add_f32(tab + (size_t)row * F + f, v);
   }
 }
 
