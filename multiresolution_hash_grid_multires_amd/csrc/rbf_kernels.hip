@@ -355,16 +355,23 @@ __global__ __launch_bounds__(kBlock) void rbf_backward_kernel(const Grid g, int6
 #pragma unroll
     for (int m = 0; m < kMaxSide; ++m)
       gx[m] = m < side ? rbf_axis(s.t[0], (int32_t)s.base[0], k, m, N, e2, Nf) : AxisG{0.0f, 0.0f, 0.0f};
+    // lanes walk the box rows in rotated orders (start row = lane % 2k along y and
+    // lane / 2k % 2k along z): lanes whose points share a cell then add into different
+    // rows at the same instruction instead of serialising on one LDS address
+    const int lane = threadIdx.x & 63;
+    const int rot_y = lane % side, rot_z = (lane / side) % side;
     const int zs = D > 2 ? side : 1;
-    for (int mz = 0; mz < zs; ++mz) {
+    for (int mz0 = 0; mz0 < zs; ++mz0) {
       AxisG gz{1.0f, 0.0f, 0.0f};
       uint32_t vz = 0;
       if constexpr (D > 2) {
+        const int mz = (mz0 + rot_z) % side;
         gz = rbf_axis(s.t[2], (int32_t)s.base[2], k, mz, N, e2, Nf);
         if (gz.g == 0.0f) continue;
         vz = s.base[2] - k + 1 + mz;
       }
-      for (int my = 0; my < side; ++my) {
+      for (int my0 = 0; my0 < side; ++my0) {
+        const int my = (my0 + rot_y) % side;
         const AxisG gy = rbf_axis(s.t[1], (int32_t)s.base[1], k, my, N, e2, Nf);
         if (gy.g == 0.0f) continue;
         const uint32_t vy = s.base[1] - k + 1 + my;
