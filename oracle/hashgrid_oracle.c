@@ -30,7 +30,8 @@
  *   - level resolution N_l = floor(N_min * b^l + 1e-6), b = (N_max/N_min)^(1/(L-1))
  *     unless b is given;
  *   - hash = XOR over axes of (uint32(v_i) * pi_i mod 2^32), then mod T, with
- *     pi = (1, 2654435761, 805459861);
+ *     pi = (1, 2654435761, 805459861) and, for the 4D space-time Hermite grid, the
+ *     fourth prime 3674653429 of the same customary list;
  *   - dense level (1:1 map) iff (N_l+1)^d <= T, index sum_i v_i (N_l+1)^i;
  *   - vertices at v / N_l, p = fl32(x * N_l) (one rounded multiply),
  *     base = min(floor(p), N_l - 1), t = p - base;
@@ -62,7 +63,7 @@
 #endif
 
 #define ORC_MAX_LEVELS 32
-#define ORC_MAX_D 3
+#define ORC_MAX_D 4
 #define ORC_MAX_F 8
 
 typedef struct {
@@ -94,7 +95,7 @@ int32_t orc_c2f_active(int32_t L, int32_t L0, int64_t t, int64_t tau) {
 }
 
 /* one prime per axis; the first is 1 so that the x axis maps to itself */
-static const uint32_t ORC_PRIMES[3] = {1u, 2654435761u, 805459861u};
+static const uint32_t ORC_PRIMES[4] = {1u, 2654435761u, 805459861u, 3674653429u};
 
 /* ---- levels: geometric progression between N_min and N_max [INGP-news, Fig. 3 paragraph] ---- */
 int orc_levels(int32_t L, int32_t n_min, int32_t n_max, double growth, int32_t* out) {
@@ -317,6 +318,7 @@ static int rbf_weights(const orc_cfg* c, int l, const float* x, int64_t* rows, d
   const int side = 2 * k;
   int total = 1;
   for (int i = 0; i < d; ++i) total *= side;
+  if (total > ORC_MAX_RBF_VERTS) return 0; /* (2k)^d beyond the supported box (d <= 3) */
   for (int m = 0; m < total; ++m) {
     int64_t v[ORC_MAX_D];
     int inside = 1, mm = m;

@@ -7,7 +7,8 @@ package imports nothing from here.
 Every function takes a plain configuration ``spec`` (a dict) and host NumPy arrays and
 returns fp64 NumPy arrays.  The spec keys are:
 
-    d, L, F           dimension (1..3), number of levels, features per slot
+    d, L, F           dimension (1..4; 4 for the space-time Hermite grid), number of levels,
+                      features per slot
     kind              "dlinear" (Instant-NGP d-linear), "hermite" (Hermite-NGP) or "rbf"
                       (DInf-Grid Gaussian RBF; rbf_eps = epsilon, rbf_rings = k)
     T                 list of table sizes, one per derivative order (d-linear: [T])
@@ -33,7 +34,7 @@ _SRC = os.path.join(_HERE, "hashgrid_oracle.c")
 _LIB = os.environ.get("HASHGRID_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 MAX_LEVELS = 32
-MAX_D = 3
+MAX_D = 4
 
 
 def build_oracle(force: bool = True) -> str:
@@ -124,8 +125,8 @@ def make_cfg(spec: dict) -> _Cfg:
     c.kind = {"dlinear": 0, "hermite": 1, "rbf": 2}[spec["kind"]]
     if c.kind == 2:
         c.rings, c.eps = int(spec["rbf_rings"]), float(spec["rbf_eps"])
-        if not (1 <= c.rings <= 4 and c.eps > 0):
-            raise ValueError("rbf_rings must be 1..4 and rbf_eps > 0")
+        if not (1 <= c.rings <= 4 and c.eps > 0 and c.d <= 3):
+            raise ValueError("rbf_rings must be 1..4, rbf_eps > 0 and d <= 3")
     c.d2_mode = 2 if spec.get("d2_mode", "laplacian") == "diag" else 1
     T = list(spec["T"])
     if len(T) == 1:

@@ -29,6 +29,8 @@ SPECS = [
      "d2_mode": "diag"},
     {"d": 3, "L": 2, "F": 1, "kind": "hermite", "T": [1 << 7] * 4, "n_min": 2, "n_max": 9,
      "d2_mode": "laplacian"},
+    {"d": 4, "L": 2, "F": 2, "kind": "hermite", "T": [1 << 9, 1 << 8, 1 << 9, 1 << 7, 1 << 8], "n_min": 2,
+     "n_max": 7, "d2_mode": "diag"},
 ]
 
 

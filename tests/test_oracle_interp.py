@@ -94,7 +94,7 @@ def _poly_field(d, F, seed):
     return deriv_fn, ev
 
 
-@pytest.mark.parametrize("d,mode", [(2, "laplacian"), (3, "diag"), (3, "laplacian")])
+@pytest.mark.parametrize("d,mode", [(2, "laplacian"), (3, "diag"), (3, "laplacian"), (4, "diag"), (4, "laplacian")])
 def test_hermite_reproduces_per_axis_cubics(orc, d, mode):
     F = 2
     spec = {"d": d, "L": 2, "F": F, "kind": "hermite", "T": [1 << 16] * (d + 1),
@@ -192,20 +192,21 @@ def test_hermite_value_tables_equal_smoothstep_dlinear(orc):
     assert np.max(np.abs(gh - gl)) < 1e-5
 
 
-def test_hermite_finite_differences_on_hashed_levels(orc):
+@pytest.mark.parametrize("d", [3, 4])
+def test_hermite_finite_differences_on_hashed_levels(orc, d):
     # random (non-polynomial across cells) tables with collisions; inside a cell the field
     # is a per-axis cubic, so central differences of step h agree to O(h^2) for the
     # gradient and exactly (up to rounding) for the diagonal second derivatives
     N = 24
-    spec = {"d": 3, "L": 1, "F": 2, "kind": "hermite", "T": [1 << 8] * 4, "resolutions": [N],
+    spec = {"d": d, "L": 1, "F": 2, "kind": "hermite", "T": [1 << 8] * (d + 1), "resolutions": [N],
             "d2_mode": "diag"}
     lay = orc.layout(spec)
     assert not lay["dense"][0, 0]
     params = np.random.default_rng(14).normal(0, 1, lay["n_params"])
     rng = np.random.default_rng(15)
     # x = k 2^-18: x*N is exact in fp32 for N < 32, so evaluation positions are known exactly
-    cell = rng.integers(0, N, size=(60, 3))
-    tq = rng.integers(int(0.1 * 2 ** 18 / N), int(0.9 * 2 ** 18 / N), size=(60, 3))
+    cell = rng.integers(0, N, size=(60, d))
+    tq = rng.integers(int(0.1 * 2 ** 18 / N), int(0.9 * 2 ** 18 / N), size=(60, d))
     k = cell * (2 ** 18 // N) + tq
     k = k.astype(np.int64)
     h = 64  # step 64 * 2^-18 = 2^-12
@@ -214,8 +215,8 @@ def test_hermite_finite_differences_on_hashed_levels(orc):
     assert np.all(np.floor(x0.astype(np.float64) * N) == np.floor((k - h) / 2.0 ** 18 * N))
     g0, dg0, d20 = orc.forward(spec, x0, params)
     hs = h / 2.0 ** 18
-    for i in range(3):
-        e = np.zeros(3, np.int64)
+    for i in range(d):
+        e = np.zeros(d, np.int64)
         e[i] = h
         gp, _, _ = orc.forward(spec, ((k + e) / 2.0 ** 18).astype(np.float32), params)
         gm, _, _ = orc.forward(spec, ((k - e) / 2.0 ** 18).astype(np.float32), params)

@@ -50,6 +50,12 @@ def test_hash_unit_vertices_give_the_primes(orc):
     assert orc.hash_vertex([0, 1, 0]) == P1
     assert orc.hash_vertex([0, 0, 1]) == P2
     assert orc.hash_vertex([0, 1]) == P1
+    # the fourth (time) axis of the space-time grid takes the next prime of the same list
+    assert orc.hash_vertex([0, 0, 0, 1]) == 3674653429
+    v = [5, 7, 11, 13]
+    M = 1 << 32
+    assert orc.hash_vertex(v) == 5 ^ (7 * P1 % M) ^ (11 * P2 % M) ^ (13 * 3674653429 % M)
+    assert orc.hash_vertex(v) == orc.hash_vertex([5, 7, 11, 0]) ^ orc.hash_vertex([0, 0, 0, 13])
 
 
 def test_hash_combines_axes_by_xor(orc):
@@ -101,7 +107,7 @@ def test_hash_covers_the_table(orc):
 
 
 # ---------------------------------------------------------------- dense levels
-@pytest.mark.parametrize("d,N", [(2, 16), (2, 54), (3, 16), (3, 30)])
+@pytest.mark.parametrize("d,N", [(2, 16), (2, 54), (3, 16), (3, 30), (4, 6)])
 def test_dense_level_is_a_bijection_x_fastest(orc, d, N):
     spec = {"d": d, "L": 1, "F": 1, "kind": "dlinear", "T": [1 << 19], "resolutions": [N]}
     lay = orc.layout(spec)
