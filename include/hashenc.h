@@ -79,7 +79,8 @@ typedef enum { HASHENC_D2_LAPLACIAN = 1, HASHENC_D2_DIAG = 2 } hashenc_d2_mode;
 #define HASHENC_MAX_LEVELS 32
 
 typedef struct hashenc_config {
-  int32_t d;             /* spatial dimension: 2 or 3 */
+  int32_t d;             /* spatial dimension: 2 or 3; the Hermite kind also 4 (space-time:
+                            Hermite-NGP notes, 局限与展望 -- 16 coefficients per vertex) */
   int32_t n_levels;      /* L: 1..32 */
   int32_t n_features;    /* F: 1, 2, 4 or 8 features per derivative slot */
   int32_t kind;          /* hashenc_kind */
@@ -88,8 +89,8 @@ typedef struct hashenc_config {
   int32_t n_max;         /* N_max >= N_min: finest resolution (used when growth <= 0) */
   int32_t reserved;      /* must be 0 */
   double growth;         /* b > 0: N_l = floor(N_min b^l + 1e-6); <= 0: derived from n_max */
-  uint32_t table_size[4];/* T_k >= 1 rows for table k (derivative order k); d-linear uses
-                            [0]; Hermite uses [0..d].  Powers of two take a mask fast path */
+  uint32_t table_size[5];/* T_k >= 1 rows for table k (derivative order k); d-linear and RBF
+                            use [0]; Hermite uses [0..d].  Powers of two take a mask fast path */
   const int32_t* resolutions; /* host, optional: explicit N_l[L] (each 1..2^20); overrides
                                  n_min/n_max/growth when not NULL */
   double rbf_eps;        /* RBF only: shape parameter eps > 0 (finite); ignored otherwise */

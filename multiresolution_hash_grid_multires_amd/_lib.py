@@ -36,7 +36,7 @@ class HashencConfig(ctypes.Structure):
         ("n_max", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
         ("growth", ctypes.c_double),
-        ("table_size", ctypes.c_uint32 * 4),
+        ("table_size", ctypes.c_uint32 * 5),
         ("resolutions", ctypes.POINTER(ctypes.c_int32)),
         ("rbf_eps", ctypes.c_double),
         ("rbf_rings", ctypes.c_int32),

@@ -34,7 +34,7 @@ def _spec_to_config(spec: dict) -> tuple[_lib.HashencConfig, object]:
     n_tab = cfg.d + 1 if cfg.kind == _lib.HASHENC_HERMITE else 1
     if len(T) == 1:
         T = T * n_tab
-    for k in range(min(len(T), 4)):
+    for k in range(min(len(T), 5)):
         cfg.table_size[k] = int(T[k])
     keep = None
     if spec.get("resolutions") is not None:

@@ -6,7 +6,8 @@
 
 namespace hg {
 
-constexpr int kMaxSeg = kMaxTables * kMaxLevels;  // segment s = table k * L + level l
+constexpr int kMaxBinTables = 4;                  // the binned backward covers d <= 3
+constexpr int kMaxSeg = kMaxBinTables * kMaxLevels;  // segment s = table k * L + level l
 constexpr int kBinLdsValues = 8192;               // 64 KB fp64 LDS accumulator per work item
 constexpr int kBinTilePoints = 1024;              // points per count / scatter workgroup (max)
 constexpr int kBinThreads = 256;

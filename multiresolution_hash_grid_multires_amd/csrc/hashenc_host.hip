@@ -76,7 +76,8 @@ const char* hashenc_last_error(void) { return g_last_error.c_str(); }
 
 int hashenc_create(const hashenc_config* cfg, hashenc** out) {
   if (!cfg || !out) return fail(HASHENC_EINVAL, "hashenc_create: cfg and out must not be NULL");
-  if (cfg->d != 2 && cfg->d != 3) return fail(HASHENC_EINVAL, "d must be 2 or 3 (got %d)", cfg->d);
+  if (cfg->d != 2 && cfg->d != 3 && !(cfg->d == 4 && cfg->kind == HASHENC_HERMITE))
+    return fail(HASHENC_EINVAL, "d must be 2 or 3, or 4 for the Hermite kind (got %d)", cfg->d);
   if (cfg->n_levels < 1 || cfg->n_levels > kMaxLevels)
     return fail(HASHENC_EINVAL, "n_levels must be in 1..%d (got %d)", kMaxLevels, cfg->n_levels);
   if (cfg->n_features != 1 && cfg->n_features != 2 && cfg->n_features != 4 && cfg->n_features != 8)
@@ -253,6 +254,8 @@ int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* pa
     e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma, nullptr, stream);
   else if (h->kind == HASHENC_RBF)
     e = hg::launch_rbf_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, gamma, dgamma, d2gamma, stream);
+  else if (h->d == 4)
+    e = hg::launch_hermite4_forward(h->grid, h->F, h->d2_mode, n, x, params, gamma, dgamma, d2gamma, stream);
   else
     e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, nullptr, nullptr, false, gamma,
                                    dgamma, d2gamma, stream);
@@ -264,9 +267,9 @@ int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL handle");
   if (!bytes) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: NULL bytes");
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: n out of range");
-  *bytes = h->kind == HASHENC_DLINEAR   ? hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n)
-           : h->kind == HASHENC_HERMITE ? hermite_forward_ws_bytes(h, n)
-                                        : 0;  // the RBF forward needs no workspace
+  *bytes = h->kind == HASHENC_DLINEAR                 ? hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n)
+           : (h->kind == HASHENC_HERMITE && h->d < 4) ? hermite_forward_ws_bytes(h, n)
+                                                      : 0;  // RBF and 4D Hermite: no workspace
   return ok();
 }
 
@@ -274,7 +277,7 @@ int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float*
                        float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
                        hashenc_stream_t stream) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_ws: NULL handle");
-  if (h->kind == HASHENC_RBF) return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
+  if (h->kind == HASHENC_RBF || h->d == 4) return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
   if (h->kind == HASHENC_HERMITE) {
     // workspace: [packed copy of the order tables (equal table sizes) | level-major staging]
     const size_t need = hermite_forward_ws_bytes(h, n);
@@ -334,6 +337,9 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
   else if (h->kind == HASHENC_RBF)
     e = hg::launch_rbf_backward(h->grid, h->d, h->F, h->d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, grad_params,
                                 stream);
+  else if (h->d == 4)
+    e = hg::launch_hermite4_backward(h->grid, h->F, h->d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, grad_params,
+                                     stream);
   else
     e = hg::launch_hermite_backward(h->grid, h->d, h->F, h->d2_mode, n, x, g_gamma, g_dgamma,
                                          g_d2gamma, nullptr, grad_params, stream);
@@ -344,7 +350,7 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
 // The binned path keeps per-bin counters and staging in LDS; larger configurations take the
 // atomic path.
 static bool binned_supported(const hashenc* h) {
-  if (h->kind == HASHENC_RBF) return false;  // the RBF backward scatters with atomics
+  if (h->kind == HASHENC_RBF || h->d == 4) return false;  // RBF and 4D Hermite scatter with atomics
   return hg::binned_fits(h->grid, h->d, h->F, h->kind == HASHENC_HERMITE);
 }
 
@@ -353,6 +359,7 @@ static int check_mlp(const hashenc* h, const hashenc_mlp* mlp, const char* who) 
   if (!mlp) return fail(HASHENC_EINVAL, "%s: NULL mlp", who);
   if (h->kind != HASHENC_HERMITE)
     return fail(HASHENC_EUNSUPPORTED, "%s: the residual needs a Hermite handle (second derivatives)", who);
+  if (h->d == 4) return fail(HASHENC_EUNSUPPORTED, "%s: the residual covers d = 2 and 3", who);
   if (mlp->in != h->L * h->F)
     return fail(HASHENC_EINVAL, "%s: mlp.in (%d) must equal L*F (%d)", who, mlp->in, h->L * h->F);
   if (mlp->in > 64) return fail(HASHENC_EUNSUPPORTED, "%s: mlp.in must be <= 64", who);
@@ -498,7 +505,8 @@ int hashenc_debug_indices(const hashenc* h, int64_t n, const float* x, int32_t o
   if (!aligned16(x) || !aligned16(out_rows)) return fail(HASHENC_EALIGN, "hashenc_debug_indices: pointers must be 16-byte aligned");
   Grid g = h->grid;
   g.L = g.Lrow;  // the lookup stage of every level, active or not
-  hipError_t e = hg::launch_debug_indices(g, h->d, order, n, x, out_rows, stream);
+  hipError_t e = h->d == 4 ? hg::launch_debug_indices4(g, order, n, x, out_rows, stream)
+                           : hg::launch_debug_indices(g, h->d, order, n, x, out_rows, stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_debug_indices launch");
   return ok();
 }

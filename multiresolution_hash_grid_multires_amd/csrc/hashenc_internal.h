@@ -12,7 +12,7 @@
 namespace hg {
 
 constexpr int kMaxLevels = HASHENC_MAX_LEVELS;
-constexpr int kMaxTables = 4;
+constexpr int kMaxTables = 5;  // order tables: d + 1 for Hermite, up to d = 4
 constexpr int kBlock = 256;
 
 // The spatial-hash primes, one per axis; the first is 1 so the x axis maps to itself.
@@ -154,6 +154,13 @@ hipError_t launch_hermite_forward(const Grid& g, int d, int F, int d2_mode, int6
 hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int64_t n,
                                    const float* x, const float* g_gamma, const float* g_dgamma,
                                    const float* g_d2gamma, const float* u_levels, float* grad, hipStream_t s);
+// Space-time Hermite (d = 4: five order tables, 16 coefficients per vertex; fp32-atomic backward)
+hipError_t launch_hermite4_forward(const Grid& g, int F, int d2_mode, int64_t n, const float* x,
+                                   const float* params, float* gamma, float* dgamma, float* d2gamma, hipStream_t s);
+hipError_t launch_hermite4_backward(const Grid& g, int F, int d2_mode, int64_t n, const float* x,
+                                    const float* g_gamma, const float* g_dgamma, const float* g_d2gamma,
+                                    float* grad, hipStream_t s);
+hipError_t launch_debug_indices4(const Grid& g, int order, int64_t n, const float* x, int32_t* out, hipStream_t s);
 // Gaussian RBF (one table per level, derivative outputs as the Hermite ones; fp32-atomic backward)
 hipError_t launch_rbf_forward(const Grid& g, int d, int F, int d2_mode, int64_t n, const float* x,
                               const float* params, float* gamma, float* dgamma, float* d2gamma, hipStream_t s);

@@ -1063,6 +1063,333 @@ hipError_t launch_bwd(const Grid& g, int d2_mode, int64_t n, const float* x, con
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ space-time (d = 4)
+// Hermite-NGP notes, section 局限与展望: in 4D the 2^d coefficients per vertex become 16, in
+// five order tables (1, 4, 6, 4, 1 slots of F floats).  One lane per (point, level), level-major
+// workgroups.  Per corner the 16 coefficients form a 2x2x2x2 tensor over the derivative bits;
+// the forward contracts it with the per-axis bases one axis at a time (w, z, y, x), carrying
+// only the derivative kinds that survive (value; first and second derivative along each axis
+// already passed): 3 -> 5 -> 7 -> 9 results.  The backward runs the same contraction
+// transposed and scatter-adds with fp32 atomics.
+constexpr uint32_t kPrime3 = 3674653429u;
+
+// alpha (bit i = derivative along axis i) of slot s of order table k, slots of one order in
+// lexicographic order of their axis tuples
+__host__ __device__ constexpr int alpha4_of_slot(int k, int s) {
+  constexpr int o1[4] = {1, 2, 4, 8};
+  constexpr int o2[6] = {3, 5, 9, 6, 10, 12};
+  constexpr int o3[4] = {7, 11, 13, 14};
+  return k == 0 ? 0 : k == 1 ? o1[s] : k == 2 ? o2[s] : k == 3 ? o3[s] : 15;
+}
+__host__ __device__ constexpr int slots4(int k) { return k == 0 || k == 4 ? 1 : k == 2 ? 6 : 4; }
+
+// Corner rows of a cell from its base vertex: dense row dense0 + sum of the strides of the
+// corner's bits, hashed XOR of the four per-axis terms.  Every choice by a corner bit is a
+// select between two computed values (no indexing by a run-time bit, which would put the
+// operands in scratch memory).
+struct Keys4 {
+  uint32_t dense0, s1, s2, s3;
+  uint32_t h0, h1, h2, h3;  // per-axis hash terms of the base vertex
+};
+
+__device__ __forceinline__ Keys4 keys4(const uint32_t (&base)[4], int32_t N) {
+  Keys4 k;
+  const uint32_t N1 = (uint32_t)N + 1u;
+  k.s1 = N1;
+  k.s2 = N1 * N1;
+  k.s3 = N1 * N1 * N1;
+  k.dense0 = base[0] + base[1] * k.s1 + base[2] * k.s2 + base[3] * k.s3;
+  k.h0 = base[0];
+  k.h1 = base[1] * kPrime1;
+  k.h2 = base[2] * kPrime2;
+  k.h3 = base[3] * kPrime3;
+  return k;
+}
+
+__device__ __forceinline__ uint32_t row4(const Keys4& k, int c, bool dense, uint32_t T, uint32_t Tmask) {
+  const bool b0 = c & 1, b1 = (c >> 1) & 1, b2 = (c >> 2) & 1, b3 = (c >> 3) & 1;
+  if (dense)
+    return k.dense0 + (b0 ? 1u : 0u) + (b1 ? k.s1 : 0u) + (b2 ? k.s2 : 0u) + (b3 ? k.s3 : 0u);
+  const uint32_t h = (b0 ? k.h0 + 1u : k.h0) ^ (b1 ? k.h1 + kPrime1 : k.h1) ^ (b2 ? k.h2 + kPrime2 : k.h2) ^
+                     (b3 ? k.h3 + kPrime3 : k.h3);
+  return Tmask ? (h & Tmask) : (h % T);
+}
+
+// The bases of one corner along one axis, indexed by the derivative bit: b[a] value basis,
+// d[a] its x-derivative, d2[a] its second x-derivative; the same expressions as axis_basis,
+// computed here for the corner bit chosen at run time.
+struct CornerAxis {
+  float b[2], d[2], d2[2];
+};
+
+__device__ __forceinline__ CornerAxis corner_axis(float t, float N, float invN, bool far) {
+  const float s = 1.0f - t;
+  const float t2 = t * t;
+  const float h00 = (1.0f + 2.0f * t) * s * s, h00p = -6.0f * t * s, h00pp = 12.0f * t - 6.0f;
+  const float h10 = t * s * s, h10p = s * (1.0f - 3.0f * t), h10pp = 6.0f * t - 4.0f;
+  const float h01 = t2 * (3.0f - 2.0f * t);
+  const float h11 = -t2 * s, h11p = t * (3.0f * t - 2.0f), h11pp = 6.0f * t - 2.0f;
+  const float N2 = N * N;
+  CornerAxis r;
+  r.b[0] = far ? h01 : h00;
+  r.b[1] = invN * (far ? h11 : h10);
+  r.d[0] = far ? -N * h00p : N * h00p;
+  r.d[1] = far ? h11p : h10p;
+  r.d2[0] = far ? -N2 * h00pp : N2 * h00pp;
+  r.d2[1] = N * (far ? h11pp : h10pp);
+  return r;
+}
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void hermite4_forward_kernel(const Grid g, int64_t n, int32_t n_tiles,
+                                                                  int d2_mode, const float* __restrict__ x,
+                                                                  const float* __restrict__ params,
+                                                                  float* __restrict__ gamma,
+                                                                  float* __restrict__ dgamma,
+                                                                  float* __restrict__ d2gamma) {
+  constexpr int D = 4;
+  const int l = blockIdx.x / n_tiles;
+  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
+  if (p >= n) return;
+  float xp[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
+  uint32_t base[D];
+  float t[D];
+  locate<D>(xp, g.N[l], g.Nf[l], base, t);
+  const float Nf = g.Nf[l], iN = g.invN[l];
+  const Keys4 keys = keys4(base, g.N[l]);
+  // results: 0 value, 1 + i first derivative along i, 5 + i second derivative along i
+  float out[9][F];
+#pragma unroll
+  for (int r = 0; r < 9; ++r)
+#pragma unroll
+    for (int f = 0; f < F; ++f) out[r][f] = 0.0f;
+#pragma unroll 1
+  for (int c = 0; c < 16; ++c) {
+    // the corner's 16 coefficients th[alpha][f]
+    float th[16][F];
+#pragma unroll
+    for (int k = 0; k <= 4; ++k) {
+      const bool dense = (g.dense[k] >> l) & 1u;
+      const uint32_t row = row4(keys, c, dense, g.T[k], g.Tmask[k]);
+      const float* src = params + g.off[k][l] + (size_t)row * (slots4(k) * F);
+#pragma unroll
+      for (int sl = 0; sl < slots4(k); ++sl) load_vec<F>(src + sl * F, th[alpha4_of_slot(k, sl)]);
+    }
+    const CornerAxis c0 = corner_axis(t[0], Nf, iN, c & 1), c1 = corner_axis(t[1], Nf, iN, (c >> 1) & 1);
+    const CornerAxis c2 = corner_axis(t[2], Nf, iN, (c >> 2) & 1), c3 = corner_axis(t[3], Nf, iN, (c >> 3) & 1);
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      // axis 3 (w): kinds value, w', w''
+      float a3[3][8];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const float lo = th[a][f], hi = th[a | 8][f];
+        a3[0][a] = c3.b[0] * lo + c3.b[1] * hi;
+        a3[1][a] = c3.d[0] * lo + c3.d[1] * hi;
+        a3[2][a] = c3.d2[0] * lo + c3.d2[1] * hi;
+      }
+      // axis 2 (z): value, w', w'', z', z''
+      float a2[5][4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) a2[q][a] = c2.b[0] * a3[q][a] + c2.b[1] * a3[q][a | 4];
+        a2[3][a] = c2.d[0] * a3[0][a] + c2.d[1] * a3[0][a | 4];
+        a2[4][a] = c2.d2[0] * a3[0][a] + c2.d2[1] * a3[0][a | 4];
+      }
+      // axis 1 (y): value, w', w'', z', z'', y', y''
+      float a1[7][2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int q = 0; q < 5; ++q) a1[q][a] = c1.b[0] * a2[q][a] + c1.b[1] * a2[q][a | 2];
+        a1[5][a] = c1.d[0] * a2[0][a] + c1.d[1] * a2[0][a | 2];
+        a1[6][a] = c1.d2[0] * a2[0][a] + c1.d2[1] * a2[0][a | 2];
+      }
+      // axis 0 (x): value, w', w'', z', z'', y', y'', x', x''
+      float a0[9];
+#pragma unroll
+      for (int q = 0; q < 7; ++q) a0[q] = c0.b[0] * a1[q][0] + c0.b[1] * a1[q][1];
+      a0[7] = c0.d[0] * a1[0][0] + c0.d[1] * a1[0][1];
+      a0[8] = c0.d2[0] * a1[0][0] + c0.d2[1] * a1[0][1];
+      out[0][f] += a0[0];
+      out[1][f] += a0[7];  // d/dx
+      out[2][f] += a0[5];  // d/dy
+      out[3][f] += a0[3];  // d/dz
+      out[4][f] += a0[1];  // d/dw
+      out[5][f] += a0[8];
+      out[6][f] += a0[6];
+      out[7][f] += a0[4];
+      out[8][f] += a0[2];
+    }
+  }
+  const int64_t LF = (int64_t)g.Lrow * F;
+  const int64_t col = (int64_t)l * F;
+  if (gamma) store_vec<F>(gamma + p * LF + col, out[0]);
+  if (dgamma) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) store_vec<F>(dgamma + (p * D + i) * LF + col, out[1 + i]);
+  }
+  if (d2gamma) {
+    if (d2_mode == HASHENC_D2_DIAG) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) store_vec<F>(d2gamma + (p * D + i) * LF + col, out[5 + i]);
+    } else {
+      float lap[F];
+#pragma unroll
+      for (int f = 0; f < F; ++f) lap[f] = out[5][f] + out[6][f] + out[7][f] + out[8][f];
+      store_vec<F>(d2gamma + p * LF + col, lap);
+    }
+  }
+}
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void hermite4_backward_kernel(const Grid g, int64_t n, int32_t n_tiles,
+                                                                   int d2_mode, const float* __restrict__ x,
+                                                                   const float* __restrict__ g_gamma,
+                                                                   const float* __restrict__ g_dgamma,
+                                                                   const float* __restrict__ g_d2gamma,
+                                                                   float* __restrict__ grad) {
+  constexpr int D = 4;
+  const int l = blockIdx.x / n_tiles;
+  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
+  if (p >= n) return;
+  float xp[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
+  uint32_t base[D];
+  float t[D];
+  locate<D>(xp, g.N[l], g.Nf[l], base, t);
+  const float Nf = g.Nf[l], iN = g.invN[l];
+  const Keys4 keys = keys4(base, g.N[l]);
+  const int64_t LF = (int64_t)g.Lrow * F;
+  const int64_t col = (int64_t)l * F;
+  // upstream in the order of the forward's axis-0 results: value, w', w'', z', z'', y', y'', x', x''
+  float U[9][F];
+#pragma unroll
+  for (int r = 0; r < 9; ++r)
+#pragma unroll
+    for (int f = 0; f < F; ++f) U[r][f] = 0.0f;
+  float G[F];
+  if (g_gamma) load_vec<F>(g_gamma + p * LF + col, U[0]);
+  if (g_dgamma) {
+    constexpr int slot1[4] = {7, 5, 3, 1};  // x', y', z', w'
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      load_vec<F>(g_dgamma + (p * D + i) * LF + col, G);
+#pragma unroll
+      for (int f = 0; f < F; ++f) U[slot1[i]][f] = G[f];
+    }
+  }
+  if (g_d2gamma) {
+    constexpr int slot2[4] = {8, 6, 4, 2};  // x'', y'', z'', w''
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (d2_mode == HASHENC_D2_DIAG || i == 0) load_vec<F>(g_d2gamma + ((d2_mode == HASHENC_D2_DIAG ? p * D + i : p)) * LF + col, G);
+#pragma unroll
+      for (int f = 0; f < F; ++f) U[slot2[i]][f] = G[f];
+    }
+  }
+#pragma unroll 1
+  for (int c = 0; c < 16; ++c) {
+    const CornerAxis c0 = corner_axis(t[0], Nf, iN, c & 1), c1 = corner_axis(t[1], Nf, iN, (c >> 1) & 1);
+    const CornerAxis c2 = corner_axis(t[2], Nf, iN, (c >> 2) & 1), c3 = corner_axis(t[3], Nf, iN, (c >> 3) & 1);
+    float th[16][F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      // transpose of the forward's axis-0 step: 9 -> 7 kinds over the x bit
+      float r1[7][2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        r1[0][a] = c0.b[a] * U[0][f] + c0.d[a] * U[7][f] + c0.d2[a] * U[8][f];
+#pragma unroll
+        for (int q = 1; q < 7; ++q) r1[q][a] = c0.b[a] * U[q][f];
+      }
+      // axis 1: 7 -> 5 kinds over the y bit
+      float r2[5][4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int ax = a & 1, ay = a >> 1;
+        r2[0][a] = c1.b[ay] * r1[0][ax] + c1.d[ay] * r1[5][ax] + c1.d2[ay] * r1[6][ax];
+#pragma unroll
+        for (int q = 1; q < 5; ++q) r2[q][a] = c1.b[ay] * r1[q][ax];
+      }
+      // axis 2: 5 -> 3 kinds over the z bit
+      float r3[3][8];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const int axy = a & 3, az = a >> 2;
+        r3[0][a] = c2.b[az] * r2[0][axy] + c2.d[az] * r2[3][axy] + c2.d2[az] * r2[4][axy];
+        r3[1][a] = c2.b[az] * r2[1][axy];
+        r3[2][a] = c2.b[az] * r2[2][axy];
+      }
+      // axis 3: 3 kinds -> the 16 coefficient adjoints
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int axyz = a & 7, aw = a >> 3;
+        th[a][f] = c3.b[aw] * r3[0][axyz] + c3.d[aw] * r3[1][axyz] + c3.d2[aw] * r3[2][axyz];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k <= 4; ++k) {
+      const bool dense = (g.dense[k] >> l) & 1u;
+      const uint32_t row = row4(keys, c, dense, g.T[k], g.Tmask[k]);
+      float* dst = grad + g.off[k][l] + (size_t)row * (slots4(k) * F);
+#pragma unroll
+      for (int sl = 0; sl < slots4(k); ++sl)
+#pragma unroll
+        for (int f = 0; f < F; ++f) atomic_add_f32(dst + sl * F + f, th[alpha4_of_slot(k, sl)][f]);
+    }
+  }
+}
+
+// Lookup-stage export for d = 4: rows of the 16 corners of table `order`, [n][L][16].
+__global__ __launch_bounds__(kBlock) void debug_indices4_kernel(const Grid g, int order, int64_t n,
+                                                                const float* __restrict__ x,
+                                                                int32_t* __restrict__ out) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p >= n) return;
+  float xp[4];
+  for (int i = 0; i < 4; ++i) xp[i] = x[p * 4 + i];
+  for (int l = 0; l < g.L; ++l) {
+    uint32_t base[4];
+    float t[4];
+    locate<4>(xp, g.N[l], g.Nf[l], base, t);
+    const Keys4 keys = keys4(base, g.N[l]);
+    const bool dense = (g.dense[order] >> l) & 1u;
+    for (int c = 0; c < 16; ++c)
+      out[(p * g.L + l) * 16 + c] = (int32_t)row4(keys, c, dense, g.T[order], g.Tmask[order]);
+  }
+}
+
+template <int F>
+hipError_t launch_fwd4(const Grid& g, int d2_mode, int64_t n, const float* x, const float* params, float* gamma,
+                       float* dgamma, float* d2gamma, hipStream_t s) {
+  const int64_t tiles = (n + kBlock - 1) / kBlock;
+  if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((hermite4_forward_kernel<F>), dim3((unsigned)(tiles * g.L)), dim3(kBlock), 0, s, g, n,
+                     (int32_t)tiles, d2_mode, x, params, gamma, dgamma, d2gamma);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.L == g.Lrow) return e;
+  const int RF = g.Lrow * F, AF = g.L * F;
+  if (gamma) e = launch_zero_columns(gamma, n, RF, AF, s);
+  if (e == hipSuccess && dgamma) e = launch_zero_columns(dgamma, n * 4, RF, AF, s);
+  if (e == hipSuccess && d2gamma) e = launch_zero_columns(d2gamma, n * (d2_mode == HASHENC_D2_DIAG ? 4 : 1), RF, AF, s);
+  return e;
+}
+
+template <int F>
+hipError_t launch_bwd4(const Grid& g, int d2_mode, int64_t n, const float* x, const float* gg, const float* gd,
+                       const float* g2, float* grad, hipStream_t s) {
+  const int64_t tiles = (n + kBlock - 1) / kBlock;
+  if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((hermite4_backward_kernel<F>), dim3((unsigned)(tiles * g.L)), dim3(kBlock), 0, s, g, n,
+                     (int32_t)tiles, d2_mode, x, gg, gd, g2, grad);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 #define HASHENC_DISPATCH_DF(d, F, FN, ...)       \
@@ -1115,6 +1442,34 @@ hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int
                                    const float* x, const float* g_gamma, const float* g_dgamma,
                                    const float* g_d2gamma, const float* u_levels, float* grad, hipStream_t s) {
   HASHENC_DISPATCH_DF(d, F, launch_bwd, g, d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, u_levels, grad, s);
+}
+
+#define HASHENC_DISPATCH_F4(F, FN, ...)         \
+  do {                                          \
+    switch (F) {                                \
+      case 1: return FN<1>(__VA_ARGS__);        \
+      case 2: return FN<2>(__VA_ARGS__);        \
+      case 4: return FN<4>(__VA_ARGS__);        \
+      case 8: return FN<8>(__VA_ARGS__);        \
+    }                                           \
+    return hipErrorInvalidValue;                \
+  } while (0)
+
+hipError_t launch_debug_indices4(const Grid& g, int order, int64_t n, const float* x, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(debug_indices4_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, g, order,
+                     n, x, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_hermite4_forward(const Grid& g, int F, int d2_mode, int64_t n, const float* x,
+                                   const float* params, float* gamma, float* dgamma, float* d2gamma, hipStream_t s) {
+  HASHENC_DISPATCH_F4(F, launch_fwd4, g, d2_mode, n, x, params, gamma, dgamma, d2gamma, s);
+}
+
+hipError_t launch_hermite4_backward(const Grid& g, int F, int d2_mode, int64_t n, const float* x,
+                                    const float* g_gamma, const float* g_dgamma, const float* g_d2gamma,
+                                    float* grad, hipStream_t s) {
+  HASHENC_DISPATCH_F4(F, launch_bwd4, g, d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, grad, s);
 }
 
 hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int d, int F,

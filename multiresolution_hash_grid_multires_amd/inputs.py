@@ -82,6 +82,17 @@ WORKLOADS: dict[str, dict] = {
         "clustered_half": True,
         "outputs": ("residual", "loss"),
     },
+    # Space-time Hermite-NGP (d = 4): 16 coefficients per vertex in five order tables of 2^16
+    # rows (widths F, 4F, 6F, 4F, F), 8 levels N 4..64 (the four coarsest dense), diagonal
+    # second derivatives, 2^18 points uniform in [0,1)^4.
+    "hermite4d_L8_T16": {
+        "id": 9,
+        "spec": {"d": 4, "L": 8, "F": 2, "kind": "hermite", "T": [1 << 16] * 5, "n_min": 4, "n_max": 64,
+                 "d2_mode": "diag"},
+        "n_points": 1 << 18,
+        "tables": ("normal", 1e-2),
+        "outputs": ("gamma", "dgamma", "d2gamma"),
+    },
     # DInf-Grid Gaussian RBF, 2D: four co-located dense grids N = 64..512 (the largest 512 on
     # a side, the 2D setting the summary recommends), eps = 1 with 3-ring neighbourhoods (36
     # vertices per level), one stratified point per pixel of a 512 x 512 image.
