@@ -1245,6 +1245,32 @@ __global__ __launch_bounds__(kBlock) void hermite4_forward_kernel(const Grid g, 
   }
 }
 
+// Backward: 16 FL lanes per point (FL = min(F, 4)), lane (alpha, f) owning feature f (and
+// f + 4 when F = 8) of the coefficient with derivative bits alpha of every corner.  Each lane
+// runs the transposed contraction for its own bits only, so the lanes of a point add one
+// order table's row (C(4,k) F contiguous floats) with one atomic instruction, one memory
+// request per row, instead of one request per float of one point.
+template <int F>
+constexpr int h4_lanes() { return 16 * (F > 4 ? 4 : F); }
+
+// Factors of one axis for a given corner bit and derivative bit: value basis, its x-derivative
+// and second x-derivative (the expressions of axis_basis; selects between computed values).
+__device__ __forceinline__ void axis_factor(float t, float N, float invN, bool far, bool deriv, float& b, float& d,
+                                            float& d2) {
+  const float s = 1.0f - t;
+  const float t2 = t * t;
+  const float h00 = (1.0f + 2.0f * t) * s * s, h00p = -6.0f * t * s, h00pp = 12.0f * t - 6.0f;
+  const float h10 = t * s * s, h10p = s * (1.0f - 3.0f * t), h10pp = 6.0f * t - 4.0f;
+  const float h01 = t2 * (3.0f - 2.0f * t);
+  const float h11 = -t2 * s, h11p = t * (3.0f * t - 2.0f), h11pp = 6.0f * t - 2.0f;
+  const float N2 = N * N;
+  const float bv = far ? h01 : h00, dv = far ? -N * h00p : N * h00p, d2v = far ? -N2 * h00pp : N2 * h00pp;
+  const float bd = invN * (far ? h11 : h10), dd = far ? h11p : h10p, d2d = N * (far ? h11pp : h10pp);
+  b = deriv ? bd : bv;
+  d = deriv ? dd : dv;
+  d2 = deriv ? d2d : d2v;
+}
+
 template <int F>
 __global__ __launch_bounds__(kBlock) void hermite4_backward_kernel(const Grid g, int64_t n, int32_t n_tiles,
                                                                    int d2_mode, const float* __restrict__ x,
@@ -1253,9 +1279,15 @@ __global__ __launch_bounds__(kBlock) void hermite4_backward_kernel(const Grid g,
                                                                    const float* __restrict__ g_d2gamma,
                                                                    float* __restrict__ grad) {
   constexpr int D = 4;
+  constexpr int FL = F > 4 ? 4 : F;  // lanes per coefficient
+  constexpr int FJ = F / FL;         // features per lane
+  constexpr int LP = h4_lanes<F>();  // lanes per point
+  constexpr int PTS = kBlock / LP;
   const int l = blockIdx.x / n_tiles;
-  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
-  if (p >= n) return;
+  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * PTS + threadIdx.x / LP;
+  const int sub = threadIdx.x % LP;
+  const int alpha = sub / FL, f0 = sub % FL;
+  if (p >= n) return;  // the lanes of a point leave together
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
@@ -1266,81 +1298,51 @@ __global__ __launch_bounds__(kBlock) void hermite4_backward_kernel(const Grid g,
   const Keys4 keys = keys4(base, g.N[l]);
   const int64_t LF = (int64_t)g.Lrow * F;
   const int64_t col = (int64_t)l * F;
-  // upstream in the order of the forward's axis-0 results: value, w', w'', z', z'', y', y'', x', x''
-  float U[9][F];
+  // this lane's features of the upstream: G0, first derivatives G1[i], second G2[i]
+  float G0[FJ], G1[D][FJ], G2[D][FJ];
 #pragma unroll
-  for (int r = 0; r < 9; ++r)
-#pragma unroll
-    for (int f = 0; f < F; ++f) U[r][f] = 0.0f;
-  float G[F];
-  if (g_gamma) load_vec<F>(g_gamma + p * LF + col, U[0]);
-  if (g_dgamma) {
-    constexpr int slot1[4] = {7, 5, 3, 1};  // x', y', z', w'
+  for (int j = 0; j < FJ; ++j) {
+    const int64_t cf = col + f0 + FL * j;
+    G0[j] = g_gamma ? g_gamma[p * LF + cf] : 0.0f;
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      load_vec<F>(g_dgamma + (p * D + i) * LF + col, G);
-#pragma unroll
-      for (int f = 0; f < F; ++f) U[slot1[i]][f] = G[f];
+      G1[i][j] = g_dgamma ? g_dgamma[(p * D + i) * LF + cf] : 0.0f;
+      G2[i][j] = !g_d2gamma ? 0.0f
+                 : d2_mode == HASHENC_D2_DIAG ? g_d2gamma[(p * D + i) * LF + cf]
+                                              : g_d2gamma[p * LF + cf];
     }
   }
-  if (g_d2gamma) {
-    constexpr int slot2[4] = {8, 6, 4, 2};  // x'', y'', z'', w''
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      if (d2_mode == HASHENC_D2_DIAG || i == 0) load_vec<F>(g_d2gamma + ((d2_mode == HASHENC_D2_DIAG ? p * D + i : p)) * LF + col, G);
-#pragma unroll
-      for (int f = 0; f < F; ++f) U[slot2[i]][f] = G[f];
-    }
-  }
+  const bool ax = alpha & 1, ay = (alpha >> 1) & 1, az = (alpha >> 2) & 1, aw = (alpha >> 3) & 1;
+  const int order = ax + ay + az + aw;
+  // slot of alpha among the alphas of its order (lexicographic axis tuples), one nibble per
+  // alpha: x y z w | xy xz xw yz yw zw | xyz xyw xzw yzw
+  constexpr uint64_t kSlots4 = 0x0325142303120100ull;
+  const int slot = (int)((kSlots4 >> (4 * alpha)) & 15u);
 #pragma unroll 1
   for (int c = 0; c < 16; ++c) {
-    const CornerAxis c0 = corner_axis(t[0], Nf, iN, c & 1), c1 = corner_axis(t[1], Nf, iN, (c >> 1) & 1);
-    const CornerAxis c2 = corner_axis(t[2], Nf, iN, (c >> 2) & 1), c3 = corner_axis(t[3], Nf, iN, (c >> 3) & 1);
-    float th[16][F];
+    float bx, dx, d2x, by, dy, d2y, bz, dz, d2z, bw, dw, d2w;
+    axis_factor(t[0], Nf, iN, c & 1, ax, bx, dx, d2x);
+    axis_factor(t[1], Nf, iN, (c >> 1) & 1, ay, by, dy, d2y);
+    axis_factor(t[2], Nf, iN, (c >> 2) & 1, az, bz, dz, d2z);
+    axis_factor(t[3], Nf, iN, (c >> 3) & 1, aw, bw, dw, d2w);
+    // d theta[alpha] = sum over outputs of the upstream times the product of the per-axis
+    // factors (value basis on every axis but the differentiated one)
+    const float xyz = bx * by * bz, xyw = bx * by * bw, xzw = bx * bz * bw, yzw = by * bz * bw;
+    float th[FJ];
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-      // transpose of the forward's axis-0 step: 9 -> 7 kinds over the x bit
-      float r1[7][2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        r1[0][a] = c0.b[a] * U[0][f] + c0.d[a] * U[7][f] + c0.d2[a] * U[8][f];
-#pragma unroll
-        for (int q = 1; q < 7; ++q) r1[q][a] = c0.b[a] * U[q][f];
-      }
-      // axis 1: 7 -> 5 kinds over the y bit
-      float r2[5][4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int ax = a & 1, ay = a >> 1;
-        r2[0][a] = c1.b[ay] * r1[0][ax] + c1.d[ay] * r1[5][ax] + c1.d2[ay] * r1[6][ax];
-#pragma unroll
-        for (int q = 1; q < 5; ++q) r2[q][a] = c1.b[ay] * r1[q][ax];
-      }
-      // axis 2: 5 -> 3 kinds over the z bit
-      float r3[3][8];
-#pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const int axy = a & 3, az = a >> 2;
-        r3[0][a] = c2.b[az] * r2[0][axy] + c2.d[az] * r2[3][axy] + c2.d2[az] * r2[4][axy];
-        r3[1][a] = c2.b[az] * r2[1][axy];
-        r3[2][a] = c2.b[az] * r2[2][axy];
-      }
-      // axis 3: 3 kinds -> the 16 coefficient adjoints
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int axyz = a & 7, aw = a >> 3;
-        th[a][f] = c3.b[aw] * r3[0][axyz] + c3.d[aw] * r3[1][axyz] + c3.d2[aw] * r3[2][axyz];
-      }
-    }
+    for (int j = 0; j < FJ; ++j)
+      th[j] = xyz * bw * G0[j] + dx * yzw * G1[0][j] + dy * xzw * G1[1][j] + dz * xyw * G1[2][j] +
+              dw * xyz * G1[3][j] + d2x * yzw * G2[0][j] + d2y * xzw * G2[1][j] + d2z * xyw * G2[2][j] +
+              d2w * xyz * G2[3][j];
+    // one order table at a time (a uniform loop), its lanes adding one contiguous row
 #pragma unroll
     for (int k = 0; k <= 4; ++k) {
+      if (order != k) continue;
       const bool dense = (g.dense[k] >> l) & 1u;
       const uint32_t row = row4(keys, c, dense, g.T[k], g.Tmask[k]);
-      float* dst = grad + g.off[k][l] + (size_t)row * (slots4(k) * F);
+      float* dst = grad + g.off[k][l] + (size_t)row * (slots4(k) * F) + slot * F + f0;
 #pragma unroll
-      for (int sl = 0; sl < slots4(k); ++sl)
-#pragma unroll
-        for (int f = 0; f < F; ++f) atomic_add_f32(dst + sl * F + f, th[alpha4_of_slot(k, sl)][f]);
+      for (int j = 0; j < FJ; ++j) atomic_add_f32(dst + FL * j, th[j]);
     }
   }
 }
@@ -1383,7 +1385,8 @@ hipError_t launch_fwd4(const Grid& g, int d2_mode, int64_t n, const float* x, co
 template <int F>
 hipError_t launch_bwd4(const Grid& g, int d2_mode, int64_t n, const float* x, const float* gg, const float* gd,
                        const float* g2, float* grad, hipStream_t s) {
-  const int64_t tiles = (n + kBlock - 1) / kBlock;
+  constexpr int PTS = kBlock / h4_lanes<F>();  // points per workgroup
+  const int64_t tiles = (n + PTS - 1) / PTS;
   if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((hermite4_backward_kernel<F>), dim3((unsigned)(tiles * g.L)), dim3(kBlock), 0, s, g, n,
                      (int32_t)tiles, d2_mode, x, gg, gd, g2, grad);
