@@ -99,6 +99,27 @@ def copy_calibration(args, torch, api) -> int:
     return 0
 
 
+def cache_read_calibration(args, torch, api) -> int:
+    """L2-resident read of --cache-bytes bytes, --cache-reps passes per launch: the L2 read
+    ceiling the gather kernels are set against (bytes read = cache bytes x reps)."""
+    n = (args.cache_bytes // 4) // 32 * 32
+    buf = torch.ones(n, device="cuda:0")
+    out = torch.zeros(1, device="cuda:0")
+    for _ in range(args.warmup):
+        api.hashenc_diag_cache_read(buf, args.cache_reps, out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        api.hashenc_diag_cache_read(buf, args.cache_reps, out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"cache_bytes": 4 * n, "reps": args.cache_reps, "ms": round(ms, 4),
+                      "read_GBps": round(4 * n * args.cache_reps / ms / 1e6, 1)}), flush=True)
+    return 0
+
+
 def mlp_flops_per_point(d: int, n_in: int, hidden: int, depth: int) -> int:
     """Multiply-add FLOPs of the SIREN part per point: forward mode carries d + 2 rows
     (value, d gradients, Laplacian) through every layer; the reverse sweep costs one product
@@ -233,6 +254,10 @@ def main() -> int:
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run the plain copy kernel over this many bytes "
                          "(bandwidth and memory-counter calibration)")
+    ap.add_argument("--cache-bytes", type=int, default=0,
+                    help="instead of the benchmark, read this many bytes (split over the 8 XCDs' L2s) "
+                         "--cache-reps times per launch: the L2 read ceiling")
+    ap.add_argument("--cache-reps", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     args = ap.parse_args()
@@ -248,6 +273,8 @@ def main() -> int:
 
     if args.copy_bytes:
         return copy_calibration(args, torch, api)
+    if args.cache_bytes:
+        return cache_read_calibration(args, torch, api)
 
     W = I.WORKLOADS[args.workload]
     if args.active_levels:

@@ -23,6 +23,15 @@ HASHENC_API int hashenc_debug_indices(const hashenc* h, int64_t n, const float* 
  * Used to measure achievable HBM bandwidth and to calibrate memory counters. */
 HASHENC_API int hashenc_diag_copy(const float* src, float* dst, int64_t n_floats, hashenc_stream_t stream);
 
+/* L2-resident read: buf (n_floats, a positive multiple of 32, 16-byte aligned) is cut into
+ * 8 equal slices, one per XCD, and each XCD's workgroups read their slice `reps` times
+ * (reps >= 1), so that with slices of at most a few MB every pass after the first is served
+ * by the XCD's L2.  Gives the L2 read ceiling (bytes = 4 * n_floats * reps) and, under a
+ * counter run, the L2 request rate the gather kernels are compared with.  buf should hold
+ * ones: out (one float) is written only if the sum is -1, which such a buffer cannot give. */
+HASHENC_API int hashenc_diag_cache_read(const float* buf, int64_t n_floats, int32_t reps, float* out,
+                                        hashenc_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     hashenc_create,
     hashenc_debug_indices,
     hashenc_destroy,
+    hashenc_diag_cache_read,
     hashenc_diag_copy,
     hashenc_forward,
     hashenc_forward_workspace_size,

@@ -85,6 +85,7 @@ SIGNATURES = [
     ("hashenc_last_error", ctypes.c_char_p, []),
     ("hashenc_debug_indices", ctypes.c_int, [P, I64, P, I32, P, P]),
     ("hashenc_diag_copy", ctypes.c_int, [P, P, I64, P]),
+    ("hashenc_diag_cache_read", ctypes.c_int, [P, I64, I32, P, P]),
 ]
 
 _lib = None

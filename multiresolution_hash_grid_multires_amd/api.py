@@ -246,6 +246,11 @@ def hashenc_diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None
     check(load().hashenc_diag_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), src.numel(), _stream(stream)))
 
 
+def hashenc_diag_cache_read(buf: torch.Tensor, reps: int, out: torch.Tensor, stream=None) -> None:
+    check(load().hashenc_diag_cache_read(_dev_ptr(buf, "buf"), buf.numel(), int(reps), _dev_ptr(out, "out"),
+                                         _stream(stream)))
+
+
 class HashGridEncoding:
     """Convenience wrapper: a handle plus output allocation (torch tensors on the GPU)."""
 

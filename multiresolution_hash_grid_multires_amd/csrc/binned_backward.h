@@ -24,7 +24,10 @@ inline int32_t bin_item_entries(int64_t entries) {
 }
 constexpr int kReduceThreads = 512;
 constexpr int kBinReduceBlocks = 512;             // persistent reduce workgroups (2 per CU)
-constexpr int kScatterThreads = 512;              // d-linear scatter workgroup
+// d-linear scatter workgroup = tile: one point per lane.  Larger tiles give each bin longer
+// runs per tile (whole lines written); the larger size is used when its LDS staging fits.
+constexpr int kScatterTileLarge = 1024;
+constexpr int kScatterTileSmall = 512;
 constexpr size_t kMaxScatterLds = 150 * 1024;     // of the 160 KB LDS of a gfx950 CU
 
 // Small, by-value plan: bins are (segment, chunk of rows) in segment order.  A chunk has
@@ -175,12 +178,13 @@ __device__ __forceinline__ void bin_of(const BinPlan& bp, int k, int l, uint32_t
 
 int bin_cshift_for_width(int W);
 void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp);
-int bin_tile_points(const BinPlan& bp, int F, bool hermite);
+int bin_tile_points(const BinPlan& bp, int d, int F, bool hermite);
 // Points (= threads) of a Hermite scatter workgroup: its LDS staging holds one order table's
 // records for every corner of the tile.
 constexpr int hermite_scatter_points(int F) { return F <= 2 ? 256 : F == 4 ? 128 : 64; }
 size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F);
-// LDS of the d-linear scatter workgroup: three per-bin arrays and the pair-record staging.
+// LDS of the d-linear scatter workgroup: two per-bin arrays, the per-level staging bases and
+// the pair-record staging.
 size_t dlinear_scatter_lds_bytes(const BinPlan& bp, int d, int F, int tile);
 BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64_t entries_per_point,
                                   int64_t floats_per_point, int tile);

@@ -355,10 +355,11 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
   }
 }
 
-int bin_tile_points(const BinPlan& bp, int F, bool hermite) {
-  (void)bp;
+int bin_tile_points(const BinPlan& bp, int d, int F, bool hermite) {
   // one point per scatter lane
-  return hermite ? hermite_scatter_points(F) : kScatterThreads;
+  if (hermite) return hermite_scatter_points(F);
+  return dlinear_scatter_lds_bytes(bp, d, F, kScatterTileLarge) <= kMaxScatterLds ? kScatterTileLarge
+                                                                                 : kScatterTileSmall;
 }
 
 size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F) {
@@ -369,7 +370,7 @@ size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F) {
 }
 
 size_t dlinear_scatter_lds_bytes(const BinPlan& bp, int d, int F, int tile) {
-  return sizeof(int32_t) * (3 * (size_t)bp.nbins + kScatterThreads / 64 + 3) +
+  return sizeof(int32_t) * (2 * (size_t)bp.nbins + tile / 64 + kMaxLevels + 3) +
          (size_t)tile * (1 << (d - 1)) * (sizeof(float) * (2 + F) + sizeof(int32_t));
 }
 
@@ -431,7 +432,7 @@ bool binned_fits(const Grid& g, int d, int F, bool hermite) {
   const int32_t count_bins = bp.fine_shift >= 0 ? bp.fine_bin0[g.L] : bp.nbins;
   if (bp.nbins > kMaxBins || count_bins > kMaxBins) return false;  // LDS counters of the count pass
   if (hermite) return hermite_scatter_lds_bytes(bp, d, F) <= kMaxScatterLds;
-  const int tile = bin_tile_points(bp, F, hermite);
+  const int tile = bin_tile_points(bp, d, F, hermite);
   return dlinear_scatter_lds_bytes(bp, d, F, tile) <= kMaxScatterLds;
 }
 
@@ -440,7 +441,7 @@ size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite
   make_bin_plan(g, d, F, hermite, bp);
   const int64_t c = n < kBinChunkPoints ? n : kBinChunkPoints;
   return bin_workspace_layout(bp, c, entries_per_point(d, g.L, hermite), floats_per_point(bp, d),
-                              bin_tile_points(bp, F, hermite)).total;
+                              bin_tile_points(bp, d, F, hermite)).total;
 }
 
 hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2_mode, int64_t n,
@@ -455,7 +456,7 @@ hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2
   for (int64_t p0 = 0; p0 < n; p0 += kBinChunkPoints) {
     const int64_t c = (n - p0) < kBinChunkPoints ? (n - p0) : kBinChunkPoints;
     const BinWorkspace w = bin_workspace_layout(bp, c, entries_per_point(d, g.L, hermite), floats_per_point(bp, d),
-                                                bin_tile_points(bp, F, hermite));
+                                                bin_tile_points(bp, d, F, hermite));
     const float* xc = x + p0 * d;
     const float* gg = g_gamma ? g_gamma + p0 * LF : nullptr;
     const float* gd = g_dgamma ? g_dgamma + p0 * d * LF : nullptr;

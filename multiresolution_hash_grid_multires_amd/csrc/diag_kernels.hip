@@ -1,5 +1,6 @@
-// Diagnostic kernels: export of the lookup stage (corner rows per point and level) and a
-// plain streaming copy used to calibrate bandwidth figures.
+// Diagnostic kernels: export of the lookup stage (corner rows per point and level), a plain
+// streaming copy used to calibrate bandwidth figures, and a cache-resident read that gives
+// the L2 ceiling the gather kernels are compared with.
 #include "hashenc_internal.h"
 
 namespace hg {
@@ -37,6 +38,32 @@ __global__ void copy_tail_kernel(const float* __restrict__ src, float* __restric
   if (i < n) dst[i] = src[i];
 }
 
+// L2-resident read.  The buffer is cut into kXcds equal slices; workgroup b reads slice
+// b % kXcds, the slice of the XCD it is dispatched to (workgroups go round-robin to the
+// XCDs), so after the first pass every read is served by that XCD's L2.  A CU holds 8
+// workgroups that each walk their own part of the slice: at 3 MB per slice that is about
+// 96 KB per CU per pass, more than the 32 KB vector L1, so the cyclic walk misses L1.  The
+// sum is stored only if it takes a value that a buffer of ones cannot give, which keeps the
+// loads without writing anything.
+constexpr int kXcds = 8;
+constexpr int kCacheReadBlocks = kXcds * 256;
+
+__global__ __launch_bounds__(kBlock) void cache_read_kernel(const float4* __restrict__ buf, int64_t slice4,
+                                                            int32_t reps, float* __restrict__ out) {
+  const int xcd = blockIdx.x % kXcds;
+  const int64_t j = blockIdx.x / kXcds;
+  const int64_t stride = (int64_t)(kCacheReadBlocks / kXcds) * kBlock;
+  const float4* s = buf + xcd * slice4;
+  float acc = 0.0f;
+  for (int r = 0; r < reps; ++r) {
+    for (int64_t i = j * kBlock + threadIdx.x; i < slice4; i += stride) {
+      const float4 v = s[i];
+      acc += (v.x + v.y) + (v.z + v.w);
+    }
+  }
+  if (acc == -1.0f) out[0] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_debug_indices(const Grid& g, int d, int order, int64_t n, const float* x,
@@ -60,6 +87,15 @@ hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t s) {
                        reinterpret_cast<const float4*>(src), reinterpret_cast<float4*>(dst), n4);
   }
   if (n % 4) hipLaunchKernelGGL(copy_tail_kernel, dim3(1), dim3(4), 0, s, src, dst, n4 * 4, n);
+  return hipGetLastError();
+}
+
+int64_t cache_read_granule() { return 4 * kXcds; }
+
+hipError_t launch_cache_read(const float* buf, int64_t n, int32_t reps, float* out, hipStream_t s) {
+  const int64_t slice4 = n / (4 * kXcds);
+  hipLaunchKernelGGL(cache_read_kernel, dim3(kCacheReadBlocks), dim3(kBlock), 0, s,
+                     reinterpret_cast<const float4*>(buf), slice4, reps, out);
   return hipGetLastError();
 }
 

@@ -204,25 +204,24 @@ __global__ __launch_bounds__(kBlock) void dlinear_backward_kernel(const Grid g, 
   }
 }
 
-// Binned backward, count pass: a workgroup owns a tile of `tile` points (at most 4 per
-// lane) and histograms their entries over all bins in LDS.  On pair-mode levels the two
+// Binned backward, count pass: a workgroup of TPB lanes owns a tile of `tile` points (at
+// most 4 per lane) and histograms their entries over all bins in LDS.  On pair-mode levels the two
 // x-corners of each (y, z) corner pair make one entry (they always share a bin); elsewhere
 // each corner is its own entry.
-template <int D>
-__global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g, const BinPlan bp, int64_t n,
-                                                                    int32_t tile, int32_t nblk,
-                                                                    const float* __restrict__ x,
-                                                                    int32_t* __restrict__ counts) {
+template <int D, int TPB>
+__global__ __launch_bounds__(TPB) void dlinear_count_kernel(const Grid g, const BinPlan bp, int64_t n, int32_t tile,
+                                                            int32_t nblk, const float* __restrict__ x,
+                                                            int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
-  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) hist[i] = 0;
+  for (int i = threadIdx.x; i < bp.nbins; i += TPB) hist[i] = 0;
   __syncthreads();
-  const int ppt = tile / kBinThreads;
+  const int ppt = tile / TPB;
   const int64_t p0 = (int64_t)blk * tile + threadIdx.x;
   float xp[4][D];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t p = p0 + (int64_t)j * kBinThreads;
+    const int64_t p = p0 + (int64_t)j * TPB;
 #pragma unroll
     for (int i = 0; i < D; ++i) xp[j][i] = (j < ppt && p < n) ? x[p * D + i] : 0.0f;
   }
@@ -232,7 +231,7 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
     const bool few = bp.seg_bin0[l + 1] - bp.seg_bin0[l] <= kFewBins;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t p = p0 + (int64_t)j * kBinThreads;
+      const int64_t p = p0 + (int64_t)j * TPB;
       if (j >= ppt || p >= n) break;
       uint32_t base[D];
       float t[D];
@@ -257,10 +256,32 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) counts[(int64_t)blk * bp.nbins + i] = hist[i];
+  for (int i = threadIdx.x; i < bp.nbins; i += TPB) counts[(int64_t)blk * bp.nbins + i] = hist[i];
 }
 
-// Binned backward, scatter pass.  One lane per point.  At the start the workgroup turns the
+// G = up[l*F .. l*F + F) for a wave-uniform l < 32 / F: per feature, a tournament over the
+// 32 / F candidates on the bits of l (15 selects for F = 2), with compile-time register
+// indices only, since indexing the register array by l can demote it to scratch.
+template <int F>
+__device__ __forceinline__ void pick_group(const float (&up)[32], int l, float (&G)[F]) {
+  constexpr int K = 32 / F;
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    float c[K / 2 > 0 ? K / 2 : 1];
+    const bool top = (l & (K / 2)) != 0;
+#pragma unroll
+    for (int j = 0; j < K / 2; ++j) c[j] = top ? up[(j + K / 2) * F + f] : up[j * F + f];
+#pragma unroll
+    for (int half = K / 4; half >= 1; half /= 2) {
+      const bool hi = (l & half) != 0;
+#pragma unroll
+      for (int j = 0; j < half; ++j) c[j] = hi ? c[j + half] : c[j];
+    }
+    G[f] = c[0];
+  }
+}
+
+// Binned backward, scatter pass.  One lane per point (TPB = tile).  At the start the workgroup turns the
 // tile's per-bin counts (from the count pass) into an exclusive prefix over all bins, which
 // is both each bin's slot range in the LDS staging area (relative to the level's first bin)
 // and its cursor.  Per level, the tile's pair records are sorted by bin in LDS and then
@@ -270,8 +291,8 @@ __global__ __launch_bounds__(kBinThreads) void dlinear_count_kernel(const Grid g
 // PRE: the point's upstream row (Lrow*F <= 32 floats, a multiple of 4) is read once into
 // registers before the level loop; otherwise each level reads its F floats of the row, or of
 // the level-major upstream u_lm when given.
-template <int D, int F, bool PRE>
-__global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
+template <int D, int F, bool PRE, int TPB>
+__global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
     const Grid g, const BinPlan bp, int64_t n, int32_t tile, int32_t nblk, const float* __restrict__ x,
     const float* __restrict__ g_gamma, const float* __restrict__ u_lm, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
@@ -280,27 +301,31 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
   constexpr int R = 2 + F;          // floats per record
   extern __shared__ int32_t lds[];
   const int nbins = bp.nbins;
-  int32_t* gstart = lds;                  // [nbins] global slot of this tile's run in each bin
-  int32_t* excl = lds + nbins;            // [nbins] exclusive prefix of the tile's bin counts
-  int32_t* lcur = lds + 2 * nbins;        // [nbins] cursors (start at excl)
-  int32_t* wsum = lds + 3 * nbins;        // [kScatterThreads / 64]
+  // A record given slot s of bin b (s counts from the bin's first slot in the tile's
+  // exclusive prefix) goes to entry delta[b] + s: delta is the bin's global start for this
+  // tile minus that first slot.
+  int32_t* delta = lds;                   // [nbins]
+  int32_t* lcur = lds + nbins;            // [nbins] slot cursors: the tile's exclusive prefix
+  int32_t* wsum = lds + 2 * nbins;        // [TPB / 64]
+  int32_t* lbase = wsum + TPB / 64;  // [kMaxLevels] first staging slot of each level
   // staged records start 16-byte aligned so each record moves with the widest LDS access
-  float* st_rec = reinterpret_cast<float*>(lds + ((3 * nbins + kScatterThreads / 64 + 3) & ~3));  // [tile*NP*R]
-  int32_t* st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)tile * NP * R);                  // [tile*NP]
+  float* st_rec = reinterpret_cast<float*>(lds + ((2 * nbins + TPB / 64 + kMaxLevels + 3) & ~3));
+  int32_t* st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)tile * NP * R);  // [tile*NP]
 
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
   const int64_t p = (int64_t)blk * tile + threadIdx.x;
   const bool on = p < n;
   const int np = (int)min((int64_t)tile, n - (int64_t)blk * tile);
-  for (int i = threadIdx.x; i < nbins; i += kScatterThreads) {
+  for (int i = threadIdx.x; i < nbins; i += TPB) {
     const int32_t pre = counts[(int64_t)blk * nbins + i];
     const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)(blk + 1) * nbins + i] : totals[i];
-    gstart[i] = bin_start[i] + pre;
-    excl[i] = nxt - pre;
+    delta[i] = bin_start[i] + pre;
+    lcur[i] = nxt - pre;
   }
   __syncthreads();
-  block_exclusive_scan<kScatterThreads>(excl, nbins, wsum);
-  for (int i = threadIdx.x; i < nbins; i += kScatterThreads) lcur[i] = excl[i];
+  block_exclusive_scan<TPB>(lcur, nbins, wsum);
+  for (int i = threadIdx.x; i < nbins; i += TPB) delta[i] -= lcur[i];
+  for (int i = threadIdx.x; i < g.L; i += TPB) lbase[i] = lcur[bp.seg_bin0[i]];
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = on ? x[p * D + i] : 0.0f;
@@ -318,7 +343,7 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
   for (int l = 0; l < g.L; ++l) {
     const int32_t b0 = bp.seg_bin0[l];
     const int nb = bp.seg_bin0[l + 1] - b0;
-    const int32_t lbase = excl[b0];  // staging slots of this level start here
+    const int32_t lb = lbase[l];  // staging slots of this level start here
     const bool dense = (g.dense[0] >> l) & 1u;
     const bool pair = (bp.pair_mask >> l) & 1u;
     const bool few = nb <= kFewBins;
@@ -363,21 +388,21 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
                bin_of(bp, 0, l, corner_row<D, (Y << 1) | 1>(keys, dense, g.T[0], g.Tmask[0]), bn1, hi);
                if (pair) {
                  const int32_t s0 = few ? wave_aggregated_add<true>(lcur, bn0) : atomicAdd(&lcur[bn0], 1);
-                 const int32_t lp = s0 - lbase;
+                 const int32_t lp = s0 - lb;
                  rec[0] = __uint_as_float(lo | (hi << 16));
                  rec[1] = t[0];
                  store_vec<R>(st_rec + (int64_t)lp * R, rec);
-                 st_pos[lp] = gstart[bn0] + (s0 - excl[bn0]);
+                 st_pos[lp] = delta[bn0] + s0;
                } else {
                  // two single-corner records, lower row gets (1 - t) aG
                  const int32_t s0 = few ? wave_aggregated_add<true>(lcur, bn0) : atomicAdd(&lcur[bn0], 1);
                  rec[0] = __uint_as_float(lo | 0xFFFF0000u);
                  rec[1] = t[0];
-                 store_vec<R>(vseg + (int64_t)(gstart[bn0] + (s0 - excl[bn0]) - ebase) * R, rec);
+                 store_vec<R>(vseg + (int64_t)(delta[bn0] + s0 - ebase) * R, rec);
                  const int32_t s1 = few ? wave_aggregated_add<true>(lcur, bn1) : atomicAdd(&lcur[bn1], 1);
                  rec[0] = __uint_as_float(hi | 0xFFFF0000u);
                  rec[1] = 1.0f - t[0];
-                 store_vec<R>(vseg + (int64_t)(gstart[bn1] + (s1 - excl[bn1]) - ebase) * R, rec);
+                 store_vec<R>(vseg + (int64_t)(delta[bn1] + s1 - ebase) * R, rec);
                }
              }()),
          ...);
@@ -386,7 +411,7 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
     if (pair) {  // uniform over the workgroup
       __syncthreads();
       const int32_t total = np * NP;
-      for (int32_t q = threadIdx.x; q < total; q += kScatterThreads) {
+      for (int32_t q = threadIdx.x; q < total; q += TPB) {
         float rec[R];
         load_vec<R>(st_rec + (int64_t)q * R, rec);
         store_vec<R>(vseg + (int64_t)(st_pos[q] - ebase) * R, rec);
@@ -396,14 +421,14 @@ __global__ __launch_bounds__(kScatterThreads) void dlinear_scatter_kernel(
   }
 }
 
-template <int D, int F>
-hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, bool scatter,
-                      int64_t n, const float* x, const float* gg, const float* u_lm, hipStream_t s) {
+template <int D, int F, int TPB>
+hipError_t launch_bin_tile(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, bool scatter,
+                           int64_t n, const float* x, const float* gg, const float* u_lm, hipStream_t s) {
   const dim3 grid((unsigned)w.nblk);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
-  if (!scatter) {
-    hipLaunchKernelGGL((dlinear_count_kernel<D>), grid, dim3(kBinThreads), sizeof(int32_t) * (size_t)bp.nbins, s,
-                       g, bp, n, w.tile, w.nblk, x, counts);
+  if (!scatter) {  // two points per count lane
+    hipLaunchKernelGGL((dlinear_count_kernel<D, TPB / 2>), grid, dim3(TPB / 2), sizeof(int32_t) * (size_t)bp.nbins,
+                       s, g, bp, n, w.tile, w.nblk, x, counts);
     return hipGetLastError();
   }
   const size_t lds = dlinear_scatter_lds_bytes(bp, D, F, w.tile);
@@ -414,19 +439,29 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   // PRE reads the row as 16-byte pieces: rows of a multiple of 4 floats only, so that every
   // piece is aligned and inside the row
   if (!u_lm && g.Lrow * F <= 32 && (g.Lrow * F) % 4 == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, true>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, true, TPB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, true>), grid, dim3(kScatterThreads), lds, s, g, bp, n, w.tile,
-                       w.nblk, x, gg, nullptr, counts, totals, bin_start, st, vals);
+    hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, true, TPB>), grid, dim3(TPB), lds, s, g, bp, n, w.tile, w.nblk,
+                       x, gg, nullptr, counts, totals, bin_start, st, vals);
   } else {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, false>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, false, TPB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, false>), grid, dim3(kScatterThreads), lds, s, g, bp, n, w.tile,
+    hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, false, TPB>), grid, dim3(TPB), lds, s, g, bp, n, w.tile,
                        w.nblk, x, gg, u_lm, counts, totals, bin_start, st, vals);
   }
   return hipGetLastError();
+}
+
+template <int D, int F>
+hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, bool scatter,
+                      int64_t n, const float* x, const float* gg, const float* u_lm, hipStream_t s) {
+  if (w.tile == kScatterTileLarge)
+    return launch_bin_tile<D, F, kScatterTileLarge>(g, bp, w, ws, scatter, n, x, gg, u_lm, s);
+  if (w.tile == kScatterTileSmall)
+    return launch_bin_tile<D, F, kScatterTileSmall>(g, bp, w, ws, scatter, n, x, gg, u_lm, s);
+  return hipErrorInvalidValue;
 }
 
 template <int D, int F>

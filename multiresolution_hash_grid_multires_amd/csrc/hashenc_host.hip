@@ -521,4 +521,16 @@ int hashenc_diag_copy(const float* src, float* dst, int64_t n_floats, hashenc_st
   return ok();
 }
 
+int hashenc_diag_cache_read(const float* buf, int64_t n_floats, int32_t reps, float* out,
+                            hashenc_stream_t stream) {
+  if (n_floats <= 0 || n_floats % hg::cache_read_granule() != 0)
+    return fail(HASHENC_EINVAL, "hashenc_diag_cache_read: n_floats must be a positive multiple of 32");
+  if (reps < 1) return fail(HASHENC_EINVAL, "hashenc_diag_cache_read: reps must be at least 1");
+  if (!buf || !out) return fail(HASHENC_EINVAL, "hashenc_diag_cache_read: NULL pointer");
+  if (!aligned16(buf)) return fail(HASHENC_EALIGN, "hashenc_diag_cache_read: buf must be 16-byte aligned");
+  hipError_t e = hg::launch_cache_read(buf, n_floats, reps, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_diag_cache_read launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -170,6 +170,9 @@ hipError_t launch_rbf_backward(const Grid& g, int d, int F, int d2_mode, int64_t
 hipError_t launch_debug_indices(const Grid& g, int d, int order, int64_t n, const float* x,
                                 int32_t* out, hipStream_t s);
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t s);
+// n must be a multiple of cache_read_granule() floats
+int64_t cache_read_granule();
+hipError_t launch_cache_read(const float* buf, int64_t n, int32_t reps, float* out, hipStream_t s);
 // Zero columns [from, row_floats) of rows rows x row_floats floats (inactive levels).
 hipError_t launch_zero_columns(float* out, int64_t rows, int32_t row_floats, int32_t from, hipStream_t s);
 

@@ -132,6 +132,11 @@ def test_forward_backward_validation_before_launch():
     assert lib.hashenc_debug_indices(h, 5, a, 0, mis, None) == _lib.HASHENC_EALIGN
     assert lib.hashenc_diag_copy(a, mis, 8, None) == _lib.HASHENC_EALIGN
     assert lib.hashenc_diag_copy(a, b, -1, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_diag_cache_read(a, 33, 1, b, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_diag_cache_read(a, 0, 1, b, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_diag_cache_read(a, 64, 0, b, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_diag_cache_read(a, 64, 1, None, None) == _lib.HASHENC_EINVAL
+    assert lib.hashenc_diag_cache_read(mis, 64, 1, b, None) == _lib.HASHENC_EALIGN
     assert lib.hashenc_param_layout(h, 1, 0, None, None, None, None) == _lib.HASHENC_EINVAL
     assert lib.hashenc_param_layout(h, 0, 2, None, None, None, None) == _lib.HASHENC_EINVAL
 
