@@ -45,6 +45,7 @@ struct BinPlan {
   int32_t d, L, ntab, nseg, nbins;
   int32_t records;              // 1: d-linear records (2 + F floats); 0: Hermite (1 + W floats)
   int32_t max_seg_bins;         // most bins of any one segment
+  int32_t max_level_bins;       // most bins of the segments of any one level (all tables)
   int32_t width[kMaxTables];    // floats per row of table k
   int32_t cshift[kMaxTables];   // log2 rows per chunk of table k (power-of-two chunks)
   uint32_t pair_mask;           // d-linear: bit l set = level l uses x-corner pair records

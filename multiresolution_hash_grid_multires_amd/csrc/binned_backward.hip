@@ -335,6 +335,12 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
   }
   bp.seg_bin0[bp.nseg] = bin;
   bp.nbins = bin;
+  bp.max_level_bins = 0;
+  for (int l = 0; l < g.L; ++l) {
+    int32_t lb = 0;
+    for (int k = 0; k < bp.ntab; ++k) lb += bp.seg_bin0[k * g.L + l + 1] - bp.seg_bin0[k * g.L + l];
+    if (lb > bp.max_level_bins) bp.max_level_bins = lb;
+  }
   bp.fine_shift = -1;
   if (hermite) {
     bool uniform = true;
@@ -365,7 +371,7 @@ int bin_tile_points(const BinPlan& bp, int d, int F, bool hermite) {
 size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F) {
   const int P = hermite_scatter_points(F);
   const int rmax = hermite_rec_width((d == 3 ? 3 : 2) * F);  // widest order table's record
-  return sizeof(int32_t) * (3 * (size_t)bp.max_seg_bins + P / 64 + 3) +
+  return sizeof(int32_t) * (2 * (size_t)bp.max_level_bins + P / 64 + 3) +
          (size_t)P * (1 << d) * (sizeof(float) * rmax + sizeof(int32_t));
 }
 

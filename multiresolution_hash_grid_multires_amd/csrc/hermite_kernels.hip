@@ -788,33 +788,67 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
   }
 }
 
-// LDS layout of the Hermite scatter workgroup (P points).
+// LDS layout of the Hermite scatter workgroup (P points).  The bins of one level's segments
+// (order tables in turn) are held side by side.
 template <int D, int F, int P>
 struct HScatterLds {
   static constexpr int NC = 1 << D;
   static constexpr int RMAX = hermite_rec_width(binom_d(D, 1) * F);  // widest record (orders 1 and 2)
-  int32_t* gstart;  // [max_seg_bins] global slot of this tile's run in each bin of the segment
-  int32_t* excl;    // [max_seg_bins] exclusive prefix of the tile's counts
-  int32_t* lcur;    // [max_seg_bins] cursors
+  int32_t* delta;   // [max_level_bins] slot s of a bin goes to entry delta + s
+  int32_t* lcur;    // [max_level_bins] slot cursors: the tile's exclusive prefix over the level
   int32_t* wsum;    // [P / 64]
   float* st_rec;    // [P * NC * RMAX]
   int32_t* st_pos;  // [P * NC]
   __device__ HScatterLds(int32_t* lds, int mb) {
-    gstart = lds;
-    excl = lds + mb;
-    lcur = lds + 2 * mb;
-    wsum = lds + 3 * mb;
-    st_rec = reinterpret_cast<float*>(lds + ((3 * mb + P / 64 + 3) & ~3));  // 16-byte aligned
+    delta = lds;
+    lcur = lds + mb;
+    wsum = lds + 2 * mb;
+    st_rec = reinterpret_cast<float*>(lds + ((2 * mb + P / 64 + 3) & ~3));  // 16-byte aligned
     st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)P * NC * RMAX);
   }
 };
 
-// Stage the two records of corner pair (0, Y) for order table K.
+// Per level: the tile's slot ranges in every bin of the level's segments, from the count
+// pass (one round of global reads per level rather than one per order table).  base[k]:
+// the first slot of table k, so that table k's records take staging slots 0 .. np * NC.
+template <int D, int P>
+__device__ __forceinline__ void hermite_level_bins(const BinPlan& bp, int l, int blk, int nblk,
+                                                   const int32_t* __restrict__ counts,
+                                                   const int32_t* __restrict__ totals,
+                                                   const int32_t* __restrict__ bin_start, int32_t* delta,
+                                                   int32_t* lcur, int32_t* wsum, int32_t (&base)[D + 1]) {
+  int lo = 0;
+#pragma unroll
+  for (int k = 0; k <= D; ++k) {
+    const int32_t b0 = bp.seg_bin0[k * bp.L + l];
+    const int nb = bp.seg_bin0[k * bp.L + l + 1] - b0;
+    for (int i = threadIdx.x; i < nb; i += P) {
+      const int32_t pre = counts[(int64_t)blk * bp.nbins + b0 + i];
+      const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)(blk + 1) * bp.nbins + b0 + i] : totals[b0 + i];
+      delta[lo + i] = bin_start[b0 + i] + pre;
+      lcur[lo + i] = nxt - pre;
+    }
+    lo += nb;
+  }
+  __syncthreads();
+  block_exclusive_scan<P>(lcur, lo, wsum);
+  for (int i = threadIdx.x; i < lo; i += P) delta[i] -= lcur[i];
+  lo = 0;
+#pragma unroll
+  for (int k = 0; k <= D; ++k) {
+    base[k] = lcur[lo];  // before any cursor moves
+    lo += bp.seg_bin0[k * bp.L + l + 1] - bp.seg_bin0[k * bp.L + l];
+  }
+  __syncthreads();
+}
+
+// Stage the two records of corner pair (0, Y) for order table K.  lo_k: the table's first bin
+// in the level's LDS arrays; b0: its first global bin.
 template <int D, int F, int K, int Y>
 __device__ __forceinline__ void stage_pair(const Grid& g, const BinPlan& bp, int l, bool dense, bool few,
-                                           int32_t b0, const CellKeys<D>& keys, const AxisBasis (&ab)[D],
-                                           const LevelUp<D, F>& u, int32_t* lcur, const int32_t* excl,
-                                           const int32_t* gstart, float* st_rec, int32_t* st_pos) {
+                                           int32_t b0, int lo_k, int32_t base, const CellKeys<D>& keys,
+                                           const AxisBasis (&ab)[D], const LevelUp<D, F>& u, int32_t* lcur,
+                                           const int32_t* delta, float* st_rec, int32_t* st_pos) {
   constexpr int W = binom_d(D, K) * F;
   constexpr int R = hermite_rec_width(W);
   float v[2][W];
@@ -826,26 +860,25 @@ __device__ __forceinline__ void stage_pair(const Grid& g, const BinPlan& bp, int
     const uint32_t row = h ? corner_row<D, (Y << 1) | 1>(keys, dense, g.T[K], g.Tmask[K])
                            : corner_row<D, (Y << 1)>(keys, dense, g.T[K], g.Tmask[K]);
     bin_of(bp, K, l, row, bin, local);
-    const int i = bin - b0;
-    const int32_t slot = few ? wave_aggregated_add<true>(lcur, i) : atomicAdd(&lcur[i], 1);
+    const int i = lo_k + (bin - b0);
+    const int32_t slot = few ? wave_aggregated_add<true>(lcur + lo_k, bin - b0) : atomicAdd(&lcur[i], 1);
+    const int32_t lp = slot - base;
     float rec[R];
     rec[0] = __uint_as_float(local);
 #pragma unroll
     for (int j = 0; j < W; ++j) rec[1 + j] = v[h][j];
-    store_vec<R>(st_rec + (int64_t)slot * R, rec);
-    st_pos[slot] = gstart[i] + (slot - excl[i]);
+    store_vec<R>(st_rec + (int64_t)lp * R, rec);
+    st_pos[lp] = delta[i] + slot;
   }
 }
 
-// One (level, order table K) phase of the scatter workgroup.
+// One (level, order table K) phase of the scatter workgroup: stage the tile's table-K
+// records sorted by bin, then copy them out.
 template <int D, int F, int P, int K>
-__device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, int l, int blk, int nblk, bool on,
-                                              int np, const CellKeys<D>& keys, const AxisBasis (&ab)[D],
-                                              const LevelUp<D, F>& u, const int32_t* __restrict__ counts,
-                                              const int32_t* __restrict__ totals,
-                                              const int32_t* __restrict__ bin_start,
-                                              const BinState* __restrict__ st, float* __restrict__ vals_out,
-                                              const HScatterLds<D, F, P>& sh) {
+__device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, int l, bool on, int np, int lo_k,
+                                              int32_t base, const CellKeys<D>& keys, const AxisBasis (&ab)[D],
+                                              const LevelUp<D, F>& u, const BinState* __restrict__ st,
+                                              float* __restrict__ vals_out, const HScatterLds<D, F, P>& sh) {
   constexpr int W = binom_d(D, K) * F;
   constexpr int R = hermite_rec_width(W);
   constexpr int NC = 1 << D;
@@ -854,23 +887,15 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
   const int nb = bp.seg_bin0[sg + 1] - b0;
   const bool dense = (g.dense[K] >> l) & 1u;
   const bool few = nb <= kFewBins;
-  for (int i = threadIdx.x; i < nb; i += P) {
-    const int32_t pre = counts[(int64_t)blk * bp.nbins + b0 + i];
-    const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)(blk + 1) * bp.nbins + b0 + i] : totals[b0 + i];
-    sh.gstart[i] = bin_start[b0 + i] + pre;
-    sh.excl[i] = nxt - pre;
-  }
-  __syncthreads();
-  block_exclusive_scan<P>(sh.excl, nb, sh.wsum);
-  for (int i = threadIdx.x; i < nb; i += P) sh.lcur[i] = sh.excl[i];
-  __syncthreads();
   if (on) {
-    stage_pair<D, F, K, 0>(g, bp, l, dense, few, b0, keys, ab, u, sh.lcur, sh.excl, sh.gstart, sh.st_rec, sh.st_pos);
-    stage_pair<D, F, K, 1>(g, bp, l, dense, few, b0, keys, ab, u, sh.lcur, sh.excl, sh.gstart, sh.st_rec, sh.st_pos);
+    stage_pair<D, F, K, 0>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec,
+                           sh.st_pos);
+    stage_pair<D, F, K, 1>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec,
+                           sh.st_pos);
     if constexpr (D == 3) {
-      stage_pair<D, F, K, 2>(g, bp, l, dense, few, b0, keys, ab, u, sh.lcur, sh.excl, sh.gstart, sh.st_rec,
+      stage_pair<D, F, K, 2>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec,
                              sh.st_pos);
-      stage_pair<D, F, K, 3>(g, bp, l, dense, few, b0, keys, ab, u, sh.lcur, sh.excl, sh.gstart, sh.st_rec,
+      stage_pair<D, F, K, 3>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec,
                              sh.st_pos);
     }
   }
@@ -878,7 +903,8 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
   const int32_t ebase = st->seg_ebase[sg];
   float* vseg = vals_out + st->seg_vbase[sg];
   // copy out one record per lane: consecutive lanes hold consecutive records of a bin's run,
-  // so the R stores of a wavefront fill the run's lines between them
+  // so the R stores of a wavefront fill the run's lines between them (a word per lane, for
+  // whole-line stores, measured slower)
   const int32_t recs = np * NC;
   for (int32_t q = threadIdx.x; q < recs; q += P) {
     float v[R];
@@ -891,11 +917,11 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
   __syncthreads();
 }
 
-// Binned backward, scatter pass.  One lane per point of a P-point tile.  Per level and
-// order table K, the tile's records {local row, W values} are computed (table K's part of
-// the pair reverse), sorted by bin in LDS (slots from the tile's exclusive prefix of its
-// per-bin counts) and copied out as flat words: consecutive lanes write consecutive words
-// of each bin's contiguous run, so lines are written whole apart from run ends.
+// Binned backward, scatter pass.  One lane per point of a P-point tile.  Per level the tile's
+// slot ranges in all of the level's bins are set up at once; then per order table K the
+// tile's records {local row, W values} are computed (table K's part of the pair reverse),
+// sorted by bin in LDS and copied out as flat words: consecutive lanes write consecutive
+// words of each bin's contiguous run, so lines are written whole apart from run ends.
 template <int D, int F, int P>
 __global__ __launch_bounds__(P) void hermite_scatter_kernel(
     const Grid g, const BinPlan bp, int64_t n, int32_t nblk, bool diag, const float* __restrict__ x,
@@ -903,7 +929,7 @@ __global__ __launch_bounds__(P) void hermite_scatter_kernel(
     const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
     const BinState* __restrict__ st, float* __restrict__ vals_out) {
   extern __shared__ int32_t lds[];
-  const HScatterLds<D, F, P> sh(lds, bp.max_seg_bins);
+  const HScatterLds<D, F, P> sh(lds, bp.max_level_bins);
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
   const int64_t p = (int64_t)blk * P + threadIdx.x;
   const bool on = p < n;
@@ -919,12 +945,18 @@ __global__ __launch_bounds__(P) void hermite_scatter_kernel(
       u = load_level_up_lm<D, F>(U, n, p, l, diag);
       level_setup<D>(g, l, xp, keys, ab);
     }
-    scatter_table<D, F, P, 0>(g, bp, l, blk, nblk, on, np, keys, ab, u, counts, totals, bin_start, st, vals_out, sh);
-    scatter_table<D, F, P, 1>(g, bp, l, blk, nblk, on, np, keys, ab, u, counts, totals, bin_start, st, vals_out, sh);
-    scatter_table<D, F, P, 2>(g, bp, l, blk, nblk, on, np, keys, ab, u, counts, totals, bin_start, st, vals_out, sh);
-    if constexpr (D == 3)
-      scatter_table<D, F, P, 3>(g, bp, l, blk, nblk, on, np, keys, ab, u, counts, totals, bin_start, st, vals_out,
-                                sh);
+    int32_t base[D + 1];
+    hermite_level_bins<D, P>(bp, l, blk, nblk, counts, totals, bin_start, sh.delta, sh.lcur, sh.wsum, base);
+    int lo = 0;
+    scatter_table<D, F, P, 0>(g, bp, l, on, np, lo, base[0], keys, ab, u, st, vals_out, sh);
+    lo += bp.seg_bin0[l + 1] - bp.seg_bin0[l];
+    scatter_table<D, F, P, 1>(g, bp, l, on, np, lo, base[1], keys, ab, u, st, vals_out, sh);
+    lo += bp.seg_bin0[bp.L + l + 1] - bp.seg_bin0[bp.L + l];
+    scatter_table<D, F, P, 2>(g, bp, l, on, np, lo, base[2], keys, ab, u, st, vals_out, sh);
+    if constexpr (D == 3) {
+      lo += bp.seg_bin0[2 * bp.L + l + 1] - bp.seg_bin0[2 * bp.L + l];
+      scatter_table<D, F, P, 3>(g, bp, l, on, np, lo, base[3], keys, ab, u, st, vals_out, sh);
+    }
   }
 }
 
