@@ -60,6 +60,9 @@ struct BinPlan {
 
 // Floats per Hermite record of a W-wide row: the row word and the W values.
 __host__ __device__ constexpr int hermite_rec_width(int W) { return W + 1; }
+// Floats per record in the scatter's LDS staging: the record, its entry index and padding to
+// a whole number of 16-byte words, so a record moves with 16-byte LDS accesses.
+__host__ __device__ constexpr int hermite_stage_width(int W) { return (hermite_rec_width(W) + 1 + 3) & ~3; }
 // Value floats of every segment start on a 128-byte boundary.
 constexpr int64_t kSegAlignFloats = 32;
 

@@ -370,9 +370,8 @@ int bin_tile_points(const BinPlan& bp, int d, int F, bool hermite) {
 
 size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F) {
   const int P = hermite_scatter_points(F);
-  const int rmax = hermite_rec_width((d == 3 ? 3 : 2) * F);  // widest order table's record
-  return sizeof(int32_t) * (2 * (size_t)bp.max_level_bins + P / 64 + 3) +
-         (size_t)P * (1 << d) * (sizeof(float) * rmax + sizeof(int32_t));
+  const int smax = hermite_stage_width((d == 3 ? 3 : 2) * F);  // widest order table's staged record
+  return sizeof(int32_t) * (2 * (size_t)bp.max_level_bins + P / 64 + 3) + (size_t)P * (1 << d) * sizeof(float) * smax;
 }
 
 size_t dlinear_scatter_lds_bytes(const BinPlan& bp, int d, int F, int tile) {

@@ -792,19 +792,15 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
 // (order tables in turn) are held side by side.
 template <int D, int F, int P>
 struct HScatterLds {
-  static constexpr int NC = 1 << D;
-  static constexpr int RMAX = hermite_rec_width(binom_d(D, 1) * F);  // widest record (orders 1 and 2)
   int32_t* delta;   // [max_level_bins] slot s of a bin goes to entry delta + s
   int32_t* lcur;    // [max_level_bins] slot cursors: the tile's exclusive prefix over the level
   int32_t* wsum;    // [P / 64]
-  float* st_rec;    // [P * NC * RMAX]
-  int32_t* st_pos;  // [P * NC]
+  float* st_rec;    // [P * 2^D * widest staged record]
   __device__ HScatterLds(int32_t* lds, int mb) {
     delta = lds;
     lcur = lds + mb;
     wsum = lds + 2 * mb;
     st_rec = reinterpret_cast<float*>(lds + ((2 * mb + P / 64 + 3) & ~3));  // 16-byte aligned
-    st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)P * NC * RMAX);
   }
 };
 
@@ -848,9 +844,10 @@ template <int D, int F, int K, int Y>
 __device__ __forceinline__ void stage_pair(const Grid& g, const BinPlan& bp, int l, bool dense, bool few,
                                            int32_t b0, int lo_k, int32_t base, const CellKeys<D>& keys,
                                            const AxisBasis (&ab)[D], const LevelUp<D, F>& u, int32_t* lcur,
-                                           const int32_t* delta, float* st_rec, int32_t* st_pos) {
+                                           const int32_t* delta, float* st_rec) {
   constexpr int W = binom_d(D, K) * F;
   constexpr int R = hermite_rec_width(W);
+  constexpr int RS = hermite_stage_width(W);
   float v[2][W];
   bwd_pair_table<D, F, Y, K>(ab, u, v[0], v[1]);
 #pragma unroll
@@ -863,12 +860,14 @@ __device__ __forceinline__ void stage_pair(const Grid& g, const BinPlan& bp, int
     const int i = lo_k + (bin - b0);
     const int32_t slot = few ? wave_aggregated_add<true>(lcur + lo_k, bin - b0) : atomicAdd(&lcur[i], 1);
     const int32_t lp = slot - base;
-    float rec[R];
+    float rec[RS];
     rec[0] = __uint_as_float(local);
 #pragma unroll
     for (int j = 0; j < W; ++j) rec[1 + j] = v[h][j];
-    store_vec<R>(st_rec + (int64_t)lp * R, rec);
-    st_pos[lp] = delta[i] + slot;
+    rec[R] = __int_as_float(delta[i] + slot);  // the record's entry in the segment
+#pragma unroll
+    for (int j = R + 1; j < RS; ++j) rec[j] = 0.0f;
+    store_vec<RS>(st_rec + (int64_t)lp * RS, rec);
   }
 }
 
@@ -881,6 +880,7 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
                                               float* __restrict__ vals_out, const HScatterLds<D, F, P>& sh) {
   constexpr int W = binom_d(D, K) * F;
   constexpr int R = hermite_rec_width(W);
+  constexpr int RS = hermite_stage_width(W);
   constexpr int NC = 1 << D;
   const int sg = K * bp.L + l;
   const int32_t b0 = bp.seg_bin0[sg];
@@ -888,15 +888,11 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
   const bool dense = (g.dense[K] >> l) & 1u;
   const bool few = nb <= kFewBins;
   if (on) {
-    stage_pair<D, F, K, 0>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec,
-                           sh.st_pos);
-    stage_pair<D, F, K, 1>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec,
-                           sh.st_pos);
+    stage_pair<D, F, K, 0>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec);
+    stage_pair<D, F, K, 1>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec);
     if constexpr (D == 3) {
-      stage_pair<D, F, K, 2>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec,
-                             sh.st_pos);
-      stage_pair<D, F, K, 3>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec,
-                             sh.st_pos);
+      stage_pair<D, F, K, 2>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec);
+      stage_pair<D, F, K, 3>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec);
     }
   }
   __syncthreads();
@@ -907,10 +903,9 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
   // whole-line stores, measured slower)
   const int32_t recs = np * NC;
   for (int32_t q = threadIdx.x; q < recs; q += P) {
-    float v[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) v[j] = sh.st_rec[(int64_t)q * R + j];
-    float* dst = vseg + (int64_t)(sh.st_pos[q] - ebase) * R;
+    float v[RS];
+    load_vec<RS>(sh.st_rec + (int64_t)q * RS, v);
+    float* dst = vseg + (int64_t)(__float_as_int(v[R]) - ebase) * R;
 #pragma unroll
     for (int j = 0; j < R; ++j) dst[j] = v[j];
   }
