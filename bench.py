@@ -34,10 +34,10 @@ HEADLINE = "dlinear3d_L16_T19"
 # were taken on (the per-kernel figures and commands are in profiles/); drop an entry when
 # one of its kernels changes.
 MEASURED_TRAFFIC_BYTES: dict = {
-    ("dlinear3d_L16_T19", "forward"): 1427618997,
-    # ("dlinear3d_L16_T19", "backward"): not re-counted since its scatter kernel last changed
-    ("hermite3d_L16_T19", "forward"): 11965429459,
-    # ("hermite3d_L16_T19", "backward"): not re-counted since its scatter kernel last changed
+    ("dlinear3d_L16_T19", "forward"): 1428051724,
+    ("dlinear3d_L16_T19", "backward"): 2511861086,
+    ("hermite3d_L16_T19", "forward"): 11965668966,
+    ("hermite3d_L16_T19", "backward"): 28523739466,
 }
 
 
@@ -117,6 +117,25 @@ def cache_read_calibration(args, torch, api) -> int:
     ms = a.elapsed_time(b) / args.steps
     print(json.dumps({"cache_bytes": 4 * n, "reps": args.cache_reps, "ms": round(ms, 4),
                       "read_GBps": round(4 * n * args.cache_reps / ms / 1e6, 1)}), flush=True)
+    return 0
+
+
+def fill_calibration(args, torch) -> int:
+    """Write-only bandwidth: torch's fill of --fill-bytes bytes (a buffer far larger than the
+    Infinity Cache, so the writes reach HBM)."""
+    buf = torch.empty(args.fill_bytes // 4, device="cuda:0")
+    for _ in range(args.warmup):
+        buf.fill_(1.0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        buf.fill_(1.0)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"fill_bytes": 4 * buf.numel(), "ms": round(ms, 4),
+                      "write_GBps": round(4 * buf.numel() / ms / 1e6, 1)}), flush=True)
     return 0
 
 
@@ -258,6 +277,8 @@ def main() -> int:
                     help="instead of the benchmark, read this many bytes (split over the 8 XCDs' L2s) "
                          "--cache-reps times per launch: the L2 read ceiling")
     ap.add_argument("--cache-reps", type=int, default=200)
+    ap.add_argument("--fill-bytes", type=int, default=0,
+                    help="instead of the benchmark, time torch's fill of this many bytes (write-only bandwidth)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     args = ap.parse_args()
@@ -275,6 +296,8 @@ def main() -> int:
         return copy_calibration(args, torch, api)
     if args.cache_bytes:
         return cache_read_calibration(args, torch, api)
+    if args.fill_bytes:
+        return fill_calibration(args, torch)
 
     W = I.WORKLOADS[args.workload]
     if args.active_levels:
