@@ -139,6 +139,34 @@ def fill_calibration(args, torch) -> int:
     return 0
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def single_thread_rate(O, spec, x_h, params_h, ups_h, n_params, sec_per_point: float) -> dict:
+    """The same oracle on one thread, over a prefix sized from the multi-thread rate to take
+    about two seconds."""
+    threads = O.max_threads()
+    m = max(1, min(x_h.shape[0], int(2.0 / max(sec_per_point * threads, 1e-12))))
+    O.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        O.forward(spec, x_h[:m], params_h)
+        O.backward(spec, x_h[:m], *[u[:m] for u in ups_h], n_params=n_params)
+        dt = time.perf_counter() - t0
+    finally:
+        O.set_threads(threads)
+    return {"value": round(m / dt, 1), "unit": "points/s", "cores": 1,
+            "sample": f"the first {m} points of the same workload, one fwd+bwd", "seconds": round(dt, 2)}
+
+
 def mlp_flops_per_point(d: int, n_in: int, hidden: int, depth: int) -> int:
     """Multiply-add FLOPs of the SIREN part per point: forward mode carries d + 2 rows
     (value, d gradients, Laplacian) through every layer; the reverse sweep costs one product
@@ -238,7 +266,7 @@ def residual_bench(args, torch, api, I, W) -> int:
             k = min(n, int(k * min(16.0, max(2.0, 0.5 * args.cpu_seconds / max(dt, 1e-3)))))
         cpu = {"value": round(k / dt, 1), "unit": "points/s", "cores": O.max_threads(), "kind": "oracle",
                "sample": f"the first {k} of the {n} points of the same workload, one step (fp64 oracle)",
-               "seconds": round(dt, 2)}
+               "seconds": round(dt, 2), "cpu_model": cpu_model()}
 
     what = "INGP-FD comparator steps" if fd else "PINN residual steps"
     print(json.dumps({
@@ -415,7 +443,9 @@ def main() -> int:
         what = (f"all {n} points of the same workload, one fwd+bwd, repeated {reps} times" if m == n
                 else f"the first {m} of the {n} points of the same workload, one fwd+bwd")
         cpu = {"value": round(reps * m / total, 1), "unit": "points/s", "cores": O.max_threads(),
-               "kind": "oracle", "sample": what + " (fp64-accumulating oracle)", "seconds": round(total, 2)}
+               "kind": "oracle", "sample": what + " (fp64-accumulating oracle, not a tuned CPU encoder)",
+               "seconds": round(total, 2), "cpu_model": cpu_model(),
+               "single_thread": single_thread_rate(O, spec, x_h, params_h, ups_h, enc.n_params, total / reps / m)}
 
     metric = METRIC if args.workload == HEADLINE else f"encoded points/s fwd+bwd ({args.workload})"
     if args.active_levels:

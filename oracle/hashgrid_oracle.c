@@ -838,3 +838,12 @@ int orc_max_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads for the following calls (timing only; results do not depend on it). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

@@ -91,6 +91,8 @@ def _load():
         lib.orc_c2f_active.restype = ctypes.c_int32
         lib.orc_max_threads.argtypes = []
         lib.orc_max_threads.restype = ctypes.c_int
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -220,6 +222,11 @@ def c2f_active_levels(L: int, L0: int, t: int, tau: int) -> int:
 
 def max_threads() -> int:
     return int(_load().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle uses from now on (for timing; results do not depend on it)."""
+    _load().orc_set_threads(int(n))
 
 
 def mlp_param_count(n_in: int, hidden: int, depth: int) -> int:
