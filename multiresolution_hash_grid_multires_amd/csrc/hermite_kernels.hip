@@ -285,9 +285,11 @@ __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
     const Grid g, const PackPlan pp, int64_t n, int32_t n_tiles, int d2_mode, const float* __restrict__ x,
     const float* __restrict__ params, float* __restrict__ gamma, float* __restrict__ dgamma,
     float* __restrict__ d2gamma, float* __restrict__ stage) {
+  constexpr int PTS = kBlock / 2;  // points per workgroup: two lanes per point
   const int l = blockIdx.x / n_tiles;
-  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
-  if (p >= n) return;
+  const int half = threadIdx.x & 1;  // which half of the cell's x-corner pairs this lane gathers
+  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * PTS + (threadIdx.x >> 1);
+  if (p >= n) return;  // both lanes of a point leave together
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
@@ -309,12 +311,28 @@ __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
     for (int i = 0; i < D; ++i) o.g[i][f] = o.h[i][f] = 0.0f;
   }
   const float* pbase = PACKED ? params + pp.poff[l] : nullptr;
-  fwd_pair<D, F, 0, PACKED>(g, keys, ts, pbase, ab, o);
-  fwd_pair<D, F, 1, PACKED>(g, keys, ts, pbase, ab, o);
-  if constexpr (D == 3) {
+  // lane 0 of the point: pairs 0 .. NP/2 - 1, lane 1: the rest; the partial sums meet through
+  // one cross-lane add per output value (fewer registers per lane, twice the wavefronts in
+  // flight on the gathers)
+  if (half == 0) {
+    fwd_pair<D, F, 0, PACKED>(g, keys, ts, pbase, ab, o);
+    if constexpr (D == 3) fwd_pair<D, F, 1, PACKED>(g, keys, ts, pbase, ab, o);
+  } else if constexpr (D == 3) {
     fwd_pair<D, F, 2, PACKED>(g, keys, ts, pbase, ab, o);
     fwd_pair<D, F, 3, PACKED>(g, keys, ts, pbase, ab, o);
+  } else {
+    fwd_pair<D, F, 1, PACKED>(g, keys, ts, pbase, ab, o);
   }
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    o.v[f] += __shfl_xor(o.v[f], 1, 64);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      o.g[i][f] += __shfl_xor(o.g[i][f], 1, 64);
+      o.h[i][f] += __shfl_xor(o.h[i][f], 1, 64);
+    }
+  }
+  if (half) return;
   if constexpr (LM) {
     const bool diag = d2_mode == HASHENC_D2_DIAG;
     const int M = 1 + D + (diag ? D : 1);
@@ -1035,7 +1053,7 @@ template <int D, int F>
 hipError_t launch_fwd(const Grid& g, int d2_mode, int64_t n, const float* x, const float* params,
                       const float* packed, float* stage, bool to_rows, float* gamma, float* dgamma,
                       float* d2gamma, hipStream_t s) {
-  const int64_t tiles = (n + kBlock - 1) / kBlock;
+  const int64_t tiles = (n + kBlock / 2 - 1) / (kBlock / 2);  // two lanes per point
   if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles * g.L));
   const PackPlan pp = make_pack_plan(g, D, F);
@@ -1175,9 +1193,11 @@ __global__ __launch_bounds__(kBlock) void hermite4_forward_kernel(const Grid g, 
                                                                   float* __restrict__ dgamma,
                                                                   float* __restrict__ d2gamma) {
   constexpr int D = 4;
+  constexpr int PTS = kBlock / 2;  // points per workgroup: two lanes per point
   const int l = blockIdx.x / n_tiles;
-  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
-  if (p >= n) return;
+  const int half = threadIdx.x & 1;  // which half of the cell's x-corner pairs this lane gathers
+  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * PTS + (threadIdx.x >> 1);
+  if (p >= n) return;  // both lanes of a point leave together
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
