@@ -34,11 +34,11 @@ struct FwdPlan {
   uint8_t last[kMaxLevels];
 };
 
-FwdPlan make_fwd_plan(const Grid& g, int d, int F, bool group) {
+FwdPlan make_fwd_plan(const Grid& g, int d, int F, bool group, int first = 0) {
   FwdPlan fp;
   fp.n_pass = 0;
   int64_t group_bytes = 0;
-  for (int l = 0; l < g.L; ++l) {
+  for (int l = first; l < g.L; ++l) {
     int64_t rows = g.T[0];
     if ((g.dense[0] >> l) & 1u) {
       rows = 1;
@@ -55,6 +55,106 @@ FwdPlan make_fwd_plan(const Grid& g, int d, int F, bool group) {
     group_bytes = bytes;
   }
   return fp;
+}
+
+// Coarse levels from LDS.  The leading dense levels whose tables fit in LDS together
+// (kFwdLdsBytes) are interpolated by one persistent workgroup per CU that copies those
+// tables into LDS once and walks its share of the points: these levels then issue no L2
+// request per point, and the L2 request rate is what bounds the gather (four line requests
+// per point and level).
+constexpr int64_t kFwdLdsBytes = 144 * 1024;
+constexpr int kFwdLdsThreads = 1024;
+
+int fwd_lds_levels(const Grid& g, int d, int F) {
+  int64_t bytes = 0;
+  int c = 0;
+  for (int l = 0; l < g.L; ++l) {
+    if (!((g.dense[0] >> l) & 1u)) break;
+    int64_t rows = 1;
+    for (int i = 0; i < d; ++i) rows *= (int64_t)g.N[l] + 1;
+    if (bytes + rows * F * (int64_t)sizeof(float) > kFwdLdsBytes) break;
+    bytes += rows * F * (int64_t)sizeof(float);
+    ++c;
+  }
+  return c;
+}
+
+// Levels 0 .. Lc-1 (dense, contiguous in the parameter array) into the level-major staging.
+// Two lanes per point as in the L2 gather; both lanes of a point run the same iterations.
+template <int D, int F>
+__global__ __launch_bounds__(kFwdLdsThreads) void dlinear_forward_lds_kernel(const Grid g, int32_t Lc,
+                                                                          int32_t nfloats, int64_t n,
+                                                                          const float* __restrict__ x,
+                                                                          const float* __restrict__ params,
+                                                                          float* __restrict__ stage) {
+  extern __shared__ float tab[];
+  // table copy in 16-byte pieces, four loads in flight per thread (table 0 level 0 starts at
+  // the 16-byte aligned start of the parameters)
+  {
+    const float4* src4 = reinterpret_cast<const float4*>(params + g.off[0][0]);
+    float4* tab4 = reinterpret_cast<float4*>(tab);
+    const int n4 = nfloats >> 2;
+    for (int i = threadIdx.x; i < n4; i += 4 * kFwdLdsThreads) {
+      const int i1 = i + kFwdLdsThreads, i2 = i + 2 * kFwdLdsThreads, i3 = i + 3 * kFwdLdsThreads;
+      const float4 a0 = src4[i];
+      const float4 a1 = src4[min(i1, n4 - 1)];
+      const float4 a2 = src4[min(i2, n4 - 1)];
+      const float4 a3 = src4[min(i3, n4 - 1)];
+      tab4[i] = a0;
+      if (i1 < n4) tab4[i1] = a1;
+      if (i2 < n4) tab4[i2] = a2;
+      if (i3 < n4) tab4[i3] = a3;
+    }
+    for (int i = 4 * n4 + threadIdx.x; i < nfloats; i += kFwdLdsThreads) tab[i] = params[g.off[0][0] + i];
+  }
+  __syncthreads();
+  constexpr int PTS = kFwdLdsThreads / 2;
+  const int c0 = threadIdx.x & 1;
+  const int64_t stride = (int64_t)gridDim.x * PTS;
+  int64_t p = (int64_t)blockIdx.x * PTS + (threadIdx.x >> 1);
+  float xn[D];  // the next point's coordinates, loaded one iteration ahead
+#pragma unroll
+  for (int i = 0; i < D; ++i) xn[i] = p < n ? x[p * D + i] : 0.0f;
+  for (; p < n; p += stride) {
+    float xp[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      xp[i] = xn[i];
+      xn[i] = p + stride < n ? x[(p + stride) * D + i] : 0.0f;
+    }
+    int32_t loff = 0;  // the level's table in LDS
+    for (int l = 0; l < Lc; ++l) {
+      uint32_t base[D];
+      float t[D];
+      locate<D>(xp, g.N[l], g.Nf[l], base, t);
+      const CellKeys<D> keys = cell_keys<D>(base, g.N[l]);
+      constexpr int NP = 1 << (D - 1);
+      float acc[F];
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[f] = 0.0f;
+      const float wx = c0 ? t[0] : 1.0f - t[0];
+      [&]<int... Y>(std::integer_sequence<int, Y...>) {
+        ((
+             [&] {
+               const uint32_t r = c0 ? corner_row<D, (Y << 1) | 1>(keys, true, g.T[0], g.Tmask[0])
+                                     : corner_row<D, (Y << 1)>(keys, true, g.T[0], g.Tmask[0]);
+               float w = wx;
+#pragma unroll
+               for (int i = 1; i < D; ++i) w *= ((Y >> (i - 1)) & 1) ? t[i] : 1.0f - t[i];
+#pragma unroll
+               for (int f = 0; f < F; ++f) acc[f] = fmaf(w, tab[loff + (int32_t)r * F + f], acc[f]);
+             }()),
+         ...);
+      }(std::make_integer_sequence<int, NP>{});
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[f] += __shfl_xor(acc[f], 1, 64);
+      if (c0 == 0) store_vec<F>(stage + ((int64_t)l * n + p) * F, acc);
+      int32_t rows = 1;
+#pragma unroll
+      for (int i = 0; i < D; ++i) rows *= g.N[l] + 1;
+      loff += rows * F;
+    }
+  }
 }
 
 // Two lanes per point: lane c0 gathers the 2^(d-1) corners with x-bit c0, so the two corners
@@ -468,7 +568,9 @@ template <int D, int F>
 hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* params, float* gamma,
                       float* scratch, hipStream_t s) {
   const int64_t tiles = (n + kBlock / 2 - 1) / (kBlock / 2);  // two lanes per point
-  const FwdPlan fp = make_fwd_plan(g, D, F, scratch != nullptr);
+  // with the level-major staging, the leading dense levels that fit in LDS go to the LDS kernel
+  const int Lc = scratch ? fwd_lds_levels(g, D, F) : 0;
+  const FwdPlan fp = make_fwd_plan(g, D, F, scratch != nullptr, Lc);
   if (tiles * fp.n_pass > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles * fp.n_pass));
   if (!scratch) {
@@ -478,9 +580,29 @@ hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* par
     if (e != hipSuccess || g.L == g.Lrow) return e;
     return launch_zero_columns(gamma, n, g.Lrow * F, g.L * F, s);
   }
-  hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, fp, n, (int32_t)tiles, x,
-                     params, scratch);
-  hipError_t e = hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (Lc > 0 && n > 0) {
+    int32_t nfl = 0;
+    for (int l = 0; l < Lc; ++l) {
+      int32_t rows = 1;
+      for (int i = 0; i < D; ++i) rows *= g.N[l] + 1;
+      nfl += rows * F;
+    }
+    const size_t lds = sizeof(float) * (size_t)nfl;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_forward_lds_kernel<D, F>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = std::min<int64_t>(256, (n + kFwdLdsThreads / 2 - 1) / (kFwdLdsThreads / 2));
+    hipLaunchKernelGGL((dlinear_forward_lds_kernel<D, F>), dim3((unsigned)blocks), dim3(kFwdLdsThreads), lds, s, g,
+                       (int32_t)Lc, nfl, n, x, params, scratch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (fp.n_pass > 0) {
+    hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, fp, n, (int32_t)tiles, x,
+                       params, scratch);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess || !gamma) return e;  // no gamma: the level-major staging is the output
   const int32_t P = g.L * F <= 128 ? 64 : 32;  // LDS tile at most 32 x 257 floats
   const size_t lds = sizeof(float) * (size_t)P * (g.L * F + 1);
