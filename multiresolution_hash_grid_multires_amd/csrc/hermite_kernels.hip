@@ -1193,11 +1193,9 @@ __global__ __launch_bounds__(kBlock) void hermite4_forward_kernel(const Grid g, 
                                                                   float* __restrict__ dgamma,
                                                                   float* __restrict__ d2gamma) {
   constexpr int D = 4;
-  constexpr int PTS = kBlock / 2;  // points per workgroup: two lanes per point
   const int l = blockIdx.x / n_tiles;
-  const int half = threadIdx.x & 1;  // which half of the cell's x-corner pairs this lane gathers
-  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * PTS + (threadIdx.x >> 1);
-  if (p >= n) return;  // both lanes of a point leave together
+  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * kBlock + threadIdx.x;
+  if (p >= n) return;
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
