@@ -161,8 +161,10 @@ __device__ inline void block_exclusive_scan(int32_t* v, int n, int32_t* wsum) {
   __syncthreads();
 }
 
-// Levels with at most this many bins use the wavefront-aggregated counters.
-constexpr int kFewBins = 16;
+// Levels with at most this many bins use the wavefront-aggregated counters (with more, one
+// LDS atomic per lane measured faster: at 16 the aggregation loop cost the config-3 count
+// and scatter 25 us and the config-4 count and scatter 127 us).
+constexpr int kFewBins = 4;
 
 // Bin of a row of segment (k, l) and its row inside the chunk.
 __device__ __forceinline__ void bin_of(const BinPlan& bp, int k, int l, uint32_t row, int32_t& bin,
