@@ -8,7 +8,7 @@ namespace hg {
 
 constexpr int kMaxBinTables = 4;                  // the binned backward covers d <= 3
 constexpr int kMaxSeg = kMaxBinTables * kMaxLevels;  // segment s = table k * L + level l
-constexpr int kBinLdsValues = 8192;               // 64 KB fp64 LDS accumulator per work item
+constexpr int kBinLdsValues = 16384;              // 128 KB fp64 LDS accumulator per work item
 constexpr int kBinTilePoints = 1024;              // points per count / scatter workgroup (max)
 constexpr int kBinThreads = 256;
 constexpr int kBinItemEntries = 1 << 18;          // entries per reduce work item (at most)
@@ -22,8 +22,8 @@ inline int32_t bin_item_entries(int64_t entries) {
   if (e > kBinItemEntries) e = kBinItemEntries;
   return (int32_t)e;
 }
-constexpr int kReduceThreads = 512;
-constexpr int kBinReduceBlocks = 512;             // persistent reduce workgroups (2 per CU)
+constexpr int kReduceThreads = 1024;
+constexpr int kBinReduceBlocks = 256;             // persistent reduce workgroups (1 per CU)
 // d-linear scatter workgroup = tile: one point per lane.  Larger tiles give each bin longer
 // runs per tile (whole lines written); the larger size is used when its LDS staging fits.
 constexpr int kScatterTileLarge = 1024;

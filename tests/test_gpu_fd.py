@@ -125,14 +125,14 @@ def test_fd_with_active_levels(orc):
 def test_fd_atomic_backward_path(orc):
     # a table too large for the binned backward's LDS counters: the fp32-atomic backward reads
     # the SIREN kernel's level-major upstream
-    # (five hashed levels of 2048 bins each: the scatter's per-bin LDS arrays exceed the budget)
-    spec = {"d": 3, "L": 5, "F": 8, "kind": "dlinear", "T": [1 << 21], "n_min": 128, "n_max": 4096}
+    # (eight hashed levels of 1024 bins each: the scatter's per-bin LDS arrays exceed the budget)
+    spec = {"d": 3, "L": 8, "F": 8, "kind": "dlinear", "T": [1 << 21], "n_min": 128, "n_max": 4096}
     h = api.hashenc_create(spec)
     assert api.hashenc_backward_workspace_size(h, 1000) == 0
     lay = orc.layout(spec)
     rng = np.random.default_rng(41)
     params = (0.3 * rng.standard_normal(lay["n_params"])).astype(np.float32)
-    mlp_params = I.siren_mlp(13, 40, 32, 1)
+    mlp_params = I.siren_mlp(13, 64, 32, 1)
     x = rng.random((600, 3), dtype=np.float32)
     _compare(orc, spec, 32, 1, 3.0, 2.0 ** -5, x, params, mlp_params)
 
