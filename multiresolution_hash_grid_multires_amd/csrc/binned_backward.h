@@ -187,7 +187,7 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp);
 int bin_tile_points(const BinPlan& bp, int d, int F, bool hermite);
 // Points (= threads) of a Hermite scatter workgroup: its LDS staging holds one order table's
 // records for every corner of the tile.
-constexpr int hermite_scatter_points(int F) { return F <= 2 ? 256 : F == 4 ? 128 : 64; }
+constexpr int hermite_scatter_points(int F) { return F <= 2 ? 512 : F == 4 ? 128 : 64; }
 size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F);
 // LDS of the d-linear scatter workgroup: two per-bin arrays, the per-level staging bases and
 // the pair-record staging.
