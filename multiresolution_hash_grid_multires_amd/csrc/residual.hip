@@ -452,6 +452,7 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
 
     // forward mode
     mf4 z[DEPTH][R];  // tape: the wavefront's neurons
+    float sn[DEPTH][4], cs[DEPTH][4];  // sin and cos of omega z, reused by the reverse sweep
     float alap[4];
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) {
@@ -481,6 +482,8 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
       for (int i = 0; i < 4; ++i) {
         float s, c;
         sincosf(om * acc[0][i], &s, &c);
+        sn[k][i] = s;
+        cs[k][i] = c;
         float sumsq = 0.0f;
 #pragma unroll
         for (int r = 1; r <= D; ++r) sumsq = fmaf(acc[r][i], acc[r][i], sumsq);
@@ -538,8 +541,7 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
       mf4 zbar[R];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float s, c;
-        sincosf(om * z[k][0][i], &s, &c);
+        const float s = sn[k][i], c = cs[k][i];
         const float wc = om * c, w2s = om * om * s;
         float sumsq = 0.0f;
 #pragma unroll
