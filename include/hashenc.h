@@ -183,7 +183,7 @@ HASHENC_API int hashenc_backward_workspace_size(const hashenc* h, int64_t n, siz
  * small enough for the LDS of one workgroup, then each bin is accumulated on chip and added
  * to grad_params.  workspace: >= hashenc_backward_workspace_size bytes, 256-byte aligned,
  * owned by the caller, contents irrelevant on entry; calls sharing a workspace must not
- * overlap.  Points are processed in chunks of 2^20. */
+ * overlap.  Points are processed in chunks of 2^21. */
 HASHENC_API int hashenc_backward_ws(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
                                     const float* g_dgamma, const float* g_d2gamma, float* grad_params,
                                     void* workspace, size_t workspace_bytes, hashenc_stream_t stream);

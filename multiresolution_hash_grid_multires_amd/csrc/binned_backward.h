@@ -213,7 +213,7 @@ hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspa
                               const float* u_levels, hipStream_t s);
 
 constexpr int32_t kMaxBins = 16384;
-constexpr int64_t kBinChunkPoints = int64_t(1) << 20;  // points per pass of the binned backward
+constexpr int64_t kBinChunkPoints = int64_t(1) << 21;  // points per pass of the binned backward
 
 // Whether this configuration's bins and staging fit the LDS budgets of the binned path.
 bool binned_fits(const Grid& g, int d, int F, bool hermite);

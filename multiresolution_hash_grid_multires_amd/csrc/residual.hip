@@ -1027,7 +1027,7 @@ __global__ __launch_bounds__(256) void reduce_partials_apply_kernel(const double
   }
 }
 
-constexpr int64_t kChunk = int64_t(1) << 20;  // points per pass over the workspace
+constexpr int64_t kChunk = int64_t(1) << 21;  // points per pass over the workspace
 constexpr int kSirenBlocks = 256;  // one workgroup per CU (LDS-limited)
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }

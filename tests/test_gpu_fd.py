@@ -138,7 +138,7 @@ def test_fd_atomic_backward_path(orc):
 
 
 def test_fd_full_workload(orc):
-    """2^21 points (14 internal chunks of 2d+1 stencil sets): sampled stencil values and
+    """2^21 points (eight internal chunks of 2d+1 stencil sets, the last 64 points): sampled stencil values and
     residuals against the oracle, the loss as the mean square of the returned residuals, and
     the gradients as the size-weighted sum of the two halves' gradients."""
     W = I.WORKLOADS["fd_residual3d"]

@@ -365,12 +365,12 @@ def test_full_size_backward(orc, name):
 
 
 def test_binned_backward_chunks_and_clusters(orc):
-    # more points than one 2^20 chunk, half of them clustered (hot bins split across work
+    # more points than one 2^21 chunk, half of them clustered (hot bins split across work
     # items), a workspace reused across calls and accumulation into a non-zero gradient
     W = I.WORKLOADS["dlinear3d_L16_T19"]
     spec = dict(W["spec"], L=6, n_max=600)
     lay = orc.layout(spec)
-    n = (1 << 20) + 777
+    n = (1 << 21) + 777
     x = I.points(5, n, 3, clustered_half=True)
     (G,) = I.upstream(3, [(n, 12)])
     enc = api.HashGridEncoding(spec)

@@ -90,16 +90,17 @@ def test_residual_parity_shapes(orc, d, depth, hidden, omega):
 
 
 def test_residual_full_size(orc):
-    """2^21 points (two internal chunks): sampled residuals against the oracle; the loss is the
-    mean square of the returned residuals; and the gradients equal the size-weighted sum of
-    the gradients of the two halves computed by separate calls."""
+    """2^21 + 777 points (one full 2^21-point internal chunk and a ragged one): sampled
+    residuals against the oracle; the loss is the mean square of the returned residuals; and
+    the gradients equal the size-weighted sum of the gradients of the two halves computed by
+    separate calls (each half fits one chunk)."""
     W = I.WORKLOADS[NAME]
     spec, m = W["spec"], W["mlp"]
     enc = api.HashGridEncoding(spec)
     mlp = api.Mlp(32, m["hidden"], m["depth"], m["omega"])
     params = I.tables(W["id"], enc.n_params, W["tables"])
     mlp_params = I.siren_mlp(W["id"], 32, m["hidden"], m["depth"])
-    x = I.points(W["id"], W["n_points"], 3, clustered_half=True)
+    x = I.points(W["id"], W["n_points"] + 777, 3, clustered_half=True)
     n = x.shape[0]
     r, loss, gp, gm = _run_gpu(spec, mlp, x, params, mlp_params)
     idx = np.sort(np.random.default_rng(2).choice(n, 1024, replace=False))
@@ -111,9 +112,10 @@ def test_residual_full_size(orc):
     ra, la, gpa, gma = _run_gpu(spec, mlp, x[:h], params, mlp_params)
     rb, lb, gpb, gmb = _run_gpu(spec, mlp, x[h:], params, mlp_params)
     np.testing.assert_array_equal(np.concatenate([ra, rb]), r)
-    assert abs(0.5 * (la + lb) - loss) <= 1e-5 * loss
-    _close(gm, 0.5 * (gma.astype(np.float64) + gmb), 1e-4, "grad_mlp halves")
-    _close(gp, 0.5 * (gpa.astype(np.float64) + gpb), 1e-4, "grad_params halves")
+    wa, wb = h / n, (n - h) / n
+    assert abs(wa * la + wb * lb - loss) <= 1e-5 * loss
+    _close(gm, wa * gma.astype(np.float64) + wb * gmb, 1e-4, "grad_mlp halves")
+    _close(gp, wa * gpa.astype(np.float64) + wb * gpb, 1e-4, "grad_params halves")
 
 
 def test_residual_argument_errors():
