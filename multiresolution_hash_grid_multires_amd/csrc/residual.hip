@@ -54,6 +54,42 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// sin and cos of x in fp32, within about 2 ulp for |x| <= 2^22: Cody and Waite's reduction
+// x = k pi/2 + r with pi/2 split into three fp32 parts, each product k * part folded in with
+// one fma; the Taylor series of sin r (through r^11) and cos r (through r^12) on |r| <= pi/4,
+// whose truncation (below 1e-11) is far under fp32 rounding; then k mod 4 picks the roles
+// and signs.  Beyond 2^22, where neighbouring fp32 arguments lie over 0.25 apart, r leaves
+// the polynomials' range and the results are unspecified; NaN and infinity give NaN.  No
+// large-argument branch and no clamp: their registers made the seven-row finite-difference
+// kernel spill.  A caller that uses only one of the two results pays only for its polynomial.
+__device__ __forceinline__ void sincos_red(float x, float& s, float& c) {
+  constexpr float kTwoOverPi = 0x1.45f306p-1f;
+  constexpr float kPio2A = 0x1.921fb6p+0f;    // pi/2 = A + B + C to about 2^-73
+  constexpr float kPio2B = -0x1.777a5cp-25f;
+  constexpr float kPio2C = -0x1.ee59dap-50f;
+  const float k = rintf(x * kTwoOverPi);
+  float r = fmaf(-k, kPio2A, x);
+  r = fmaf(-k, kPio2B, r);
+  r = fmaf(-k, kPio2C, r);
+  const float r2 = r * r;
+  float ps = fmaf(r2, -1.0f / 39916800.0f, 1.0f / 362880.0f);
+  ps = fmaf(r2, ps, -1.0f / 5040.0f);
+  ps = fmaf(r2, ps, 1.0f / 120.0f);
+  ps = fmaf(r2, ps, -1.0f / 6.0f);
+  const float sr = fmaf(r * r2, ps, r);
+  float pc = fmaf(r2, 1.0f / 479001600.0f, -1.0f / 3628800.0f);
+  pc = fmaf(r2, pc, 1.0f / 40320.0f);
+  pc = fmaf(r2, pc, -1.0f / 720.0f);
+  pc = fmaf(r2, pc, 1.0f / 24.0f);
+  pc = fmaf(r2, pc, -0.5f);
+  const float cr = fmaf(r2, pc, 1.0f);
+  const int q = __float2int_rz(k) & 3;  // x = q pi/2 + r (mod 2 pi)
+  const float sv = (q & 1) ? cr : sr;
+  const float cv = (q & 1) ? sr : cr;
+  s = (q & 2) ? -sv : sv;
+  c = ((q + 1) & 2) ? -cv : cv;
+}
+
 // Encoder outputs and their upstream are level-major, [L][n][R][F] (R = value, d gradient
 // rows, Laplacian): the index of feature j = l F + f, row r of point p.
 __device__ __forceinline__ int64_t lm_index(const MlpArgs& a, int64_t n, int64_t p, int j, int r, int R) {
@@ -181,7 +217,7 @@ __global__ __launch_bounds__(kW * siren_waves(DEPTH, INP)) void siren_residual_k
       for (int b = 0; b < kPB; ++b) {
         const float* zz = z + b * R;
         float s, c;
-        sincosf(w * zz[0], &s, &c);
+        sincos_red(w * zz[0], s, c);
         ts[k][b] = s;
         tc[k][b] = c;
         float sumsq = 0.0f;
@@ -481,7 +517,7 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float s, c;
-        sincosf(om * acc[0][i], &s, &c);
+        sincos_red(om * acc[0][i], s, c);
         sn[k][i] = s;
         cs[k][i] = c;
         float sumsq = 0.0f;
@@ -794,7 +830,8 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
         const int o = 16 * wn + 4 * lq + i;
 #pragma unroll
         for (int rr = 0; rr < RG; ++rr) {
-          const float sv = sinf(om * acc[rr][i]);
+          float sv, cv_unused;
+          sincos_red(om * acc[rr][i], sv, cv_unused);
           if constexpr (K + 1 < DEPTH) {
             if (r0 + rr < R) sh.act1[o][(r0 + rr) * kMP + lm] = sv;
           } else {
@@ -869,7 +906,9 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
 #pragma unroll
         for (int rr = 0; rr < RG; ++rr) {
           if (r0 + rr < R) {
-            const float zbar = abar[rr][i] * om * cosf(om * z[K][rr][i]);
+            float sv_unused, cv;
+            sincos_red(om * z[K][rr][i], sv_unused, cv);
+            const float zbar = abar[rr][i] * om * cv;
             zsum += zbar;
             sh.zb[o][(r0 + rr) * kMP + lm] = zbar;
           }
