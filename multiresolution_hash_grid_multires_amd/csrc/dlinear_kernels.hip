@@ -216,10 +216,11 @@ __global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, c
 }
 
 // [L][n][F] -> [n][Lrow*F] through LDS.  A workgroup owns P consecutive points: it reads
-// the P*F contiguous floats of each level (coalesced runs), parks them in LDS as P rows of
-// L*F (pitch L*F + 1 keeps the scattered LDS writes free of bank conflicts) and writes the
-// P*Lrow*F contiguous output floats as 16-byte pieces, so every output line is written
-// whole.  Columns of the inactive levels L..Lrow-1 are written as zeros.
+// the P*F contiguous floats of each level (coalesced runs; 16-byte loads, four in flight per
+// lane before the first LDS write, when every run is 16-byte aligned), parks them in LDS as
+// P rows of L*F (pitch L*F + 1 keeps the scattered LDS writes free of bank conflicts) and
+// writes the P*Lrow*F contiguous output floats as 16-byte pieces, so every output line is
+// written whole.  Columns of the inactive levels L..Lrow-1 are written as zeros.
 template <int F>
 __global__ __launch_bounds__(kBlock) void level_major_to_rows_kernel(int32_t L, int32_t Lrow, int64_t n, int32_t P,
                                                                      const float* __restrict__ lm,
@@ -231,25 +232,47 @@ __global__ __launch_bounds__(kBlock) void level_major_to_rows_kernel(int32_t L, 
   const int64_t p0 = (int64_t)blockIdx.x * P;
   const int np = (int)min((int64_t)P, n - p0);
   const int per_level = np * F;
-  for (int i = threadIdx.x; i < L * per_level; i += kBlock) {
-    const int l = i / per_level, r = i - l * per_level;
-    tile[(r / F) * pitch + l * F + r % F] = lm[((int64_t)l * n + p0) * F + r];
+  if (((n * F) & 3) == 0 && (per_level & 3) == 0 && ((P * F) & 3) == 0) {
+    constexpr int U = 4;
+    const int q_per = per_level >> 2;  // 16-byte pieces per level
+    const int total = L * q_per;
+    for (int i0 = threadIdx.x; i0 < total; i0 += U * kBlock) {
+      float4 v[U];
+      int lv[U], rv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kBlock;
+        lv[u] = i / q_per;
+        rv[u] = 4 * (i - lv[u] * q_per);  // float index inside the level's run
+        if (i < total) v[u] = *reinterpret_cast<const float4*>(lm + ((int64_t)lv[u] * n + p0) * F + rv[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (i0 + u * kBlock >= total) break;
+        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tile[((rv[u] + k) / F) * pitch + lv[u] * F + (rv[u] + k) % F] = e[k];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < L * per_level; i += kBlock) {
+      const int l = i / per_level, r = i - l * per_level;
+      tile[(r / F) * pitch + l * F + r % F] = lm[((int64_t)l * n + p0) * F + r];
+    }
   }
   __syncthreads();
   float* dst = out + p0 * LF;
-  const int total = np * LF;
   if ((LF & 3) == 0) {  // every row, hence the block's output, is 16-byte aligned
-    for (int q = threadIdx.x; 4 * q < total; q += kBlock) {
+    const int q4 = LF >> 2;  // 16-byte pieces per row
+    for (int q = threadIdx.x; q < np * q4; q += kBlock) {
+      const int pt = q / q4, c = 4 * (q - pt * q4);
       float v[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e = 4 * q + k;
-        const int c = e % LF;
-        v[k] = c < AF ? tile[(e / LF) * pitch + c] : 0.0f;
-      }
+      for (int k = 0; k < 4; ++k) v[k] = c + k < AF ? tile[pt * pitch + c + k] : 0.0f;
       reinterpret_cast<float4*>(dst)[q] = make_float4(v[0], v[1], v[2], v[3]);
     }
   } else {
+    const int total = np * LF;
     for (int e = threadIdx.x; e < total; e += kBlock) {
       const int c = e % LF;
       dst[e] = c < AF ? tile[(e / LF) * pitch + c] : 0.0f;

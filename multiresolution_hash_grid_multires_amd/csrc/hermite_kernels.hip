@@ -569,26 +569,60 @@ __global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t
   const int pitch = L * MF + 1;
   const int64_t p0 = (int64_t)blockIdx.x * P;
   const int np = (int)min((int64_t)P, n - p0);
-  // read phase: one thread per (point, component) row of L*F floats, read with independent
-  // 16-byte loads when rows are 16-byte aligned
-  for (int row = threadIdx.x; row < np * M; row += kBlock) {
-    const int i = row / M, m = row - i * M;
-    const int64_t p = p0 + i;
-    const float* src = m == 0 ? (gg ? gg + p * LF : nullptr)
-                     : m <= D ? (gd ? gd + (p * D + (m - 1)) * LF : nullptr)
-                              : (g2 ? g2 + (p * D2 + (m - 1 - D)) * LF : nullptr);
-    float* t = tile + i * pitch + m * F;
-    if (((LF | AF) & 3) == 0) {
-      for (int c = 0; c < AF; c += 4) {
-        const float4 v = src ? *reinterpret_cast<const float4*>(src + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        const float e[4] = {v.x, v.y, v.z, v.w};
+  if (((LF | AF) & 3) == 0) {
+    // read phase: the tile's rows of each upstream array form one contiguous block (C rows of
+    // LF floats per point); lanes take consecutive 16-byte pieces of it, four loads in flight
+    // per lane before the LDS writes, and skip the pieces of inactive levels (columns >= AF)
+    const int q_row = LF >> 2;  // 16-byte pieces per row
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int l = (c + j) / F, f = (c + j) - l * F;
-          t[l * MF + f] = e[j];
+    for (int sidx = 0; sidx < 3; ++sidx) {
+      const int C = sidx == 0 ? 1 : sidx == 1 ? D : D2;  // rows per point of this array
+      const int m0 = sidx == 0 ? 0 : sidx == 1 ? 1 : 1 + D;
+      const float* src = sidx == 0 ? gg : sidx == 1 ? gd : g2;
+      if (!src) {  // absent upstream reads as zero
+        for (int e = threadIdx.x; e < np * C * AF; e += kBlock) {
+          const int row = e / AF, c = e - row * AF;
+          const int i = row / C, m = m0 + row - i * C;
+          tile[i * pitch + (c / F) * MF + m * F + c % F] = 0.0f;
+        }
+        continue;
+      }
+      const float4* s4 = reinterpret_cast<const float4*>(src + p0 * C * LF);
+      const int total = np * C * q_row;
+      for (int q0 = threadIdx.x; q0 < total; q0 += 4 * kBlock) {
+        float4 v[4];
+        int rowv[4], cv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q0 + u * kBlock;
+          rowv[u] = q / q_row;
+          cv[u] = 4 * (q - rowv[u] * q_row);
+          if (q < total && cv[u] < AF) v[u] = s4[q];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (q0 + u * kBlock >= total) break;
+          if (cv[u] >= AF) continue;
+          const int i = rowv[u] / C, m = m0 + rowv[u] - i * C;
+          float* t = tile + i * pitch + m * F;
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int l = (cv[u] + j) / F, f = (cv[u] + j) - l * F;
+            t[l * MF + f] = e[j];
+          }
         }
       }
-    } else {
+    }
+  } else {
+    // one thread per (point, component) row of L*F floats
+    for (int row = threadIdx.x; row < np * M; row += kBlock) {
+      const int i = row / M, m = row - i * M;
+      const int64_t p = p0 + i;
+      const float* src = m == 0 ? (gg ? gg + p * LF : nullptr)
+                       : m <= D ? (gd ? gd + (p * D + (m - 1)) * LF : nullptr)
+                                : (g2 ? g2 + (p * D2 + (m - 1 - D)) * LF : nullptr);
+      float* t = tile + i * pitch + m * F;
       for (int c = 0; c < AF; ++c) {
         const int l = c / F, f = c - l * F;
         t[l * MF + f] = src ? src[c] : 0.0f;
