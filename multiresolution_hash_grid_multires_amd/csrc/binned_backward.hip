@@ -61,9 +61,31 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void bin_scan_apply_kernel
   int r0, r1, seg;
   scan_segment(nblk, r0, r1, seg);
   int32_t run = 0;
-  for (int j = 0; j < seg; ++j) run += seg_sums[(int64_t)j * nbins + bin];
+  {
+    int32_t part[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // eight loads in flight
+    int j = 0;
+    for (; j + 8 <= seg; j += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) part[u] += seg_sums[(int64_t)(j + u) * nbins + bin];
+    for (; j < seg; ++j) part[0] += seg_sums[(int64_t)j * nbins + bin];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) run += part[u];
+  }
   if (seg == kScanSegs - 1) totals[bin] = run + seg_sums[(int64_t)seg * nbins + bin];
-  for (int r = r0; r < r1; ++r) {
+  // eight rows' loads in flight before their stores (a store between two loads of the same
+  // array would otherwise hold every load back until the one before it returns)
+  int r = r0;
+  for (; r + 8 <= r1; r += 8) {
+    int32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = counts[(int64_t)(r + u) * nbins + bin];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      counts[(int64_t)(r + u) * nbins + bin] = run;
+      run += c[u];
+    }
+  }
+  for (; r < r1; ++r) {
     const int32_t c = counts[(int64_t)r * nbins + bin];
     counts[(int64_t)r * nbins + bin] = run;
     run += c;
@@ -74,20 +96,33 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
                                                         int32_t* __restrict__ bin_start,
                                                         WorkItem* __restrict__ items,
                                                         BinState* __restrict__ st, int32_t emax) {
-  // One workgroup: bin_start = exclusive scan of totals; work items; segment bases.
+  // One workgroup: bin_start = exclusive scan of totals; work items; segment bases.  The
+  // totals are staged in LDS by coalesced loads (four in flight per thread), and the first
+  // entry of every segment is kept in LDS for the segment bases.
   __shared__ int32_t part[1024];
   __shared__ int32_t ipart[1024];
   __shared__ int32_t seg0[kMaxSeg + 1];
+  __shared__ int32_t seg_first[kMaxSeg];
+  __shared__ int32_t tot_sh[kMaxBins];
   const int t = threadIdx.x;
   for (int i = t; i <= bp.nseg; i += 1024) seg0[i] = bp.seg_bin0[i];
   const int nb = bp.nbins;
+  for (int i0 = t; i0 < nb; i0 += 4 * 1024) {
+    int32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i0 + u * 1024 < nb ? totals[i0 + u * 1024] : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * 1024 < nb) tot_sh[i0 + u * 1024] = v[u];
+  }
+  __syncthreads();
   const int per = (nb + 1023) / 1024;
   const int b0 = t * per;
   int32_t s = 0, si = 0;
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
     if (b < nb) {
-      const int32_t tot = totals[b];
+      const int32_t tot = tot_sh[b];
       s += tot;
       si += (tot + emax - 1) / emax;
     }
@@ -109,9 +144,10 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
     if (b < nb) {
-      const int32_t tot = totals[b];
+      const int32_t tot = tot_sh[b];
       bin_start[b] = run;
       while (sg + 1 < bp.nseg && seg0[sg + 1] <= b) ++sg;  // segment owning bin b
+      if (seg0[sg] == b) seg_first[sg] = run;  // every segment has at least one bin
       const int32_t nit = (tot + emax - 1) / emax;
       for (int j = 0; j < nit; ++j) {
         WorkItem w;
@@ -135,8 +171,8 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
   if (t == 0) {
     int64_t vb = 0;
     for (int g = 0; g < bp.nseg; ++g) {
-      const int32_t e0 = g == 0 ? 0 : bin_start[seg0[g]];
-      const int32_t e1 = seg0[g + 1] >= nb ? part[1023] : bin_start[seg0[g + 1]];
+      const int32_t e0 = seg_first[g];
+      const int32_t e1 = g + 1 < bp.nseg ? seg_first[g + 1] : part[1023];
       st->seg_ebase[g] = e0;
       st->seg_vbase[g] = vb;
       vb += (int64_t)(e1 - e0) * (bp.records ? 2 + bp.width[0] : hermite_rec_width(bp.width[g / bp.L]));
