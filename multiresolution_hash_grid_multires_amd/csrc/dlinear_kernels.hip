@@ -327,8 +327,8 @@ __global__ __launch_bounds__(kBlock) void dlinear_backward_kernel(const Grid g, 
   }
 }
 
-// Binned backward, count pass: a workgroup of TPB lanes owns a tile of `tile` points (at
-// most 4 per lane) and histograms their entries over all bins in LDS.  On pair-mode levels the two
+// Binned backward, count pass: a workgroup of TPB lanes owns a tile of `tile` = 2 TPB points
+// (two per lane) and histograms their entries over all bins in LDS.  On pair-mode levels the two
 // x-corners of each (y, z) corner pair make one entry (they always share a bin); elsewhere
 // each corner is its own entry.
 template <int D, int TPB>
@@ -339,23 +339,25 @@ __global__ __launch_bounds__(TPB) void dlinear_count_kernel(const Grid g, const 
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
   for (int i = threadIdx.x; i < bp.nbins; i += TPB) hist[i] = 0;
   __syncthreads();
-  const int ppt = tile / TPB;
+  constexpr int PPT = 2;  // points per lane
   const int64_t p0 = (int64_t)blk * tile + threadIdx.x;
-  float xp[4][D];
+  // both points' coordinates in flight at once (lanes past the end re-read the last point and
+  // skip it below): a guarded load per coordinate would wait for each before the next
+  float xp[PPT][D];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t p = p0 + (int64_t)j * TPB;
+  for (int j = 0; j < PPT; ++j) {
+    const int64_t p = min(p0 + (int64_t)j * TPB, n - 1);
 #pragma unroll
-    for (int i = 0; i < D; ++i) xp[j][i] = (j < ppt && p < n) ? x[p * D + i] : 0.0f;
+    for (int i = 0; i < D; ++i) xp[j][i] = x[p * D + i];
   }
   for (int l = 0; l < g.L; ++l) {
     const bool dense = (g.dense[0] >> l) & 1u;
     const bool pair = (bp.pair_mask >> l) & 1u;
     const bool few = bp.seg_bin0[l + 1] - bp.seg_bin0[l] <= kFewBins;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < PPT; ++j) {
       const int64_t p = p0 + (int64_t)j * TPB;
-      if (j >= ppt || p >= n) break;
+      if (p >= n) break;
       uint32_t base[D];
       float t[D];
       locate<D>(xp[j], g.N[l], g.Nf[l], base, t);
@@ -550,6 +552,7 @@ hipError_t launch_bin_tile(const Grid& g, const BinPlan& bp, const BinWorkspace&
   const dim3 grid((unsigned)w.nblk);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
   if (!scatter) {  // two points per count lane
+    if (w.tile != TPB) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dlinear_count_kernel<D, TPB / 2>), grid, dim3(TPB / 2), sizeof(int32_t) * (size_t)bp.nbins,
                        s, g, bp, n, w.tile, w.nblk, x, counts);
     return hipGetLastError();
