@@ -144,24 +144,41 @@ __device__ __forceinline__ void gather_corner_packed(const float* __restrict__ b
   }
 }
 
-// One thread per packed row: gather the row's slots from the d + 1 order tables.
+// One thread per packed row: gather the row's slots from the d + 1 order tables.  Packed row
+// t sits at float t * RW across all levels, so a workgroup's rows form one contiguous block:
+// they are parked in LDS (pitch RW + 4 floats against bank conflicts) and written out as
+// consecutive 16-byte pieces, whole lines per store instruction, where each lane storing its
+// own row would touch one line per lane and instruction.
 template <int D, int F>
 __global__ __launch_bounds__(kBlock) void hermite_pack_kernel(const Grid g, const PackPlan pp,
                                                               const float* __restrict__ params,
                                                               float* __restrict__ packed) {
   constexpr int W1 = binom_d(D, 1) * F, W2 = binom_d(D, 2) * F;
   constexpr int RW = (1 << D) * F;
-  const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (t * RW >= pp.poff[g.L]) return;
-  int l = 0;
-  while (l + 1 < g.L && t * RW >= pp.poff[l + 1]) ++l;
-  const int64_t r = t - pp.poff[l] / RW;
-  float v[RW];
-  load_vec_at<F>(params + g.off[0][l] + r * F, v, 0);
-  load_vec_at<W1>(params + g.off[1][l] + r * W1, v, F);
-  load_vec_at<W2>(params + g.off[2][l] + r * W2, v, F + W1);
-  if constexpr (D == 3) load_vec_at<F>(params + g.off[3][l] + r * F, v, F + W1 + W2);
-  store_vec<RW>(packed + pp.poff[l] + r * RW, v);
+  constexpr int PITCH = RW + 4;
+  __shared__ float stage[kBlock * PITCH];
+  const int64_t total = pp.poff[g.L] / RW;  // packed rows
+  const int64_t t0 = (int64_t)blockIdx.x * kBlock;
+  const int64_t t = t0 + threadIdx.x;
+  if (t < total) {
+    int l = 0;
+    while (l + 1 < g.L && t * RW >= pp.poff[l + 1]) ++l;
+    const int64_t r = t - pp.poff[l] / RW;
+    float v[RW];
+    load_vec_at<F>(params + g.off[0][l] + r * F, v, 0);
+    load_vec_at<W1>(params + g.off[1][l] + r * W1, v, F);
+    load_vec_at<W2>(params + g.off[2][l] + r * W2, v, F + W1);
+    if constexpr (D == 3) load_vec_at<F>(params + g.off[3][l] + r * F, v, F + W1 + W2);
+    store_vec<RW>(stage + threadIdx.x * PITCH, v);
+  }
+  __syncthreads();
+  const int nr = (int)(total - t0 < kBlock ? total - t0 : kBlock);
+  constexpr int Q = RW / 4;  // 16-byte pieces per row
+  float4* dst = reinterpret_cast<float4*>(packed + t0 * RW);
+  for (int q = threadIdx.x; q < nr * Q; q += kBlock) {
+    const int row = q / Q, c = q - row * Q;
+    dst[q] = *reinterpret_cast<const float4*>(stage + row * PITCH + 4 * c);
+  }
 }
 
 template <int D, int F, int C>
