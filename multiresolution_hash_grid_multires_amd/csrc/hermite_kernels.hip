@@ -297,6 +297,9 @@ __device__ __forceinline__ void level_setup(const Grid& g, int l, const float (&
 // LM: write the level's outputs level-major into stage[l][p][m][F], m = value, d gradient
 // components, then the second-derivative components (d diagonal ones or the Laplacian):
 // whole lines per workgroup, where the point-major rows take 8-byte pieces of many lines.
+// The workgroup's outputs are one contiguous run there; they are parked in LDS and written
+// as consecutive 16-byte pieces (a lane storing its own point's M F floats would touch one
+// line per lane and store instruction).
 template <int D, int F, bool PACKED, bool LM>
 __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
     const Grid g, const PackPlan pp, int64_t n, int32_t n_tiles, int d2_mode, const float* __restrict__ x,
@@ -305,11 +308,16 @@ __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
   constexpr int PTS = kBlock / 2;  // points per workgroup: two lanes per point
   const int l = blockIdx.x / n_tiles;
   const int half = threadIdx.x & 1;  // which half of the cell's x-corner pairs this lane gathers
-  const int64_t p = (int64_t)(blockIdx.x % n_tiles) * PTS + (threadIdx.x >> 1);
-  if (p >= n) return;  // both lanes of a point leave together
+  const int64_t p0 = (int64_t)(blockIdx.x % n_tiles) * PTS;
+  const int64_t p = p0 + (threadIdx.x >> 1);
+  if constexpr (!LM) {
+    if (p >= n) return;  // both lanes of a point leave together
+  }
+  // with LM every lane reaches the staging barrier: lanes past the end evaluate the last point
+  const int64_t pc = p < n ? p : n - 1;
   float xp[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
+  for (int i = 0; i < D; ++i) xp[i] = x[pc * D + i];
   const int64_t LF = (int64_t)g.Lrow * F;
   CellKeys<D> keys;
   AxisBasis ab[D];
@@ -349,30 +357,47 @@ __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
       o.h[i][f] += __shfl_xor(o.h[i][f], 1, 64);
     }
   }
-  if (half) return;
   if constexpr (LM) {
+    __shared__ __align__(16) float ob[PTS * (1 + 2 * D) * F];
     const bool diag = d2_mode == HASHENC_D2_DIAG;
     const int M = 1 + D + (diag ? D : 1);
-    float* dst = stage + ((int64_t)l * n + p) * M * F;
-    store_vec<F>(dst, o.v);
+    const int MF = M * F;
+    if (!half) {
+      float* o_pt = ob + (threadIdx.x >> 1) * MF;
 #pragma unroll
-    for (int i = 0; i < D; ++i) store_vec<F>(dst + (1 + i) * F, o.g[i]);
-    if (diag) {
+      for (int f = 0; f < F; ++f) o_pt[f] = o.v[f];
 #pragma unroll
-      for (int i = 0; i < D; ++i) store_vec<F>(dst + (1 + D + i) * F, o.h[i]);
-    } else {
-      float lap[F];
+      for (int i = 0; i < D; ++i)
 #pragma unroll
-      for (int f = 0; f < F; ++f) {
-        float s = 0.0f;
+        for (int f = 0; f < F; ++f) o_pt[(1 + i) * F + f] = o.g[i][f];
+      if (diag) {
 #pragma unroll
-        for (int i = 0; i < D; ++i) s += o.h[i][f];
-        lap[f] = s;
+        for (int i = 0; i < D; ++i)
+#pragma unroll
+          for (int f = 0; f < F; ++f) o_pt[(1 + D + i) * F + f] = o.h[i][f];
+      } else {
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          float s = 0.0f;
+#pragma unroll
+          for (int i = 0; i < D; ++i) s += o.h[i][f];
+          o_pt[(1 + D) * F + f] = s;
+        }
       }
-      store_vec<F>(dst + (1 + D) * F, lap);
+    }
+    __syncthreads();
+    const int np = (int)(n - p0 < PTS ? n - p0 : PTS);
+    const int tot = np * MF;
+    float* dst = stage + ((int64_t)l * n + p0) * MF;
+    if (((n * MF) & 3) == 0 && (tot & 3) == 0) {  // the run starts and ends on 16-byte boundaries
+      for (int q = threadIdx.x; q < (tot >> 2); q += kBlock)
+        reinterpret_cast<float4*>(dst)[q] = reinterpret_cast<const float4*>(ob)[q];
+    } else {
+      for (int e = threadIdx.x; e < tot; e += kBlock) dst[e] = ob[e];
     }
     return;
   }
+  if (half) return;
   const int64_t col = (int64_t)l * F;
   if (gamma) store_vec<F>(gamma + p * LF + col, o.v);
   if (dgamma) {
