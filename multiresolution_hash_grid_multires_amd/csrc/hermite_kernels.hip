@@ -684,10 +684,11 @@ __global__ __launch_bounds__(kBlock) void hermite_upstream_levels_kernel(int32_t
 // The forward's level-major staging [l][p][m][F] -> gamma [n, L*F], dgamma [n, d, L*F],
 // d2gamma [n, d2, L*F] (NULL outputs skipped).  A workgroup owns P consecutive points: it
 // reads each level's P * M * F contiguous floats into LDS (each point's rows in output
-// order, pitch M * L * F + 1) and writes every (point, component) row of L*F floats with
-// 16-byte stores when rows are 16-byte aligned; the P rows of one output array are
-// contiguous, so lines are written whole.  Rows are Lrow * F floats: the columns of the
-// inactive levels L..Lrow-1 are written as zeros.
+// order, pitch M * L * F + 1) and writes the tile's rows of each output array, one
+// contiguous block per array; both phases move consecutive 16-byte pieces across the lanes
+// when the runs are 16-byte aligned, so every load and store instruction covers whole
+// lines.  Rows are Lrow * F floats: the columns of the inactive levels L..Lrow-1 are
+// written as zeros.
 template <int F, int D, int M>
 __global__ __launch_bounds__(kBlock) void hermite_levels_to_rows_kernel(int32_t L, int32_t Lrow, int64_t n,
                                                                         int32_t P,
@@ -703,33 +704,71 @@ __global__ __launch_bounds__(kBlock) void hermite_levels_to_rows_kernel(int32_t 
   const int pitch = M * LF + 1;
   const int64_t p0 = (int64_t)blockIdx.x * P;
   const int np = (int)min((int64_t)P, n - p0);
-  // one thread per (level, point): its M * F contiguous floats, loaded before any is stored
-  for (int pr = threadIdx.x; pr < L * np; pr += kBlock) {
-    const int l = pr / np, i = pr - l * np;
-    float v[MF];
-    load_vec<MF>(stage + ((int64_t)l * n + p0 + i) * MF, v);
-    float* t = tile + i * pitch + l * F;
+  // read phase: each level's run of the tile (np * MF floats) is contiguous; lanes take
+  // consecutive 16-byte pieces, four loads in flight per lane before the LDS writes
+  if (((n * MF) & 3) == 0 && ((np * MF) & 3) == 0 && ((P * MF) & 3) == 0) {
+    const int q_per = (np * MF) >> 2;
+    const int total = L * q_per;
+    for (int q0 = threadIdx.x; q0 < total; q0 += 4 * kBlock) {
+      float4 v[4];
+      int lv[4], ev[4];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + u * kBlock;
+        lv[u] = q / q_per;
+        ev[u] = 4 * (q - lv[u] * q_per);  // float index inside the level's run
+        if (q < total) v[u] = *reinterpret_cast<const float4*>(stage + ((int64_t)lv[u] * n + p0) * MF + ev[u]);
+      }
 #pragma unroll
-      for (int f = 0; f < F; ++f) t[m * LF + f] = v[m * F + f];
+      for (int u = 0; u < 4; ++u) {
+        if (q0 + u * kBlock >= total) break;
+        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = (ev[u] + k) / MF, r = (ev[u] + k) - i * MF;
+          const int m = r / F, f = r - m * F;
+          tile[i * pitch + m * LF + lv[u] * F + f] = e[k];
+        }
+      }
+    }
+  } else {
+    // one thread per (level, point): its M * F contiguous floats
+    for (int pr = threadIdx.x; pr < L * np; pr += kBlock) {
+      const int l = pr / np, i = pr - l * np;
+      float v[MF];
+      load_vec<MF>(stage + ((int64_t)l * n + p0 + i) * MF, v);
+      float* t = tile + i * pitch + l * F;
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int f = 0; f < F; ++f) t[m * LF + f] = v[m * F + f];
+    }
   }
   __syncthreads();
-  for (int row = threadIdx.x; row < np * M; row += kBlock) {
-    const int i = row / M, m = row - i * M;
-    const int64_t p = p0 + i;
-    float* dst = m == 0 ? (gamma ? gamma + p * RF : nullptr)
-               : m <= D ? (dgamma ? dgamma + (p * D + (m - 1)) * RF : nullptr)
-                        : (d2gamma ? d2gamma + (p * D2 + (m - 1 - D)) * RF : nullptr);
-    if (!dst) continue;
-    const float* t = tile + i * pitch + m * LF;
+  // write phase: each output array's rows for the tile (np * C rows of RF floats, C components
+  // per point) form one contiguous block; lanes write its consecutive 16-byte pieces
+#pragma unroll
+  for (int aidx = 0; aidx < 3; ++aidx) {
+    const int C = aidx == 0 ? 1 : aidx == 1 ? D : D2;
+    const int m0 = aidx == 0 ? 0 : aidx == 1 ? 1 : 1 + D;
+    float* out = aidx == 0 ? gamma : aidx == 1 ? dgamma : d2gamma;
+    if (!out) continue;
+    float* dst = out + p0 * C * RF;
     if (((LF | RF) & 3) == 0) {
-      for (int c = 0; c < LF; c += 4)
-        *reinterpret_cast<float4*>(dst + c) = make_float4(t[c], t[c + 1], t[c + 2], t[c + 3]);
-      for (int c = LF; c < RF; c += 4) *reinterpret_cast<float4*>(dst + c) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      const int qr = RF >> 2;  // pieces per row
+      for (int q = threadIdx.x; q < np * C * qr; q += kBlock) {
+        const int row = q / qr, c = 4 * (q - row * qr);
+        const int i = row / C, m = m0 + row - i * C;
+        const float* t = tile + i * pitch + m * LF;
+        const float4 w = c < LF ? make_float4(t[c], t[c + 1], t[c + 2], t[c + 3]) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        reinterpret_cast<float4*>(dst)[q] = w;
+      }
     } else {
-      for (int c = 0; c < LF; ++c) dst[c] = t[c];
-      for (int c = LF; c < RF; ++c) dst[c] = 0.0f;
+      for (int e = threadIdx.x; e < np * C * RF; e += kBlock) {
+        const int row = e / RF, c = e - row * RF;
+        const int i = row / C, m = m0 + row - i * C;
+        dst[e] = c < LF ? tile[i * pitch + m * LF + c] : 0.0f;
+      }
     }
   }
 }
