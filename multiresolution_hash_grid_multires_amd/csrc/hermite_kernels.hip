@@ -1111,7 +1111,7 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   const bool diag = d2_mode == HASHENC_D2_DIAG;
   const int M = 1 + D + (diag ? D : 1);
   const int LF = g.L * F;
-  const int PU = (int)std::max(1, std::min(64, 16384 / (M * LF)));  // LDS tile <= 64 KB
+  const int PU = (int)std::max(1, std::min(32, 8192 / (M * LF)));  // LDS tile <= 32 KB: several workgroups per CU
   const float* U = u_levels ? u_levels : reinterpret_cast<const float*>(ws + w.ups);
   float* Uw = reinterpret_cast<float*>(ws + w.ups);
   const size_t ulds = sizeof(float) * (size_t)PU * (M * LF + 1);
@@ -1198,7 +1198,7 @@ hipError_t launch_fwd(const Grid& g, int d2_mode, int64_t n, const float* x, con
   }
   const int M = 1 + D + (diag ? D : 1);
   const int LF = g.L * F;
-  const int P = (int)std::max(1, std::min(64, 16384 / (M * LF)));  // LDS tile <= 64 KB
+  const int P = (int)std::max(1, std::min(32, 8192 / (M * LF)));  // LDS tile <= 32 KB: several workgroups per CU
   const size_t lds = sizeof(float) * (size_t)P * (M * LF + 1);
   const void* kern = diag ? reinterpret_cast<const void*>(&hermite_levels_to_rows_kernel<F, D, 1 + 2 * D>)
                           : reinterpret_cast<const void*>(&hermite_levels_to_rows_kernel<F, D, 2 + D>);
