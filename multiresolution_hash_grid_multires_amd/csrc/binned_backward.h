@@ -9,7 +9,6 @@ namespace hg {
 constexpr int kMaxBinTables = 4;                  // the binned backward covers d <= 3
 constexpr int kMaxSeg = kMaxBinTables * kMaxLevels;  // segment s = table k * L + level l
 constexpr int kBinLdsValues = 16384;              // 128 KB fp64 LDS accumulator per work item
-constexpr int kBinTilePoints = 1024;              // points per count / scatter workgroup (max)
 constexpr int kBinThreads = 256;
 constexpr int kBinItemEntries = 1 << 18;          // entries per reduce work item (at most)
 constexpr int kBinItemMin = 1 << 12;              // ... and at least, when bins are split
