@@ -49,6 +49,7 @@ class Handle:
     def __init__(self, ptr: int, spec: dict):
         self.ptr = ctypes.c_void_p(ptr)
         self.spec = dict(spec)
+        self._sizes = None  # (n_params, L*F), read from the library on first use
 
     def __del__(self):
         # at interpreter shutdown the module globals may already be gone
@@ -74,6 +75,58 @@ def _dev_ptr(t: torch.Tensor | None, name: str, dtype=torch.float32):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _sizes(h: Handle) -> tuple[int, int]:
+    if h._sizes is None:
+        n_params, width = ctypes.c_int64(), ctypes.c_int32()
+        check(load().hashenc_info(h, ctypes.byref(n_params), ctypes.byref(width), None))
+        h._sizes = (int(n_params.value), int(width.value))
+    return h._sizes
+
+
+def _expect(t, numel: int, name: str) -> None:
+    """Size check of an optional tensor argument, before any pointer reaches the library:
+    the kernels trust the sizes the layout implies, so a short buffer would be overrun on
+    the device."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.numel() != numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; this call needs {numel}")
+
+
+def _points(h: Handle, x) -> int:
+    """n from x [n, d] (checked)."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    d = int(h.spec["d"])
+    if x.dim() != 2 or x.shape[1] != d:
+        raise ValueError(f"x must be [n, {d}] (got {list(x.shape)})")
+    return int(x.shape[0])
+
+
+def _check_encoder_io(h: Handle, n: int, params=None, gamma=None, dgamma=None, d2gamma=None,
+                      grad_params=None) -> None:
+    n_params, width = _sizes(h)
+    d = int(h.spec["d"])
+    d2 = d if h.spec.get("d2_mode") == "diag" else 1
+    _expect(params, n_params, "params")
+    _expect(grad_params, n_params, "grad_params")
+    _expect(gamma, n * width, "gamma")
+    _expect(dgamma, n * d * width, "dgamma")
+    _expect(d2gamma, n * d2 * width, "d2gamma")
+
+
+def mlp_param_count(n_in: int, hidden: int, depth: int) -> int:
+    """Floats of the packed SIREN parameters W1, b1, ..., Wo, bo (output width 1)."""
+    n = 0
+    for k in range(depth + 1):
+        fi = n_in if k == 0 else hidden
+        fo = 1 if k == depth else hidden
+        n += fi * fo + fo
+    return n
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -133,7 +186,8 @@ def hashenc_param_layout(h: Handle, order: int, level: int) -> dict:
 
 def hashenc_forward(h: Handle, x: torch.Tensor, params: torch.Tensor, gamma=None, dgamma=None,
                     d2gamma=None, stream=None) -> None:
-    n = x.shape[0]
+    n = _points(h, x)
+    _check_encoder_io(h, n, params, gamma, dgamma, d2gamma)
     check(load().hashenc_forward(h, n, _dev_ptr(x, "x"), _dev_ptr(params, "params"),
                                  _dev_ptr(gamma, "gamma"), _dev_ptr(dgamma, "dgamma"),
                                  _dev_ptr(d2gamma, "d2gamma"), _stream(stream)))
@@ -141,7 +195,8 @@ def hashenc_forward(h: Handle, x: torch.Tensor, params: torch.Tensor, gamma=None
 
 def hashenc_backward(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_d2gamma=None,
                      grad_params=None, stream=None) -> None:
-    n = x.shape[0]
+    n = _points(h, x)
+    _check_encoder_io(h, n, None, g_gamma, g_dgamma, g_d2gamma, grad_params)
     check(load().hashenc_backward(h, n, _dev_ptr(x, "x"), _dev_ptr(g_gamma, "g_gamma"),
                                   _dev_ptr(g_dgamma, "g_dgamma"), _dev_ptr(g_d2gamma, "g_d2gamma"),
                                   _dev_ptr(grad_params, "grad_params"), _stream(stream)))
@@ -163,8 +218,10 @@ def _ws(workspace):
 
 def hashenc_forward_ws(h: Handle, x: torch.Tensor, params: torch.Tensor, gamma=None, dgamma=None,
                        d2gamma=None, workspace: torch.Tensor | None = None, stream=None) -> None:
+    n = _points(h, x)
+    _check_encoder_io(h, n, params, gamma, dgamma, d2gamma)
     ws_ptr, ws_bytes = _ws(workspace)
-    check(load().hashenc_forward_ws(h, x.shape[0], _dev_ptr(x, "x"), _dev_ptr(params, "params"),
+    check(load().hashenc_forward_ws(h, n, _dev_ptr(x, "x"), _dev_ptr(params, "params"),
                                     _dev_ptr(gamma, "gamma"), _dev_ptr(dgamma, "dgamma"),
                                     _dev_ptr(d2gamma, "d2gamma"), ws_ptr, ws_bytes, _stream(stream)))
 
@@ -177,7 +234,8 @@ def hashenc_backward_workspace_size(h: Handle, n: int) -> int:
 
 def hashenc_backward_ws(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_d2gamma=None,
                         grad_params=None, workspace: torch.Tensor | None = None, stream=None) -> None:
-    n = x.shape[0]
+    n = _points(h, x)
+    _check_encoder_io(h, n, None, g_gamma, g_dgamma, g_d2gamma, grad_params)
     ws_ptr, ws_bytes = _ws(workspace)
     check(load().hashenc_backward_ws(h, n, _dev_ptr(x, "x"), _dev_ptr(g_gamma, "g_gamma"),
                                      _dev_ptr(g_dgamma, "g_dgamma"), _dev_ptr(g_d2gamma, "g_d2gamma"),
@@ -207,8 +265,15 @@ def hashenc_residual_workspace_size(h: Handle, mlp: Mlp, n: int) -> int:
 def hashenc_residual(h: Handle, mlp: Mlp, x: torch.Tensor, params: torch.Tensor,
                      mlp_params: torch.Tensor, residual, loss: torch.Tensor, grad_params,
                      grad_mlp, workspace: torch.Tensor, stream=None) -> None:
+    n = _points(h, x)
+    _check_encoder_io(h, n, params, grad_params=grad_params)
+    n_mlp = mlp_param_count(mlp.n_in, mlp.hidden, mlp.depth)
+    _expect(mlp_params, n_mlp, "mlp_params")
+    _expect(grad_mlp, n_mlp, "grad_mlp")
+    _expect(residual, n, "residual")
+    _expect(loss, 1, "loss")
     m = mlp.as_c()
-    check(load().hashenc_residual(h, ctypes.byref(m), x.shape[0], _dev_ptr(x, "x"),
+    check(load().hashenc_residual(h, ctypes.byref(m), n, _dev_ptr(x, "x"),
                                   _dev_ptr(params, "params"), _dev_ptr(mlp_params, "mlp_params"),
                                   _dev_ptr(residual, "residual"), _dev_ptr(loss, "loss"),
                                   _dev_ptr(grad_params, "grad_params"), _dev_ptr(grad_mlp, "grad_mlp"),
@@ -226,8 +291,16 @@ def hashenc_fd_residual_workspace_size(h: Handle, mlp: Mlp, n: int) -> int:
 def hashenc_fd_residual(h: Handle, mlp: Mlp, eps: float, x: torch.Tensor, params: torch.Tensor,
                         mlp_params: torch.Tensor, u_stencil, residual, loss: torch.Tensor, grad_params,
                         grad_mlp, workspace: torch.Tensor, stream=None) -> None:
+    n = _points(h, x)
+    _check_encoder_io(h, n, params, grad_params=grad_params)
+    n_mlp = mlp_param_count(mlp.n_in, mlp.hidden, mlp.depth)
+    _expect(mlp_params, n_mlp, "mlp_params")
+    _expect(grad_mlp, n_mlp, "grad_mlp")
+    _expect(u_stencil, n * (2 * int(h.spec["d"]) + 1), "u_stencil")
+    _expect(residual, n, "residual")
+    _expect(loss, 1, "loss")
     m = mlp.as_c()
-    check(load().hashenc_fd_residual(h, ctypes.byref(m), float(eps), x.shape[0], _dev_ptr(x, "x"),
+    check(load().hashenc_fd_residual(h, ctypes.byref(m), float(eps), n, _dev_ptr(x, "x"),
                                      _dev_ptr(params, "params"), _dev_ptr(mlp_params, "mlp_params"),
                                      _dev_ptr(u_stencil, "u_stencil"), _dev_ptr(residual, "residual"),
                                      _dev_ptr(loss, "loss"), _dev_ptr(grad_params, "grad_params"),
@@ -238,11 +311,14 @@ def hashenc_fd_residual(h: Handle, mlp: Mlp, eps: float, x: torch.Tensor, params
 
 def hashenc_debug_indices(h: Handle, x: torch.Tensor, order: int, out_rows: torch.Tensor,
                           stream=None) -> None:
-    check(load().hashenc_debug_indices(h, x.shape[0], _dev_ptr(x, "x"), order,
+    n = _points(h, x)
+    _expect(out_rows, n * int(h.spec["L"]) * (1 << int(h.spec["d"])), "out_rows")
+    check(load().hashenc_debug_indices(h, n, _dev_ptr(x, "x"), order,
                                        _dev_ptr(out_rows, "out_rows", dtype=torch.int32), _stream(stream)))
 
 
 def hashenc_diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    _expect(dst, src.numel(), "dst")
     check(load().hashenc_diag_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), src.numel(), _stream(stream)))
 
 

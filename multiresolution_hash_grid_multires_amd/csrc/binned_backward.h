@@ -213,6 +213,21 @@ hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspa
 
 constexpr int32_t kMaxBins = 16384;
 constexpr int64_t kBinChunkPoints = int64_t(1) << 21;  // points per pass of the binned backward
+// Entry indices (bin starts, work-item ranges, per-tile slots) are int32: a chunk holds at
+// most this many entries, which leaves room for one work item past the last entry.
+constexpr int64_t kMaxChunkEntries = (int64_t(1) << 31) - (int64_t(1) << 20);
+
+// Entries per point at most (every corner its own entry; Hermite: one per order table).
+inline int64_t bin_entries_per_point(int d, int L, bool hermite) {
+  return (int64_t)L * (1 << d) * (hermite ? d + 1 : 1);
+}
+// Points per pass of the binned backward: kBinChunkPoints, fewer when the chunk's entries
+// would not fit the int32 indices (L = 32 Hermite 3D reaches 2^31 entries at 2^21 points);
+// a multiple of 1024 so every tile size divides it.
+inline int64_t bin_chunk_points(const Grid& g, int d, bool hermite) {
+  const int64_t cap = (kMaxChunkEntries / bin_entries_per_point(d, g.L, hermite)) & ~int64_t(1023);
+  return cap < kBinChunkPoints ? cap : kBinChunkPoints;
+}
 
 // Whether this configuration's bins and staging fit the LDS budgets of the binned path.
 bool binned_fits(const Grid& g, int d, int F, bool hermite);

@@ -313,9 +313,7 @@ __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g
 }
 
 // Workspace bound: every corner its own entry (single records on d-linear segments).
-int64_t entries_per_point(int d, int L, bool hermite) {
-  return (int64_t)L * (1 << d) * (hermite ? d + 1 : 1);
-}
+int64_t entries_per_point(int d, int L, bool hermite) { return bin_entries_per_point(d, L, hermite); }
 
 int64_t floats_per_point(const BinPlan& bp, int d) {
   if (bp.records) return (int64_t)bp.L * (1 << d) * (2 + bp.width[0]);
@@ -480,7 +478,8 @@ bool binned_fits(const Grid& g, int d, int F, bool hermite) {
 size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite, int64_t n) {
   BinPlan bp;
   make_bin_plan(g, d, F, hermite, bp);
-  const int64_t c = n < kBinChunkPoints ? n : kBinChunkPoints;
+  const int64_t cmax = bin_chunk_points(g, d, hermite);
+  const int64_t c = n < cmax ? n : cmax;
   return bin_workspace_layout(bp, c, entries_per_point(d, g.L, hermite), floats_per_point(bp, d),
                               bin_tile_points(bp, d, F, hermite)).total;
 }
@@ -491,11 +490,12 @@ hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2
                                hipStream_t s) {
   BinPlan bp;
   make_bin_plan(g, d, F, hermite, bp);
-  if (u_levels && n > kBinChunkPoints) return hipErrorInvalidValue;  // one chunk only
+  const int64_t cmax = bin_chunk_points(g, d, hermite);
+  if (u_levels && n > cmax) return hipErrorInvalidValue;  // one chunk only
   char* ws = static_cast<char*>(workspace);
   const int64_t LF = (int64_t)g.Lrow * F;  // upstream row stride
-  for (int64_t p0 = 0; p0 < n; p0 += kBinChunkPoints) {
-    const int64_t c = (n - p0) < kBinChunkPoints ? (n - p0) : kBinChunkPoints;
+  for (int64_t p0 = 0; p0 < n; p0 += cmax) {
+    const int64_t c = (n - p0) < cmax ? (n - p0) : cmax;
     const BinWorkspace w = bin_workspace_layout(bp, c, entries_per_point(d, g.L, hermite), floats_per_point(bp, d),
                                                 bin_tile_points(bp, d, F, hermite));
     const float* xc = x + p0 * d;

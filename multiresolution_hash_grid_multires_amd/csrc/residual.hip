@@ -1066,7 +1066,14 @@ __global__ __launch_bounds__(256) void reduce_partials_apply_kernel(const double
   }
 }
 
-constexpr int64_t kChunk = int64_t(1) << 21;  // points per pass over the workspace
+constexpr int64_t kChunk = int64_t(1) << 21;  // points per pass over the workspace (at most)
+
+// Points per pass: one binned-backward chunk, so the SIREN kernel's level-major upstream
+// feeds the binned backward directly.
+int64_t residual_chunk_points(const Grid& g, int d) {
+  const int64_t b = bin_chunk_points(g, d, true);
+  return b < kChunk ? b : kChunk;
+}
 constexpr int kSirenBlocks = 256;  // one workgroup per CU (LDS-limited)
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -1077,7 +1084,8 @@ struct WorkspaceLayout {
 
 WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t n_mlp, bool binned) {
   const int LF = g.L * F;
-  const int64_t c = n < kChunk ? n : kChunk;
+  const int64_t cmax = residual_chunk_points(g, d);
+  const int64_t c = n < cmax ? n : cmax;
   WorkspaceLayout w;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
@@ -1179,14 +1187,16 @@ hipError_t fd_dispatch(int d, int depth, int in, const MlpArgs& a, int64_t n, do
 
 // Centre points per FD chunk: the chunk's 2d+1 stencil sets fit one binned-backward chunk,
 // whose level-major upstream then comes straight from the SIREN kernel.
-int64_t fd_chunk_points(int d) { return (kBinChunkPoints / (2 * d + 1)) & ~int64_t(kMP - 1); }
+int64_t fd_chunk_points(const Grid& g, int d) {
+  return (bin_chunk_points(g, d, false) / (2 * d + 1)) & ~int64_t(kMP - 1);
+}
 
 struct FdWorkspaceLayout {
   size_t xp, xs, enc, up, partial, slices, bins, total;
 };
 
 FdWorkspaceLayout fd_workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t n_mlp, bool binned) {
-  const int64_t cmax = fd_chunk_points(d);
+  const int64_t cmax = fd_chunk_points(g, d);
   const int64_t c = n < cmax ? n : cmax;
   const int64_t cs = c * (2 * d + 1);
   FdWorkspaceLayout w;
@@ -1260,7 +1270,7 @@ hipError_t run_fd_residual(const Grid& g, int d, int F, int64_t n, const float* 
   const double inv_n = 1.0 / (double)n;
   const float inv_eps2 = (float)(1.0 / ((double)eps * (double)eps));
   const int S = 2 * d + 1;
-  const int64_t cmax = fd_chunk_points(d);
+  const int64_t cmax = fd_chunk_points(g, d);
   for (int64_t p0 = 0; p0 < n; p0 += cmax) {
     const int64_t c = (n - p0) < cmax ? (n - p0) : cmax;
     const float* xc = x + p0 * d;
@@ -1336,8 +1346,9 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
     hipError_t e = launch_hermite_pack(g, d, F, params, packed, s);
     if (e != hipSuccess) return e;
   }
-  for (int64_t p0 = 0; p0 < n; p0 += kChunk) {
-    const int64_t c = (n - p0) < kChunk ? (n - p0) : kChunk;
+  const int64_t cmax = residual_chunk_points(g, d);
+  for (int64_t p0 = 0; p0 < n; p0 += cmax) {
+    const int64_t c = (n - p0) < cmax ? (n - p0) : cmax;
     const float* xc = x + p0 * d;
     // Hermite forward straight into the level-major layout the SIREN kernels read
     hipError_t e = launch_hermite_forward(g, d, F, HASHENC_D2_LAPLACIAN, c, xc, params, packed, enc, false, nullptr,

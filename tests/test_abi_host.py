@@ -221,3 +221,74 @@ def test_derive_active_rejects_bad_count(n_active):
     assert out.value is None
     assert _lib.load().hashenc_derive_active(None, 1, ctypes.byref(out)) == _lib.HASHENC_EINVAL
     assert _lib.load().hashenc_derive_active(h, 1, None) == _lib.HASHENC_EINVAL
+
+
+# ---------------------------------------------------------------- binding size checks
+def test_binding_rejects_mismatched_sizes_before_launch():
+    """Every tensor's element count is checked against the layout before a pointer reaches
+    the library (host tensors: the size check comes before the device check)."""
+    import torch
+    h = api.hashenc_create({"d": 3, "L": 2, "F": 2, "kind": "hermite", "T": [1 << 10] * 4,
+                            "n_min": 4, "n_max": 8, "d2_mode": "diag"})
+    n_params, width, _ = api.hashenc_info(h)
+    n = 5
+    x = torch.zeros(n, 3)
+    good = dict(params=torch.zeros(n_params), gamma=torch.zeros(n, width),
+                dgamma=torch.zeros(n, 3, width), d2gamma=torch.zeros(n, 3, width))
+    # the right sizes pass the size check and stop at the device check
+    with pytest.raises(ValueError, match="device"):
+        api.hashenc_forward(h, x, **good)
+    for key in good:
+        bad = dict(good)
+        bad[key] = torch.zeros(good[key].numel() - 1)
+        with pytest.raises(ValueError, match=key):
+            api.hashenc_forward(h, x, **bad)
+        with pytest.raises(ValueError, match=key):
+            api.hashenc_forward_ws(h, x, **bad, workspace=None)
+    with pytest.raises(ValueError, match="x must be"):
+        api.hashenc_forward(h, torch.zeros(n, 2), **good)
+    ups = dict(g_gamma=torch.zeros(n, width), g_dgamma=torch.zeros(n, 3, width),
+               g_d2gamma=torch.zeros(n, 3, width), grad_params=torch.zeros(n_params))
+    for key in ups:
+        bad = dict(ups)
+        bad[key] = torch.zeros(ups[key].numel() + 3)
+        with pytest.raises(ValueError, match=key.replace("g_", "") if key != "grad_params" else key):
+            api.hashenc_backward(h, x, **bad)
+        with pytest.raises(ValueError, match=key.replace("g_", "") if key != "grad_params" else key):
+            api.hashenc_backward_ws(h, x, **bad)
+    mlp = api.Mlp(4, 16, 2, 30.0)
+    n_mlp = api.mlp_param_count(4, 16, 2)
+    assert n_mlp == 4 * 16 + 16 + 16 * 16 + 16 + 16 + 1
+    with pytest.raises(ValueError, match="mlp_params"):
+        api.hashenc_residual(h, mlp, x, good["params"], torch.zeros(n_mlp + 1), None, torch.zeros(1),
+                             None, None, torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="residual"):
+        api.hashenc_residual(h, mlp, x, good["params"], torch.zeros(n_mlp), torch.zeros(n - 1), torch.zeros(1),
+                             None, None, torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="out_rows"):
+        api.hashenc_debug_indices(h, x, 0, torch.zeros(n * 2 * 8 - 1, dtype=torch.int32))
+
+
+# ---------------------------------------------------------------- binned chunk bound
+def test_binned_chunk_keeps_entries_in_int32():
+    """The binned backward indexes a chunk's entries with int32.  A 32-level 3D Hermite grid
+    has 32 * 8 * 4 = 1024 entries per point, so a 2^21-point chunk would hold 2^31; the chunk
+    is cut to the largest multiple of 1024 points with at most 2^31 - 2^20 entries, and the
+    workspace stops growing there."""
+    h = api.hashenc_create({"d": 3, "L": 32, "F": 1, "kind": "hermite", "T": [1 << 19] * 4,
+                            "n_min": 16, "n_max": 2048, "d2_mode": "laplacian"})
+    epp = 32 * 8 * 4
+    cap = ((2 ** 31 - 2 ** 20) // epp) // 1024 * 1024
+    assert cap * epp < 2 ** 31 - 2 ** 18 and cap < 1 << 21
+    ws = lambda n: api.hashenc_backward_workspace_size(h, n)
+    assert ws(cap) > 0  # the binned path takes this configuration
+    assert ws(1 << 21) == ws(cap) == ws(3 * cap)
+    assert ws(cap - 1024) < ws(cap)
+    # the fused residual runs one binned chunk per pass: its workspace stops growing there too
+    mlp = api.Mlp(32, 64, 2, 30.0)
+    rs = lambda n: api.hashenc_residual_workspace_size(h, mlp, n)
+    assert rs(1 << 21) == rs(cap) > rs(cap - 1024)
+    # 16 levels (the PINN workload) keep the full 2^21-point chunk
+    h16 = api.hashenc_create({"d": 3, "L": 16, "F": 2, "kind": "hermite", "T": [1 << 19] * 4,
+                              "n_min": 16, "n_max": 1024, "d2_mode": "laplacian"})
+    assert api.hashenc_backward_workspace_size(h16, 1 << 21) > api.hashenc_backward_workspace_size(h16, cap)
