@@ -57,10 +57,26 @@ def _kappa(ref, x, d, eps, bo):
     return float(np.max(np.abs(ref["u_stencil"] - bo) @ np.abs(c)) / np.max(np.abs(lap)))
 
 
+def _assembly_close(got, x, d, eps):
+    """The residual the GPU returns against the central-difference formula evaluated in fp64
+    on the GPU's own stencil values: r = sum_i (u_{2i+1} - 2 u_0 + u_{2i+2}) / eps^2 - g(x).
+    The returned u are fp32 roundings (each within 2^-24 |u| of the value the kernel
+    differenced), which the stencil weights sum_s |c_s| = 4d / eps^2 carry into r; beyond that
+    the assembly is held to 1e-5 of max|r|, whatever the error of u itself."""
+    u = got["u_stencil"].astype(np.float64)
+    lap = sum(u[:, 2 * i + 1] - 2.0 * u[:, 0] + u[:, 2 * i + 2] for i in range(d)) / eps ** 2
+    g = -d * np.pi ** 2 * np.prod(np.sin(np.pi * x.astype(np.float64)), axis=1)
+    r64 = lap - g
+    err = float(np.max(np.abs(got["r"] - r64)))
+    bar = 1e-5 * float(np.max(np.abs(r64))) + (4 * d / eps ** 2) * 2.0 ** -24 * float(np.max(np.abs(u)))
+    assert err <= bar, f"FD assembly: {err:.3e} vs bar {bar:.3e}"
+
+
 def _compare(orc, spec, hidden, depth, omega, eps, x, params, mlp_params):
     d = spec["d"]
     mlp = api.Mlp(spec["L"] * spec["F"], hidden, depth, omega)
     got = _run_gpu(spec, mlp, eps, x, params, mlp_params)
+    _assembly_close(got, x, d, eps)
     ref = orc.fd_residual(spec, hidden, depth, omega, eps, x, params, mlp_params)
     _close(got["u_stencil"], ref["u_stencil"], 1e-5, "u at the stencil points")
     dr = np.max(np.abs(got["r"] - ref["r"]))
@@ -175,14 +191,15 @@ def test_fd_argument_errors():
     p = torch.zeros(enc.n_params, device=DEV)
     loss = torch.empty(1, device=DEV)
     ok = api.Mlp(4, 16, 2, 30.0)
-    mp = torch.zeros(1024, device=DEV)
+    mp = torch.zeros(api.mlp_param_count(4, 16, 2), device=DEV)
     wsz = api.hashenc_fd_residual_workspace_size(enc.handle, ok, 64)
     ws = torch.empty(wsz, dtype=torch.uint8, device=DEV)
     for mlp, eps, code in [(api.Mlp(4, 16, 3, 30.0), 0.01, HASHENC_EUNSUPPORTED),
                            (api.Mlp(6, 16, 2, 30.0), 0.01, HASHENC_EINVAL),
                            (ok, 0.0, HASHENC_EINVAL), (ok, float("inf"), HASHENC_EINVAL)]:
+        mpm = torch.zeros(api.mlp_param_count(mlp.n_in, mlp.hidden, mlp.depth), device=DEV)
         with pytest.raises(HashencError) as e:
-            api.hashenc_fd_residual(enc.handle, mlp, eps, x, p, mp, None, None, loss, None, None, ws)
+            api.hashenc_fd_residual(enc.handle, mlp, eps, x, p, mpm, None, None, loss, None, None, ws)
         assert e.value.code == code
     with pytest.raises(HashencError) as e:  # workspace too small
         api.hashenc_fd_residual(enc.handle, ok, 0.01, x, p, mp, None, None, loss, None, None, ws[: wsz // 2])

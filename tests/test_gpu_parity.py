@@ -351,6 +351,38 @@ def test_full_size_forward_sampled(orc, name):
         _blocks_close(got["d2gamma"][idx], d2, spec, FWD_TOL, "d2gamma")
 
 
+@pytest.mark.parametrize("name", ["dlinear3d_L16_T19", "hermite3d_L16_T19", "hermite2d_L8_T14"])
+def test_full_size_forward_ws_sampled(orc, name):
+    """The workspace forward in the launch configuration the benchmark times: every level
+    active, all of the workload's points, the workspace shared with the backward (d-linear:
+    LDS levels, L2 passes and the level-major transpose; Hermite: packed tables, level-major
+    staging and the rearrangement into rows).  4096 sampled points and the last one against
+    the oracle, per level and component."""
+    W = I.WORKLOADS[name]
+    spec = W["spec"]
+    lay = orc.layout(spec)
+    params = _tables(name, lay["n_params"])
+    n = W["n_points"]
+    x = I.points(W["id"], n, spec["d"])
+    enc = api.HashGridEncoding(spec)
+    ws = enc.workspace(n)
+    shapes = enc.output_shapes(n)
+    outs = {k: torch.full(s, float("nan"), device=DEV) for k, s in shapes.items()}
+    api.hashenc_forward_ws(enc.handle, _dev(x), _dev(params), outs["gamma"], outs.get("dgamma"),
+                           outs.get("d2gamma"), ws)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in outs.items()}
+    for k, v in got.items():
+        assert np.isfinite(v).all(), f"{k}: unwritten entries"
+    idx = np.sort(np.random.default_rng(11).choice(n, 4096, replace=False))
+    idx[-1] = n - 1
+    g, dg, d2 = orc.forward(spec, x[idx], params)
+    _blocks_close(got["gamma"][idx], g, spec, FWD_TOL, "gamma")
+    if spec["kind"] == "hermite":
+        _blocks_close(got["dgamma"][idx], dg, spec, FWD_TOL, "dgamma")
+        _blocks_close(got["d2gamma"][idx], d2, spec, FWD_TOL, "d2gamma")
+
+
 @pytest.mark.parametrize("name", ["dlinear3d_L16_T19", "hermite3d_L16_T19"])
 def test_full_size_backward(orc, name):
     W = I.WORKLOADS[name]

@@ -118,6 +118,20 @@ def test_residual_full_size(orc):
     _close(gp, wa * gpa.astype(np.float64) + wb * gpb, 1e-4, "grad_params halves")
 
 
+def test_residual_full_size_against_oracle(orc):
+    """The PINN workload as the benchmark runs it: all 2^21 points (the uniform half and the
+    clustered half) in one call, every residual, the loss and every gradient block -- per
+    table-level block and per MLP parameter block -- against the oracle on the same points."""
+    W = I.WORKLOADS[NAME]
+    spec, m = W["spec"], W["mlp"]
+    lay = orc.layout(spec)
+    params = I.tables(W["id"], lay["n_params"], W["tables"])
+    mlp_params = I.siren_mlp(W["id"], spec["L"] * spec["F"], m["hidden"], m["depth"])
+    x = I.points(W["id"], W["n_points"], spec["d"], clustered_half=True)
+    assert x.shape[0] == 1 << 21
+    _compare(orc, spec, m["hidden"], m["depth"], m["omega"], x, params, mlp_params)
+
+
 def test_residual_argument_errors():
     from multiresolution_hash_grid_multires_amd._lib import HashencError
     W = I.WORKLOADS[NAME]
@@ -131,7 +145,8 @@ def test_residual_argument_errors():
     with pytest.raises(HashencError):
         api.hashenc_residual(enc.handle, mlp, x, p, mp, None, loss, None, None, small)
     with pytest.raises(HashencError):
-        api.hashenc_residual(enc.handle, api.Mlp(16, 64, 2, 30.0), x, p, mp, None, loss, None, None, small)
+        api.hashenc_residual(enc.handle, api.Mlp(16, 64, 2, 30.0), x, p, torch.zeros(api.mlp_param_count(16, 64, 2),
+                             device=DEV), None, loss, None, None, small)
     lin = api.HashGridEncoding(I.WORKLOADS["dlinear3d_L16_T19"]["spec"])
     with pytest.raises(HashencError):
         api.hashenc_residual_workspace_size(lin.handle, mlp, 8)
