@@ -8,12 +8,17 @@ backward (scatter-add into the tables) with inputs already resident in GPU memor
 Prints ONE JSON line.  Besides the headline value it carries
   roofline      achieved algorithmic GB/s of the dominant kernel against the 8 TB/s HBM peak,
                 its average launch duration from HIP events on the launch stream, and the
-                HBM traffic measured by counters (when recorded for the current kernels);
+                HBM traffic of one launch measured by rocprofv3 counters -- read from
+                profiles/traffic_counters.json only when those counters were taken on
+                kernel sources identical to the ones built now (else null);
   cpu_baseline  the plain CPU oracle timed on the host cores on a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -28,17 +33,104 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "encoded points/s fwd+bwd (3D L=16 T=2^19 F=2) + % of HBM roofline"
 HEADLINE = "dlinear3d_L16_T19"
 
-# HBM traffic per call of an entry point, from rocprofv3 counters: FETCH_SIZE x 2 +
-# WRITE_SIZE x 1 (the factors the same counters need to read a plain copy kernel's known
-# traffic), summed over the entry point's kernels.  Valid only for the kernel sources they
-# were taken on (the per-kernel figures and commands are in profiles/); drop an entry when
-# one of its kernels changes.
-MEASURED_TRAFFIC_BYTES: dict = {
-    ("dlinear3d_L16_T19", "forward"): 1424102960,
-    ("dlinear3d_L16_T19", "backward"): 2482735543,
-    ("hermite3d_L16_T19", "forward"): 12100044348,
-    ("hermite3d_L16_T19", "backward"): 26630460758,
+# Counter-measured traffic per entry-point call: written by --summarize-counters from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script, scaled by what the same
+# counters read for the copy kernel's known traffic, and stamped with the digest of the
+# kernel sources it was taken on.  A figure whose digest differs from the current sources
+# is not reported.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# kernels of each entry point (name fragments), for summing counters per call
+ENTRY_KERNELS = {
+    "forward": ("forward", "pack_kernel", "levels_to_rows", "level_major_to_rows", "zero_columns"),
+    "backward": ("count_kernel", "scan_", "plan_kernel", "scatter_kernel", "reduce_kernel", "upstream_levels",
+                 "backward_kernel"),
 }
+
+
+def source_digest() -> str:
+    """sha256 over the kernel and ABI sources (the library the counters were taken on)."""
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "multiresolution_hash_grid_multires_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(pkg, "*.hip")) + glob.glob(os.path.join(pkg, "*.h"))
+                   + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, entry: str):
+    """(bytes per call, note) from the counter file when it matches the current sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter record"
+    if rec.get("source_digest") != source_digest():
+        return None, "counters were taken on other kernel sources"
+    v = rec.get("workloads", {}).get(workload, {}).get(entry)
+    return (int(v) if v is not None else None), ("profiles/traffic_counters.json" if v is not None
+                                                  else "no counters for this workload")
+
+
+def _counter_rows(run_dir: str, counter: str) -> dict:
+    """{kernel name: [per-dispatch values]} from a rocprofv3 --pmc CSV under run_dir."""
+    out: dict = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    if not out:
+        raise SystemExit(f"no {counter} rows under {run_dir}")
+    return out
+
+
+def summarize_counters(args) -> int:
+    """Turn four rocprofv3 --pmc runs (the workload's FETCH_SIZE and WRITE_SIZE, the copy
+    calibration's FETCH_SIZE and WRITE_SIZE) into bytes per entry-point call, and record them
+    in profiles/traffic_counters.json with the current source digest."""
+    wl_fetch, wl_write, cp_fetch, cp_write = args.summarize_counters
+    copy_bytes = args.copy_bytes or (1 << 30)
+    kib = copy_bytes / 1024.0
+    cf = _counter_rows(cp_fetch, "FETCH_SIZE")
+    cw = _counter_rows(cp_write, "WRITE_SIZE")
+    ck = next(k for k in cf if "copy_kernel" in k)
+    f_factor = kib / (sum(cf[ck]) / len(cf[ck]))
+    w_factor = kib / (sum(cw[ck]) / len(cw[ck]))
+    fetch = _counter_rows(wl_fetch, "FETCH_SIZE")
+    write = _counter_rows(wl_write, "WRITE_SIZE")
+    calls = args.steps + args.warmup
+    per_kernel, entries = {}, {"forward": 0.0, "backward": 0.0}
+    for name, vals in fetch.items():
+        entry = next((e for e, frags in ENTRY_KERNELS.items() if any(fr in name for fr in frags)), None)
+        if entry is None or "copy_kernel" in name:
+            continue
+        wv = write.get(name, [0.0])
+        per_call = 1024.0 * (f_factor * sum(vals) + w_factor * sum(wv) * len(vals) / len(wv)) / calls
+        per_kernel[name] = {"entry": entry, "dispatches_per_call": len(vals) / calls,
+                            "fetch_KiB_per_dispatch": sum(vals) / len(vals),
+                            "write_KiB_per_dispatch": sum(wv) / len(wv), "bytes_per_call": round(per_call)}
+        entries[entry] += per_call
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    digest = source_digest()
+    if rec.get("source_digest") != digest:
+        rec = {"source_digest": digest, "workloads": {}, "kernels": {}}
+    rec["calibration"] = {"copy_bytes": copy_bytes, "fetch_factor": round(f_factor, 4),
+                          "write_factor": round(w_factor, 4)}
+    rec["workloads"][args.workload] = {k: round(v) for k, v in entries.items()}
+    rec["kernels"][args.workload] = per_kernel
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps({"workload": args.workload, **rec["workloads"][args.workload],
+                      "calibration": rec["calibration"]}), flush=True)
+    return 0
 
 
 def algorithmic_bytes_per_point(spec: dict) -> dict:
@@ -309,7 +401,14 @@ def main() -> int:
                     help="instead of the benchmark, time torch's fill of this many bytes (write-only bandwidth)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("WL_FETCH", "WL_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="instead of the benchmark, turn the output folders of four rocprofv3 --pmc runs "
+                         "(this workload's FETCH_SIZE and WRITE_SIZE runs with the same --steps/--warmup, "
+                         "the copy calibration's FETCH_SIZE and WRITE_SIZE runs with the same --copy-bytes) "
+                         "into bytes per entry-point call in profiles/traffic_counters.json")
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(args)
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
@@ -349,8 +448,14 @@ def main() -> int:
     grad = torch.zeros(enc.n_params, device=dev)
     stream = torch.cuda.current_stream()
     workspace = enc.workspace(n) if args.backward == "binned" else None
+    # the backward the library actually runs: the workspace entry point falls back to the
+    # atomic scatter-add when the configuration has no binned plan (RBF, 4D Hermite)
+    backward_path = ("binned" if workspace is not None and api.hashenc_backward_workspace_size(enc.handle, n) > 0
+                     else "atomic")
 
     def step(ev=None):
+        if ev is not None:
+            ev[3].record(stream)
         grad.zero_()
         if ev is not None:
             ev[0].record(stream)
@@ -373,7 +478,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, HIP events on the launch stream around each kernel
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -387,6 +492,7 @@ def main() -> int:
     total_ms = start.elapsed_time(stop)
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    step_median_ms = float(np.median([e[3].elapsed_time(e[2]) for e in evs]))
     ms_per_step = total_ms / args.steps
     value = n / (ms_per_step * 1e-3)
 
@@ -396,18 +502,18 @@ def main() -> int:
     for k in kern.values():
         k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
     dom = max(kern, key=lambda k: kern[k]["ms"])
-    # recorded for the default (workspace) entry points only
-    traffic = (MEASURED_TRAFFIC_BYTES.get((args.workload, dom))
-               if workspace is not None and not args.active_levels else None)
+    # counters are recorded for the default (workspace) entry points with every level active
+    traffic, traffic_note = ((recorded_traffic(args.workload, dom)) if workspace is not None and not args.active_levels
+                             else (None, "counters recorded for the workspace entry points, all levels active"))
     roofline = {"bound": "hbm", "achieved": round(kern[dom]["GBps"], 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(kern[dom]["GBps"] / HBM_PEAK_GBPS, 4),
-                "traffic": traffic,
+                "traffic": traffic, "traffic_source": traffic_note, "source_digest": source_digest(),
                 "kernel": ("hashenc_" + dom + ("_ws" if workspace is not None else "")
                            + f" ({spec['kind']}; its kernels back to back on one stream)"),
                 "avg_launch_ms": round(kern[dom]["ms"], 4),
                 "alg_bytes_per_launch": kern[dom]["alg_bytes"]}
-    # the same launch against the copy kernel's bandwidth measured now, and the counter-
-    # measured traffic of the launch as a bandwidth
+    # the same launch against the copy kernel's bandwidth measured now (read + write), and the
+    # counter-measured traffic of the launch as a bandwidth
     achievable = copy_bandwidth(torch, api)
     roofline["achievable_GBps"] = round(achievable, 1)
     roofline["frac_of_achievable"] = round(kern[dom]["GBps"] / achievable, 4)
@@ -464,8 +570,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "n_points": n, "d": spec["d"], "L": spec["L"],
-                   "F": spec["F"], "T": spec["T"], "kind": spec["kind"], "backward": args.backward,
+                   "F": spec["F"], "T": spec["T"], "kind": spec["kind"], "backward": backward_path,
                    "active_levels": int(spec.get("active_levels") or spec["L"])},
+        "ms_per_step_median": round(step_median_ms, 4),
         "hbm_roofline_pct_step": round(100.0 * value * step_alg / (HBM_PEAK_GBPS * 1e9), 2),
         "kernels": {k: {"ms": round(v["ms"], 4), "GBps": round(v["GBps"], 1)} for k, v in kern.items()},
         "roofline": roofline,

@@ -26,10 +26,31 @@ __global__ __launch_bounds__(kBlock) void debug_indices_kernel(const Grid g, int
   }
 }
 
-__global__ __launch_bounds__(kBlock) void copy_kernel(const float4* __restrict__ src,
-                                                      float4* __restrict__ dst, int64_t n4) {
-  const int64_t stride = (int64_t)gridDim.x * kBlock;
-  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
+// Streaming copy tuned for HBM: a workgroup moves whole 16 KB pieces, each lane four 16-byte
+// loads in flight before its four stores, with the non-temporal cache policy on both sides
+// (nothing is reused).  Of the variants measured on MI355X over 4 GiB (one or four loads per
+// lane, temporal or not, 1024..8192 workgroups, eight loads per lane) this one was fastest:
+// 5.44 TB/s of read + write against 4.83 TB/s for one plain load per lane.
+constexpr int kCopyUnroll = 4;
+constexpr int64_t kCopyPiece = (int64_t)kBlock * kCopyUnroll;  // float4 per workgroup piece
+constexpr int kCopyBlocks = 4096;
+typedef float copy_f4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kBlock) void copy_kernel(const copy_f4* __restrict__ src,
+                                                      copy_f4* __restrict__ dst, int64_t n4) {
+  const int64_t pieces = n4 / kCopyPiece;
+  for (int64_t c = blockIdx.x; c < pieces; c += gridDim.x) {
+    const int64_t base = c * kCopyPiece + threadIdx.x;
+    copy_f4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(src + base + u * kBlock);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], dst + base + u * kBlock);
+  }
+  // the float4 past the last whole piece
+  for (int64_t i = pieces * kCopyPiece + (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * kBlock)
+    dst[i] = src[i];
 }
 
 __global__ void copy_tail_kernel(const float* __restrict__ src, float* __restrict__ dst,
@@ -81,10 +102,10 @@ hipError_t launch_debug_indices(const Grid& g, int d, int order, int64_t n, cons
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t s) {
   const int64_t n4 = n / 4;
   if (n4 > 0) {
-    int64_t blocks = (n4 + kBlock - 1) / kBlock;
-    if (blocks > 256 * 64) blocks = 256 * 64;  // grid-stride: 64 blocks per CU
+    int64_t blocks = (n4 + kCopyPiece - 1) / kCopyPiece;
+    if (blocks > kCopyBlocks) blocks = kCopyBlocks;  // grid-stride over the pieces
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s,
-                       reinterpret_cast<const float4*>(src), reinterpret_cast<float4*>(dst), n4);
+                       reinterpret_cast<const copy_f4*>(src), reinterpret_cast<copy_f4*>(dst), n4);
   }
   if (n % 4) hipLaunchKernelGGL(copy_tail_kernel, dim3(1), dim3(4), 0, s, src, dst, n4 * 4, n);
   return hipGetLastError();

@@ -53,6 +53,13 @@
  * Parity of the hash against any third-party implementation is unpinned (the
  * pages print no example value); it is pinned against its own definition's
  * special cases and invariants in the test-suite.
+ *
+ * Working precision.  Everything after the fp32 position stage is computed in
+ * `real`: fp64 in the oracle proper.  A second build with -DORC_FP32 reruns the
+ * same per-point arithmetic in fp32 (float operations, float sin / cos / exp /
+ * pow), which measures the fp32 rounding floor of each output; the buffers at the
+ * interface stay fp64 and sums over points (gradients, loss) stay fp64 in both
+ * builds, so the floor is that of the per-point arithmetic alone.
  */
 #include <math.h>
 #include <stdint.h>
@@ -60,6 +67,20 @@
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
+#endif
+
+#ifdef ORC_FP32
+typedef float real;
+#define R_SIN sinf
+#define R_COS cosf
+#define R_EXP expf
+#define R_POW powf
+#else
+typedef double real;
+#define R_SIN sin
+#define R_COS cos
+#define R_EXP exp
+#define R_POW pow
 #endif
 
 #define ORC_MAX_LEVELS 32
@@ -221,7 +242,7 @@ static int64_t vertex_row(const orc_cfg* c, int k, int l, const uint32_t* v) {
 
 /* Cell of point x at level l [INGP-explainer, step 1: the 2^d grid vertices around x].
  * Position stage in IEEE fp32: p = x*N_l rounded once, base = floor, t = p - base. */
-static void locate(const orc_cfg* c, int l, const float* x, uint32_t* base, double* t) {
+static void locate(const orc_cfg* c, int l, const float* x, uint32_t* base, real* t) {
   volatile float nl = (float)c->N[l];
   for (int i = 0; i < c->d; ++i) {
     float xi = x[i];
@@ -233,7 +254,7 @@ static void locate(const orc_cfg* c, int l, const float* x, uint32_t* base, doub
     if (b > c->N[l] - 1) b = c->N[l] - 1;
     float tf = p - (float)b; /* exact (Sterbenz) */
     base[i] = (uint32_t)b;
-    t[i] = (double)tf;
+    t[i] = (real)tf;
   }
 }
 
@@ -245,7 +266,7 @@ void orc_indices(const orc_cfg* c, int64_t n, const float* x, int k, int32_t* ou
   for (int64_t p = 0; p < n; ++p) {
     for (int l = 0; l < c->L; ++l) {
       uint32_t base[ORC_MAX_D];
-      double t[ORC_MAX_D];
+      real t[ORC_MAX_D];
       locate(c, l, x + p * c->d, base, t);
       for (int cc = 0; cc < nc; ++cc) {
         uint32_t v[ORC_MAX_D];
@@ -260,7 +281,7 @@ void orc_indices(const orc_cfg* c, int64_t n, const float* x, int k, int32_t* ou
  * corner bit cb (0 = near vertex at t=0, 1 = far vertex at t=1), derivative bit a.
  * Far corner: value basis 3t^2-2t^3, derivative basis t^3-t^2 (printed on the page);
  * near corner: their reflections t -> 1-t (derivative basis changes sign). */
-static void hermite_1d(int cb, int a, double t, double* B, double* dB, double* d2B) {
+static void hermite_1d(int cb, int a, real t, real* B, real* dB, real* d2B) {
   if (!a && !cb) { *B = 1 - 3 * t * t + 2 * t * t * t; *dB = -6 * t + 6 * t * t; *d2B = -6 + 12 * t; }
   else if (!a && cb) { *B = 3 * t * t - 2 * t * t * t; *dB = 6 * t - 6 * t * t; *d2B = 6 - 12 * t; }
   else if (a && !cb) { *B = t - 2 * t * t + t * t * t; *dB = 1 - 4 * t + 3 * t * t; *d2B = -4 + 6 * t; }
@@ -271,24 +292,24 @@ static void hermite_1d(int cb, int a, double t, double* B, double* dB, double* d
  * theta^(alpha) at that corner in gamma (w0), in d gamma/dx_i (w1[i]) and in
  * d^2 gamma/dx_i^2 (w2[i]).  Hermite: Delta x^{|alpha|} H^(alpha)(t) with the chain rule
  * d/dx = N_l d/dt; d-linear: prod_i (c_i ? t_i : 1-t_i), alpha = 0 only. */
-static void corner_weights(const orc_cfg* c, int l, int cc, int alpha, const double* t,
-                           double* w0, double* w1, double* w2) {
-  const double Nl = (double)c->N[l];
+static void corner_weights(const orc_cfg* c, int l, int cc, int alpha, const real* t,
+                           real* w0, real* w1, real* w2) {
+  const real Nl = (real)c->N[l];
   if (c->kind == 0) {
-    double w = 1.0;
+    real w = 1.0;
     for (int i = 0; i < c->d; ++i) w *= ((cc >> i) & 1) ? t[i] : 1.0 - t[i];
     *w0 = w;
     return;
   }
-  double B[ORC_MAX_D], dB[ORC_MAX_D], d2B[ORC_MAX_D];
+  real B[ORC_MAX_D], dB[ORC_MAX_D], d2B[ORC_MAX_D];
   for (int i = 0; i < c->d; ++i)
     hermite_1d((cc >> i) & 1, (alpha >> i) & 1, t[i], &B[i], &dB[i], &d2B[i]);
-  double s = pow(Nl, -(double)popcount_bits(alpha)); /* Delta x_l^{|alpha|} */
-  double prod = 1.0;
+  real s = R_POW(Nl, -(real)popcount_bits(alpha)); /* Delta x_l^{|alpha|} */
+  real prod = 1.0;
   for (int i = 0; i < c->d; ++i) prod *= B[i];
   *w0 = s * prod;
   for (int i = 0; i < c->d; ++i) {
-    double others = 1.0;
+    real others = 1.0;
     for (int k = 0; k < c->d; ++k) if (k != i) others *= B[k];
     w1[i] = s * Nl * dB[i] * others;
     w2[i] = s * Nl * Nl * d2B[i] * others;
@@ -304,16 +325,16 @@ static void corner_weights(const orc_cfg* c, int l, int cc, int alpha, const dou
  *     dphi/dp_i = -2 eps^2 (p_i - v_i) phi,  d^2phi/dp_i^2 = (4 eps^4 (p_i - v_i)^2 - 2 eps^2) phi,
  *     dw = (dphi - w dS) / S,  d^2w = (d^2phi - 2 dw dS - w d^2S) / S.
  * Returns the number of vertices. */
-static int rbf_weights(const orc_cfg* c, int l, const float* x, int64_t* rows, double* w,
-                       double (*w1)[ORC_MAX_D], double (*w2)[ORC_MAX_D]) {
+static int rbf_weights(const orc_cfg* c, int l, const float* x, int64_t* rows, real* w,
+                       real (*w1)[ORC_MAX_D], real (*w2)[ORC_MAX_D]) {
   const int d = c->d, k = c->rings;
-  const double e2 = c->eps * c->eps, N = (double)c->N[l];
+  const real e2 = (real)(c->eps * c->eps), N = (real)c->N[l];
   uint32_t base[ORC_MAX_D];
-  double t[ORC_MAX_D];
+  real t[ORC_MAX_D];
   locate(c, l, x, base, t);
-  double p[ORC_MAX_D];
-  for (int i = 0; i < d; ++i) p[i] = (double)base[i] + t[i]; /* = fl32(x N), exactly */
-  double phi[ORC_MAX_RBF_VERTS], d1[ORC_MAX_RBF_VERTS][ORC_MAX_D], d2[ORC_MAX_RBF_VERTS][ORC_MAX_D];
+  real p[ORC_MAX_D];
+  for (int i = 0; i < d; ++i) p[i] = (real)base[i] + t[i]; /* = fl32(x N), exactly */
+  real phi[ORC_MAX_RBF_VERTS], d1[ORC_MAX_RBF_VERTS][ORC_MAX_D], d2[ORC_MAX_RBF_VERTS][ORC_MAX_D];
   int nv = 0;
   const int side = 2 * k;
   int total = 1;
@@ -328,11 +349,11 @@ static int rbf_weights(const orc_cfg* c, int l, const float* x, int64_t* rows, d
       if (v[i] < 0 || v[i] > (int64_t)c->N[l]) inside = 0;
     }
     if (!inside) continue;
-    double r2 = 0.0;
-    for (int i = 0; i < d; ++i) r2 += (p[i] - (double)v[i]) * (p[i] - (double)v[i]);
-    phi[nv] = exp(-e2 * r2);
+    real r2 = 0.0;
+    for (int i = 0; i < d; ++i) r2 += (p[i] - (real)v[i]) * (p[i] - (real)v[i]);
+    phi[nv] = R_EXP(-e2 * r2);
     for (int i = 0; i < d; ++i) {
-      const double del = p[i] - (double)v[i];
+      const real del = p[i] - (real)v[i];
       d1[nv][i] = -2.0 * e2 * del * phi[nv] * N;
       d2[nv][i] = (4.0 * e2 * e2 * del * del - 2.0 * e2) * phi[nv] * N * N;
     }
@@ -341,7 +362,7 @@ static int rbf_weights(const orc_cfg* c, int l, const float* x, int64_t* rows, d
     rows[nv] = vertex_row(c, 0, l, vu);
     ++nv;
   }
-  double S = 0.0, S1[ORC_MAX_D] = {0}, S2[ORC_MAX_D] = {0};
+  real S = 0.0, S1[ORC_MAX_D] = {0}, S2[ORC_MAX_D] = {0};
   for (int q = 0; q < nv; ++q) {
     S += phi[q];
     for (int i = 0; i < d; ++i) { S1[i] += d1[q][i]; S2[i] += d2[q][i]; }
@@ -373,21 +394,22 @@ void orc_forward(const orc_cfg* c, int64_t n, const float* x, const double* para
   for (int64_t p = 0; p < n; ++p) {
     for (int l = 0; l < c->L; ++l) {
       uint32_t base[ORC_MAX_D];
-      double t[ORC_MAX_D];
+      real t[ORC_MAX_D];
       locate(c, l, x + p * d, base, t);
-      double g0[ORC_MAX_F] = {0}, g1[ORC_MAX_F][ORC_MAX_D] = {{0}}, g2[ORC_MAX_F][ORC_MAX_D] = {{0}};
+      real g0[ORC_MAX_F] = {0}, g1[ORC_MAX_F][ORC_MAX_D] = {{0}}, g2[ORC_MAX_F][ORC_MAX_D] = {{0}};
       if (c->kind == 2 && l < active_levels(c)) {
         /* Gaussian RBF: sum over the k-ring box [DInf-Grid] */
         int64_t rows[ORC_MAX_RBF_VERTS];
-        double w[ORC_MAX_RBF_VERTS], w1[ORC_MAX_RBF_VERTS][ORC_MAX_D], w2[ORC_MAX_RBF_VERTS][ORC_MAX_D];
+        real w[ORC_MAX_RBF_VERTS], w1[ORC_MAX_RBF_VERTS][ORC_MAX_D], w2[ORC_MAX_RBF_VERTS][ORC_MAX_D];
         const int nv = rbf_weights(c, l, x + p * d, rows, w, w1, w2);
         for (int q = 0; q < nv; ++q) {
           const double* th = params + offs[l] + rows[q] * wid[l];
           for (int f = 0; f < c->F; ++f) {
-            g0[f] += w[q] * th[f];
+            const real v = (real)th[f];
+            g0[f] += w[q] * v;
             for (int i = 0; i < d; ++i) {
-              g1[f][i] += w1[q][i] * th[f];
-              g2[f][i] += w2[q][i] * th[f];
+              g1[f][i] += w1[q][i] * v;
+              g2[f][i] += w2[q][i] * v;
             }
           }
         }
@@ -402,14 +424,15 @@ void orc_forward(const orc_cfg* c, int64_t n, const float* x, const double* para
           const int64_t row = vertex_row(c, k, l, v);
           const int slot = c->kind == 1 ? slot_of_alpha(d, alpha) : 0;
           const double* th = params + offs[k * c->L + l] + row * wid[k * c->L + l] + (int64_t)slot * c->F;
-          double w0, w1[ORC_MAX_D], w2[ORC_MAX_D];
+          real w0, w1[ORC_MAX_D], w2[ORC_MAX_D];
           corner_weights(c, l, cc, alpha, t, &w0, w1, w2);
           for (int f = 0; f < c->F; ++f) {
-            g0[f] += w0 * th[f];
+            const real v = (real)th[f];
+            g0[f] += w0 * v;
             if (c->kind == 1)
               for (int i = 0; i < d; ++i) {
-                g1[f][i] += w1[i] * th[f];
-                g2[f][i] += w2[i] * th[f];
+                g1[f][i] += w1[i] * v;
+                g2[f][i] += w2[i] * v;
               }
           }
         }
@@ -423,7 +446,7 @@ void orc_forward(const orc_cfg* c, int64_t n, const float* x, const double* para
             if (c->d2_mode == 2) {
               for (int i = 0; i < d; ++i) d2gamma[(p * d + i) * LF + col] = g2[f][i];
             } else {
-              double lap = 0.0;
+              real lap = 0.0;
               for (int i = 0; i < d; ++i) lap += g2[f][i];
               d2gamma[p * LF + col] = lap;
             }
@@ -458,17 +481,17 @@ void orc_backward_f64(const orc_cfg* c, int64_t n, const float* x, const double*
       /* Gaussian RBF: each box vertex receives its weights times the upstream */
       for (int64_t p = 0; p < n; ++p) {
         int64_t rows[ORC_MAX_RBF_VERTS];
-        double w[ORC_MAX_RBF_VERTS], w1[ORC_MAX_RBF_VERTS][ORC_MAX_D], w2[ORC_MAX_RBF_VERTS][ORC_MAX_D];
+        real w[ORC_MAX_RBF_VERTS], w1[ORC_MAX_RBF_VERTS][ORC_MAX_D], w2[ORC_MAX_RBF_VERTS][ORC_MAX_D];
         const int nv = rbf_weights(c, l, x + p * d, rows, w, w1, w2);
         for (int q = 0; q < nv; ++q)
           for (int f = 0; f < c->F; ++f) {
             const int col = l * c->F + f;
-            double acc = 0.0;
-            if (g_gamma) acc += w[q] * g_gamma[p * LF + col];
+            real acc = 0.0;
+            if (g_gamma) acc += w[q] * (real)g_gamma[p * LF + col];
             for (int i = 0; i < d; ++i) {
-              if (g_dgamma) acc += w1[q][i] * g_dgamma[(p * d + i) * LF + col];
+              if (g_dgamma) acc += w1[q][i] * (real)g_dgamma[(p * d + i) * LF + col];
               if (g_d2) {
-                double up = c->d2_mode == 2 ? g_d2[(p * d + i) * LF + col] : g_d2[p * LF + col];
+                real up = (real)(c->d2_mode == 2 ? g_d2[(p * d + i) * LF + col] : g_d2[p * LF + col]);
                 acc += w2[q][i] * up;
               }
             }
@@ -479,7 +502,7 @@ void orc_backward_f64(const orc_cfg* c, int64_t n, const float* x, const double*
     }
     for (int64_t p = 0; p < n; ++p) {
       uint32_t base[ORC_MAX_D];
-      double t[ORC_MAX_D];
+      real t[ORC_MAX_D];
       locate(c, l, x + p * d, base, t);
       for (int cc = 0; cc < nc; ++cc) {
         uint32_t v[ORC_MAX_D];
@@ -488,17 +511,17 @@ void orc_backward_f64(const orc_cfg* c, int64_t n, const float* x, const double*
           if (popcount_bits(alpha) != k) continue;
           int64_t row = vertex_row(c, k, l, v);
           int slot = c->kind == 1 ? slot_of_alpha(d, alpha) : 0;
-          double w0, w1[ORC_MAX_D], w2[ORC_MAX_D];
+          real w0, w1[ORC_MAX_D], w2[ORC_MAX_D];
           corner_weights(c, l, cc, alpha, t, &w0, w1, w2);
           for (int f = 0; f < c->F; ++f) {
             const int col = l * c->F + f;
-            double acc = 0.0;
-            if (g_gamma) acc += w0 * g_gamma[p * LF + col];
+            real acc = 0.0;
+            if (g_gamma) acc += w0 * (real)g_gamma[p * LF + col];
             if (c->kind == 1) {
               for (int i = 0; i < d; ++i) {
-                if (g_dgamma) acc += w1[i] * g_dgamma[(p * d + i) * LF + col];
+                if (g_dgamma) acc += w1[i] * (real)g_dgamma[(p * d + i) * LF + col];
                 if (g_d2) {
-                  double up = c->d2_mode == 2 ? g_d2[(p * d + i) * LF + col] : g_d2[p * LF + col];
+                  real up = (real)(c->d2_mode == 2 ? g_d2[(p * d + i) * LF + col] : g_d2[p * LF + col]);
                   acc += w2[i] * up;
                 }
               }
@@ -562,7 +585,8 @@ int orc_residual(const orc_cfg* c, int32_t hidden, int32_t depth, double omega, 
 #endif
   double* gm_all = (double*)calloc((size_t)(nthreads * n_mlp), sizeof(double));
   const double inv_n = n > 0 ? 1.0 / (double)n : 0.0;
-  const double PI = 3.14159265358979323846;
+  const real PI = (real)3.14159265358979323846;
+  const real om = (real)omega;
 #pragma omp parallel
   {
     int tid = 0;
@@ -571,16 +595,16 @@ int orc_residual(const orc_cfg* c, int32_t hidden, int32_t depth, double omega, 
 #endif
     double* gm = gm_all + (int64_t)tid * n_mlp;
     /* tape: act[k] = inputs of layer k (R rows of width W), zs[k] = z, Z_i, Z_lap */
-    double* act = (double*)malloc(sizeof(double) * (size_t)((depth + 1) * R * W));
-    double* zs = (double*)malloc(sizeof(double) * (size_t)(depth * R * H));
-    double* bar = (double*)malloc(sizeof(double) * (size_t)(R * W));
-    double* nbar = (double*)malloc(sizeof(double) * (size_t)(R * W));
+    real* act = (real*)malloc(sizeof(real) * (size_t)((depth + 1) * R * W));
+    real* zs = (real*)malloc(sizeof(real) * (size_t)(depth * R * H));
+    real* bar = (real*)malloc(sizeof(real) * (size_t)(R * W));
+    real* nbar = (real*)malloc(sizeof(real) * (size_t)(R * W));
 #pragma omp for schedule(static)
     for (int64_t p = 0; p < n; ++p) {
       for (int j = 0; j < LF; ++j) {
-        act[0 * W + j] = g[p * LF + j];
-        for (int i = 0; i < d; ++i) act[(1 + i) * W + j] = dg[(p * d + i) * LF + j];
-        act[(1 + d) * W + j] = lp[p * LF + j];
+        act[0 * W + j] = (real)g[p * LF + j];
+        for (int i = 0; i < d; ++i) act[(1 + i) * W + j] = (real)dg[(p * d + i) * LF + j];
+        act[(1 + d) * W + j] = (real)lp[p * LF + j];
       }
       for (int k = 0; k < depth; ++k) {
         const double* Wk = mlp + woff[k];
@@ -588,78 +612,78 @@ int orc_residual(const orc_cfg* c, int32_t hidden, int32_t depth, double omega, 
         const int64_t fi = in_w[k];
         for (int o = 0; o < H; ++o) {
           for (int r = 0; r < R; ++r) {
-            double z = (r == 0) ? bk[o] : 0.0; /* the bias enters the value row only */
-            for (int j = 0; j < fi; ++j) z += Wk[o * fi + j] * act[(k * R + r) * W + j];
+            real z = (r == 0) ? (real)bk[o] : 0.0; /* the bias enters the value row only */
+            for (int j = 0; j < fi; ++j) z += (real)Wk[o * fi + j] * act[(k * R + r) * W + j];
             zs[(k * R + r) * H + o] = z;
           }
-          const double z0 = zs[(k * R + 0) * H + o];
-          const double s = sin(omega * z0), co = cos(omega * z0);
-          double sumsq = 0.0;
-          for (int i = 0; i < d; ++i) { double zi = zs[(k * R + 1 + i) * H + o]; sumsq += zi * zi; }
+          const real z0 = zs[(k * R + 0) * H + o];
+          const real s = R_SIN(om * z0), co = R_COS(om * z0);
+          real sumsq = 0.0;
+          for (int i = 0; i < d; ++i) { real zi = zs[(k * R + 1 + i) * H + o]; sumsq += zi * zi; }
           act[((k + 1) * R + 0) * W + o] = s;
           for (int i = 0; i < d; ++i)
-            act[((k + 1) * R + 1 + i) * W + o] = omega * co * zs[(k * R + 1 + i) * H + o];
+            act[((k + 1) * R + 1 + i) * W + o] = om * co * zs[(k * R + 1 + i) * H + o];
           act[((k + 1) * R + 1 + d) * W + o] =
-              -omega * omega * s * sumsq + omega * co * zs[(k * R + 1 + d) * H + o];
+              -om * om * s * sumsq + om * co * zs[(k * R + 1 + d) * H + o];
         }
       }
       /* linear output layer */
       const double* Wo = mlp + woff[depth];
-      double uval = mlp[boff[depth]], lap_u = 0.0, gu[ORC_MAX_D] = {0};
+      real uval = (real)mlp[boff[depth]], lap_u = 0.0, gu[ORC_MAX_D] = {0};
       for (int j = 0; j < H; ++j) {
-        uval += Wo[j] * act[(depth * R + 0) * W + j];
-        for (int i = 0; i < d; ++i) gu[i] += Wo[j] * act[(depth * R + 1 + i) * W + j];
-        lap_u += Wo[j] * act[(depth * R + 1 + d) * W + j];
+        uval += (real)Wo[j] * act[(depth * R + 0) * W + j];
+        for (int i = 0; i < d; ++i) gu[i] += (real)Wo[j] * act[(depth * R + 1 + i) * W + j];
+        lap_u += (real)Wo[j] * act[(depth * R + 1 + d) * W + j];
       }
       if (u_out) u_out[p] = uval;
       if (gu_out) for (int i = 0; i < d; ++i) gu_out[p * d + i] = gu[i];
       if (lu_out) lu_out[p] = lap_u;
-      double src = -(double)d * PI * PI;
-      for (int i = 0; i < d; ++i) src *= sin(PI * (double)x[p * d + i]);
-      const double r = lap_u - src;
+      real src = -(real)d * PI * PI;
+      for (int i = 0; i < d; ++i) src *= R_SIN(PI * (real)x[p * d + i]);
+      const real r = lap_u - src;
       rr[p] = r;
       /* reverse sweep: d loss / d Lap u = 2 r / n seeds the Laplacian row only */
-      const double seed = 2.0 * r * inv_n;
+      const real seed = (real)(2.0 * (double)r * inv_n);
       for (int j = 0; j < H; ++j) {
         gm[woff[depth] + j] += seed * act[(depth * R + 1 + d) * W + j];
         for (int q = 0; q < R; ++q) bar[q * W + j] = 0.0;
-        bar[(1 + d) * W + j] = seed * Wo[j];
+        bar[(1 + d) * W + j] = seed * (real)Wo[j];
       }
       for (int k = depth - 1; k >= 0; --k) {
         const double* Wk = mlp + woff[k];
         const int64_t fi = in_w[k];
         for (int q = 0; q < R; ++q) for (int j = 0; j < fi; ++j) nbar[q * W + j] = 0.0;
         for (int o = 0; o < H; ++o) {
-          const double z0 = zs[(k * R + 0) * H + o];
-          const double s = sin(omega * z0), co = cos(omega * z0);
-          const double zl = zs[(k * R + 1 + d) * H + o];
-          double sumsq = 0.0;
-          for (int i = 0; i < d; ++i) { double zi = zs[(k * R + 1 + i) * H + o]; sumsq += zi * zi; }
-          const double abar = bar[0 * W + o];
-          const double lbar = bar[(1 + d) * W + o];
-          double zbar[ORC_MAX_D + 2];
+          const real z0 = zs[(k * R + 0) * H + o];
+          const real s = R_SIN(om * z0), co = R_COS(om * z0);
+          const real zl = zs[(k * R + 1 + d) * H + o];
+          real sumsq = 0.0;
+          for (int i = 0; i < d; ++i) { real zi = zs[(k * R + 1 + i) * H + o]; sumsq += zi * zi; }
+          const real abar = bar[0 * W + o];
+          const real lbar = bar[(1 + d) * W + o];
+          real zbar[ORC_MAX_D + 2];
           /* d a/dz = w cos;  d A_i/dz = -w^2 sin Z_i;  d A_lap/dz = -w^3 cos sum Z_i^2 - w^2 sin Z_lap */
-          double z0bar = abar * omega * co +
-                         lbar * (-omega * omega * omega * co * sumsq - omega * omega * s * zl);
+          real z0bar = abar * om * co +
+                       lbar * (-om * om * om * co * sumsq - om * om * s * zl);
           for (int i = 0; i < d; ++i) {
-            const double aib = bar[(1 + i) * W + o];
-            const double zi = zs[(k * R + 1 + i) * H + o];
-            z0bar += aib * (-omega * omega * s * zi);
+            const real aib = bar[(1 + i) * W + o];
+            const real zi = zs[(k * R + 1 + i) * H + o];
+            z0bar += aib * (-om * om * s * zi);
             /* d A_i/dZ_i = w cos;  d A_lap/dZ_i = -2 w^2 sin Z_i */
-            zbar[1 + i] = aib * omega * co + lbar * (-2.0 * omega * omega * s * zi);
+            zbar[1 + i] = aib * om * co + lbar * (-(real)2.0 * om * om * s * zi);
           }
           zbar[0] = z0bar;
-          zbar[1 + d] = lbar * omega * co; /* d A_lap/dZ_lap = w cos */
+          zbar[1 + d] = lbar * om * co; /* d A_lap/dZ_lap = w cos */
           gm[boff[k] + o] += z0bar;
           for (int q = 0; q < R; ++q) {
-            const double zb = zbar[q];
+            const real zb = zbar[q];
             for (int j = 0; j < fi; ++j) {
               gm[woff[k] + o * fi + j] += zb * act[(k * R + q) * W + j];
-              nbar[q * W + j] += Wk[o * fi + j] * zb;
+              nbar[q * W + j] += (real)Wk[o * fi + j] * zb;
             }
           }
         }
-        double* tmp = bar; bar = nbar; nbar = tmp;
+        real* tmp = bar; bar = nbar; nbar = tmp;
       }
       for (int j = 0; j < LF; ++j) {
         ug[p * LF + j] = bar[0 * W + j];
@@ -737,7 +761,8 @@ int orc_fd_residual(const orc_cfg* c, int32_t hidden, int32_t depth, double omeg
 #endif
   double* gm_all = (double*)calloc((size_t)(nthreads * n_mlp), sizeof(double));
   const double inv_n = n > 0 ? 1.0 / (double)n : 0.0;
-  const double PI = 3.14159265358979323846;
+  const real PI = (real)3.14159265358979323846;
+  const real om = (real)omega, ep = (real)eps;
 #pragma omp parallel
   {
     int tid = 0;
@@ -746,60 +771,60 @@ int orc_fd_residual(const orc_cfg* c, int32_t hidden, int32_t depth, double omeg
 #endif
     double* gm = gm_all + (int64_t)tid * n_mlp;
     /* tape per stencil point: act[s][k] = inputs of layer k (width W), zs[s][k] = z */
-    double* act = (double*)malloc(sizeof(double) * (size_t)(S * (depth + 1) * W));
-    double* zs = (double*)malloc(sizeof(double) * (size_t)(S * depth * H));
-    double* bar = (double*)malloc(sizeof(double) * (size_t)W);
-    double* nbar = (double*)malloc(sizeof(double) * (size_t)W);
-    double u[2 * ORC_MAX_D + 1];
+    real* act = (real*)malloc(sizeof(real) * (size_t)(S * (depth + 1) * W));
+    real* zs = (real*)malloc(sizeof(real) * (size_t)(S * depth * H));
+    real* bar = (real*)malloc(sizeof(real) * (size_t)W);
+    real* nbar = (real*)malloc(sizeof(real) * (size_t)W);
+    real u[2 * ORC_MAX_D + 1];
 #pragma omp for schedule(static)
     for (int64_t p = 0; p < n; ++p) {
       for (int s = 0; s < S; ++s) {
-        double* a_s = act + (int64_t)s * (depth + 1) * W;
-        double* z_s = zs + (int64_t)s * depth * H;
-        for (int j = 0; j < LF; ++j) a_s[j] = g[(p * S + s) * LF + j];
+        real* a_s = act + (int64_t)s * (depth + 1) * W;
+        real* z_s = zs + (int64_t)s * depth * H;
+        for (int j = 0; j < LF; ++j) a_s[j] = (real)g[(p * S + s) * LF + j];
         for (int k = 0; k < depth; ++k) {
           const double* Wk = mlp + woff[k];
           for (int o = 0; o < H; ++o) {
-            double z = mlp[boff[k] + o];
-            for (int j = 0; j < in_w[k]; ++j) z += Wk[o * in_w[k] + j] * a_s[k * W + j];
+            real z = (real)mlp[boff[k] + o];
+            for (int j = 0; j < in_w[k]; ++j) z += (real)Wk[o * in_w[k] + j] * a_s[k * W + j];
             z_s[k * H + o] = z;
-            a_s[(k + 1) * W + o] = sin(omega * z);
+            a_s[(k + 1) * W + o] = R_SIN(om * z);
           }
         }
-        double us = mlp[boff[depth]];
-        for (int j = 0; j < H; ++j) us += mlp[woff[depth] + j] * a_s[depth * W + j];
+        real us = (real)mlp[boff[depth]];
+        for (int j = 0; j < H; ++j) us += (real)mlp[woff[depth] + j] * a_s[depth * W + j];
         u[s] = us;
         if (u_stencil) u_stencil[p * S + s] = us;
       }
-      double lap = 0.0;
-      for (int i = 0; i < d; ++i) lap += (u[2 * i + 1] - 2.0 * u[0] + u[2 * i + 2]) / (eps * eps);
-      double src = -(double)d * PI * PI;
-      for (int i = 0; i < d; ++i) src *= sin(PI * (double)x[p * d + i]);
-      const double r = lap - src;
+      real lap = 0.0;
+      for (int i = 0; i < d; ++i) lap += (u[2 * i + 1] - (real)2.0 * u[0] + u[2 * i + 2]) / (ep * ep);
+      real src = -(real)d * PI * PI;
+      for (int i = 0; i < d; ++i) src *= R_SIN(PI * (real)x[p * d + i]);
+      const real r = lap - src;
       rr[p] = r;
-      const double seed = 2.0 * r * inv_n;
+      const real seed = (real)(2.0 * (double)r * inv_n);
       for (int s = 0; s < S; ++s) {
-        const double cs = s == 0 ? -2.0 * (double)d / (eps * eps) : 1.0 / (eps * eps);
-        const double ubar = seed * cs;
-        double* a_s = act + (int64_t)s * (depth + 1) * W;
-        double* z_s = zs + (int64_t)s * depth * H;
+        const real cs = s == 0 ? -(real)2.0 * (real)d / (ep * ep) : (real)1.0 / (ep * ep);
+        const real ubar = seed * cs;
+        real* a_s = act + (int64_t)s * (depth + 1) * W;
+        real* z_s = zs + (int64_t)s * depth * H;
         for (int j = 0; j < H; ++j) {
           gm[woff[depth] + j] += ubar * a_s[depth * W + j];
-          bar[j] = ubar * mlp[woff[depth] + j];
+          bar[j] = ubar * (real)mlp[woff[depth] + j];
         }
         for (int k = depth - 1; k >= 0; --k) {
           const double* Wk = mlp + woff[k];
           const int64_t fi = in_w[k];
           for (int j = 0; j < fi; ++j) nbar[j] = 0.0;
           for (int o = 0; o < H; ++o) {
-            const double zbar = bar[o] * omega * cos(omega * z_s[k * H + o]); /* d sin(w z)/dz */
+            const real zbar = bar[o] * om * R_COS(om * z_s[k * H + o]); /* d sin(w z)/dz */
             gm[boff[k] + o] += zbar;
             for (int j = 0; j < fi; ++j) {
               gm[woff[k] + o * fi + j] += zbar * a_s[k * W + j];
-              nbar[j] += Wk[o * fi + j] * zbar;
+              nbar[j] += (real)Wk[o * fi + j] * zbar;
             }
           }
-          double* tmp = bar; bar = nbar; nbar = tmp;
+          real* tmp = bar; bar = nbar; nbar = tmp;
         }
         for (int j = 0; j < LF; ++j) ug[(p * S + s) * LF + j] = bar[j];
       }

@@ -32,19 +32,32 @@ _SRC = os.path.join(_HERE, "hashgrid_oracle.c")
 # HASHGRID_ORACLE_LIB points the wrapper at another build of the same source (used to check,
 # on the CPU, that the pins catch mistakes planted in a copy of the oracle).
 _LIB = os.environ.get("HASHGRID_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+# The same source built with -DORC_FP32: the per-point arithmetic after the position stage in
+# fp32 (its outputs measure the fp32 rounding floor; it is not a reference).
+_LIB32 = os.path.join(_HERE, "liboracle_f32.so")
 
 MAX_LEVELS = 32
 MAX_D = 4
 
 
-def build_oracle(force: bool = True) -> str:
-    """Compile the oracle with gcc (plain IEEE arithmetic: no fast-math, no contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-             "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-Wall"]
+
+
+def build_oracle(force: bool = True, out: str | None = None, extra_flags: list[str] | None = None,
+                 src: str | None = None) -> str:
+    """Compile the oracle with gcc (plain IEEE arithmetic: no fast-math, no contraction), and
+    its fp32 working-precision build beside it.  `out`, `extra_flags` and `src` build one
+    other variant instead (a sanitizer build, or a planted-mistake copy in a test)."""
+    if out is not None:
+        tmp = out + ".tmp"
+        subprocess.check_call(["gcc", *GCC_FLAGS, *(extra_flags or []), "-o", tmp, src or _SRC, "-lm"])
+        os.replace(tmp, out)
+        return out
+    for lib, flags in ((_LIB, []), (_LIB32, ["-DORC_FP32"])):
+        if force or not os.path.exists(lib):
+            tmp = lib + ".tmp"
+            subprocess.check_call(["gcc", *GCC_FLAGS, *flags, "-o", tmp, _SRC, "-lm"])
+            os.replace(tmp, lib)
     return _LIB
 
 
@@ -57,15 +70,18 @@ class _Cfg(ctypes.Structure):
     ]
 
 
-_lib = None
+_libs: dict = {}
 
 
-def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB):
+def _load(precision: str = "f64"):
+    """The oracle library (precision "f64"), or its fp32 working-precision build ("f32")."""
+    if precision not in ("f64", "f32"):
+        raise ValueError("precision must be 'f64' or 'f32'")
+    if precision not in _libs:
+        path = _LIB if precision == "f64" else _LIB32
+        if not os.path.exists(path):
             build_oracle(force=False)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         lib.orc_levels.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P]
         lib.orc_levels.restype = ctypes.c_int
@@ -93,8 +109,8 @@ def _load():
         lib.orc_max_threads.restype = ctypes.c_int
         lib.orc_set_threads.argtypes = [ctypes.c_int]
         lib.orc_set_threads.restype = None
-        _lib = lib
-    return _lib
+        _libs[precision] = lib
+    return _libs[precision]
 
 
 def _ptr(a):
@@ -182,10 +198,11 @@ def _f64(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
 
 
-def forward(spec: dict, x: np.ndarray, params: np.ndarray):
+def forward(spec: dict, x: np.ndarray, params: np.ndarray, precision: str = "f64"):
     """gamma [n, L*F]; Hermite and RBF add dgamma [n, d, L*F] and d2gamma (Laplacian
     [n, L*F] or diagonal [n, d, L*F]).  Returns (gamma, dgamma, d2gamma), None where not
-    defined.  ``params`` may be fp32 (widened exactly) or fp64."""
+    defined.  ``params`` may be fp32 (widened exactly) or fp64.  precision "f32": the same
+    arithmetic in fp32 (the rounding floor, not a reference)."""
     c = make_cfg(spec)
     x, params = _f32(x), _f64(params)
     n, d, LF = x.shape[0], spec["d"], spec["L"] * spec["F"]
@@ -194,11 +211,12 @@ def forward(spec: dict, x: np.ndarray, params: np.ndarray):
     if spec["kind"] in ("hermite", "rbf"):
         dg = np.zeros((n, d, LF))
         d2 = np.zeros((n, d, LF)) if c.d2_mode == 2 else np.zeros((n, LF))
-    _load().orc_forward(ctypes.byref(c), n, _ptr(x), _ptr(params), _ptr(gamma), _ptr(dg), _ptr(d2))
+    _load(precision).orc_forward(ctypes.byref(c), n, _ptr(x), _ptr(params), _ptr(gamma), _ptr(dg), _ptr(d2))
     return gamma, dg, d2
 
 
-def backward(spec: dict, x: np.ndarray, g_gamma=None, g_dgamma=None, g_d2=None, n_params=None):
+def backward(spec: dict, x: np.ndarray, g_gamma=None, g_dgamma=None, g_d2=None, n_params=None,
+             precision: str = "f64"):
     """Gradient of <G, forward(theta)> with respect to theta (fp64, params layout).
     Upstream arrays are fp32 (exactly widened) or fp64; None means zero."""
     c = make_cfg(spec)
@@ -207,7 +225,7 @@ def backward(spec: dict, x: np.ndarray, g_gamma=None, g_dgamma=None, g_d2=None, 
     if n_params is None:
         n_params = layout(spec)["n_params"]
     grad = np.zeros(n_params)
-    _load().orc_backward_f64(ctypes.byref(c), n, _ptr(x), _ptr(_f64(g_gamma)), _ptr(_f64(g_dgamma)),
+    _load(precision).orc_backward_f64(ctypes.byref(c), n, _ptr(x), _ptr(_f64(g_gamma)), _ptr(_f64(g_dgamma)),
                              _ptr(_f64(g_d2)), _ptr(grad))
     return grad
 
@@ -233,7 +251,7 @@ def mlp_param_count(n_in: int, hidden: int, depth: int) -> int:
     return int(_load().orc_mlp_param_count(n_in, hidden, depth))
 
 
-def residual(spec: dict, hidden: int, depth: int, omega: float, x, params, mlp):
+def residual(spec: dict, hidden: int, depth: int, omega: float, x, params, mlp, precision: str = "f64"):
     """Fused PINN residual.  Returns a dict of fp64 results: u [n], grad_u [n, d], lap_u [n],
     r [n], loss (float), grad_params [n_params], grad_mlp [n_mlp]."""
     c = make_cfg(spec)
@@ -242,7 +260,7 @@ def residual(spec: dict, hidden: int, depth: int, omega: float, x, params, mlp):
     out = {"u": np.zeros(n), "grad_u": np.zeros((n, d)), "lap_u": np.zeros(n), "r": np.zeros(n),
            "grad_params": np.zeros(params.size), "grad_mlp": np.zeros(mlp.size)}
     loss = np.zeros(1)
-    rc = _load().orc_residual(ctypes.byref(c), hidden, depth, float(omega), n, _ptr(x), _ptr(params),
+    rc = _load(precision).orc_residual(ctypes.byref(c), hidden, depth, float(omega), n, _ptr(x), _ptr(params),
                               _ptr(mlp), _ptr(out["u"]), _ptr(out["grad_u"]), _ptr(out["lap_u"]),
                               _ptr(out["r"]), _ptr(loss), _ptr(out["grad_params"]),
                               _ptr(out["grad_mlp"]))
@@ -252,7 +270,8 @@ def residual(spec: dict, hidden: int, depth: int, omega: float, x, params, mlp):
     return out
 
 
-def fd_residual(spec: dict, hidden: int, depth: int, omega: float, eps: float, x, params, mlp):
+def fd_residual(spec: dict, hidden: int, depth: int, omega: float, eps: float, x, params, mlp,
+                precision: str = "f64"):
     """INGP-FD comparator: the residual with the Laplacian of u taken by central differences
     over the 2d+1 stencil points (d-linear encoding).  Returns a dict of fp64 results:
     u_stencil [n, 2d+1], r [n], loss (float), grad_params [n_params], grad_mlp [n_mlp]."""
@@ -262,7 +281,7 @@ def fd_residual(spec: dict, hidden: int, depth: int, omega: float, eps: float, x
     out = {"u_stencil": np.zeros((n, 2 * d + 1)), "r": np.zeros(n),
            "grad_params": np.zeros(params.size), "grad_mlp": np.zeros(mlp.size)}
     loss = np.zeros(1)
-    rc = _load().orc_fd_residual(ctypes.byref(c), hidden, depth, float(omega), float(eps), n, _ptr(x),
+    rc = _load(precision).orc_fd_residual(ctypes.byref(c), hidden, depth, float(omega), float(eps), n, _ptr(x),
                                  _ptr(params), _ptr(mlp), _ptr(out["u_stencil"]), _ptr(out["r"]), _ptr(loss),
                                  _ptr(out["grad_params"]), _ptr(out["grad_mlp"]))
     if rc != 0:
