@@ -188,6 +188,26 @@ HASHENC_API int hashenc_backward_ws(const hashenc* h, int64_t n, const float* x,
                                     const float* g_dgamma, const float* g_d2gamma, float* grad_params,
                                     void* workspace, size_t workspace_bytes, hashenc_stream_t stream);
 
+/* Allocation-free variant of hashenc_backward_ws, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments as hashenc_backward (all device pointers owned by the caller)
+ * and the same result as hashenc_backward_ws: grad_params += dL/dtheta.  In place of a
+ * workspace argument it uses a file-scope static device array of
+ * HASHENC_NOALLOC_SCRATCH_BYTES, which every GPU the library runs on holds from the first
+ * call on that GPU until the process ends; points run in chunks small enough for the binned
+ * backward's workspace to fit it (the chunk size depends on the configuration; more chunks
+ * cost more passes over the gradient).  Configurations the binned path does not cover take
+ * the atomic path, as hashenc_backward_ws does.  Nothing is allocated: no hipMalloc,
+ * hipFree or allocating library routine is called.  No part of the scratch needs to start
+ * at zero, and each call leaves its last chunk's plan in it.  All calls on one GPU share
+ * that GPU's array: calls that overlap on one GPU (different streams or threads) race and
+ * give wrong results; the caller serialises them.  HASHENC_EINVAL (before any launch) when
+ * even a 1024-point chunk of this configuration needs more scratch than the array holds. */
+#define HASHENC_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+HASHENC_API int hashenc_backward_noalloc(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
+                                         const float* g_dgamma, const float* g_d2gamma, float* grad_params,
+                                         hashenc_stream_t stream);
+
 /* SIREN decoder of the fused PINN residual (Hermite-NGP key design 2; loss section):
  * `depth` hidden layers of width `hidden`, activation sin(omega (W v + b)), then a linear
  * output of width 1.  `in` must equal L*F. */

@@ -242,6 +242,17 @@ def hashenc_backward_ws(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None,
                                      _dev_ptr(grad_params, "grad_params"), ws_ptr, ws_bytes, _stream(stream)))
 
 
+def hashenc_backward_noalloc(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_d2gamma=None,
+                             grad_params=None, stream=None) -> None:
+    """The binned backward on the library's static scratch (no workspace, nothing allocated);
+    calls on one GPU must not overlap."""
+    n = _points(h, x)
+    _check_encoder_io(h, n, None, g_gamma, g_dgamma, g_d2gamma, grad_params)
+    check(load().hashenc_backward_noalloc(h, n, _dev_ptr(x, "x"), _dev_ptr(g_gamma, "g_gamma"),
+                                          _dev_ptr(g_dgamma, "g_dgamma"), _dev_ptr(g_d2gamma, "g_d2gamma"),
+                                          _dev_ptr(grad_params, "grad_params"), _stream(stream)))
+
+
 @dataclass
 class Mlp:
     n_in: int

@@ -237,9 +237,11 @@ size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite
 // u_levels (else NULL): upstream already level-major for all n points (Hermite [L][n][M][F],
 // d-linear [L][n][F]; n at most one internal chunk); then the row-major upstream pointers are
 // ignored.
+// max_chunk > 0 lowers the points per pass below bin_chunk_points (a workspace sized for
+// max_chunk points then suffices).
 hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2_mode, int64_t n,
                                const float* x, const float* g_gamma, const float* g_dgamma,
                                const float* g_d2gamma, const float* u_levels, float* grad, void* workspace,
-                               hipStream_t s);
+                               hipStream_t s, int64_t max_chunk = 0);
 
 }  // namespace hg

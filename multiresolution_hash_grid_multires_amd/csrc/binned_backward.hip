@@ -487,10 +487,11 @@ size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite
 hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2_mode, int64_t n,
                                const float* x, const float* g_gamma, const float* g_dgamma,
                                const float* g_d2gamma, const float* u_levels, float* grad, void* workspace,
-                               hipStream_t s) {
+                               hipStream_t s, int64_t max_chunk) {
   BinPlan bp;
   make_bin_plan(g, d, F, hermite, bp);
-  const int64_t cmax = bin_chunk_points(g, d, hermite);
+  int64_t cmax = bin_chunk_points(g, d, hermite);
+  if (max_chunk > 0 && max_chunk < cmax) cmax = max_chunk;
   if (u_levels && n > cmax) return hipErrorInvalidValue;  // one chunk only
   char* ws = static_cast<char*>(workspace);
   const int64_t LF = (int64_t)g.Lrow * F;  // upstream row stride

@@ -1,9 +1,11 @@
 // Host side of the C ABI: configuration checks, level progression, parameter layout,
 // argument validation and kernel dispatch.  No device memory is owned by a handle.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -61,6 +63,41 @@ int64_t binom(int n, int k) {
 // with up to 16 lanes per point) then stays below 2^31 workgroups.
 constexpr int64_t kMaxPoints = int64_t(1) << 33;
 
+}  // namespace
+
+// Scratch of the allocation-free backward (hashenc_backward_noalloc): a file-scope device
+// array that each GPU holds from module load to process end.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels and copies get its per-device address from
+// hipGetSymbolAddress, taken once per device with that device current.
+namespace {
+static __device__ __align__(256) unsigned char scratch[HASHENC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch (the current device), or NULL with *err set.
+void* scratch_ptr(hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 }  // namespace
 
 // Hermite forward_ws workspace: the packed order tables (when their sizes are equal), then
@@ -492,6 +529,45 @@ int hashenc_backward_ws(const hashenc* h, int64_t n, const float* x, const float
   hipError_t e = hg::run_binned_backward(h->grid, h->d, h->F, h->kind == HASHENC_HERMITE, h->d2_mode, n, x,
                                          g_gamma, g_dgamma, g_d2gamma, nullptr, grad_params, workspace, stream);
   if (e != hipSuccess) return hip_fail(e, "hashenc_backward_ws launch");
+  return ok();
+}
+
+int hashenc_backward_noalloc(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
+                             const float* g_dgamma, const float* g_d2gamma, float* grad_params,
+                             hashenc_stream_t stream) {
+  if (!h) return fail(HASHENC_EINVAL, "hashenc_backward_noalloc: NULL handle");
+  if (n < 0 || n > kMaxPoints)
+    return fail(HASHENC_EINVAL, "hashenc_backward_noalloc: n = %lld out of range", (long long)n);
+  if (h->kind == HASHENC_DLINEAR && (g_dgamma || g_d2gamma))
+    return fail(HASHENC_EUNSUPPORTED, "hashenc_backward_noalloc: derivative upstream needs the Hermite kind");
+  if (n == 0 || (!g_gamma && !g_dgamma && !g_d2gamma)) return ok();
+  if (!binned_supported(h))  // the atomic scatter-add uses no scratch
+    return hashenc_backward(h, n, x, g_gamma, g_dgamma, g_d2gamma, grad_params, stream);
+  if (!x || !grad_params) return fail(HASHENC_EINVAL, "hashenc_backward_noalloc: x and grad_params must not be NULL");
+  if (!aligned16(x) || !aligned16(grad_params) || !aligned16(g_gamma) || !aligned16(g_dgamma) ||
+      !aligned16(g_d2gamma))
+    return fail(HASHENC_EALIGN, "hashenc_backward_noalloc: device pointers must be 16-byte aligned");
+  const bool hermite = h->kind == HASHENC_HERMITE;
+  // the largest chunk (a multiple of 1024 points) whose binned workspace fits the scratch
+  const size_t cap = HASHENC_NOALLOC_SCRATCH_BYTES;
+  if (hg::binned_backward_workspace_bytes(h->grid, h->d, h->F, hermite, 1024) > cap)
+    return fail(HASHENC_EINVAL,
+                "hashenc_backward_noalloc: a 1024-point chunk of this configuration needs %zu bytes of scratch; "
+                "the static scratch holds %zu (use hashenc_backward_ws with a workspace)",
+                hg::binned_backward_workspace_bytes(h->grid, h->d, h->F, hermite, 1024), cap);
+  int64_t lo = 1, hi = (n + 1023) / 1024;  // in units of 1024 points; lo always fits
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (hg::binned_backward_workspace_bytes(h->grid, h->d, h->F, hermite, mid * 1024) <= cap) lo = mid;
+    else hi = mid - 1;
+  }
+  const int64_t chunk = lo * 1024;
+  hipError_t e = hipSuccess;
+  void* ptr = scratch_ptr(&e);
+  if (!ptr) return hip_fail(e, "hashenc_backward_noalloc: address of the static scratch");
+  e = hg::run_binned_backward(h->grid, h->d, h->F, hermite, h->d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma,
+                              nullptr, grad_params, ptr, stream, chunk);
+  if (e != hipSuccess) return hip_fail(e, "hashenc_backward_noalloc launch");
   return ok();
 }
 
