@@ -390,6 +390,8 @@ def main() -> int:
     ap.add_argument("--active-levels", type=int, default=0,
                     help="coarse-to-fine activation: compute only the first A levels (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--n-points", type=int, default=0,
+                    help="points per step instead of the workload's own count (the first N of its points)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run the plain copy kernel over this many bytes "
                          "(bandwidth and memory-counter calibration)")
@@ -427,6 +429,8 @@ def main() -> int:
         return fill_calibration(args, torch)
 
     W = I.WORKLOADS[args.workload]
+    if args.n_points:
+        W = dict(W, n_points=args.n_points)
     if args.active_levels:
         W = dict(W, spec=dict(W["spec"], active_levels=args.active_levels))
     if "mlp" in W:
@@ -436,7 +440,7 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     enc = api.HashGridEncoding(spec)
-    x_h = I.workload_points(args.workload) if "stratified_side" in W else I.points(W["id"], n, spec["d"])
+    x_h = I.workload_points(args.workload)[:n] if "stratified_side" in W else I.points(W["id"], n, spec["d"])
     params_h = I.tables(W["id"], enc.n_params, W["tables"])
     shapes = enc.output_shapes(n)
     ups_h = I.upstream(W["id"], list(shapes.values()))
@@ -553,7 +557,8 @@ def main() -> int:
                "seconds": round(total, 2), "cpu_model": cpu_model(),
                "single_thread": single_thread_rate(O, spec, x_h, params_h, ups_h, enc.n_params, total / reps / m)}
 
-    metric = METRIC if args.workload == HEADLINE else f"encoded points/s fwd+bwd ({args.workload})"
+    metric = (METRIC if args.workload == HEADLINE and not args.n_points
+              else f"encoded points/s fwd+bwd ({args.workload}" + (f", {n} points)" if args.n_points else ")"))
     if args.active_levels:
         metric = f"encoded points/s fwd+bwd ({args.workload}, {args.active_levels} of {spec['L']} levels active)"
     line = {

@@ -175,7 +175,9 @@ HASHENC_API int hashenc_backward(const hashenc* h, int64_t n, const float* x, co
                      hashenc_stream_t stream);
 
 /* Device workspace (bytes) that hashenc_backward_ws needs for n points (0 when this handle's
- * configuration does not use one; hashenc_backward_ws then takes the atomic path). */
+ * configuration, or a d-linear batch with n * L < 2^18, does not use one;
+ * hashenc_backward_ws then takes the atomic path).  A workspace sized for n points serves
+ * every smaller n. */
 HASHENC_API int hashenc_backward_workspace_size(const hashenc* h, int64_t n, size_t* bytes);
 
 /* Same result as hashenc_backward (grad_params += dL/dtheta), computed without global
@@ -183,7 +185,9 @@ HASHENC_API int hashenc_backward_workspace_size(const hashenc* h, int64_t n, siz
  * small enough for the LDS of one workgroup, then each bin is accumulated on chip and added
  * to grad_params.  workspace: >= hashenc_backward_workspace_size bytes, 256-byte aligned,
  * owned by the caller, contents irrelevant on entry; calls sharing a workspace must not
- * overlap.  Points are processed in chunks of 2^21. */
+ * overlap.  Points are processed in chunks of 2^21 (fewer when a chunk would hold 2^31
+ * entries).  Small d-linear batches (n * L < 2^18) take the atomic path, which is faster
+ * there. */
 HASHENC_API int hashenc_backward_ws(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
                                     const float* g_dgamma, const float* g_d2gamma, float* grad_params,
                                     void* workspace, size_t workspace_bytes, hashenc_stream_t stream);

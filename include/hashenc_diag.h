@@ -19,6 +19,15 @@ extern "C" {
 HASHENC_API int hashenc_debug_indices(const hashenc* h, int64_t n, const float* x, int32_t order,
                           int32_t* out_rows, hashenc_stream_t stream);
 
+/* The binned backward of hashenc_backward_ws at any n, for testing its kernels on small
+ * batches (which hashenc_backward_ws itself may hand to the atomic scatter-add).  Same
+ * arguments and result as hashenc_backward_ws; HASHENC_EUNSUPPORTED when the configuration
+ * has no binned plan.  hashenc_diag_binned_workspace_size gives the workspace it needs. */
+HASHENC_API int hashenc_diag_binned_workspace_size(const hashenc* h, int64_t n, size_t* bytes);
+HASHENC_API int hashenc_diag_backward_binned(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
+                                             const float* g_dgamma, const float* g_d2gamma, float* grad_params,
+                                             void* workspace, size_t workspace_bytes, hashenc_stream_t stream);
+
 /* Plain streaming copy dst[i] = src[i], i < n_floats (both 16-byte aligned, no overlap).
  * Used to measure achievable HBM bandwidth and to calibrate memory counters. */
 HASHENC_API int hashenc_diag_copy(const float* src, float* dst, int64_t n_floats, hashenc_stream_t stream);

@@ -85,6 +85,8 @@ SIGNATURES = [
      [P, ctypes.POINTER(HashencMlp), ctypes.c_float, I64, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     ("hashenc_last_error", ctypes.c_char_p, []),
     ("hashenc_debug_indices", ctypes.c_int, [P, I64, P, I32, P, P]),
+    ("hashenc_diag_binned_workspace_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)]),
+    ("hashenc_diag_backward_binned", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),
     ("hashenc_diag_copy", ctypes.c_int, [P, P, I64, P]),
     ("hashenc_diag_cache_read", ctypes.c_int, [P, I64, I32, P, P]),
 ]

@@ -328,6 +328,27 @@ def hashenc_debug_indices(h: Handle, x: torch.Tensor, order: int, out_rows: torc
                                        _dev_ptr(out_rows, "out_rows", dtype=torch.int32), _stream(stream)))
 
 
+def hashenc_diag_binned_workspace_size(h: Handle, n: int) -> int:
+    b = ctypes.c_size_t()
+    check(load().hashenc_diag_binned_workspace_size(h, n, ctypes.byref(b)))
+    return int(b.value)
+
+
+def hashenc_diag_backward_binned(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_d2gamma=None,
+                                 grad_params=None, workspace: torch.Tensor | None = None, stream=None) -> None:
+    """The binned backward at any batch size (diagnostics: its kernels on small batches)."""
+    n = _points(h, x)
+    _check_encoder_io(h, n, None, g_gamma, g_dgamma, g_d2gamma, grad_params)
+    if workspace is None:
+        b = hashenc_diag_binned_workspace_size(h, n)
+        workspace = torch.empty(max(b, 1), dtype=torch.uint8, device=x.device)
+    ws_ptr, ws_bytes = _ws(workspace)
+    check(load().hashenc_diag_backward_binned(h, n, _dev_ptr(x, "x"), _dev_ptr(g_gamma, "g_gamma"),
+                                              _dev_ptr(g_dgamma, "g_dgamma"), _dev_ptr(g_d2gamma, "g_d2gamma"),
+                                              _dev_ptr(grad_params, "grad_params"), ws_ptr, ws_bytes,
+                                              _stream(stream)))
+
+
 def hashenc_diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     _expect(dst, src.numel(), "dst")
     check(load().hashenc_diag_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), src.numel(), _stream(stream)))
@@ -396,6 +417,12 @@ class HashGridEncoding:
         hashenc_forward_ws(self.handle, x, params, out["gamma"], out.get("dgamma"), out.get("d2gamma"),
                            workspace, stream)
         return out
+
+    def backward_binned(self, x: torch.Tensor, grad_params: torch.Tensor, g_gamma=None, g_dgamma=None,
+                        g_d2gamma=None, stream=None) -> torch.Tensor:
+        """The binned backward whatever the batch size (diagnostics)."""
+        hashenc_diag_backward_binned(self.handle, x, g_gamma, g_dgamma, g_d2gamma, grad_params, None, stream)
+        return grad_params
 
     def backward_ws(self, x: torch.Tensor, grad_params: torch.Tensor, g_gamma=None, g_dgamma=None,
                     g_d2gamma=None, workspace=None, stream=None) -> torch.Tensor:

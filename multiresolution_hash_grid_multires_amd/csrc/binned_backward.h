@@ -80,6 +80,10 @@ struct BinState {
 struct BinWorkspace {
   int32_t tile;   // points per count / scatter workgroup
   int32_t nblk;
+  // Levels are split over lgroups workgroups per tile (lpg levels each) when there are too
+  // few tiles to fill the chip: a workgroup's levels run one after the other, so a small
+  // batch would otherwise wait on the per-level chain of a few workgroups.
+  int32_t lgroups, lpg;
   int64_t max_items;
   int32_t item_entries;  // entries per reduce work item
   size_t counts, totals, seg_sums, state, bin_start, items, vals, ups, total;

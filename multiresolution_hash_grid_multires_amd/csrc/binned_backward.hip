@@ -17,6 +17,8 @@
 //              single item, atomics only when a large bin was split across items)
 // Steps 1 and 4 are interpolant-specific (d-linear, Hermite kernel files); 2, 3 and 5 live
 // here.  Within one call the chunks of points run back to back on the stream.
+#include <algorithm>
+
 #include "binned_backward.h"
 #include "vec_io.h"
 
@@ -306,7 +308,12 @@ __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g
         if (a != 0.0f) atomic_add_f32(dst + i, a);
       }
     } else {
-      for (int i = threadIdx.x; i < nfl; i += kReduceThreads) dst[i] += (float)acc[(i % W) * plane + i / W];
+      // rows no entry touched keep their gradient: no read-modify-write for them (a bin of a
+      // small batch touches few of its rows)
+      for (int i = threadIdx.x; i < nfl; i += kReduceThreads) {
+        const float a = (float)acc[(i % W) * plane + i / W];
+        if (a != 0.0f) dst[i] += a;
+      }
     }
     __syncthreads();
   }
@@ -340,10 +347,26 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
   for (int k = 0; k < kMaxTables; ++k) { bp.width[k] = 0; bp.cshift[k] = 0; }
   int32_t bin = 0;
   bp.max_seg_bins = 0;
+  // Rows per bin: what the LDS accumulator holds at the table's width, but at most about
+  // 1/512 of all rows, so that a small configuration still has a few hundred bins -- enough
+  // to spread the reduce over the CUs without splitting bins into several work items, each of
+  // which would accumulate and flush the whole chunk.  d-linear pair records keep the chunks
+  // they need (whole x-lines of dense levels, 2N rows of hashed ones).
+  int64_t all_rows = 0;
+  for (int k = 0; k < bp.ntab; ++k)
+    for (int l = 0; l < g.L; ++l) all_rows += seg_rows(g, d, k, l);
+  int cap = 8;
+  while ((int64_t(2) << cap) <= all_rows / 512) ++cap;
+  if (!hermite)
+    for (int l = 0; l < g.L; ++l) {
+      const bool dense = (g.dense[0] >> l) & 1u;
+      const int64_t need = dense ? (int64_t)g.N[l] + 1 : 2 * (int64_t)g.N[l];
+      while ((int64_t(1) << cap) < need && cap < 30) ++cap;
+    }
   for (int k = 0; k < bp.ntab; ++k) {
     const int W = hermite ? (k == 0 || k == d ? F : (d == 3 ? 3 * F : 2 * F)) : F;
     bp.width[k] = W;
-    bp.cshift[k] = bin_cshift_for_width(W);
+    bp.cshift[k] = std::min(bin_cshift_for_width(W), cap);
     const int64_t C = (int64_t)1 << bp.cshift[k];
     for (int l = 0; l < g.L; ++l) {
       const int s = k * g.L + l;
@@ -418,6 +441,12 @@ BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64
   auto al = [](size_t b) { return (b + 255) & ~size_t(255); };
   w.tile = tile;
   w.nblk = (int32_t)((chunk_points + tile - 1) / tile);
+  // about 512 count / scatter workgroups at least, when the levels allow (more groups re-read
+  // the points and repeat the per-workgroup set-up: at 2^18 points of the 16-level d-linear
+  // grid, 4 groups were slower than 1)
+  int32_t groups = (int32_t)std::min<int64_t>(bp.L, (512 + w.nblk - 1) / w.nblk);
+  w.lpg = (bp.L + groups - 1) / groups;
+  w.lgroups = (bp.L + w.lpg - 1) / w.lpg;
   const int64_t entries = chunk_points * epp;
   w.item_entries = bin_item_entries(entries);
   // bins split into items of item_entries: at most entries / item_entries <= max(512,

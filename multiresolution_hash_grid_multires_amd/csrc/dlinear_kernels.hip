@@ -328,16 +328,18 @@ __global__ __launch_bounds__(kBlock) void dlinear_backward_kernel(const Grid g, 
 }
 
 // Binned backward, count pass: a workgroup of TPB lanes owns a tile of `tile` = 2 TPB points
-// (two per lane) and histograms their entries over all bins in LDS.  On pair-mode levels the two
-// x-corners of each (y, z) corner pair make one entry (they always share a bin); elsewhere
-// each corner is its own entry.
+// (two per lane) and one group of lpg levels (blockIdx.y), and histograms their entries over
+// that group's bins in LDS.  On pair-mode levels the two x-corners of each (y, z) corner pair
+// make one entry (they always share a bin); elsewhere each corner is its own entry.
 template <int D, int TPB>
 __global__ __launch_bounds__(TPB) void dlinear_count_kernel(const Grid g, const BinPlan bp, int64_t n, int32_t tile,
-                                                            int32_t nblk, const float* __restrict__ x,
+                                                            int32_t nblk, int32_t lpg, const float* __restrict__ x,
                                                             int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
-  for (int i = threadIdx.x; i < bp.nbins; i += TPB) hist[i] = 0;
+  const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);
+  const int32_t gb0 = bp.seg_bin0[l0], gb1 = bp.seg_bin0[l1];
+  for (int i = gb0 + threadIdx.x; i < gb1; i += TPB) hist[i] = 0;
   __syncthreads();
   constexpr int PPT = 2;  // points per lane
   const int64_t p0 = (int64_t)blk * tile + threadIdx.x;
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(TPB) void dlinear_count_kernel(const Grid g, const 
 #pragma unroll
     for (int i = 0; i < D; ++i) xp[j][i] = x[p * D + i];
   }
-  for (int l = 0; l < g.L; ++l) {
+  for (int l = l0; l < l1; ++l) {
     const bool dense = (g.dense[0] >> l) & 1u;
     const bool pair = (bp.pair_mask >> l) & 1u;
     const bool few = bp.seg_bin0[l + 1] - bp.seg_bin0[l] <= kFewBins;
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(TPB) void dlinear_count_kernel(const Grid g, const 
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < bp.nbins; i += TPB) counts[(int64_t)blk * bp.nbins + i] = hist[i];
+  for (int i = gb0 + threadIdx.x; i < gb1; i += TPB) counts[(int64_t)blk * bp.nbins + i] = hist[i];
 }
 
 // G = up[l*F .. l*F + F) for a wave-uniform l < 32 / F: per feature, a tournament over the
@@ -413,12 +415,12 @@ __device__ __forceinline__ void pick_group(const float (&up)[32], int l, float (
 // copied out so that each bin receives one contiguous run: consecutive lanes write
 // consecutive records and cache lines are written whole.  Single-corner records (levels
 // not in pair mode) are written straight to their slots.
-// PRE: the point's upstream row (Lrow*F <= 32 floats, a multiple of 4) is read once into
-// registers before the level loop; otherwise each level reads its F floats of the row, or of
-// the level-major upstream u_lm when given.
+// PRE: the workgroup's part of the point's upstream row (lpg*F <= 32 floats, a multiple of 4,
+// from column l0*F) is read once into registers before the level loop; otherwise each level
+// reads its F floats of the row, or of the level-major upstream u_lm when given.
 template <int D, int F, bool PRE, int TPB>
 __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
-    const Grid g, const BinPlan bp, int64_t n, int32_t tile, int32_t nblk, const float* __restrict__ x,
+    const Grid g, const BinPlan bp, int64_t n, int32_t tile, int32_t nblk, int32_t lpg, const float* __restrict__ x,
     const float* __restrict__ g_gamma, const float* __restrict__ u_lm, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
     const BinState* __restrict__ st, float* __restrict__ vals_out) {
@@ -441,31 +443,35 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
   const int64_t p = (int64_t)blk * tile + threadIdx.x;
   const bool on = p < n;
   const int np = (int)min((int64_t)tile, n - (int64_t)blk * tile);
-  for (int i = threadIdx.x; i < nbins; i += TPB) {
+  // this workgroup's levels and their bins (all of them unless the levels are split)
+  const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);
+  const int32_t gb0 = bp.seg_bin0[l0], gb1 = bp.seg_bin0[l1];
+  for (int i = gb0 + threadIdx.x; i < gb1; i += TPB) {
     const int32_t pre = counts[(int64_t)blk * nbins + i];
     const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)(blk + 1) * nbins + i] : totals[i];
     delta[i] = bin_start[i] + pre;
     lcur[i] = nxt - pre;
   }
   __syncthreads();
-  block_exclusive_scan<TPB>(lcur, nbins, wsum);
-  for (int i = threadIdx.x; i < nbins; i += TPB) delta[i] -= lcur[i];
-  for (int i = threadIdx.x; i < g.L; i += TPB) lbase[i] = lcur[bp.seg_bin0[i]];
+  block_exclusive_scan<TPB>(lcur + gb0, gb1 - gb0, wsum);
+  for (int i = gb0 + threadIdx.x; i < gb1; i += TPB) delta[i] -= lcur[i];
+  for (int i = l0 + threadIdx.x; i < l1; i += TPB) lbase[i] = lcur[bp.seg_bin0[i]];
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = on ? x[p * D + i] : 0.0f;
   const int64_t LF = (int64_t)g.Lrow * F;
   float up[PRE ? 32 : 1];
   if constexpr (PRE) {
+    const int gf = (l1 - l0) * F;  // floats of this workgroup's levels
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (on && g_gamma && 4 * q < LF) a = reinterpret_cast<const float4*>(g_gamma + p * LF)[q];
+      if (on && g_gamma && 4 * q < gf) a = reinterpret_cast<const float4*>(g_gamma + p * LF + (int64_t)l0 * F)[q];
       up[4 * q] = a.x; up[4 * q + 1] = a.y; up[4 * q + 2] = a.z; up[4 * q + 3] = a.w;
     }
   }
   __syncthreads();
-  for (int l = 0; l < g.L; ++l) {
+  for (int l = l0; l < l1; ++l) {
     const int32_t b0 = bp.seg_bin0[l];
     const int nb = bp.seg_bin0[l + 1] - b0;
     const int32_t lb = lbase[l];  // staging slots of this level start here
@@ -487,7 +493,7 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
           float v = 0.0f;
 #pragma unroll
           for (int c = f; c < 32; c += F)
-            if (c == l * F + f) v = up[c];
+            if (c == (l - l0) * F + f) v = up[c];
           G[f] = v;
         }
       } else if (u_lm) {
@@ -549,12 +555,12 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
 template <int D, int F, int TPB>
 hipError_t launch_bin_tile(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, bool scatter,
                            int64_t n, const float* x, const float* gg, const float* u_lm, hipStream_t s) {
-  const dim3 grid((unsigned)w.nblk);
+  const dim3 grid((unsigned)w.nblk, (unsigned)w.lgroups);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
   if (!scatter) {  // two points per count lane
     if (w.tile != TPB) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dlinear_count_kernel<D, TPB / 2>), grid, dim3(TPB / 2), sizeof(int32_t) * (size_t)bp.nbins,
-                       s, g, bp, n, w.tile, w.nblk, x, counts);
+                       s, g, bp, n, w.tile, w.nblk, w.lpg, x, counts);
     return hipGetLastError();
   }
   const size_t lds = dlinear_scatter_lds_bytes(bp, D, F, w.tile);
@@ -562,20 +568,20 @@ hipError_t launch_bin_tile(const Grid& g, const BinPlan& bp, const BinWorkspace&
   const int32_t* bin_start = reinterpret_cast<const int32_t*>(ws + w.bin_start);
   const BinState* st = reinterpret_cast<const BinState*>(ws + w.state);
   float* vals = reinterpret_cast<float*>(ws + w.vals);
-  // PRE reads the row as 16-byte pieces: rows of a multiple of 4 floats only, so that every
-  // piece is aligned and inside the row
-  if (!u_lm && g.Lrow * F <= 32 && (g.Lrow * F) % 4 == 0) {
+  // PRE reads the group's part of the row as 16-byte pieces: rows and groups of a multiple of
+  // 4 floats only, so that every piece is aligned and inside the row
+  if (!u_lm && w.lpg * F <= 32 && (w.lpg * F) % 4 == 0 && (g.Lrow * F) % 4 == 0) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, true, TPB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, true, TPB>), grid, dim3(TPB), lds, s, g, bp, n, w.tile, w.nblk,
-                       x, gg, nullptr, counts, totals, bin_start, st, vals);
+                       w.lpg, x, gg, nullptr, counts, totals, bin_start, st, vals);
   } else {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, false, TPB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, false, TPB>), grid, dim3(TPB), lds, s, g, bp, n, w.tile,
-                       w.nblk, x, gg, u_lm, counts, totals, bin_start, st, vals);
+                       w.nblk, w.lpg, x, gg, u_lm, counts, totals, bin_start, st, vals);
   }
   return hipGetLastError();
 }

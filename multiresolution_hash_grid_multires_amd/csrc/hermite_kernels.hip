@@ -842,16 +842,17 @@ __global__ __launch_bounds__(kBlock) void hermite_backward_kernel(
 }
 
 // Binned backward, count pass: a workgroup histograms the entries of its tile of `tile`
-// points (one per corner and order table) over all bins in LDS.  With equal table sizes
-// (bp.fine_shift >= 0) the rows are histogrammed once per level in fine chunks and each
-// table's bin counts are sums of consecutive fine bins.
+// points (one per corner and order table) at its group of lpg levels (blockIdx.y) in LDS.
+// With equal table sizes (bp.fine_shift >= 0) the rows are histogrammed once per level in
+// fine chunks and each table's bin counts are sums of consecutive fine bins.
 template <int D>
 __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g, const BinPlan bp, int64_t n,
-                                                                    int32_t tile, int32_t nblk,
+                                                                    int32_t tile, int32_t nblk, int32_t lpg,
                                                                     const float* __restrict__ x,
                                                                     int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
+  const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);
   const bool fine = bp.fine_shift >= 0;
   const int nh = fine ? bp.fine_bin0[g.L] : bp.nbins;
   for (int i = threadIdx.x; i < nh; i += kBinThreads) hist[i] = 0;
@@ -862,7 +863,7 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
     float xp[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
-    for (int l = 0; l < g.L; ++l) {
+    for (int l = l0; l < l1; ++l) {
       uint32_t base[D];
       float t[D];
       locate<D>(xp, g.N[l], g.Nf[l], base, t);
@@ -903,11 +904,14 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
   __syncthreads();
   int32_t* row = counts + (int64_t)blk * bp.nbins;
   if (!fine) {
-    for (int i = threadIdx.x; i < bp.nbins; i += kBinThreads) row[i] = hist[i];
+    for (int k = 0; k <= D; ++k)
+      for (int i = bp.seg_bin0[k * bp.L + l0] + threadIdx.x; i < bp.seg_bin0[k * bp.L + l1]; i += kBinThreads)
+        row[i] = hist[i];
     return;
   }
   for (int sg = 0; sg < bp.nseg; ++sg) {
     const int k = sg / bp.L, l = sg % bp.L;
+    if (l < l0 || l >= l1) continue;
     const int ratio_shift = bp.cshift[k] - bp.fine_shift;
     const int32_t f0 = bp.fine_bin0[l], f1 = bp.fine_bin0[l + 1];
     const int32_t b0 = bp.seg_bin0[sg], nb = bp.seg_bin0[sg + 1] - b0;
@@ -1052,7 +1056,7 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
 // words of each bin's contiguous run, so lines are written whole apart from run ends.
 template <int D, int F, int P>
 __global__ __launch_bounds__(P) void hermite_scatter_kernel(
-    const Grid g, const BinPlan bp, int64_t n, int32_t nblk, bool diag, const float* __restrict__ x,
+    const Grid g, const BinPlan bp, int64_t n, int32_t nblk, int32_t lpg, bool diag, const float* __restrict__ x,
     const float* __restrict__ U, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
     const BinState* __restrict__ st, float* __restrict__ vals_out) {
@@ -1065,7 +1069,8 @@ __global__ __launch_bounds__(P) void hermite_scatter_kernel(
   float xp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = on ? x[p * D + i] : 0.0f;
-  for (int l = 0; l < g.L; ++l) {
+  const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);  // this workgroup's levels
+  for (int l = l0; l < l1; ++l) {
     LevelUp<D, F> u;
     CellKeys<D> keys;
     AxisBasis ab[D];
@@ -1092,12 +1097,12 @@ template <int D, int F>
 hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int d2_mode,
                       bool scatter, int64_t n, const float* x, const float* gg, const float* gd,
                       const float* g2, const float* u_levels, hipStream_t s) {
-  const dim3 grid((unsigned)w.nblk);
+  const dim3 grid((unsigned)w.nblk, (unsigned)w.lgroups);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
   if (!scatter) {
     const size_t hist = sizeof(int32_t) * (size_t)(bp.fine_shift >= 0 ? bp.fine_bin0[g.L] : bp.nbins);
     hipLaunchKernelGGL((hermite_count_kernel<D>), grid, dim3(kBinThreads), hist, s,
-                       g, bp, n, w.tile, w.nblk, x, counts);
+                       g, bp, n, w.tile, w.nblk, w.lpg, x, counts);
     return hipGetLastError();
   }
   constexpr int P = hermite_scatter_points(F);
@@ -1134,8 +1139,8 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hermite_scatter_kernel<D, F, P>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((hermite_scatter_kernel<D, F, P>), grid, dim3(P), lds, s, g, bp, n, w.nblk, diag, x, U, counts,
-                     totals, bin_start, st, vals);
+  hipLaunchKernelGGL((hermite_scatter_kernel<D, F, P>), grid, dim3(P), lds, s, g, bp, n, w.nblk, w.lpg, diag, x, U,
+                     counts, totals, bin_start, st, vals);
   return hipGetLastError();
 }
 

@@ -292,3 +292,21 @@ def test_binned_chunk_keeps_entries_in_int32():
     h16 = api.hashenc_create({"d": 3, "L": 16, "F": 2, "kind": "hermite", "T": [1 << 19] * 4,
                               "n_min": 16, "n_max": 1024, "d2_mode": "laplacian"})
     assert api.hashenc_backward_workspace_size(h16, 1 << 21) > api.hashenc_backward_workspace_size(h16, cap)
+
+
+def test_small_dlinear_batches_take_the_atomic_path():
+    """Below n * L = 2^18 a d-linear backward_ws scatters with atomics (no workspace); the
+    Hermite kind keeps the binned path at every size; the diagnostic binned entry point sizes
+    a workspace at any n."""
+    lin = api.hashenc_create({"d": 3, "L": 16, "F": 2, "kind": "dlinear", "T": [1 << 19], "n_min": 16,
+                              "n_max": 2048})
+    assert api.hashenc_backward_workspace_size(lin, (1 << 14) - 1) == 0
+    assert api.hashenc_backward_workspace_size(lin, 1 << 14) > 0
+    assert api.hashenc_diag_binned_workspace_size(lin, 100) > 0
+    herm = api.hashenc_create({"d": 2, "L": 8, "F": 2, "kind": "hermite", "T": [1 << 14] * 3, "n_min": 16,
+                               "n_max": 512, "d2_mode": "laplacian"})
+    assert api.hashenc_backward_workspace_size(herm, 1) > 0
+    rbf = api.hashenc_create({"d": 2, "L": 2, "F": 2, "kind": "rbf", "T": [1 << 12], "n_min": 8, "n_max": 16,
+                              "rbf_eps": 1.0, "rbf_rings": 2})
+    with pytest.raises(_lib.HashencError):
+        api.hashenc_diag_binned_workspace_size(rbf, 100)

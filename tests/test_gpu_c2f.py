@@ -83,7 +83,7 @@ def test_masked_backward_parity(orc, name, path):
         enc = api.HashGridEncoding(dict(spec, active_levels=a))
         grad = _dev(init)
         if path == "binned":
-            enc.backward_ws(xt, grad, *U)
+            enc.backward_binned(xt, grad, *U)
         else:
             enc.backward(xt, grad, *U)
         torch.cuda.synchronize()

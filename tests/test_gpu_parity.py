@@ -94,7 +94,7 @@ def _gpu_backward(spec, x, ups, n_params, path="binned"):
     grad = torch.zeros(n_params, device=DEV)
     U = [_dev(u) for u in ups] + [None] * (3 - len(ups))
     if path == "binned":
-        enc.backward_ws(_dev(x), grad, *U)
+        enc.backward_binned(_dev(x), grad, *U)
     else:
         enc.backward(_dev(x), grad, *U)
     torch.cuda.synchronize()
