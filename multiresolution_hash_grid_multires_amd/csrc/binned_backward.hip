@@ -249,22 +249,28 @@ __device__ __forceinline__ void accumulate_records(double* __restrict__ acc, int
   }
 }
 
-__global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g, const BinPlan bp,
+// ACC fp64 accumulator values and THREADS lanes per workgroup: the 128 KB accumulator (one
+// 1024-lane workgroup per CU) for bins of up to 16384 values, and a 16 KB one (eight 256-lane
+// workgroups per CU) for the small bins of small grids, whose work items are short enough that
+// the per-item latency (fetch, zero, flush) rather than the records sets the time.
+template <int ACC, int THREADS>
+__global__ __launch_bounds__(THREADS) void bin_reduce_kernel(const Grid g, const BinPlan bp,
                                                                     BinState* __restrict__ st,
                                                                     const WorkItem* __restrict__ items,
                                                                     const float* __restrict__ vals,
                                                                     float* __restrict__ grad) {
   // fp64 accumulator: LDS fp64 atomics run several times faster than fp32 ones on gfx950
   // and the chunk sum is exact to far below the fp32 result precision.
-  __shared__ double acc[kBinLdsValues];
-  __shared__ int item_sh;
+  __shared__ double acc[ACC];
+  __shared__ int item_sh[2];
   const int n_items = st->n_items;
-  for (;;) {
-    if (threadIdx.x == 0) item_sh = atomicAdd(&st->next_item, 1);
-    __syncthreads();
-    const int it = item_sh;
-    __syncthreads();
-    if (it >= n_items) break;
+  // Workgroup b takes item b first; later items come from a counter (which starts after the
+  // first gridDim.x items), claimed once the current item's entries are accumulated, so the
+  // claim's latency hides behind the flush without holding an item back during the long part
+  // (two slots, so a claim never overwrites the index others are still reading).
+  int it = blockIdx.x;
+  int slot = 0;
+  while (it < n_items) {
     const WorkItem w = items[it];
     const int sg = __builtin_amdgcn_readfirstlane(w.seg);
     const int k = sg / bp.L, l = sg % bp.L;
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g
     const int64_t rem = seg_rows(g, bp.d, k, l) - row0;
     const int64_t nrows = rem < C ? rem : C;
     const int nfl = (int)(nrows * W);
-    for (int i = threadIdx.x; i < nfl; i += kReduceThreads) acc[i] = 0.0;
+    for (int i = threadIdx.x; i < nfl; i += THREADS) acc[i] = 0.0;
     __syncthreads();
     // values of entry e of segment sg start at vseg + (e - ebase) * W
     const float* vseg = vals + st->seg_vbase[sg];
@@ -299,23 +305,26 @@ __global__ __launch_bounds__(kReduceThreads) void bin_reduce_kernel(const Grid g
       case 16: accumulate_entries<16>(acc, plane, vseg, eb, w.begin, w.end); break;
       default: accumulate_entries<24>(acc, plane, vseg, eb, w.begin, w.end); break;
     }
+    if (threadIdx.x == 0) item_sh[slot] = (int)gridDim.x + atomicAdd(&st->next_item, 1);
     __syncthreads();
     // flush: element i of the chunk is row i / W, component i % W
     float* dst = grad + g.off[k][l] + row0 * W;
     if (w.split) {
-      for (int i = threadIdx.x; i < nfl; i += kReduceThreads) {
+      for (int i = threadIdx.x; i < nfl; i += THREADS) {
         const float a = (float)acc[(i % W) * plane + i / W];
         if (a != 0.0f) atomic_add_f32(dst + i, a);
       }
     } else {
       // rows no entry touched keep their gradient: no read-modify-write for them (a bin of a
       // small batch touches few of its rows)
-      for (int i = threadIdx.x; i < nfl; i += kReduceThreads) {
+      for (int i = threadIdx.x; i < nfl; i += THREADS) {
         const float a = (float)acc[(i % W) * plane + i / W];
         if (a != 0.0f) dst[i] += a;
       }
     }
     __syncthreads();
+    it = item_sh[slot];
+    slot ^= 1;
   }
 }
 
@@ -487,7 +496,16 @@ hipError_t run_bin_middle(const BinPlan& bp, const BinWorkspace& w, char* ws, hi
 
 hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, float* grad,
                           hipStream_t s) {
-  hipLaunchKernelGGL(bin_reduce_kernel, dim3(kBinReduceBlocks), dim3(kReduceThreads), 0, s, g, bp,
+  // the largest chunk of any table, in values: the small accumulator when it fits
+  int64_t chunk_values = 0;
+  for (int k = 0; k < bp.ntab; ++k) chunk_values = std::max<int64_t>(chunk_values, (int64_t)bp.width[k] << bp.cshift[k]);
+  if (chunk_values <= kBinLdsValuesSmall) {
+    hipLaunchKernelGGL((bin_reduce_kernel<kBinLdsValuesSmall, 256>), dim3(kBinReduceBlocks * 8), dim3(256), 0, s, g,
+                       bp, reinterpret_cast<BinState*>(ws + w.state), reinterpret_cast<const WorkItem*>(ws + w.items),
+                       reinterpret_cast<const float*>(ws + w.vals), grad);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((bin_reduce_kernel<kBinLdsValues, kReduceThreads>), dim3(kBinReduceBlocks), dim3(kReduceThreads), 0, s, g, bp,
                      reinterpret_cast<BinState*>(ws + w.state), reinterpret_cast<const WorkItem*>(ws + w.items),
                      reinterpret_cast<const float*>(ws + w.vals),
                      grad);
