@@ -116,11 +116,15 @@ __device__ __forceinline__ void gather_corner(const Grid& g, const CellKeys<D>& 
     load_vec<F>(ts.base[3] + (size_t)corner_row<D, C>(keys, ts.dense[3], g.T[3], g.Tmask[3]) * F, cr.r3);
 }
 
-// Packed copy of the order tables, for handles whose tables all have the same size (then a
-// vertex has the same row in every order table): row r of level l holds [order 0: F |
-// order 1: C(d,1) F | order 2: C(d,2) F | order 3: F] contiguously, 2^d F floats (one 64-byte
-// sector for d = 3, F = 2), so the forward reads a corner's coefficients in one contiguous
-// access instead of one per order table.
+// Packed copy of the order tables: row r of level l -- the row a vertex has in the order-0
+// table -- holds [order 0: F | order 1: C(d,1) F | order 2: C(d,2) F | order 3: F]
+// contiguously, 2^d F floats (one 64-byte sector for d = 3, F = 2), so the forward reads a
+// corner's coefficients in one contiguous access instead of one per order table.  With
+// equal table sizes a vertex has the same row everywhere.  A smaller order table (power-of-
+// two sizes no larger than the order-0 one, as in the pages' best 14-14-10 sizing) is hashed
+// wherever the order-0 table is, with a row that is the order-0 row modulo its size, and a
+// dense order-0 row names its vertex: so the vertex's row in every table follows from r, and
+// the smaller table's rows are repeated across the packed rows that share them.
 struct PackPlan {
   int64_t poff[kMaxLevels + 1];  // float offset of level l in the packed copy
 };
@@ -164,11 +168,22 @@ __global__ __launch_bounds__(kBlock) void hermite_pack_kernel(const Grid g, cons
     int l = 0;
     while (l + 1 < g.L && t * RW >= pp.poff[l + 1]) ++l;
     const int64_t r = t - pp.poff[l] / RW;
+    // row of the same vertex (or hash bucket) in table k
+    auto row_in = [&](int k) -> int64_t {
+      if (g.T[k] == g.T[0]) return r;
+      if (!((g.dense[0] >> l) & 1u)) return r & (int64_t)(g.T[k] - 1);  // both hashed, T_k | T_0
+      if ((g.dense[k] >> l) & 1u) return r;                                // both dense
+      const uint32_t N1 = (uint32_t)g.N[l] + 1u;                           // dense row -> vertex
+      uint32_t h = (uint32_t)(r % N1);
+      if (D > 1) h ^= (uint32_t)((r / N1) % N1) * kPrime1;
+      if (D > 2) h ^= (uint32_t)(r / ((int64_t)N1 * N1)) * kPrime2;
+      return h & (g.T[k] - 1u);
+    };
     float v[RW];
     load_vec_at<F>(params + g.off[0][l] + r * F, v, 0);
-    load_vec_at<W1>(params + g.off[1][l] + r * W1, v, F);
-    load_vec_at<W2>(params + g.off[2][l] + r * W2, v, F + W1);
-    if constexpr (D == 3) load_vec_at<F>(params + g.off[3][l] + r * F, v, F + W1 + W2);
+    load_vec_at<W1>(params + g.off[1][l] + row_in(1) * W1, v, F);
+    load_vec_at<W2>(params + g.off[2][l] + row_in(2) * W2, v, F + W1);
+    if constexpr (D == 3) load_vec_at<F>(params + g.off[3][l] + row_in(3) * F, v, F + W1 + W2);
     store_vec<RW>(stage + threadIdx.x * PITCH, v);
   }
   __syncthreads();
@@ -1581,8 +1596,10 @@ hipError_t launch_bwd4(const Grid& g, int d2_mode, int64_t n, const float* x, co
   } while (0)
 
 bool hermite_packable(const Grid& g, int d) {
+  // every table equal to the order-0 one, or a power of two no larger than it (which the
+  // order-0 size then is too): the row of a vertex in table k follows from its order-0 row
   for (int k = 1; k <= d; ++k)
-    if (g.T[k] != g.T[0]) return false;
+    if (g.T[k] != g.T[0] && !(g.Tmask[k] && g.Tmask[0] && g.T[k] < g.T[0])) return false;
   return true;
 }
 

@@ -36,6 +36,16 @@ WORKLOADS: dict[str, dict] = {
         "tables": ("normal", 1e-2),
         "outputs": ("gamma", "dgamma", "d2gamma"),
     },
+    # 2D Hermite-NGP with the order-table sizes of the Hermite-NGP ablation's best setting
+    # (14-14-10: f and (f_x, f_y) in 2^14 rows, f_xy in 2^10), otherwise as workload 2.
+    "hermite2d_L8_T14_14_10": {
+        "id": 10,
+        "spec": {"d": 2, "L": 8, "F": 2, "kind": "hermite", "T": [1 << 14, 1 << 14, 1 << 10], "n_min": 16,
+                 "n_max": 512, "d2_mode": "laplacian"},
+        "n_points": 1 << 16,
+        "tables": ("normal", 1e-2),
+        "outputs": ("gamma", "dgamma", "d2gamma"),
+    },
     # 3D Instant-NGP d-linear at the standard size: L=16, F=2, T=2^19, N 16..2048.
     "dlinear3d_L16_T19": {
         "id": 3,

@@ -61,3 +61,4 @@ def test_workloads_follow_the_page_configurations():
     assert (s["L"], s["F"], s["T"][0]) == (facts["ingp_levels"], facts["ingp_features"], 1 << facts["ingp_table_log2"])
     assert I.WORKLOADS["hermite2d_L8_T14"]["spec"]["T"][0] == 1 << facts["hermite_table_log2"]
     assert I.WORKLOADS["pinn_residual3d"]["mlp"]["omega"] == facts["siren_omega0"]
+    assert I.WORKLOADS["hermite2d_L8_T14_14_10"]["spec"]["T"] == [1 << facts[f"hermite_best_t{k}_log2"] for k in range(3)]

@@ -230,26 +230,36 @@ def test_feature_widths(orc, kind, F):  # both backward paths
         _grad_close(_gpu_backward(spec, x, ups, lay["n_params"], path), ref, lay, BWD_TOL)
 
 
-@pytest.mark.parametrize("T", [[1000, 3001, 777, 5], [1 << 12, 1 << 13, 1 << 11, 1 << 12]])
+@pytest.mark.parametrize("T", [[1000, 3001, 777, 5], [1 << 12, 1 << 13, 1 << 11, 1 << 12],
+                               [1 << 12, 1 << 12, 1 << 10, 1 << 8], [1 << 14, 1 << 14, 1 << 10]])
 def test_hermite_unequal_tables(orc, T):
     # order tables of different sizes (dense on different levels, modulo and mask hashing):
-    # the count pass histograms every table separately
-    spec = {"d": 3, "L": 4, "F": 2, "kind": "hermite", "T": T, "n_min": 8, "n_max": 64, "d2_mode": "diag"}
+    # the count pass histograms every table separately.  Power-of-two tables no larger than
+    # the order-0 one are packed (their rows repeated across the order-0 rows that share
+    # them), including levels dense in the order-0 table and hashed in a smaller one; the
+    # last case is the 2D 14-14-10 sizing
+    d = len(T) - 1
+    spec = {"d": d, "L": 4, "F": 2, "kind": "hermite", "T": T, "n_min": 8, "n_max": 64 if d == 3 else 512,
+            "d2_mode": "diag"}
     lay = orc.layout(spec)
     rng = np.random.default_rng(sum(T))
     params = rng.standard_normal(lay["n_params"]).astype(np.float32)
-    x = rng.random((3000, 3), dtype=np.float32)
+    n = 3000
+    x = rng.random((n, d), dtype=np.float32)
     got = _gpu_forward(spec, x, params)
     for name, r in zip(("gamma", "dgamma", "d2gamma"), orc.forward(spec, x, params)):
         _blocks_close(got[name], r, spec, FWD_TOL, name)
     enc = api.HashGridEncoding(spec)
-    # unequal tables: nothing to pack, only the level-major staging [L][n][1 + 2d][F]
-    assert api.hashenc_forward_workspace_size(enc.handle, 3000) == 4 * 3000 * spec["L"] * 7 * spec["F"]
+    pow2 = lambda t: t > 1 and t & (t - 1) == 0
+    packable = all(t == T[0] or (pow2(t) and pow2(T[0]) and t < T[0]) for t in T)
+    stage = 4 * n * spec["L"] * (1 + 2 * d) * spec["F"]  # level-major staging [L][n][1 + 2d][F]
+    packed = 4 * int(sum(lay["rows"][0])) * (1 << d) * spec["F"] if packable else 0
+    assert api.hashenc_forward_workspace_size(enc.handle, n) == (packed + 255) // 256 * 256 + stage
     ws_out = enc.forward_ws(_dev(x), _dev(params))
     torch.cuda.synchronize()
     for k in got:
         assert np.array_equal(ws_out[k].cpu().numpy(), got[k]), k
-    ups = [u.astype(np.float32) for u in (rng.standard_normal(s) for s in _upstream_shapes(spec, 3000))]
+    ups = [u.astype(np.float32) for u in (rng.standard_normal(s) for s in _upstream_shapes(spec, n))]
     ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
     for path in PATHS:
         _grad_close(_gpu_backward(spec, x, ups, lay["n_params"], path), ref, lay, BWD_TOL)
@@ -351,7 +361,8 @@ def test_full_size_forward_sampled(orc, name):
         _blocks_close(got["d2gamma"][idx], d2, spec, FWD_TOL, "d2gamma")
 
 
-@pytest.mark.parametrize("name", ["dlinear3d_L16_T19", "hermite3d_L16_T19", "hermite2d_L8_T14"])
+@pytest.mark.parametrize("name", ["dlinear3d_L16_T19", "hermite3d_L16_T19", "hermite2d_L8_T14",
+                                  "hermite2d_L8_T14_14_10"])
 def test_full_size_forward_ws_sampled(orc, name):
     """The workspace forward in the launch configuration the benchmark times: every level
     active, all of the workload's points, the workspace shared with the backward (d-linear:
