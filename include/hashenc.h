@@ -176,7 +176,9 @@ HASHENC_API int hashenc_backward(const hashenc* h, int64_t n, const float* x, co
 
 /* Device workspace (bytes) that hashenc_backward_ws needs for n points (0 when this handle's
  * configuration, or a d-linear batch with n * L < 2^18, does not use one;
- * hashenc_backward_ws then takes the atomic path).  A workspace sized for n points serves
+ * hashenc_backward_ws then takes the atomic path).  Configurations without a binned plan:
+ * the RBF kind, order-table rows wider than 24 floats (d = 4 with F = 8), and grids whose
+ * bins or LDS staging exceed the workgroup budgets.  A workspace sized for n points serves
  * every smaller n. */
 HASHENC_API int hashenc_backward_workspace_size(const hashenc* h, int64_t n, size_t* bytes);
 

@@ -6,7 +6,7 @@
 
 namespace hg {
 
-constexpr int kMaxBinTables = 4;                  // the binned backward covers d <= 3
+constexpr int kMaxBinTables = 5;                  // order tables of the binned backward (d <= 4)
 constexpr int kMaxSeg = kMaxBinTables * kMaxLevels;  // segment s = table k * L + level l
 constexpr int kBinLdsValues = 16384;              // 128 KB fp64 LDS accumulator per work item
 constexpr int kBinLdsValuesSmall = 2048;          // 16 KB accumulator for grids with small bins
@@ -192,6 +192,9 @@ int bin_tile_points(const BinPlan& bp, int d, int F, bool hermite);
 // Points (= threads) of a Hermite scatter workgroup: its LDS staging holds one order table's
 // records for every corner of the tile.
 constexpr int hermite_scatter_points(int F) { return F <= 2 ? 512 : F == 4 ? 128 : 64; }
+// d = 4: a scatter workgroup has one lane per (point, corner), 16 lanes per point; its LDS
+// staging holds one order table's records (at most 6F values) for every lane.
+constexpr int hermite4_scatter_points(int F) { return F <= 2 ? 64 : 32; }
 size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F);
 // LDS of the d-linear scatter workgroup: two per-bin arrays, the per-level staging bases and
 // the pair-record staging.
@@ -209,6 +212,10 @@ hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& 
 hipError_t launch_dlinear_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws,
                               int d, int F, bool scatter, int64_t n, const float* x,
                               const float* g_gamma, const float* u_levels, hipStream_t s);
+// d = 4 Hermite count / scatter (upstream read from the row-major arrays)
+hipError_t launch_hermite4_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int F,
+                               int d2_mode, bool scatter, int64_t n, const float* x, const float* g_gamma,
+                               const float* g_dgamma, const float* g_d2gamma, hipStream_t s);
 // Hermite count / scatter; u_levels: the chunk's upstream already level-major
 // ([L][n][M][F], as the forward's staging) or NULL to rearrange g_gamma / g_dgamma / g_d2gamma
 hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws,

@@ -373,7 +373,9 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
       while ((int64_t(1) << cap) < need && cap < 30) ++cap;
     }
   for (int k = 0; k < bp.ntab; ++k) {
-    const int W = hermite ? (k == 0 || k == d ? F : (d == 3 ? 3 * F : 2 * F)) : F;
+    int W = F;  // Hermite: C(d, k) slots of F floats
+    if (hermite)
+      for (int i = 1; i <= k; ++i) W = W * (d - k + i) / i;
     bp.width[k] = W;
     bp.cshift[k] = std::min(bin_cshift_for_width(W), cap);
     const int64_t C = (int64_t)1 << bp.cshift[k];
@@ -429,12 +431,15 @@ void make_bin_plan(const Grid& g, int d, int F, bool hermite, BinPlan& bp) {
 
 int bin_tile_points(const BinPlan& bp, int d, int F, bool hermite) {
   // one point per scatter lane
-  if (hermite) return hermite_scatter_points(F);
+  if (hermite) return d == 4 ? hermite4_scatter_points(F) : hermite_scatter_points(F);
   return dlinear_scatter_lds_bytes(bp, d, F, kScatterTileLarge) <= kMaxScatterLds ? kScatterTileLarge
                                                                                  : kScatterTileSmall;
 }
 
 size_t hermite_scatter_lds_bytes(const BinPlan& bp, int d, int F) {
+  if (d == 4)  // one staged record of the widest table (6F values) per lane, 16 lanes a point
+    return sizeof(int32_t) * (2 * (size_t)bp.max_level_bins + 16 * hermite4_scatter_points(F) / 64 + 3) +
+           (size_t)16 * hermite4_scatter_points(F) * sizeof(float) * hermite_stage_width(6 * F);
   const int P = hermite_scatter_points(F);
   const int smax = hermite_stage_width((d == 3 ? 3 : 2) * F);  // widest order table's staged record
   return sizeof(int32_t) * (2 * (size_t)bp.max_level_bins + P / 64 + 3) + (size_t)P * (1 << d) * sizeof(float) * smax;
@@ -470,7 +475,8 @@ BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64
   w.items = off; off += al(sizeof(WorkItem) * (size_t)w.max_items);
   w.vals = off; off += al(sizeof(float) * (size_t)(chunk_points * fpp + bp.nseg * kSegAlignFloats));
   // Hermite: the chunk's upstream rearranged level-major, [L][point][1 + 2d][F] at most
-  w.ups = off; off += al(bp.records ? 0 : sizeof(float) * (size_t)chunk_points * bp.L * (1 + 2 * bp.d) * bp.width[0]);
+  w.ups = off;
+  off += al(bp.records || bp.d == 4 ? 0 : sizeof(float) * (size_t)chunk_points * bp.L * (1 + 2 * bp.d) * bp.width[0]);
   w.total = off;
   return w;
 }
@@ -517,6 +523,8 @@ bool binned_fits(const Grid& g, int d, int F, bool hermite) {
   make_bin_plan(g, d, F, hermite, bp);
   const int32_t count_bins = bp.fine_shift >= 0 ? bp.fine_bin0[g.L] : bp.nbins;
   if (bp.nbins > kMaxBins || count_bins > kMaxBins) return false;  // LDS counters of the count pass
+  for (int k = 0; k < bp.ntab; ++k)
+    if (bp.width[k] > 24) return false;  // the reduce's widest record
   if (hermite) return hermite_scatter_lds_bytes(bp, d, F) <= kMaxScatterLds;
   const int tile = bin_tile_points(bp, d, F, hermite);
   return dlinear_scatter_lds_bytes(bp, d, F, tile) <= kMaxScatterLds;
@@ -551,9 +559,10 @@ hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2
     const float* gd = g_dgamma ? g_dgamma + p0 * d * LF : nullptr;
     const float* g2 = g_d2gamma ? g_d2gamma + p0 * (d2_mode == HASHENC_D2_DIAG ? d : 1) * LF : nullptr;
     for (int pass = 0; pass < 2; ++pass) {
-      hipError_t e = hermite ? launch_hermite_bin(g, bp, w, ws, d, F, d2_mode, pass == 1, c, xc, gg, gd, g2,
-                                                  u_levels, s)
-                             : launch_dlinear_bin(g, bp, w, ws, d, F, pass == 1, c, xc, gg, u_levels, s);
+      hipError_t e = !hermite ? launch_dlinear_bin(g, bp, w, ws, d, F, pass == 1, c, xc, gg, u_levels, s)
+                     : d == 4 ? launch_hermite4_bin(g, bp, w, ws, F, d2_mode, pass == 1, c, xc, gg, gd, g2, s)
+                              : launch_hermite_bin(g, bp, w, ws, d, F, d2_mode, pass == 1, c, xc, gg, gd, g2,
+                                                   u_levels, s);
       if (e != hipSuccess) return e;
       if (pass == 0) {
         e = run_bin_middle(bp, w, ws, s);

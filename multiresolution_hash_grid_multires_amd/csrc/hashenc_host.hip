@@ -387,7 +387,7 @@ int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g
 // The binned path keeps per-bin counters and staging in LDS; larger configurations take the
 // atomic path.
 static bool binned_supported(const hashenc* h) {
-  if (h->kind == HASHENC_RBF || h->d == 4) return false;  // RBF and 4D Hermite scatter with atomics
+  if (h->kind == HASHENC_RBF) return false;  // the RBF backward accumulates per level in LDS
   return hg::binned_fits(h->grid, h->d, h->F, h->kind == HASHENC_HERMITE);
 }
 

@@ -856,6 +856,33 @@ __global__ __launch_bounds__(kBlock) void hermite_backward_kernel(
   }
 }
 
+// End of a count workgroup: its LDS histogram becomes the tile's row of per-bin counts for
+// levels l0..l1 of every order table.  A fine histogram (equal table sizes) gives each table's
+// bin counts as sums of consecutive fine bins.
+__device__ __forceinline__ void store_tile_counts(const BinPlan& bp, int l0, int l1, bool fine,
+                                                  const int32_t* hist, int32_t* __restrict__ row) {
+  if (!fine) {
+    for (int k = 0; k < bp.ntab; ++k)
+      for (int i = bp.seg_bin0[k * bp.L + l0] + threadIdx.x; i < bp.seg_bin0[k * bp.L + l1]; i += kBinThreads)
+        row[i] = hist[i];
+    return;
+  }
+  for (int sg = 0; sg < bp.nseg; ++sg) {
+    const int k = sg / bp.L, l = sg % bp.L;
+    if (l < l0 || l >= l1) continue;
+    const int ratio_shift = bp.cshift[k] - bp.fine_shift;
+    const int32_t f0 = bp.fine_bin0[l], f1 = bp.fine_bin0[l + 1];
+    const int32_t b0 = bp.seg_bin0[sg], nb = bp.seg_bin0[sg + 1] - b0;
+    for (int jb = threadIdx.x; jb < nb; jb += kBinThreads) {
+      const int32_t lo = f0 + (jb << ratio_shift);
+      const int32_t hi = min(f1, f0 + ((jb + 1) << ratio_shift));
+      int32_t c = 0;
+      for (int i = lo; i < hi; ++i) c += hist[i];
+      row[b0 + jb] = c;
+    }
+  }
+}
+
 // Binned backward, count pass: a workgroup histograms the entries of its tile of `tile`
 // points (one per corner and order table) at its group of lpg levels (blockIdx.y) in LDS.
 // With equal table sizes (bp.fine_shift >= 0) the rows are histogrammed once per level in
@@ -917,27 +944,7 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
     }
   }
   __syncthreads();
-  int32_t* row = counts + (int64_t)blk * bp.nbins;
-  if (!fine) {
-    for (int k = 0; k <= D; ++k)
-      for (int i = bp.seg_bin0[k * bp.L + l0] + threadIdx.x; i < bp.seg_bin0[k * bp.L + l1]; i += kBinThreads)
-        row[i] = hist[i];
-    return;
-  }
-  for (int sg = 0; sg < bp.nseg; ++sg) {
-    const int k = sg / bp.L, l = sg % bp.L;
-    if (l < l0 || l >= l1) continue;
-    const int ratio_shift = bp.cshift[k] - bp.fine_shift;
-    const int32_t f0 = bp.fine_bin0[l], f1 = bp.fine_bin0[l + 1];
-    const int32_t b0 = bp.seg_bin0[sg], nb = bp.seg_bin0[sg + 1] - b0;
-    for (int jb = threadIdx.x; jb < nb; jb += kBinThreads) {
-      const int32_t lo = f0 + (jb << ratio_shift);
-      const int32_t hi = min(f1, f0 + ((jb + 1) << ratio_shift));
-      int32_t c = 0;
-      for (int i = lo; i < hi; ++i) c += hist[i];
-      row[b0 + jb] = c;
-    }
-  }
+  store_tile_counts(bp, l0, l1, fine, hist, counts + (int64_t)blk * bp.nbins);
 }
 
 // LDS layout of the Hermite scatter workgroup (P points).  The bins of one level's segments
@@ -1546,6 +1553,222 @@ __global__ __launch_bounds__(kBlock) void debug_indices4_kernel(const Grid g, in
   }
 }
 
+// Binned backward for d = 4, count pass: lane j of the workgroup's loop takes point j / 16
+// of the tile and its corner j % 16, and histograms that corner's row in every order table
+// at each level of the group (once, in fine bins, when the table sizes are equal).
+__global__ __launch_bounds__(kBinThreads) void hermite4_count_kernel(const Grid g, const BinPlan bp, int64_t n,
+                                                                     int32_t tile, int32_t nblk, int32_t lpg,
+                                                                     const float* __restrict__ x,
+                                                                     int32_t* __restrict__ counts) {
+  extern __shared__ int32_t hist[];
+  const int blk = bin_tile_of_block(blockIdx.x, nblk);
+  const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);
+  const bool fine = bp.fine_shift >= 0;
+  const int nh = fine ? bp.fine_bin0[g.L] : bp.nbins;
+  for (int i = threadIdx.x; i < nh; i += kBinThreads) hist[i] = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < 16 * tile; j += kBinThreads) {
+    const int64_t p = (int64_t)blk * tile + j / 16;
+    if (p >= n) break;
+    const int c = j % 16;
+    float xp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xp[i] = x[p * 4 + i];
+    for (int l = l0; l < l1; ++l) {
+      uint32_t base[4];
+      float t[4];
+      locate<4>(xp, g.N[l], g.Nf[l], base, t);
+      const Keys4 keys = keys4(base, g.N[l]);
+      if (fine) {
+        const int32_t bin =
+            bp.fine_bin0[l] + (int32_t)(row4(keys, c, (g.dense[0] >> l) & 1u, g.T[0], g.Tmask[0]) >> bp.fine_shift);
+        if (bp.fine_bin0[l + 1] - bp.fine_bin0[l] <= kFewBins) wave_aggregated_add<false>(hist, bin);
+        else atomicAdd(&hist[bin], 1);
+        continue;
+      }
+#pragma unroll
+      for (int k = 0; k <= 4; ++k) {
+        int32_t bin;
+        uint32_t local;
+        bin_of(bp, k, l, row4(keys, c, (g.dense[k] >> l) & 1u, g.T[k], g.Tmask[k]), bin, local);
+        if (bp.seg_bin0[k * bp.L + l + 1] - bp.seg_bin0[k * bp.L + l] <= kFewBins) wave_aggregated_add<false>(hist, bin);
+        else atomicAdd(&hist[bin], 1);
+      }
+    }
+  }
+  __syncthreads();
+  store_tile_counts(bp, l0, l1, fine, hist, counts + (int64_t)blk * bp.nbins);
+}
+
+// Upstream of one point at one level for the d = 4 scatter: G0 value, G1[i] first and G2[i]
+// second derivative along axis i (the Laplacian's upstream counts for every axis).
+template <int F>
+struct Up4 {
+  float G0[F], G1[4][F], G2[4][F];
+};
+
+template <int F>
+__device__ __forceinline__ Up4<F> load_up4(const Grid& g, int64_t p, int l, int d2_mode, const float* __restrict__ gg,
+                                          const float* __restrict__ gd, const float* __restrict__ g2) {
+  const int64_t LF = (int64_t)g.Lrow * F;
+  const int64_t col = (int64_t)l * F;
+  Up4<F> u;
+  if (gg) load_vec<F>(gg + p * LF + col, u.G0);
+  else
+#pragma unroll
+    for (int f = 0; f < F; ++f) u.G0[f] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (gd) load_vec<F>(gd + (p * 4 + i) * LF + col, u.G1[i]);
+    else
+#pragma unroll
+      for (int f = 0; f < F; ++f) u.G1[i][f] = 0.0f;
+    if (!g2) {
+#pragma unroll
+      for (int f = 0; f < F; ++f) u.G2[i][f] = 0.0f;
+    } else {
+      load_vec<F>(g2 + (d2_mode == HASHENC_D2_DIAG ? (p * 4 + i) * LF : p * LF) + col, u.G2[i]);
+    }
+  }
+  return u;
+}
+
+// d theta of the coefficient with derivative bits A of one corner: the upstream of every
+// output times the product of that corner's per-axis factors for the bits of A (value basis
+// on every axis but the differentiated one; the transpose of the forward's contraction).
+template <int F, int A>
+__device__ __forceinline__ void coef_grad4(const CornerAxis (&ca)[4], const Up4<F>& u, float* v) {
+  constexpr int ax = A & 1, ay = (A >> 1) & 1, az = (A >> 2) & 1, aw = (A >> 3) & 1;
+  const float bx = ca[0].b[ax], by = ca[1].b[ay], bz = ca[2].b[az], bw = ca[3].b[aw];
+  const float xyz = bx * by * bz, xyw = bx * by * bw, xzw = bx * bz * bw, yzw = by * bz * bw;
+  const float w0 = xyz * bw;
+  const float w1x = ca[0].d[ax] * yzw, w1y = ca[1].d[ay] * xzw, w1z = ca[2].d[az] * xyw, w1w = ca[3].d[aw] * xyz;
+  const float w2x = ca[0].d2[ax] * yzw, w2y = ca[1].d2[ay] * xzw, w2z = ca[2].d2[az] * xyw,
+              w2w = ca[3].d2[aw] * xyz;
+#pragma unroll
+  for (int f = 0; f < F; ++f)
+    v[f] = w0 * u.G0[f] + w1x * u.G1[0][f] + w1y * u.G1[1][f] + w1z * u.G1[2][f] + w1w * u.G1[3][f] +
+           w2x * u.G2[0][f] + w2y * u.G2[1][f] + w2z * u.G2[2][f] + w2w * u.G2[3][f];
+}
+
+// One (level, order table K) phase of the d = 4 scatter workgroup (T lanes, 16 per point):
+// each lane stages its corner's table-K record {local row, C(4,K) F values} at its slot,
+// sorted by bin, then the records are copied out one per lane.
+template <int F, int T, int K>
+__device__ __forceinline__ void scatter4_table(const Grid& g, const BinPlan& bp, int l, bool on, int c, int np,
+                                               int lo_k, int32_t base, const Keys4& keys, const CornerAxis (&ca)[4],
+                                               const Up4<F>& u, const BinState* __restrict__ st,
+                                               float* __restrict__ vals_out, const HScatterLds<4, F, T>& sh) {
+  constexpr int S = slots4(K);
+  constexpr int W = S * F;
+  constexpr int R = hermite_rec_width(W);
+  constexpr int RS = hermite_stage_width(W);
+  const int sg = K * bp.L + l;
+  const int32_t b0 = bp.seg_bin0[sg];
+  const int nb = bp.seg_bin0[sg + 1] - b0;
+  if (on) {
+    float rec[RS];
+    [&]<int... Q>(std::integer_sequence<int, Q...>) {
+      (coef_grad4<F, alpha4_of_slot(K, Q)>(ca, u, rec + 1 + Q * F), ...);
+    }(std::make_integer_sequence<int, S>{});
+    int32_t bin;
+    uint32_t local;
+    bin_of(bp, K, l, row4(keys, c, (g.dense[K] >> l) & 1u, g.T[K], g.Tmask[K]), bin, local);
+    const int i = lo_k + (bin - b0);
+    const int32_t slot = nb <= kFewBins ? wave_aggregated_add<true>(sh.lcur + lo_k, bin - b0) : atomicAdd(&sh.lcur[i], 1);
+    rec[0] = __uint_as_float(local);
+    rec[R] = __int_as_float(sh.delta[i] + slot);  // the record's entry in the segment
+#pragma unroll
+    for (int j = R + 1; j < RS; ++j) rec[j] = 0.0f;
+    store_vec<RS>(sh.st_rec + (int64_t)(slot - base) * RS, rec);
+  }
+  __syncthreads();
+  const int32_t ebase = st->seg_ebase[sg];
+  float* vseg = vals_out + st->seg_vbase[sg];
+  for (int32_t q = threadIdx.x; q < np * 16; q += T) {
+    float v[RS];
+    load_vec<RS>(sh.st_rec + (int64_t)q * RS, v);
+    float* dst = vseg + (int64_t)(__float_as_int(v[R]) - ebase) * R;
+#pragma unroll
+    for (int j = 0; j < R; ++j) dst[j] = v[j];
+  }
+  __syncthreads();
+}
+
+// Binned backward for d = 4, scatter pass: 16 lanes per point of a P-point tile, lane c
+// owning corner c.  Per level the tile's slot ranges in all of the level's bins are set up at
+// once; then per order table each lane computes its corner's record, stages it by bin and the
+// workgroup copies the records out as contiguous runs.
+template <int F, int P>
+__global__ __launch_bounds__(16 * P) void hermite4_scatter_kernel(
+    const Grid g, const BinPlan bp, int64_t n, int32_t nblk, int32_t lpg, int d2_mode, const float* __restrict__ x,
+    const float* __restrict__ gg, const float* __restrict__ gd, const float* __restrict__ g2,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
+    const BinState* __restrict__ st, float* __restrict__ vals_out) {
+  constexpr int T = 16 * P;
+  extern __shared__ int32_t lds[];
+  const HScatterLds<4, F, T> sh(lds, bp.max_level_bins);
+  const int blk = bin_tile_of_block(blockIdx.x, nblk);
+  const int c = threadIdx.x % 16;
+  const int64_t p = (int64_t)blk * P + threadIdx.x / 16;
+  const bool on = p < n;
+  const int np = (int)min((int64_t)P, n - (int64_t)blk * P);
+  float xp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xp[i] = on ? x[p * 4 + i] : 0.0f;
+  const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);
+  for (int l = l0; l < l1; ++l) {
+    Up4<F> u;
+    Keys4 keys;
+    CornerAxis ca[4];
+    if (on) {
+      u = load_up4<F>(g, p, l, d2_mode, gg, gd, g2);
+      uint32_t base[4];
+      float t[4];
+      locate<4>(xp, g.N[l], g.Nf[l], base, t);
+      keys = keys4(base, g.N[l]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ca[i] = corner_axis(t[i], g.Nf[l], g.invN[l], (c >> i) & 1);
+    }
+    int32_t base_k[5];
+    hermite_level_bins<4, T>(bp, l, blk, nblk, counts, totals, bin_start, sh.delta, sh.lcur, sh.wsum, base_k);
+    int lo = 0;
+    scatter4_table<F, T, 0>(g, bp, l, on, c, np, lo, base_k[0], keys, ca, u, st, vals_out, sh);
+    lo += bp.seg_bin0[l + 1] - bp.seg_bin0[l];
+    scatter4_table<F, T, 1>(g, bp, l, on, c, np, lo, base_k[1], keys, ca, u, st, vals_out, sh);
+    lo += bp.seg_bin0[bp.L + l + 1] - bp.seg_bin0[bp.L + l];
+    scatter4_table<F, T, 2>(g, bp, l, on, c, np, lo, base_k[2], keys, ca, u, st, vals_out, sh);
+    lo += bp.seg_bin0[2 * bp.L + l + 1] - bp.seg_bin0[2 * bp.L + l];
+    scatter4_table<F, T, 3>(g, bp, l, on, c, np, lo, base_k[3], keys, ca, u, st, vals_out, sh);
+    lo += bp.seg_bin0[3 * bp.L + l + 1] - bp.seg_bin0[3 * bp.L + l];
+    scatter4_table<F, T, 4>(g, bp, l, on, c, np, lo, base_k[4], keys, ca, u, st, vals_out, sh);
+  }
+}
+
+template <int F>
+hipError_t launch_bin4(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int d2_mode, bool scatter,
+                       int64_t n, const float* x, const float* gg, const float* gd, const float* g2, hipStream_t s) {
+  const dim3 grid((unsigned)w.nblk, (unsigned)w.lgroups);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
+  if (!scatter) {
+    const size_t hist = sizeof(int32_t) * (size_t)(bp.fine_shift >= 0 ? bp.fine_bin0[g.L] : bp.nbins);
+    hipLaunchKernelGGL(hermite4_count_kernel, grid, dim3(kBinThreads), hist, s, g, bp, n, w.tile, w.nblk, w.lpg, x,
+                       counts);
+    return hipGetLastError();
+  }
+  constexpr int P = hermite4_scatter_points(F);
+  if (w.tile != P) return hipErrorInvalidValue;
+  const size_t lds = hermite_scatter_lds_bytes(bp, 4, F);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hermite4_scatter_kernel<F, P>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((hermite4_scatter_kernel<F, P>), grid, dim3(16 * P), lds, s, g, bp, n, w.nblk, w.lpg, d2_mode, x,
+                     gg, gd, g2, counts, reinterpret_cast<const int32_t*>(ws + w.totals),
+                     reinterpret_cast<const int32_t*>(ws + w.bin_start), reinterpret_cast<const BinState*>(ws + w.state),
+                     reinterpret_cast<float*>(ws + w.vals));
+  return hipGetLastError();
+}
+
 template <int F>
 hipError_t launch_fwd4(const Grid& g, int d2_mode, int64_t n, const float* x, const float* params, float* gamma,
                        float* dgamma, float* d2gamma, hipStream_t s) {
@@ -1655,6 +1878,17 @@ hipError_t launch_hermite4_backward(const Grid& g, int F, int d2_mode, int64_t n
                                     const float* g_gamma, const float* g_dgamma, const float* g_d2gamma,
                                     float* grad, hipStream_t s) {
   HASHENC_DISPATCH_F4(F, launch_bwd4, g, d2_mode, n, x, g_gamma, g_dgamma, g_d2gamma, grad, s);
+}
+
+hipError_t launch_hermite4_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int F,
+                               int d2_mode, bool scatter, int64_t n, const float* x, const float* g_gamma,
+                               const float* g_dgamma, const float* g_d2gamma, hipStream_t s) {
+  switch (F) {  // F = 8 has rows wider than the reduce takes (no binned plan)
+    case 1: return launch_bin4<1>(g, bp, w, ws, d2_mode, scatter, n, x, g_gamma, g_dgamma, g_d2gamma, s);
+    case 2: return launch_bin4<2>(g, bp, w, ws, d2_mode, scatter, n, x, g_gamma, g_dgamma, g_d2gamma, s);
+    case 4: return launch_bin4<4>(g, bp, w, ws, d2_mode, scatter, n, x, g_gamma, g_dgamma, g_d2gamma, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_hermite_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, int d, int F,

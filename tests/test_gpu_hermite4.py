@@ -99,6 +99,33 @@ def test_hermite4_full_size(orc):
     _grad_close(_backward(spec, x[:m], ups, lay["n_params"]), ref, lay, BWD_TOL)
 
 
+def test_hermite4_binned_full_size(orc):
+    """The binned backward (workspace entry point) on all 2^18 points of the workload, the
+    configuration the benchmark times, every gradient block against the oracle."""
+    W = I.WORKLOADS[NAME]
+    spec = W["spec"]
+    lay = orc.layout(spec)
+    x = I.points(W["id"], W["n_points"], 4)
+    n = x.shape[0]
+    assert api.hashenc_backward_workspace_size(api.hashenc_create(spec), n) > 0  # the binned path
+    ups = I.upstream(W["id"], _shapes(spec, n))
+    ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
+    _grad_close(_backward(spec, x, ups, lay["n_params"], ws=True), ref, lay, BWD_TOL)
+
+
+@pytest.mark.parametrize("n", [1, 63, 65, 1000])
+def test_hermite4_binned_ragged(orc, n):
+    """Tiles of 64 points: a single point, one short tile, one full tile and a ragged one, and
+    a batch whose levels are split over several workgroups per tile."""
+    W = I.WORKLOADS[NAME]
+    spec = W["spec"]
+    lay = orc.layout(spec)
+    x = _points(max(n, 128), 20 + n)[:n]
+    ups = I.upstream(W["id"] + n, _shapes(spec, n))
+    ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
+    _grad_close(_backward(spec, x, ups, lay["n_params"], ws=True), ref, lay, BWD_TOL)
+
+
 def test_hermite4_active_levels(orc):
     W = I.WORKLOADS[NAME]
     spec = dict(W["spec"], active_levels=5)
@@ -115,7 +142,10 @@ def test_hermite4_unsupported_paths():
     spec = I.WORKLOADS[NAME]["spec"]
     h = api.hashenc_create(spec)
     assert api.hashenc_forward_workspace_size(h, 1000) == 0
-    assert api.hashenc_backward_workspace_size(h, 1000) == 0
+    assert api.hashenc_backward_workspace_size(h, 1000) > 0  # binned
+    # F = 8: rows of 48 floats in the order-2 table, wider than the binned reduce takes
+    wide = api.hashenc_create(dict(spec, F=8))
+    assert api.hashenc_backward_workspace_size(wide, 1000) == 0
     with pytest.raises(HashencError) as e:
         api.hashenc_residual_workspace_size(h, api.Mlp(16, 32, 2, 30.0), 100)
     assert e.value.code == HASHENC_EUNSUPPORTED

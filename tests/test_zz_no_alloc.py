@@ -77,3 +77,8 @@ def test_noalloc_hermite_then_smaller():
 def test_noalloc_hermite2d_and_atomic_fallback():
     _check("hermite2d_L8_T14", [I.WORKLOADS["hermite2d_L8_T14"]["n_points"], 777])
     _check("rbf3d_L4_N56", [4096, 1000])  # no binned plan: the atomic scatter-add, no scratch
+
+
+def test_noalloc_hermite4d_chunked_then_smaller():
+    # about 19 KB of records per 4D point: 50k points take several chunks of the scratch
+    _check("hermite4d_L8_T16", [50_001, 999])
