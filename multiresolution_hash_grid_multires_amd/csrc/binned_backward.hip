@@ -249,6 +249,8 @@ __device__ __forceinline__ void accumulate_records(double* __restrict__ acc, int
   }
 }
 
+constexpr int kFlushBatch = 8;  // gradient values per thread in flight in the reduce's flush
+
 // ACC fp64 accumulator values and THREADS lanes per workgroup: the 128 KB accumulator (one
 // 1024-lane workgroup per CU) for bins of up to 16384 values, and a 16 KB one (eight 256-lane
 // workgroups per CU) for the small bins of small grids, whose work items are short enough that
@@ -261,7 +263,9 @@ __global__ __launch_bounds__(THREADS) void bin_reduce_kernel(const Grid g, const
                                                                     float* __restrict__ grad) {
   // fp64 accumulator: LDS fp64 atomics run several times faster than fp32 ones on gfx950
   // and the chunk sum is exact to far below the fp32 result precision.
-  __shared__ double acc[ACC];
+  // component planes of nrows + 1 values (odd for even nrows), so that the W components of a
+  // row fall in different LDS banks when the flush reads them side by side
+  __shared__ double acc[ACC + 32];
   __shared__ int item_sh[2];
   const int n_items = st->n_items;
   // Workgroup b takes item b first; later items come from a counter (which starts after the
@@ -281,12 +285,12 @@ __global__ __launch_bounds__(THREADS) void bin_reduce_kernel(const Grid g, const
     const int64_t rem = seg_rows(g, bp.d, k, l) - row0;
     const int64_t nrows = rem < C ? rem : C;
     const int nfl = (int)(nrows * W);
-    for (int i = threadIdx.x; i < nfl; i += THREADS) acc[i] = 0.0;
+    const int plane = (int)nrows + 1;
+    for (int i = threadIdx.x; i < plane * W; i += THREADS) acc[i] = 0.0;
     __syncthreads();
     // values of entry e of segment sg start at vseg + (e - ebase) * W
     const float* vseg = vals + st->seg_vbase[sg];
     const int32_t eb = st->seg_ebase[sg];
-    const int plane = (int)nrows;
     if (bp.records) {
       switch (W) {
         case 1: accumulate_records<1>(acc, plane, vseg, eb, w.begin, w.end); break;
@@ -316,10 +320,22 @@ __global__ __launch_bounds__(THREADS) void bin_reduce_kernel(const Grid g, const
       }
     } else {
       // rows no entry touched keep their gradient: no read-modify-write for them (a bin of a
-      // small batch touches few of its rows)
-      for (int i = threadIdx.x; i < nfl; i += THREADS) {
-        const float a = (float)acc[(i % W) * plane + i / W];
-        if (a != 0.0f) dst[i] += a;
+      // small batch touches few of its rows).  kFlushBatch gradient loads per thread are in
+      // flight before their stores: one read-modify-write round trip per batch rather than
+      // one per value.
+      for (int i0 = threadIdx.x; i0 < nfl; i0 += THREADS * kFlushBatch) {
+        float a[kFlushBatch], gv[kFlushBatch];
+#pragma unroll
+        for (int u = 0; u < kFlushBatch; ++u) {
+          const int i = i0 + u * THREADS;
+          a[u] = i < nfl ? (float)acc[(i % W) * plane + i / W] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kFlushBatch; ++u)
+          if (a[u] != 0.0f) gv[u] = dst[i0 + u * THREADS];
+#pragma unroll
+        for (int u = 0; u < kFlushBatch; ++u)
+          if (a[u] != 0.0f) dst[i0 + u * THREADS] = gv[u] + a[u];
       }
     }
     __syncthreads();

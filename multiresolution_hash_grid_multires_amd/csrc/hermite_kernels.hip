@@ -1061,12 +1061,23 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
   // so the R stores of a wavefront fill the run's lines between them (a word per lane, for
   // whole-line stores, measured slower)
   const int32_t recs = np * NC;
-  for (int32_t q = threadIdx.x; q < recs; q += P) {
-    float v[RS];
-    load_vec<RS>(sh.st_rec + (int64_t)q * RS, v);
+  auto put = [&](const float (&v)[RS]) {
     float* dst = vseg + (int64_t)(__float_as_int(v[R]) - ebase) * R;
 #pragma unroll
     for (int j = 0; j < R; ++j) dst[j] = v[j];
+  };
+  int32_t q = threadIdx.x;
+  for (; q + P < recs; q += 2 * P) {  // two records' LDS reads in flight before their stores
+    float v0[RS], v1[RS];
+    load_vec<RS>(sh.st_rec + (int64_t)q * RS, v0);
+    load_vec<RS>(sh.st_rec + (int64_t)(q + P) * RS, v1);
+    put(v0);
+    put(v1);
+  }
+  if (q < recs) {
+    float v[RS];
+    load_vec<RS>(sh.st_rec + (int64_t)q * RS, v);
+    put(v);
   }
   __syncthreads();
 }

@@ -471,20 +471,52 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
     for (int k = 0; k < DEPTH; ++k) gb[k][i] = 0.0f;
   }
 
-  const int64_t n_iter = (n + kMP - 1) / kMP;
-  for (int64_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
-    const int64_t p0 = it * kMP;
-    // encoder rows -> V_0[j][16 r + p]; walked level by level, the 16 points' R rows of F
-    // features of one level being contiguous in the level-major encoder output
-    for (int e = threadIdx.x; e < kMP * R * NI; e += kW * kMWaves) {
+  // Encoder rows -> V_0[j][16 r + p]: element e of an iteration's rows, walked level by level
+  // (the 16 points' R rows of F features of one level are contiguous in the level-major
+  // encoder output), goes to thread e % T.  The next iteration's rows are loaded into
+  // registers right after this iteration's are parked in LDS, so their memory latency hides
+  // behind the iteration's products instead of stalling its start.
+  constexpr int T = kW * kMWaves;
+  constexpr int EPT = kMP * R * NI / T;
+  static_assert(kMP * R * NI % T == 0, "encoder rows split evenly over the workgroup");
+  // Byte offsets from the iteration's first row are 32-bit (one chunk's encoder output is
+  // below 4 GiB, checked at launch): one offset register per load from a uniform base.
+  const uint32_t level_bytes = (uint32_t)(((uint64_t)n * R << a.fshift) * sizeof(float));
+  auto rows_load = [&](int64_t q0, float (&ev)[EPT]) {
+    const char* base = reinterpret_cast<const char*>(enc + ((q0 * R) << a.fshift));
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = threadIdx.x + u * T;
+      const int f = e & ((1 << a.fshift) - 1), t = e >> a.fshift;
+      const int t2 = t / R;
+      const int p = t2 % kMP, l = t2 / kMP;
+      const int j = (l << a.fshift) + f;
+      const uint32_t off = (uint32_t)l * level_bytes + (uint32_t)(e - ((l * kMP * R) << a.fshift)) * 4u;
+      ev[u] = (j < a.ain && q0 + p < n) ? *reinterpret_cast<const float*>(base + off) : 0.0f;
+    }
+  };
+  auto rows_park = [&](const float (&ev)[EPT]) {
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = threadIdx.x + u * T;
       const int f = e & ((1 << a.fshift) - 1), t = e >> a.fshift;
       const int r = t % R, t2 = t / R;
       const int p = t2 % kMP, l = t2 / kMP;
-      const int j = (l << a.fshift) + f;
-      const int64_t pp = p0 + p;
-      sh.act0[j][r * kMP + p] = (j < a.ain && pp < n) ? enc[lm_index(a, n, pp, j, r, R)] : 0.0f;
+      sh.act0[(l << a.fshift) + f][r * kMP + p] = ev[u];
     }
+  };
+  const int64_t n_iter = (n + kMP - 1) / kMP;
+  float ev[EPT];
+  if (blockIdx.x < n_iter) rows_load((int64_t)blockIdx.x * kMP, ev);
+  for (int64_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
+    const int64_t p0 = it * kMP;
+    rows_park(ev);
     __syncthreads();
+    // this iteration's coordinates (the source term), used after the forward
+    const int64_t pp = p0 + lm;
+    float xs[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) xs[i] = pp < n ? x[pp * D + i] : 0.0f;
 
     // forward mode
     mf4 z[DEPTH][R];  // tape: the wavefront's neurons
@@ -547,7 +579,6 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
       if (lq == 0) sh.lapw[w][lm] = part;
     }
     __syncthreads();
-    const int64_t pp = p0 + lm;
     float seed = 0.0f;
     if (pp < n) {
       float lap_u = 0.0f;
@@ -555,7 +586,7 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
       for (int v = 0; v < kMWaves; ++v) lap_u += sh.lapw[v][lm];
       float src = -(float)D * 9.8696044010893586f;  // -d pi^2
 #pragma unroll
-      for (int i = 0; i < D; ++i) src *= sinpif(x[pp * D + i]);
+      for (int i = 0; i < D; ++i) src *= sinpif(xs[i]);
       const float res = lap_u - src;
       if (w == 0 && lq == 0) {
         sq = fmaf(res, res, sq);
@@ -574,6 +605,8 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
     for (int i = 0; i < 4; ++i) abar[R - 1][i] = seed * wout[i];
 #pragma unroll
     for (int k = DEPTH - 1; k >= 0; --k) {
+      // the next iteration's encoder rows, issued where the tape of the upper layer is dead
+      if (k == 0 && it + gridDim.x < n_iter) rows_load((it + gridDim.x) * kMP, ev);
       mf4 zbar[R];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -629,13 +662,18 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) abar[r] = vbar[r];
       } else if (16 * w < fi && pp < n) {
-        // encoder upstream, inputs j = 16w + 4lq + i of point pp
+        // encoder upstream, inputs j = 16w + 4lq + i of point pp (the encoder output's layout,
+        // 32-bit byte offsets from the iteration's first row)
+        char* ubase = reinterpret_cast<char*>(up + ((p0 * R) << a.fshift));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = 16 * w + 4 * lq + i;
           if (j < a.ain) {
+            const int l = j >> a.fshift, f = j & ((1 << a.fshift) - 1);
+            const uint32_t off = (uint32_t)l * level_bytes + (uint32_t)(((lm * R) << a.fshift) + f) * 4u;
 #pragma unroll
-            for (int r = 0; r < R; ++r) up[lm_index(a, n, pp, j, r, R)] = vbar[r][i];
+            for (int r = 0; r < R; ++r)
+              *reinterpret_cast<float*>(ubase + off + ((uint32_t)r << a.fshift) * 4u) = vbar[r][i];
           }
         }
       }
@@ -780,19 +818,50 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
     for (int k = 0; k < DEPTH; ++k) gb[k][i] = 0.0f;
   }
 
-  const int64_t n_iter = (n + kMP - 1) / kMP;
-  for (int64_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
-    const int64_t p0 = it * kMP;
-    // walked level by level: the 16 points' R stencil rows of F features are contiguous
-    for (int e = threadIdx.x; e < kMP * R * NI; e += kW * kFdWaves) {
+  // Encoder rows of the stencil points, walked level by level (the 16 points' R stencil rows
+  // of F features are contiguous): element e to thread e % T.  The next iteration's rows are
+  // loaded into registers during this iteration's reverse sweep, so their latency hides
+  // behind its products.  Byte offsets from the iteration's first row are 32-bit
+  // (one chunk's encoder output is below 4 GiB, checked at launch).
+  constexpr int T = kW * kFdWaves;
+  constexpr int TOT = kMP * R * NI;
+  constexpr int EPT = (TOT + T - 1) / T;
+  const uint32_t level_bytes = (uint32_t)(((uint64_t)n * R << a.fshift) * sizeof(float));
+  auto rows_load = [&](int64_t q0, float (&ev)[EPT]) {
+    const char* base = reinterpret_cast<const char*>(enc + ((q0 * R) << a.fshift));
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = threadIdx.x + u * T;
+      const int f = e & ((1 << a.fshift) - 1), t = e >> a.fshift;
+      const int t2 = t / R;
+      const int p = t2 % kMP, l = t2 / kMP;
+      const int j = (l << a.fshift) + f;
+      const uint32_t off = (uint32_t)l * level_bytes + (uint32_t)(e - ((l * kMP * R) << a.fshift)) * 4u;
+      ev[u] = (e < TOT && j < a.ain && q0 + p < n) ? *reinterpret_cast<const float*>(base + off) : 0.0f;
+    }
+  };
+  auto rows_park = [&](const float (&ev)[EPT]) {
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = threadIdx.x + u * T;
       const int f = e & ((1 << a.fshift) - 1), t = e >> a.fshift;
       const int r = t % R, t2 = t / R;
       const int p = t2 % kMP, l = t2 / kMP;
-      const int j = (l << a.fshift) + f;
-      const int64_t pp = p0 + p;
-      sh.act0[j][r * kMP + p] = (j < a.ain && pp < n) ? enc[lm_index(a, n, pp, j, r, R)] : 0.0f;
+      if (e < TOT) sh.act0[(l << a.fshift) + f][r * kMP + p] = ev[u];
     }
+  };
+  const int64_t n_iter = (n + kMP - 1) / kMP;
+  float ev[EPT];
+  if (blockIdx.x < n_iter) rows_load((int64_t)blockIdx.x * kMP, ev);
+  for (int64_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
+    const int64_t p0 = it * kMP;
+    rows_park(ev);
     __syncthreads();
+    // this iteration's coordinates (the source term), used after the forward
+    const int64_t pp = p0 + lm;
+    float xs[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) xs[i] = pp < n ? x[pp * D + i] : 0.0f;
 
     // forward: every column group is a value row; layers as compile-time steps so the tape
     // stays in registers
@@ -855,7 +924,6 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
       if (lq == 0 && r0 + rr < R) sh.uw[wn][r0 + rr][lm] = part;
     }
     __syncthreads();
-    const int64_t pp = p0 + lm;
     float seed = 0.0f;
     if (pp < n) {
       float u0 = 0.0f, lap = 0.0f;  // the output bias cancels in every second difference
@@ -880,7 +948,7 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
       }
       float src = -(float)D * 9.8696044010893586f;  // -d pi^2
 #pragma unroll
-      for (int i = 0; i < D; ++i) src *= sinpif(x[pp * D + i]);
+      for (int i = 0; i < D; ++i) src *= sinpif(xs[i]);
       const float res = lap - src;
       if (w == 0 && lq == 0) {
         sq = fmaf(res, res, sq);
@@ -962,6 +1030,8 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
       }
     };
     if constexpr (DEPTH > 1) rev_layer.template operator()<1>();
+    // the next iteration's encoder rows, issued where the upper layer's tape is dead
+    if (it + gridDim.x < n_iter) rows_load((it + gridDim.x) * kMP, ev);
     rev_layer.template operator()<0>();
   }
 
@@ -1108,7 +1178,9 @@ template <int D, int DEPTH, int INP>
 hipError_t launch_siren(const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* enc,
                         const float* mlp, float* up, float* residual, float* partial, int& rows, hipStream_t s) {
   if constexpr (DEPTH <= 2) {
-    // matrix cores: one partial row per workgroup
+    // matrix cores: one partial row per workgroup; the kernel addresses the encoder output
+    // with 32-bit byte offsets
+    if ((uint64_t)n * (D + 2) * a.in * sizeof(float) >= (uint64_t(1) << 32)) return hipErrorInvalidValue;
     int blocks = (int)((n + kMP - 1) / kMP);
     if (blocks > kMfmaBlocks) blocks = kMfmaBlocks;
     rows = blocks;
@@ -1159,6 +1231,8 @@ template <int D, int DEPTH, int NI>
 hipError_t launch_fd_siren(const MlpArgs& a, int64_t n, double inv_n, float inv_eps2, const float* x,
                            const float* enc, const float* mlp, float* up, float* u_stencil, float* residual,
                            float* partial, int& rows, hipStream_t s) {
+  // the kernel addresses the encoder output with 32-bit byte offsets
+  if ((uint64_t)n * (2 * D + 1) * a.in * sizeof(float) >= (uint64_t(1) << 32)) return hipErrorInvalidValue;
   int blocks = (int)((n + kMP - 1) / kMP);
   if (blocks > kFdBlocks) blocks = kFdBlocks;
   rows = blocks * kFdGroups;  // one partial row per row group
