@@ -964,26 +964,71 @@ struct HScatterLds {
 };
 
 // Per level: the tile's slot ranges in every bin of the level's segments, from the count
-// pass (one round of global reads per level rather than one per order table).  base[k]:
-// the first slot of table k, so that table k's records take staging slots 0 .. np * NC.
-template <int D, int P>
-__device__ __forceinline__ void hermite_level_bins(const BinPlan& bp, int l, int blk, int nblk,
-                                                   const int32_t* __restrict__ counts,
-                                                   const int32_t* __restrict__ totals,
-                                                   const int32_t* __restrict__ bin_start, int32_t* delta,
-                                                   int32_t* lcur, int32_t* wsum, int32_t (&base)[D + 1]) {
+// pass (one round of global reads per level rather than one per order table).  The level's
+// bins (order tables in turn) are numbered 0 .. lo; bin i is read by thread i % P into
+// register slot i / P (NPB slots; bins past NPB * P are read when applied).  Loading and
+// applying are separate so that the next level's reads can be issued a level ahead: waiting
+// for them then does not wait for the record stores issued in between.
+template <int NPB>
+struct LevelBinRegs {
+  int32_t start[NPB], cur[NPB], nxt[NPB];
+};
+
+// global bin of level-bin i (order tables in turn), or -1 past the level's bins
+template <int D>
+__device__ __forceinline__ int32_t level_bin_global(const BinPlan& bp, int l, int i) {
   int lo = 0;
 #pragma unroll
   for (int k = 0; k <= D; ++k) {
     const int32_t b0 = bp.seg_bin0[k * bp.L + l];
     const int nb = bp.seg_bin0[k * bp.L + l + 1] - b0;
-    for (int i = threadIdx.x; i < nb; i += P) {
-      const int32_t pre = counts[(int64_t)blk * bp.nbins + b0 + i];
-      const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)(blk + 1) * bp.nbins + b0 + i] : totals[b0 + i];
-      delta[lo + i] = bin_start[b0 + i] + pre;
-      lcur[lo + i] = nxt - pre;
-    }
+    if (i < lo + nb) return b0 + (i - lo);
     lo += nb;
+  }
+  return -1;
+}
+
+template <int D, int P, int NPB>
+__device__ __forceinline__ void level_bins_load(const BinPlan& bp, int l, int blk, int nblk,
+                                                const int32_t* __restrict__ counts,
+                                                const int32_t* __restrict__ totals,
+                                                const int32_t* __restrict__ bin_start, LevelBinRegs<NPB>& r) {
+#pragma unroll
+  for (int q = 0; q < NPB; ++q) {
+    const int32_t b = level_bin_global<D>(bp, l, threadIdx.x + q * P);
+    if (b >= 0) {
+      r.start[q] = bin_start[b];
+      r.cur[q] = counts[(int64_t)blk * bp.nbins + b];
+      r.nxt[q] = blk + 1 < nblk ? counts[(int64_t)(blk + 1) * bp.nbins + b] : totals[b];
+    }
+  }
+}
+
+// base[k]: the first slot of table k, so that table k's records take staging slots
+// 0 .. np * NC.
+template <int D, int P, int NPB>
+__device__ __forceinline__ void level_bins_apply(const BinPlan& bp, int l, int blk, int nblk,
+                                                 const int32_t* __restrict__ counts,
+                                                 const int32_t* __restrict__ totals,
+                                                 const int32_t* __restrict__ bin_start, const LevelBinRegs<NPB>& r,
+                                                 int32_t* delta, int32_t* lcur, int32_t* wsum, int32_t (&base)[D + 1]) {
+  int lo = 0;
+#pragma unroll
+  for (int k = 0; k <= D; ++k) lo += bp.seg_bin0[k * bp.L + l + 1] - bp.seg_bin0[k * bp.L + l];
+#pragma unroll
+  for (int q = 0; q < NPB; ++q) {
+    const int i = threadIdx.x + q * P;
+    if (i < lo) {
+      delta[i] = r.start[q] + r.cur[q];
+      lcur[i] = r.nxt[q] - r.cur[q];
+    }
+  }
+  for (int i = threadIdx.x + NPB * P; i < lo; i += P) {  // bins beyond the register slots
+    const int32_t b = level_bin_global<D>(bp, l, i);
+    const int32_t pre = counts[(int64_t)blk * bp.nbins + b];
+    const int32_t nxt = blk + 1 < nblk ? counts[(int64_t)(blk + 1) * bp.nbins + b] : totals[b];
+    delta[i] = bin_start[b] + pre;
+    lcur[i] = nxt - pre;
   }
   __syncthreads();
   block_exclusive_scan<P>(lcur, lo, wsum);
@@ -995,6 +1040,17 @@ __device__ __forceinline__ void hermite_level_bins(const BinPlan& bp, int l, int
     lo += bp.seg_bin0[k * bp.L + l + 1] - bp.seg_bin0[k * bp.L + l];
   }
   __syncthreads();
+}
+
+template <int D, int P>
+__device__ __forceinline__ void hermite_level_bins(const BinPlan& bp, int l, int blk, int nblk,
+                                                   const int32_t* __restrict__ counts,
+                                                   const int32_t* __restrict__ totals,
+                                                   const int32_t* __restrict__ bin_start, int32_t* delta,
+                                                   int32_t* lcur, int32_t* wsum, int32_t (&base)[D + 1]) {
+  LevelBinRegs<1> r;
+  level_bins_load<D, P, 1>(bp, l, blk, nblk, counts, totals, bin_start, r);
+  level_bins_apply<D, P, 1>(bp, l, blk, nblk, counts, totals, bin_start, r, delta, lcur, wsum, base);
 }
 
 // Stage the two records of corner pair (0, Y) for order table K.  lo_k: the table's first bin
@@ -1103,16 +1159,26 @@ __global__ __launch_bounds__(P) void hermite_scatter_kernel(
 #pragma unroll
   for (int i = 0; i < D; ++i) xp[i] = on ? x[p * D + i] : 0.0f;
   const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);  // this workgroup's levels
+  // the next level's upstream and bin ranges are loaded while this level's records are
+  // staged and stored
+  constexpr int NPB = 2;
+  LevelUp<D, F> un;
+  LevelBinRegs<NPB> rn;
+  if (l0 < l1) {
+    if (on) un = load_level_up_lm<D, F>(U, n, p, l0, diag);
+    level_bins_load<D, P, NPB>(bp, l0, blk, nblk, counts, totals, bin_start, rn);
+  }
   for (int l = l0; l < l1; ++l) {
-    LevelUp<D, F> u;
+    const LevelUp<D, F> u = un;
+    int32_t base[D + 1];
+    level_bins_apply<D, P, NPB>(bp, l, blk, nblk, counts, totals, bin_start, rn, sh.delta, sh.lcur, sh.wsum, base);
+    if (l + 1 < l1) {
+      if (on) un = load_level_up_lm<D, F>(U, n, p, l + 1, diag);
+      level_bins_load<D, P, NPB>(bp, l + 1, blk, nblk, counts, totals, bin_start, rn);
+    }
     CellKeys<D> keys;
     AxisBasis ab[D];
-    if (on) {
-      u = load_level_up_lm<D, F>(U, n, p, l, diag);
-      level_setup<D>(g, l, xp, keys, ab);
-    }
-    int32_t base[D + 1];
-    hermite_level_bins<D, P>(bp, l, blk, nblk, counts, totals, bin_start, sh.delta, sh.lcur, sh.wsum, base);
+    if (on) level_setup<D>(g, l, xp, keys, ab);
     int lo = 0;
     scatter_table<D, F, P, 0>(g, bp, l, on, np, lo, base[0], keys, ab, u, st, vals_out, sh);
     lo += bp.seg_bin0[l + 1] - bp.seg_bin0[l];
@@ -1730,10 +1796,12 @@ __global__ __launch_bounds__(16 * P) void hermite4_scatter_kernel(
   const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);
   for (int l = l0; l < l1; ++l) {
     Up4<F> u;
+    if (on) u = load_up4<F>(g, p, l, d2_mode, gg, gd, g2);
+    int32_t base_k[5];
+    hermite_level_bins<4, T>(bp, l, blk, nblk, counts, totals, bin_start, sh.delta, sh.lcur, sh.wsum, base_k);
     Keys4 keys;
     CornerAxis ca[4];
     if (on) {
-      u = load_up4<F>(g, p, l, d2_mode, gg, gd, g2);
       uint32_t base[4];
       float t[4];
       locate<4>(xp, g.N[l], g.Nf[l], base, t);
@@ -1741,8 +1809,6 @@ __global__ __launch_bounds__(16 * P) void hermite4_scatter_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) ca[i] = corner_axis(t[i], g.Nf[l], g.invN[l], (c >> i) & 1);
     }
-    int32_t base_k[5];
-    hermite_level_bins<4, T>(bp, l, blk, nblk, counts, totals, bin_start, sh.delta, sh.lcur, sh.wsum, base_k);
     int lo = 0;
     scatter4_table<F, T, 0>(g, bp, l, on, c, np, lo, base_k[0], keys, ca, u, st, vals_out, sh);
     lo += bp.seg_bin0[l + 1] - bp.seg_bin0[l];
