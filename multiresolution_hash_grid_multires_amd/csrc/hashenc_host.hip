@@ -292,7 +292,8 @@ int hashenc_forward(const hashenc* h, int64_t n, const float* x, const float* pa
   else if (h->kind == HASHENC_RBF)
     e = hg::launch_rbf_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, gamma, dgamma, d2gamma, stream);
   else if (h->d == 4)
-    e = hg::launch_hermite4_forward(h->grid, h->F, h->d2_mode, n, x, params, gamma, dgamma, d2gamma, stream);
+    e = hg::launch_hermite4_forward(h->grid, h->F, h->d2_mode, n, x, params, nullptr, gamma, dgamma, d2gamma,
+                                    stream);
   else
     e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, nullptr, nullptr, false, gamma,
                                    dgamma, d2gamma, stream);
@@ -306,7 +307,8 @@ int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_workspace_size: n out of range");
   *bytes = h->kind == HASHENC_DLINEAR                 ? hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n)
            : (h->kind == HASHENC_HERMITE && h->d < 4) ? hermite_forward_ws_bytes(h, n)
-                                                      : 0;  // RBF and 4D Hermite: no workspace
+           : h->kind == HASHENC_HERMITE               ? hg::hermite4_packed_bytes(h->grid, h->F)  // 4D: packed copy
+                                                      : 0;  // RBF: no workspace
   return ok();
 }
 
@@ -314,7 +316,27 @@ int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float*
                        float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
                        hashenc_stream_t stream) {
   if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_ws: NULL handle");
-  if (h->kind == HASHENC_RBF || h->d == 4) return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
+  if (h->kind == HASHENC_RBF || (h->d == 4 && hg::hermite4_packed_bytes(h->grid, h->F) == 0))
+    return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
+  if (h->d == 4) {
+    // workspace: the packed copy of the five order tables, written and then read by the forward
+    const size_t need = hg::hermite4_packed_bytes(h->grid, h->F);
+    if (n == 0 || (!gamma && !dgamma && !d2gamma))
+      return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
+    if (n < 0 || n > kMaxPoints)
+      return fail(HASHENC_EINVAL, "hashenc_forward_ws: n = %lld out of range", (long long)n);
+    if (!x || !params || !workspace)
+      return fail(HASHENC_EINVAL, "hashenc_forward_ws: x, params and workspace must not be NULL");
+    if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || !aligned16(dgamma) || !aligned16(d2gamma) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+      return fail(HASHENC_EALIGN, "hashenc_forward_ws: pointers must be 16-byte aligned (workspace 256-byte)");
+    if (workspace_bytes < need)
+      return fail(HASHENC_EINVAL, "hashenc_forward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    hipError_t e = hg::launch_hermite4_forward(h->grid, h->F, h->d2_mode, n, x, params, static_cast<float*>(workspace),
+                                               gamma, dgamma, d2gamma, stream);
+    if (e != hipSuccess) return hip_fail(e, "hashenc_forward_ws launch");
+    return ok();
+  }
   if (h->kind == HASHENC_HERMITE) {
     // workspace: [packed copy of the order tables (equal table sizes) | level-major staging]
     const size_t need = hermite_forward_ws_bytes(h, n);

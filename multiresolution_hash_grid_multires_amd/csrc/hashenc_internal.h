@@ -154,9 +154,13 @@ hipError_t launch_hermite_forward(const Grid& g, int d, int F, int d2_mode, int6
 hipError_t launch_hermite_backward(const Grid& g, int d, int F, int d2_mode, int64_t n,
                                    const float* x, const float* g_gamma, const float* g_dgamma,
                                    const float* g_d2gamma, const float* u_levels, float* grad, hipStream_t s);
-// Space-time Hermite (d = 4: five order tables, 16 coefficients per vertex; fp32-atomic backward)
+// Space-time Hermite (d = 4: five order tables, 16 coefficients per vertex).  packed: NULL to
+// read the tables, else room for the packed copy (hermite4_packed_bytes, nonzero for F <= 2 and
+// packable table sizes), which the forward writes and then reads.
+size_t hermite4_packed_bytes(const Grid& g, int F);
 hipError_t launch_hermite4_forward(const Grid& g, int F, int d2_mode, int64_t n, const float* x,
-                                   const float* params, float* gamma, float* dgamma, float* d2gamma, hipStream_t s);
+                                   const float* params, float* packed, float* gamma, float* dgamma, float* d2gamma,
+                                   hipStream_t s);
 hipError_t launch_hermite4_backward(const Grid& g, int F, int d2_mode, int64_t n, const float* x,
                                     const float* g_gamma, const float* g_dgamma, const float* g_d2gamma,
                                     float* grad, hipStream_t s);

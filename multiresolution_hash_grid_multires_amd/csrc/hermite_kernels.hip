@@ -1334,7 +1334,8 @@ hipError_t launch_bwd(const Grid& g, int d2_mode, int64_t n, const float* x, con
 // the forward contracts it with the per-axis bases one axis at a time (w, z, y, x), carrying
 // only the derivative kinds that survive (value; first and second derivative along each axis
 // already passed): 3 -> 5 -> 7 -> 9 results.  The backward runs the same contraction
-// transposed and scatter-adds with fp32 atomics.
+// transposed, per coefficient, and either scatter-adds with fp32 atomics or writes binned
+// records (one per point, level, corner and order table) for the binned reduce.
 constexpr uint32_t kPrime3 = 3674653429u;
 
 // alpha (bit i = derivative along axis i) of slot s of order table k, slots of one order in
@@ -1404,9 +1405,63 @@ __device__ __forceinline__ CornerAxis corner_axis(float t, float N, float invN, 
   return r;
 }
 
+// Packed copy of the five order tables for d = 4: packed row t of level l (t counts the
+// order-0 table's rows) holds the vertex's rows of tables 0..4 side by side (16 F floats).
+// A smaller power-of-two table's row follows from the order-0 row as in the 2D / 3D packing
+// (a dense order-0 row names its vertex, which is hashed with the four primes).  Rows go
+// through LDS and out as 16-byte pieces, whole lines per store instruction.
 template <int F>
-__global__ __launch_bounds__(kBlock) void hermite4_forward_kernel(const Grid g, int64_t n, int32_t n_tiles,
-                                                                  int d2_mode, const float* __restrict__ x,
+__global__ __launch_bounds__(kBlock) void hermite4_pack_kernel(const Grid g, const PackPlan pp,
+                                                               const float* __restrict__ params,
+                                                               float* __restrict__ packed) {
+  constexpr int RW = 16 * F;
+  constexpr int PITCH = RW + 4;
+  __shared__ float stage[kBlock * PITCH];
+  const int64_t total = pp.poff[g.L] / RW;
+  const int64_t t0 = (int64_t)blockIdx.x * kBlock;
+  const int64_t t = t0 + threadIdx.x;
+  if (t < total) {
+    int l = 0;
+    while (l + 1 < g.L && t * RW >= pp.poff[l + 1]) ++l;
+    const int64_t r = t - pp.poff[l] / RW;
+    auto row_in = [&](int k) -> int64_t {
+      if (g.T[k] == g.T[0]) return r;
+      if (!((g.dense[0] >> l) & 1u)) return r & (int64_t)(g.T[k] - 1);  // both hashed, T_k | T_0
+      if ((g.dense[k] >> l) & 1u) return r;                                // both dense
+      const int64_t N1 = (int64_t)g.N[l] + 1;                              // dense row -> vertex
+      const uint32_t h = (uint32_t)(r % N1) ^ (uint32_t)((r / N1) % N1) * kPrime1 ^
+                         (uint32_t)((r / (N1 * N1)) % N1) * kPrime2 ^ (uint32_t)(r / (N1 * N1 * N1)) * kPrime3;
+      return h & (g.T[k] - 1u);
+    };
+    float v[RW];
+    int o = 0;
+#pragma unroll
+    for (int k = 0; k <= 4; ++k) {
+      const int W = slots4(k) * F;
+      const float* src = params + g.off[k][l] + row_in(k) * W;
+#pragma unroll
+      for (int j = 0; j < slots4(k) * F; ++j) v[o + j] = src[j];
+      o += W;
+    }
+    store_vec<RW>(stage + threadIdx.x * PITCH, v);
+  }
+  __syncthreads();
+  const int nr = (int)(total - t0 < kBlock ? total - t0 : kBlock);
+  constexpr int Q = RW / 4;
+  float4* dst = reinterpret_cast<float4*>(packed + t0 * RW);
+  for (int q = threadIdx.x; q < nr * Q; q += kBlock) {
+    const int row = q / Q, cq = q - row * Q;
+    dst[q] = *reinterpret_cast<const float4*>(stage + row * PITCH + 4 * cq);
+  }
+}
+
+// PACKED: the 16 coefficients of a vertex are read as one row of the packed copy (five order
+// tables side by side, 16 F contiguous floats: one 128-byte line at F = 2) instead of one row
+// of each of the five tables.
+template <int F, bool PACKED>
+__global__ __launch_bounds__(kBlock) void hermite4_forward_kernel(const Grid g, const PackPlan pp, int64_t n,
+                                                                  int32_t n_tiles, int d2_mode,
+                                                                  const float* __restrict__ x,
                                                                   const float* __restrict__ params,
                                                                   float* __restrict__ gamma,
                                                                   float* __restrict__ dgamma,
@@ -1433,13 +1488,26 @@ __global__ __launch_bounds__(kBlock) void hermite4_forward_kernel(const Grid g, 
   for (int c = 0; c < 16; ++c) {
     // the corner's 16 coefficients th[alpha][f]
     float th[16][F];
+    if constexpr (PACKED) {
+      const uint32_t row = row4(keys, c, (g.dense[0] >> l) & 1u, g.T[0], g.Tmask[0]);
+      float v[16 * F];
+      load_vec<16 * F>(params + pp.poff[l] + (size_t)row * (16 * F), v);
+      int o = 0;
 #pragma unroll
-    for (int k = 0; k <= 4; ++k) {
-      const bool dense = (g.dense[k] >> l) & 1u;
-      const uint32_t row = row4(keys, c, dense, g.T[k], g.Tmask[k]);
-      const float* src = params + g.off[k][l] + (size_t)row * (slots4(k) * F);
+      for (int k = 0; k <= 4; ++k)
 #pragma unroll
-      for (int sl = 0; sl < slots4(k); ++sl) load_vec<F>(src + sl * F, th[alpha4_of_slot(k, sl)]);
+        for (int sl = 0; sl < slots4(k); ++sl, o += F)
+#pragma unroll
+          for (int f = 0; f < F; ++f) th[alpha4_of_slot(k, sl)][f] = v[o + f];
+    } else {
+#pragma unroll
+      for (int k = 0; k <= 4; ++k) {
+        const bool dense = (g.dense[k] >> l) & 1u;
+        const uint32_t row = row4(keys, c, dense, g.T[k], g.Tmask[k]);
+        const float* src = params + g.off[k][l] + (size_t)row * (slots4(k) * F);
+#pragma unroll
+        for (int sl = 0; sl < slots4(k); ++sl) load_vec<F>(src + sl * F, th[alpha4_of_slot(k, sl)]);
+      }
     }
     const CornerAxis c0 = corner_axis(t[0], Nf, iN, c & 1), c1 = corner_axis(t[1], Nf, iN, (c >> 1) & 1);
     const CornerAxis c2 = corner_axis(t[2], Nf, iN, (c >> 2) & 1), c3 = corner_axis(t[3], Nf, iN, (c >> 3) & 1);
@@ -1847,12 +1915,29 @@ hipError_t launch_bin4(const Grid& g, const BinPlan& bp, const BinWorkspace& w, 
 }
 
 template <int F>
-hipError_t launch_fwd4(const Grid& g, int d2_mode, int64_t n, const float* x, const float* params, float* gamma,
-                       float* dgamma, float* d2gamma, hipStream_t s) {
+hipError_t launch_fwd4(const Grid& g, int d2_mode, int64_t n, const float* x, const float* params, float* packed,
+                       float* gamma, float* dgamma, float* d2gamma, hipStream_t s) {
   const int64_t tiles = (n + kBlock - 1) / kBlock;
   if (tiles * g.L > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((hermite4_forward_kernel<F>), dim3((unsigned)(tiles * g.L)), dim3(kBlock), 0, s, g, n,
-                     (int32_t)tiles, d2_mode, x, params, gamma, dgamma, d2gamma);
+  const dim3 grid((unsigned)(tiles * g.L));
+  if constexpr (F <= 2) {
+    if (packed) {
+      const PackPlan pp = make_pack_plan(g, 4, F);
+      hipLaunchKernelGGL((hermite4_pack_kernel<F>), dim3((unsigned)((pp.poff[g.L] / (16 * F) + kBlock - 1) / kBlock)),
+                         dim3(kBlock), 0, s, g, pp, params, packed);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((hermite4_forward_kernel<F, true>), grid, dim3(kBlock), 0, s, g, pp, n, (int32_t)tiles,
+                         d2_mode, x, packed, gamma, dgamma, d2gamma);
+    } else {
+      hipLaunchKernelGGL((hermite4_forward_kernel<F, false>), grid, dim3(kBlock), 0, s, g, PackPlan{}, n,
+                         (int32_t)tiles, d2_mode, x, params, gamma, dgamma, d2gamma);
+    }
+  } else {
+    if (packed) return hipErrorInvalidValue;  // F > 2: no packed copy
+    hipLaunchKernelGGL((hermite4_forward_kernel<F, false>), grid, dim3(kBlock), 0, s, g, PackPlan{}, n,
+                       (int32_t)tiles, d2_mode, x, params, gamma, dgamma, d2gamma);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.L == g.Lrow) return e;
   const int RF = g.Lrow * F, AF = g.L * F;
@@ -1946,9 +2031,14 @@ hipError_t launch_debug_indices4(const Grid& g, int order, int64_t n, const floa
   return hipGetLastError();
 }
 
+size_t hermite4_packed_bytes(const Grid& g, int F) {
+  return F <= 2 && hermite_packable(g, 4) ? sizeof(float) * (size_t)make_pack_plan(g, 4, F).poff[g.L] : 0;
+}
+
 hipError_t launch_hermite4_forward(const Grid& g, int F, int d2_mode, int64_t n, const float* x,
-                                   const float* params, float* gamma, float* dgamma, float* d2gamma, hipStream_t s) {
-  HASHENC_DISPATCH_F4(F, launch_fwd4, g, d2_mode, n, x, params, gamma, dgamma, d2gamma, s);
+                                   const float* params, float* packed, float* gamma, float* dgamma, float* d2gamma,
+                                   hipStream_t s) {
+  HASHENC_DISPATCH_F4(F, launch_fwd4, g, d2_mode, n, x, params, packed, gamma, dgamma, d2gamma, s);
 }
 
 hipError_t launch_hermite4_backward(const Grid& g, int F, int d2_mode, int64_t n, const float* x,

@@ -26,6 +26,17 @@ def _forward(spec, x, params):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
+def _forward_ws(spec, x, params):
+    """The workspace forward: the packed copy of the five tables when F <= 2 and the sizes
+    allow it, else the plain forward."""
+    enc = api.HashGridEncoding(spec)
+    out = {k: torch.full(v, float("nan"), device=DEV) for k, v in enc.output_shapes(x.shape[0]).items()}
+    api.hashenc_forward_ws(enc.handle, _dev(x), _dev(params), out["gamma"], out["dgamma"], out["d2gamma"],
+                           enc.workspace(x.shape[0]))
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
 def _backward(spec, x, ups, n_params, ws=False):
     enc = api.HashGridEncoding(spec)
     grad = torch.zeros(n_params, device=DEV)
@@ -43,9 +54,10 @@ def _points(n, seed):
 
 
 def _check(orc, spec, x, params, ups_seed):
-    got = _forward(spec, x, params)
+    got, got_ws = _forward(spec, x, params), _forward_ws(spec, x, params)
     for k, r in zip(("gamma", "dgamma", "d2gamma"), orc.forward(spec, x, params)):
         _blocks_close(got[k], r, spec, FWD_TOL, k)
+        _blocks_close(got_ws[k], r, spec, FWD_TOL, f"{k} (workspace forward)")
     lay = orc.layout(spec)
     rng = np.random.default_rng(ups_seed)
     ups = [rng.standard_normal(s).astype(np.float32) for s in _shapes(spec, x.shape[0])]
@@ -73,7 +85,10 @@ def test_hermite4_parity_workload(orc):
 
 
 @pytest.mark.parametrize("F,T,mode", [(1, [1 << 12] * 5, "laplacian"), (4, [1000, 3001, 777, 5000, 64], "diag"),
-                                      (8, [1 << 10, 1 << 12, 1 << 11, 1 << 12, 1 << 10], "laplacian")])
+                                      (8, [1 << 10, 1 << 12, 1 << 11, 1 << 12, 1 << 10], "laplacian"),
+                                      # packed copy with smaller power-of-two tables: level 1 is dense
+                                      # in tables 0 and 1 and hashed in the others
+                                      (2, [1 << 12, 1 << 12, 1 << 10, 1 << 11, 1 << 9], "diag")])
 def test_hermite4_shapes(orc, F, T, mode):
     spec = {"d": 4, "L": 3, "F": F, "kind": "hermite", "T": T, "n_min": 3, "n_max": 20, "d2_mode": mode}
     lay = orc.layout(spec)
@@ -141,11 +156,13 @@ def test_hermite4_unsupported_paths():
     from multiresolution_hash_grid_multires_amd._lib import HASHENC_EUNSUPPORTED, HashencError
     spec = I.WORKLOADS[NAME]["spec"]
     h = api.hashenc_create(spec)
-    assert api.hashenc_forward_workspace_size(h, 1000) == 0
+    assert api.hashenc_forward_workspace_size(h, 1000) > 0  # the packed copy of the tables
     assert api.hashenc_backward_workspace_size(h, 1000) > 0  # binned
-    # F = 8: rows of 48 floats in the order-2 table, wider than the binned reduce takes
+    # F = 8: rows of 48 floats in the order-2 table, wider than the binned reduce takes; no
+    # packed copy either
     wide = api.hashenc_create(dict(spec, F=8))
     assert api.hashenc_backward_workspace_size(wide, 1000) == 0
+    assert api.hashenc_forward_workspace_size(wide, 1000) == 0
     with pytest.raises(HashencError) as e:
         api.hashenc_residual_workspace_size(h, api.Mlp(16, 32, 2, 30.0), 100)
     assert e.value.code == HASHENC_EUNSUPPORTED

@@ -362,13 +362,13 @@ def test_full_size_forward_sampled(orc, name):
 
 
 @pytest.mark.parametrize("name", ["dlinear3d_L16_T19", "hermite3d_L16_T19", "hermite2d_L8_T14",
-                                  "hermite2d_L8_T14_14_10"])
+                                  "hermite2d_L8_T14_14_10", "hermite4d_L8_T16"])
 def test_full_size_forward_ws_sampled(orc, name):
     """The workspace forward in the launch configuration the benchmark times: every level
     active, all of the workload's points, the workspace shared with the backward (d-linear:
     LDS levels, L2 passes and the level-major transpose; Hermite: packed tables, level-major
-    staging and the rearrangement into rows).  4096 sampled points and the last one against
-    the oracle, per level and component."""
+    staging and the rearrangement into rows; 4D Hermite: the packed copy of the five tables).
+    4096 sampled points and the last one against the oracle, per level and component."""
     W = I.WORKLOADS[name]
     spec = W["spec"]
     lay = orc.layout(spec)
