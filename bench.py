@@ -453,7 +453,7 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     workspace = enc.workspace(n) if args.backward == "binned" else None
     # the backward the library actually runs: the workspace entry point falls back to the
-    # atomic scatter-add when the configuration has no binned plan (RBF, 4D Hermite)
+    # atomic scatter-add when the configuration has no binned plan (RBF; 4D Hermite with F = 8)
     backward_path = ("binned" if workspace is not None and api.hashenc_backward_workspace_size(enc.handle, n) > 0
                      else "atomic")
 
