@@ -138,7 +138,11 @@ HASHENC_API int hashenc_c2f_active_levels(int32_t n_levels, int32_t l0, int64_t 
 HASHENC_API int hashenc_param_layout(const hashenc* h, int32_t order, int32_t level, int64_t* offset,
                          int64_t* rows, int32_t* row_width, int32_t* is_dense);
 
-/* Forward encoding of n points.
+/* Forward encoding of n points: per level the cell around x, the lookup of its corners and
+ * the interpolant, concatenated over levels (Instant-NGP explainer, encoding pipeline steps
+ * 1-4; Hermite kind: Hermite-NGP notes, key design 1 for the value and key design 2 for the
+ * analytic first and second derivatives; RBF kind: DInf-Grid summary, section
+ * 可微的径向基函数插值).
  *   x       [n, d] fp32, row-major
  *   params  [n_params] fp32 in the layout above
  *   gamma   [n, L*F]  level-major then feature (may be NULL)
@@ -155,11 +159,14 @@ HASHENC_API int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size
 
 /* Same outputs as hashenc_forward.  With a workspace the d-linear encoding is computed
  * level by level into a level-major staging buffer [L][n][F] (every store writes whole
- * cache lines) and then rearranged into gamma [n, L*F] in one pass.  A Hermite handle also
- * stages its outputs level-major ([L][n][M][F], M = 1 + d + (d or 1)) and, when its order
- * tables all have the same size, first packs the tables into the workspace (one contiguous
- * row of every order table per vertex) and reads the corners from that copy.  An RBF handle
- * needs no workspace (size 0) and runs as hashenc_forward.
+ * cache lines) and then rearranged into gamma [n, L*F] in one pass.  A Hermite handle with
+ * d = 2 or 3 also stages its outputs level-major ([L][n][M][F], M = 1 + d + (d or 1)) and,
+ * when every order table has the order-0 table's size or is a power of two no larger than it,
+ * first packs the tables into the workspace (one contiguous row of every order table per
+ * vertex) and reads the corners from that copy.  A d = 4 Hermite handle with F <= 2 and such
+ * table sizes packs its five tables the same way (16 F floats per vertex) and writes its
+ * outputs directly; with F > 2 it needs no workspace.  An RBF handle needs no workspace (size
+ * 0) and runs as hashenc_forward.
  * workspace: >= hashenc_forward_workspace_size bytes, 256-byte aligned; calls sharing it
  * must not overlap.  Results are bit-identical to hashenc_forward. */
 HASHENC_API int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float* params,
@@ -167,7 +174,9 @@ HASHENC_API int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, 
                                    size_t workspace_bytes, hashenc_stream_t stream);
 
 /* Backward: grad_params += d<G, forward(theta)>/d theta for the upstream gradients G
- * (shapes as the forward outputs; NULL = zero).  Contributions of colliding vertices sum.
+ * (shapes as the forward outputs; NULL = zero): the transpose of the forward's interpolation
+ * (same passages as hashenc_forward).  Contributions of colliding vertices sum (Instant-NGP
+ * news article, adaptivity paragraph: gradients of colliding points combine).
  * Accumulated with fp32 atomics: the summation order, and so the last bits, vary from
  * run to run.  The caller zeroes grad_params when it wants a fresh gradient. */
 HASHENC_API int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
