@@ -287,7 +287,9 @@ def fd_mlp_flops_per_point(d: int, n_in: int, hidden: int, depth: int) -> int:
 def residual_bench(args, torch, api, I, W) -> int:
     """One fused residual step (hashenc_residual, Hermite) or one finite-difference comparator
     step (hashenc_fd_residual, d-linear, when the workload names an FD step)."""
-    spec, m = W["spec"], W["mlp"]
+    spec, m = W["spec"], dict(W["mlp"])
+    if args.mlp_depth:
+        m["depth"] = args.mlp_depth  # the pages' depth ablation (same width and omega)
     fd = "fd_eps" in W
     n = W["n_points"]
     dev = torch.device("cuda:0")
@@ -390,6 +392,8 @@ def main() -> int:
     ap.add_argument("--active-levels", type=int, default=0,
                     help="coarse-to-fine activation: compute only the first A levels (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mlp-depth", type=int, default=0,
+                    help="residual workloads: SIREN hidden layers instead of the workload's own (1..4)")
     ap.add_argument("--n-points", type=int, default=0,
                     help="points per step instead of the workload's own count (the first N of its points)")
     ap.add_argument("--copy-bytes", type=int, default=0,

@@ -264,13 +264,14 @@ HASHENC_API int hashenc_residual(const hashenc* h, const hashenc_mlp* mlp, int64
  *   loss = mean r^2, with g as for hashenc_residual; the reverse sweep runs through all
  *   2d+1 stencil points' networks and encodings.  The output bias cancels in the stencil:
  *   its gradient is zero.
- *   mlp          depth 1 or 2 (matrix-core kernel), hidden <= 64, in == L*F <= 64
+ *   mlp          depth 1..4 (1 and 2 on the matrix cores, 3 and 4 on the vector ALUs),
+ *                hidden <= 64, in == L*F <= 64
  *   eps          FD step (> 0, finite)
  *   u_stencil    [n, 2d+1] u at the stencil points (may be NULL)
  *   residual     [n] r (may be NULL);  loss [1] (overwritten)
  *   grad_params  += dloss/dtheta;  grad_mlp += dloss/dmlp_params (either may be NULL)
  *   workspace    >= hashenc_fd_residual_workspace_size bytes, 256-byte aligned
- * HASHENC_EUNSUPPORTED for a Hermite handle or depth > 2.  n must be >= 1. */
+ * HASHENC_EUNSUPPORTED for a Hermite handle or depth > 4.  n must be >= 1. */
 HASHENC_API int hashenc_fd_residual_workspace_size(const hashenc* h, const hashenc_mlp* mlp, int64_t n,
                                                    size_t* bytes);
 HASHENC_API int hashenc_fd_residual(const hashenc* h, const hashenc_mlp* mlp, float eps, int64_t n,

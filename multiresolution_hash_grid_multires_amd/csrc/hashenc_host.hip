@@ -488,8 +488,8 @@ static int check_fd(const hashenc* h, const hashenc_mlp* mlp, const char* who) {
   if (mlp->in > 64) return fail(HASHENC_EUNSUPPORTED, "%s: mlp.in must be <= 64", who);
   if (mlp->hidden < 1 || mlp->hidden > 64)
     return fail(HASHENC_EUNSUPPORTED, "%s: hidden width must be in 1..64 (got %d)", who, mlp->hidden);
-  if (mlp->depth < 1 || mlp->depth > 2)
-    return fail(HASHENC_EUNSUPPORTED, "%s: depth must be 1 or 2 (got %d)", who, mlp->depth);
+  if (mlp->depth < 1 || mlp->depth > 4)
+    return fail(HASHENC_EUNSUPPORTED, "%s: depth must be in 1..4 (got %d)", who, mlp->depth);
   if (mlp->out != 1) return fail(HASHENC_EUNSUPPORTED, "%s: output width must be 1", who);
   if (mlp->reserved != 0) return fail(HASHENC_EINVAL, "%s: mlp.reserved must be 0", who);
   if (!std::isfinite(mlp->omega)) return fail(HASHENC_EINVAL, "%s: omega must be finite", who);

@@ -1225,20 +1225,301 @@ hipError_t dispatch_siren(int d, int depth, int in, const MlpArgs& a, int64_t n,
   return dispatch_depth<3>(depth, in, a, n, inv_n, x, enc, mlp, up, residual, partial, rows, s);
 }
 
+// INGP-FD comparator for SIREN depth 3 and 4 on the vector ALUs (the matrix-core kernel
+// above holds the tape of at most two layers).  The layout of the fused residual's vector
+// kernel: a wavefront takes kPB points at a time, lane = neuron, and the columns are the
+// (point, stencil copy) pairs, each a plain value row: z = W v + b, a = sin(omega z) on
+// every column, u_s = wout . a_s, Lap u by the second differences of the copies, and the
+// reverse seeds ubar_s = (2 r / n) c_s / eps^2 (c_0 = -2d, else 1), zbar = abar omega
+// cos(omega z).
+// Wavefronts per workgroup: the most (4, 2 or 1) whose activation rows fit the CU's 160 KB
+// beside the weights.
+__host__ __device__ constexpr int fd_vec_waves(int d, int depth, int inp) {
+  const int rb = kPB * (2 * d + 1);
+  const int fixed_bytes = 4 * (depth * kW * (kW + 1) + depth * kW + kW);
+  const int wave_bytes = 4 * rb * (inp + (depth - 1) * kW + kW);
+  return fixed_bytes + 4 * wave_bytes <= 160 * 1024 ? 4 : fixed_bytes + 2 * wave_bytes <= 160 * 1024 ? 2 : 1;
+}
+
+template <int D, int DEPTH, int INP>
+struct FdVecLds {
+  static constexpr int R = 2 * D + 1;
+  static constexpr int RB = kPB * R;  // columns: kPB points x R stencil copies
+  static constexpr int WV = fd_vec_waves(D, DEPTH, INP);
+  float W[DEPTH][kW][kW + 1];  // W[k][o][j] = W_k[o][j]
+  float bias[DEPTH][kW];
+  float wout[kW];
+  __attribute__((aligned(16))) float act0[WV][INP][RB];
+  __attribute__((aligned(16))) float act[WV][DEPTH - 1][kW][RB];
+  __attribute__((aligned(16))) float zb[WV][kW][RB];
+};
+
+template <int D, int DEPTH, int INP>
+__global__ __launch_bounds__(kW * fd_vec_waves(D, DEPTH, INP)) void siren_fd_vec_kernel(
+    const MlpArgs a, int64_t n, double inv_n_total, float inv_eps2, const float* __restrict__ x,
+    const float* __restrict__ enc, const float* __restrict__ mlp, float* __restrict__ up,
+    float* __restrict__ u_stencil, float* __restrict__ residual, float* __restrict__ partial) {
+  using Sh = FdVecLds<D, DEPTH, INP>;
+  constexpr int R = Sh::R;
+  constexpr int RB = Sh::RB;
+  constexpr int WV = Sh::WV;
+  static_assert(DEPTH >= 2, "depth 1 and 2 run on the matrix cores");
+  static_assert(RB % 4 == 0, "activation rows move as 16-byte pieces");
+  static_assert(sizeof(Sh) <= 160 * 1024, "FD workgroup LDS exceeds the CU's 160 KB");
+  __shared__ Sh sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kW - 1);
+  const int wv = tid / kW;
+  const float w = a.omega;
+  for (int k = 0; k < DEPTH; ++k) {
+    const int fi = k == 0 ? a.in : a.H;
+    const float* Wk = mlp + a.woff[k];
+    for (int e = tid; e < kW * kW; e += kW * WV) {
+      const int o = e / kW, j = e % kW;
+      sh.W[k][o][j] = (o < a.H && j < fi) ? Wk[o * fi + j] : 0.0f;
+    }
+    for (int o = tid; o < kW; o += kW * WV) sh.bias[k][o] = o < a.H ? mlp[a.boff[k] + o] : 0.0f;
+  }
+  for (int o = tid; o < kW; o += kW * WV) sh.wout[o] = o < a.H ? mlp[a.woff[DEPTH] + o] : 0.0f;
+  const float bo = mlp[a.boff[DEPTH]];
+  __syncthreads();
+
+  float gW0[INP];
+  float gW[DEPTH - 1][kW];
+  float gb[DEPTH];
+  float gWo = 0.0f, sq = 0.0f;
+#pragma unroll
+  for (int j = 0; j < INP; ++j) gW0[j] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k) gb[k] = 0.0f;
+#pragma unroll
+  for (int k = 0; k + 1 < DEPTH; ++k)
+#pragma unroll
+    for (int j = 0; j < kW; ++j) gW[k][j] = 0.0f;
+
+  auto in_row = [&](int k, int j) -> float* { return k == 0 ? sh.act0[wv][j] : sh.act[wv][k - 1][j]; };
+
+  const int64_t wave_id = (int64_t)blockIdx.x * WV + wv;
+  const int64_t n_waves = (int64_t)gridDim.x * WV;
+  for (int64_t p0 = wave_id * kPB; p0 < n; p0 += n_waves * kPB) {
+    // encoder rows of the points' stencil copies (lm_index layout, R = 2d + 1)
+    if (lane < INP) {
+      float row[RB];
+#pragma unroll
+      for (int b = 0; b < kPB; ++b) {
+        const int64_t p = p0 + b;
+        const bool on = lane < a.ain && p < n;
+#pragma unroll
+        for (int r = 0; r < R; ++r) row[b * R + r] = on ? enc[lm_index(a, n, p, lane, r, R)] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < RB; q += 4)
+        *reinterpret_cast<float4*>(&sh.act0[wv][lane][q]) = make_float4(row[q], row[q + 1], row[q + 2], row[q + 3]);
+    }
+    wave_lds_sync();
+
+    // forward: every column a value row; the tape keeps omega cos(omega z)
+    float tc[DEPTH][RB];
+    float atop[RB];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) {
+      const int fi = k == 0 ? INP : kW;
+      float z[RB];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) z[q] = sh.bias[k][lane];
+#pragma unroll 4
+      for (int j = 0; j < fi; ++j) {
+        const float wj = sh.W[k][lane][j];
+        const float* v = in_row(k, j);
+#pragma unroll
+        for (int q = 0; q < RB; q += 4) {
+          const float4 a4 = *reinterpret_cast<const float4*>(v + q);
+          z[q] = fmaf(wj, a4.x, z[q]);
+          z[q + 1] = fmaf(wj, a4.y, z[q + 1]);
+          z[q + 2] = fmaf(wj, a4.z, z[q + 2]);
+          z[q + 3] = fmaf(wj, a4.w, z[q + 3]);
+        }
+      }
+      float out[RB];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        float sv, cv;
+        sincos_red(w * z[q], sv, cv);
+        out[q] = sv;
+        tc[k][q] = w * cv;
+      }
+      if (k + 1 < DEPTH) {
+#pragma unroll
+        for (int q = 0; q < RB; q += 4)
+          *reinterpret_cast<float4*>(&sh.act[wv][k][lane][q]) = make_float4(out[q], out[q + 1], out[q + 2], out[q + 3]);
+        wave_lds_sync();
+      } else {
+#pragma unroll
+        for (int q = 0; q < RB; ++q) atop[q] = out[q];
+      }
+    }
+    // u_s = wout . a_s per column (the output bias cancels in every second difference),
+    // the residual and the seeds
+    float ab[RB];
+#pragma unroll
+    for (int b = 0; b < kPB; ++b) {
+      const int64_t p = p0 + b;
+      float u[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) u[r] = wave_sum(sh.wout[lane] * atop[b * R + r]);
+      float seed = 0.0f;
+      if (p < n) {
+        float lap = 0.0f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) lap += ((u[2 * i + 1] - u[0]) + (u[2 * i + 2] - u[0])) * inv_eps2;
+        float src = -(float)D * 9.8696044010893586f;  // -d pi^2
+#pragma unroll
+        for (int i = 0; i < D; ++i) src *= sinpif(x[p * D + i]);
+        const float res = lap - src;
+        if (lane == 0) {
+          sq = fmaf(res, res, sq);
+          if (residual) residual[p] = res;
+          if (u_stencil)
+#pragma unroll
+            for (int r = 0; r < R; ++r) u_stencil[p * R + r] = u[r] + bo;
+        }
+        seed = (float)(2.0 * (double)res * inv_n_total) * inv_eps2;
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float ubar = r == 0 ? -2.0f * (float)D * seed : seed;
+        gWo = fmaf(ubar, atop[b * R + r], gWo);
+        ab[b * R + r] = ubar * sh.wout[lane];
+      }
+    }
+    // reverse sweep
+#pragma unroll
+    for (int k = DEPTH - 1; k >= 0; --k) {
+      float zbar[RB];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        zbar[q] = ab[q] * tc[k][q];
+        gb[k] += zbar[q];
+      }
+      if (k == 0) {
+#pragma unroll
+        for (int j = 0; j < INP; ++j) {
+          const float* v = sh.act0[wv][j];
+          float acc = gW0[j];
+#pragma unroll
+          for (int q = 0; q < RB; q += 4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(v + q);
+            acc = fmaf(zbar[q], a4.x, acc);
+            acc = fmaf(zbar[q + 1], a4.y, acc);
+            acc = fmaf(zbar[q + 2], a4.z, acc);
+            acc = fmaf(zbar[q + 3], a4.w, acc);
+          }
+          gW0[j] = acc;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kW; ++j) {
+          const float* v = sh.act[wv][k - 1][j];
+          float acc = gW[k - 1][j];
+#pragma unroll
+          for (int q = 0; q < RB; q += 4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(v + q);
+            acc = fmaf(zbar[q], a4.x, acc);
+            acc = fmaf(zbar[q + 1], a4.y, acc);
+            acc = fmaf(zbar[q + 2], a4.z, acc);
+            acc = fmaf(zbar[q + 3], a4.w, acc);
+          }
+          gW[k - 1][j] = acc;
+        }
+      }
+      // input adjoint: lane j <- sum_o W_k[o][j] zbar_o
+#pragma unroll
+      for (int q = 0; q < RB; q += 4)
+        *reinterpret_cast<float4*>(&sh.zb[wv][lane][q]) = make_float4(zbar[q], zbar[q + 1], zbar[q + 2], zbar[q + 3]);
+      wave_lds_sync();
+#pragma unroll
+      for (int q = 0; q < RB; ++q) ab[q] = 0.0f;
+#pragma unroll 4
+      for (int o = 0; o < kW; ++o) {
+        const float wo = sh.W[k][o][lane];
+        const float* zr = sh.zb[wv][o];
+#pragma unroll
+        for (int q = 0; q < RB; q += 4) {
+          const float4 z4 = *reinterpret_cast<const float4*>(zr + q);
+          ab[q] = fmaf(wo, z4.x, ab[q]);
+          ab[q + 1] = fmaf(wo, z4.y, ab[q + 1]);
+          ab[q + 2] = fmaf(wo, z4.z, ab[q + 2]);
+          ab[q + 3] = fmaf(wo, z4.w, ab[q + 3]);
+        }
+      }
+      wave_lds_sync();  // zb is rewritten by the next layer
+    }
+    // encoder upstream, stencil-major ([L][R][n][F]), for the inputs this lane owns
+    if (lane < a.ain) {
+#pragma unroll
+      for (int b = 0; b < kPB; ++b) {
+        const int64_t p = p0 + b;
+        if (p >= n) break;
+#pragma unroll
+        for (int r = 0; r < R; ++r) up[fd_index(a, n, p, lane, r, R)] = ab[b * R + r];
+      }
+    }
+  }
+
+  // this wave's partial MLP gradient and sum of r^2
+  float* part = partial + wave_id * (a.n_mlp + 1);
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k) {
+    const int fi = k == 0 ? a.in : a.H;
+    if (lane < a.H) {
+      if (k == 0) {
+#pragma unroll
+        for (int j = 0; j < INP; ++j)
+          if (j < fi) part[a.woff[0] + (int64_t)lane * fi + j] = gW0[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kW; ++j)
+          if (j < fi) part[a.woff[k] + (int64_t)lane * fi + j] = gW[k - 1][j];
+      }
+      part[a.boff[k] + lane] = gb[k];
+    }
+  }
+  if (lane < a.H) part[a.woff[DEPTH] + lane] = gWo;
+  if (lane == 0) {
+    part[a.boff[DEPTH]] = 0.0f;  // the output bias cancels in the stencil
+    part[a.n_mlp] = sq;
+  }
+}
+
 constexpr int kFdBlocks = 256;  // one workgroup per CU (LDS-limited)
+
+// Partial rows of the FD network kernels: one per row group (matrix cores) or per wavefront
+// (vector ALUs, depth 3 and 4).
+constexpr int kFdPartialRows = kSirenBlocks * kMaxWavesPerBlock;
 
 template <int D, int DEPTH, int NI>
 hipError_t launch_fd_siren(const MlpArgs& a, int64_t n, double inv_n, float inv_eps2, const float* x,
                            const float* enc, const float* mlp, float* up, float* u_stencil, float* residual,
                            float* partial, int& rows, hipStream_t s) {
-  // the kernel addresses the encoder output with 32-bit byte offsets
-  if ((uint64_t)n * (2 * D + 1) * a.in * sizeof(float) >= (uint64_t(1) << 32)) return hipErrorInvalidValue;
-  int blocks = (int)((n + kMP - 1) / kMP);
-  if (blocks > kFdBlocks) blocks = kFdBlocks;
-  rows = blocks * kFdGroups;  // one partial row per row group
-  hipLaunchKernelGGL((siren_fd_mfma_kernel<D, DEPTH, NI>), dim3(blocks), dim3(kW * kFdWaves), 0, s, a, n, inv_n,
-                     inv_eps2, x, enc, mlp, up, u_stencil, residual, partial);
-  return hipGetLastError();
+  if constexpr (DEPTH > 2) {
+    constexpr int wpb = FdVecLds<D, DEPTH, NI>::WV;
+    int blocks = (int)((n + wpb * kPB - 1) / (wpb * kPB));
+    if (blocks > kSirenBlocks) blocks = kSirenBlocks;
+    rows = blocks * wpb;
+    hipLaunchKernelGGL((siren_fd_vec_kernel<D, DEPTH, NI>), dim3(blocks), dim3(kW * wpb), 0, s, a, n, inv_n, inv_eps2,
+                       x, enc, mlp, up, u_stencil, residual, partial);
+    return hipGetLastError();
+  } else {
+    // the kernel addresses the encoder output with 32-bit byte offsets
+    if ((uint64_t)n * (2 * D + 1) * a.in * sizeof(float) >= (uint64_t(1) << 32)) return hipErrorInvalidValue;
+    int blocks = (int)((n + kMP - 1) / kMP);
+    if (blocks > kFdBlocks) blocks = kFdBlocks;
+    rows = blocks * kFdGroups;  // one partial row per row group
+    hipLaunchKernelGGL((siren_fd_mfma_kernel<D, DEPTH, NI>), dim3(blocks), dim3(kW * kFdWaves), 0, s, a, n, inv_n,
+                       inv_eps2, x, enc, mlp, up, u_stencil, residual, partial);
+    return hipGetLastError();
+  }
 }
 
 template <int D, int DEPTH>
@@ -1255,11 +1536,17 @@ hipError_t fd_dispatch_in(int in, const MlpArgs& a, int64_t n, double inv_n, flo
 hipError_t fd_dispatch(int d, int depth, int in, const MlpArgs& a, int64_t n, double inv_n, float inv_eps2,
                        const float* x, const float* enc, const float* mlp, float* up, float* u_stencil,
                        float* residual, float* partial, int& rows, hipStream_t s) {
-  if (d == 2)
-    return depth == 1 ? fd_dispatch_in<2, 1>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s)
-                      : fd_dispatch_in<2, 2>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s);
-  return depth == 1 ? fd_dispatch_in<3, 1>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s)
-                    : fd_dispatch_in<3, 2>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s);
+#define HASHENC_FD_DEPTHS(DD)                                                                                  \
+  switch (depth) {                                                                                             \
+    case 1: return fd_dispatch_in<DD, 1>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s); \
+    case 2: return fd_dispatch_in<DD, 2>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s); \
+    case 3: return fd_dispatch_in<DD, 3>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s); \
+    case 4: return fd_dispatch_in<DD, 4>(in, a, n, inv_n, inv_eps2, x, enc, mlp, up, u_stencil, residual, partial, rows, s); \
+  }                                                                                                            \
+  return hipErrorInvalidValue
+  if (d == 2) { HASHENC_FD_DEPTHS(2); }
+  HASHENC_FD_DEPTHS(3);
+#undef HASHENC_FD_DEPTHS
 }
 
 // Centre points per FD chunk: the chunk's 2d+1 stencil sets fit one binned-backward chunk,
@@ -1283,8 +1570,8 @@ FdWorkspaceLayout fd_workspace_layout(const Grid& g, int d, int F, int64_t n, in
   w.xs = take(sizeof(float) * (size_t)cs * d);
   w.enc = take(dlinear_forward_workspace_bytes(g, d, F, cs));  // level-major [L][c (2d+1)][F]
   w.up = take(dlinear_forward_workspace_bytes(g, d, F, cs));
-  w.partial = take(sizeof(float) * (size_t)kFdBlocks * kFdGroups * (n_mlp + 1));
-  w.slices = take(sizeof(double) * (size_t)((kFdBlocks * kFdGroups + kSliceRows - 1) / kSliceRows) * (n_mlp + 1));
+  w.partial = take(sizeof(float) * (size_t)kFdPartialRows * (n_mlp + 1));
+  w.slices = take(sizeof(double) * (size_t)((kFdPartialRows + kSliceRows - 1) / kSliceRows) * (n_mlp + 1));
   w.bins = take(binned ? binned_backward_workspace_bytes(g, d, F, false, cs) : 0);
   w.total = off;
   return w;

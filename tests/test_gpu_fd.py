@@ -85,21 +85,38 @@ def _compare(orc, spec, hidden, depth, omega, eps, x, params, mlp_params):
     assert abs(got["loss"] - float(np.mean(got["r"].astype(np.float64) ** 2))) <= 1e-5 * got["loss"]
     assert abs(got["loss"] - ref["loss"]) <= (1e-5 + 2 * rel_r) * ref["loss"]
     gtol = 1e-4 + 2 * rel_r + _kappa(ref, x, d, eps, mlp_params[-1]) * 2.0 ** -17
+    # Deeper networks: the second differences over the stencil copies act on every hidden
+    # layer's activations, whose own cancellation can exceed the output's (kappa above).  The
+    # oracle's fp32 evaluation of the same arithmetic measures that floor per block; the GPU
+    # is held to three times it where it exceeds gtol.
+    ref32 = orc.fd_residual(spec, hidden, depth, omega, eps, x, params, mlp_params, precision="f32") \
+        if depth > 2 else None
     for name, off, size in _mlp_blocks(spec["L"] * spec["F"], hidden, depth):
         if name == f"b{depth}":
             assert got["grad_mlp"][off] == 0.0  # the output bias cancels in the stencil
             continue
-        _close(got["grad_mlp"][off:off + size], ref["grad_mlp"][off:off + size], gtol, f"grad {name}")
+        tol = gtol
+        if ref32 is not None:
+            b64, b32 = ref["grad_mlp"][off:off + size], ref32["grad_mlp"][off:off + size]
+            tol = max(tol, 3.0 * float(np.max(np.abs(b32 - b64))) / max(float(np.max(np.abs(b64))), 1e-30))
+        _close(got["grad_mlp"][off:off + size], ref["grad_mlp"][off:off + size], tol, f"grad {name}")
     lay = orc.layout(spec)
     nt, L = lay["offset"].shape
     for k in range(nt):
         for l in range(L):
             o, m = lay["offset"][k, l], lay["rows"][k, l] * lay["width"][k, l]
-            _close(got["grad_params"][o:o + m], ref["grad_params"][o:o + m], gtol, f"grad level {l}")
+            tol = gtol
+            if ref32 is not None:
+                b64, b32 = ref["grad_params"][o:o + m], ref32["grad_params"][o:o + m]
+                tol = max(tol, 3.0 * float(np.max(np.abs(b32 - b64))) / max(float(np.max(np.abs(b64))), 1e-30))
+            _close(got["grad_params"][o:o + m], ref["grad_params"][o:o + m], tol, f"grad level {l}")
     return got, ref
 
 
-@pytest.mark.parametrize("d,depth,hidden,omega,L", [(3, 2, 64, 3.0, 4), (3, 1, 32, 5.0, 8), (2, 2, 16, 2.0, 4)])
+@pytest.mark.parametrize("d,depth,hidden,omega,L", [(3, 2, 64, 3.0, 4), (3, 1, 32, 5.0, 8), (2, 2, 16, 2.0, 4),
+                                                    # depth 3 and 4: the vector-ALU network kernel, as in
+                                                    # the pages' depth ablation (depth 2 against 4)
+                                                    (3, 3, 64, 3.0, 4), (3, 4, 32, 3.0, 8), (2, 4, 64, 2.0, 4)])
 def test_fd_parity_shapes(orc, d, depth, hidden, omega, L):
     spec = {"d": d, "L": L, "F": 2, "kind": "dlinear", "T": [1 << 12], "n_min": 4, "n_max": 60 if d == 3 else 150}
     lay = orc.layout(spec)
@@ -194,7 +211,7 @@ def test_fd_argument_errors():
     mp = torch.zeros(api.mlp_param_count(4, 16, 2), device=DEV)
     wsz = api.hashenc_fd_residual_workspace_size(enc.handle, ok, 64)
     ws = torch.empty(wsz, dtype=torch.uint8, device=DEV)
-    for mlp, eps, code in [(api.Mlp(4, 16, 3, 30.0), 0.01, HASHENC_EUNSUPPORTED),
+    for mlp, eps, code in [(api.Mlp(4, 16, 5, 30.0), 0.01, HASHENC_EUNSUPPORTED),
                            (api.Mlp(6, 16, 2, 30.0), 0.01, HASHENC_EINVAL),
                            (ok, 0.0, HASHENC_EINVAL), (ok, float("inf"), HASHENC_EINVAL)]:
         mpm = torch.zeros(api.mlp_param_count(mlp.n_in, mlp.hidden, mlp.depth), device=DEV)
