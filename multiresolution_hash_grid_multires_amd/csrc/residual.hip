@@ -411,9 +411,9 @@ constexpr int kMfmaBlocks = 512;  // two resident workgroups per CU, all in one 
 template <int D, int DEPTH, int NI>
 struct MfmaLds {
   float w0[kW][NI + 4];                               // W_0 (padded rows)
-  float w1[DEPTH > 1 ? kW : 1][kW + 4];               // W_1
+  float w1[DEPTH > 1 ? DEPTH - 1 : 1][kW][kW + 4];    // W_1 .. W_{DEPTH-1}
   float act0[NI][kMPitch];                            // V_0: encoder rows
-  float act1[DEPTH > 1 ? kW : 1][kMPitch];            // V_1: layer-0 activations
+  float act1[DEPTH > 1 ? DEPTH - 1 : 1][kW][kMPitch]; // V_1 ..: the hidden layers' inputs
   float zb[kW][kMPitch];                              // Zbar of the layer in reverse
   float lapw[kMWaves][kMP];                           // per-wave partial Laplacians
 };
@@ -423,11 +423,11 @@ __device__ __forceinline__ mf4 mfma16(float a, float b, mf4 c) {
 }
 
 template <int D, int DEPTH, int NI>
-__global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
+__global__ __launch_bounds__(kW * kMWaves, (DEPTH <= 2 ? 2 : 1)) void siren_mfma_kernel(
     const MlpArgs a, int64_t n, double inv_n_total, const float* __restrict__ x,
     const float* __restrict__ enc, const float* __restrict__ mlp, float* __restrict__ up,
     float* __restrict__ residual, float* __restrict__ partial) {
-  static_assert(DEPTH == 1 || DEPTH == 2, "matrix-core SIREN covers one or two hidden layers");
+  static_assert(DEPTH >= 1 && DEPTH <= 4, "matrix-core SIREN covers one to four hidden layers");
   constexpr int R = D + 2;
   constexpr int NC = kMP * R;  // columns
   __shared__ MfmaLds<D, DEPTH, NI> sh;
@@ -442,12 +442,12 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
     const int o = e / NI, j = e % NI;
     sh.w0[o][j] = (o < H && j < a.in) ? mlp[a.woff[0] + o * a.in + j] : 0.0f;
   }
-  if constexpr (DEPTH > 1) {
+#pragma unroll
+  for (int k = 1; k < DEPTH; ++k)
     for (int e = threadIdx.x; e < kW * kW; e += kW * kMWaves) {
       const int o = e / kW, j = e % kW;
-      sh.w1[o][j] = (o < H && j < H) ? mlp[a.woff[1] + o * H + j] : 0.0f;
+      sh.w1[k - 1][o][j] = (o < H && j < H) ? mlp[a.woff[k] + o * H + j] : 0.0f;
     }
-  }
   // per-lane neurons in D layout: o = 16w + 4lq + i
   float bias[DEPTH][4], wout[4];
 #pragma unroll
@@ -458,11 +458,13 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
     wout[i] = o < H ? mlp[a.woff[DEPTH] + o] : 0.0f;
   }
   mf4 gW0[NI / 16];
-  mf4 gW1[DEPTH > 1 ? 4 : 1];
+  mf4 gW1[DEPTH > 1 ? DEPTH - 1 : 1][4];
 #pragma unroll
   for (int t = 0; t < NI / 16; ++t) gW0[t] = mf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int t = 0; t < (DEPTH > 1 ? 4 : 1); ++t) gW1[t] = mf4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < (DEPTH > 1 ? DEPTH - 1 : 1); ++k)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) gW1[k][t] = mf4{0.f, 0.f, 0.f, 0.f};
   float gb[DEPTH][4], gWo[4], sq = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -537,9 +539,9 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
       } else {
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-          const float aw = sh.w1[16 * w + lm][4 * kk + lq];
+          const float aw = sh.w1[k - 1][16 * w + lm][4 * kk + lq];
 #pragma unroll
-          for (int r = 0; r < R; ++r) acc[r] = mfma16(aw, sh.act1[4 * kk + lq][r * kMP + lm], acc[r]);
+          for (int r = 0; r < R; ++r) acc[r] = mfma16(aw, sh.act1[k - 1][4 * kk + lq][r * kMP + lm], acc[r]);
         }
       }
 #pragma unroll
@@ -559,10 +561,10 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
         const float a_lap = fmaf(-om * om * s, sumsq, wc * acc[R - 1][i]);
         if (k + 1 < DEPTH) {
           const int o = 16 * w + 4 * lq + i;
-          sh.act1[o][lm] = s;
+          sh.act1[k][o][lm] = s;
 #pragma unroll
-          for (int r = 1; r <= D; ++r) sh.act1[o][r * kMP + lm] = wc * acc[r][i];
-          sh.act1[o][(R - 1) * kMP + lm] = a_lap;
+          for (int r = 1; r <= D; ++r) sh.act1[k][o][r * kMP + lm] = wc * acc[r][i];
+          sh.act1[k][o][(R - 1) * kMP + lm] = a_lap;
         } else {
           alap[i] = a_lap;
         }
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
           for (int t = 0; t < NI / 16; ++t) gW0[t] = mfma16(az, sh.act0[16 * t + lm][4 * kk + lq], gW0[t]);
         } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) gW1[t] = mfma16(az, sh.act1[16 * t + lm][4 * kk + lq], gW1[t]);
+          for (int t = 0; t < 4; ++t) gW1[k - 1][t] = mfma16(az, sh.act1[k - 1][16 * t + lm][4 * kk + lq], gW1[k - 1][t]);
         }
       }
       // input adjoint for the wavefront's tile of input neurons j = 16w + .
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
       if (16 * w < fi) {
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-          const float aw = k == 0 ? sh.w0[4 * kk + lq][16 * w + lm] : sh.w1[4 * kk + lq][16 * w + lm];
+          const float aw = k == 0 ? sh.w0[4 * kk + lq][16 * w + lm] : sh.w1[k - 1][4 * kk + lq][16 * w + lm];
 #pragma unroll
           for (int r = 0; r < R; ++r) vbar[r] = mfma16(aw, sh.zb[4 * kk + lq][r * kMP + lm], vbar[r]);
         }
@@ -691,13 +693,13 @@ __global__ __launch_bounds__(kW * kMWaves, 2) void siren_mfma_kernel(
         const int j = 16 * t + lm;
         if (j < a.in) part[a.woff[0] + (int64_t)o * a.in + j] = gW0[t][i];
       }
-      if constexpr (DEPTH > 1) {
+#pragma unroll
+      for (int k = 1; k < DEPTH; ++k)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int j = 16 * t + lm;
-          if (j < H) part[a.woff[1] + (int64_t)o * H + j] = gW1[t][i];
+          if (j < H) part[a.woff[k] + (int64_t)o * H + j] = gW1[k - 1][t][i];
         }
-      }
     }
   }
   // bias and output-weight gradients: sum over the 16 points (lanes lm) of each lane group
@@ -1177,12 +1179,15 @@ WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t
 template <int D, int DEPTH, int INP>
 hipError_t launch_siren(const MlpArgs& a, int64_t n, double inv_n, const float* x, const float* enc,
                         const float* mlp, float* up, float* residual, float* partial, int& rows, hipStream_t s) {
-  if constexpr (DEPTH <= 2) {
-    // matrix cores: one partial row per workgroup; the kernel addresses the encoder output
-    // with 32-bit byte offsets
+  // matrix cores whenever the layers' weights and inputs fit one workgroup's LDS (all but
+  // depth 4 with a 64-wide encoder); deeper networks hold one workgroup per CU
+  if constexpr (DEPTH <= 2 || sizeof(MfmaLds<D, DEPTH, INP>) <= 160 * 1024) {
+    // one partial row per workgroup; the kernel addresses the encoder output with 32-bit
+    // byte offsets
     if ((uint64_t)n * (D + 2) * a.in * sizeof(float) >= (uint64_t(1) << 32)) return hipErrorInvalidValue;
     int blocks = (int)((n + kMP - 1) / kMP);
-    if (blocks > kMfmaBlocks) blocks = kMfmaBlocks;
+    const int max_blocks = DEPTH <= 2 ? kMfmaBlocks : kSirenBlocks;
+    if (blocks > max_blocks) blocks = max_blocks;
     rows = blocks;
     hipLaunchKernelGGL((siren_mfma_kernel<D, DEPTH, INP>), dim3(blocks), dim3(kW * kMWaves), 0, s, a, n, inv_n, x,
                        enc, mlp, up, residual, partial);

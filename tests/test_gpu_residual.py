@@ -77,7 +77,22 @@ def test_residual_parity_pinn_workload(orc):
     _compare(orc, spec, m["hidden"], m["depth"], m["omega"], x, params, mlp_params)
 
 
-@pytest.mark.parametrize("d,depth,hidden,omega", [(3, 1, 16, 3.0), (2, 2, 32, 30.0), (3, 3, 64, 10.0)])
+@pytest.mark.parametrize("depth", [3, 4])
+def test_residual_parity_pinn_deeper(orc, depth):
+    """The PINN workload's encoder and network width at depth 3 and 4 (the pages' depth
+    ablation): 3 072 of its points, uniform and clustered, on the matrix-core kernel."""
+    W = I.WORKLOADS[NAME]
+    spec, m = W["spec"], W["mlp"]
+    lay = orc.layout(spec)
+    params = I.tables(W["id"], lay["n_params"], W["tables"])
+    mlp_params = I.siren_mlp(W["id"] + depth, spec["L"] * spec["F"], m["hidden"], depth)
+    x_full = I.points(W["id"], W["n_points"], spec["d"], clustered_half=True)
+    x = np.concatenate([x_full[:1536], x_full[-1536:]])
+    _compare(orc, spec, m["hidden"], depth, m["omega"], x, params, mlp_params)
+
+
+@pytest.mark.parametrize("d,depth,hidden,omega", [(3, 1, 16, 3.0), (2, 2, 32, 30.0), (3, 3, 64, 10.0),
+                                                  (3, 4, 64, 10.0), (2, 4, 48, 30.0)])
 def test_residual_parity_shapes(orc, d, depth, hidden, omega):
     spec = {"d": d, "L": 4, "F": 2, "kind": "hermite", "T": [1 << 12] * (d + 1), "n_min": 4,
             "n_max": 40, "d2_mode": "diag"}
