@@ -166,7 +166,9 @@ HASHENC_API int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size
  * vertex) and reads the corners from that copy.  A d = 4 Hermite handle with F <= 2 and such
  * table sizes packs its five tables the same way (16 F floats per vertex) and writes its
  * outputs directly; with F > 2 it needs no workspace.  An RBF handle needs no workspace (size
- * 0) and runs as hashenc_forward.
+ * 0) and runs as hashenc_forward.  2D and 3D Hermite batches of fewer than 32768 points run
+ * as hashenc_forward (the workspace is then not touched): for them the pass over every order
+ * table that the packing costs outweighs the faster gather.
  * workspace: >= hashenc_forward_workspace_size bytes, 256-byte aligned; calls sharing it
  * must not overlap.  Results are bit-identical to hashenc_forward. */
 HASHENC_API int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float* params,

@@ -28,6 +28,14 @@ HASHENC_API int hashenc_diag_backward_binned(const hashenc* h, int64_t n, const 
                                              const float* g_dgamma, const float* g_d2gamma, float* grad_params,
                                              void* workspace, size_t workspace_bytes, hashenc_stream_t stream);
 
+/* The workspace forward of hashenc_forward_ws with the packed order tables at any n, for
+ * testing the packed path on small batches (which hashenc_forward_ws itself hands to the
+ * direct forward below 32768 points for 2D and 3D Hermite grids).  Same arguments, workspace
+ * (hashenc_forward_workspace_size) and results as hashenc_forward_ws. */
+HASHENC_API int hashenc_diag_forward_packed(const hashenc* h, int64_t n, const float* x, const float* params,
+                                            float* gamma, float* dgamma, float* d2gamma, void* workspace,
+                                            size_t workspace_bytes, hashenc_stream_t stream);
+
 /* Plain streaming copy dst[i] = src[i], i < n_floats (both 16-byte aligned, no overlap).
  * Used to measure achievable HBM bandwidth and to calibrate memory counters. */
 HASHENC_API int hashenc_diag_copy(const float* src, float* dst, int64_t n_floats, hashenc_stream_t stream);

@@ -71,6 +71,7 @@ SIGNATURES = [
     ("hashenc_forward", ctypes.c_int, [P, I64, P, P, P, P, P, P]),
     ("hashenc_forward_workspace_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)]),
     ("hashenc_forward_ws", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    ("hashenc_diag_forward_packed", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),
     ("hashenc_backward", ctypes.c_int, [P, I64, P, P, P, P, P, P]),
     ("hashenc_backward_workspace_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)]),
     ("hashenc_backward_ws", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),

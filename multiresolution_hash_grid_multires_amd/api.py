@@ -226,6 +226,17 @@ def hashenc_forward_ws(h: Handle, x: torch.Tensor, params: torch.Tensor, gamma=N
                                     _dev_ptr(d2gamma, "d2gamma"), ws_ptr, ws_bytes, _stream(stream)))
 
 
+def hashenc_diag_forward_packed(h: Handle, x: torch.Tensor, params: torch.Tensor, gamma=None, dgamma=None,
+                                d2gamma=None, workspace: torch.Tensor | None = None, stream=None) -> None:
+    """The workspace forward with the packed tables at any batch size (diagnostics)."""
+    n = _points(h, x)
+    _check_encoder_io(h, n, params, gamma, dgamma, d2gamma)
+    ws_ptr, ws_bytes = _ws(workspace)
+    check(load().hashenc_diag_forward_packed(h, n, _dev_ptr(x, "x"), _dev_ptr(params, "params"),
+                                             _dev_ptr(gamma, "gamma"), _dev_ptr(dgamma, "dgamma"),
+                                             _dev_ptr(d2gamma, "d2gamma"), ws_ptr, ws_bytes, _stream(stream)))
+
+
 def hashenc_backward_workspace_size(h: Handle, n: int) -> int:
     b = ctypes.c_size_t()
     check(load().hashenc_backward_workspace_size(h, n, ctypes.byref(b)))
@@ -416,6 +427,16 @@ class HashGridEncoding:
             workspace = self.workspace(x.shape[0])
         hashenc_forward_ws(self.handle, x, params, out["gamma"], out.get("dgamma"), out.get("d2gamma"),
                            workspace, stream)
+        return out
+
+    def forward_packed(self, x: torch.Tensor, params: torch.Tensor, workspace=None, stream=None) -> dict:
+        """The workspace forward with the packed tables whatever the batch size (diagnostics)."""
+        out = {k: torch.empty(v, device=x.device, dtype=torch.float32)
+               for k, v in self.output_shapes(x.shape[0]).items()}
+        if workspace is None:
+            workspace = self.workspace(x.shape[0])
+        hashenc_diag_forward_packed(self.handle, x, params, out["gamma"], out.get("dgamma"), out.get("d2gamma"),
+                                    workspace, stream)
         return out
 
     def backward_binned(self, x: torch.Tensor, grad_params: torch.Tensor, g_gamma=None, g_dgamma=None,

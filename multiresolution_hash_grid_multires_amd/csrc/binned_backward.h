@@ -29,6 +29,9 @@ constexpr int kBinReduceBlocks = 256;             // persistent reduce workgroup
 constexpr int kScatterTileLarge = 1024;
 constexpr int kScatterTileSmall = 512;
 constexpr size_t kMaxScatterLds = 150 * 1024;     // of the 160 KB LDS of a gfx950 CU
+// Below this many entries per bin on average the reduce walks its items in a static order
+// (all items short: the per-item round trips, not balance, set the time).
+constexpr int64_t kSparseBinEntries = 4096;
 
 // Small, by-value plan: bins are (segment, chunk of rows) in segment order.  A chunk has
 // 2^cshift rows, except on dense d-linear segments in pair mode, where it holds whole
@@ -203,8 +206,9 @@ BinWorkspace bin_workspace_layout(const BinPlan& bp, int64_t chunk_points, int64
                                   int64_t floats_per_point, int tile);
 // Stages 2-3 (after the interpolant's count kernel) and stage 5 (after its scatter kernel).
 hipError_t run_bin_middle(const BinPlan& bp, const BinWorkspace& w, char* ws, hipStream_t s);
+// entries: the chunk's entry count (or a bound on it), which picks the reduce's item order
 hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws,
-                          float* grad, hipStream_t s);
+                          float* grad, int64_t entries, hipStream_t s);
 
 // Interpolant-specific count / scatter launches (d-linear and Hermite kernel files).
 // d-linear count / scatter; u_levels: the chunk's upstream level-major ([L][n][F]) or NULL

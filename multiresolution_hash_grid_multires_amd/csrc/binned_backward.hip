@@ -249,7 +249,55 @@ __device__ __forceinline__ void accumulate_records(double* __restrict__ acc, int
   }
 }
 
-constexpr int kFlushBatch = 8;  // gradient values per thread in flight in the reduce's flush
+constexpr int kFlushBatch = 16;  // gradient values per thread in flight in the reduce's flush (at most)
+
+// Flush of one chunk of the LDS accumulator into the gradient: element i of the chunk is row
+// i / W, component i % W (component-major planes of `plane` values).  Each value is read and
+// set back to zero, so the accumulator is all zeros again when the next item starts.  Rows no
+// entry touched keep their gradient: no read-modify-write for them (a bin of a small batch
+// touches few of its rows).  FB gradient loads per thread are in flight before their stores:
+// one read-modify-write round trip per batch rather than one per value.  A bin split over
+// several items (split) adds its part with atomics instead.  i / W is taken as the truncation
+// of (i + 1/2) / W in fp32: that quotient lies at least 1/(2W) from an integer, and its
+// rounding error, below (i + 1/2) / W * 2^-23, stays smaller for every i < 2^22 (a chunk holds
+// at most kBinLdsValues = 16384 values), so the truncation is exact.
+template <int FB, int THREADS>
+__device__ __forceinline__ void flush_chunk(double* __restrict__ acc, int W, int plane, int nfl,
+                                            float* __restrict__ dst, bool split) {
+  const float rw = 1.0f / (float)W;
+  auto slot = [&](int i) {
+    const int q = (int)(((float)i + 0.5f) * rw);
+    return (i - q * W) * plane + q;
+  };
+  if (split) {
+    for (int i = threadIdx.x; i < nfl; i += THREADS) {
+      const int a_i = slot(i);
+      const float a = (float)acc[a_i];
+      acc[a_i] = 0.0;
+      if (a != 0.0f) atomic_add_f32(dst + i, a);
+    }
+    return;
+  }
+  for (int i0 = threadIdx.x; i0 < nfl; i0 += THREADS * FB) {
+    float a[FB], gv[FB];
+#pragma unroll
+    for (int u = 0; u < FB; ++u) {
+      const int i = i0 + u * THREADS;
+      a[u] = 0.0f;
+      if (i < nfl) {
+        const int a_i = slot(i);
+        a[u] = (float)acc[a_i];
+        acc[a_i] = 0.0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < FB; ++u)
+      if (a[u] != 0.0f) gv[u] = dst[i0 + u * THREADS];
+#pragma unroll
+    for (int u = 0; u < FB; ++u)
+      if (a[u] != 0.0f) dst[i0 + u * THREADS] = gv[u] + a[u];
+  }
+}
 
 // ACC fp64 accumulator values and THREADS lanes per workgroup: the 128 KB accumulator (one
 // 1024-lane workgroup per CU) for bins of up to 16384 values, and a 16 KB one (eight 256-lane
@@ -260,22 +308,49 @@ __global__ __launch_bounds__(THREADS) void bin_reduce_kernel(const Grid g, const
                                                                     BinState* __restrict__ st,
                                                                     const WorkItem* __restrict__ items,
                                                                     const float* __restrict__ vals,
-                                                                    float* __restrict__ grad) {
+                                                                    float* __restrict__ grad, int static_items) {
   // fp64 accumulator: LDS fp64 atomics run several times faster than fp32 ones on gfx950
   // and the chunk sum is exact to far below the fp32 result precision.
   // component planes of nrows + 1 values (odd for even nrows), so that the W components of a
   // row fall in different LDS banks when the flush reads them side by side
   __shared__ double acc[ACC + 32];
   __shared__ int item_sh[2];
+  __shared__ int64_t vbase_sh[kMaxSeg];  // the segments' value and entry bases, read once
+  __shared__ int32_t ebase_sh[kMaxSeg];
+  __shared__ WorkItem next_sh[2];
+  for (int i = threadIdx.x; i < bp.nseg; i += THREADS) {
+    vbase_sh[i] = st->seg_vbase[i];
+    ebase_sh[i] = st->seg_ebase[i];
+  }
+  // zeroed once: every flush leaves the accumulator zero again
+  for (int i = threadIdx.x; i < ACC + 32; i += THREADS) acc[i] = 0.0;
   const int n_items = st->n_items;
-  // Workgroup b takes item b first; later items come from a counter (which starts after the
-  // first gridDim.x items), claimed once the current item's entries are accumulated, so the
-  // claim's latency hides behind the flush without holding an item back during the long part
-  // (two slots, so a claim never overwrites the index others are still reading).
+  // Workgroup b takes item b first.  Dynamic order (static_items == 0): later items come
+  // from a counter (which starts after the first gridDim.x items), claimed once the current
+  // item's entries are accumulated: the claiming thread keeps the index in a register until
+  // the flush is done, so the claim's round trip overlaps the flush's instead of holding the
+  // barrier before it, and no item is held back during the long part.  Static order (small
+  // batches, whose items are all short): workgroup b takes items b, b + gridDim.x, ..., and
+  // each next item's descriptor is loaded while the current item runs.  Two slots, so a new
+  // index or descriptor never overwrites the one others are still reading.
   int it = blockIdx.x;
   int slot = 0;
+  if (threadIdx.x < 5 && it < n_items)
+    reinterpret_cast<int*>(&next_sh[0])[threadIdx.x] = reinterpret_cast<const int*>(items + it)[threadIdx.x];
+  __syncthreads();
   while (it < n_items) {
-    const WorkItem w = items[it];
+    const WorkItem w = next_sh[slot];
+    // static order: the next descriptor, in a register of five lanes until the flush is done
+    const int nxt = it + (int)gridDim.x;
+    int pre = 0;
+    if (static_items && threadIdx.x < 5 && nxt < n_items) {
+      // a global vector load through a register the compiler cannot see into (not a scalar
+      // or flat load): its wait comes at the use after the flush, not at the barriers between
+      using global_ci32 = const __attribute__((address_space(1))) int32_t;
+      global_ci32* src = (global_ci32*)(reinterpret_cast<const int32_t*>(items + nxt) + threadIdx.x);
+      __asm__ volatile("" : "+v"(src));
+      pre = *src;
+    }
     const int sg = __builtin_amdgcn_readfirstlane(w.seg);
     const int k = sg / bp.L, l = sg % bp.L;
     const int W = bp.width[k];
@@ -286,11 +361,9 @@ __global__ __launch_bounds__(THREADS) void bin_reduce_kernel(const Grid g, const
     const int64_t nrows = rem < C ? rem : C;
     const int nfl = (int)(nrows * W);
     const int plane = (int)nrows + 1;
-    for (int i = threadIdx.x; i < plane * W; i += THREADS) acc[i] = 0.0;
-    __syncthreads();
     // values of entry e of segment sg start at vseg + (e - ebase) * W
-    const float* vseg = vals + st->seg_vbase[sg];
-    const int32_t eb = st->seg_ebase[sg];
+    const float* vseg = vals + vbase_sh[sg];
+    const int32_t eb = ebase_sh[sg];
     if (bp.records) {
       switch (W) {
         case 1: accumulate_records<1>(acc, plane, vseg, eb, w.begin, w.end); break;
@@ -309,37 +382,32 @@ __global__ __launch_bounds__(THREADS) void bin_reduce_kernel(const Grid g, const
       case 16: accumulate_entries<16>(acc, plane, vseg, eb, w.begin, w.end); break;
       default: accumulate_entries<24>(acc, plane, vseg, eb, w.begin, w.end); break;
     }
-    if (threadIdx.x == 0) item_sh[slot] = (int)gridDim.x + atomicAdd(&st->next_item, 1);
-    __syncthreads();
-    // flush: element i of the chunk is row i / W, component i % W
-    float* dst = grad + g.off[k][l] + row0 * W;
-    if (w.split) {
-      for (int i = threadIdx.x; i < nfl; i += THREADS) {
-        const float a = (float)acc[(i % W) * plane + i / W];
-        if (a != 0.0f) atomic_add_f32(dst + i, a);
-      }
-    } else {
-      // rows no entry touched keep their gradient: no read-modify-write for them (a bin of a
-      // small batch touches few of its rows).  kFlushBatch gradient loads per thread are in
-      // flight before their stores: one read-modify-write round trip per batch rather than
-      // one per value.
-      for (int i0 = threadIdx.x; i0 < nfl; i0 += THREADS * kFlushBatch) {
-        float a[kFlushBatch], gv[kFlushBatch];
-#pragma unroll
-        for (int u = 0; u < kFlushBatch; ++u) {
-          const int i = i0 + u * THREADS;
-          a[u] = i < nfl ? (float)acc[(i % W) * plane + i / W] : 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < kFlushBatch; ++u)
-          if (a[u] != 0.0f) gv[u] = dst[i0 + u * THREADS];
-#pragma unroll
-        for (int u = 0; u < kFlushBatch; ++u)
-          if (a[u] != 0.0f) dst[i0 + u * THREADS] = gv[u] + a[u];
-      }
+    int claimed = 0;  // counter value, the item index less gridDim.x
+    if (!static_items && threadIdx.x == 0) {
+      // the counter's (global) address through a register the compiler cannot see into:
+      // otherwise the one-lane atomic becomes a wavefront-aggregated one whose result is read
+      // back (and waited for) at once
+      using global_i32 = __attribute__((address_space(1))) int32_t;
+      global_i32* ctr = (global_i32*)&st->next_item;
+      __asm__ volatile("" : "+v"(ctr));
+      claimed = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    it = item_sh[slot];
+    float* dst = grad + g.off[k][l] + row0 * W;
+    constexpr int FB = ACC / THREADS < kFlushBatch ? ACC / THREADS : kFlushBatch;
+    flush_chunk<FB, THREADS>(acc, W, plane, nfl, dst, w.split);
+    if (static_items) {
+      if (threadIdx.x < 5 && nxt < n_items) reinterpret_cast<int*>(&next_sh[slot ^ 1])[threadIdx.x] = pre;
+      __syncthreads();
+      it = nxt;
+    } else {
+      if (threadIdx.x == 0) item_sh[slot] = (int)gridDim.x + claimed;
+      __syncthreads();
+      it = item_sh[slot];
+      if (threadIdx.x < 5 && it < n_items)
+        reinterpret_cast<int*>(&next_sh[slot ^ 1])[threadIdx.x] = reinterpret_cast<const int*>(items + it)[threadIdx.x];
+      __syncthreads();
+    }
     slot ^= 1;
   }
 }
@@ -517,20 +585,22 @@ hipError_t run_bin_middle(const BinPlan& bp, const BinWorkspace& w, char* ws, hi
 }
 
 hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& w, char* ws, float* grad,
-                          hipStream_t s) {
+                          int64_t entries, hipStream_t s) {
+  // small batches (few entries per bin): static item order with the next descriptor loaded
+  // ahead, since every item is short and the per-item round trips set the time
+  const int static_items = entries < (int64_t)bp.nbins * kSparseBinEntries ? 1 : 0;
   // the largest chunk of any table, in values: the small accumulator when it fits
   int64_t chunk_values = 0;
   for (int k = 0; k < bp.ntab; ++k) chunk_values = std::max<int64_t>(chunk_values, (int64_t)bp.width[k] << bp.cshift[k]);
   if (chunk_values <= kBinLdsValuesSmall) {
     hipLaunchKernelGGL((bin_reduce_kernel<kBinLdsValuesSmall, 256>), dim3(kBinReduceBlocks * 8), dim3(256), 0, s, g,
                        bp, reinterpret_cast<BinState*>(ws + w.state), reinterpret_cast<const WorkItem*>(ws + w.items),
-                       reinterpret_cast<const float*>(ws + w.vals), grad);
+                       reinterpret_cast<const float*>(ws + w.vals), grad, static_items);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((bin_reduce_kernel<kBinLdsValues, kReduceThreads>), dim3(kBinReduceBlocks), dim3(kReduceThreads), 0, s, g, bp,
                      reinterpret_cast<BinState*>(ws + w.state), reinterpret_cast<const WorkItem*>(ws + w.items),
-                     reinterpret_cast<const float*>(ws + w.vals),
-                     grad);
+                     reinterpret_cast<const float*>(ws + w.vals), grad, static_items);
   return hipGetLastError();
 }
 
@@ -585,7 +655,7 @@ hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2
         if (e != hipSuccess) return e;
       }
     }
-    hipError_t e = run_bin_reduce(g, bp, w, ws, grad, s);
+    hipError_t e = run_bin_reduce(g, bp, w, ws, grad, c * entries_per_point(d, g.L, hermite), s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -312,10 +312,16 @@ int hashenc_forward_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
   return ok();
 }
 
-int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float* params, float* gamma,
-                       float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
-                       hashenc_stream_t stream) {
-  if (!h) return fail(HASHENC_EINVAL, "hashenc_forward_ws: NULL handle");
+// The workspace forward (who: the entry point named in messages).  With direct_small, 2D and
+// 3D Hermite batches below kPackMinPoints take the direct forward: there the fixed cost of
+// packing every order table (about 0.14 ms for four 2^19-row tables) exceeds what the packed
+// gather saves (measured on MI355X: at 4096 points of the 16-level 3D grid 0.028 ms direct
+// against 0.147 ms packed; equal near 32 K points; the 2D 2^14-row grid about 50 K points).
+// The 4D packed copy costs little (five 2^16-row tables) and is taken at every n.
+static int forward_ws_impl(const char* who, const hashenc* h, int64_t n, const float* x, const float* params,
+                           float* gamma, float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
+                           hashenc_stream_t stream, bool direct_small) {
+  if (!h) return fail(HASHENC_EINVAL, "%s: NULL handle", who);
   if (h->kind == HASHENC_RBF || (h->d == 4 && hg::hermite4_packed_bytes(h->grid, h->F) == 0))
     return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
   if (h->d == 4) {
@@ -324,33 +330,33 @@ int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float*
     if (n == 0 || (!gamma && !dgamma && !d2gamma))
       return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
     if (n < 0 || n > kMaxPoints)
-      return fail(HASHENC_EINVAL, "hashenc_forward_ws: n = %lld out of range", (long long)n);
+      return fail(HASHENC_EINVAL, "%s: n = %lld out of range", who, (long long)n);
     if (!x || !params || !workspace)
-      return fail(HASHENC_EINVAL, "hashenc_forward_ws: x, params and workspace must not be NULL");
+      return fail(HASHENC_EINVAL, "%s: x, params and workspace must not be NULL", who);
     if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || !aligned16(dgamma) || !aligned16(d2gamma) ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
-      return fail(HASHENC_EALIGN, "hashenc_forward_ws: pointers must be 16-byte aligned (workspace 256-byte)");
+      return fail(HASHENC_EALIGN, "%s: pointers must be 16-byte aligned (workspace 256-byte)", who);
     if (workspace_bytes < need)
-      return fail(HASHENC_EINVAL, "hashenc_forward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
+      return fail(HASHENC_EINVAL, "%s: workspace of %zu bytes < %zu needed", who, workspace_bytes, need);
     hipError_t e = hg::launch_hermite4_forward(h->grid, h->F, h->d2_mode, n, x, params, static_cast<float*>(workspace),
                                                gamma, dgamma, d2gamma, stream);
-    if (e != hipSuccess) return hip_fail(e, "hashenc_forward_ws launch");
+    if (e != hipSuccess) return hip_fail(e, who);
     return ok();
   }
   if (h->kind == HASHENC_HERMITE) {
     // workspace: [packed copy of the order tables (equal table sizes) | level-major staging]
     const size_t need = hermite_forward_ws_bytes(h, n);
-    if (n == 0 || (!gamma && !dgamma && !d2gamma))
+    if (n == 0 || (!gamma && !dgamma && !d2gamma) || (direct_small && n < hg::kPackMinPoints))
       return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
     if (n < 0 || n > kMaxPoints)
-      return fail(HASHENC_EINVAL, "hashenc_forward_ws: n = %lld out of range", (long long)n);
+      return fail(HASHENC_EINVAL, "%s: n = %lld out of range", who, (long long)n);
     if (!x || !params || !workspace)
-      return fail(HASHENC_EINVAL, "hashenc_forward_ws: x, params and workspace must not be NULL");
+      return fail(HASHENC_EINVAL, "%s: x, params and workspace must not be NULL", who);
     if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || !aligned16(dgamma) || !aligned16(d2gamma) ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
-      return fail(HASHENC_EALIGN, "hashenc_forward_ws: pointers must be 16-byte aligned (workspace 256-byte)");
+      return fail(HASHENC_EALIGN, "%s: pointers must be 16-byte aligned (workspace 256-byte)", who);
     if (workspace_bytes < need)
-      return fail(HASHENC_EINVAL, "hashenc_forward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
+      return fail(HASHENC_EINVAL, "%s: workspace of %zu bytes < %zu needed", who, workspace_bytes, need);
     const size_t pk = hg::hermite_packed_bytes(h->grid, h->d, h->F);
     float* packed = pk ? static_cast<float*>(workspace) : nullptr;
     float* stage = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((pk + 255) & ~size_t(255)));
@@ -358,24 +364,38 @@ int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float*
     if (e == hipSuccess)
       e = hg::launch_hermite_forward(h->grid, h->d, h->F, h->d2_mode, n, x, params, packed, stage, true, gamma,
                                      dgamma, d2gamma, stream);
-    if (e != hipSuccess) return hip_fail(e, "hashenc_forward_ws launch");
+    if (e != hipSuccess) return hip_fail(e, who);
     return ok();
   }
   if (!gamma || n == 0) return hashenc_forward(h, n, x, params, gamma, dgamma, d2gamma, stream);
-  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_forward_ws: n = %lld out of range", (long long)n);
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "%s: n = %lld out of range", who, (long long)n);
   if (dgamma || d2gamma)
-    return fail(HASHENC_EUNSUPPORTED, "hashenc_forward_ws: derivative outputs need the Hermite kind");
+    return fail(HASHENC_EUNSUPPORTED, "%s: derivative outputs need the Hermite kind", who);
   if (!x || !params || !workspace)
-    return fail(HASHENC_EINVAL, "hashenc_forward_ws: x, params and workspace must not be NULL");
+    return fail(HASHENC_EINVAL, "%s: x, params and workspace must not be NULL", who);
   if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return fail(HASHENC_EALIGN, "hashenc_forward_ws: pointers must be 16-byte aligned (workspace 256-byte)");
+    return fail(HASHENC_EALIGN, "%s: pointers must be 16-byte aligned (workspace 256-byte)", who);
   const size_t need = hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n);
   if (workspace_bytes < need)
-    return fail(HASHENC_EINVAL, "hashenc_forward_ws: workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    return fail(HASHENC_EINVAL, "%s: workspace of %zu bytes < %zu needed", who, workspace_bytes, need);
   hipError_t e = hg::launch_dlinear_forward(h->grid, h->d, h->F, n, x, params, gamma,
                                             static_cast<float*>(workspace), stream);
-  if (e != hipSuccess) return hip_fail(e, "hashenc_forward_ws launch");
+  if (e != hipSuccess) return hip_fail(e, who);
   return ok();
+}
+
+int hashenc_forward_ws(const hashenc* h, int64_t n, const float* x, const float* params, float* gamma,
+                       float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
+                       hashenc_stream_t stream) {
+  return forward_ws_impl("hashenc_forward_ws", h, n, x, params, gamma, dgamma, d2gamma, workspace, workspace_bytes,
+                         stream, true);
+}
+
+int hashenc_diag_forward_packed(const hashenc* h, int64_t n, const float* x, const float* params, float* gamma,
+                                float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
+                                hashenc_stream_t stream) {
+  return forward_ws_impl("hashenc_diag_forward_packed", h, n, x, params, gamma, dgamma, d2gamma, workspace,
+                         workspace_bytes, stream, false);
 }
 
 int hashenc_backward(const hashenc* h, int64_t n, const float* x, const float* g_gamma,

@@ -142,6 +142,9 @@ hipError_t launch_dlinear_backward(const Grid& g, int d, int F, int64_t n, const
 bool hermite_packable(const Grid& g, int d);
 size_t hermite_packed_bytes(const Grid& g, int d, int F);
 hipError_t launch_hermite_pack(const Grid& g, int d, int F, const float* params, float* packed, hipStream_t s);
+// Smallest batch for which a 2D or 3D call packs the tables: below it the pack's fixed cost
+// (a pass over every order table) exceeds the packed gather's saving.
+constexpr int64_t kPackMinPoints = int64_t(1) << 15;
 // Level-major output staging of the Hermite forward: [L][n][M][F] floats, M = 1 + d + (d or 1).
 size_t hermite_stage_bytes(const Grid& g, int d, int F, int d2_mode, int64_t n);
 // packed: NULL to read params directly, else the packed copy of params.  stage: NULL to write

@@ -1107,21 +1107,38 @@ __global__ __launch_bounds__(kBlock) void fd_stencil_kernel(int64_t n, float eps
   }
 }
 
-// Sum of the per-wave partial rows, in two passes: each workgroup of the first pass adds a
-// slice of kSliceRows rows for 256 columns in fp64; the second pass adds the slices and
-// applies the result (grad_mlp += ..., loss (+)= ... / n).
-constexpr int kSliceRows = 128;
+// Sum of the partial rows, in two passes: each workgroup of the first pass adds a slice of
+// about sqrt(rows) rows for 256 columns in fp64; the second pass adds the slices and applies
+// the result (grad_mlp += ..., loss (+)= ... / n).  Both passes thus run about sqrt(rows)
+// loads per thread, four independent sums in flight: a few hundred rows of a small batch
+// take a few microseconds instead of one long serial chain per column.
+int slice_rows_for(int64_t rows) {
+  int r = 4;
+  while ((int64_t)r * r < rows) ++r;
+  return r;
+}
+// slices of a pass over at most max_rows rows: ceil(rows / slice_rows_for(rows)) <=
+// ceil(sqrt(rows)) <= slice_rows_for(max_rows)
+int max_slices_for(int64_t max_rows) { return slice_rows_for(max_rows); }
 
 __global__ __launch_bounds__(256) void reduce_partials_slices_kernel(const float* __restrict__ partial,
                                                                      int64_t n_waves, int64_t n_cols,
+                                                                     int slice_rows,
                                                                      double* __restrict__ slices) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= n_cols) return;
-  const int64_t r0 = (int64_t)blockIdx.y * kSliceRows;
-  const int64_t r1 = r0 + kSliceRows < n_waves ? r0 + kSliceRows : n_waves;
-  double s = 0.0;
-  for (int64_t r = r0; r < r1; ++r) s += (double)partial[r * n_cols + c];
-  slices[(int64_t)blockIdx.y * n_cols + c] = s;
+  const int64_t r0 = (int64_t)blockIdx.y * slice_rows;
+  const int64_t r1 = r0 + slice_rows < n_waves ? r0 + slice_rows : n_waves;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    s0 += (double)partial[r * n_cols + c];
+    s1 += (double)partial[(r + 1) * n_cols + c];
+    s2 += (double)partial[(r + 2) * n_cols + c];
+    s3 += (double)partial[(r + 3) * n_cols + c];
+  }
+  for (; r < r1; ++r) s0 += (double)partial[r * n_cols + c];
+  slices[(int64_t)blockIdx.y * n_cols + c] = (s0 + s1) + (s2 + s3);
 }
 
 __global__ __launch_bounds__(256) void reduce_partials_apply_kernel(const double* __restrict__ slices,
@@ -1131,8 +1148,16 @@ __global__ __launch_bounds__(256) void reduce_partials_apply_kernel(const double
                                                                     float* __restrict__ loss) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c > n_mlp) return;
-  double s = 0.0;
-  for (int i = 0; i < n_slices; ++i) s += slices[(int64_t)i * (n_mlp + 1) + c];
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int i = 0;
+  for (; i + 4 <= n_slices; i += 4) {
+    s0 += slices[(int64_t)i * (n_mlp + 1) + c];
+    s1 += slices[(int64_t)(i + 1) * (n_mlp + 1) + c];
+    s2 += slices[(int64_t)(i + 2) * (n_mlp + 1) + c];
+    s3 += slices[(int64_t)(i + 3) * (n_mlp + 1) + c];
+  }
+  for (; i < n_slices; ++i) s0 += slices[(int64_t)i * (n_mlp + 1) + c];
+  const double s = (s0 + s1) + (s2 + s3);
   if (c < n_mlp) {
     if (grad_mlp) grad_mlp[c] += (float)s;
   } else {
@@ -1168,7 +1193,7 @@ WorkspaceLayout workspace_layout(const Grid& g, int d, int F, int64_t n, int64_t
   w.enc = take(sizeof(float) * c * LF * (d + 2));
   w.up = take(sizeof(float) * c * LF * (d + 2));
   w.partial = take(sizeof(float) * (size_t)kSirenBlocks * kMaxWavesPerBlock * (n_mlp + 1));
-  w.slices = take(sizeof(double) * (size_t)((kSirenBlocks * kMaxWavesPerBlock + kSliceRows - 1) / kSliceRows) *
+  w.slices = take(sizeof(double) * (size_t)max_slices_for(kSirenBlocks * kMaxWavesPerBlock) *
                   (n_mlp + 1));
   w.packed = take(hermite_packed_bytes(g, d, F));  // packed order tables for the forward
   w.bins = take(binned ? binned_backward_workspace_bytes(g, d, F, true, c) : 0);
@@ -1576,7 +1601,7 @@ FdWorkspaceLayout fd_workspace_layout(const Grid& g, int d, int F, int64_t n, in
   w.enc = take(dlinear_forward_workspace_bytes(g, d, F, cs));  // level-major [L][c (2d+1)][F]
   w.up = take(dlinear_forward_workspace_bytes(g, d, F, cs));
   w.partial = take(sizeof(float) * (size_t)kFdPartialRows * (n_mlp + 1));
-  w.slices = take(sizeof(double) * (size_t)((kFdPartialRows + kSliceRows - 1) / kSliceRows) * (n_mlp + 1));
+  w.slices = take(sizeof(double) * (size_t)max_slices_for(kFdPartialRows) * (n_mlp + 1));
   w.bins = take(binned ? binned_backward_workspace_bytes(g, d, F, false, cs) : 0);
   w.total = off;
   return w;
@@ -1606,10 +1631,11 @@ MlpArgs make_mlp_args(const Grid& g, int F, int in, int H, int depth, float omeg
 // Sum the partial rows of one chunk into grad_mlp and the loss (first chunk: loss = ...).
 hipError_t reduce_partials(const MlpArgs& a, const float* partial, int64_t rows, double* slices, double inv_n,
                            bool first, float* grad_mlp, float* loss, hipStream_t s) {
-  const int n_slices = (int)((rows + kSliceRows - 1) / kSliceRows);
+  const int sr = slice_rows_for(rows);
+  const int n_slices = (int)((rows + sr - 1) / sr);
   const unsigned col_blocks = (unsigned)((a.n_mlp + 1 + 255) / 256);
   hipLaunchKernelGGL(reduce_partials_slices_kernel, dim3(col_blocks, (unsigned)n_slices), dim3(256), 0, s,
-                     partial, rows, a.n_mlp + 1, slices);
+                     partial, rows, a.n_mlp + 1, sr, slices);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(reduce_partials_apply_kernel, dim3(col_blocks), dim3(256), 0, s, slices, n_slices, a.n_mlp,
@@ -1709,8 +1735,10 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
   float* up = reinterpret_cast<float*>(ws + wl.up);
   float* partial = reinterpret_cast<float*>(ws + wl.partial);
   const double inv_n = 1.0 / (double)n;
-  // the parameters do not change between chunks: pack the order tables once
-  float* packed = hermite_packed_bytes(g, d, F) ? reinterpret_cast<float*>(ws + wl.packed) : nullptr;
+  // the parameters do not change between chunks: pack the order tables once (batches of at
+  // least kPackMinPoints; smaller ones gather from the tables)
+  float* packed =
+      hermite_packed_bytes(g, d, F) && n >= kPackMinPoints ? reinterpret_cast<float*>(ws + wl.packed) : nullptr;
   if (packed) {
     hipError_t e = launch_hermite_pack(g, d, F, params, packed, s);
     if (e != hipSuccess) return e;
@@ -1727,17 +1755,8 @@ hipError_t run_residual(const Grid& g, int d, int F, int64_t n, const float* x, 
     int rows = 0;  // partial rows written (per wavefront or per workgroup)
     e = dispatch_siren(d, depth, in, a, c, inv_n, xc, enc, mlp, up, rc, partial, rows, s);
     if (e != hipSuccess) return e;
-    const int64_t n_waves = rows;
-    const int n_slices = (int)((n_waves + kSliceRows - 1) / kSliceRows);
-    double* slices = reinterpret_cast<double*>(ws + wl.slices);
-    const unsigned col_blocks = (unsigned)((a.n_mlp + 1 + 255) / 256);
-    hipLaunchKernelGGL(reduce_partials_slices_kernel, dim3(col_blocks, (unsigned)n_slices), dim3(256), 0, s,
-                       partial, n_waves, a.n_mlp + 1, slices);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_partials_apply_kernel, dim3(col_blocks), dim3(256), 0, s, slices, n_slices, a.n_mlp,
-                       inv_n, p0 == 0 ? 1 : 0, grad_mlp, loss);
-    e = hipGetLastError();
+    e = reduce_partials(a, partial, rows, reinterpret_cast<double*>(ws + wl.slices), inv_n, p0 == 0, grad_mlp, loss,
+                        s);
     if (e != hipSuccess) return e;
     if (grad_params) {
       // the SIREN kernels wrote the upstream level-major, as the backward reads it

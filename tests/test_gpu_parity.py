@@ -161,13 +161,37 @@ def test_forward_ws_matches_forward(orc, name):
     ws = enc.workspace(5003)
     for _ in range(2):  # workspace reused
         b = enc.forward_ws(x, params, workspace=ws)
+        c = enc.forward_packed(x, params, workspace=ws)  # Hermite: packed tables at this size too
     torch.cuda.synchronize()
-    # same arithmetic per level on both paths: identical values, within the bar vs the oracle
+    # same arithmetic per level on every path: identical values, within the bar vs the oracle
     ref = orc.forward(spec, xh, _tables(name, lay["n_params"]))
     for k, r in zip(("gamma", "dgamma", "d2gamma"), ref):
         if k in a:
             assert torch.equal(a[k], b[k]), k
+            assert torch.equal(a[k], c[k]), k
             _blocks_close(b[k].cpu().numpy(), r, spec, FWD_TOL, k)
+
+
+@pytest.mark.parametrize("n", [(1 << 15) - 1, 1 << 15])
+def test_forward_ws_pack_threshold(orc, n):
+    # 2D and 3D Hermite workspace forwards pack the tables from 32768 points on and run the
+    # direct forward below: the same bits on both sides of the switch, against the oracle
+    name = "hermite2d_L8_T14"
+    spec = I.WORKLOADS[name]["spec"]
+    lay = orc.layout(spec)
+    tab = _tables(name, lay["n_params"])
+    xh = _points(name, n)
+    x, params = _dev(xh), _dev(tab)
+    enc = api.HashGridEncoding(spec)
+    a = enc.forward(x, params)
+    b = enc.forward_ws(x, params)
+    c = enc.forward_packed(x, params)
+    torch.cuda.synchronize()
+    ref = orc.forward(spec, xh, tab)
+    for k, r in zip(("gamma", "dgamma", "d2gamma"), ref):
+        assert torch.equal(a[k], b[k]), k
+        assert torch.equal(a[k], c[k]), k
+        _blocks_close(b[k].cpu().numpy(), r, spec, FWD_TOL, k)
 
 
 @pytest.mark.parametrize("L,F", [(5, 1), (3, 2), (32, 8), (7, 4)])
@@ -220,9 +244,11 @@ def test_feature_widths(orc, kind, F):  # both backward paths
     # the workspace forward (packed order tables for Hermite) gives the same bits
     enc = api.HashGridEncoding(spec)
     ws_out = enc.forward_ws(_dev(x), _dev(params), workspace=enc.workspace(x.shape[0]))
+    pk_out = enc.forward_packed(_dev(x), _dev(params), workspace=enc.workspace(x.shape[0]))
     torch.cuda.synchronize()
     for k in got:
         assert np.array_equal(ws_out[k].cpu().numpy(), got[k]), k
+        assert np.array_equal(pk_out[k].cpu().numpy(), got[k]), k
     ups = [u.astype(np.float32) for u in
            (rng.standard_normal(s) for s in _upstream_shapes(spec, 777))]
     ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
@@ -256,9 +282,11 @@ def test_hermite_unequal_tables(orc, T):
     packed = 4 * int(sum(lay["rows"][0])) * (1 << d) * spec["F"] if packable else 0
     assert api.hashenc_forward_workspace_size(enc.handle, n) == (packed + 255) // 256 * 256 + stage
     ws_out = enc.forward_ws(_dev(x), _dev(params))
+    pk_out = enc.forward_packed(_dev(x), _dev(params))  # packed copy at this size as well
     torch.cuda.synchronize()
     for k in got:
         assert np.array_equal(ws_out[k].cpu().numpy(), got[k]), k
+        assert np.array_equal(pk_out[k].cpu().numpy(), got[k]), k
     ups = [u.astype(np.float32) for u in (rng.standard_normal(s) for s in _upstream_shapes(spec, n))]
     ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
     for path in PATHS:
