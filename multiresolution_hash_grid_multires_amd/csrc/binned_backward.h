@@ -77,9 +77,53 @@ struct WorkItem {
 struct BinState {
   int32_t n_items;
   int32_t next_item;
+  // Per segment s: an upper bound on |v| over every value the chunk's records of segment s
+  // add to a row, as fp32 bits (non-negative floats order like their bit patterns; inf and
+  // NaN lie above every finite bound).  Zeroed by the plan stage, raised by the scatter, read
+  // by the reduce to pick each work item's fixed-point scale.
+  uint32_t vmax_bits[kMaxSeg];
   int32_t seg_ebase[kMaxSeg];   // first entry of segment s
   int64_t seg_vbase[kMaxSeg];   // first value float of segment s
 };
+
+// |v| as its fp32 bit pattern: the unsigned maximum of these is the bits of max |v|, with
+// NaN (and inf) above every finite value, which a float max would drop.
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+
+// Bound on |value| of a Hermite record per unit of upstream: every record value is
+// sum_o u_o * dO_o/dtheta over the level's outputs o (gamma, d first derivatives, the d
+// second derivatives of the diagonal or their sum), and per axis the cubic Hermite factors
+// are at most 1 (value; a derivative slot carries Delta x = 1/N), 1.5 N (first derivative)
+// and 6 N^2 (second derivative), so |value| <= max|u| (1 + 1.5 d N + 6 d N^2); doubled to
+// cover the fp32 rounding of the factor chains.  While this bound is finite no value
+// overflows, so the largest value written (which a float max over the values finds, NaN
+// aside) is a finite bound; where it is not, the level's segments get a NaN bound.
+__device__ __forceinline__ float hermite_value_bound(float N, int d) {
+  return 2.0f * (1.0f + 1.5f * (float)d * N + 6.0f * (float)d * N * N);
+}
+// 0, or NaN bits when max|u| (as abs_bits) times the level's bound is not finite
+__device__ __forceinline__ uint32_t hermite_nonfinite_floor(uint32_t ubits, float N, int d) {
+  return __uint_as_float(ubits) * hermite_value_bound(N, d) < __builtin_inff() ? 0u : 0x7fc00000u;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  return m;
+}
+
+// Segment bounds of a scatter workgroup: raised per wavefront in LDS (vsh[kMaxSeg], zeroed
+// before the workgroup's first barrier), added to the chunk's bounds once per workgroup.
+// Every lane of the wavefront calls raise_seg_vmax.
+__device__ __forceinline__ void raise_seg_vmax(uint32_t* vsh, int s, uint32_t m) {
+  m = wave_max_u32(m);
+  if (__lane_id() == 0 && m != 0u) atomicMax(&vsh[s], m);
+}
+// after a barrier that follows the last raise_seg_vmax
+__device__ __forceinline__ void publish_seg_vmax(const uint32_t* vsh, int nseg, uint32_t* vmax) {
+  for (int i = (int)threadIdx.x; i < nseg; i += (int)blockDim.x)
+    if (vsh[i] != 0u) atomicMax(&vmax[i], vsh[i]);
+}
 
 struct BinWorkspace {
   int32_t tile;   // points per count / scatter workgroup

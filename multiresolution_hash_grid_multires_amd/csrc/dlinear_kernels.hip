@@ -423,7 +423,7 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
     const Grid g, const BinPlan bp, int64_t n, int32_t tile, int32_t nblk, int32_t lpg, const float* __restrict__ x,
     const float* __restrict__ g_gamma, const float* __restrict__ u_lm, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
-    const BinState* __restrict__ st, float* __restrict__ vals_out) {
+    const BinState* __restrict__ st, float* __restrict__ vals_out, uint32_t* __restrict__ vmax) {
   constexpr int NP = 1 << (D - 1);  // x-corner pairs per cell
   constexpr int R = 2 + F;          // floats per record
   extern __shared__ int32_t lds[];
@@ -439,6 +439,8 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
   float* st_rec = reinterpret_cast<float*>(lds + ((2 * nbins + TPB / 64 + kMaxLevels + 3) & ~3));
   int32_t* st_pos = reinterpret_cast<int32_t*>(st_rec + (int64_t)tile * NP * R);  // [tile*NP]
 
+  __shared__ uint32_t vsh[kMaxSeg];  // the workgroup's segment (= level) bounds
+  for (int i = threadIdx.x; i < kMaxSeg; i += TPB) vsh[i] = 0u;
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
   const int64_t p = (int64_t)blk * tile + threadIdx.x;
   const bool on = p < n;
@@ -480,6 +482,9 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
     const bool few = nb <= kFewBins;
     const int32_t ebase = st->seg_ebase[l];
     float* vseg = vals_out + st->seg_vbase[l];
+    // bound on the values the level's records add to rows: each is t aG or (1 - t) aG with a
+    // weight a <= 1, so max |G| bounds them
+    uint32_t vm = 0u;
     if (on) {
       uint32_t base[D];
       float t[D];
@@ -504,6 +509,8 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
 #pragma unroll
         for (int f = 0; f < F; ++f) G[f] = 0.0f;
       }
+#pragma unroll
+      for (int f = 0; f < F; ++f) vm = max(vm, abs_bits(G[f]));
       [&]<int... Y>(std::integer_sequence<int, Y...>) {
         ((
              [&] {
@@ -539,6 +546,7 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
          ...);
       }(std::make_integer_sequence<int, NP>{});
     }
+    raise_seg_vmax(vsh, l, vm);
     if (pair) {  // uniform over the workgroup
       __syncthreads();
       const int32_t total = np * NP;
@@ -550,6 +558,8 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
       __syncthreads();
     }
   }
+  __syncthreads();
+  publish_seg_vmax(vsh, bp.nseg, vmax);
 }
 
 template <int D, int F, int TPB>
@@ -568,6 +578,7 @@ hipError_t launch_bin_tile(const Grid& g, const BinPlan& bp, const BinWorkspace&
   const int32_t* bin_start = reinterpret_cast<const int32_t*>(ws + w.bin_start);
   const BinState* st = reinterpret_cast<const BinState*>(ws + w.state);
   float* vals = reinterpret_cast<float*>(ws + w.vals);
+  uint32_t* vmax = reinterpret_cast<BinState*>(ws + w.state)->vmax_bits;
   // PRE reads the group's part of the row as 16-byte pieces: rows and groups of a multiple of
   // 4 floats only, so that every piece is aligned and inside the row
   if (!u_lm && w.lpg * F <= 32 && (w.lpg * F) % 4 == 0 && (g.Lrow * F) % 4 == 0) {
@@ -575,13 +586,13 @@ hipError_t launch_bin_tile(const Grid& g, const BinPlan& bp, const BinWorkspace&
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, true, TPB>), grid, dim3(TPB), lds, s, g, bp, n, w.tile, w.nblk,
-                       w.lpg, x, gg, nullptr, counts, totals, bin_start, st, vals);
+                       w.lpg, x, gg, nullptr, counts, totals, bin_start, st, vals, vmax);
   } else {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlinear_scatter_kernel<D, F, false, TPB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dlinear_scatter_kernel<D, F, false, TPB>), grid, dim3(TPB), lds, s, g, bp, n, w.tile,
-                       w.nblk, w.lpg, x, gg, u_lm, counts, totals, bin_start, st, vals);
+                       w.nblk, w.lpg, x, gg, u_lm, counts, totals, bin_start, st, vals, vmax);
   }
   return hipGetLastError();
 }

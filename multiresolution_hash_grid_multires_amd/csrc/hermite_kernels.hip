@@ -445,6 +445,19 @@ struct LevelUp {
   float h[D][F];
 };
 
+// max |u| over a level's upstream, as fp32 bits (NaN above inf above every finite value)
+template <int D, int F>
+__device__ __forceinline__ uint32_t level_up_absmax(const LevelUp<D, F>& u) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    m = max(m, abs_bits(u.v[f]));
+#pragma unroll
+    for (int i = 0; i < D; ++i) m = max(m, max(abs_bits(u.g[i][f]), abs_bits(u.h[i][f])));
+  }
+  return m;
+}
+
 // Reverse of fwd_pair: distribute the level upstream onto the coefficients of corner pair
 // (0, Y) and scatter-add them.
 template <int D, int F, int Y, class Sink>
@@ -1059,12 +1072,14 @@ template <int D, int F, int K, int Y>
 __device__ __forceinline__ void stage_pair(const Grid& g, const BinPlan& bp, int l, bool dense, bool few,
                                            int32_t b0, int lo_k, int32_t base, const CellKeys<D>& keys,
                                            const AxisBasis (&ab)[D], const LevelUp<D, F>& u, int32_t* lcur,
-                                           const int32_t* delta, float* st_rec) {
+                                           const int32_t* delta, float* st_rec, float& vmx) {
   constexpr int W = binom_d(D, K) * F;
   constexpr int R = hermite_rec_width(W);
   constexpr int RS = hermite_stage_width(W);
   float v[2][W];
   bwd_pair_table<D, F, Y, K>(ab, u, v[0], v[1]);
+#pragma unroll
+  for (int j = 0; j < W; ++j) vmx = fmaxf(vmx, fmaxf(fabsf(v[0][j]), fabsf(v[1][j])));
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     int32_t bin;
@@ -1092,7 +1107,8 @@ template <int D, int F, int P, int K>
 __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, int l, bool on, int np, int lo_k,
                                               int32_t base, const CellKeys<D>& keys, const AxisBasis (&ab)[D],
                                               const LevelUp<D, F>& u, const BinState* __restrict__ st,
-                                              float* __restrict__ vals_out, const HScatterLds<D, F, P>& sh) {
+                                              float* __restrict__ vals_out, const HScatterLds<D, F, P>& sh,
+                                              uint32_t* vsh, uint32_t nf) {
   constexpr int W = binom_d(D, K) * F;
   constexpr int R = hermite_rec_width(W);
   constexpr int RS = hermite_stage_width(W);
@@ -1102,14 +1118,16 @@ __device__ __forceinline__ void scatter_table(const Grid& g, const BinPlan& bp, 
   const int nb = bp.seg_bin0[sg + 1] - b0;
   const bool dense = (g.dense[K] >> l) & 1u;
   const bool few = nb <= kFewBins;
+  float vmx = 0.0f;  // largest |value| of this lane's records (NaN values aside: nf)
   if (on) {
-    stage_pair<D, F, K, 0>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec);
-    stage_pair<D, F, K, 1>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec);
+    stage_pair<D, F, K, 0>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec, vmx);
+    stage_pair<D, F, K, 1>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec, vmx);
     if constexpr (D == 3) {
-      stage_pair<D, F, K, 2>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec);
-      stage_pair<D, F, K, 3>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec);
+      stage_pair<D, F, K, 2>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec, vmx);
+      stage_pair<D, F, K, 3>(g, bp, l, dense, few, b0, lo_k, base, keys, ab, u, sh.lcur, sh.delta, sh.st_rec, vmx);
     }
   }
+  raise_seg_vmax(vsh, sg, max(__float_as_uint(vmx), nf));
   __syncthreads();
   const int32_t ebase = st->seg_ebase[sg];
   float* vseg = vals_out + st->seg_vbase[sg];
@@ -1148,9 +1166,12 @@ __global__ __launch_bounds__(P) void hermite_scatter_kernel(
     const Grid g, const BinPlan bp, int64_t n, int32_t nblk, int32_t lpg, bool diag, const float* __restrict__ x,
     const float* __restrict__ U, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
-    const BinState* __restrict__ st, float* __restrict__ vals_out) {
+    const BinState* __restrict__ st, float* __restrict__ vals_out, uint32_t* __restrict__ vmax) {
   extern __shared__ int32_t lds[];
   const HScatterLds<D, F, P> sh(lds, bp.max_level_bins);
+  __shared__ uint32_t vsh[kMaxSeg];  // the workgroup's segment bounds
+  for (int i = threadIdx.x; i < kMaxSeg; i += P) vsh[i] = 0u;
+  __syncthreads();
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
   const int64_t p = (int64_t)blk * P + threadIdx.x;
   const bool on = p < n;
@@ -1170,6 +1191,8 @@ __global__ __launch_bounds__(P) void hermite_scatter_kernel(
   }
   for (int l = l0; l < l1; ++l) {
     const LevelUp<D, F> u = un;
+    // NaN bound for the level's segments unless its values are finite
+    const uint32_t nf = on ? hermite_nonfinite_floor(level_up_absmax<D, F>(u), g.Nf[l], D) : 0u;
     int32_t base[D + 1];
     level_bins_apply<D, P, NPB>(bp, l, blk, nblk, counts, totals, bin_start, rn, sh.delta, sh.lcur, sh.wsum, base);
     if (l + 1 < l1) {
@@ -1180,16 +1203,18 @@ __global__ __launch_bounds__(P) void hermite_scatter_kernel(
     AxisBasis ab[D];
     if (on) level_setup<D>(g, l, xp, keys, ab);
     int lo = 0;
-    scatter_table<D, F, P, 0>(g, bp, l, on, np, lo, base[0], keys, ab, u, st, vals_out, sh);
+    scatter_table<D, F, P, 0>(g, bp, l, on, np, lo, base[0], keys, ab, u, st, vals_out, sh, vsh, nf);
     lo += bp.seg_bin0[l + 1] - bp.seg_bin0[l];
-    scatter_table<D, F, P, 1>(g, bp, l, on, np, lo, base[1], keys, ab, u, st, vals_out, sh);
+    scatter_table<D, F, P, 1>(g, bp, l, on, np, lo, base[1], keys, ab, u, st, vals_out, sh, vsh, nf);
     lo += bp.seg_bin0[bp.L + l + 1] - bp.seg_bin0[bp.L + l];
-    scatter_table<D, F, P, 2>(g, bp, l, on, np, lo, base[2], keys, ab, u, st, vals_out, sh);
+    scatter_table<D, F, P, 2>(g, bp, l, on, np, lo, base[2], keys, ab, u, st, vals_out, sh, vsh, nf);
     if constexpr (D == 3) {
       lo += bp.seg_bin0[2 * bp.L + l + 1] - bp.seg_bin0[2 * bp.L + l];
-      scatter_table<D, F, P, 3>(g, bp, l, on, np, lo, base[3], keys, ab, u, st, vals_out, sh);
+      scatter_table<D, F, P, 3>(g, bp, l, on, np, lo, base[3], keys, ab, u, st, vals_out, sh, vsh, nf);
     }
   }
+  __syncthreads();
+  publish_seg_vmax(vsh, bp.nseg, vmax);
 }
 
 template <int D, int F>
@@ -1239,7 +1264,8 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((hermite_scatter_kernel<D, F, P>), grid, dim3(P), lds, s, g, bp, n, w.nblk, w.lpg, diag, x, U,
-                     counts, totals, bin_start, st, vals);
+                     counts, totals, bin_start, st, vals,
+                     reinterpret_cast<BinState*>(ws + w.state)->vmax_bits);
   return hipGetLastError();
 }
 
@@ -1803,7 +1829,8 @@ template <int F, int T, int K>
 __device__ __forceinline__ void scatter4_table(const Grid& g, const BinPlan& bp, int l, bool on, int c, int np,
                                                int lo_k, int32_t base, const Keys4& keys, const CornerAxis (&ca)[4],
                                                const Up4<F>& u, const BinState* __restrict__ st,
-                                               float* __restrict__ vals_out, const HScatterLds<4, F, T>& sh) {
+                                               float* __restrict__ vals_out, const HScatterLds<4, F, T>& sh,
+                                               uint32_t* vsh, uint32_t nf) {
   constexpr int S = slots4(K);
   constexpr int W = S * F;
   constexpr int R = hermite_rec_width(W);
@@ -1811,11 +1838,14 @@ __device__ __forceinline__ void scatter4_table(const Grid& g, const BinPlan& bp,
   const int sg = K * bp.L + l;
   const int32_t b0 = bp.seg_bin0[sg];
   const int nb = bp.seg_bin0[sg + 1] - b0;
+  float vmx = 0.0f;  // largest |value| of this lane's record (NaN values aside: nf)
   if (on) {
     float rec[RS];
     [&]<int... Q>(std::integer_sequence<int, Q...>) {
       (coef_grad4<F, alpha4_of_slot(K, Q)>(ca, u, rec + 1 + Q * F), ...);
     }(std::make_integer_sequence<int, S>{});
+#pragma unroll
+    for (int j = 1; j <= W; ++j) vmx = fmaxf(vmx, fabsf(rec[j]));
     int32_t bin;
     uint32_t local;
     bin_of(bp, K, l, row4(keys, c, (g.dense[K] >> l) & 1u, g.T[K], g.Tmask[K]), bin, local);
@@ -1827,6 +1857,7 @@ __device__ __forceinline__ void scatter4_table(const Grid& g, const BinPlan& bp,
     for (int j = R + 1; j < RS; ++j) rec[j] = 0.0f;
     store_vec<RS>(sh.st_rec + (int64_t)(slot - base) * RS, rec);
   }
+  raise_seg_vmax(vsh, sg, max(__float_as_uint(vmx), nf));
   __syncthreads();
   const int32_t ebase = st->seg_ebase[sg];
   float* vseg = vals_out + st->seg_vbase[sg];
@@ -1849,10 +1880,13 @@ __global__ __launch_bounds__(16 * P) void hermite4_scatter_kernel(
     const Grid g, const BinPlan bp, int64_t n, int32_t nblk, int32_t lpg, int d2_mode, const float* __restrict__ x,
     const float* __restrict__ gg, const float* __restrict__ gd, const float* __restrict__ g2,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ totals, const int32_t* __restrict__ bin_start,
-    const BinState* __restrict__ st, float* __restrict__ vals_out) {
+    const BinState* __restrict__ st, float* __restrict__ vals_out, uint32_t* __restrict__ vmax) {
   constexpr int T = 16 * P;
   extern __shared__ int32_t lds[];
   const HScatterLds<4, F, T> sh(lds, bp.max_level_bins);
+  __shared__ uint32_t vsh[kMaxSeg];  // the workgroup's segment bounds
+  for (int i = threadIdx.x; i < kMaxSeg; i += T) vsh[i] = 0u;
+  __syncthreads();
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
   const int c = threadIdx.x % 16;
   const int64_t p = (int64_t)blk * P + threadIdx.x / 16;
@@ -1864,7 +1898,18 @@ __global__ __launch_bounds__(16 * P) void hermite4_scatter_kernel(
   const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);
   for (int l = l0; l < l1; ++l) {
     Up4<F> u;
-    if (on) u = load_up4<F>(g, p, l, d2_mode, gg, gd, g2);
+    uint32_t nf = 0u;  // NaN bound for the level's segments unless its values are finite
+    if (on) {
+      u = load_up4<F>(g, p, l, d2_mode, gg, gd, g2);
+      uint32_t m = 0u;
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        m = max(m, abs_bits(u.G0[f]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, max(abs_bits(u.G1[i][f]), abs_bits(u.G2[i][f])));
+      }
+      nf = hermite_nonfinite_floor(m, g.Nf[l], 4);
+    }
     int32_t base_k[5];
     hermite_level_bins<4, T>(bp, l, blk, nblk, counts, totals, bin_start, sh.delta, sh.lcur, sh.wsum, base_k);
     Keys4 keys;
@@ -1878,16 +1923,18 @@ __global__ __launch_bounds__(16 * P) void hermite4_scatter_kernel(
       for (int i = 0; i < 4; ++i) ca[i] = corner_axis(t[i], g.Nf[l], g.invN[l], (c >> i) & 1);
     }
     int lo = 0;
-    scatter4_table<F, T, 0>(g, bp, l, on, c, np, lo, base_k[0], keys, ca, u, st, vals_out, sh);
+    scatter4_table<F, T, 0>(g, bp, l, on, c, np, lo, base_k[0], keys, ca, u, st, vals_out, sh, vsh, nf);
     lo += bp.seg_bin0[l + 1] - bp.seg_bin0[l];
-    scatter4_table<F, T, 1>(g, bp, l, on, c, np, lo, base_k[1], keys, ca, u, st, vals_out, sh);
+    scatter4_table<F, T, 1>(g, bp, l, on, c, np, lo, base_k[1], keys, ca, u, st, vals_out, sh, vsh, nf);
     lo += bp.seg_bin0[bp.L + l + 1] - bp.seg_bin0[bp.L + l];
-    scatter4_table<F, T, 2>(g, bp, l, on, c, np, lo, base_k[2], keys, ca, u, st, vals_out, sh);
+    scatter4_table<F, T, 2>(g, bp, l, on, c, np, lo, base_k[2], keys, ca, u, st, vals_out, sh, vsh, nf);
     lo += bp.seg_bin0[2 * bp.L + l + 1] - bp.seg_bin0[2 * bp.L + l];
-    scatter4_table<F, T, 3>(g, bp, l, on, c, np, lo, base_k[3], keys, ca, u, st, vals_out, sh);
+    scatter4_table<F, T, 3>(g, bp, l, on, c, np, lo, base_k[3], keys, ca, u, st, vals_out, sh, vsh, nf);
     lo += bp.seg_bin0[3 * bp.L + l + 1] - bp.seg_bin0[3 * bp.L + l];
-    scatter4_table<F, T, 4>(g, bp, l, on, c, np, lo, base_k[4], keys, ca, u, st, vals_out, sh);
+    scatter4_table<F, T, 4>(g, bp, l, on, c, np, lo, base_k[4], keys, ca, u, st, vals_out, sh, vsh, nf);
   }
+  __syncthreads();
+  publish_seg_vmax(vsh, bp.nseg, vmax);
 }
 
 template <int F>
@@ -1910,7 +1957,7 @@ hipError_t launch_bin4(const Grid& g, const BinPlan& bp, const BinWorkspace& w, 
   hipLaunchKernelGGL((hermite4_scatter_kernel<F, P>), grid, dim3(16 * P), lds, s, g, bp, n, w.nblk, w.lpg, d2_mode, x,
                      gg, gd, g2, counts, reinterpret_cast<const int32_t*>(ws + w.totals),
                      reinterpret_cast<const int32_t*>(ws + w.bin_start), reinterpret_cast<const BinState*>(ws + w.state),
-                     reinterpret_cast<float*>(ws + w.vals));
+                     reinterpret_cast<float*>(ws + w.vals), reinterpret_cast<BinState*>(ws + w.state)->vmax_bits);
   return hipGetLastError();
 }
 
