@@ -39,12 +39,20 @@ HEADLINE = "dlinear3d_L16_T19"
 # kernel sources it was taken on.  A figure whose digest differs from the current sources
 # is not reported.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-# kernels of each entry point (name fragments), for summing counters per call
+# kernels of each entry point (name fragments), for summing counters per call; the d-linear
+# workloads run the counting pair, whose forward launches the count kernel
 ENTRY_KERNELS = {
     "forward": ("forward", "pack_kernel", "levels_to_rows", "level_major_to_rows", "zero_columns"),
     "backward": ("count_kernel", "scan_", "plan_kernel", "scatter_kernel", "reduce_kernel", "upstream_levels",
                  "backward_kernel"),
 }
+
+
+def entry_kernels(workload: str) -> dict:
+    if workload.startswith("dlinear"):
+        return {"forward": ENTRY_KERNELS["forward"] + ("count_kernel",),
+                "backward": tuple(f for f in ENTRY_KERNELS["backward"] if f != "count_kernel")}
+    return ENTRY_KERNELS
 
 
 def source_digest() -> str:
@@ -105,7 +113,8 @@ def summarize_counters(args) -> int:
     calls = args.steps + args.warmup
     per_kernel, entries = {}, {"forward": 0.0, "backward": 0.0}
     for name, vals in fetch.items():
-        entry = next((e for e, frags in ENTRY_KERNELS.items() if any(fr in name for fr in frags)), None)
+        entry = next((e for e, frags in entry_kernels(args.workload).items() if any(fr in name for fr in frags)),
+                     None)
         if entry is None or "copy_kernel" in name:
             continue
         wv = write.get(name, [0.0])
@@ -392,6 +401,8 @@ def main() -> int:
     ap.add_argument("--active-levels", type=int, default=0,
                     help="coarse-to-fine activation: compute only the first A levels (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-counting", action="store_true",
+                    help="d-linear: hashenc_forward_ws + hashenc_backward_ws instead of the counting pair")
     ap.add_argument("--mlp-depth", type=int, default=0,
                     help="residual workloads: SIREN hidden layers instead of the workload's own (1..4)")
     ap.add_argument("--n-points", type=int, default=0,
@@ -460,6 +471,13 @@ def main() -> int:
     # atomic scatter-add when the configuration has no binned plan (RBF; 4D Hermite with F = 8)
     backward_path = ("binned" if workspace is not None and api.hashenc_backward_workspace_size(enc.handle, n) > 0
                      else "atomic")
+    # d-linear: the counting pair (the forward takes the backward's bin counts while it
+    # gathers; separate forward and backward workspaces)
+    counting = workspace is not None and spec["kind"] == "dlinear" and not args.no_counting
+    if counting:
+        fws, bws = enc.forward_workspace(n), enc.backward_workspace(n)
+        if backward_path == "binned":
+            backward_path = "binned, counts taken by the forward"
 
     def step(ev=None):
         if ev is not None:
@@ -467,14 +485,18 @@ def main() -> int:
         grad.zero_()
         if ev is not None:
             ev[0].record(stream)
-        if workspace is not None:
+        if counting:
+            api.hashenc_forward_counting(enc.handle, x, params, outs["gamma"], None, None, fws, bws)
+        elif workspace is not None:
             api.hashenc_forward_ws(enc.handle, x, params, outs["gamma"], outs.get("dgamma"), outs.get("d2gamma"),
                                    workspace)
         else:
             api.hashenc_forward(enc.handle, x, params, outs["gamma"], outs.get("dgamma"), outs.get("d2gamma"))
         if ev is not None:
             ev[1].record(stream)
-        if workspace is not None:
+        if counting:
+            api.hashenc_backward_counted(enc.handle, x, ups[0], None, None, grad, bws)
+        elif workspace is not None:
             api.hashenc_backward_ws(enc.handle, x, ups[0], ups[1], ups[2], grad, workspace)
         else:
             api.hashenc_backward(enc.handle, x, ups[0], ups[1], ups[2], grad)
@@ -516,7 +538,8 @@ def main() -> int:
     roofline = {"bound": "hbm", "achieved": round(kern[dom]["GBps"], 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(kern[dom]["GBps"] / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "traffic_source": traffic_note, "source_digest": source_digest(),
-                "kernel": ("hashenc_" + dom + ("_ws" if workspace is not None else "")
+                "kernel": ("hashenc_" + dom + (("_counting" if dom == "forward" else "_counted") if counting
+                                                else "_ws" if workspace is not None else "")
                            + f" ({spec['kind']}; its kernels back to back on one stream)"),
                 "avg_launch_ms": round(kern[dom]["ms"], 4),
                 "alg_bytes_per_launch": kern[dom]["alg_bytes"]}

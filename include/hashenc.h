@@ -205,6 +205,33 @@ HASHENC_API int hashenc_backward_ws(const hashenc* h, int64_t n, const float* x,
                                     const float* g_dgamma, const float* g_d2gamma, float* grad_params,
                                     void* workspace, size_t workspace_bytes, hashenc_stream_t stream);
 
+/* Training pair for the d-linear kind: a forward that also prepares the binned backward of
+ * the same points, and that backward.  The forward of one point and level already computes
+ * the corner rows of its cell (Instant-NGP explainer, encoding pipeline steps 1-2); the
+ * binned backward's first pass (a per-tile histogram of those rows over the bins of rows that
+ * one workgroup accumulates) needs exactly these rows, so hashenc_forward_counting writes the
+ * histogram into bwd_workspace while it gathers, and hashenc_backward_counted starts from it.
+ *
+ * hashenc_forward_counting: outputs and workspace as hashenc_forward_ws (bit-identical
+ *   results); bwd_workspace: >= hashenc_backward_workspace_size(h, n) bytes, 256-byte aligned,
+ *   caller-owned, contents irrelevant on entry, not overlapping workspace; it is written.
+ * hashenc_backward_counted: result and arguments as hashenc_backward_ws (grad_params +=
+ *   dL/dtheta, the same passages), with bwd_workspace the one the counting forward wrote.
+ * Contract: between the two calls x, n and bwd_workspace stay the same and nothing else
+ * writes the workspace.  Broken, the gradient is undefined but every write stays inside
+ * bwd_workspace and grad_params (the backward's stores are bounds-guarded).
+ * Where the counts would not apply -- other kinds, batches that take the atomic path or more
+ * than one 2^21-point chunk, forward passes with more than 512 bins -- the two calls behave
+ * exactly as hashenc_forward_ws and hashenc_backward_ws (the forward then leaves bwd_workspace
+ * untouched); both decide from (h, n) alone. */
+HASHENC_API int hashenc_forward_counting(const hashenc* h, int64_t n, const float* x, const float* params,
+                                         float* gamma, float* dgamma, float* d2gamma, void* workspace,
+                                         size_t workspace_bytes, void* bwd_workspace, size_t bwd_workspace_bytes,
+                                         hashenc_stream_t stream);
+HASHENC_API int hashenc_backward_counted(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
+                                         const float* g_dgamma, const float* g_d2gamma, float* grad_params,
+                                         void* bwd_workspace, size_t bwd_workspace_bytes, hashenc_stream_t stream);
+
 /* Allocation-free variant of hashenc_backward_ws, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments as hashenc_backward (all device pointers owned by the caller)

@@ -76,6 +76,8 @@ SIGNATURES = [
     ("hashenc_backward_workspace_size", ctypes.c_int, [P, I64, ctypes.POINTER(ctypes.c_size_t)]),
     ("hashenc_backward_ws", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),
     ("hashenc_backward_noalloc", ctypes.c_int, [P, I64, P, P, P, P, P, P]),
+    ("hashenc_forward_counting", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P, ctypes.c_size_t, P]),
+    ("hashenc_backward_counted", ctypes.c_int, [P, I64, P, P, P, P, P, P, ctypes.c_size_t, P]),
     ("hashenc_residual_workspace_size", ctypes.c_int,
      [P, ctypes.POINTER(HashencMlp), I64, ctypes.POINTER(ctypes.c_size_t)]),
     ("hashenc_residual", ctypes.c_int,

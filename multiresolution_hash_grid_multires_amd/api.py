@@ -253,6 +253,32 @@ def hashenc_backward_ws(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None,
                                      _dev_ptr(grad_params, "grad_params"), ws_ptr, ws_bytes, _stream(stream)))
 
 
+def hashenc_forward_counting(h: Handle, x: torch.Tensor, params: torch.Tensor, gamma=None, dgamma=None,
+                             d2gamma=None, workspace: torch.Tensor | None = None,
+                             bwd_workspace: torch.Tensor | None = None, stream=None) -> None:
+    """hashenc_forward_ws that also leaves the binned backward's counts of x in bwd_workspace."""
+    n = _points(h, x)
+    _check_encoder_io(h, n, params, gamma, dgamma, d2gamma)
+    ws_ptr, ws_bytes = _ws(workspace)
+    bws_ptr, bws_bytes = _ws(bwd_workspace)
+    check(load().hashenc_forward_counting(h, n, _dev_ptr(x, "x"), _dev_ptr(params, "params"),
+                                          _dev_ptr(gamma, "gamma"), _dev_ptr(dgamma, "dgamma"),
+                                          _dev_ptr(d2gamma, "d2gamma"), ws_ptr, ws_bytes, bws_ptr, bws_bytes,
+                                          _stream(stream)))
+
+
+def hashenc_backward_counted(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_d2gamma=None,
+                             grad_params=None, bwd_workspace: torch.Tensor | None = None, stream=None) -> None:
+    """hashenc_backward_ws starting from the counts hashenc_forward_counting left for the same x."""
+    n = _points(h, x)
+    _check_encoder_io(h, n, None, g_gamma, g_dgamma, g_d2gamma, grad_params)
+    ws_ptr, ws_bytes = _ws(bwd_workspace)
+    check(load().hashenc_backward_counted(h, n, _dev_ptr(x, "x"), _dev_ptr(g_gamma, "g_gamma"),
+                                          _dev_ptr(g_dgamma, "g_dgamma"), _dev_ptr(g_d2gamma, "g_d2gamma"),
+                                          _dev_ptr(grad_params, "grad_params"), ws_ptr, ws_bytes,
+                                          _stream(stream)))
+
+
 def hashenc_backward_noalloc(h: Handle, x: torch.Tensor, g_gamma=None, g_dgamma=None, g_d2gamma=None,
                              grad_params=None, stream=None) -> None:
     """The binned backward on the library's static scratch (no workspace, nothing allocated);
@@ -414,6 +440,14 @@ class HashGridEncoding:
         hashenc_backward(self.handle, x, g_gamma, g_dgamma, g_d2gamma, grad_params, stream)
         return grad_params
 
+    def forward_workspace(self, n: int) -> torch.Tensor | None:
+        b = hashenc_forward_workspace_size(self.handle, n)
+        return torch.empty(b, dtype=torch.uint8, device="cuda") if b else None
+
+    def backward_workspace(self, n: int) -> torch.Tensor | None:
+        b = hashenc_backward_workspace_size(self.handle, n)
+        return torch.empty(b, dtype=torch.uint8, device="cuda") if b else None
+
     def workspace(self, n: int) -> torch.Tensor | None:
         """A device workspace for forward_ws and backward_ws on n points (None when neither
         uses one); the two calls may share it when they do not overlap."""
@@ -438,6 +472,22 @@ class HashGridEncoding:
         hashenc_diag_forward_packed(self.handle, x, params, out["gamma"], out.get("dgamma"), out.get("d2gamma"),
                                     workspace, stream)
         return out
+
+    def forward_counting(self, x: torch.Tensor, params: torch.Tensor, workspace: torch.Tensor,
+                         bwd_workspace: torch.Tensor, stream=None) -> dict:
+        """forward_ws that also prepares backward_counted on the same x (two separate, non-overlapping
+        workspaces: forward_workspace(n) and backward_workspace(n))."""
+        out = {k: torch.empty(v, device=x.device, dtype=torch.float32)
+               for k, v in self.output_shapes(x.shape[0]).items()}
+        hashenc_forward_counting(self.handle, x, params, out["gamma"], out.get("dgamma"), out.get("d2gamma"),
+                                 workspace, bwd_workspace, stream)
+        return out
+
+    def backward_counted(self, x: torch.Tensor, grad_params: torch.Tensor, g_gamma=None, g_dgamma=None,
+                         g_d2gamma=None, bwd_workspace=None, stream=None) -> torch.Tensor:
+        """backward_ws after forward_counting on the same x and bwd_workspace."""
+        hashenc_backward_counted(self.handle, x, g_gamma, g_dgamma, g_d2gamma, grad_params, bwd_workspace, stream)
+        return grad_params
 
     def backward_binned(self, x: torch.Tensor, grad_params: torch.Tensor, g_gamma=None, g_dgamma=None,
                         g_d2gamma=None, stream=None) -> torch.Tensor:

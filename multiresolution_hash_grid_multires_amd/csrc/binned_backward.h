@@ -299,9 +299,23 @@ size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite
 // ignored.
 // max_chunk > 0 lowers the points per pass below bin_chunk_points (a workspace sized for
 // max_chunk points then suffices).
+// counted: the chunk's counts are already in the workspace (left by the counting d-linear
+// forward on the same x; n at most one chunk), so the count pass is skipped.
 hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2_mode, int64_t n,
                                const float* x, const float* g_gamma, const float* g_dgamma,
                                const float* g_d2gamma, const float* u_levels, float* grad, void* workspace,
-                               hipStream_t s, int64_t max_chunk = 0);
+                               hipStream_t s, int64_t max_chunk = 0, bool counted = false);
+// Workspace layout of one chunk of chunk_points points.
+BinWorkspace bin_workspace_for(const Grid& g, const BinPlan& bp, int d, int F, bool hermite, int64_t chunk_points);
+
+// Counting d-linear forward: the workspace forward (level-major staging in scratch, then rows
+// in gamma) that also writes the binned backward's per-tile counts of these n points (at most
+// one chunk) into the backward workspace bws, so that run_binned_backward(..., counted) on
+// the same x skips its count pass.  dlinear_forward_counts: whether this configuration's
+// forward passes can count (each pass's bins fit the forward's LDS counters).
+bool dlinear_forward_counts(const Grid& g, int d, int F);
+hipError_t launch_dlinear_forward_counting(const Grid& g, int d, int F, int64_t n, const float* x,
+                                           const float* params, float* gamma, float* scratch, void* bws,
+                                           hipStream_t s);
 
 }  // namespace hg

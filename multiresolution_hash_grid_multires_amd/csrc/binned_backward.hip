@@ -700,26 +700,34 @@ size_t binned_backward_workspace_bytes(const Grid& g, int d, int F, bool hermite
                               bin_tile_points(bp, d, F, hermite)).total;
 }
 
+BinWorkspace bin_workspace_for(const Grid& g, const BinPlan& bp, int d, int F, bool hermite, int64_t chunk_points) {
+  return bin_workspace_layout(bp, chunk_points, entries_per_point(d, g.L, hermite), floats_per_point(bp, d),
+                              bin_tile_points(bp, d, F, hermite));
+}
+
 hipError_t run_binned_backward(const Grid& g, int d, int F, bool hermite, int d2_mode, int64_t n,
                                const float* x, const float* g_gamma, const float* g_dgamma,
                                const float* g_d2gamma, const float* u_levels, float* grad, void* workspace,
-                               hipStream_t s, int64_t max_chunk) {
+                               hipStream_t s, int64_t max_chunk, bool counted) {
   BinPlan bp;
   make_bin_plan(g, d, F, hermite, bp);
   int64_t cmax = bin_chunk_points(g, d, hermite);
   if (max_chunk > 0 && max_chunk < cmax) cmax = max_chunk;
-  if (u_levels && n > cmax) return hipErrorInvalidValue;  // one chunk only
+  if ((u_levels || counted) && n > cmax) return hipErrorInvalidValue;  // one chunk only
   char* ws = static_cast<char*>(workspace);
   const int64_t LF = (int64_t)g.Lrow * F;  // upstream row stride
   for (int64_t p0 = 0; p0 < n; p0 += cmax) {
     const int64_t c = (n - p0) < cmax ? (n - p0) : cmax;
-    const BinWorkspace w = bin_workspace_layout(bp, c, entries_per_point(d, g.L, hermite), floats_per_point(bp, d),
-                                                bin_tile_points(bp, d, F, hermite));
+    const BinWorkspace w = bin_workspace_for(g, bp, d, F, hermite, c);
     const float* xc = x + p0 * d;
     const float* gg = g_gamma ? g_gamma + p0 * LF : nullptr;
     const float* gd = g_dgamma ? g_dgamma + p0 * d * LF : nullptr;
     const float* g2 = g_d2gamma ? g_d2gamma + p0 * (d2_mode == HASHENC_D2_DIAG ? d : 1) * LF : nullptr;
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = counted ? 1 : 0; pass < 2; ++pass) {
+      if (counted && pass == 1) {  // the counting forward left this chunk's counts
+        hipError_t e = run_bin_middle(bp, w, ws, s);
+        if (e != hipSuccess) return e;
+      }
       hipError_t e = !hermite ? launch_dlinear_bin(g, bp, w, ws, d, F, pass == 1, c, xc, gg, u_levels, s)
                      : d == 4 ? launch_hermite4_bin(g, bp, w, ws, F, d2_mode, pass == 1, c, xc, gg, gd, g2, s)
                               : launch_hermite_bin(g, bp, w, ws, d, F, d2_mode, pass == 1, c, xc, gg, gd, g2,

@@ -161,20 +161,39 @@ __global__ __launch_bounds__(kFwdLdsThreads) void dlinear_forward_lds_kernel(con
 // of every x-pair -- adjacent rows on dense levels, rows differing in the low bits on hashed
 // levels -- are read by neighbouring lanes of one load instruction and share one L2 request
 // whenever they share a cache line.  The lane sums meet through one cross-lane add.
-template <int D, int F, bool LM_OUT>
+// CNT: also histogram the binned backward's entries of these points over the pass's bins
+// (the count pass, from the corner rows the gather computes anyway) and add the workgroup's
+// histogram to counts[tile][bin] (ctile points per backward tile, a multiple of the
+// workgroup's points).  On pair-mode levels the two x-corners of a pair make one entry and
+// share its bin, so each lane counts the pairs whose y/z index has its parity; elsewhere each
+// lane counts its own corners.
+constexpr int kFwdCntBins = 512;  // LDS counters of one pass's bins (a pass with more counts in the backward)
+
+template <int D, int F, bool LM_OUT, bool CNT>
 __global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, const FwdPlan fp, int64_t n,
                                                                  int32_t n_tiles, const float* __restrict__ x,
                                                                  const float* __restrict__ params,
-                                                                 float* __restrict__ gamma) {
+                                                                 float* __restrict__ gamma, const BinPlan bp,
+                                                                 int32_t ctile, int32_t* __restrict__ counts) {
   constexpr int PTS = kBlock / 2;  // points per workgroup
   const int pass = blockIdx.x / n_tiles;
   const int l0 = fp.first[pass], l1 = fp.last[pass];
   const int c0 = threadIdx.x & 1;
   const int64_t p = (int64_t)(blockIdx.x % n_tiles) * PTS + (threadIdx.x >> 1);
-  if (p >= n) return;  // both lanes of a point leave together
+  [[maybe_unused]] __shared__ int32_t hist[CNT ? kFwdCntBins : 1];
+  [[maybe_unused]] int32_t pb0 = 0, pb1 = 0;
+  if constexpr (CNT) {
+    pb0 = bp.seg_bin0[l0];
+    pb1 = bp.seg_bin0[l1 + 1];
+    for (int i = threadIdx.x; i < pb1 - pb0; i += kBlock) hist[i] = 0;
+    __syncthreads();
+  } else {
+    if (p >= n) return;  // both lanes of a point leave together
+  }
+  const bool on = p < n;
   float xp[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) xp[i] = x[p * D + i];
+  for (int i = 0; i < D; ++i) xp[i] = x[(on ? p : n - 1) * D + i];
   for (int l = l0; l <= l1; ++l) {
     uint32_t base[D];
     float t[D];
@@ -184,6 +203,7 @@ __global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, c
     const float* tab = params + g.off[0][l];
     constexpr int NP = 1 << (D - 1);
     float rows[NP][F];
+    [[maybe_unused]] uint32_t rr[NP];
     // issue every gather of the level before using any of them
     [&]<int... Y>(std::integer_sequence<int, Y...>) {
       ((
@@ -191,9 +211,25 @@ __global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, c
              const uint32_t r = c0 ? corner_row<D, (Y << 1) | 1>(keys, dense, g.T[0], g.Tmask[0])
                                    : corner_row<D, (Y << 1)>(keys, dense, g.T[0], g.Tmask[0]);
              load_vec<F>(tab + (size_t)r * F, rows[Y]);
+             if constexpr (CNT) rr[Y] = r;
            }()),
        ...);
     }(std::make_integer_sequence<int, NP>{});
+    if constexpr (CNT) {
+      if (on) {
+        const bool pair = (bp.pair_mask >> l) & 1u;
+        const bool few = bp.seg_bin0[l + 1] - bp.seg_bin0[l] <= kFewBins;
+#pragma unroll
+        for (int y = 0; y < NP; ++y) {
+          if (pair && (y & 1) != c0) continue;
+          int32_t b;
+          uint32_t local;
+          bin_of(bp, 0, l, rr[y], b, local);
+          if (few) wave_aggregated_add<false>(hist, b - pb0);
+          else atomicAdd(&hist[b - pb0], 1);
+        }
+      }
+    }
     float acc[F];
 #pragma unroll
     for (int f = 0; f < F; ++f) acc[f] = 0.0f;
@@ -208,10 +244,16 @@ __global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, c
     }
 #pragma unroll
     for (int f = 0; f < F; ++f) acc[f] += __shfl_xor(acc[f], 1, 64);
-    if (c0 == 0) {
+    if (c0 == 0 && on) {
       if constexpr (LM_OUT) store_vec<F>(gamma + ((int64_t)l * n + p) * F, acc);
       else store_vec<F>(gamma + p * (int64_t)g.Lrow * F + (int64_t)l * F, acc);
     }
+  }
+  if constexpr (CNT) {
+    __syncthreads();
+    const int64_t row = (int64_t)(blockIdx.x % n_tiles) * PTS / ctile;
+    for (int i = threadIdx.x; i < pb1 - pb0; i += kBlock)
+      if (hist[i] != 0) atomicAdd(&counts[row * bp.nbins + pb0 + i], hist[i]);
   }
 }
 
@@ -331,10 +373,12 @@ __global__ __launch_bounds__(kBlock) void dlinear_backward_kernel(const Grid g, 
 // (two per lane) and one group of lpg levels (blockIdx.y), and histograms their entries over
 // that group's bins in LDS.  On pair-mode levels the two x-corners of each (y, z) corner pair
 // make one entry (they always share a bin); elsewhere each corner is its own entry.
+// zero_rest: also zero the tile's counters of every later bin (whose levels the counting
+// forward then adds with atomics).
 template <int D, int TPB>
 __global__ __launch_bounds__(TPB) void dlinear_count_kernel(const Grid g, const BinPlan bp, int64_t n, int32_t tile,
                                                             int32_t nblk, int32_t lpg, const float* __restrict__ x,
-                                                            int32_t* __restrict__ counts) {
+                                                            int32_t* __restrict__ counts, int32_t zero_rest) {
   extern __shared__ int32_t hist[];
   const int blk = bin_tile_of_block(blockIdx.x, nblk);
   const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);
@@ -383,7 +427,8 @@ __global__ __launch_bounds__(TPB) void dlinear_count_kernel(const Grid g, const 
     }
   }
   __syncthreads();
-  for (int i = gb0 + threadIdx.x; i < gb1; i += TPB) counts[(int64_t)blk * bp.nbins + i] = hist[i];
+  const int32_t ge = zero_rest ? bp.nbins : gb1;
+  for (int i = gb0 + threadIdx.x; i < ge; i += TPB) counts[(int64_t)blk * bp.nbins + i] = i < gb1 ? hist[i] : 0;
 }
 
 // G = up[l*F .. l*F + F) for a wave-uniform l < 32 / F: per feature, a tournament over the
@@ -445,6 +490,11 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
   const int64_t p = (int64_t)blk * tile + threadIdx.x;
   const bool on = p < n;
   const int np = (int)min((int64_t)tile, n - (int64_t)blk * tile);
+  // Every store below lands inside the chunk's entries and staging even when the counts do
+  // not describe these points (counts left by a counting forward on other x): per level a
+  // tile has np * NP pair records (2 np NP single ones) whatever x is, so only the bins of
+  // mismatched records are wrong; the guards keep them in bounds (the gradient is then wrong).
+  const int32_t etot = bin_start[nbins];
   // this workgroup's levels and their bins (all of them unless the levels are split)
   const int l0 = blockIdx.y * lpg, l1 = min(g.L, l0 + lpg);
   const int32_t gb0 = bp.seg_bin0[l0], gb1 = bp.seg_bin0[l1];
@@ -529,18 +579,22 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
                  const int32_t lp = s0 - lb;
                  rec[0] = __uint_as_float(lo | (hi << 16));
                  rec[1] = t[0];
-                 store_vec<R>(st_rec + (int64_t)lp * R, rec);
-                 st_pos[lp] = delta[bn0] + s0;
+                 if ((uint32_t)lp < (uint32_t)(np * NP)) {
+                   store_vec<R>(st_rec + (int64_t)lp * R, rec);
+                   st_pos[lp] = delta[bn0] + s0;
+                 }
                } else {
                  // two single-corner records, lower row gets (1 - t) aG
                  const int32_t s0 = few ? wave_aggregated_add<true>(lcur, bn0) : atomicAdd(&lcur[bn0], 1);
                  rec[0] = __uint_as_float(lo | 0xFFFF0000u);
                  rec[1] = t[0];
-                 store_vec<R>(vseg + (int64_t)(delta[bn0] + s0 - ebase) * R, rec);
+                 const int32_t e0 = delta[bn0] + s0;
+                 if ((uint32_t)e0 < (uint32_t)etot) store_vec<R>(vseg + (int64_t)(e0 - ebase) * R, rec);
                  const int32_t s1 = few ? wave_aggregated_add<true>(lcur, bn1) : atomicAdd(&lcur[bn1], 1);
                  rec[0] = __uint_as_float(hi | 0xFFFF0000u);
                  rec[1] = 1.0f - t[0];
-                 store_vec<R>(vseg + (int64_t)(delta[bn1] + s1 - ebase) * R, rec);
+                 const int32_t e1 = delta[bn1] + s1;
+                 if ((uint32_t)e1 < (uint32_t)etot) store_vec<R>(vseg + (int64_t)(e1 - ebase) * R, rec);
                }
              }()),
          ...);
@@ -553,7 +607,8 @@ __global__ __launch_bounds__(TPB) void dlinear_scatter_kernel(
       for (int32_t q = threadIdx.x; q < total; q += TPB) {
         float rec[R];
         load_vec<R>(st_rec + (int64_t)q * R, rec);
-        store_vec<R>(vseg + (int64_t)(st_pos[q] - ebase) * R, rec);
+        const int32_t e = st_pos[q];
+        if ((uint32_t)e < (uint32_t)etot) store_vec<R>(vseg + (int64_t)(e - ebase) * R, rec);
       }
       __syncthreads();
     }
@@ -570,7 +625,7 @@ hipError_t launch_bin_tile(const Grid& g, const BinPlan& bp, const BinWorkspace&
   if (!scatter) {  // two points per count lane
     if (w.tile != TPB) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dlinear_count_kernel<D, TPB / 2>), grid, dim3(TPB / 2), sizeof(int32_t) * (size_t)bp.nbins,
-                       s, g, bp, n, w.tile, w.nblk, w.lpg, x, counts);
+                       s, g, bp, n, w.tile, w.nblk, w.lpg, x, counts, 0);
     return hipGetLastError();
   }
   const size_t lds = dlinear_scatter_lds_bytes(bp, D, F, w.tile);
@@ -607,23 +662,50 @@ hipError_t launch_bin(const Grid& g, const BinPlan& bp, const BinWorkspace& w, c
   return hipErrorInvalidValue;
 }
 
+// The counting forward's backward workspace: plan, layout and base (all NULL: no counting).
+struct FwdCounts {
+  const BinPlan* bp;
+  const BinWorkspace* w;
+  char* ws;
+};
+
 template <int D, int F>
 hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* params, float* gamma,
-                      float* scratch, hipStream_t s) {
+                      float* scratch, hipStream_t s, const FwdCounts& cnt) {
   const int64_t tiles = (n + kBlock / 2 - 1) / (kBlock / 2);  // two lanes per point
   // with the level-major staging, the leading dense levels that fit in LDS go to the LDS kernel
   const int Lc = scratch ? fwd_lds_levels(g, D, F) : 0;
   const FwdPlan fp = make_fwd_plan(g, D, F, scratch != nullptr, Lc);
   if (tiles * fp.n_pass > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles * fp.n_pass));
+  BinPlan nobp;
+  nobp.nbins = 0;
   if (!scratch) {
-    hipLaunchKernelGGL((dlinear_forward_kernel<D, F, false>), grid, dim3(kBlock), 0, s, g, fp, n, (int32_t)tiles, x,
-                       params, gamma);
+    hipLaunchKernelGGL((dlinear_forward_kernel<D, F, false, false>), grid, dim3(kBlock), 0, s, g, fp, n,
+                       (int32_t)tiles, x, params, gamma, nobp, 0, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.L == g.Lrow) return e;
     return launch_zero_columns(gamma, n, g.Lrow * F, g.L * F, s);
   }
   hipError_t e = hipSuccess;
+  int32_t* counts = cnt.ws ? reinterpret_cast<int32_t*>(cnt.ws + cnt.w->counts) : nullptr;
+  if (counts && n > 0) {
+    // the LDS kernel's levels 0 .. Lc-1 by the count kernel, which also zeroes every later
+    // counter of its tile for the forward's atomics
+    const BinWorkspace& w = *cnt.w;
+    const int tpb = w.tile / 2;
+    const size_t hist = sizeof(int32_t) * (size_t)cnt.bp->nbins;
+    if (tpb == kScatterTileLarge / 2)
+      hipLaunchKernelGGL((dlinear_count_kernel<D, kScatterTileLarge / 2>), dim3((unsigned)w.nblk, 1), dim3(tpb), hist,
+                         s, g, *cnt.bp, n, w.tile, w.nblk, (int32_t)Lc, x, counts, 1);
+    else if (tpb == kScatterTileSmall / 2)
+      hipLaunchKernelGGL((dlinear_count_kernel<D, kScatterTileSmall / 2>), dim3((unsigned)w.nblk, 1), dim3(tpb), hist,
+                         s, g, *cnt.bp, n, w.tile, w.nblk, (int32_t)Lc, x, counts, 1);
+    else
+      return hipErrorInvalidValue;
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (Lc > 0 && n > 0) {
     int32_t nfl = 0;
     for (int l = 0; l < Lc; ++l) {
@@ -642,8 +724,12 @@ hipError_t launch_fwd(const Grid& g, int64_t n, const float* x, const float* par
     if (e != hipSuccess) return e;
   }
   if (fp.n_pass > 0) {
-    hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true>), grid, dim3(kBlock), 0, s, g, fp, n, (int32_t)tiles, x,
-                       params, scratch);
+    if (counts)
+      hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true, true>), grid, dim3(kBlock), 0, s, g, fp, n,
+                         (int32_t)tiles, x, params, scratch, *cnt.bp, cnt.w->tile, counts);
+    else
+      hipLaunchKernelGGL((dlinear_forward_kernel<D, F, true, false>), grid, dim3(kBlock), 0, s, g, fp, n,
+                         (int32_t)tiles, x, params, scratch, nobp, 0, nullptr);
     e = hipGetLastError();
   }
   if (e != hipSuccess || !gamma) return e;  // no gamma: the level-major staging is the output
@@ -692,7 +778,30 @@ size_t dlinear_forward_workspace_bytes(const Grid& g, int d, int F, int64_t n) {
 
 hipError_t launch_dlinear_forward(const Grid& g, int d, int F, int64_t n, const float* x,
                                   const float* params, float* gamma, float* scratch, hipStream_t s) {
-  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, n, x, params, gamma, scratch, s);
+  const FwdCounts none{nullptr, nullptr, nullptr};
+  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, n, x, params, gamma, scratch, s, none);
+}
+
+bool dlinear_forward_counts(const Grid& g, int d, int F) {
+  if (!binned_fits(g, d, F, false)) return false;
+  BinPlan bp;
+  make_bin_plan(g, d, F, false, bp);
+  const int Lc = fwd_lds_levels(g, d, F);
+  const FwdPlan fp = make_fwd_plan(g, d, F, true, Lc);
+  for (int i = 0; i < fp.n_pass; ++i)
+    if (bp.seg_bin0[fp.last[i] + 1] - bp.seg_bin0[fp.first[i]] > kFwdCntBins) return false;
+  return true;
+}
+
+hipError_t launch_dlinear_forward_counting(const Grid& g, int d, int F, int64_t n, const float* x,
+                                           const float* params, float* gamma, float* scratch, void* bws,
+                                           hipStream_t s) {
+  if (n > bin_chunk_points(g, d, false)) return hipErrorInvalidValue;  // one chunk of the backward
+  BinPlan bp;
+  make_bin_plan(g, d, F, false, bp);
+  const BinWorkspace w = bin_workspace_for(g, bp, d, F, false, n);
+  const FwdCounts cnt{&bp, &w, static_cast<char*>(bws)};
+  HASHENC_DISPATCH_DF(d, F, launch_fwd, g, n, x, params, gamma, scratch, s, cnt);
 }
 
 hipError_t launch_dlinear_backward(const Grid& g, int d, int F, int64_t n, const float* x,

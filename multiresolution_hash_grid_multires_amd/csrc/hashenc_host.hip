@@ -594,6 +594,70 @@ int hashenc_backward_ws(const hashenc* h, int64_t n, const float* x, const float
                          workspace_bytes, stream);
 }
 
+// Whether hashenc_forward_counting leaves counts for a backward of these n points: the
+// d-linear binned path, one chunk, and forward passes whose bins fit its LDS counters.  The
+// counting forward and the counted backward decide alike from (h, n) alone.
+static bool counting_for(const hashenc* h, int64_t n) {
+  return h->kind == HASHENC_DLINEAR && n > 0 && binned_for(h, n) &&
+         n <= hg::bin_chunk_points(h->grid, h->d, false) && hg::dlinear_forward_counts(h->grid, h->d, h->F);
+}
+
+int hashenc_forward_counting(const hashenc* h, int64_t n, const float* x, const float* params, float* gamma,
+                             float* dgamma, float* d2gamma, void* workspace, size_t workspace_bytes,
+                             void* bwd_workspace, size_t bwd_workspace_bytes, hashenc_stream_t stream) {
+  const char* who = "hashenc_forward_counting";
+  if (!h) return fail(HASHENC_EINVAL, "%s: NULL handle", who);
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "%s: n = %lld out of range", who, (long long)n);
+  if (!counting_for(h, n))
+    return forward_ws_impl(who, h, n, x, params, gamma, dgamma, d2gamma, workspace, workspace_bytes, stream, true);
+  if (dgamma || d2gamma)
+    return fail(HASHENC_EUNSUPPORTED, "%s: derivative outputs need the Hermite kind", who);
+  if (!x || !params || !gamma || !workspace || !bwd_workspace)
+    return fail(HASHENC_EINVAL, "%s: x, params, gamma and both workspaces must not be NULL", who);
+  if (!aligned16(x) || !aligned16(params) || !aligned16(gamma) || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      (reinterpret_cast<uintptr_t>(bwd_workspace) & 255u))
+    return fail(HASHENC_EALIGN, "%s: pointers must be 16-byte aligned (workspaces 256-byte)", who);
+  const size_t need = hg::dlinear_forward_workspace_bytes(h->grid, h->d, h->F, n);
+  if (workspace_bytes < need)
+    return fail(HASHENC_EINVAL, "%s: workspace of %zu bytes < %zu needed", who, workspace_bytes, need);
+  const size_t bneed = hg::binned_backward_workspace_bytes(h->grid, h->d, h->F, false, n);
+  if (bwd_workspace_bytes < bneed)
+    return fail(HASHENC_EINVAL, "%s: backward workspace of %zu bytes < %zu needed", who, bwd_workspace_bytes, bneed);
+  const uintptr_t f0 = reinterpret_cast<uintptr_t>(workspace), b0 = reinterpret_cast<uintptr_t>(bwd_workspace);
+  if (f0 < b0 + bneed && b0 < f0 + need)
+    return fail(HASHENC_EINVAL, "%s: the two workspaces overlap", who);
+  hipError_t e = hg::launch_dlinear_forward_counting(h->grid, h->d, h->F, n, x, params, gamma,
+                                                     static_cast<float*>(workspace), bwd_workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
+}
+
+int hashenc_backward_counted(const hashenc* h, int64_t n, const float* x, const float* g_gamma,
+                             const float* g_dgamma, const float* g_d2gamma, float* grad_params,
+                             void* bwd_workspace, size_t bwd_workspace_bytes, hashenc_stream_t stream) {
+  const char* who = "hashenc_backward_counted";
+  if (!h) return fail(HASHENC_EINVAL, "%s: NULL handle", who);
+  if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "%s: n = %lld out of range", who, (long long)n);
+  if (!counting_for(h, n))
+    return hashenc_backward_ws(h, n, x, g_gamma, g_dgamma, g_d2gamma, grad_params, bwd_workspace,
+                               bwd_workspace_bytes, stream);
+  if (g_dgamma || g_d2gamma)
+    return fail(HASHENC_EUNSUPPORTED, "%s: derivative upstream needs the Hermite kind", who);
+  if (!g_gamma) return ok();
+  if (!x || !grad_params || !bwd_workspace)
+    return fail(HASHENC_EINVAL, "%s: x, grad_params and the workspace must not be NULL", who);
+  if (!aligned16(x) || !aligned16(grad_params) || !aligned16(g_gamma) ||
+      (reinterpret_cast<uintptr_t>(bwd_workspace) & 255u))
+    return fail(HASHENC_EALIGN, "%s: pointers must be 16-byte aligned (workspace 256-byte)", who);
+  const size_t need = hg::binned_backward_workspace_bytes(h->grid, h->d, h->F, false, n);
+  if (bwd_workspace_bytes < need)
+    return fail(HASHENC_EINVAL, "%s: workspace of %zu bytes < %zu needed", who, bwd_workspace_bytes, need);
+  hipError_t e = hg::run_binned_backward(h->grid, h->d, h->F, false, h->d2_mode, n, x, g_gamma, nullptr, nullptr,
+                                         nullptr, grad_params, bwd_workspace, stream, 0, true);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
+}
+
 int hashenc_diag_binned_workspace_size(const hashenc* h, int64_t n, size_t* bytes) {
   if (!h || !bytes) return fail(HASHENC_EINVAL, "hashenc_diag_binned_workspace_size: NULL pointer");
   if (n < 0 || n > kMaxPoints) return fail(HASHENC_EINVAL, "hashenc_diag_binned_workspace_size: n out of range");

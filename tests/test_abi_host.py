@@ -310,3 +310,32 @@ def test_small_dlinear_batches_take_the_atomic_path():
                               "rbf_eps": 1.0, "rbf_rings": 2})
     with pytest.raises(_lib.HashencError):
         api.hashenc_diag_binned_workspace_size(rbf, 100)
+
+
+def test_counting_pair_validation_before_launch():
+    """hashenc_forward_counting / hashenc_backward_counted: argument errors (NULL, alignment,
+    sizes, overlapping workspaces) are reported before any launch."""
+    lib = _lib.load()
+    h = api.hashenc_create({"d": 3, "L": 16, "F": 2, "kind": "dlinear", "T": [1 << 19], "n_min": 16,
+                            "n_max": 2048})
+    n = 1 << 15  # binned, one chunk: the counting path
+    fneed = api.hashenc_forward_workspace_size(h, n)
+    bneed = api.hashenc_backward_workspace_size(h, n)
+    assert fneed > 0 and bneed > 0
+    P = ctypes.c_void_p
+    x, p, g = P(0x10000), P(0x20000), P(0x30000)   # aligned, never dereferenced
+    fws, bws = P(1 << 40), P(1 << 41)
+    call = lambda *a: lib.hashenc_forward_counting(h, n, *a, None)   # noqa: E731
+    assert call(x, p, g, None, None, fws, fneed, None, bneed) == _lib.HASHENC_EINVAL
+    assert call(x, p, g, None, None, fws, fneed - 1, bws, bneed) == _lib.HASHENC_EINVAL
+    assert call(x, p, g, None, None, fws, fneed, bws, bneed - 1) == _lib.HASHENC_EINVAL
+    assert call(x, p, g, None, None, fws, fneed, P((1 << 41) + 4), bneed) == _lib.HASHENC_EALIGN
+    assert call(x, p, g, g, None, fws, fneed, bws, bneed) == _lib.HASHENC_EUNSUPPORTED
+    # the backward workspace starting inside the forward's
+    assert call(x, p, g, None, None, fws, fneed, P((1 << 40) + 256), bneed) == _lib.HASHENC_EINVAL
+    back = lambda *a: lib.hashenc_backward_counted(h, n, *a, None)   # noqa: E731
+    assert back(x, g, None, None, p, bws, bneed - 1) == _lib.HASHENC_EINVAL
+    assert back(x, g, None, None, p, None, bneed) == _lib.HASHENC_EINVAL
+    assert back(x, g, g, None, p, bws, bneed) == _lib.HASHENC_EUNSUPPORTED
+    assert back(x, g, None, None, P(0x20004), bws, bneed) == _lib.HASHENC_EALIGN
+    assert back(x, None, None, None, p, bws, bneed) == 0   # no upstream: nothing to add

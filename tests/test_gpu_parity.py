@@ -474,6 +474,95 @@ def test_adjoint_identity_on_gpu(name):
     assert abs(lhs - rhs) <= 1e-5 * scale
 
 
+@pytest.mark.parametrize("name,n", [("dlinear3d_L16_T19", 3 * 8192 + 37), ("dlinear2d_L4_T12", 65536 + 5)])
+def test_counting_pair(orc, name, n):
+    """The counting forward (bin counts taken while gathering) and the counted backward: gamma
+    bit-identical to forward_ws, gradient against the oracle and against backward_ws.  The
+    2D grid keeps all four levels in LDS, so its counts all come from the count kernel."""
+    W = I.WORKLOADS[name]
+    spec = W["spec"]
+    lay = orc.layout(spec)
+    enc = api.HashGridEncoding(spec)
+    x = _points(name, n)
+    params = _tables(name, lay["n_params"])
+    (G,) = I.upstream(W["id"], _upstream_shapes(spec, n))
+    xt, pt, Gt = _dev(x), _dev(params), _dev(G)
+    fws, bws = enc.forward_workspace(n), enc.backward_workspace(n)
+    assert bws is not None
+    bws.fill_(0x7b)   # stale contents must not matter
+    out = enc.forward_counting(xt, pt, fws, bws)
+    ref_out = enc.forward_ws(xt, pt, enc.workspace(n))
+    assert torch.equal(out["gamma"], ref_out["gamma"])
+    got = enc.backward_counted(xt, torch.zeros(enc.n_params, device=DEV), Gt, bwd_workspace=bws)
+    want = enc.backward_ws(xt, torch.zeros(enc.n_params, device=DEV), Gt, workspace=enc.workspace(n))
+    torch.cuda.synchronize()
+    got, want = got.cpu().numpy(), want.cpu().numpy()
+    _grad_close(got, orc.backward(spec, x, G, n_params=lay["n_params"]), lay, BWD_TOL)
+    _grad_close(got, want.astype(np.float64), lay, 1e-5)
+    # a second pair on the same workspaces (counters re-zeroed by the forward)
+    enc.forward_counting(xt, pt, fws, bws)
+    again = enc.backward_counted(xt, torch.zeros(enc.n_params, device=DEV), Gt, bwd_workspace=bws)
+    torch.cuda.synchronize()
+    _grad_close(again.cpu().numpy(), got.astype(np.float64), lay, 1e-5)
+
+
+def test_counting_pair_full_size_and_fallbacks():
+    """The headline batch through the counting pair matches forward_ws / backward_ws; where the
+    counts do not apply (a small d-linear batch, the Hermite kind) the pair is forward_ws and
+    backward_ws."""
+    for name, n in (("dlinear3d_L16_T19", None), ("dlinear3d_L16_T19", 1000), ("hermite3d_L16_T19", 40000)):
+        W = I.WORKLOADS[name]
+        spec = W["spec"]
+        n = n or W["n_points"]
+        enc = api.HashGridEncoding(spec)
+        x = _dev(I.points(W["id"], n, spec["d"]))
+        p = _dev(_tables(name, enc.n_params))
+        ups = [_dev(u) for u in I.upstream(W["id"], _upstream_shapes(spec, n))]
+        ups += [None] * (3 - len(ups))
+        fws = enc.forward_workspace(n)
+        bws = enc.backward_workspace(n)
+        out = enc.forward_counting(x, p, fws, bws)
+        ref = enc.forward_ws(x, p, enc.workspace(n))
+        for k in ref:
+            assert torch.equal(out[k], ref[k]), (name, n, k)
+        a = enc.backward_counted(x, torch.zeros(enc.n_params, device=DEV), *ups, bwd_workspace=bws)
+        b = enc.backward_ws(x, torch.zeros(enc.n_params, device=DEV), *ups, workspace=enc.workspace(n))
+        torch.cuda.synchronize()
+        assert float((a - b).abs().max()) <= 1e-5 * float(b.abs().max()), (name, n)
+
+
+@pytest.mark.parametrize("name", ["dlinear3d_L16_T19", "hermite3d_L16_T19"])
+def test_binned_nonfinite_upstream(orc, name):
+    """A NaN and an inf upstream value: the levels they reach take the binned reduce's fp64
+    path, the others its fixed-point path.  Non-finite gradient entries sit where the atomic
+    path (plain fp32 adds) puts them; every other entry matches the oracle."""
+    W = I.WORKLOADS[name]
+    spec = W["spec"]
+    lay = orc.layout(spec)
+    n = 3 * 1024 + 37
+    x = _points(name, n, with_edges=False)
+    ups = I.upstream(W["id"], _upstream_shapes(spec, n))
+    F = spec["F"]
+    ups[0][5, 0] = np.nan                # level 0, feature 0 of point 5
+    ups[0][9, 3 * F + 1] = np.inf        # level 3, feature 1 of point 9
+    got = _gpu_backward(spec, x, ups, lay["n_params"], "binned")
+    atom = _gpu_backward(spec, x, ups, lay["n_params"], "atomic")
+    bad = ~np.isfinite(got)
+    assert bad.any()
+    assert np.array_equal(bad, ~np.isfinite(atom))
+    clean = [u.copy() for u in ups]
+    clean[0][5, 0] = 0.0
+    clean[0][9, 3 * F + 1] = 0.0
+    ref = orc.backward(spec, x, *clean, n_params=lay["n_params"])
+    nt, L = lay["offset"].shape
+    for k in range(nt):
+        for l in range(L):
+            o, m = lay["offset"][k, l], lay["rows"][k, l] * lay["width"][k, l]
+            ok = np.isfinite(got[o:o + m])
+            err = np.max(np.abs(got[o:o + m][ok] - ref[o:o + m][ok]), initial=0.0)
+            assert err <= BWD_TOL * np.max(np.abs(ref[o:o + m])), f"table {k} level {l}: {err:.3e}"
+
+
 def test_backward_run_to_run_spread():
     W = I.WORKLOADS["dlinear3d_L16_T19"]
     spec = W["spec"]
