@@ -106,10 +106,19 @@ __device__ __forceinline__ uint32_t hermite_nonfinite_floor(uint32_t ubits, floa
   return __uint_as_float(ubits) * hermite_value_bound(N, d) < __builtin_inff() ? 0u : 0x7fc00000u;
 }
 
+// Largest m over the wavefront (all 64 lanes active), in every lane: DPP row shifts build
+// each 16-lane row's running max, two row broadcasts carry it across rows, lane 63 ends with
+// the whole wavefront's.  VALU only -- a chain of cross-lane LDS permutes costs a round trip
+// per step, which the scatter's wavefronts cannot hide.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  return m;
+  int v = (int)m;
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));  // row_shr:1
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));  // row_shr:2
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true));  // row_shr:4
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true));  // row_shr:8
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
 
 // Segment bounds of a scatter workgroup: raised per wavefront in LDS (vsh[kMaxSeg], zeroed
