@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kFwdLdsThreads) void dlinear_forward_lds_kernel(con
          ...);
       }(std::make_integer_sequence<int, NP>{});
 #pragma unroll
-      for (int f = 0; f < F; ++f) acc[f] += __shfl_xor(acc[f], 1, 64);
+      for (int f = 0; f < F; ++f) acc[f] = add_lane_pair(acc[f]);
       if (c0 == 0) store_vec<F>(stage + ((int64_t)l * n + p) * F, acc);
       int32_t rows = 1;
 #pragma unroll
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kBlock) void dlinear_forward_kernel(const Grid g, c
       for (int f = 0; f < F; ++f) acc[f] = fmaf(w, rows[y][f], acc[f]);
     }
 #pragma unroll
-    for (int f = 0; f < F; ++f) acc[f] += __shfl_xor(acc[f], 1, 64);
+    for (int f = 0; f < F; ++f) acc[f] = add_lane_pair(acc[f]);
     if (c0 == 0 && on) {
       if constexpr (LM_OUT) store_vec<F>(gamma + ((int64_t)l * n + p) * F, acc);
       else store_vec<F>(gamma + p * (int64_t)g.Lrow * F + (int64_t)l * F, acc);

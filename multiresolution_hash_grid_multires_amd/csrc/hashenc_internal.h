@@ -40,6 +40,13 @@ struct Grid {
   int32_t rings;                // Gaussian RBF: neighbourhood rings k
 };
 
+// v plus the value of the neighbouring lane (lane ^ 1): a DPP quad permutation [1, 0, 3, 2],
+// one VALU operation instead of an LDS permute round trip.  Both lanes of the pair must be
+// active.
+__device__ __forceinline__ float add_lane_pair(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+}
+
 // One rounded fp32 product, never fused into a neighbouring add: the cell a point falls in
 // must not depend on the compiler's contraction choices.
 __device__ __forceinline__ float mul_rn(float a, float b) {

@@ -365,11 +365,11 @@ __global__ __launch_bounds__(kBlock) void hermite_forward_kernel(
   }
 #pragma unroll
   for (int f = 0; f < F; ++f) {
-    o.v[f] += __shfl_xor(o.v[f], 1, 64);
+    o.v[f] = add_lane_pair(o.v[f]);
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      o.g[i][f] += __shfl_xor(o.g[i][f], 1, 64);
-      o.h[i][f] += __shfl_xor(o.h[i][f], 1, 64);
+      o.g[i][f] = add_lane_pair(o.g[i][f]);
+      o.h[i][f] = add_lane_pair(o.h[i][f]);
     }
   }
   if constexpr (LM) {
