@@ -224,57 +224,40 @@ __device__ __forceinline__ float acc_value(const uint64_t* acc, int i, const Fix
 }
 
 // Accumulate entries [begin, end) of one segment (a chunk-local row stored as the bits of
-// the first float, then the row's W values) into the LDS chunk.  acc holds the chunk
+// the first float, then the row's W values) into the LDS chunk: each thread keeps U entries
+// (about 32 value registers) in flight before its LDS adds.  acc holds the chunk
 // component-major (acc[j * plane + row]) so that the W components of one row fall in
-// different LDS banks' rotation and a wavefront's random rows spread over all banks.
-// Each thread takes U entries per batch (about 32 value registers) and keeps two batches:
-// the next batch's loads are issued before the current batch's LDS adds, so every wavefront
-// has loads in flight while it accumulates.  Loads past the end re-read the last entry (in
-// bounds, a fixed number of loads per batch, so that each batch waits only for its own).
-template <int R, int U, class Body>
-__device__ __forceinline__ void stream_entries(const float* __restrict__ vseg, int32_t ebase, int32_t begin,
-                                               int32_t end, Body&& body) {
-  const int32_t T = (int32_t)blockDim.x;
-  int32_t e = begin + (int32_t)threadIdx.x;
-  if (e >= end) return;
-  auto load = [&](float (&buf)[U][R], int32_t e0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int32_t eu = min(e0 + u * T, end - 1);
-      load_vec_nt<R>(vseg + (int64_t)(eu - ebase) * R, buf[u]);
-    }
-  };
-  auto run = [&](const float (&buf)[U][R], int32_t e0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (e0 + u * T < end) body(buf[u]);
-  };
-  float a[U][R], b[U][R];
-  load(a, e);
-  for (;;) {
-    const int32_t eb = e + U * T;
-    load(b, eb);
-    run(a, e);
-    if (eb >= end) break;
-    const int32_t ea = eb + U * T;
-    load(a, ea);
-    run(b, eb);
-    if (ea >= end) break;
-    e = ea;
-  }
-}
-
+// different LDS banks' rotation and a wavefront's random rows spread over all banks.  Only
+// entries inside the item are loaded: the small items of small batches would otherwise
+// issue many loads per useful one.
 template <int W, bool FX>
 __device__ __forceinline__ void accumulate_entries(uint64_t* __restrict__ acc, int plane,
                                                    const float* __restrict__ vseg, int32_t ebase,
                                                    int32_t begin, int32_t end, const FixedScale& fs) {
   constexpr int R = hermite_rec_width(W);
-  constexpr int U = W >= 16 ? 1 : 16 / W > 8 ? 8 : 16 / W;
-  stream_entries<R, U>(vseg, ebase, begin, end, [&](const float (&rec)[R]) {
-    const int r = (int)__float_as_uint(rec[0]);
+  // the fp64 fallback (non-finite bounds only) keeps one entry in flight: its registers would
+  // otherwise set the whole kernel's allocation
+  constexpr int U = !FX ? 1 : W >= 32 ? 1 : 32 / W > 8 ? 8 : 32 / W;
+  const int T = blockDim.x;
+  for (int32_t e0 = begin + (int32_t)threadIdx.x; e0 < end; e0 += T * U) {
+    int r[U];
+    float rec[U][R];
 #pragma unroll
-    for (int j = 0; j < W; ++j) acc_add<FX>(acc, j * plane + r, (double)rec[1 + j], fs);
-  });
+    for (int u = 0; u < U; ++u) {
+      const int32_t e = e0 + u * T;
+      if (e < end) {
+        load_vec_nt<R>(vseg + (int64_t)(e - ebase) * R, rec[u]);
+        r[u] = (int)__float_as_uint(rec[u][0]);
+      } else {
+        r[u] = -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (r[u] >= 0)
+#pragma unroll
+        for (int j = 0; j < W; ++j) acc_add<FX>(acc, j * plane + r[u], (double)rec[u][1 + j], fs);
+  }
 }
 
 // d-linear records {rows, t, aG[F]}: the lower row gets (1 - t) aG, the upper (if any) t aG.
@@ -283,18 +266,31 @@ __device__ __forceinline__ void accumulate_records(uint64_t* __restrict__ acc, i
                                                    const float* __restrict__ vseg, int32_t ebase,
                                                    int32_t begin, int32_t end, const FixedScale& fs) {
   constexpr int R = 2 + F;
-  constexpr int U = 32 / R > 8 ? 8 : (32 / R < 1 ? 1 : 32 / R);
-  stream_entries<R, U>(vseg, ebase, begin, end, [&](const float (&rec)[R]) {
-    const uint32_t rows = __float_as_uint(rec[0]);
-    const int lo = (int)(rows & 0xFFFFu), hi = (int)(rows >> 16);
-    const double t = rec[1];
+  constexpr int U = !FX ? 1 : 32 / R > 8 ? 8 : (32 / R < 1 ? 1 : 32 / R);
+  const int T = blockDim.x;
+  for (int32_t e0 = begin + (int32_t)threadIdx.x; e0 < end; e0 += T * U) {
+    float rec[U][R];
+    bool on[U];
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-      const double a = rec[2 + f];
-      acc_add<FX>(acc, f * plane + lo, (1.0 - t) * a, fs);
-      if (hi != 0xFFFF) acc_add<FX>(acc, f * plane + hi, t * a, fs);
+    for (int u = 0; u < U; ++u) {
+      const int32_t e = e0 + u * T;
+      on[u] = e < end;
+      if (on[u]) load_vec_nt<R>(vseg + (int64_t)(e - ebase) * R, rec[u]);
     }
-  });
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!on[u]) continue;
+      const uint32_t rows = __float_as_uint(rec[u][0]);
+      const int lo = (int)(rows & 0xFFFFu), hi = (int)(rows >> 16);
+      const double t = rec[u][1];
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const double a = rec[u][2 + f];
+        acc_add<FX>(acc, f * plane + lo, (1.0 - t) * a, fs);
+        if (hi != 0xFFFF) acc_add<FX>(acc, f * plane + hi, t * a, fs);
+      }
+    }
+  }
 }
 
 constexpr int kFlushBatch = 16;  // gradient values per thread in flight in the reduce's flush (at most)
@@ -348,30 +344,31 @@ __device__ __forceinline__ void flush_chunk(uint64_t* __restrict__ acc, int W, i
 }
 
 // One work item: accumulate its entries into the LDS chunk and flush the chunk into the
-// gradient.  The claim of the next item (dynamic order) is issued between the two.
-template <int ACC, int THREADS, bool FX>
+// gradient.  The claim of the next item (dynamic order) is issued between the two.  The
+// kernel is compiled for one set of record widths (REC: d-linear records of W0 features;
+// else Hermite entries of the widths W0, W1, W2, 0 = none): a kernel holding every width's
+// loop gets the register allocation of the widest and spills the others' addresses.
+template <bool FX, bool REC, int W0, int W1, int W2>
+__device__ __forceinline__ void accumulate_item(uint64_t* __restrict__ acc, int W, int plane,
+                                                const float* __restrict__ vseg, int32_t eb, const WorkItem& w,
+                                                const FixedScale& fs) {
+  if constexpr (REC) {
+    accumulate_records<W0, FX>(acc, plane, vseg, eb, w.begin, w.end, fs);
+  } else {
+    if (W == W0) accumulate_entries<W0, FX>(acc, plane, vseg, eb, w.begin, w.end, fs);
+    if constexpr (W1 > 0)
+      if (W == W1) accumulate_entries<W1, FX>(acc, plane, vseg, eb, w.begin, w.end, fs);
+    if constexpr (W2 > 0)
+      if (W == W2) accumulate_entries<W2, FX>(acc, plane, vseg, eb, w.begin, w.end, fs);
+  }
+}
+
+template <int ACC, int THREADS, bool FX, bool REC, int W0, int W1, int W2>
 __device__ __forceinline__ void reduce_item(uint64_t* __restrict__ acc, const BinPlan& bp, int W, int plane, int nfl,
                                             const float* __restrict__ vseg, int32_t eb, const WorkItem& w,
                                             float* __restrict__ dst, const FixedScale& fs, bool claim,
                                             int32_t* __restrict__ ctr_ptr, int& claimed) {
-  if (bp.records) {
-    switch (W) {
-      case 1: accumulate_records<1, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-      case 2: accumulate_records<2, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-      case 4: accumulate_records<4, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-      default: accumulate_records<8, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-    }
-  } else switch (W) {
-    case 1: accumulate_entries<1, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-    case 2: accumulate_entries<2, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-    case 3: accumulate_entries<3, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-    case 4: accumulate_entries<4, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-    case 6: accumulate_entries<6, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-    case 8: accumulate_entries<8, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-    case 12: accumulate_entries<12, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-    case 16: accumulate_entries<16, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-    default: accumulate_entries<24, FX>(acc, plane, vseg, eb, w.begin, w.end, fs); break;
-  }
+  accumulate_item<FX, REC, W0, W1, W2>(acc, W, plane, vseg, eb, w, fs);
   if (claim && threadIdx.x == 0) {
     // the counter's (global) address through a register the compiler cannot see into:
     // otherwise the one-lane atomic becomes a wavefront-aggregated one whose result is read
@@ -390,7 +387,7 @@ __device__ __forceinline__ void reduce_item(uint64_t* __restrict__ acc, const Bi
 // 1024-lane workgroup per CU) for bins of up to 16384 values, and a 16 KB one (eight 256-lane
 // workgroups per CU) for the small bins of small grids, whose work items are short enough that
 // the per-item latency (fetch, zero, flush) rather than the records sets the time.
-template <int ACC, int THREADS>
+template <int ACC, int THREADS, bool REC, int W0, int W1, int W2>
 __global__ __launch_bounds__(THREADS) void bin_reduce_kernel(const Grid g, const BinPlan bp,
                                                                     BinState* __restrict__ st,
                                                                     const WorkItem* __restrict__ items,
@@ -466,11 +463,11 @@ __global__ __launch_bounds__(THREADS) void bin_reduce_kernel(const Grid g, const
       fs.inv = ldexp(1.0, e - 43);
     }
     if (fixed)
-      reduce_item<ACC, THREADS, true>(acc, bp, W, plane, nfl, vseg, eb, w, dst, fs, !static_items, &st->next_item,
-                                      claimed);
+      reduce_item<ACC, THREADS, true, REC, W0, W1, W2>(acc, bp, W, plane, nfl, vseg, eb, w, dst, fs, !static_items,
+                                                       &st->next_item, claimed);
     else
-      reduce_item<ACC, THREADS, false>(acc, bp, W, plane, nfl, vseg, eb, w, dst, fs, !static_items, &st->next_item,
-                                       claimed);
+      reduce_item<ACC, THREADS, false, REC, W0, W1, W2>(acc, bp, W, plane, nfl, vseg, eb, w, dst, fs, !static_items,
+                                                        &st->next_item, claimed);
     if (static_items) {
       if (threadIdx.x < 5 && nxt < n_items) reinterpret_cast<int*>(&next_sh[slot ^ 1])[threadIdx.x] = pre;
       __syncthreads();
@@ -667,16 +664,44 @@ hipError_t run_bin_reduce(const Grid& g, const BinPlan& bp, const BinWorkspace& 
   // the largest chunk of any table, in values: the small accumulator when it fits
   int64_t chunk_values = 0;
   for (int k = 0; k < bp.ntab; ++k) chunk_values = std::max<int64_t>(chunk_values, (int64_t)bp.width[k] << bp.cshift[k]);
-  if (chunk_values <= kBinLdsValuesSmall) {
-    hipLaunchKernelGGL((bin_reduce_kernel<kBinLdsValuesSmall, 256>), dim3(kBinReduceBlocks * 8), dim3(256), 0, s, g,
-                       bp, reinterpret_cast<BinState*>(ws + w.state), reinterpret_cast<const WorkItem*>(ws + w.items),
-                       reinterpret_cast<const float*>(ws + w.vals), grad, static_items);
+  const bool small = chunk_values <= kBinLdsValuesSmall;
+  // the plan's record widths select the kernel: d-linear F; Hermite F with 2F (d = 2),
+  // 3F (d = 3) or 4F and 6F (d = 4)
+  const int F = bp.width[0];
+  const int code = bp.records ? F : bp.d * 100 + F;
+  switch (code) {
+#define HG_REDUCE(C, REC, W0, W1, W2)                                                                       \
+  case C:                                                                                                   \
+    if (small)                                                                                              \
+      hipLaunchKernelGGL((bin_reduce_kernel<kBinLdsValuesSmall, 256, REC, W0, W1, W2>),                     \
+                         dim3(kBinReduceBlocks * 8), dim3(256), 0, s, g, bp, reinterpret_cast<BinState*>(ws + w.state), \
+                         reinterpret_cast<const WorkItem*>(ws + w.items), reinterpret_cast<const float*>(ws + w.vals), \
+                         grad, static_items);                                                               \
+    else                                                                                                    \
+      hipLaunchKernelGGL((bin_reduce_kernel<kBinLdsValues, kReduceThreads, REC, W0, W1, W2>),               \
+                         dim3(kBinReduceBlocks), dim3(kReduceThreads), 0, s, g, bp,                         \
+                         reinterpret_cast<BinState*>(ws + w.state), reinterpret_cast<const WorkItem*>(ws + w.items), \
+                         reinterpret_cast<const float*>(ws + w.vals), grad, static_items);                   \
     return hipGetLastError();
+    HG_REDUCE(1, true, 1, 0, 0)
+    HG_REDUCE(2, true, 2, 0, 0)
+    HG_REDUCE(4, true, 4, 0, 0)
+    HG_REDUCE(8, true, 8, 0, 0)
+    HG_REDUCE(201, false, 1, 2, 0)
+    HG_REDUCE(202, false, 2, 4, 0)
+    HG_REDUCE(204, false, 4, 8, 0)
+    HG_REDUCE(208, false, 8, 16, 0)
+    HG_REDUCE(301, false, 1, 3, 0)
+    HG_REDUCE(302, false, 2, 6, 0)
+    HG_REDUCE(304, false, 4, 12, 0)
+    HG_REDUCE(308, false, 8, 24, 0)
+    HG_REDUCE(401, false, 1, 4, 6)
+    HG_REDUCE(402, false, 2, 8, 12)
+    HG_REDUCE(404, false, 4, 16, 24)
+#undef HG_REDUCE
+    default:
+      return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((bin_reduce_kernel<kBinLdsValues, kReduceThreads>), dim3(kBinReduceBlocks), dim3(kReduceThreads), 0, s, g, bp,
-                     reinterpret_cast<BinState*>(ws + w.state), reinterpret_cast<const WorkItem*>(ws + w.items),
-                     reinterpret_cast<const float*>(ws + w.vals), grad, static_items);
-  return hipGetLastError();
 }
 
 bool binned_fits(const Grid& g, int d, int F, bool hermite) {
