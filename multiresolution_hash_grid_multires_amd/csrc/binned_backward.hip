@@ -101,10 +101,10 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
   // One workgroup: bin_start = exclusive scan of totals; work items; segment bases.  The
   // totals are staged in LDS by coalesced loads (four in flight per thread), and the first
   // entry of every segment is kept in LDS for the segment bases.
-  __shared__ int32_t part[1024];
-  __shared__ int32_t ipart[1024];
+  __shared__ int32_t part[16];   // per-wavefront totals
+  __shared__ int32_t ipart[16];
   __shared__ int32_t seg0[kMaxSeg + 1];
-  __shared__ int32_t seg_first[kMaxSeg];
+  __shared__ int32_t seg_first[kMaxSeg + 1];
   __shared__ int32_t tot_sh[kMaxBins];
   const int t = threadIdx.x;
   if (t < kMaxSeg) st->vmax_bits[t] = 0u;  // raised by the scatter that follows
@@ -130,19 +130,30 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
       si += (tot + emax - 1) / emax;
     }
   }
-  part[t] = s;
-  ipart[t] = si;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = t >= off ? part[t - off] : 0;
-    const int32_t vi = t >= off ? ipart[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    ipart[t] += vi;
-    __syncthreads();
+  // inclusive scans of (s, si) over the workgroup: within each wavefront by shuffles, then
+  // the 16 wavefront totals (two barriers in all, where a scan over LDS took twenty)
+  int32_t inc = s, inci = si;
+  const int lane = t & 63, wv = t >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t a = __shfl_up(inc, off, 64), ai = __shfl_up(inci, off, 64);
+    if (lane >= off) {
+      inc += a;
+      inci += ai;
+    }
   }
-  int32_t run = part[t] - s;
-  int32_t irun = ipart[t] - si;
+  if (lane == 63) {
+    part[wv] = inc;
+    ipart[wv] = inci;
+  }
+  __syncthreads();
+  int32_t before = 0, beforei = 0;
+  for (int w = 0; w < wv; ++w) {
+    before += part[w];
+    beforei += ipart[w];
+  }
+  int32_t run = before + inc - s;
+  int32_t irun = beforei + inci - si;
   int sg = 0;
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
@@ -166,20 +177,44 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
     }
   }
   if (t == 1023) {
-    bin_start[nb] = part[1023];
-    st->n_items = ipart[1023];
+    bin_start[nb] = run;
+    st->n_items = irun;
     st->next_item = 0;
+    seg_first[bp.nseg] = run;  // the entry count closes the last segment
   }
   __syncthreads();
-  if (t == 0) {
-    int64_t vb = 0;
-    for (int g = 0; g < bp.nseg; ++g) {
-      const int32_t e0 = seg_first[g];
-      const int32_t e1 = g + 1 < bp.nseg ? seg_first[g + 1] : part[1023];
-      st->seg_ebase[g] = e0;
-      st->seg_vbase[g] = vb;
-      vb += (int64_t)(e1 - e0) * (bp.records ? 2 + bp.width[0] : hermite_rec_width(bp.width[g / bp.L]));
-      vb = (vb + kSegAlignFloats - 1) / kSegAlignFloats * kSegAlignFloats;
+  // segment bases: the value floats of each segment rounded up to whole 128-byte lines,
+  // prefix-summed by the first wavefront (a few consecutive segments per lane, then a scan)
+  if (t < 64) {
+    constexpr int SPL = (kMaxSeg + 63) / 64;
+    int64_t sz[SPL];
+    int64_t own = 0;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int g = t * SPL + j;
+      sz[j] = 0;
+      if (g < bp.nseg) {
+        sz[j] = (int64_t)(seg_first[g + 1] - seg_first[g]) *
+                (bp.records ? 2 + bp.width[0] : hermite_rec_width(bp.width[g / bp.L]));
+        sz[j] = (sz[j] + kSegAlignFloats - 1) / kSegAlignFloats * kSegAlignFloats;
+      }
+      own += sz[j];
+    }
+    int64_t incv = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t a = __shfl_up(incv, off, 64);
+      if (lane >= off) incv += a;
+    }
+    int64_t vb = incv - own;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int g = t * SPL + j;
+      if (g < bp.nseg) {
+        st->seg_ebase[g] = seg_first[g];
+        st->seg_vbase[g] = vb;
+      }
+      vb += sz[j];
     }
   }
 }
