@@ -926,16 +926,27 @@ __global__ __launch_bounds__(kBinThreads) void hermite_count_kernel(const Grid g
       if (fine) {
         const bool dense = (g.dense[0] >> l) & 1u;
         const bool few = bp.fine_bin0[l + 1] - bp.fine_bin0[l] <= kFewBins;
-        [&]<int... C>(std::integer_sequence<int, C...>) {
+        // x-corner pairs (Y, Y | 1) usually share a bin: one LDS atomic of 2 then
+        [&]<int... Y>(std::integer_sequence<int, Y...>) {
           ((
                [&] {
-                 const int32_t bin =
-                     bp.fine_bin0[l] + (int32_t)(corner_row<D, C>(keys, dense, g.T[0], g.Tmask[0]) >> bp.fine_shift);
-                 if (few) wave_aggregated_add<false>(hist, bin);
-                 else atomicAdd(&hist[bin], 1);
+                 const int32_t b0 = bp.fine_bin0[l] +
+                                    (int32_t)(corner_row<D, (Y << 1)>(keys, dense, g.T[0], g.Tmask[0]) >> bp.fine_shift);
+                 const int32_t b1 = bp.fine_bin0[l] + (int32_t)(corner_row<D, (Y << 1) | 1>(keys, dense, g.T[0],
+                                                                                              g.Tmask[0]) >>
+                                                                bp.fine_shift);
+                 if (few) {
+                   wave_aggregated_add<false>(hist, b0);
+                   wave_aggregated_add<false>(hist, b1);
+                 } else if (b0 == b1) {
+                   atomicAdd(&hist[b0], 2);
+                 } else {
+                   atomicAdd(&hist[b0], 1);
+                   atomicAdd(&hist[b1], 1);
+                 }
                }()),
            ...);
-        }(std::make_integer_sequence<int, 1 << D>{});
+        }(std::make_integer_sequence<int, 1 << (D - 1)>{});
         continue;
       }
 #pragma unroll
