@@ -582,3 +582,11 @@ def test_backward_run_to_run_spread():
     # accumulation: a second call adds
     enc.backward(x, a, G)
     assert float((a - 2 * b).abs().max()) <= 1e-5 * float(b.abs().max())
+    # The binned reduce sums each bin's values as exact fixed-point integers, so a bin that one
+    # work item covers gets the same bits whatever order its records arrive in.  Here the
+    # hashed levels' bins hold about 2^20 * 4 / 64 = 65536 pair records, below the work-item
+    # size (2^18 entries), so the finest eight levels are bit-identical from run to run.
+    d = torch.zeros(enc.n_params, device=DEV)
+    enc.backward_ws(x, d, G)
+    off = api.hashenc_param_layout(enc.handle, 0, 8)["offset"]
+    assert torch.equal(c[off:], d[off:])
