@@ -646,38 +646,47 @@ __global__ __launch_bounds__(kW * kMWaves, (DEPTH <= 2 ? 2 : 1)) void siren_mfma
           for (int t = 0; t < 4; ++t) gW1[k - 1][t] = mfma16(az, sh.act1[k - 1][16 * t + lm][4 * kk + lq], gW1[k - 1][t]);
         }
       }
-      // input adjoint for the wavefront's tile of input neurons j = 16w + .
-      const int fi = k == 0 ? NI : kW;
-      mf4 vbar[R];
+      if (k > 0) {
+        // input adjoint for the wavefront's tile of input neurons j = 16w + .
+        mf4 vbar[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) vbar[r] = mf4{0.f, 0.f, 0.f, 0.f};
-      if (16 * w < fi) {
+        for (int r = 0; r < R; ++r) vbar[r] = mf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-          const float aw = k == 0 ? sh.w0[4 * kk + lq][16 * w + lm] : sh.w1[k - 1][4 * kk + lq][16 * w + lm];
+          const float aw = sh.w1[k - 1][4 * kk + lq][16 * w + lm];
 #pragma unroll
           for (int r = 0; r < R; ++r) vbar[r] = mfma16(aw, sh.zb[4 * kk + lq][r * kMP + lm], vbar[r]);
         }
-      }
-      __syncthreads();  // zb and the layer's inputs are rewritten next
-      if (k > 0) {
+        __syncthreads();  // zb and the layer's inputs are rewritten next
 #pragma unroll
         for (int r = 0; r < R; ++r) abar[r] = vbar[r];
-      } else if (16 * w < fi && pp < n) {
-        // encoder upstream, inputs j = 16w + 4lq + i of point pp (the encoder output's layout,
-        // 32-bit byte offsets from the iteration's first row)
+      } else {
+        // encoder upstream: the NI / 16 tiles of input neurons times the R row kinds, dealt
+        // round-robin over the wavefronts (with NI = 32 two wavefronts would otherwise carry
+        // all of it while the other two wait at the barrier), each stored as soon as it is
+        // done: inputs j = 16 jt + 4 lq + i of point pp (the encoder output's layout, 32-bit
+        // byte offsets from the iteration's first row)
+        constexpr int NT = NI / 16;
         char* ubase = reinterpret_cast<char*>(up + ((p0 * R) << a.fshift));
+        for (int T = w; T < NT * R; T += kMWaves) {
+          const int jt = T % NT, r = T / NT;
+          mf4 acc = mf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = 16 * w + 4 * lq + i;
-          if (j < a.ain) {
-            const int l = j >> a.fshift, f = j & ((1 << a.fshift) - 1);
-            const uint32_t off = (uint32_t)l * level_bytes + (uint32_t)(((lm * R) << a.fshift) + f) * 4u;
+          for (int kk = 0; kk < 16; ++kk)
+            acc = mfma16(sh.w0[4 * kk + lq][16 * jt + lm], sh.zb[4 * kk + lq][r * kMP + lm], acc);
+          if (pp < n) {
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-              *reinterpret_cast<float*>(ubase + off + ((uint32_t)r << a.fshift) * 4u) = vbar[r][i];
+            for (int i = 0; i < 4; ++i) {
+              const int j = 16 * jt + 4 * lq + i;
+              if (j < a.ain) {
+                const int l = j >> a.fshift, f = j & ((1 << a.fshift) - 1);
+                const uint32_t off = (uint32_t)l * level_bytes + (uint32_t)(((lm * R) << a.fshift) + f) * 4u;
+                *reinterpret_cast<float*>(ubase + off + ((uint32_t)r << a.fshift) * 4u) = acc[i];
+              }
+            }
           }
         }
+        __syncthreads();  // zb and the layer's inputs are rewritten next
       }
     }
   }
@@ -1002,33 +1011,42 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
           for (int t = 0; t < 4; ++t) gW1[t] = mfma16(az, sh.act1[16 * t + lm][c], gW1[t]);
         }
       }
-      constexpr int fi = K == 0 ? NI : kW;
-      mf4 vbar[RG];
+      if constexpr (K > 0) {
+        // input adjoint for the wavefront's tile of input neurons j = 16 wn + .
+        mf4 vbar[RG];
 #pragma unroll
-      for (int rr = 0; rr < RG; ++rr) vbar[rr] = mf4{0.f, 0.f, 0.f, 0.f};
-      if (16 * wn < fi) {
+        for (int rr = 0; rr < RG; ++rr) vbar[rr] = mf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-          const float aw = K == 0 ? sh.w0[4 * kk + lq][16 * wn + lm] : sh.w1[4 * kk + lq][16 * wn + lm];
+          const float aw = sh.w1[4 * kk + lq][16 * wn + lm];
 #pragma unroll
           for (int rr = 0; rr < RG; ++rr)
             if (r0 + rr < R) vbar[rr] = mfma16(aw, sh.zb[4 * kk + lq][(r0 + rr) * kMP + lm], vbar[rr]);
         }
-      }
-      __syncthreads();  // zb and the layer's inputs are rewritten next
-      if constexpr (K > 0) {
+        __syncthreads();  // zb and the layer's inputs are rewritten next
 #pragma unroll
         for (int rr = 0; rr < RG; ++rr) abar[rr] = vbar[rr];
-      } else if (16 * wn < fi && pp < n) {
+      } else {
+        // encoder upstream: the group's (input tile, row) pairs dealt round-robin over its four
+        // wavefronts (with NI = 32 two of them would otherwise carry all of it), each stored
+        // as soon as it is done
+        constexpr int NT = NI / 16;
+        const int nrows = R - r0 < RG ? R - r0 : RG;
+        for (int T = wn; T < NT * nrows; T += kMWaves) {
+          const int jt = T % NT, rr = T / NT;
+          mf4 acc = mf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = 16 * wn + 4 * lq + i;
-          if (j < a.ain) {
+          for (int kk = 0; kk < 16; ++kk)
+            acc = mfma16(sh.w0[4 * kk + lq][16 * jt + lm], sh.zb[4 * kk + lq][(r0 + rr) * kMP + lm], acc);
+          if (pp < n) {
 #pragma unroll
-            for (int rr = 0; rr < RG; ++rr)
-              if (r0 + rr < R) up[fd_index(a, n, pp, j, r0 + rr, R)] = vbar[rr][i];
+            for (int i = 0; i < 4; ++i) {
+              const int j = 16 * jt + 4 * lq + i;
+              if (j < a.ain) up[fd_index(a, n, pp, j, r0 + rr, R)] = acc[i];
+            }
           }
         }
+        __syncthreads();  // zb and the layer's inputs are rewritten next
       }
     };
     if constexpr (DEPTH > 1) rev_layer.template operator()<1>();
