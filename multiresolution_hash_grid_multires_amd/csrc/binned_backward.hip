@@ -94,6 +94,42 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void bin_scan_apply_kernel
   }
 }
 
+// The same scan in one pass when there are at most kScanOneRows tiles: a 1024-lane workgroup
+// per 64 bins, its 16 wavefronts taking consecutive runs of at most 16 tiles each, held in
+// registers between the segment sums (exchanged through LDS) and the rewrite.  Small batches
+// have few tiles, and there the second launch and its round trips are a visible share.
+constexpr int kScanOneWaves = 16;
+constexpr int kScanOneRowsPerWave = 16;
+constexpr int kScanOneRows = kScanOneWaves * kScanOneRowsPerWave;
+
+__global__ __launch_bounds__(64 * kScanOneWaves) void bin_scan_one_pass_kernel(int32_t* __restrict__ counts,
+                                                                             int32_t nblk, int32_t nbins,
+                                                                             int32_t* __restrict__ totals) {
+  __shared__ int32_t wsum[kScanOneWaves][64];
+  const int lane = (int)(threadIdx.x & 63), wave = (int)(threadIdx.x >> 6);
+  const int bin = blockIdx.x * 64 + lane;
+  const int per = (nblk + kScanOneWaves - 1) / kScanOneWaves;  // <= kScanOneRowsPerWave
+  const int r0 = min(nblk, wave * per), r1 = min(nblk, r0 + per);
+  const bool on = bin < nbins;
+  int32_t c[kScanOneRowsPerWave];
+  int32_t s = 0;
+#pragma unroll
+  for (int u = 0; u < kScanOneRowsPerWave; ++u) {
+    c[u] = (on && r0 + u < r1) ? counts[(int64_t)(r0 + u) * nbins + bin] : 0;
+    s += c[u];
+  }
+  wsum[wave][lane] = s;
+  __syncthreads();
+  int32_t run = 0;
+  for (int w = 0; w < wave; ++w) run += wsum[w][lane];
+  if (on && wave == kScanOneWaves - 1) totals[bin] = run + s;
+#pragma unroll
+  for (int u = 0; u < kScanOneRowsPerWave; ++u) {
+    if (on && r0 + u < r1) counts[(int64_t)(r0 + u) * nbins + bin] = run;
+    run += c[u];
+  }
+}
+
 __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const int32_t* __restrict__ totals,
                                                         int32_t* __restrict__ bin_start,
                                                         WorkItem* __restrict__ items,
@@ -676,13 +712,19 @@ hipError_t run_bin_middle(const BinPlan& bp, const BinWorkspace& w, char* ws, hi
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.counts);
   int32_t* totals = reinterpret_cast<int32_t*>(ws + w.totals);
   int32_t* seg_sums = reinterpret_cast<int32_t*>(ws + w.seg_sums);
-  const dim3 sgrid((unsigned)((bp.nbins + 63) / 64), kScanSegs / kScanWavesPerBlock);
-  hipLaunchKernelGGL(bin_scan_sums_kernel, sgrid, dim3(64 * kScanWavesPerBlock), 0, s, counts, w.nblk, bp.nbins,
-                     seg_sums);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bin_scan_apply_kernel, sgrid, dim3(64 * kScanWavesPerBlock), 0, s, counts, w.nblk, bp.nbins,
-                     seg_sums, totals);
+  hipError_t e;
+  if (w.nblk <= kScanOneRows) {
+    hipLaunchKernelGGL(bin_scan_one_pass_kernel, dim3((unsigned)((bp.nbins + 63) / 64)), dim3(64 * kScanOneWaves), 0,
+                       s, counts, w.nblk, bp.nbins, totals);
+  } else {
+    const dim3 sgrid((unsigned)((bp.nbins + 63) / 64), kScanSegs / kScanWavesPerBlock);
+    hipLaunchKernelGGL(bin_scan_sums_kernel, sgrid, dim3(64 * kScanWavesPerBlock), 0, s, counts, w.nblk, bp.nbins,
+                       seg_sums);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bin_scan_apply_kernel, sgrid, dim3(64 * kScanWavesPerBlock), 0, s, counts, w.nblk, bp.nbins,
+                       seg_sums, totals);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bin_plan_kernel, dim3(1), dim3(1024), 0, s, bp, totals,
