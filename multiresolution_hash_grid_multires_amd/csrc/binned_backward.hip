@@ -146,13 +146,14 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
   if (t < kMaxSeg) st->vmax_bits[t] = 0u;  // raised by the scatter that follows
   for (int i = t; i <= bp.nseg; i += 1024) seg0[i] = bp.seg_bin0[i];
   const int nb = bp.nbins;
-  for (int i0 = t; i0 < nb; i0 += 4 * 1024) {
-    int32_t v[4];
+  {
+    constexpr int U = kMaxBins / 1024;  // every load in flight before the first LDS store
+    int32_t v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = i0 + u * 1024 < nb ? totals[i0 + u * 1024] : 0;
+    for (int u = 0; u < U; ++u) v[u] = t + u * 1024 < nb ? totals[t + u * 1024] : 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (i0 + u * 1024 < nb) tot_sh[i0 + u * 1024] = v[u];
+    for (int u = 0; u < U; ++u)
+      if (t + u * 1024 < nb) tot_sh[t + u * 1024] = v[u];
   }
   __syncthreads();
   const int per = (nb + 1023) / 1024;
@@ -190,7 +191,14 @@ __global__ __launch_bounds__(1024) void bin_plan_kernel(const BinPlan bp, const 
   }
   int32_t run = before + inc - s;
   int32_t irun = beforei + inci - si;
+  // segment owning bin b0 (the last with seg0 <= b0; seg0[0] = 0) by bisection, then walked
+  // forward over this thread's few bins
   int sg = 0;
+  for (int hi = bp.nseg - 1; sg < hi;) {
+    const int mid = (sg + hi + 1) >> 1;
+    if (seg0[mid] <= b0) sg = mid;
+    else hi = mid - 1;
+  }
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
     if (b < nb) {
