@@ -435,6 +435,19 @@ def test_full_size_backward(orc, name):
         _grad_close(_gpu_backward(spec, x, ups, lay["n_params"], path), ref, lay, BWD_TOL)
 
 
+@pytest.mark.parametrize("n", [256 * 512, 256 * 512 + 1])
+def test_binned_scan_tile_limit(orc, n):
+    # 2D Hermite scatter tiles hold 512 points at F = 2: 256 tiles is the largest count matrix
+    # scanned in one pass (16 tiles per wavefront), 257 tiles the smallest scanned in two
+    W = I.WORKLOADS["hermite2d_L8_T14"]
+    spec = W["spec"]
+    lay = orc.layout(spec)
+    x = _points("hermite2d_L8_T14", n)
+    ups = I.upstream(W["id"], _upstream_shapes(spec, n))
+    ref = orc.backward(spec, x, *ups, n_params=lay["n_params"])
+    _grad_close(_gpu_backward(spec, x, ups, lay["n_params"], "binned"), ref, lay, BWD_TOL)
+
+
 def test_binned_backward_chunks_and_clusters(orc):
     # more points than one 2^21 chunk, half of them clustered (hot bins split across work
     # items), a workspace reused across calls and accumulation into a non-zero gradient
