@@ -422,6 +422,12 @@ __device__ __forceinline__ mf4 mfma16(float a, float b, mf4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// The matrix-core runs of the SIREN kernels are issued at raised wavefront priority (the
+// instruction arbiter's, per wave): of the two wavefronts on a SIMD, the one in a run of
+// MFMAs keeps the matrix core fed while the other does its LDS and VALU work.
+__device__ __forceinline__ void mfma_prio_hi() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void mfma_prio_lo() { __builtin_amdgcn_s_setprio(0); }
+
 template <int D, int DEPTH, int NI>
 __global__ __launch_bounds__(kW * kMWaves, (DEPTH <= 2 ? 2 : 1)) void siren_mfma_kernel(
     const MlpArgs a, int64_t n, double inv_n_total, const float* __restrict__ x,
@@ -529,6 +535,7 @@ __global__ __launch_bounds__(kW * kMWaves, (DEPTH <= 2 ? 2 : 1)) void siren_mfma
       mf4 acc[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r] = mf4{0.f, 0.f, 0.f, 0.f};
+      mfma_prio_hi();
       if (k == 0) {
 #pragma unroll
         for (int kk = 0; kk < NI / 4; ++kk) {
@@ -544,6 +551,7 @@ __global__ __launch_bounds__(kW * kMWaves, (DEPTH <= 2 ? 2 : 1)) void siren_mfma
           for (int r = 0; r < R; ++r) acc[r] = mfma16(aw, sh.act1[k - 1][4 * kk + lq][r * kMP + lm], acc[r]);
         }
       }
+      mfma_prio_lo();
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[0][i] += bias[k][i];
 #pragma unroll
@@ -635,6 +643,7 @@ __global__ __launch_bounds__(kW * kMWaves, (DEPTH <= 2 ? 2 : 1)) void siren_mfma
       }
       __syncthreads();
       // weight gradient: dL/dW_k[16w + .][j] += sum_c Zbar[o][c] V_k[j][c]
+      mfma_prio_hi();
 #pragma unroll
       for (int kk = 0; kk < NC / 4; ++kk) {
         const float az = sh.zb[16 * w + lm][4 * kk + lq];
@@ -646,17 +655,20 @@ __global__ __launch_bounds__(kW * kMWaves, (DEPTH <= 2 ? 2 : 1)) void siren_mfma
           for (int t = 0; t < 4; ++t) gW1[k - 1][t] = mfma16(az, sh.act1[k - 1][16 * t + lm][4 * kk + lq], gW1[k - 1][t]);
         }
       }
+      mfma_prio_lo();
       if (k > 0) {
         // input adjoint for the wavefront's tile of input neurons j = 16w + .
         mf4 vbar[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) vbar[r] = mf4{0.f, 0.f, 0.f, 0.f};
+        mfma_prio_hi();
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
           const float aw = sh.w1[k - 1][4 * kk + lq][16 * w + lm];
 #pragma unroll
           for (int r = 0; r < R; ++r) vbar[r] = mfma16(aw, sh.zb[4 * kk + lq][r * kMP + lm], vbar[r]);
         }
+        mfma_prio_lo();
         __syncthreads();  // zb and the layer's inputs are rewritten next
 #pragma unroll
         for (int r = 0; r < R; ++r) abar[r] = vbar[r];
@@ -671,9 +683,11 @@ __global__ __launch_bounds__(kW * kMWaves, (DEPTH <= 2 ? 2 : 1)) void siren_mfma
         for (int T = w; T < NT * R; T += kMWaves) {
           const int jt = T % NT, r = T / NT;
           mf4 acc = mf4{0.f, 0.f, 0.f, 0.f};
+          mfma_prio_hi();
 #pragma unroll
           for (int kk = 0; kk < 16; ++kk)
             acc = mfma16(sh.w0[4 * kk + lq][16 * jt + lm], sh.zb[4 * kk + lq][r * kMP + lm], acc);
+          mfma_prio_lo();
           if (pp < n) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -882,6 +896,7 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
       mf4 acc[RG];
 #pragma unroll
       for (int rr = 0; rr < RG; ++rr) acc[rr] = mf4{0.f, 0.f, 0.f, 0.f};
+      mfma_prio_hi();
       if constexpr (K == 0) {
 #pragma unroll
         for (int kk = 0; kk < NI / 4; ++kk) {
@@ -899,6 +914,7 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
             if (r0 + rr < R) acc[rr] = mfma16(aw, sh.act1[4 * kk + lq][(r0 + rr) * kMP + lm], acc[rr]);
         }
       }
+      mfma_prio_lo();
 #pragma unroll
       for (int rr = 0; rr < RG; ++rr) {
 #pragma unroll
@@ -1000,6 +1016,7 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
       __syncthreads();
       // weight gradient over the group's columns: dL/dW_K[16wn + .][j] += sum_c Zbar[o][c] V_K[j][c]
       const int nc4 = (R - r0 < RG ? R - r0 : RG) * (kMP / 4);
+      mfma_prio_hi();
       for (int kk = 0; kk < nc4; ++kk) {
         const int c = r0 * kMP + 4 * kk + lq;
         const float az = sh.zb[16 * wn + lm][c];
@@ -1011,11 +1028,13 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
           for (int t = 0; t < 4; ++t) gW1[t] = mfma16(az, sh.act1[16 * t + lm][c], gW1[t]);
         }
       }
+      mfma_prio_lo();
       if constexpr (K > 0) {
         // input adjoint for the wavefront's tile of input neurons j = 16 wn + .
         mf4 vbar[RG];
 #pragma unroll
         for (int rr = 0; rr < RG; ++rr) vbar[rr] = mf4{0.f, 0.f, 0.f, 0.f};
+        mfma_prio_hi();
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
           const float aw = sh.w1[4 * kk + lq][16 * wn + lm];
@@ -1023,6 +1042,7 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
           for (int rr = 0; rr < RG; ++rr)
             if (r0 + rr < R) vbar[rr] = mfma16(aw, sh.zb[4 * kk + lq][(r0 + rr) * kMP + lm], vbar[rr]);
         }
+        mfma_prio_lo();
         __syncthreads();  // zb and the layer's inputs are rewritten next
 #pragma unroll
         for (int rr = 0; rr < RG; ++rr) abar[rr] = vbar[rr];
@@ -1035,9 +1055,11 @@ __global__ __launch_bounds__(kW * kFdWaves) void siren_fd_mfma_kernel(
         for (int T = wn; T < NT * nrows; T += kMWaves) {
           const int jt = T % NT, rr = T / NT;
           mf4 acc = mf4{0.f, 0.f, 0.f, 0.f};
+          mfma_prio_hi();
 #pragma unroll
           for (int kk = 0; kk < 16; ++kk)
             acc = mfma16(sh.w0[4 * kk + lq][16 * jt + lm], sh.zb[4 * kk + lq][(r0 + rr) * kMP + lm], acc);
+          mfma_prio_lo();
           if (pp < n) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
